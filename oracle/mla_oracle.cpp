@@ -1,0 +1,359 @@
+// Plain, slow CPU oracle of the Multi-Head Latent Attention (MLA) prolog.
+//
+// TEST INFRASTRUCTURE ONLY.  The HIP library never links, loads or calls this
+// file; only the tests, the smoke check and the benchmark's CPU-baseline leg
+// do.  It shares no code, header, table or helper with the HIP path.
+//
+// What it computes is the formula block of the MLA prolog operator page
+// (aclnnMlaPrologV2WeightNz, "Function", formulas), per token t:
+//
+//   c^Q  = RmsNorm(x W^DQ)                      (query down-projection + norm)
+//   q^C  = c^Q W^UQ,   q^N = q^C W^UK  per head (the two up-projections)
+//   q^R  = ROPE(c^Q W^QR)                       (query rotary part)
+//   c^KV = RmsNorm(x W^DKV)  -> kvCache[cacheIndex[t]]
+//   k^R  = ROPE(x W^KR)      -> krCache[cacheIndex[t]]
+//   optional: dequantScaleQNope = RowMax(|q^N|)/127, q^N = round(q^N/scale)
+//
+// RmsNorm(v)_i = gamma_i v_i / sqrt((1/n) sum_j v_j^2 + eps), eps inside the
+// root and n the vector length (same page, "RmsNorm formula").  RoPE is the
+// rotate-half form, the only mode the MLA preprocess page (aclnnMlaPreprocess,
+// constraints, rope mode) supports: pairs (i, i + Dr/2) with one cos/sin
+// table entry per element.
+//
+// Arithmetic is double.  In the int8 full-quantisation scenario (same page,
+// scenario and dtype tables) the integer products are summed exactly in
+// int64 and dequantised as acc * scaleX[t] * scaleW[n].  A value is rounded
+// exactly where the operator stores it as a tensor or feeds it to a bf16/int8
+// matrix product (the readings R1..R7):
+//   R1 kvCache row = bf16(c^KV)          R2 krCache row = bf16(k^R)
+//   R3 bf16 operand bf16(c^Q)            R3' int8 operand: per-token dynamic
+//                                            int8 of c^Q, decided in float32
+//   R4 queryRopeOut = bf16(q^R)          R5 W^UK operand bf16(q^C)
+//   R6 queryOut = bf16(q^N)              R7 int8 queryOut: per-(token, head)
+//                                            dynamic int8, decided in float32
+// round_intermediates = 0 skips R3 and R5 (used by the composition pin).
+//
+// Every function here is pinned by the CPU tests (closed forms, invariants,
+// special cases, brute force on tiny shapes, planted mistakes); none is
+// unpinned.
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <thread>
+#include <vector>
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// bf16 codec.  bf16 is the upper half of an IEEE-754 binary32 word: 1 sign
+// bit, 8 exponent bits (bias 127), 7 stored fraction bits.
+// ---------------------------------------------------------------------------
+double bf16_value(uint16_t bits) {
+  uint32_t w = static_cast<uint32_t>(bits) << 16;
+  float f;
+  std::memcpy(&f, &w, sizeof f);
+  return static_cast<double>(f);
+}
+
+// Nearest bf16 to v, ties to even, computed from v directly (no detour
+// through binary32, which could round twice).  The spacing of bf16 values
+// near |v| in [2^e, 2^(e+1)) is 2^(e-7), and 2^-133 below 2^-126.
+uint16_t bf16_bits(double v) {
+  if (std::isnan(v)) return 0x7FC0;
+  const double kMax = (2.0 - std::ldexp(1.0, -7)) * std::ldexp(1.0, 127);
+  uint16_t sign = std::signbit(v) ? 0x8000 : 0;
+  double a = std::fabs(v);
+  if (std::isinf(a)) return sign | 0x7F80;
+  if (a == 0.0) return sign;
+  int e = std::ilogb(a);
+  if (e < -126) e = -126;
+  double r = std::ldexp(std::nearbyint(std::ldexp(a, 7 - e)), e - 7);  // RNE
+  if (r > kMax) return sign | 0x7F80;
+  float f = static_cast<float>(r);  // exact: r is a bf16 value
+  uint32_t w;
+  std::memcpy(&w, &f, sizeof w);
+  return sign | static_cast<uint16_t>(w >> 16);
+}
+
+double bf16_round(double v) { return bf16_value(bf16_bits(v)); }
+
+// RmsNorm over n values (aclnnMlaPrologV2WeightNz, "RmsNorm formula").
+void rmsnorm(const double* v, const double* gamma, int64_t n, double eps, double* out,
+             int mutation) {
+  double ss = 0.0;
+  for (int64_t i = 0; i < n; ++i) ss += v[i] * v[i];
+  double ms = ss / static_cast<double>(n);
+  double rms = std::sqrt(ms + eps);
+  if (mutation == 2) rms = std::sqrt(ms) + eps;  // planted: eps outside the root
+  for (int64_t i = 0; i < n; ++i) {
+    double g = (mutation == 5) ? 1.0 : gamma[i];  // planted: gamma dropped
+    out[i] = g * v[i] / rms;
+  }
+}
+
+// Rotate-half RoPE of one vector of length Dr:
+//   out_i     = v_i     cos_i     - v_{i+h} sin_i
+//   out_{i+h} = v_{i+h} cos_{i+h} + v_i     sin_{i+h}        (h = Dr/2)
+void rope(const double* v, const double* cos, const double* sin, int64_t Dr, double* out,
+          int mutation) {
+  int64_t h = Dr / 2;
+  double s = (mutation == 1) ? -1.0 : 1.0;  // planted: rotation sign flipped
+  for (int64_t i = 0; i < h; ++i) {
+    out[i] = v[i] * cos[i] - s * v[i + h] * sin[i];
+    out[i + h] = v[i + h] * cos[i + h] + s * v[i] * sin[i + h];
+  }
+}
+
+// Symmetric dynamic int8 of one row, decided in float32:
+//   scale = RowMax(|v|)/127,  q = round(v/scale) ties to even, within [-127, 127]
+// (aclnnMlaPrologV2WeightNz, "Dequant Scale Query Nope calculation formula").
+// A row of zeros gets scale 0 and q = 0.
+void quant_int8(const double* v, int64_t n, int8_t* q, float* scale) {
+  float amax = 0.0f;
+  for (int64_t i = 0; i < n; ++i) amax = std::max(amax, std::fabs(static_cast<float>(v[i])));
+  float s = amax / 127.0f;
+  *scale = s;
+  for (int64_t i = 0; i < n; ++i) {
+    if (s == 0.0f) { q[i] = 0; continue; }
+    float r = std::nearbyint(static_cast<float>(v[i]) / s);
+    r = std::min(127.0f, std::max(-127.0f, r));
+    q[i] = static_cast<int8_t>(r);
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+// One problem: dims, attributes, host tensors.  Layouts are those of the
+// operator's parameter table: tokenX (T, He); weightDq (He, Hcq);
+// weightUqQr (Hcq, N*(D+Dr)); weightUk (N, D, Hckv); weightDkvKr
+// (He, Hckv+Dr); gammas (Hcq), (Hckv); ropeSin/ropeCos (T, Dr); cacheIndex
+// (T) int64; caches (BlockNum, BlockSize, 1, Hckv|Dr).  All weights are
+// (k, n) row-major.  weightUqQr columns are head-interleaved: column
+// h*(D+Dr)+j is W^UQ column h*D+j for j < D and W^QR column h*Dr+j-D
+// otherwise.  weightDkvKr holds W^DKV in columns [0, Hckv), W^KR after.
+typedef struct {
+  int64_t T, He, Hcq, Hckv, N, D, Dr;
+  int64_t block_num, block_size;
+  double eps_cq, eps_ckv;
+  int32_t quant_in;             // 1: int8 x, W^DQ, W^UqQr, W^DkvKr + fp32 scales
+  int32_t query_int8;           // 1: q^N as int8 + per-(token, head) scale
+  int32_t round_intermediates;  // 0: skip R3 and R5
+  int32_t mutation;             // planted mistake for the pin tests, 0 = none
+  const void* x;                // uint16 bf16 bits, or int8
+  const void* w_dq;
+  const void* w_uq_qr;
+  const uint16_t* w_uk;
+  const void* w_dkv_kr;
+  const uint16_t* gamma_cq;
+  const uint16_t* gamma_ckv;
+  const uint16_t* rope_sin;
+  const uint16_t* rope_cos;
+  const int64_t* cache_index;
+  uint16_t* kv_cache;           // updated in place; NULL = no cache writes
+  uint16_t* kr_cache;
+  const float* scale_x;         // (T)
+  const float* scale_w_dq;      // (Hcq)
+  const float* scale_w_uq_qr;   // (N*(D+Dr))
+  const float* scale_w_dkv_kr;  // (Hckv+Dr)
+  const int64_t* tokens;        // rows to compute; NULL = 0..T-1
+  int64_t n_tokens;
+  // outputs, row r of each holds token tokens[r]
+  void* query_out;              // (n, N, Hckv) bf16 bits or int8
+  uint16_t* query_rope_out;     // (n, N, Dr)
+  float* dequant_scale_q_nope;  // (n, N), int8 query only
+  uint16_t* kv_rows;            // optional (n, Hckv): the row written to kvCache
+  uint16_t* kr_rows;            // optional (n, Dr)
+  double* y_out;                // optional (n, Hcq+Hckv+Dr): x W^DQ | x W^DKV | x W^KR
+  double* cq_out;               // optional (n, Hcq): c^Q before rounding
+  double* u_out;                // optional (n, N*(D+Dr)): c^Q W^UqQr
+  double* qn_out;               // optional (n, N, Hckv): q^N before rounding
+} mla_oracle_problem;
+
+double mla_oracle_bf16_value(uint16_t bits) { return bf16_value(bits); }
+uint16_t mla_oracle_bf16_bits(double v) { return bf16_bits(v); }
+
+void mla_oracle_rmsnorm(const double* v, const double* gamma, int64_t n, double eps,
+                        double* out) {
+  rmsnorm(v, gamma, n, eps, out, 0);
+}
+
+void mla_oracle_rope(const double* v, const double* cos, const double* sin, int64_t Dr,
+                     double* out) {
+  rope(v, cos, sin, Dr, out, 0);
+}
+
+void mla_oracle_quant_int8(const double* v, int64_t n, int8_t* q, float* scale) {
+  quant_int8(v, n, q, scale);
+}
+
+static double load(const void* base, int64_t i, int32_t is_int8) {
+  if (is_int8) return static_cast<double>(static_cast<const int8_t*>(base)[i]);
+  return bf16_value(static_cast<const uint16_t*>(base)[i]);
+}
+
+// The whole prolog for row r (token t) of the problem.
+static void one_token(const mla_oracle_problem* p, int64_t r, int64_t t) {
+  const int64_t He = p->He, Hcq = p->Hcq, Hckv = p->Hckv, N = p->N, D = p->D, Dr = p->Dr;
+  const int64_t Wkr = Hckv + Dr, Wuq = N * (D + Dr);
+  const int32_t q8in = p->quant_in;
+  const int mut = p->mutation;
+
+  // down-projections: y_q = x W^DQ (Hcq), y_kvr = x [W^DKV | W^KR] (Hckv+Dr)
+  std::vector<double> y_q(Hcq, 0.0), y_kvr(Wkr, 0.0);
+  if (q8in) {
+    const int8_t* x = static_cast<const int8_t*>(p->x) + t * He;
+    const int8_t* wq = static_cast<const int8_t*>(p->w_dq);
+    const int8_t* wk = static_cast<const int8_t*>(p->w_dkv_kr);
+    std::vector<int64_t> aq(Hcq, 0), ak(Wkr, 0);
+    for (int64_t k = 0; k < He; ++k) {
+      int64_t xv = x[k];
+      for (int64_t n = 0; n < Hcq; ++n) aq[n] += xv * wq[k * Hcq + n];
+      for (int64_t n = 0; n < Wkr; ++n) ak[n] += xv * wk[k * Wkr + n];
+    }
+    double sx = p->scale_x[t];
+    for (int64_t n = 0; n < Hcq; ++n) y_q[n] = static_cast<double>(aq[n]) * sx * p->scale_w_dq[n];
+    for (int64_t n = 0; n < Wkr; ++n) y_kvr[n] = static_cast<double>(ak[n]) * sx * p->scale_w_dkv_kr[n];
+  } else {
+    for (int64_t k = 0; k < He; ++k) {
+      double xv = load(p->x, t * He + k, 0);
+      for (int64_t n = 0; n < Hcq; ++n) y_q[n] += xv * load(p->w_dq, k * Hcq + n, 0);
+      for (int64_t n = 0; n < Wkr; ++n) y_kvr[n] += xv * load(p->w_dkv_kr, k * Wkr + n, 0);
+    }
+  }
+  if (p->y_out) {
+    double* yo = p->y_out + r * (Hcq + Wkr);
+    for (int64_t n = 0; n < Hcq; ++n) yo[n] = y_q[n];
+    for (int64_t n = 0; n < Wkr; ++n) yo[Hcq + n] = y_kvr[n];
+  }
+
+  std::vector<double> cosv(Dr), sinv(Dr);
+  for (int64_t i = 0; i < Dr; ++i) {
+    cosv[i] = bf16_value(p->rope_cos[t * Dr + i]);
+    sinv[i] = bf16_value(p->rope_sin[t * Dr + i]);
+  }
+
+  // c^Q and c^KV
+  std::vector<double> g(std::max(Hcq, Hckv));
+  std::vector<double> c_q(Hcq), c_kv(Hckv), k_r(Dr);
+  for (int64_t i = 0; i < Hcq; ++i) g[i] = bf16_value(p->gamma_cq[i]);
+  rmsnorm(y_q.data(), g.data(), Hcq, p->eps_cq, c_q.data(), mut);
+  for (int64_t i = 0; i < Hckv; ++i) g[i] = bf16_value(p->gamma_ckv[i]);
+  rmsnorm(y_kvr.data(), g.data(), Hckv, p->eps_ckv, c_kv.data(), mut);
+  rope(y_kvr.data() + Hckv, cosv.data(), sinv.data(), Dr, k_r.data(), mut);
+  if (p->cq_out)
+    for (int64_t i = 0; i < Hcq; ++i) p->cq_out[r * Hcq + i] = c_q[i];
+  if (p->kv_rows)
+    for (int64_t i = 0; i < Hckv; ++i) p->kv_rows[r * Hckv + i] = bf16_bits(c_kv[i]);  // R1
+  if (p->kr_rows)
+    for (int64_t i = 0; i < Dr; ++i) p->kr_rows[r * Dr + i] = bf16_bits(k_r[i]);      // R2
+
+  // up-projection u = c^Q [W^UQ | W^QR]
+  std::vector<double> u(Wuq, 0.0);
+  if (q8in) {  // R3'
+    std::vector<int8_t> c8(Hcq);
+    float s_cq;
+    quant_int8(c_q.data(), Hcq, c8.data(), &s_cq);
+    const int8_t* w = static_cast<const int8_t*>(p->w_uq_qr);
+    std::vector<int64_t> acc(Wuq, 0);
+    for (int64_t k = 0; k < Hcq; ++k) {
+      int64_t cv = c8[k];
+      for (int64_t n = 0; n < Wuq; ++n) acc[n] += cv * w[k * Wuq + n];
+    }
+    for (int64_t n = 0; n < Wuq; ++n)
+      u[n] = static_cast<double>(acc[n]) * static_cast<double>(s_cq) * p->scale_w_uq_qr[n];
+  } else {
+    for (int64_t k = 0; k < Hcq; ++k) {
+      double cv = p->round_intermediates ? bf16_round(c_q[k]) : c_q[k];  // R3
+      for (int64_t n = 0; n < Wuq; ++n) u[n] += cv * load(p->w_uq_qr, k * Wuq + n, 0);
+    }
+  }
+  if (p->u_out)
+    for (int64_t n = 0; n < Wuq; ++n) p->u_out[r * Wuq + n] = u[n];
+
+  // per head: split, q^R = RoPE(rope part), q^N = bf16(nope part) W^UK[h]
+  std::vector<double> qc(D), qr(Dr), qn(Hckv);
+  for (int64_t h = 0; h < N; ++h) {
+    // column offsets of head h inside weightUqQr
+    int64_t nope0 = h * (D + Dr), rope0 = h * (D + Dr) + D;
+    if (mut == 3) { nope0 = h * D; rope0 = N * D + h * Dr; }  // planted: blocked, not interleaved
+    rope(u.data() + rope0, cosv.data(), sinv.data(), Dr, qr.data(), mut);
+    for (int64_t i = 0; i < Dr; ++i)
+      p->query_rope_out[(r * N + h) * Dr + i] = bf16_bits(qr[i]);  // R4
+    for (int64_t d = 0; d < D; ++d)
+      qc[d] = p->round_intermediates ? bf16_round(u[nope0 + d]) : u[nope0 + d];  // R5
+    for (int64_t j = 0; j < Hckv; ++j) qn[j] = 0.0;
+    for (int64_t d = 0; d < D; ++d) {
+      for (int64_t j = 0; j < Hckv; ++j) {
+        // W^UK[h][d][j]; planted mistake 4 reads it as if laid out (N, Hckv, D)
+        int64_t idx = (mut == 4) ? (h * Hckv + j) * D + d : (h * D + d) * Hckv + j;
+        qn[j] += qc[d] * bf16_value(p->w_uk[idx]);
+      }
+    }
+    if (p->qn_out)
+      for (int64_t j = 0; j < Hckv; ++j) p->qn_out[(r * N + h) * Hckv + j] = qn[j];
+    if (p->query_int8) {  // R7
+      quant_int8(qn.data(), Hckv, static_cast<int8_t*>(p->query_out) + (r * N + h) * Hckv,
+                 p->dequant_scale_q_nope + r * N + h);
+    } else {              // R6
+      uint16_t* qo = static_cast<uint16_t*>(p->query_out) + (r * N + h) * Hckv;
+      for (int64_t j = 0; j < Hckv; ++j) qo[j] = bf16_bits(qn[j]);
+    }
+  }
+}
+
+// Runs the prolog on the selected rows with nthreads threads (0 = all cores),
+// then writes the cache rows at cacheIndex, in row order, skipping indices
+// outside [0, BlockNum*BlockSize).  Returns 0, or -1 on a bad argument.
+int mla_oracle_run(mla_oracle_problem* p, int nthreads) {
+  if (!p || !p->x || !p->w_dq || !p->w_uq_qr || !p->w_uk || !p->w_dkv_kr || !p->gamma_cq ||
+      !p->gamma_ckv || !p->rope_sin || !p->rope_cos || !p->query_out || !p->query_rope_out)
+    return -1;
+  if (p->Dr % 2 != 0 || p->Hcq <= 0 || p->Hckv <= 0 || p->N <= 0 || p->D <= 0 || p->Dr <= 0)
+    return -1;
+  if (p->quant_in && (!p->scale_x || !p->scale_w_dq || !p->scale_w_uq_qr || !p->scale_w_dkv_kr))
+    return -1;
+  if (p->query_int8 && !p->dequant_scale_q_nope) return -1;
+  const int64_t n = p->tokens ? p->n_tokens : p->T;
+  for (int64_t r = 0; r < n; ++r) {
+    int64_t t = p->tokens ? p->tokens[r] : r;
+    if (t < 0 || t >= p->T) return -1;
+  }
+  // cache rows are always produced (into caller buffers or scratch)
+  std::vector<uint16_t> kv_tmp, kr_tmp;
+  mla_oracle_problem q = *p;
+  if (!q.kv_rows) { kv_tmp.resize(static_cast<size_t>(n * p->Hckv)); q.kv_rows = kv_tmp.data(); }
+  if (!q.kr_rows) { kr_tmp.resize(static_cast<size_t>(n * p->Dr)); q.kr_rows = kr_tmp.data(); }
+
+  unsigned hw = std::thread::hardware_concurrency();
+  int nt = nthreads > 0 ? nthreads : static_cast<int>(hw ? hw : 1);
+  nt = static_cast<int>(std::min<int64_t>(nt, std::max<int64_t>(n, 1)));
+  std::vector<std::thread> pool;
+  for (int w = 0; w < nt; ++w) {
+    pool.emplace_back([&q, w, nt, n]() {
+      for (int64_t r = w; r < n; r += nt) one_token(&q, r, q.tokens ? q.tokens[r] : r);
+    });
+  }
+  for (auto& th : pool) th.join();
+
+  // scatter (aclnnMlaPrologV2WeightNz, parameters cacheIndex / kvCacheRef /
+  // krCacheRef): flat slot s is block s / BlockSize, offset s % BlockSize
+  if (p->kv_cache && p->kr_cache && p->cache_index) {
+    const int64_t slots = p->block_num * p->block_size;
+    for (int64_t r = 0; r < n; ++r) {
+      int64_t t = p->tokens ? p->tokens[r] : r;
+      int64_t s = p->cache_index[t];
+      if (s < 0 || s >= slots) continue;
+      int64_t blk = s / p->block_size, off = s % p->block_size;
+      uint16_t* kv = p->kv_cache + (blk * p->block_size + off) * p->Hckv;
+      uint16_t* kr = p->kr_cache + (blk * p->block_size + off) * p->Dr;
+      std::memcpy(kv, q.kv_rows + r * p->Hckv, sizeof(uint16_t) * p->Hckv);
+      std::memcpy(kr, q.kr_rows + r * p->Dr, sizeof(uint16_t) * p->Dr);
+    }
+  }
+  return 0;
+}
+
+}  // extern "C"
