@@ -1,0 +1,194 @@
+#!/usr/bin/env python3
+"""Benchmark of the MLA prolog on one MI355X.
+
+One step is one ``mla_prolog_run`` over one batch of synthetic tokens (all
+four kernels: down-projection, norms/RoPE/cache scatter, up-projection with
+q-RoPE, W^UK product).  Inputs are resident in HBM before timing starts; the
+weights rotate over enough replicas that consecutive steps cannot find them
+in the 256 MB Infinity Cache, so every step streams its weights from HBM.
+
+Prints one JSON line: tokens/s, the roofline of the dominant kernel (the
+up-projection) from HIP events recorded around each kernel, the roofline of
+the whole step, and the CPU oracle timed on the host cores on a bounded
+sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA-prolog tokens/s; % HBM roofline (decode), % MFMA peak (prefill)"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+INT8_PEAK_TOPS = 5000.0
+MALL_BYTES = 256 << 20
+
+
+def algorithmic(inp, T):
+    """Bytes and flops each kernel must move / do at minimum for T tokens."""
+    d = inp["dims"]
+    q8 = bool(inp["quant"])
+    eb = 1 if q8 else 2                       # x and the three int8-able weights
+    W = d.N * (d.D + d.Dr)
+    Nkr = d.Hckv + d.Dr
+    qo = 1 if q8 else 2
+    k1_bytes = d.He * (d.Hcq + Nkr) * eb + T * d.He * eb + (q8 and (d.Hcq + Nkr + T) * 4)
+    k1_flop = 2 * T * d.He * (d.Hcq + Nkr)
+    k2_bytes = T * (d.Hckv + d.Dr) * 2 + T * d.Hcq * (1 if q8 else 2) + T * 2 * d.Dr * 2 + T * 8
+    k3_bytes = (d.Hcq * W * eb + T * d.Hcq * (1 if q8 else 2) + T * d.N * d.D * 2
+                + T * d.N * d.Dr * 2 + T * 2 * d.Dr * 2 + (q8 and W * 4 + T * 4))
+    k3_flop = 2 * T * d.Hcq * W
+    k4_bytes = d.N * d.D * d.Hckv * 2 + T * d.N * d.D * 2 + T * d.N * d.Hckv * qo + (q8 and T * d.N * 4)
+    k4_flop = 2 * T * d.N * d.D * d.Hckv
+    weights = d.He * (d.Hcq + Nkr) * eb + d.Hcq * W * eb + d.N * d.D * d.Hckv * 2
+    step_bytes = (weights + T * d.He * eb + T * 2 * d.Dr * 2 + T * 8 + T * d.N * d.Hckv * qo
+                  + T * d.N * d.Dr * 2 + T * (d.Hckv + d.Dr) * 2
+                  + (q8 and (T + d.Hcq + Nkr + W + T * d.N) * 4))
+    return dict(k1_bytes=k1_bytes, k1_flop=k1_flop, k2_bytes=k2_bytes, k3_bytes=k3_bytes,
+                k3_flop=k3_flop, k4_bytes=k4_bytes, k4_flop=k4_flop, weights=weights,
+                step_bytes=step_bytes, step_flop=k1_flop + k3_flop + k4_flop)
+
+
+def cpu_baseline(inp, seconds):
+    """The oracle, as it is, over repeated passes of the workload's first
+    tokens until about ``seconds`` of host time are spent."""
+    import oracle
+    T = int(inp["T"])
+    cores = len(os.sched_getaffinity(0))
+    per_pass = min(T, 64)
+    rows = list(range(per_pass))
+    oracle.run(inp, tokens=rows[:1], caches=False, nthreads=cores)   # load + warm
+    done, t0 = 0, time.perf_counter()
+    while True:
+        oracle.run(inp, tokens=rows, caches=False, nthreads=cores)
+        done += per_pass
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": done / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} tokens ({done // per_pass} passes over the first {per_pass} tokens "
+                      f"of {inp['workload']}) in {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_t32",
+                    choices=["decode_t32", "decode_t256", "prefill_t8192", "int8_decode_t128",
+                             "tiny_t4"])
+    ap.add_argument("--replicas", type=int, default=0, help="weight replicas (0 = enough to "
+                    "exceed twice the Infinity Cache)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the prolog shards by tokens or heads with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import head_latent_attention_amd as mla
+    import synth
+    from synth import device as dev
+
+    wl = synth.workload(args.workload)
+    inp = synth.make_inputs(wl)
+    T = int(inp["T"])
+    d = inp["dims"]
+    alg = algorithmic(inp, T)
+    R = args.replicas or max(1, -(-2 * MALL_BYTES // alg["weights"]) + 1)
+
+    base = dev.upload(inp, device="cuda:0")
+    wnames = ("weight_dq", "weight_uq_qr", "weight_uk", "weight_dkv_kr")
+    sets = [base]
+    for _ in range(R - 1):
+        s = dict(base)
+        for k in wnames:
+            s[k] = base[k].clone()
+        sets.append(s)
+    desc = mla.make_desc(**dev.desc_args(inp))
+    h = mla.MlaProlog(desc)
+    stream = torch.cuda.current_stream()
+
+    for i in range(args.warmup):
+        h.run(sets[i % R], T, stream)
+    torch.cuda.synchronize()
+
+    # timed region 1: throughput
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        h.run(sets[i % R], T, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / args.steps
+
+    # timed region 2: the same steps with HIP events around every kernel
+    h.profile(True)
+    torch.cuda.synchronize()
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0.record(stream)
+    for i in range(args.steps):
+        h.run(sets[i % R], T, stream)
+    p1.record(stream)
+    torch.cuda.synchronize()
+    kms, runs = h.profile_read()
+    ms_step_profiled = p0.elapsed_time(p1) / args.steps
+    h.profile(False)
+    kernel_us = {k: 1000.0 * v / runs for k, v in kms.items()}
+    h.close()
+
+    decode = T < 1024
+    k3_us = kernel_us["up_proj"]
+    if decode:
+        achieved = alg["k3_bytes"] / (k3_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None}
+        path_ach = alg["step_bytes"] / (ms_step * 1e-3) / 1e9
+        path = {"bound": "hbm", "achieved": path_ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": path_ach / HBM_PEAK_GBS, "bytes_per_step": alg["step_bytes"]}
+    else:
+        peak = INT8_PEAK_TOPS if inp["quant"] else BF16_PEAK_TFLOPS
+        achieved = alg["k3_flop"] / (k3_us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak, "traffic": None}
+        path_ach = alg["step_flop"] / (ms_step * 1e-3) / 1e12
+        path = {"bound": "mfma", "achieved": path_ach, "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": path_ach / BF16_PEAK_TFLOPS,
+                "flop_per_step": alg["step_flop"]}
+    roof["kernel"] = "up_proj"
+    roof["per_launch"] = (f"{alg['k3_bytes']} B" if decode else f"{alg['k3_flop']} FLOP")
+
+    out = {
+        "metric": METRIC, "value": T * args.steps / (ms_total * 1e-3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8" if inp["quant"] else "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "T": T, "He": d.He, "Hcq": d.Hcq, "Hckv": d.Hckv,
+                   "N": d.N, "D": d.D, "Dr": d.Dr, "block_num": wl.block_num,
+                   "block_size": wl.block_size, "weight_replicas": R,
+                   "query_out": "int8" if inp["quant"] else "bf16"},
+        "roofline": roof,
+        "path_roofline": path,
+        "kernel_us": kernel_us,
+        "ms_per_step_profiled": ms_step_profiled,
+        "wall_s": wall,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,172 @@
+/*
+ * mla_prolog.h -- C ABI of the MI355X (gfx950) Multi-Head Latent Attention
+ * prolog library, libmla_prolog.so.
+ *
+ * The operation is the MLA prolog of the Ascend operator page
+ * aclnnMlaPrologV2WeightNz ("Function", formula block), per token t:
+ *
+ *   c^Q  = RmsNorm(x W^DQ)
+ *   q^C  = c^Q W^UQ,  q^N = q^C W^UK         (per head)      -> queryOut
+ *   q^R  = ROPE(c^Q W^QR)                    (per head)      -> queryRopeOut
+ *   c^KV = RmsNorm(x W^DKV)                  -> kvCache[cacheIndex[t]]
+ *   k^R  = ROPE(x W^KR)                      -> krCache[cacheIndex[t]]
+ *   optional: dequantScaleQNope = RowMax(|q^N|)/127, q^N = round(q^N/scale)
+ *
+ * RmsNorm(v)_i = gamma_i v_i / sqrt(mean(v^2) + eps) ("RmsNorm formula").
+ * ROPE is the rotate-half form (aclnnMlaPreprocess, constraints, rope mode):
+ * for h = Dr/2 and i < h,
+ *   out_i = v_i cos_i - v_{i+h} sin_i,  out_{i+h} = v_{i+h} cos_{i+h} + v_i sin_{i+h},
+ * with cos/sin the caller's per-token table rows.
+ *
+ * Everything is stream-ordered on the caller's HIP stream; no call blocks on
+ * the device.  All tensor arguments are caller-owned device pointers to
+ * contiguous row-major data, 16-byte aligned.  The library never frees them.
+ *
+ * Status codes follow the operator page's return-code table ("Return Value").
+ */
+#ifndef MLA_PROLOG_H
+#define MLA_PROLOG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULLPTR = 161001,       /* a required pointer is NULL */
+  MLA_ERR_PARAM_INVALID = 161002, /* a shape, dtype, alignment or size is outside the domain */
+  MLA_ERR_RUNTIME = 361001,       /* a HIP runtime call failed (allocation, launch) */
+  MLA_ERR_UNSUPPORTED = 561002    /* legal on the page but no kernel tiling for it here */
+} mla_status;
+
+typedef enum { MLA_BF16 = 0, MLA_INT8 = 1 } mla_dtype;
+
+/*
+ * Problem description, fixed at create time (the page's "Shape format field
+ * description"): He hidden size, Hcq q low-rank size, Hckv kv low-rank size,
+ * N heads, D nope head dim, Dr rope dim, Nkv = 1.  Supported here: He, Hcq,
+ * Hckv, D and Dr positive multiples of 8, Dr at most 64, D and Hckv at most
+ * 512, N any positive count; in int8 mode He, Hcq, Hckv+Dr, D and Dr
+ * multiples of 16.
+ *
+ * in_dtype MLA_BF16: the non-quantised scenario, every tensor bf16.
+ * in_dtype MLA_INT8: the int8 full-quantisation scenario with a bf16 cache:
+ *   tokenX, weightDq, weightUqQr, weightDkvKr int8 with fp32 dequantisation
+ *   scales (per token for x, per output channel for the weights); weightUk,
+ *   gammas, sin/cos and both caches bf16.  The RmsNorm output c^Q is
+ *   quantised per token (scale RowMax(|c^Q|)/127) before the int8 W^UqQr
+ *   product.
+ * query_dtype MLA_INT8: queryOut is int8 with one fp32 dequantisation scale
+ *   per (token, head), RowMax(|q^N|)/127 ("Dequant Scale Query Nope
+ *   calculation formula"); MLA_BF16: queryOut is bf16.
+ * max_tokens bounds T of every run; it sizes the handle's workspace.
+ * eps_cq / eps_ckv: the two RmsNorm epsilons (the page recommends 1e-5).
+ */
+typedef struct {
+  int64_t He, Hcq, Hckv, N, D, Dr;
+  int64_t block_num, block_size; /* paged caches [block_num, block_size, 1, .] */
+  int64_t max_tokens;
+  double eps_cq, eps_ckv;
+  int32_t in_dtype;    /* mla_dtype */
+  int32_t query_dtype; /* mla_dtype */
+  int32_t device;      /* HIP device ordinal the handle and all tensors live on */
+} mla_prolog_desc;
+
+/*
+ * Tensors of one run (the page's parameter table), all device pointers:
+ *   token_x          (T, He)            bf16, or int8
+ *   weight_dq        (He, Hcq)          (k, n) row-major, bf16 or int8
+ *   weight_uq_qr     (Hcq, N*(D+Dr))    head-interleaved columns: column
+ *                                       h*(D+Dr)+j is W^UQ column h*D+j for
+ *                                       j < D, W^QR column h*Dr+j-D otherwise
+ *   weight_uk        (N, D, Hckv)       bf16
+ *   weight_dkv_kr    (He, Hckv+Dr)      W^DKV columns first, then W^KR
+ *   gamma_cq (Hcq), gamma_ckv (Hckv)    bf16
+ *   rope_sin, rope_cos (T, Dr)          bf16
+ *   cache_index      (T)                int64 flat slot block*block_size+offset;
+ *                                       entries outside [0, block_num*block_size)
+ *                                       are skipped; duplicates are undefined
+ *   kv_cache (block_num, block_size, 1, Hckv), kr_cache (.., Dr)
+ *                                       bf16, updated in place at the named
+ *                                       slots only; may be NULL iff block_num
+ *                                       is 0 (no cache update)
+ *   scale_x (T), scale_w_dq (Hcq), scale_w_uq_qr (N*(D+Dr)),
+ *   scale_w_dkv_kr (Hckv+Dr)            fp32, int8 mode only, else NULL
+ *   query_out        (T, N, Hckv)       bf16, or int8 when query_dtype is INT8
+ *   query_rope_out   (T, N, Dr)         bf16
+ *   dequant_scale_q_nope (T, N)         fp32 when query_dtype is INT8, else NULL
+ * Outputs must not alias inputs.
+ */
+typedef struct {
+  const void* token_x;
+  const void* weight_dq;
+  const void* weight_uq_qr;
+  const void* weight_uk;
+  const void* weight_dkv_kr;
+  const void* gamma_cq;
+  const void* gamma_ckv;
+  const void* rope_sin;
+  const void* rope_cos;
+  const int64_t* cache_index;
+  void* kv_cache;
+  void* kr_cache;
+  const float* scale_x;
+  const float* scale_w_dq;
+  const float* scale_w_uq_qr;
+  const float* scale_w_dkv_kr;
+  void* query_out;
+  void* query_rope_out;
+  float* dequant_scale_q_nope;
+} mla_prolog_tensors;
+
+typedef struct mla_prolog* mla_prolog_t;
+
+/* Checks a description and, when tensors is not NULL, one run's pointers
+ * (presence, 16-byte alignment) and T (0 <= T <= max_tokens).  Pure host
+ * code: it touches no device and no device memory. */
+mla_status mla_prolog_validate(const mla_prolog_desc* desc, const mla_prolog_tensors* tensors,
+                               int64_t T);
+
+/* Bytes of device workspace a handle for desc owns (0 if desc is invalid). */
+size_t mla_prolog_workspace_bytes(const mla_prolog_desc* desc);
+
+/* Validates desc, allocates the handle and its device workspace on
+ * desc->device (the caller's current device is restored).  On error *out is
+ * set to NULL. */
+mla_status mla_prolog_create(const mla_prolog_desc* desc, mla_prolog_t* out);
+
+/* Enqueues one prolog over T tokens on stream (a hipStream_t; NULL = the
+ * default stream).  Returns after enqueueing; the outputs and caches are
+ * ready when the stream reaches this point.  T = 0 enqueues nothing.  A
+ * handle's workspace is shared by its runs: runs of one handle on different
+ * streams must be ordered by the caller.  The result is deterministic: the
+ * same inputs give bit-identical outputs. */
+mla_status mla_prolog_run(mla_prolog_t handle, const mla_prolog_tensors* tensors, int64_t T,
+                          void* stream);
+
+/* Frees the workspace and the handle (after synchronising its device). */
+mla_status mla_prolog_destroy(mla_prolog_t handle);
+
+/* Kernel timing with HIP events, for benchmarks.  After
+ * mla_prolog_profile_enable(h, 1) every run of h records HIP events on its
+ * stream before its first kernel and after each of its four kernels
+ * (down_proj, norm_rope_cache, up_proj, uk).  mla_prolog_profile_read waits
+ * for the recorded events and returns, per kernel, the elapsed milliseconds
+ * summed over the runs since the previous read (kernel_ms[4]) and the number
+ * of those runs; at most 2048 runs are kept between reads (more is an
+ * MLA_ERR_PARAM_INVALID at read time).  Enabling creates the events;
+ * disabling destroys them. */
+mla_status mla_prolog_profile_enable(mla_prolog_t handle, int enable);
+mla_status mla_prolog_profile_read(mla_prolog_t handle, double* kernel_ms, int64_t* runs);
+
+/* Text of a status code. */
+const char* mla_prolog_status_string(mla_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_PROLOG_H */

@@ -1,0 +1,61 @@
+"""Copies of the generated inputs in device memory (torch tensors), plus the
+output buffers a run writes, keyed by the library's tensor names.  Data
+movement only: nothing here computes any part of the prolog."""
+from __future__ import annotations
+
+from typing import Dict
+
+import numpy as np
+import torch
+
+
+def _tensor(a: np.ndarray, device) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:          # bf16 bit patterns
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a).to(device)
+
+
+def upload(inp: Dict[str, object], device="cuda:0", query_int8=None) -> Dict[str, torch.Tensor]:
+    """Device tensors for every input of ``inp`` and zeroed outputs."""
+    quant = bool(inp["quant"])
+    q8 = quant if query_int8 is None else bool(query_int8)
+    d = inp["dims"]
+    T = int(inp["T"])
+    names = {"token_x": "token_x", "weight_dq": "weight_dq", "weight_uq_qr": "weight_uq_qr",
+             "weight_uk": "weight_uk", "weight_dkv_kr": "weight_dkv_kr",
+             "rmsnorm_gamma_cq": "gamma_cq", "rmsnorm_gamma_ckv": "gamma_ckv",
+             "rope_sin": "rope_sin", "rope_cos": "rope_cos", "cache_index": "cache_index",
+             "kv_cache": "kv_cache", "kr_cache": "kr_cache"}
+    if quant:
+        names.update({"dequant_scale_x": "scale_x", "dequant_scale_w_dq": "scale_w_dq",
+                      "dequant_scale_w_uq_qr": "scale_w_uq_qr",
+                      "dequant_scale_w_dkv_kr": "scale_w_dkv_kr"})
+    out = {lib_name: _tensor(np.asarray(inp[key]), device) for key, lib_name in names.items()
+           if key in inp}
+    out["query_out"] = torch.zeros((T, d.N, d.Hckv), dtype=torch.int8 if q8 else torch.bfloat16,
+                                   device=device)
+    out["query_rope_out"] = torch.zeros((T, d.N, d.Dr), dtype=torch.bfloat16, device=device)
+    if q8:
+        out["dequant_scale_q_nope"] = torch.zeros((T, d.N), dtype=torch.float32, device=device)
+    return out
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """Host copy of a device tensor; bf16 as uint16 bit patterns."""
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def desc_args(inp: Dict[str, object], max_tokens=None, query_int8=None) -> Dict[str, object]:
+    """Keyword arguments of ``make_desc`` for these inputs."""
+    d = inp["dims"]
+    quant = bool(inp["quant"])
+    q8 = quant if query_int8 is None else bool(query_int8)
+    return dict(He=d.He, Hcq=d.Hcq, Hckv=d.Hckv, N=d.N, D=d.D, Dr=d.Dr,
+                block_num=int(inp["block_num"]), block_size=int(inp["block_size"]),
+                max_tokens=int(inp["T"]) if max_tokens is None else int(max_tokens),
+                eps_cq=float(inp["eps_cq"]), eps_ckv=float(inp["eps_ckv"]),
+                in_dtype=int(quant), query_dtype=int(q8))

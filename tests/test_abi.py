@@ -1,0 +1,105 @@
+"""The C ABI on the host: the library loads, exports every symbol the header
+declares, and its pure-host validation returns the page's status classes
+(aclnnMlaPrologV2WeightNz, "Return Value").  No device is touched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import head_latent_attention_amd as mla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "mla_prolog.h")).read()
+    return sorted(set(re.findall(r"^\w[\w\s\*]*?\b(mla_prolog_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    declared = header_functions()
+    assert set(declared) == set(mla.EXPORTS), declared
+    L = mla.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def model_desc(**kw):
+    a = dict(He=7168, Hcq=1536, Hckv=512, N=128, D=128, Dr=64, block_num=1024, block_size=128,
+             max_tokens=256, eps_cq=1e-6, eps_ckv=1e-6)
+    a.update(kw)
+    return mla.make_desc(**a)
+
+
+FAKE = 1 << 40   # an aligned address; validate never dereferences it
+
+
+def fake_tensors(q8=False, in8=False):
+    t = {f: FAKE for f in mla.TENSOR_FIELDS}
+    if not in8:
+        for f in ("scale_x", "scale_w_dq", "scale_w_uq_qr", "scale_w_dkv_kr"):
+            t[f] = None
+    if not q8:
+        t["dequant_scale_q_nope"] = None
+    return t
+
+
+def test_valid_descriptions():
+    assert mla.validate(model_desc()) == mla.MLA_OK
+    assert mla.validate(model_desc(), fake_tensors(), 32) == mla.MLA_OK
+    assert mla.validate(model_desc(in_dtype=1, query_dtype=1), fake_tensors(True, True), 128) == mla.MLA_OK
+    tiny = mla.make_desc(256, 64, 32, 2, 16, 8, 4, 16, 4)
+    assert mla.validate(tiny, fake_tensors(), 4) == mla.MLA_OK
+    assert mla.workspace_bytes(model_desc()) > 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(He=0), mla.MLA_ERR_PARAM_INVALID),
+    (dict(N=-2), mla.MLA_ERR_PARAM_INVALID),
+    (dict(block_size=24), mla.MLA_ERR_PARAM_INVALID),
+    (dict(block_num=-1), mla.MLA_ERR_PARAM_INVALID),
+    (dict(eps_cq=-1.0), mla.MLA_ERR_PARAM_INVALID),
+    (dict(in_dtype=3), mla.MLA_ERR_PARAM_INVALID),
+    (dict(He=7164), mla.MLA_ERR_UNSUPPORTED),
+    (dict(Dr=128), mla.MLA_ERR_UNSUPPORTED),
+    (dict(Hckv=1024), mla.MLA_ERR_UNSUPPORTED),
+    (dict(in_dtype=1, Hcq=1544), mla.MLA_ERR_UNSUPPORTED),
+    (dict(in_dtype=1, Hckv=504), mla.MLA_ERR_UNSUPPORTED),
+    (dict(in_dtype=1, Dr=56), mla.MLA_ERR_UNSUPPORTED),
+])
+def test_bad_descriptions(kw, code):
+    assert mla.validate(model_desc(**kw)) == code
+    assert mla.workspace_bytes(model_desc(**kw)) == 0
+
+
+def test_bad_run_arguments():
+    d = model_desc()
+    assert mla.validate(d, fake_tensors(), 257) == mla.MLA_ERR_PARAM_INVALID   # T > max_tokens
+    assert mla.validate(d, fake_tensors(), -1) == mla.MLA_ERR_PARAM_INVALID
+    t = fake_tensors(); t["weight_uk"] = None
+    assert mla.validate(d, t, 8) == mla.MLA_ERR_NULLPTR
+    t = fake_tensors(); t["kv_cache"] = None
+    assert mla.validate(d, t, 8) == mla.MLA_ERR_NULLPTR
+    t = fake_tensors(); t["token_x"] = FAKE + 2
+    assert mla.validate(d, t, 8) == mla.MLA_ERR_PARAM_INVALID                  # misaligned
+    t = fake_tensors(); t["scale_x"] = FAKE
+    assert mla.validate(d, t, 8) == mla.MLA_ERR_PARAM_INVALID                  # scale in bf16 mode
+    d8 = model_desc(in_dtype=1, query_dtype=1)
+    assert mla.validate(d8, fake_tensors(q8=False, in8=True), 8) == mla.MLA_ERR_NULLPTR
+    assert mla.validate(d8, fake_tensors(q8=True, in8=False), 8) == mla.MLA_ERR_NULLPTR
+
+
+def test_empty_run_needs_no_tensors():
+    # T = 0: empty tensors are allowed, nothing is checked or launched
+    assert mla.validate(model_desc(), {}, 0) == mla.MLA_OK
+
+
+def test_no_cache_blocks_needs_no_caches():
+    t = fake_tensors(); t["kv_cache"] = None; t["kr_cache"] = None
+    assert mla.validate(model_desc(block_num=0), t, 8) == mla.MLA_OK
+
+
+def test_status_strings():
+    for code in (0, 161001, 161002, 361001, 561002):
+        assert mla.status_string(code) != "unknown status"

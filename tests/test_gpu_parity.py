@@ -1,0 +1,162 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on
+the same seeded inputs, at the tolerances of tests/parity.py.
+
+Small shapes are compared element by element over every token; the full
+model-size workloads are compared on sampled tokens (all of their queries and
+cache rows), plus a bitwise scan of every untouched cache slot.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth import device as dev
+from synth.generate import Dims, custom_workload
+from parity import check_caches, check_queries
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import head_latent_attention_amd as mla  # noqa: E402
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(inp, query_int8=None, max_tokens=None, T=None, repeat=1):
+    """Upload, run through the C ABI, download.  Returns host arrays."""
+    T = int(inp["T"]) if T is None else T
+    t = dev.upload(inp, query_int8=query_int8)
+    desc = mla.make_desc(**dev.desc_args(inp, max_tokens=max_tokens, query_int8=query_int8))
+    with mla.MlaProlog(desc) as h:
+        for _ in range(repeat):
+            h.run(t, T)
+        torch.cuda.synchronize()
+    return {k: dev.bits(v) for k, v in t.items()
+            if k in ("query_out", "query_rope_out", "dequant_scale_q_nope", "kv_cache", "kr_cache")}
+
+
+def full_check(inp, query_int8=None, rows=None):
+    q8 = bool(inp["quant"]) if query_int8 is None else bool(query_int8)
+    rows = np.arange(int(inp["T"])) if rows is None else np.asarray(rows)
+    say(f"case {inp['workload']} T={inp['T']} dims={inp['dims']} q8={q8} rows={len(rows)}")
+    got = run_gpu(inp, query_int8=query_int8)
+    ref = oracle.run(inp, tokens=rows, query_int8=query_int8, caches=False)
+    check_queries(got, ref, rows, q8)
+    check_caches(inp, got["kv_cache"], got["kr_cache"], ref, rows)
+    return got
+
+
+SMALL = {
+    "tiny_t4": synth.workload("tiny_t4"),
+    "ragged_t37": custom_workload("ragged_t37", T=37, dims=Dims(He=264, Hcq=72, Hckv=40, N=3, D=24, Dr=16),
+                                  block_num=4, block_size=16, seed=31),
+    "ragged_t5_wide": custom_workload("ragged_t5_wide", T=5, dims=Dims(He=520, Hcq=200, Hckv=136, N=5, D=136, Dr=64),
+                                      block_num=2, block_size=32, seed=32),
+    "mid_t70": custom_workload("mid_t70", T=70, dims=Dims(He=1024, Hcq=256, Hckv=512, N=4, D=128, Dr=64),
+                               block_num=8, block_size=16, seed=33),
+    "t300_split1": custom_workload("t300", T=600, dims=Dims(He=512, Hcq=128, Hckv=64, N=2, D=32, Dr=16),
+                                   block_num=40, block_size=16, seed=34),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_bf16(name):
+    full_check(synth.make_inputs(SMALL[name]))
+
+
+@pytest.mark.parametrize("name", ["tiny_t4", "ragged_t37", "mid_t70"])
+def test_small_bf16_int8_query(name):
+    full_check(synth.make_inputs(SMALL[name]), query_int8=True)
+
+
+INT8_SMALL = {
+    "q8_t9": custom_workload("q8_t9", T=9, dims=Dims(He=256, Hcq=64, Hckv=32, N=2, D=16, Dr=16),
+                             block_num=2, block_size=16, quant=True, seed=41),
+    "q8_t130": custom_workload("q8_t130", T=130, dims=Dims(He=1024, Hcq=192, Hckv=512, N=3, D=128, Dr=64),
+                               block_num=16, block_size=16, quant=True, seed=42),
+}
+
+
+@pytest.mark.parametrize("name", list(INT8_SMALL))
+def test_small_int8(name):
+    full_check(synth.make_inputs(INT8_SMALL[name]))
+
+
+def test_int8_inputs_bf16_query():
+    full_check(synth.make_inputs(INT8_SMALL["q8_t130"]), query_int8=False)
+
+
+def test_deterministic():
+    inp = synth.make_inputs(SMALL["mid_t70"])
+    say("case determinism mid_t70")
+    a = run_gpu(inp)
+    b = run_gpu(inp, repeat=2)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_zero_tokens_is_a_no_op():
+    inp = synth.make_inputs(SMALL["tiny_t4"])
+    say("case T=0")
+    got = run_gpu(inp, T=0)
+    assert np.all(got["kv_cache"] == synth.SENTINEL_BF16)
+    assert not np.asarray(got["query_out"]).any()
+
+
+def test_no_cache_blocks_still_computes_queries():
+    wl = custom_workload("nocache", T=6, dims=Dims(He=256, Hcq=64, Hckv=32, N=2, D=16, Dr=8),
+                         block_num=1, block_size=16, seed=51)
+    inp = synth.make_inputs(wl)
+    say("case block_num=0")
+    t = dev.upload(inp)
+    t.pop("kv_cache"), t.pop("kr_cache")
+    args = dev.desc_args(inp)
+    args["block_num"] = 0
+    with mla.MlaProlog(mla.make_desc(**args)) as h:
+        h.run(t, 6)
+        torch.cuda.synchronize()
+    ref = oracle.run(inp, caches=False)
+    got = {k: dev.bits(v) for k, v in t.items()}
+    check_queries(got, ref, np.arange(6), False)
+
+
+def test_out_of_range_slots_are_skipped():
+    inp = synth.make_inputs(SMALL["ragged_t37"])
+    n = inp["block_num"] * inp["block_size"]
+    idx = np.array(inp["cache_index"])
+    idx[:3] = [-5, n, n + 1000]
+    inp["cache_index"] = idx
+    full_check(inp)
+
+
+def test_smaller_run_than_max_tokens():
+    inp = synth.make_inputs(SMALL["mid_t70"])
+    say("case T=19 of max 70")
+    small = synth.make_inputs(SMALL["mid_t70"], T=19)
+    got = run_gpu(small, max_tokens=70)
+    ref = oracle.run(small, caches=False)
+    check_queries(got, ref, np.arange(19), False)
+    check_caches(small, got["kv_cache"], got["kr_cache"], ref, np.arange(19))
+
+
+# ---- the model-size workloads, sampled ---------------------------------------
+FULL = ["decode_t32", "decode_t256", "int8_decode_t128", "prefill_t8192"]
+
+
+def sample_rows(T, k=12, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set([0, T - 1]) | set(rng.choice(T, size=min(k, T), replace=False).tolist())
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    inp = synth.make_inputs(synth.workload(name))
+    T = int(inp["T"])
+    rows = np.arange(T) if T <= 32 else sample_rows(T)
+    full_check(inp, rows=rows)
