@@ -526,15 +526,18 @@ mla_status check_desc(const mla_prolog_desc* d) {
   const int64_t dims[6] = {d->He, d->Hcq, d->Hckv, d->N, d->D, d->Dr};
   for (int64_t v : dims)
     if (v <= 0 || v > (1 << 20)) return MLA_ERR_PARAM_INVALID;
+  // the page's dtype table has an int8 queryOut only in the int8
+  // full-quantisation scenario
+  if ((d->in_dtype != MLA_BF16 && d->in_dtype != MLA_INT8) ||
+      (d->query_dtype != MLA_BF16 && d->query_dtype != MLA_INT8))
+    return MLA_ERR_PARAM_INVALID;
+  if (d->query_dtype == MLA_INT8 && d->in_dtype != MLA_INT8) return MLA_ERR_PARAM_INVALID;
   if (d->block_num < 0 || d->max_tokens < 0 || d->max_tokens > (1 << 20))
     return MLA_ERR_PARAM_INVALID;
   if (d->block_num > 0 && (d->block_size < 16 || d->block_size > 1024 || d->block_size % 16))
     return MLA_ERR_PARAM_INVALID;
   if (!(d->eps_cq >= 0.0) || !(d->eps_ckv >= 0.0) || !std::isfinite(d->eps_cq) ||
       !std::isfinite(d->eps_ckv))
-    return MLA_ERR_PARAM_INVALID;
-  if ((d->in_dtype != MLA_BF16 && d->in_dtype != MLA_INT8) ||
-      (d->query_dtype != MLA_BF16 && d->query_dtype != MLA_INT8))
     return MLA_ERR_PARAM_INVALID;
   const int64_t vec_dims[5] = {d->He, d->Hcq, d->Hckv, d->D, d->Dr};
   for (int64_t v : vec_dims)

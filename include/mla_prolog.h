@@ -61,7 +61,9 @@ typedef enum { MLA_BF16 = 0, MLA_INT8 = 1 } mla_dtype;
  *   product.
  * query_dtype MLA_INT8: queryOut is int8 with one fp32 dequantisation scale
  *   per (token, head), RowMax(|q^N|)/127 ("Dequant Scale Query Nope
- *   calculation formula"); MLA_BF16: queryOut is bf16.
+ *   calculation formula"); MLA_BF16: queryOut is bf16.  As in the page's
+ *   dtype table, an int8 queryOut needs in_dtype MLA_INT8 (otherwise
+ *   MLA_ERR_PARAM_INVALID); int8 inputs with a bf16 queryOut are allowed.
  * max_tokens bounds T of every run; it sizes the handle's workspace.
  * eps_cq / eps_ckv: the two RmsNorm epsilons (the page recommends 1e-5).
  */

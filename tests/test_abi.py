@@ -61,6 +61,7 @@ def test_valid_descriptions():
     (dict(block_num=-1), mla.MLA_ERR_PARAM_INVALID),
     (dict(eps_cq=-1.0), mla.MLA_ERR_PARAM_INVALID),
     (dict(in_dtype=3), mla.MLA_ERR_PARAM_INVALID),
+    (dict(query_dtype=1), mla.MLA_ERR_PARAM_INVALID),   # int8 q^N needs int8 inputs
     (dict(He=7164), mla.MLA_ERR_UNSUPPORTED),
     (dict(Dr=128), mla.MLA_ERR_UNSUPPORTED),
     (dict(Hckv=1024), mla.MLA_ERR_UNSUPPORTED),

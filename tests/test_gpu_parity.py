@@ -69,11 +69,6 @@ def test_small_bf16(name):
     full_check(synth.make_inputs(SMALL[name]))
 
 
-@pytest.mark.parametrize("name", ["tiny_t4", "ragged_t37", "mid_t70"])
-def test_small_bf16_int8_query(name):
-    full_check(synth.make_inputs(SMALL[name]), query_int8=True)
-
-
 INT8_SMALL = {
     "q8_t9": custom_workload("q8_t9", T=9, dims=Dims(He=256, Hcq=64, Hckv=32, N=2, D=16, Dr=16),
                              block_num=2, block_size=16, quant=True, seed=41),
