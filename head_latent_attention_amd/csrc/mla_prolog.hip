@@ -239,6 +239,11 @@ struct Ptrs {
   uint8_t* cq;       // [T][Hcq] bf16 (int8 in int8 mode)
   float* cq_scale;   // [T]
   uint16_t* qc;      // [T][N][D] bf16
+  // streaming (small-T) path
+  float* y;          // [T][Hcq+Hckv+Dr] fp32: x [W^DQ | W^DkvKr], split-K reduced
+  float* ssq;        // [column tile][T]: sum of squares of the tile's q or kv columns
+  float* amax;       // [q column tile][T]: max |gamma_cq * y| over the tile's columns
+  unsigned* ticket;  // [column tile]: split-K arrival counters, zero between runs
 };
 
 // K1 ------------------------------------------------------------------------
@@ -454,9 +459,610 @@ __global__ __launch_bounds__(kThreads) void k_uk(Dims d, Ptrs p) {
 }
 
 // ---------------------------------------------------------------------------
+// Streaming path for small token counts (T <= 32): weight-bandwidth bound.
+//
+// Every wave streams its own k-stages of a 64-column weight window: a stage
+// is one MFMA k-step (32 bf16 rows or 64 int8 rows, 4 KB), loaded with
+// 16-byte coalesced loads into a register ring D stages deep (the activation
+// fragments of the same stage travel in the same ring, so the in-order
+// vector-memory counter never makes a stage wait for a later one), written
+// to the wave's own 4 KB LDS buffer with an XOR swizzle, and read back as
+// MFMA B fragments with the gfx950 transpose reads (ds_read_b64_tr_b16 /
+// ds_read_b64_tr_b8), two per fragment.  No block barrier is needed while
+// streaming; the waves of a block cover interleaved stages of one k range
+// and are summed through LDS in a fixed order at the end.
+//
+// Transpose-read lane layout (gfx950): within each 16-lane group, lane l
+// receives element l%4 (b16) or l%8 (b8) of the 8 bytes addressed by source
+// lanes l/4 + 4j (b16, j < 4) or l/8 + 2j (b8, j < 8).  With source lane s
+// of group g addressing row 8g + s/4 (b16) or 16g + s/2 (b8) and column
+// 16*ct + 4*(s%4) (b16) or 16*ct + 8*(s%2) (b8), lane l gets column 16*ct + l
+// for consecutive rows: exactly the k-run an MFMA B operand holds.
+// ---------------------------------------------------------------------------
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ s16x4 lds_tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+}
+__device__ __forceinline__ i32x2 lds_tr8(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (__attribute__((address_space(3))) i32x2*)(p));
+}
+
+template <bool I8>
+struct Stage {
+  static constexpr int EB = I8 ? 1 : 2;
+  static constexpr int KS = I8 ? 64 : 32;    // k rows per stage (one MFMA k-step)
+  static constexpr int KL = 16 / EB;         // k per lane per MFMA
+  static constexpr int RB = 64 * EB;         // bytes per stage row (64 columns)
+  static constexpr int CPR = RB / 16;        // 16-byte chunks per row
+  static constexpr int BYTES = KS * RB;      // 4096
+  using Acc = typename std::conditional<I8, i32x4, f32x4>::type;
+  using Frag = typename std::conditional<I8, i32x4, bf16x8>::type;
+  // 16-byte chunk index XOR of row r: makes the transpose reads of the four
+  // lane groups (and both halves of a wave) hit distinct banks
+  __device__ static __forceinline__ int swz(int r) {
+    if constexpr (I8) return ((r >> 1) & 3) ^ ((r >> 4) & 1);
+    else return 2 * ((r & 3) ^ ((r >> 3) & 1));
+  }
+  __device__ static __forceinline__ int off(int r, int chunk) { return r * RB + 16 * (chunk ^ swz(r)); }
+  // B fragment of column tile ct from a stage buffer
+  __device__ static __forceinline__ Frag frag(const uint8_t* buf, int lane, int ct) {
+    const int g = lane >> 4, s = lane & 15;
+    if constexpr (I8) {
+      const int r1 = 16 * g + (s >> 1), r2 = r1 + 8, o = 8 * (s & 1);
+      const i32x2 v1 = lds_tr8(buf + off(r1, ct) + o);
+      const i32x2 v2 = lds_tr8(buf + off(r2, ct) + o);
+      i32x4 f = {v1[0], v1[1], v2[0], v2[1]};
+      return f;
+    } else {
+      const int r1 = 8 * g + (s >> 2), r2 = r1 + 4, ch = 2 * ct + ((s & 3) >> 1), o = 8 * (s & 1);
+      const s16x4 v1 = lds_tr16(buf + off(r1, ch) + o);
+      const s16x4 v2 = lds_tr16(buf + off(r2, ch) + o);
+      union { s16x4 h[2]; bf16x8 v; } u;
+      u.h[0] = v1; u.h[1] = v2;
+      return u.v;
+    }
+  }
+};
+
+// Buffer loads: an offset at or past num_records returns zeros without a
+// memory request, so predicated loads need no branch.  Every buffer here is
+// addressed with 32-bit offsets below 2 GiB.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOOB = 0x80000000u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = static_cast<int>(bytes < int64_t(kOOB) ? bytes : int64_t(kOOB) - 1);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t off) {
+  const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return __builtin_bit_cast(uint4, v);
+}
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ i32x4 mfma(i32x4 a, i32x4 b, i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// Activation operands.  A policy loads the raw 16-byte registers of the MT
+// fragments of one stage (load) and turns them into MFMA A fragments (frag).
+
+// Fragments read as stored (bf16 or int8, k-contiguous rows); rows are
+// relative to the buffer base (the block's first row).
+template <bool I8, int MT>
+struct APlain {
+  static constexpr int NR = MT;  // 16-byte registers per stage
+  rsrc_t A;
+  uint32_t lda;  // bytes per row
+  int M;         // valid rows from the base
+  __device__ __forceinline__ void load(uint4 (&r)[NR], int m0, int ka, int ke) const {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = m0 + 16 * mt;
+      const bool ok = m < M && ka < ke;
+      r[mt] = bload16(A, ok ? uint32_t(m) * lda + uint32_t(ka) * Stage<I8>::EB : kOOB);
+    }
+  }
+  __device__ __forceinline__ typename Stage<I8>::Frag frag(const uint4 (&r)[NR], int mt, int) const {
+    union { uint4 u; typename Stage<I8>::Frag f; } c;
+    c.u = r[mt];
+    return c.f;
+  }
+};
+
+// c^Q fragments computed from the reduced down-projection y (fp32):
+// c = (gamma * y) * inv_rms, then bf16 (nearest even), or the per-token
+// int8 code nearest to c / s_cq.  gamma is loaded once per stage.
+template <bool I8, int MT>
+struct ACq {
+  static constexpr int NY = I8 ? 4 : 2;   // 16-byte y registers per fragment
+  static constexpr int NG = I8 ? 2 : 1;   // 16-byte gamma registers per stage
+  static constexpr int NR = MT * NY + NG;
+  rsrc_t y;        // [M][ldy] fp32
+  uint32_t ldy;    // bytes per y row
+  rsrc_t gamma;    // [Hcq] bf16
+  int M;
+  const float* inv;    // LDS, per row of the block
+  const float* scale;  // LDS, per row (int8)
+  __device__ __forceinline__ void load(uint4 (&r)[NR], int m0, int ka, int ke) const {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = m0 + 16 * mt;
+      const bool ok = m < M && ka < ke;
+#pragma unroll
+      for (int i = 0; i < NY; ++i)
+        r[mt * NY + i] = bload16(y, ok ? uint32_t(m) * ldy + uint32_t(ka + 4 * i) * 4 : kOOB);
+    }
+#pragma unroll
+    for (int i = 0; i < NG; ++i)
+      r[MT * NY + i] = bload16(gamma, ka < ke ? uint32_t(ka + 8 * i) * 2 : kOOB);
+  }
+  __device__ __forceinline__ typename Stage<I8>::Frag frag(const uint4 (&r)[NR], int mt, int ml) const {
+    constexpr int NV = I8 ? 16 : 8;
+    const float* yv = reinterpret_cast<const float*>(&r[mt * NY]);
+    const uint16_t* gv = reinterpret_cast<const uint16_t*>(&r[MT * NY]);
+    const float iv = inv[ml];
+    if constexpr (I8) {
+      const float sc = scale[ml];
+      union { int8_t b[16]; i32x4 v; } u;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const float c = (bf2f(gv[i]) * yv[i]) * iv;
+        u.b[i] = sc > 0.0f ? quant_code(c, sc) : 0;
+      }
+      return u.v;
+    } else {
+      union { uint16_t h[8]; bf16x8 v; } u;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) u.h[i] = f2bf((bf2f(gv[i]) * yv[i]) * iv);
+      return u.v;
+    }
+  }
+};
+
+// One wave streams stages j = 0..ns-1 (rows kfirst + j*kstep .. +KS, clipped
+// to ke) of the 64-column weight window starting at byte n0b of each row of
+// the weight buffer Bw (row stride ldb bytes, wbytes valid bytes per row)
+// against MT activation fragments of rows m0 + 16*mt + lane%16.  The ring
+// loop is straight-line: stages past the end load zeros (no memory traffic)
+// and add nothing.
+template <bool I8, int MT, int D, class AP>
+__device__ __forceinline__ void stream_wave(const AP& ap, int m0, rsrc_t Bw, uint32_t ldb,
+                                            uint32_t n0b, int wbytes, int kfirst, int kstep,
+                                            int ns, int ke, typename Stage<I8>::Acc (&acc)[MT][4],
+                                            uint8_t* buf) {
+  using S = Stage<I8>;
+  const int lane = threadIdx.x & 63;
+  const int ml = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) acc[mt][ct] = typename S::Acc{0, 0, 0, 0};
+
+  uint4 bq[D][4];
+  uint4 aq[D][AP::NR];
+  auto issue = [&](uint4 (&b)[4], uint4 (&a)[AP::NR], int j) {
+    const int k0 = kfirst + j * kstep;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = lane + 64 * i, r = q / S::CPR, c = q % S::CPR;
+      const bool ok = j < ns && k0 + r < ke && 16 * c < wbytes;
+      b[i] = bload16(Bw, ok ? uint32_t(k0 + r) * ldb + n0b + 16 * c : kOOB);
+    }
+    ap.load(a, m0 + ml, j < ns ? k0 + S::KL * g : ke, ke);
+  };
+#pragma unroll
+  for (int p = 0; p < D; ++p) issue(bq[p], aq[p], p);
+
+  const int nsr = (ns + D - 1) / D * D;
+  for (int j0 = 0; j0 < nsr; j0 += D) {
+#pragma unroll
+    for (int p = 0; p < D; ++p) {
+      const int j = j0 + p;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = lane + 64 * i, r = q / S::CPR, c = q % S::CPR;
+        *reinterpret_cast<uint4*>(buf + S::off(r, c)) = bq[p][i];
+      }
+      typename S::Frag af[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) af[mt] = ap.frag(aq[p], mt, 16 * mt + ml);
+      issue(bq[p], aq[p], j + D);
+      typename S::Frag bf[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) bf[ct] = S::frag(buf, lane, ct);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) acc[mt][ct] = mfma(af[mt], bf[ct], acc[mt][ct]);
+    }
+  }
+}
+
+// Sum of the NW waves' accumulators into wave 0, in a fixed pairing order.
+// red: (NW/2) * MT * 16 * 64 words of LDS.  Ends with a block barrier.
+template <int NW, int MT, class Acc>
+__device__ __forceinline__ void reduce_waves(Acc (&acc)[MT][4], uint32_t* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int half = NW / 2; half >= 1; half /= 2) {
+    __syncthreads();
+    if (w >= half && w < 2 * half) {
+      uint32_t* r = red + (w - half) * (MT * 16 * 64);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            // copy the vector element to a scalar first: bit-casting the
+            // element expression itself reads element 0
+            const auto e = acc[mt][ct][i];
+            r[((mt * 4 + ct) * 4 + i) * 64 + lane] = __builtin_bit_cast(uint32_t, e);
+          }
+    }
+    __syncthreads();
+    if (w < half) {
+      const uint32_t* r = red + w * (MT * 16 * 64);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            using E = decltype(acc[mt][ct][i] + 0);
+            const E add = __builtin_bit_cast(E, r[((mt * 4 + ct) * 4 + i) * 64 + lane]);
+            acc[mt][ct][i] += add;
+          }
+    }
+  }
+  __syncthreads();
+}
+
+template <bool I8, int MT, int NW>
+struct StreamLds {
+  static constexpr int STAGE = NW * Stage<I8>::BYTES;
+  static constexpr int RED = (NW / 2) * MT * 16 * 64 * 4;
+  static constexpr int BYTES = STAGE > RED ? STAGE : RED;
+};
+
+// K1s: grid (column tiles x splits).  The block streams its k range of one
+// 64-column window of [W^DQ | W^DkvKr] and writes a partial tile; the last
+// block of a column tile to arrive sums the S partials in split order into y
+// and writes the tile's per-token statistics.
+template <bool I8, int MT, int NW, int D>
+__global__ __launch_bounds__(64 * NW) void k1_stream(Dims d, Ptrs p, int tiles_q, int tiles, int S,
+                                                     int kps) {
+  using St = Stage<I8>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[StreamLds<I8, MT, NW>::BYTES];
+  __shared__ int last;
+  const int jt = blockIdx.x % tiles, split = blockIdx.x / tiles;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int Nkr = d.Hckv + d.Dr, Ntot = d.Hcq + Nkr;
+  const uint8_t* B;
+  int64_t ldb;
+  int n0, width, outc;
+  if (jt < tiles_q) {
+    n0 = 64 * jt; width = min(64, d.Hcq - n0); B = p.w_dq; ldb = int64_t(d.Hcq) * St::EB; outc = n0;
+  } else {
+    n0 = 64 * (jt - tiles_q); width = min(64, Nkr - n0); B = p.w_dkv_kr;
+    ldb = int64_t(Nkr) * St::EB; outc = d.Hcq + n0;
+  }
+  const int kb = split * kps, ke = min(d.He, kb + kps);
+  const int nst = (ke - kb + St::KS - 1) / St::KS;
+  const int ns = w < nst ? (nst - w + NW - 1) / NW : 0;
+  typename St::Acc acc[MT][4];
+  const APlain<I8, MT> ap{make_rsrc(p.x, int64_t(d.T) * d.He * St::EB), uint32_t(d.He * St::EB), d.T};
+  const rsrc_t Bw = make_rsrc(B, int64_t(d.He) * ldb);
+  stream_wave<I8, MT, D>(ap, 0, Bw, uint32_t(ldb), uint32_t(n0 * St::EB), width * St::EB,
+                         kb + w * St::KS, NW * St::KS, ns, ke, acc, lds + w * St::BYTES);
+  reduce_waves<NW, MT>(acc, reinterpret_cast<uint32_t*>(lds));
+
+  // partial tile, written by wave 0
+  if (w == 0) {
+    const int g = lane >> 4, c = lane & 15;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int col = 16 * ct + c;
+        if (col >= width) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = 16 * mt + 4 * g + i;
+          if (m >= d.T) continue;
+          const int64_t o = (int64_t(split) * d.T + m) * Ntot + outc + col;
+          if constexpr (I8) static_cast<int32_t*>(p.part)[o] = acc[mt][ct][i];
+          else static_cast<float*>(p.part)[o] = acc[mt][ct][i];
+        }
+      }
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) last = atomicAdd(&p.ticket[jt], 1u) == unsigned(S - 1);
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+
+  // the last arrival: y = sum of the partials (split order), and statistics.
+  // 16 threads per row, 4 columns each, 4*NW rows per pass; the partials of
+  // 8 splits are loaded before they are added (splits past S read as zeros).
+  const rsrc_t P = make_rsrc(p.part, int64_t(S) * d.T * Ntot * 4);
+  const int cq = 4 * (tid & 15);
+  const bool col_ok = cq < width;
+  for (int m = tid >> 4; m < 16 * MT; m += 4 * NW) {
+    const bool row_ok = m < d.T;
+    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    int32_t iv[4] = {0, 0, 0, 0};
+    for (int s0 = 0; s0 < S; s0 += 8) {
+      uint4 r[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sp = s0 + e;
+        const bool ok = row_ok && col_ok && sp < S;
+        r[e] = bload16(P, ok ? uint32_t(((int64_t(sp) * d.T + m) * Ntot + outc + cq) * 4) : kOOB);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if constexpr (I8) {
+          const int4 q = __builtin_bit_cast(int4, r[e]);
+          iv[0] += q.x; iv[1] += q.y; iv[2] += q.z; iv[3] += q.w;
+        } else {
+          const float4 q = __builtin_bit_cast(float4, r[e]);
+          v[0] += q.x; v[1] += q.y; v[2] += q.z; v[3] += q.w;
+        }
+      }
+    }
+    float ss = 0.0f, am = 0.0f;
+    if (row_ok && col_ok) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int gc = outc + cq + e;   // column of y
+        if constexpr (I8) {
+          const float sw = gc < d.Hcq ? p.sw_dq[gc] : p.sw_dkv_kr[gc - d.Hcq];
+          v[e] = static_cast<float>(iv[e]) * p.sx[m] * sw;
+        }
+        if (gc < d.Hcq + d.Hckv) ss += v[e] * v[e];
+        if (gc < d.Hcq) am = fmaxf(am, fabsf(bf2f(p.gamma_cq[gc]) * v[e]));
+      }
+      *reinterpret_cast<float4*>(p.y + int64_t(m) * Ntot + outc + cq) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+    for (int o = 1; o < 16; o <<= 1) {
+      ss += __shfl_xor(ss, o, 64);
+      am = fmaxf(am, __shfl_xor(am, o, 64));
+    }
+    if ((tid & 15) == 0 && row_ok) {
+      p.ssq[int64_t(jt) * d.T + m] = ss;
+      if (jt < tiles_q) p.amax[int64_t(jt) * d.T + m] = am;
+    }
+  }
+  if (tid == 0) p.ticket[jt] = 0u;
+}
+
+// Per-token RmsNorm factors of the query rows: inv = 1/sqrt(sum ssq / Hcq + eps)
+// (tiles summed in order), and in int8 mode the c^Q scale max|c| / 127.
+template <bool I8>
+__device__ __forceinline__ void cq_factors(const Dims& d, const Ptrs& p, int tiles_q, int m,
+                                           float& inv, float& scale) {
+  float ss = 0.0f, am = 0.0f;
+  for (int jt = 0; jt < tiles_q; ++jt) {
+    ss += p.ssq[int64_t(jt) * d.T + m];
+    if constexpr (I8) am = fmaxf(am, p.amax[int64_t(jt) * d.T + m]);
+  }
+  inv = 1.0f / sqrtf(ss / float(d.Hcq) + d.eps_cq);
+  scale = I8 ? (am * inv) / 127.0f : 0.0f;
+}
+
+// K3s: grid (head tiles + kv blocks).  Head tiles: per head the nope columns
+// in windows of 64, then the Dr rope columns; the block's waves split the
+// whole Hcq reduction.  kv blocks: RmsNorm of c^KV and RoPE of k^R for
+// kv_tpb tokens each, written at their cacheIndex slots.
+template <bool I8, int MT, int NW, int D>
+__global__ __launch_bounds__(64 * NW) void k3_stream(Dims d, Ptrs p, int nope_tiles, int tiles_q,
+                                                     int tiles_kr, int head_blocks, int kv_tpb) {
+  using St = Stage<I8>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[StreamLds<I8, MT, NW>::BYTES];
+  __shared__ float inv_s[16 * MT], scale_s[16 * MT];
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int Nkr = d.Hckv + d.Dr, Ntot = d.Hcq + Nkr;
+
+  if (int(blockIdx.x) >= head_blocks) {
+    // c^KV and k^R for tokens [t0, t0 + kv_tpb)
+    const int t0 = (blockIdx.x - head_blocks) * kv_tpb;
+    for (int t = t0; t < min(d.T, t0 + kv_tpb); ++t) {
+      const int64_t slot = p.cache_index[t];
+      if (slot < 0 || slot >= d.slots) continue;
+      float ss = 0.0f;
+      for (int jt = tiles_q; jt < tiles_q + tiles_kr; ++jt) ss += p.ssq[int64_t(jt) * d.T + t];
+      const float inv = 1.0f / sqrtf(ss / float(d.Hckv) + d.eps_ckv);
+      const float* yk = p.y + int64_t(t) * Ntot + d.Hcq;
+      uint16_t* kv = p.kv_cache + slot * d.Hckv;
+      for (int n = tid; n < d.Hckv; n += 64 * NW) kv[n] = f2bf((bf2f(p.gamma_ckv[n]) * yk[n]) * inv);
+      const int h = d.Dr / 2;
+      const float* yr = yk + d.Hckv;
+      const uint16_t* cs = p.cos + int64_t(t) * d.Dr;
+      const uint16_t* sn = p.sin + int64_t(t) * d.Dr;
+      uint16_t* kr = p.kr_cache + slot * d.Dr;
+      for (int i = tid; i < h; i += 64 * NW) {
+        const float a = yr[i], b = yr[i + h];
+        kr[i] = f2bf(a * bf2f(cs[i]) - b * bf2f(sn[i]));
+        kr[i + h] = f2bf(b * bf2f(cs[i + h]) + a * bf2f(sn[i + h]));
+      }
+    }
+    return;
+  }
+
+  const int hp = nope_tiles + 1;
+  const int h = blockIdx.x / hp, part = blockIdx.x % hp;
+  const bool rope = part == nope_tiles;
+  const int W = d.N * (d.D + d.Dr);
+  const int col0 = h * (d.D + d.Dr) + (rope ? d.D : 64 * part);
+  const int width = rope ? d.Dr : min(64, d.D - 64 * part);
+  for (int m = tid; m < 16 * MT; m += 64 * NW) {
+    float iv = 0.0f, sc = 0.0f;
+    if (m < d.T) cq_factors<I8>(d, p, tiles_q, m, iv, sc);
+    inv_s[m] = iv;
+    scale_s[m] = sc;
+  }
+  __syncthreads();
+  const int nst = (d.Hcq + St::KS - 1) / St::KS;
+  const int ns = w < nst ? (nst - w + NW - 1) / NW : 0;
+  typename St::Acc acc[MT][4];
+  const ACq<I8, MT> ap{make_rsrc(p.y, int64_t(d.T) * Ntot * 4), uint32_t(Ntot * 4),
+                       make_rsrc(p.gamma_cq, int64_t(d.Hcq) * 2), d.T, inv_s, scale_s};
+  const rsrc_t Bw = make_rsrc(p.w_uq_qr, int64_t(d.Hcq) * W * St::EB);
+  stream_wave<I8, MT, D>(ap, 0, Bw, uint32_t(W * St::EB), uint32_t(col0 * St::EB), width * St::EB,
+                         w * St::KS, NW * St::KS, ns, d.Hcq, acc, lds + w * St::BYTES);
+  reduce_waves<NW, MT>(acc, reinterpret_cast<uint32_t*>(lds));
+
+  // epilogue: the reduced tile goes to LDS (fp32), then out
+  float* E = reinterpret_cast<float*>(lds);   // [16*MT][65]
+  if (w == 0) {
+    const int g = lane >> 4, c = lane & 15;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ml = 16 * mt + 4 * g + i, col = 16 * ct + c;
+          float v;
+          if constexpr (I8)
+            v = (ml < d.T && col < width)
+                    ? static_cast<float>(acc[mt][ct][i]) * scale_s[ml] * p.sw_uq_qr[col0 + col]
+                    : 0.0f;
+          else
+            v = acc[mt][ct][i];
+          E[ml * 65 + col] = v;
+        }
+  }
+  __syncthreads();
+  const int BM = 16 * MT;
+  if (!rope) {
+    for (int idx = tid; idx < BM * width; idx += 64 * NW) {
+      const int ml = idx / width, cc = idx % width;
+      if (ml < d.T) p.qc[(int64_t(ml) * d.N + h) * d.D + 64 * part + cc] = f2bf(E[ml * 65 + cc]);
+    }
+  } else {
+    const int hf = d.Dr / 2;
+    for (int idx = tid; idx < BM * hf; idx += 64 * NW) {
+      const int ml = idx / hf, i = idx % hf;
+      if (ml >= d.T) continue;
+      const float a = E[ml * 65 + i], b = E[ml * 65 + i + hf];
+      const uint16_t* cs = p.cos + int64_t(ml) * d.Dr;
+      const uint16_t* sn = p.sin + int64_t(ml) * d.Dr;
+      uint16_t* o = p.qr_out + (int64_t(ml) * d.N + h) * d.Dr;
+      o[i] = f2bf(a * bf2f(cs[i]) - b * bf2f(sn[i]));
+      o[i + hf] = f2bf(b * bf2f(cs[i + hf]) + a * bf2f(sn[i + hf]));
+    }
+  }
+}
+
+// K4s, bf16 query: grid (head x 64-column window of Hckv); the block's waves
+// split the D reduction.
+template <int MT, int NW, int D>
+__global__ __launch_bounds__(64 * NW) void k4_stream(Dims d, Ptrs p, int windows) {
+  using St = Stage<false>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[StreamLds<false, MT, NW>::BYTES];
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = blockIdx.x / windows, win = blockIdx.x % windows;
+  const int c0 = 64 * win, width = min(64, d.Hckv - c0);
+  const int nst = (d.D + St::KS - 1) / St::KS;
+  const int ns = w < nst ? (nst - w + NW - 1) / NW : 0;
+  typename St::Acc acc[MT][4];
+  const APlain<false, MT> ap{make_rsrc(p.qc + int64_t(h) * d.D, (int64_t(d.T) * d.N - h) * d.D * 2),
+                             uint32_t(d.N * d.D * 2), d.T};
+  const rsrc_t Bw = make_rsrc(p.w_uk + int64_t(h) * d.D * d.Hckv, int64_t(d.D) * d.Hckv * 2);
+  stream_wave<false, MT, D>(ap, 0, Bw, uint32_t(d.Hckv * 2), uint32_t(c0 * 2), width * 2,
+                            w * St::KS, NW * St::KS, ns, d.D, acc, lds + w * St::BYTES);
+  reduce_waves<NW, MT>(acc, reinterpret_cast<uint32_t*>(lds));
+  // stage the tile through LDS as bf16, then 16-byte stores
+  uint16_t* E = reinterpret_cast<uint16_t*>(lds);  // [16*MT][64]
+  if (w == 0) {
+    const int g = lane >> 4, c = lane & 15;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) E[(16 * mt + 4 * g + i) * 64 + 16 * ct + c] = f2bf(acc[mt][ct][i]);
+  }
+  __syncthreads();
+  uint16_t* qo = static_cast<uint16_t*>(p.q_out);
+  for (int idx = tid; idx < 16 * MT * 8; idx += 64 * NW) {
+    const int ml = idx / 8, ch = idx % 8;
+    if (ml < d.T && 8 * ch < width)
+      *reinterpret_cast<uint4*>(qo + (int64_t(ml) * d.N + h) * d.Hckv + c0 + 8 * ch) =
+          *reinterpret_cast<const uint4*>(E + ml * 64 + 8 * ch);
+  }
+}
+
+// K4s, int8 query: grid (head); wave w owns the 64-column window w of Hckv
+// (Hckv <= 512) over the whole D reduction; the row maximum is taken across
+// the waves.
+template <int MT, int D>
+__global__ __launch_bounds__(512) void k4_stream_q8(Dims d, Ptrs p) {
+  using St = Stage<false>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[8 * St::BYTES];
+  __shared__ float rmax[8][16 * MT];
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = blockIdx.x;
+  const int c0 = 64 * w, width = max(0, min(64, d.Hckv - c0));
+  const int nst = (d.D + St::KS - 1) / St::KS;
+  const int ns = width > 0 ? nst : 0;
+  typename St::Acc acc[MT][4];
+  const APlain<false, MT> ap{make_rsrc(p.qc + int64_t(h) * d.D, (int64_t(d.T) * d.N - h) * d.D * 2),
+                             uint32_t(d.N * d.D * 2), d.T};
+  const rsrc_t Bw = make_rsrc(p.w_uk + int64_t(h) * d.D * d.Hckv, int64_t(d.D) * d.Hckv * 2);
+  stream_wave<false, MT, D>(ap, 0, Bw, uint32_t(d.Hckv * 2), uint32_t(max(0, c0) * 2), width * 2,
+                            0, St::KS, ns, d.D, acc, lds + w * St::BYTES);
+  const int g = lane >> 4, c = lane & 15;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float mx = 0.0f;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        if (16 * ct + c < width) mx = fmaxf(mx, fabsf(acc[mt][ct][i]));
+      for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+      if (c == 0) rmax[w][16 * mt + 4 * g + i] = mx;
+    }
+  __syncthreads();
+  int8_t* qo = static_cast<int8_t*>(p.q_out);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ml = 16 * mt + 4 * g + i;
+      if (ml >= d.T) continue;
+      float amax = rmax[0][ml];
+      for (int ww = 1; ww < 8; ++ww) amax = fmaxf(amax, rmax[ww][ml]);
+      const float s = amax / 127.0f;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int col = 16 * ct + c;
+        if (col < width)
+          qo[(int64_t(ml) * d.N + h) * d.Hckv + c0 + col] = s > 0.0f ? quant_code(acc[mt][ct][i], s) : 0;
+      }
+      if (w == 0 && c == 0) p.q_scale[int64_t(ml) * d.N + h] = s;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
+// Token counts up to this run on the streaming kernels.
+constexpr int kStreamMaxT = 32;
+constexpr int kStreamWaves = 4;
+
 struct Plan {
+  bool stream;       // small-T streaming path
   int mt1, S, kps;   // K1 rows per tile (16*mt1), split count, k per split
   int mt3;           // K3
   int ntw4, cs4;     // K4 column tiles per wave, column splits
@@ -470,9 +1076,25 @@ int mt_for(int64_t T, int cap) {
   return mt;
 }
 
+int column_tiles(const mla_prolog_desc& d) { return ceil_div(d.Hcq, 64) + ceil_div(d.Hckv + d.Dr, 64); }
+
 Plan make_plan(const mla_prolog_desc& d, int64_t T) {
   Plan pl;
   const bool i8 = d.in_dtype == MLA_INT8;
+  pl.stream = T <= kStreamMaxT;
+  if (pl.stream) {
+    // about two blocks of 8 waves per CU over the column tiles x splits
+    const int ks = i8 ? 64 : 32;
+    const int tiles = column_tiles(d);
+    const int nst = ceil_div(d.He, ks);
+    int S = std::max(1, std::min(nst, (512 + tiles / 2) / tiles));
+    pl.kps = ceil_div(nst, S) * ks;
+    pl.S = ceil_div(d.He, pl.kps);
+    pl.mt1 = T <= 16 ? 1 : 2;
+    pl.mt3 = pl.mt1;
+    pl.ntw4 = pl.cs4 = 0;
+    return pl;
+  }
   const int bk = i8 ? 128 : 64;
   pl.mt1 = mt_for(T, 16);
   const int col_tiles = ceil_div(d.Hcq, 64) + ceil_div(d.Hckv + d.Dr, 64);
@@ -497,7 +1119,7 @@ Plan make_plan(const mla_prolog_desc& d, int64_t T) {
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t part, cq, cq_scale, qc, total;
+  size_t part, cq, cq_scale, qc, y, ssq, amax, ticket, total;
 };
 
 Layout layout(const mla_prolog_desc& d) {
@@ -514,7 +1136,13 @@ Layout layout(const mla_prolog_desc& d) {
   L.cq = align256(L.part + size_t(part_rows) * Ntot * 4);
   L.cq_scale = align256(L.cq + size_t(d.max_tokens) * d.Hcq * 2);
   L.qc = align256(L.cq_scale + size_t(d.max_tokens) * 4);
-  L.total = align256(L.qc + size_t(d.max_tokens) * d.N * d.D * 2);
+  const int64_t Ts = std::min<int64_t>(d.max_tokens, kStreamMaxT);
+  const int tiles = column_tiles(d);
+  L.y = align256(L.qc + size_t(d.max_tokens) * d.N * d.D * 2);
+  L.ssq = align256(L.y + size_t(Ts) * Ntot * 4);
+  L.amax = align256(L.ssq + size_t(tiles) * Ts * 4);
+  L.ticket = align256(L.amax + size_t(tiles) * Ts * 4);
+  L.total = align256(L.ticket + size_t(tiles) * 4);
   return L;
 }
 
@@ -626,6 +1254,57 @@ void launch_k4(int ntw, dim3 grid, hipStream_t s, const Dims& d, const Ptrs& p) 
   }
 }
 
+template <bool I8, int MT>
+void stream_k1k3(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p) {
+  constexpr int D = I8 ? 2 : 4;
+  const int tiles_q = ceil_div(d.Hcq, 64), tiles_kr = ceil_div(d.Hckv + d.Dr, 64);
+  const int tiles = tiles_q + tiles_kr;
+  k1_stream<I8, MT, kStreamWaves, D><<<dim3(tiles * pl.S), 64 * kStreamWaves, 0, s>>>(
+      d, p, tiles_q, tiles, pl.S, pl.kps);
+}
+
+template <bool I8, int MT>
+void stream_k3(hipStream_t s, const Dims& d, const Ptrs& p) {
+  constexpr int D = I8 ? 2 : 3;
+  const int tiles_q = ceil_div(d.Hcq, 64), tiles_kr = ceil_div(d.Hckv + d.Dr, 64);
+  const int nope_tiles = ceil_div(d.D, 64);
+  const int head_blocks = d.N * (nope_tiles + 1);
+  const int kv_tpb = 4;
+  const int kv_blocks = ceil_div(d.T, kv_tpb);
+  k3_stream<I8, MT, kStreamWaves, D><<<dim3(head_blocks + kv_blocks), 64 * kStreamWaves, 0, s>>>(
+      d, p, nope_tiles, tiles_q, tiles_kr, head_blocks, kv_tpb);
+}
+
+template <int MT>
+void stream_k4(hipStream_t s, const Dims& d, const Ptrs& p, bool q8) {
+  if (q8) {
+    k4_stream_q8<MT, 2><<<dim3(d.N), 512, 0, s>>>(d, p);
+  } else {
+    const int windows = ceil_div(d.Hckv, 64);
+    k4_stream<MT, 4, 1><<<dim3(d.N * windows), 256, 0, s>>>(d, p, windows);
+  }
+}
+
+template <class Mark>
+void launch_stream(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p, bool i8, bool q8,
+                   Mark& mark) {
+  if (pl.mt1 == 1) {
+    if (i8) stream_k1k3<true, 1>(pl, s, d, p); else stream_k1k3<false, 1>(pl, s, d, p);
+  } else {
+    if (i8) stream_k1k3<true, 2>(pl, s, d, p); else stream_k1k3<false, 2>(pl, s, d, p);
+  }
+  mark(1);
+  mark(2);
+  if (pl.mt1 == 1) {
+    if (i8) stream_k3<true, 1>(s, d, p); else stream_k3<false, 1>(s, d, p);
+  } else {
+    if (i8) stream_k3<true, 2>(s, d, p); else stream_k3<false, 2>(s, d, p);
+  }
+  mark(3);
+  if (pl.mt1 == 1) stream_k4<1>(s, d, p, q8); else stream_k4<2>(s, d, p, q8);
+  mark(4);
+}
+
 }  // namespace
 
 extern "C" {
@@ -658,6 +1337,14 @@ mla_status mla_prolog_create(const mla_prolog_desc* desc, mla_prolog_t* out) {
   h->events = nullptr;
   h->recorded = 0;
   if (hipMalloc(&h->ws, h->lay.total) != hipSuccess) {
+    delete h;
+    (void)hipSetDevice(prev);
+    return MLA_ERR_RUNTIME;
+  }
+  // split-K arrival counters start at zero; every run leaves them at zero
+  if (hipMemset(h->ws + h->lay.ticket, 0, h->lay.total - h->lay.ticket) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess) {
+    (void)hipFree(h->ws);
     delete h;
     (void)hipSetDevice(prev);
     return MLA_ERR_RUNTIME;
@@ -707,6 +1394,10 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   p.cq = h->ws + h->lay.cq;
   p.cq_scale = reinterpret_cast<float*>(h->ws + h->lay.cq_scale);
   p.qc = reinterpret_cast<uint16_t*>(h->ws + h->lay.qc);
+  p.y = reinterpret_cast<float*>(h->ws + h->lay.y);
+  p.ssq = reinterpret_cast<float*>(h->ws + h->lay.ssq);
+  p.amax = reinterpret_cast<float*>(h->ws + h->lay.amax);
+  p.ticket = reinterpret_cast<unsigned*>(h->ws + h->lay.ticket);
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   hipEvent_t* ev = nullptr;
@@ -718,6 +1409,12 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
     if (ev) (void)hipEventRecord(ev[i], s);
   };
   mark(0);
+  if (pl.stream) {
+    launch_stream(pl, s, d, p, i8, q8, mark);
+    const hipError_t e = hipGetLastError();
+    if (prev != dd.device) (void)hipSetDevice(prev);
+    return e == hipSuccess ? MLA_OK : MLA_ERR_RUNTIME;
+  }
   const int tiles_q = ceil_div(d.Hcq, 64);
   const int tiles_kr = ceil_div(d.Hckv + d.Dr, 64);
   dim3 g1(tiles_q + tiles_kr, pl.S, ceil_div(T, 16 * pl.mt1));
