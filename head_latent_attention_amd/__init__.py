@@ -30,7 +30,8 @@ MLA_BF16 = 0
 MLA_INT8 = 1
 
 #: the symbols include/mla_prolog.h declares
-EXPORTS = ("mla_prolog_validate", "mla_prolog_workspace_bytes", "mla_prolog_create",
+EXPORTS = ("mla_prolog_validate", "mla_prolog_workspace_bytes", "mla_prolog_packed_weights_bytes",
+           "mla_prolog_pack_weights", "mla_prolog_create",
            "mla_prolog_run", "mla_prolog_destroy", "mla_prolog_profile_enable",
            "mla_prolog_profile_read", "mla_prolog_status_string")
 #: kernel order of mla_prolog_profile_read
@@ -57,7 +58,8 @@ class Desc(ctypes.Structure):
 TENSOR_FIELDS = ("token_x", "weight_dq", "weight_uq_qr", "weight_uk", "weight_dkv_kr",
                  "gamma_cq", "gamma_ckv", "rope_sin", "rope_cos", "cache_index",
                  "kv_cache", "kr_cache", "scale_x", "scale_w_dq", "scale_w_uq_qr",
-                 "scale_w_dkv_kr", "query_out", "query_rope_out", "dequant_scale_q_nope")
+                 "scale_w_dkv_kr", "query_out", "query_rope_out", "dequant_scale_q_nope",
+                 "packed_weights")
 
 
 class Tensors(ctypes.Structure):
@@ -84,6 +86,11 @@ def lib() -> ctypes.CDLL:
         L.mla_prolog_validate.restype = ctypes.c_int
         L.mla_prolog_workspace_bytes.argtypes = [ctypes.POINTER(Desc)]
         L.mla_prolog_workspace_bytes.restype = ctypes.c_size_t
+        L.mla_prolog_packed_weights_bytes.argtypes = [ctypes.POINTER(Desc)]
+        L.mla_prolog_packed_weights_bytes.restype = ctypes.c_size_t
+        L.mla_prolog_pack_weights.argtypes = [ctypes.c_void_p, ctypes.POINTER(Tensors), ctypes.c_void_p,
+                                              ctypes.c_void_p]
+        L.mla_prolog_pack_weights.restype = ctypes.c_int
         L.mla_prolog_create.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_void_p)]
         L.mla_prolog_create.restype = ctypes.c_int
         L.mla_prolog_run.argtypes = [ctypes.c_void_p, ctypes.POINTER(Tensors), ctypes.c_int64,
@@ -138,6 +145,17 @@ def workspace_bytes(desc: Desc) -> int:
     return int(lib().mla_prolog_workspace_bytes(ctypes.byref(desc)))
 
 
+def packed_weights_bytes(desc: Desc) -> int:
+    return int(lib().mla_prolog_packed_weights_bytes(ctypes.byref(desc)))
+
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
 class MlaProlog:
     """A library handle: ``MlaProlog(desc)``, then ``run(tensors, T, stream)``."""
 
@@ -152,15 +170,20 @@ class MlaProlog:
     def run(self, tensors: Dict[str, object], T: int, stream=None) -> None:
         """Enqueue one prolog over T tokens on ``stream`` (a torch stream, a
         raw hipStream_t address, or None for the current torch stream)."""
-        if stream is None:
-            import torch
-            stream = torch.cuda.current_stream().cuda_stream
-        elif not isinstance(stream, int):
-            stream = stream.cuda_stream
         t = make_tensors(tensors)
-        st = lib().mla_prolog_run(self._h, ctypes.byref(t), int(T), ctypes.c_void_p(stream))
+        st = lib().mla_prolog_run(self._h, ctypes.byref(t), int(T),
+                                  ctypes.c_void_p(_stream_handle(stream)))
         if st != MLA_OK:
             raise MlaError(st, "mla_prolog_run")
+
+    def pack_weights(self, tensors: Dict[str, object], packed, stream=None) -> None:
+        """Enqueue the conversion of the four weights of ``tensors`` into
+        ``packed`` (a device buffer of ``packed_weights_bytes(desc)`` bytes)."""
+        t = make_tensors(tensors)
+        st = lib().mla_prolog_pack_weights(self._h, ctypes.byref(t), ctypes.c_void_p(_address(packed)),
+                                           ctypes.c_void_p(_stream_handle(stream)))
+        if st != MLA_OK:
+            raise MlaError(st, "mla_prolog_pack_weights")
 
     def profile(self, enable: bool = True) -> None:
         """Start (or stop) recording per-kernel HIP events on every run."""

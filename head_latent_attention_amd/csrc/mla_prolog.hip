@@ -7,9 +7,9 @@
 //
 //   K1 down_proj        y = x [W^DQ | W^DKV | W^KR], split-K partials (fp32,
 //                       or exact int32 in int8 mode) into the workspace
-//   K2 norm_rope_cache  fixed-order split-K sum, both RmsNorms, k^R RoPE,
-//                       kv/kr rows scattered at cacheIndex, c^Q emitted as
-//                       bf16 (or per-token int8 + scale)
+//   K2 norm             fixed-order split-K sum, both RmsNorms (in double),
+//                       k^R RoPE, kv/kr rows scattered at cacheIndex, c^Q
+//                       emitted as bf16 (or per-token int8 + scale)
 //   K3 up_proj          u = c^Q [W^UQ | W^QR] per head; nope columns -> q^C
 //                       (bf16, workspace), rope columns -> RoPE -> queryRopeOut
 //   K4 uk               q^N = q^C W^UK[h] per head; bf16 store, or per-(token,
@@ -211,7 +211,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ A, int64_t
 struct Dims {
   int T, He, Hcq, Hckv, N, D, Dr;
   int64_t slots;  // block_num * block_size
-  float eps_cq, eps_ckv;
+  double eps_cq, eps_ckv;
 };
 
 struct Ptrs {
@@ -239,11 +239,7 @@ struct Ptrs {
   uint8_t* cq;       // [T][Hcq] bf16 (int8 in int8 mode)
   float* cq_scale;   // [T]
   uint16_t* qc;      // [T][N][D] bf16
-  // streaming (small-T) path
-  float* y;          // [T][Hcq+Hckv+Dr] fp32: x [W^DQ | W^DkvKr], split-K reduced
-  float* ssq;        // [column tile][T]: sum of squares of the tile's q or kv columns
-  float* amax;       // [q column tile][T]: max |gamma_cq * y| over the tile's columns
-  unsigned* ticket;  // [column tile]: split-K arrival counters, zero between runs
+  const uint8_t* packed;  // weights in the packed layout, or NULL
 };
 
 // K1 ------------------------------------------------------------------------
@@ -278,74 +274,6 @@ __global__ __launch_bounds__(kThreads) void k_down_proj(Dims d, Ptrs p, int tile
       if constexpr (I8) static_cast<int32_t*>(p.part)[o] = acc[mt][0][i];
       else static_cast<float*>(p.part)[o] = acc[mt][0][i];
     }
-}
-
-// K2 ------------------------------------------------------------------------
-// one block per token
-template <bool I8>
-__global__ __launch_bounds__(kThreads) void k_norm_rope_cache(Dims d, Ptrs p, int S) {
-  extern __shared__ float y[];  // Hcq + Hckv + Dr
-  __shared__ float red[4];
-  const int t = blockIdx.x, tid = threadIdx.x;
-  const int Nkr = d.Hckv + d.Dr, Ntot = d.Hcq + Nkr;
-  for (int n = tid; n < Ntot; n += kThreads) {
-    float v;
-    if constexpr (I8) {
-      const int32_t* part = static_cast<const int32_t*>(p.part);
-      int32_t a = 0;
-      for (int s = 0; s < S; ++s) a += part[(int64_t(s) * d.T + t) * Ntot + n];
-      const float sw = n < d.Hcq ? p.sw_dq[n] : p.sw_dkv_kr[n - d.Hcq];
-      v = static_cast<float>(a) * p.sx[t] * sw;
-    } else {
-      const float* part = static_cast<const float*>(p.part);
-      v = 0.0f;
-      for (int s = 0; s < S; ++s) v += part[(int64_t(s) * d.T + t) * Ntot + n];
-    }
-    y[n] = v;
-  }
-  __syncthreads();
-  float sq = 0.0f, skv = 0.0f;
-  for (int n = tid; n < d.Hcq; n += kThreads) sq += y[n] * y[n];
-  for (int n = tid; n < d.Hckv; n += kThreads) skv += y[d.Hcq + n] * y[d.Hcq + n];
-  sq = block_reduce<false>(sq, red);
-  skv = block_reduce<false>(skv, red);
-  const float inv_q = 1.0f / sqrtf(sq / float(d.Hcq) + d.eps_cq);
-  const float inv_kv = 1.0f / sqrtf(skv / float(d.Hckv) + d.eps_ckv);
-
-  // c^Q
-  if constexpr (I8) {
-    float amax = 0.0f;
-    for (int n = tid; n < d.Hcq; n += kThreads) {
-      const float v = bf2f(p.gamma_cq[n]) * (y[n] * inv_q);
-      y[n] = v;
-      amax = fmaxf(amax, fabsf(v));
-    }
-    amax = block_reduce<true>(amax, red);
-    const float s = amax / 127.0f;
-    int8_t* cq = reinterpret_cast<int8_t*>(p.cq) + int64_t(t) * d.Hcq;
-    for (int n = tid; n < d.Hcq; n += kThreads) cq[n] = s > 0.0f ? quant_code(y[n], s) : 0;
-    if (tid == 0) p.cq_scale[t] = s;
-  } else {
-    uint16_t* cq = reinterpret_cast<uint16_t*>(p.cq) + int64_t(t) * d.Hcq;
-    for (int n = tid; n < d.Hcq; n += kThreads) cq[n] = f2bf(bf2f(p.gamma_cq[n]) * (y[n] * inv_q));
-  }
-
-  // c^KV and k^R into the caches
-  const int64_t slot = p.cache_index[t];
-  if (slot < 0 || slot >= d.slots) return;
-  uint16_t* kv = p.kv_cache + slot * d.Hckv;
-  for (int n = tid; n < d.Hckv; n += kThreads)
-    kv[n] = f2bf(bf2f(p.gamma_ckv[n]) * (y[d.Hcq + n] * inv_kv));
-  const int h = d.Dr / 2;
-  const float* yr = y + d.Hcq + d.Hckv;
-  const uint16_t* cs = p.cos + int64_t(t) * d.Dr;
-  const uint16_t* sn = p.sin + int64_t(t) * d.Dr;
-  uint16_t* kr = p.kr_cache + slot * d.Dr;
-  for (int i = tid; i < h; i += kThreads) {
-    const float a = yr[i], b = yr[i + h];
-    kr[i] = f2bf(a * bf2f(cs[i]) - b * bf2f(sn[i]));
-    kr[i + h] = f2bf(b * bf2f(cs[i + h]) + a * bf2f(sn[i + h]));
-  }
 }
 
 // K3 ------------------------------------------------------------------------
@@ -459,73 +387,16 @@ __global__ __launch_bounds__(kThreads) void k_uk(Dims d, Ptrs p) {
 }
 
 // ---------------------------------------------------------------------------
-// Streaming path for small token counts (T <= 32): weight-bandwidth bound.
-//
-// Every wave streams its own k-stages of a 64-column weight window: a stage
-// is one MFMA k-step (32 bf16 rows or 64 int8 rows, 4 KB), loaded with
-// 16-byte coalesced loads into a register ring D stages deep (the activation
-// fragments of the same stage travel in the same ring, so the in-order
-// vector-memory counter never makes a stage wait for a later one), written
-// to the wave's own 4 KB LDS buffer with an XOR swizzle, and read back as
-// MFMA B fragments with the gfx950 transpose reads (ds_read_b64_tr_b16 /
-// ds_read_b64_tr_b8), two per fragment.  No block barrier is needed while
-// streaming; the waves of a block cover interleaved stages of one k range
-// and are summed through LDS in a fixed order at the end.
-//
-// Transpose-read lane layout (gfx950): within each 16-lane group, lane l
-// receives element l%4 (b16) or l%8 (b8) of the 8 bytes addressed by source
-// lanes l/4 + 4j (b16, j < 4) or l/8 + 2j (b8, j < 8).  With source lane s
-// of group g addressing row 8g + s/4 (b16) or 16g + s/2 (b8) and column
-// 16*ct + 4*(s%4) (b16) or 16*ct + 8*(s%2) (b8), lane l gets column 16*ct + l
-// for consecutive rows: exactly the k-run an MFMA B operand holds.
+// Small-T building blocks: MFMA operand geometry, buffer loads, activation
+// operands and the fixed-order sum of several waves' accumulators.
 // ---------------------------------------------------------------------------
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ s16x4 lds_tr16(const uint8_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(p));
-}
-__device__ __forceinline__ i32x2 lds_tr8(const uint8_t* p) {
-  return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-      (__attribute__((address_space(3))) i32x2*)(p));
-}
-
 template <bool I8>
 struct Stage {
   static constexpr int EB = I8 ? 1 : 2;
   static constexpr int KS = I8 ? 64 : 32;    // k rows per stage (one MFMA k-step)
   static constexpr int KL = 16 / EB;         // k per lane per MFMA
-  static constexpr int RB = 64 * EB;         // bytes per stage row (64 columns)
-  static constexpr int CPR = RB / 16;        // 16-byte chunks per row
-  static constexpr int BYTES = KS * RB;      // 4096
   using Acc = typename std::conditional<I8, i32x4, f32x4>::type;
   using Frag = typename std::conditional<I8, i32x4, bf16x8>::type;
-  // 16-byte chunk index XOR of row r: makes the transpose reads of the four
-  // lane groups (and both halves of a wave) hit distinct banks
-  __device__ static __forceinline__ int swz(int r) {
-    if constexpr (I8) return ((r >> 1) & 3) ^ ((r >> 4) & 1);
-    else return 2 * ((r & 3) ^ ((r >> 3) & 1));
-  }
-  __device__ static __forceinline__ int off(int r, int chunk) { return r * RB + 16 * (chunk ^ swz(r)); }
-  // B fragment of column tile ct from a stage buffer
-  __device__ static __forceinline__ Frag frag(const uint8_t* buf, int lane, int ct) {
-    const int g = lane >> 4, s = lane & 15;
-    if constexpr (I8) {
-      const int r1 = 16 * g + (s >> 1), r2 = r1 + 8, o = 8 * (s & 1);
-      const i32x2 v1 = lds_tr8(buf + off(r1, ct) + o);
-      const i32x2 v2 = lds_tr8(buf + off(r2, ct) + o);
-      i32x4 f = {v1[0], v1[1], v2[0], v2[1]};
-      return f;
-    } else {
-      const int r1 = 8 * g + (s >> 2), r2 = r1 + 4, ch = 2 * ct + ((s & 3) >> 1), o = 8 * (s & 1);
-      const s16x4 v1 = lds_tr16(buf + off(r1, ch) + o);
-      const s16x4 v2 = lds_tr16(buf + off(r2, ch) + o);
-      union { s16x4 h[2]; bf16x8 v; } u;
-      u.h[0] = v1; u.h[1] = v2;
-      return u.v;
-    }
-  }
 };
 
 // Buffer loads: an offset at or past num_records returns zeros without a
@@ -552,9 +423,8 @@ __device__ __forceinline__ i32x4 mfma(i32x4 a, i32x4 b, i32x4 c) {
 
 // Activation operands.  A policy loads the raw 16-byte registers of the MT
 // fragments of one stage (load) and turns them into MFMA A fragments (frag).
-
-// Fragments read as stored (bf16 or int8, k-contiguous rows); rows are
-// relative to the buffer base (the block's first row).
+// This one reads them as stored (bf16 or int8, k-contiguous rows); rows are
+// relative to the buffer base.
 template <bool I8, int MT>
 struct APlain {
   static constexpr int NR = MT;  // 16-byte registers per stage
@@ -570,120 +440,9 @@ struct APlain {
     }
   }
   __device__ __forceinline__ typename Stage<I8>::Frag frag(const uint4 (&r)[NR], int mt, int) const {
-    union { uint4 u; typename Stage<I8>::Frag f; } c;
-    c.u = r[mt];
-    return c.f;
+    return __builtin_bit_cast(typename Stage<I8>::Frag, r[mt]);
   }
 };
-
-// c^Q fragments computed from the reduced down-projection y (fp32):
-// c = (gamma * y) * inv_rms, then bf16 (nearest even), or the per-token
-// int8 code nearest to c / s_cq.  gamma is loaded once per stage.
-template <bool I8, int MT>
-struct ACq {
-  static constexpr int NY = I8 ? 4 : 2;   // 16-byte y registers per fragment
-  static constexpr int NG = I8 ? 2 : 1;   // 16-byte gamma registers per stage
-  static constexpr int NR = MT * NY + NG;
-  rsrc_t y;        // [M][ldy] fp32
-  uint32_t ldy;    // bytes per y row
-  rsrc_t gamma;    // [Hcq] bf16
-  int M;
-  const float* inv;    // LDS, per row of the block
-  const float* scale;  // LDS, per row (int8)
-  __device__ __forceinline__ void load(uint4 (&r)[NR], int m0, int ka, int ke) const {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int m = m0 + 16 * mt;
-      const bool ok = m < M && ka < ke;
-#pragma unroll
-      for (int i = 0; i < NY; ++i)
-        r[mt * NY + i] = bload16(y, ok ? uint32_t(m) * ldy + uint32_t(ka + 4 * i) * 4 : kOOB);
-    }
-#pragma unroll
-    for (int i = 0; i < NG; ++i)
-      r[MT * NY + i] = bload16(gamma, ka < ke ? uint32_t(ka + 8 * i) * 2 : kOOB);
-  }
-  __device__ __forceinline__ typename Stage<I8>::Frag frag(const uint4 (&r)[NR], int mt, int ml) const {
-    constexpr int NV = I8 ? 16 : 8;
-    const float* yv = reinterpret_cast<const float*>(&r[mt * NY]);
-    const uint16_t* gv = reinterpret_cast<const uint16_t*>(&r[MT * NY]);
-    const float iv = inv[ml];
-    if constexpr (I8) {
-      const float sc = scale[ml];
-      union { int8_t b[16]; i32x4 v; } u;
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const float c = (bf2f(gv[i]) * yv[i]) * iv;
-        u.b[i] = sc > 0.0f ? quant_code(c, sc) : 0;
-      }
-      return u.v;
-    } else {
-      union { uint16_t h[8]; bf16x8 v; } u;
-#pragma unroll
-      for (int i = 0; i < NV; ++i) u.h[i] = f2bf((bf2f(gv[i]) * yv[i]) * iv);
-      return u.v;
-    }
-  }
-};
-
-// One wave streams stages j = 0..ns-1 (rows kfirst + j*kstep .. +KS, clipped
-// to ke) of the 64-column weight window starting at byte n0b of each row of
-// the weight buffer Bw (row stride ldb bytes, wbytes valid bytes per row)
-// against MT activation fragments of rows m0 + 16*mt + lane%16.  The ring
-// loop is straight-line: stages past the end load zeros (no memory traffic)
-// and add nothing.
-template <bool I8, int MT, int D, class AP>
-__device__ __forceinline__ void stream_wave(const AP& ap, int m0, rsrc_t Bw, uint32_t ldb,
-                                            uint32_t n0b, int wbytes, int kfirst, int kstep,
-                                            int ns, int ke, typename Stage<I8>::Acc (&acc)[MT][4],
-                                            uint8_t* buf) {
-  using S = Stage<I8>;
-  const int lane = threadIdx.x & 63;
-  const int ml = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) acc[mt][ct] = typename S::Acc{0, 0, 0, 0};
-
-  uint4 bq[D][4];
-  uint4 aq[D][AP::NR];
-  auto issue = [&](uint4 (&b)[4], uint4 (&a)[AP::NR], int j) {
-    const int k0 = kfirst + j * kstep;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = lane + 64 * i, r = q / S::CPR, c = q % S::CPR;
-      const bool ok = j < ns && k0 + r < ke && 16 * c < wbytes;
-      b[i] = bload16(Bw, ok ? uint32_t(k0 + r) * ldb + n0b + 16 * c : kOOB);
-    }
-    ap.load(a, m0 + ml, j < ns ? k0 + S::KL * g : ke, ke);
-  };
-#pragma unroll
-  for (int p = 0; p < D; ++p) issue(bq[p], aq[p], p);
-
-  const int nsr = (ns + D - 1) / D * D;
-  for (int j0 = 0; j0 < nsr; j0 += D) {
-#pragma unroll
-    for (int p = 0; p < D; ++p) {
-      const int j = j0 + p;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int q = lane + 64 * i, r = q / S::CPR, c = q % S::CPR;
-        *reinterpret_cast<uint4*>(buf + S::off(r, c)) = bq[p][i];
-      }
-      typename S::Frag af[MT];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) af[mt] = ap.frag(aq[p], mt, 16 * mt + ml);
-      issue(bq[p], aq[p], j + D);
-      typename S::Frag bf[4];
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) bf[ct] = S::frag(buf, lane, ct);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) acc[mt][ct] = mfma(af[mt], bf[ct], acc[mt][ct]);
-    }
-  }
-}
 
 // Sum of the NW waves' accumulators into wave 0, in a fixed pairing order.
 // red: (NW/2) * MT * 16 * 64 words of LDS.  Ends with a block barrier.
@@ -724,91 +483,219 @@ __device__ __forceinline__ void reduce_waves(Acc (&acc)[MT][4], uint32_t* red) {
   __syncthreads();
 }
 
-template <bool I8, int MT, int NW>
-struct StreamLds {
-  static constexpr int STAGE = NW * Stage<I8>::BYTES;
-  static constexpr int RED = (NW / 2) * MT * 16 * 64 * 4;
-  static constexpr int BYTES = STAGE > RED ? STAGE : RED;
+// ---------------------------------------------------------------------------
+// Packed weights.  Each weight matrix is cut into windows of 64 columns; a
+// window is stored as its k-stages one after the other (32 bf16 rows or 64
+// int8 rows per stage, 4 KB), and inside a stage as 4 column tiles x 64
+// lanes x 16 bytes in MFMA B-fragment order: lane l of column tile ct holds
+// rows KL*(l/16) + i (i < KL) of column 16*ct + l%16.  A block streaming a
+// window reads one contiguous region, and every 16-byte load lands directly
+// in the register an MFMA reads; no LDS transposition is needed.
+//
+// Windows: W^DQ in 64-column steps; W^DkvKr likewise; W^UqQr per head, its
+// nope columns in 64-column steps then its Dr rope columns; W^UK per head,
+// Hckv in 64-column steps (k = the D rows).  Zero padding fills ragged
+// windows and stages.
+// ---------------------------------------------------------------------------
+struct PackGeo {
+  int64_t off_dq, off_kr, off_uq, off_uk, total;  // byte offsets in the packed buffer
+  int win_dq, win_kr, win_uq, win_uk;             // windows per matrix
+  int nst_he, nst_cq, nst_d;                      // stages along He, Hcq, D
+  int nope_w, uk_w;                               // nope windows per head, W^UK windows per head
 };
 
-// K1s: grid (column tiles x splits).  The block streams its k range of one
-// 64-column window of [W^DQ | W^DkvKr] and writes a partial tile; the last
-// block of a column tile to arrive sums the S partials in split order into y
-// and writes the tile's per-token statistics.
-template <bool I8, int MT, int NW, int D>
-__global__ __launch_bounds__(64 * NW) void k1_stream(Dims d, Ptrs p, int tiles_q, int tiles, int S,
-                                                     int kps) {
-  using St = Stage<I8>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[StreamLds<I8, MT, NW>::BYTES];
-  __shared__ int last;
-  const int jt = blockIdx.x % tiles, split = blockIdx.x / tiles;
-  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int Nkr = d.Hckv + d.Dr, Ntot = d.Hcq + Nkr;
-  const uint8_t* B;
-  int64_t ldb;
-  int n0, width, outc;
-  if (jt < tiles_q) {
-    n0 = 64 * jt; width = min(64, d.Hcq - n0); B = p.w_dq; ldb = int64_t(d.Hcq) * St::EB; outc = n0;
+PackGeo pack_geo(int64_t He, int64_t Hcq, int64_t Hckv, int64_t N, int64_t D, int64_t Dr, bool i8) {
+  PackGeo g;
+  const int ks = i8 ? 64 : 32;
+  g.nst_he = int((He + ks - 1) / ks);
+  g.nst_cq = int((Hcq + ks - 1) / ks);
+  g.nst_d = int((D + 31) / 32);
+  g.nope_w = int((D + 63) / 64);
+  g.uk_w = int((Hckv + 63) / 64);
+  g.win_dq = int((Hcq + 63) / 64);
+  g.win_kr = int((Hckv + Dr + 63) / 64);
+  g.win_uq = int(N) * (g.nope_w + 1);
+  g.win_uk = int(N) * g.uk_w;
+  g.off_dq = 0;
+  g.off_kr = g.off_dq + int64_t(g.win_dq) * g.nst_he * 4096;
+  g.off_uq = g.off_kr + int64_t(g.win_kr) * g.nst_he * 4096;
+  g.off_uk = g.off_uq + int64_t(g.win_uq) * g.nst_cq * 4096;
+  g.total = g.off_uk + int64_t(g.win_uk) * g.nst_d * 4096;
+  return g;
+}
+
+// One 16-byte chunk per thread: (window, stage, column tile, lane) of one
+// matrix, gathered from the row-major source.
+__global__ __launch_bounds__(256) void k_pack(Dims d, Ptrs p, PackGeo g, int i8, uint8_t* out) {
+  const int64_t q = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t off = q * 16;
+  if (off >= g.total) return;
+  int64_t rel;
+  int nst, win;
+  const uint8_t* src;
+  int64_t ld;          // source row stride, elements
+  int K, col0, width, eb, kl;
+  if (off < g.off_kr) {
+    rel = off - g.off_dq; nst = g.nst_he; win = int(rel / (int64_t(nst) * 4096));
+    src = p.w_dq; ld = d.Hcq; K = d.He; col0 = 64 * win; width = min(64, d.Hcq - col0);
+    eb = i8 ? 1 : 2;
+  } else if (off < g.off_uq) {
+    rel = off - g.off_kr; nst = g.nst_he; win = int(rel / (int64_t(nst) * 4096));
+    src = p.w_dkv_kr; ld = d.Hckv + d.Dr; K = d.He; col0 = 64 * win; width = min(64, d.Hckv + d.Dr - col0);
+    eb = i8 ? 1 : 2;
+  } else if (off < g.off_uk) {
+    rel = off - g.off_uq; nst = g.nst_cq; win = int(rel / (int64_t(nst) * 4096));
+    const int h = win / (g.nope_w + 1), part = win % (g.nope_w + 1);
+    src = p.w_uq_qr; ld = int64_t(d.N) * (d.D + d.Dr); K = d.Hcq;
+    col0 = h * (d.D + d.Dr) + (part < g.nope_w ? 64 * part : d.D);
+    width = part < g.nope_w ? min(64, d.D - 64 * part) : d.Dr;
+    eb = i8 ? 1 : 2;
   } else {
-    n0 = 64 * (jt - tiles_q); width = min(64, Nkr - n0); B = p.w_dkv_kr;
-    ldb = int64_t(Nkr) * St::EB; outc = d.Hcq + n0;
+    rel = off - g.off_uk; nst = g.nst_d; win = int(rel / (int64_t(nst) * 4096));
+    const int h = win / g.uk_w, part = win % g.uk_w;
+    src = reinterpret_cast<const uint8_t*>(p.w_uk + int64_t(h) * d.D * d.Hckv);
+    ld = d.Hckv; K = d.D; col0 = 64 * part; width = min(64, d.Hckv - col0);
+    eb = 2;
   }
-  const int kb = split * kps, ke = min(d.He, kb + kps);
-  const int nst = (ke - kb + St::KS - 1) / St::KS;
-  const int ns = w < nst ? (nst - w + NW - 1) / NW : 0;
+  const int in_win = int(rel % (int64_t(nst) * 4096));
+  const int stage = in_win / 4096, ct = (in_win % 4096) / 1024, lane = (in_win % 1024) / 16;
+  kl = 16 / eb;
+  const int ks = 4 * kl;  // rows per stage: 32 bf16, 64 int8
+  const int c = 16 * ct + (lane & 15);
+  union { uint4 v; uint8_t b[16]; uint16_t h[8]; } u;
+  u.v = make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < kl; ++i) {
+    const int k = stage * ks + kl * (lane >> 4) + i;
+    if (k >= K || c >= width) continue;
+    const int64_t e = int64_t(k) * ld + col0 + c;
+    if (eb == 1) u.b[i] = src[e];
+    else u.h[i] = reinterpret_cast<const uint16_t*>(src)[e];
+  }
+  *reinterpret_cast<uint4*>(out + off) = u.v;
+}
+
+// One wave streams stages s = sfirst + j*sstep (j < ns) of the packed window
+// at byte wbase against MT activation fragments; all loads go through one
+// register ring D stages deep.
+template <bool I8, int MT, int D, class AP>
+__device__ __forceinline__ void stream_packed(const AP& ap, int m0, rsrc_t Wp, uint32_t wbase,
+                                              int sfirst, int sstep, int ns, int ke,
+                                              typename Stage<I8>::Acc (&acc)[MT][4]) {
+  using S = Stage<I8>;
+  const int lane = threadIdx.x & 63;
+  const int ml = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) acc[mt][ct] = typename S::Acc{0, 0, 0, 0};
+  uint4 bq[D][4];
+  uint4 aq[D][AP::NR];
+  auto issue = [&](uint4 (&b)[4], uint4 (&a)[AP::NR], int j) {
+    const int st = sfirst + j * sstep;
+    const bool ok = j < ns;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+      b[ct] = bload16(Wp, ok ? wbase + uint32_t(st) * 4096u + uint32_t(ct * 1024 + lane * 16) : kOOB);
+    ap.load(a, m0 + ml, ok ? st * S::KS + S::KL * g : ke, ke);
+  };
+#pragma unroll
+  for (int q = 0; q < D; ++q) issue(bq[q], aq[q], q);
+  const int nsr = (ns + D - 1) / D * D;
+  for (int j0 = 0; j0 < nsr; j0 += D) {
+#pragma unroll
+    for (int q = 0; q < D; ++q) {
+      typename S::Frag af[MT], bf[4];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) af[mt] = ap.frag(aq[q], mt, 16 * mt + ml);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) bf[ct] = __builtin_bit_cast(typename S::Frag, bq[q][ct]);
+      issue(bq[q], aq[q], j0 + q + D);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) acc[mt][ct] = mfma(af[mt], bf[ct], acc[mt][ct]);
+    }
+  }
+}
+
+// K1p: grid (windows of W^DQ and W^DkvKr x splits); writes split partials.
+template <bool I8, int MT, int NW, int D>
+__global__ __launch_bounds__(64 * NW) void k1_packed(Dims d, Ptrs p, PackGeo pg, int S, int sps) {
+  using St = Stage<I8>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[(NW / 2) * MT * 16 * 64 * 4];
+  const int tiles = pg.win_dq + pg.win_kr;
+  const int jt = blockIdx.x % tiles, split = blockIdx.x / tiles;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int Nkr = d.Hckv + d.Dr, Ntot = d.Hcq + Nkr;
+  int64_t wbase;
+  int width, outc;
+  if (jt < pg.win_dq) {
+    wbase = pg.off_dq + int64_t(jt) * pg.nst_he * 4096; width = min(64, d.Hcq - 64 * jt); outc = 64 * jt;
+  } else {
+    const int j = jt - pg.win_dq;
+    wbase = pg.off_kr + int64_t(j) * pg.nst_he * 4096; width = min(64, Nkr - 64 * j); outc = d.Hcq + 64 * j;
+  }
+  const int s0 = split * sps, s1 = min(pg.nst_he, s0 + sps);
+  const int ns = s0 + w < s1 ? (s1 - s0 - w + NW - 1) / NW : 0;
   typename St::Acc acc[MT][4];
   const APlain<I8, MT> ap{make_rsrc(p.x, int64_t(d.T) * d.He * St::EB), uint32_t(d.He * St::EB), d.T};
-  const rsrc_t Bw = make_rsrc(B, int64_t(d.He) * ldb);
-  stream_wave<I8, MT, D>(ap, 0, Bw, uint32_t(ldb), uint32_t(n0 * St::EB), width * St::EB,
-                         kb + w * St::KS, NW * St::KS, ns, ke, acc, lds + w * St::BYTES);
+  stream_packed<I8, MT, D>(ap, 0, make_rsrc(p.packed, pg.total), uint32_t(wbase), s0 + w, NW, ns,
+                           d.He, acc);
   reduce_waves<NW, MT>(acc, reinterpret_cast<uint32_t*>(lds));
-
-  // partial tile, written by wave 0
-  if (w == 0) {
-    const int g = lane >> 4, c = lane & 15;
+  if (w != 0) return;
+  const int g = lane >> 4, c = lane & 15;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const int col = 16 * ct + c;
-        if (col >= width) continue;
+    for (int ct = 0; ct < 4; ++ct) {
+      const int col = 16 * ct + c;
+      if (col >= width) continue;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = 16 * mt + 4 * g + i;
-          if (m >= d.T) continue;
-          const int64_t o = (int64_t(split) * d.T + m) * Ntot + outc + col;
-          if constexpr (I8) static_cast<int32_t*>(p.part)[o] = acc[mt][ct][i];
-          else static_cast<float*>(p.part)[o] = acc[mt][ct][i];
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * mt + 4 * g + i;
+        if (m >= d.T) continue;
+        const int64_t o = (int64_t(split) * d.T + m) * Ntot + outc + col;
+        if constexpr (I8) static_cast<int32_t*>(p.part)[o] = acc[mt][ct][i];
+        else static_cast<float*>(p.part)[o] = acc[mt][ct][i];
       }
-  }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) last = atomicAdd(&p.ticket[jt], 1u) == unsigned(S - 1);
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
+    }
+}
 
-  // the last arrival: y = sum of the partials (split order), and statistics.
-  // 16 threads per row, 4 columns each, 4*NW rows per pass; the partials of
-  // 8 splits are loaded before they are added (splits past S read as zeros).
+// K2: one block per token, 1024 threads.  Sums the S split partials (in
+// split order) of x [W^DQ | W^DkvKr] into y, then applies both RmsNorms,
+// writes c^Q (bf16, or per-token int8 + scale) to the workspace and the
+// c^KV / RoPE(k^R) rows to the token's cacheIndex slot.  y, the RMS factors
+// and c are computed in double (a few thousand values per token), so the
+// per-token int8 decision of c^Q sees c rounded once to fp32.
+__device__ double block_sum_f64(double v, double* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  double r = red[0];
+  for (int w = 1; w < nw; ++w) r += red[w];
+  return r;
+}
+
+template <bool I8>
+__global__ __launch_bounds__(1024) void k2_norm(Dims d, Ptrs p, int S) {
+  extern __shared__ double y[];  // Hcq + Hckv + Dr
+  __shared__ double red[16];
+  __shared__ float redf[16];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int Nkr = d.Hckv + d.Dr, Ntot = d.Hcq + Nkr, n4 = Ntot / 4;
   const rsrc_t P = make_rsrc(p.part, int64_t(S) * d.T * Ntot * 4);
-  const int cq = 4 * (tid & 15);
-  const bool col_ok = cq < width;
-  for (int m = tid >> 4; m < 16 * MT; m += 4 * NW) {
-    const bool row_ok = m < d.T;
-    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int c4 = tid; c4 < n4; c4 += 1024) {
+    double v[4] = {0.0, 0.0, 0.0, 0.0};
     int32_t iv[4] = {0, 0, 0, 0};
-    for (int s0 = 0; s0 < S; s0 += 8) {
-      uint4 r[8];
+    for (int s0 = 0; s0 < S; s0 += 16) {
+      uint4 r[16];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sp = s0 + e;
-        const bool ok = row_ok && col_ok && sp < S;
-        r[e] = bload16(P, ok ? uint32_t(((int64_t(sp) * d.T + m) * Ntot + outc + cq) * 4) : kOOB);
-      }
+      for (int e = 0; e < 16; ++e)
+        r[e] = bload16(P, s0 + e < S ? uint32_t(((int64_t(s0 + e) * d.T + t) * Ntot + 4 * c4) * 4) : kOOB);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < 16; ++e) {
         if constexpr (I8) {
           const int4 q = __builtin_bit_cast(int4, r[e]);
           iv[0] += q.x; iv[1] += q.y; iv[2] += q.z; iv[3] += q.w;
@@ -818,240 +705,240 @@ __global__ __launch_bounds__(64 * NW) void k1_stream(Dims d, Ptrs p, int tiles_q
         }
       }
     }
-    float ss = 0.0f, am = 0.0f;
-    if (row_ok && col_ok) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int gc = outc + cq + e;   // column of y
-        if constexpr (I8) {
-          const float sw = gc < d.Hcq ? p.sw_dq[gc] : p.sw_dkv_kr[gc - d.Hcq];
-          v[e] = static_cast<float>(iv[e]) * p.sx[m] * sw;
-        }
-        if (gc < d.Hcq + d.Hckv) ss += v[e] * v[e];
-        if (gc < d.Hcq) am = fmaxf(am, fabsf(bf2f(p.gamma_cq[gc]) * v[e]));
+    for (int e = 0; e < 4; ++e) {
+      const int n = 4 * c4 + e;
+      if constexpr (I8) {
+        const double sw = n < d.Hcq ? p.sw_dq[n] : p.sw_dkv_kr[n - d.Hcq];
+        v[e] = double(iv[e]) * double(p.sx[t]) * sw;
       }
-      *reinterpret_cast<float4*>(p.y + int64_t(m) * Ntot + outc + cq) = make_float4(v[0], v[1], v[2], v[3]);
+      y[n] = v[e];
     }
-    for (int o = 1; o < 16; o <<= 1) {
-      ss += __shfl_xor(ss, o, 64);
-      am = fmaxf(am, __shfl_xor(am, o, 64));
-    }
-    if ((tid & 15) == 0 && row_ok) {
-      p.ssq[int64_t(jt) * d.T + m] = ss;
-      if (jt < tiles_q) p.amax[int64_t(jt) * d.T + m] = am;
-    }
-  }
-  if (tid == 0) p.ticket[jt] = 0u;
-}
-
-// Per-token RmsNorm factors of the query rows: inv = 1/sqrt(sum ssq / Hcq + eps)
-// (tiles summed in order), and in int8 mode the c^Q scale max|c| / 127.
-template <bool I8>
-__device__ __forceinline__ void cq_factors(const Dims& d, const Ptrs& p, int tiles_q, int m,
-                                           float& inv, float& scale) {
-  float ss = 0.0f, am = 0.0f;
-  for (int jt = 0; jt < tiles_q; ++jt) {
-    ss += p.ssq[int64_t(jt) * d.T + m];
-    if constexpr (I8) am = fmaxf(am, p.amax[int64_t(jt) * d.T + m]);
-  }
-  inv = 1.0f / sqrtf(ss / float(d.Hcq) + d.eps_cq);
-  scale = I8 ? (am * inv) / 127.0f : 0.0f;
-}
-
-// K3s: grid (head tiles + kv blocks).  Head tiles: per head the nope columns
-// in windows of 64, then the Dr rope columns; the block's waves split the
-// whole Hcq reduction.  kv blocks: RmsNorm of c^KV and RoPE of k^R for
-// kv_tpb tokens each, written at their cacheIndex slots.
-template <bool I8, int MT, int NW, int D>
-__global__ __launch_bounds__(64 * NW) void k3_stream(Dims d, Ptrs p, int nope_tiles, int tiles_q,
-                                                     int tiles_kr, int head_blocks, int kv_tpb) {
-  using St = Stage<I8>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[StreamLds<I8, MT, NW>::BYTES];
-  __shared__ float inv_s[16 * MT], scale_s[16 * MT];
-  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int Nkr = d.Hckv + d.Dr, Ntot = d.Hcq + Nkr;
-
-  if (int(blockIdx.x) >= head_blocks) {
-    // c^KV and k^R for tokens [t0, t0 + kv_tpb)
-    const int t0 = (blockIdx.x - head_blocks) * kv_tpb;
-    for (int t = t0; t < min(d.T, t0 + kv_tpb); ++t) {
-      const int64_t slot = p.cache_index[t];
-      if (slot < 0 || slot >= d.slots) continue;
-      float ss = 0.0f;
-      for (int jt = tiles_q; jt < tiles_q + tiles_kr; ++jt) ss += p.ssq[int64_t(jt) * d.T + t];
-      const float inv = 1.0f / sqrtf(ss / float(d.Hckv) + d.eps_ckv);
-      const float* yk = p.y + int64_t(t) * Ntot + d.Hcq;
-      uint16_t* kv = p.kv_cache + slot * d.Hckv;
-      for (int n = tid; n < d.Hckv; n += 64 * NW) kv[n] = f2bf((bf2f(p.gamma_ckv[n]) * yk[n]) * inv);
-      const int h = d.Dr / 2;
-      const float* yr = yk + d.Hckv;
-      const uint16_t* cs = p.cos + int64_t(t) * d.Dr;
-      const uint16_t* sn = p.sin + int64_t(t) * d.Dr;
-      uint16_t* kr = p.kr_cache + slot * d.Dr;
-      for (int i = tid; i < h; i += 64 * NW) {
-        const float a = yr[i], b = yr[i + h];
-        kr[i] = f2bf(a * bf2f(cs[i]) - b * bf2f(sn[i]));
-        kr[i + h] = f2bf(b * bf2f(cs[i + h]) + a * bf2f(sn[i + h]));
-      }
-    }
-    return;
-  }
-
-  const int hp = nope_tiles + 1;
-  const int h = blockIdx.x / hp, part = blockIdx.x % hp;
-  const bool rope = part == nope_tiles;
-  const int W = d.N * (d.D + d.Dr);
-  const int col0 = h * (d.D + d.Dr) + (rope ? d.D : 64 * part);
-  const int width = rope ? d.Dr : min(64, d.D - 64 * part);
-  for (int m = tid; m < 16 * MT; m += 64 * NW) {
-    float iv = 0.0f, sc = 0.0f;
-    if (m < d.T) cq_factors<I8>(d, p, tiles_q, m, iv, sc);
-    inv_s[m] = iv;
-    scale_s[m] = sc;
   }
   __syncthreads();
-  const int nst = (d.Hcq + St::KS - 1) / St::KS;
-  const int ns = w < nst ? (nst - w + NW - 1) / NW : 0;
-  typename St::Acc acc[MT][4];
-  const ACq<I8, MT> ap{make_rsrc(p.y, int64_t(d.T) * Ntot * 4), uint32_t(Ntot * 4),
-                       make_rsrc(p.gamma_cq, int64_t(d.Hcq) * 2), d.T, inv_s, scale_s};
-  const rsrc_t Bw = make_rsrc(p.w_uq_qr, int64_t(d.Hcq) * W * St::EB);
-  stream_wave<I8, MT, D>(ap, 0, Bw, uint32_t(W * St::EB), uint32_t(col0 * St::EB), width * St::EB,
-                         w * St::KS, NW * St::KS, ns, d.Hcq, acc, lds + w * St::BYTES);
-  reduce_waves<NW, MT>(acc, reinterpret_cast<uint32_t*>(lds));
+  double sq = 0.0, skv = 0.0;
+  for (int n = tid; n < d.Hcq; n += 1024) sq += y[n] * y[n];
+  for (int n = tid; n < d.Hckv; n += 1024) skv += y[d.Hcq + n] * y[d.Hcq + n];
+  sq = block_sum_f64(sq, red);
+  skv = block_sum_f64(skv, red);
+  const double rms_q = sqrt(sq / double(d.Hcq) + d.eps_cq);
+  const double rms_kv = sqrt(skv / double(d.Hckv) + d.eps_ckv);
+  if constexpr (I8) {
+    float amax = 0.0f;
+    for (int n = tid; n < d.Hcq; n += 1024) {
+      const float c = float(double(bf2f(p.gamma_cq[n])) * y[n] / rms_q);
+      y[n] = c;
+      amax = fmaxf(amax, fabsf(c));
+    }
+    for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    __syncthreads();
+    if ((tid & 63) == 0) redf[tid >> 6] = amax;
+    __syncthreads();
+    amax = redf[0];
+    for (int w = 1; w < 16; ++w) amax = fmaxf(amax, redf[w]);
+    const float sc = amax / 127.0f;
+    int8_t* cq = reinterpret_cast<int8_t*>(p.cq) + int64_t(t) * d.Hcq;
+    for (int n = tid; n < d.Hcq; n += 1024) cq[n] = sc > 0.0f ? quant_code(float(y[n]), sc) : 0;
+    if (tid == 0) p.cq_scale[t] = sc;
+  } else {
+    uint16_t* cq = reinterpret_cast<uint16_t*>(p.cq) + int64_t(t) * d.Hcq;
+    for (int n = tid; n < d.Hcq; n += 1024)
+      cq[n] = f2bf(float(double(bf2f(p.gamma_cq[n])) * y[n] / rms_q));
+  }
+  const int64_t slot = p.cache_index[t];
+  if (slot < 0 || slot >= d.slots) return;
+  uint16_t* kv = p.kv_cache + slot * d.Hckv;
+  for (int n = tid; n < d.Hckv; n += 1024)
+    kv[n] = f2bf(float(double(bf2f(p.gamma_ckv[n])) * y[d.Hcq + n] / rms_kv));
+  const int h = d.Dr / 2;
+  const double* yr = y + d.Hcq + d.Hckv;
+  const uint16_t* cs = p.cos + int64_t(t) * d.Dr;
+  const uint16_t* sn = p.sin + int64_t(t) * d.Dr;
+  uint16_t* kr = p.kr_cache + slot * d.Dr;
+  for (int i = tid; i < h; i += 1024) {
+    const double a = yr[i], b = yr[i + h];
+    kr[i] = f2bf(float(a * bf2f(cs[i]) - b * bf2f(sn[i])));
+    kr[i + h] = f2bf(float(b * bf2f(cs[i + h]) + a * bf2f(sn[i + h])));
+  }
+}
 
-  // epilogue: the reduced tile goes to LDS (fp32), then out
-  float* E = reinterpret_cast<float*>(lds);   // [16*MT][65]
-  if (w == 0) {
-    const int g = lane >> 4, c = lane & 15;
+// A fragments from a bf16 tile in LDS (rows of ld elements).
+template <int MT>
+struct ALds {
+  static constexpr int NR = MT;
+  const uint16_t* base;
+  int ld;
+  __device__ __forceinline__ void load(uint4 (&r)[NR], int m0, int ka, int ke) const {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
+      r[mt] = ka < ke ? *reinterpret_cast<const uint4*>(base + (m0 + 16 * mt) * ld + ka)
+                      : make_uint4(0, 0, 0, 0);
+  }
+  __device__ __forceinline__ bf16x8 frag(const uint4 (&r)[NR], int mt, int) const {
+    return __builtin_bit_cast(bf16x8, r[mt]);
+  }
+};
+
+// LDS carve of K34p (bytes): partial accumulators of the up-projection waves,
+// the u tile (fp32), q^C (bf16) and the row maxima.
+struct K34Lds {
+  int red, u, qc, rmax, total, qc_ld, u_ld;
+};
+constexpr int kK34Waves = 12;
+constexpr int kK34LdsBytes = 152 * 1024;
+
+K34Lds k34_lds(int MT, int P, int D) {
+  K34Lds L;
+  const int BM = 16 * MT;
+  L.u_ld = P * 64;
+  L.qc_ld = D + 8;
+  L.red = 0;
+  L.u = L.red + kK34Waves * MT * 16 * 64 * 4;
+  L.qc = L.u + BM * L.u_ld * 4;
+  L.rmax = L.qc + ((BM * L.qc_ld * 2 + 15) / 16) * 16;
+  L.total = L.rmax + 8 * BM * 4;
+  return L;
+}
+
+// K34p: one block per head, 12 waves.  Phase A: u = c^Q [W^UQ | W^QR] for
+// the head's P windows, the waves splitting windows and k; the partial
+// accumulators are summed in LDS in a fixed order, the rope window goes
+// through RoPE to queryRopeOut and the nope windows are rounded to bf16 q^C
+// in LDS.  Phase B: q^N = q^C W^UK[h], one wave per 64-column window of
+// Hckv, stored as bf16 or as per-(token, head) int8 with its scale.
+template <bool I8, bool Q8, int MT, int DA>
+__global__ __launch_bounds__(64 * kK34Waves) void k34_packed(Dims d, Ptrs p, PackGeo pg, K34Lds L,
+                                                             int KP) {
+  using St = Stage<I8>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kK34LdsBytes];
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int P = pg.nope_w + 1, BM = 16 * MT;
+  uint32_t* red = reinterpret_cast<uint32_t*>(lds + L.red);
+  float* U = reinterpret_cast<float*>(lds + L.u);
+  uint16_t* QC = reinterpret_cast<uint16_t*>(lds + L.qc);
+  float* rmax = reinterpret_cast<float*>(lds + L.rmax);
+  const rsrc_t Wp = make_rsrc(p.packed, pg.total);
+
+  // phase A
+  {
+    typename St::Acc acc[MT][4];
+    const int pw = w % P, kpart = w / P;
+    if (kpart < KP) {
+      const int ns = kpart < pg.nst_cq ? (pg.nst_cq - kpart + KP - 1) / KP : 0;
+      const int64_t wbase = pg.off_uq + int64_t(h * P + pw) * pg.nst_cq * 4096;
+      const APlain<I8, MT> ap{make_rsrc(p.cq, int64_t(d.T) * d.Hcq * St::EB), uint32_t(d.Hcq * St::EB), d.T};
+      stream_packed<I8, MT, DA>(ap, 0, Wp, uint32_t(wbase), kpart, KP, ns, d.Hcq, acc);
+      uint32_t* r = red + w * (MT * 16 * 64);
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int ml = 16 * mt + 4 * g + i, col = 16 * ct + c;
-          float v;
-          if constexpr (I8)
-            v = (ml < d.T && col < width)
-                    ? static_cast<float>(acc[mt][ct][i]) * scale_s[ml] * p.sw_uq_qr[col0 + col]
-                    : 0.0f;
-          else
-            v = acc[mt][ct][i];
-          E[ml * 65 + col] = v;
-        }
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const auto e = acc[mt][ct][i];
+            r[((mt * 4 + ct) * 4 + i) * 64 + lane] = __builtin_bit_cast(uint32_t, e);
+          }
+    }
   }
   __syncthreads();
-  const int BM = 16 * MT;
-  if (!rope) {
-    for (int idx = tid; idx < BM * width; idx += 64 * NW) {
-      const int ml = idx / width, cc = idx % width;
-      if (ml < d.T) p.qc[(int64_t(ml) * d.N + h) * d.D + 64 * part + cc] = f2bf(E[ml * 65 + cc]);
+  // u = sum over k parts (in order), dequantised in int8 mode
+  for (int idx = tid; idx < BM * P * 64; idx += 64 * kK34Waves) {
+    const int m = idx / (P * 64), pc = idx % (P * 64), pw = pc / 64, col = pc % 64;
+    const int mt = m / 16, mr = m % 16, ct = col / 16;
+    const int e = ((mt * 4 + ct) * 4 + (mr % 4)) * 64 + (col % 16) + 16 * (mr / 4);
+    float v;
+    if constexpr (I8) {
+      int32_t a = 0;
+      for (int kp = 0; kp < KP; ++kp) a += static_cast<int32_t>(red[(kp * P + pw) * (MT * 16 * 64) + e]);
+      const int width = pw < pg.nope_w ? min(64, d.D - 64 * pw) : d.Dr;
+      const int gcol = h * (d.D + d.Dr) + (pw < pg.nope_w ? 64 * pw : d.D) + col;
+      v = (m < d.T && col < width) ? static_cast<float>(a) * p.cq_scale[m] * p.sw_uq_qr[gcol] : 0.0f;
+    } else {
+      v = 0.0f;
+      for (int kp = 0; kp < KP; ++kp) v += __builtin_bit_cast(float, red[(kp * P + pw) * (MT * 16 * 64) + e]);
     }
-  } else {
-    const int hf = d.Dr / 2;
-    for (int idx = tid; idx < BM * hf; idx += 64 * NW) {
-      const int ml = idx / hf, i = idx % hf;
-      if (ml >= d.T) continue;
-      const float a = E[ml * 65 + i], b = E[ml * 65 + i + hf];
-      const uint16_t* cs = p.cos + int64_t(ml) * d.Dr;
-      const uint16_t* sn = p.sin + int64_t(ml) * d.Dr;
-      uint16_t* o = p.qr_out + (int64_t(ml) * d.N + h) * d.Dr;
+    U[m * L.u_ld + pc] = v;
+  }
+  __syncthreads();
+  // q^C (bf16, LDS) and q^R (RoPE, global)
+  for (int idx = tid; idx < BM * d.D; idx += 64 * kK34Waves) {
+    const int m = idx / d.D, k = idx % d.D;
+    QC[m * L.qc_ld + k] = f2bf(U[m * L.u_ld + 64 * (k / 64) + k % 64]);
+  }
+  {
+    const int hf = d.Dr / 2, rc = 64 * pg.nope_w;
+    for (int idx = tid; idx < BM * hf; idx += 64 * kK34Waves) {
+      const int m = idx / hf, i = idx % hf;
+      if (m >= d.T) continue;
+      const float a = U[m * L.u_ld + rc + i], b = U[m * L.u_ld + rc + i + hf];
+      const uint16_t* cs = p.cos + int64_t(m) * d.Dr;
+      const uint16_t* sn = p.sin + int64_t(m) * d.Dr;
+      uint16_t* o = p.qr_out + (int64_t(m) * d.N + h) * d.Dr;
       o[i] = f2bf(a * bf2f(cs[i]) - b * bf2f(sn[i]));
       o[i + hf] = f2bf(b * bf2f(cs[i + hf]) + a * bf2f(sn[i + hf]));
     }
   }
-}
+  __syncthreads();
 
-// K4s, bf16 query: grid (head x 64-column window of Hckv); the block's waves
-// split the D reduction.
-template <int MT, int NW, int D>
-__global__ __launch_bounds__(64 * NW) void k4_stream(Dims d, Ptrs p, int windows) {
-  using St = Stage<false>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[StreamLds<false, MT, NW>::BYTES];
-  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = blockIdx.x / windows, win = blockIdx.x % windows;
-  const int c0 = 64 * win, width = min(64, d.Hckv - c0);
-  const int nst = (d.D + St::KS - 1) / St::KS;
-  const int ns = w < nst ? (nst - w + NW - 1) / NW : 0;
-  typename St::Acc acc[MT][4];
-  const APlain<false, MT> ap{make_rsrc(p.qc + int64_t(h) * d.D, (int64_t(d.T) * d.N - h) * d.D * 2),
-                             uint32_t(d.N * d.D * 2), d.T};
-  const rsrc_t Bw = make_rsrc(p.w_uk + int64_t(h) * d.D * d.Hckv, int64_t(d.D) * d.Hckv * 2);
-  stream_wave<false, MT, D>(ap, 0, Bw, uint32_t(d.Hckv * 2), uint32_t(c0 * 2), width * 2,
-                            w * St::KS, NW * St::KS, ns, d.D, acc, lds + w * St::BYTES);
-  reduce_waves<NW, MT>(acc, reinterpret_cast<uint32_t*>(lds));
-  // stage the tile through LDS as bf16, then 16-byte stores
-  uint16_t* E = reinterpret_cast<uint16_t*>(lds);  // [16*MT][64]
-  if (w == 0) {
-    const int g = lane >> 4, c = lane & 15;
+  // phase B
+  typename Stage<false>::Acc acc[MT][4];
+  const bool active = w < pg.uk_w;
+  const int c0 = 64 * w, width = active ? min(64, d.Hckv - c0) : 0;
+  if (active) {
+    const int64_t wbase = pg.off_uk + int64_t(h * pg.uk_w + w) * pg.nst_d * 4096;
+    const ALds<MT> ap{QC, L.qc_ld};
+    stream_packed<false, MT, 2>(ap, 0, Wp, uint32_t(wbase), 0, 1, pg.nst_d, d.D, acc);
+  }
+  if constexpr (!Q8) {
+    if (!active) return;
+    uint16_t* qo = static_cast<uint16_t*>(p.q_out);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) E[(16 * mt + 4 * g + i) * 64 + 16 * ct + c] = f2bf(acc[mt][ct][i]);
-  }
-  __syncthreads();
-  uint16_t* qo = static_cast<uint16_t*>(p.q_out);
-  for (int idx = tid; idx < 16 * MT * 8; idx += 64 * NW) {
-    const int ml = idx / 8, ch = idx % 8;
-    if (ml < d.T && 8 * ch < width)
-      *reinterpret_cast<uint4*>(qo + (int64_t(ml) * d.N + h) * d.Hckv + c0 + 8 * ch) =
-          *reinterpret_cast<const uint4*>(E + ml * 64 + 8 * ch);
-  }
-}
-
-// K4s, int8 query: grid (head); wave w owns the 64-column window w of Hckv
-// (Hckv <= 512) over the whole D reduction; the row maximum is taken across
-// the waves.
-template <int MT, int D>
-__global__ __launch_bounds__(512) void k4_stream_q8(Dims d, Ptrs p) {
-  using St = Stage<false>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[8 * St::BYTES];
-  __shared__ float rmax[8][16 * MT];
-  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = blockIdx.x;
-  const int c0 = 64 * w, width = max(0, min(64, d.Hckv - c0));
-  const int nst = (d.D + St::KS - 1) / St::KS;
-  const int ns = width > 0 ? nst : 0;
-  typename St::Acc acc[MT][4];
-  const APlain<false, MT> ap{make_rsrc(p.qc + int64_t(h) * d.D, (int64_t(d.T) * d.N - h) * d.D * 2),
-                             uint32_t(d.N * d.D * 2), d.T};
-  const rsrc_t Bw = make_rsrc(p.w_uk + int64_t(h) * d.D * d.Hckv, int64_t(d.D) * d.Hckv * 2);
-  stream_wave<false, MT, D>(ap, 0, Bw, uint32_t(d.Hckv * 2), uint32_t(max(0, c0) * 2), width * 2,
-                            0, St::KS, ns, d.D, acc, lds + w * St::BYTES);
-  const int g = lane >> 4, c = lane & 15;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float mx = 0.0f;
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-        if (16 * ct + c < width) mx = fmaxf(mx, fabsf(acc[mt][ct][i]));
-      for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-      if (c == 0) rmax[w][16 * mt + 4 * g + i] = mx;
-    }
-  __syncthreads();
-  int8_t* qo = static_cast<int8_t*>(p.q_out);
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ml = 16 * mt + 4 * g + i;
-      if (ml >= d.T) continue;
-      float amax = rmax[0][ml];
-      for (int ww = 1; ww < 8; ++ww) amax = fmaxf(amax, rmax[ww][ml]);
-      const float s = amax / 127.0f;
-#pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
         const int col = 16 * ct + c;
-        if (col < width)
-          qo[(int64_t(ml) * d.N + h) * d.Hckv + c0 + col] = s > 0.0f ? quant_code(acc[mt][ct][i], s) : 0;
+        if (col >= width) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = 16 * mt + 4 * g + i;
+          if (m < d.T) qo[(int64_t(m) * d.N + h) * d.Hckv + c0 + col] = f2bf(acc[mt][ct][i]);
+        }
       }
-      if (w == 0 && c == 0) p.q_scale[int64_t(ml) * d.N + h] = s;
-    }
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float mx = 0.0f;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+          if (16 * ct + c < width) mx = fmaxf(mx, fabsf(acc[mt][ct][i]));
+        for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        if (active && c == 0) rmax[w * BM + 16 * mt + 4 * g + i] = mx;
+      }
+    __syncthreads();
+    if (!active) return;
+    int8_t* qo = static_cast<int8_t*>(p.q_out);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * mt + 4 * g + i;
+        if (m >= d.T) continue;
+        float amax = rmax[m];
+        for (int ww = 1; ww < pg.uk_w; ++ww) amax = fmaxf(amax, rmax[ww * BM + m]);
+        const float sc = amax / 127.0f;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const int col = 16 * ct + c;
+          if (col < width)
+            qo[(int64_t(m) * d.N + h) * d.Hckv + c0 + col] = sc > 0.0f ? quant_code(acc[mt][ct][i], sc) : 0;
+        }
+        if (w == 0 && c == 0) p.q_scale[int64_t(m) * d.N + h] = sc;
+      }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1059,10 +946,12 @@ __global__ __launch_bounds__(512) void k4_stream_q8(Dims d, Ptrs p) {
 // ---------------------------------------------------------------------------
 // Token counts up to this run on the streaming kernels.
 constexpr int kStreamMaxT = 32;
-constexpr int kStreamWaves = 4;
 
 struct Plan {
-  bool stream;       // small-T streaming path
+  bool packed;       // small-T path on packed weights (set by the run)
+  int Sp, sps;       // packed K1: split count, stages per split
+  int kp34;          // packed K34: k parts per window
+  bool stream;       // T small enough for the packed kernels
   int mt1, S, kps;   // K1 rows per tile (16*mt1), split count, k per split
   int mt3;           // K3
   int ntw4, cs4;     // K4 column tiles per wave, column splits
@@ -1076,24 +965,18 @@ int mt_for(int64_t T, int cap) {
   return mt;
 }
 
-int column_tiles(const mla_prolog_desc& d) { return ceil_div(d.Hcq, 64) + ceil_div(d.Hckv + d.Dr, 64); }
-
 Plan make_plan(const mla_prolog_desc& d, int64_t T) {
   Plan pl;
   const bool i8 = d.in_dtype == MLA_INT8;
+  pl.packed = false;
   pl.stream = T <= kStreamMaxT;
-  if (pl.stream) {
-    // about two blocks of 8 waves per CU over the column tiles x splits
-    const int ks = i8 ? 64 : 32;
-    const int tiles = column_tiles(d);
-    const int nst = ceil_div(d.He, ks);
-    int S = std::max(1, std::min(nst, (512 + tiles / 2) / tiles));
-    pl.kps = ceil_div(nst, S) * ks;
-    pl.S = ceil_div(d.He, pl.kps);
-    pl.mt1 = T <= 16 ? 1 : 2;
-    pl.mt3 = pl.mt1;
-    pl.ntw4 = pl.cs4 = 0;
-    return pl;
+  {
+    const PackGeo g = pack_geo(d.He, d.Hcq, d.Hckv, d.N, d.D, d.Dr, i8);
+    const int ptiles = g.win_dq + g.win_kr;
+    int Sp = std::max(1, std::min(g.nst_he, (512 + ptiles / 2) / ptiles));
+    pl.sps = ceil_div(g.nst_he, Sp);
+    pl.Sp = ceil_div(g.nst_he, pl.sps);
+    pl.kp34 = std::max(1, kK34Waves / (g.nope_w + 1));
   }
   const int bk = i8 ? 128 : 64;
   pl.mt1 = mt_for(T, 16);
@@ -1119,7 +1002,7 @@ Plan make_plan(const mla_prolog_desc& d, int64_t T) {
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t part, cq, cq_scale, qc, y, ssq, amax, ticket, total;
+  size_t part, cq, cq_scale, qc, total;
 };
 
 Layout layout(const mla_prolog_desc& d) {
@@ -1130,19 +1013,14 @@ Layout layout(const mla_prolog_desc& d) {
   for (int64_t T = 1; T <= d.max_tokens; ++T) {
     const Plan pl = make_plan(d, T);
     part_rows = std::max<int64_t>(part_rows, int64_t(pl.S) * T);
+    if (pl.stream) part_rows = std::max<int64_t>(part_rows, int64_t(pl.Sp) * T);
     if (T >= 512) { part_rows = std::max<int64_t>(part_rows, d.max_tokens); break; }
   }
   L.part = 0;
   L.cq = align256(L.part + size_t(part_rows) * Ntot * 4);
   L.cq_scale = align256(L.cq + size_t(d.max_tokens) * d.Hcq * 2);
   L.qc = align256(L.cq_scale + size_t(d.max_tokens) * 4);
-  const int64_t Ts = std::min<int64_t>(d.max_tokens, kStreamMaxT);
-  const int tiles = column_tiles(d);
-  L.y = align256(L.qc + size_t(d.max_tokens) * d.N * d.D * 2);
-  L.ssq = align256(L.y + size_t(Ts) * Ntot * 4);
-  L.amax = align256(L.ssq + size_t(tiles) * Ts * 4);
-  L.ticket = align256(L.amax + size_t(tiles) * Ts * 4);
-  L.total = align256(L.ticket + size_t(tiles) * 4);
+  L.total = align256(L.qc + size_t(d.max_tokens) * d.N * d.D * 2);
   return L;
 }
 
@@ -1170,8 +1048,9 @@ mla_status check_desc(const mla_prolog_desc* d) {
   const int64_t vec_dims[5] = {d->He, d->Hcq, d->Hckv, d->D, d->Dr};
   for (int64_t v : vec_dims)
     if (v % 8) return MLA_ERR_UNSUPPORTED;
-  if (d->Dr > 64 || d->Hckv > 512 || d->D > 512 || d->Hcq > 8192 || d->He > 65536)
-    return MLA_ERR_UNSUPPORTED;
+  if (d->Dr > 64 || d->Hckv > 512 || d->D > 512 || d->He > 65536) return MLA_ERR_UNSUPPORTED;
+  // the norm kernel keeps one token's Hcq + Hckv + Dr values in 64 KB of LDS
+  if (d->Hcq + d->Hckv + d->Dr > 8192) return MLA_ERR_UNSUPPORTED;
   // int8 operands move in 16-byte (16-element) chunks that must not cross a
   // row or column-block end
   if (d->in_dtype == MLA_INT8 &&
@@ -1202,6 +1081,8 @@ mla_status check_tensors(const mla_prolog_desc* d, const mla_prolog_tensors* t, 
     if (d->in_dtype == MLA_BF16 && q) return MLA_ERR_PARAM_INVALID;
     if (q && !aligned4(q)) return MLA_ERR_PARAM_INVALID;
   }
+  if (t->packed_weights && (reinterpret_cast<uintptr_t>(t->packed_weights) & 255u))
+    return MLA_ERR_PARAM_INVALID;
   if (d->query_dtype == MLA_INT8 && !t->dequant_scale_q_nope) return MLA_ERR_NULLPTR;
   if (d->query_dtype == MLA_BF16 && t->dequant_scale_q_nope) return MLA_ERR_PARAM_INVALID;
   if (t->dequant_scale_q_nope && !aligned4(t->dequant_scale_q_nope)) return MLA_ERR_PARAM_INVALID;
@@ -1254,55 +1135,42 @@ void launch_k4(int ntw, dim3 grid, hipStream_t s, const Dims& d, const Ptrs& p) 
   }
 }
 
-template <bool I8, int MT>
-void stream_k1k3(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p) {
-  constexpr int D = I8 ? 2 : 4;
-  const int tiles_q = ceil_div(d.Hcq, 64), tiles_kr = ceil_div(d.Hckv + d.Dr, 64);
-  const int tiles = tiles_q + tiles_kr;
-  k1_stream<I8, MT, kStreamWaves, D><<<dim3(tiles * pl.S), 64 * kStreamWaves, 0, s>>>(
-      d, p, tiles_q, tiles, pl.S, pl.kps);
+bool k34_fits(const mla_prolog_desc& dd, int mt) {
+  const PackGeo g = pack_geo(dd.He, dd.Hcq, dd.Hckv, dd.N, dd.D, dd.Dr, dd.in_dtype == MLA_INT8);
+  return g.uk_w <= kK34Waves && k34_lds(mt, g.nope_w + 1, int(dd.D)).total <= kK34LdsBytes;
 }
 
-template <bool I8, int MT>
-void stream_k3(hipStream_t s, const Dims& d, const Ptrs& p) {
-  constexpr int D = I8 ? 2 : 3;
-  const int tiles_q = ceil_div(d.Hcq, 64), tiles_kr = ceil_div(d.Hckv + d.Dr, 64);
-  const int nope_tiles = ceil_div(d.D, 64);
-  const int head_blocks = d.N * (nope_tiles + 1);
-  const int kv_tpb = 4;
-  const int kv_blocks = ceil_div(d.T, kv_tpb);
-  k3_stream<I8, MT, kStreamWaves, D><<<dim3(head_blocks + kv_blocks), 64 * kStreamWaves, 0, s>>>(
-      d, p, nope_tiles, tiles_q, tiles_kr, head_blocks, kv_tpb);
-}
-
-template <int MT>
-void stream_k4(hipStream_t s, const Dims& d, const Ptrs& p, bool q8) {
-  if (q8) {
-    k4_stream_q8<MT, 2><<<dim3(d.N), 512, 0, s>>>(d, p);
-  } else {
-    const int windows = ceil_div(d.Hckv, 64);
-    k4_stream<MT, 4, 1><<<dim3(d.N * windows), 256, 0, s>>>(d, p, windows);
-  }
+// Small-T run on packed weights: K1p, K2, K34p.  Profiling marks: after
+// K1p, after K2, after K34p (which holds both the up-projection and the
+// W^UK product), and an empty last interval.
+template <bool I8, int MT, class Mark>
+void packed_launch(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g,
+                   bool q8, Mark& mark) {
+  constexpr int D1 = I8 ? 3 : 4;
+  const int tiles = g.win_dq + g.win_kr;
+  k1_packed<I8, MT, 4, D1><<<dim3(tiles * pl.Sp), 256, 0, s>>>(d, p, g, pl.Sp, pl.sps);
+  mark(1);
+  const size_t y_bytes = size_t(d.Hcq + d.Hckv + d.Dr) * sizeof(double);
+  k2_norm<I8><<<dim3(d.T), 1024, y_bytes, s>>>(d, p, pl.Sp);
+  mark(2);
+  const K34Lds L = k34_lds(MT, g.nope_w + 1, d.D);
+  if (q8) k34_packed<I8, true, MT, 3><<<dim3(d.N), 64 * kK34Waves, 0, s>>>(d, p, g, L, pl.kp34);
+  else k34_packed<I8, false, MT, 3><<<dim3(d.N), 64 * kK34Waves, 0, s>>>(d, p, g, L, pl.kp34);
+  mark(3);
+  mark(4);
 }
 
 template <class Mark>
-void launch_stream(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p, bool i8, bool q8,
-                   Mark& mark) {
+void launch_packed(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p,
+                   const mla_prolog_desc& dd, bool i8, bool q8, Mark& mark) {
+  const PackGeo g = pack_geo(dd.He, dd.Hcq, dd.Hckv, dd.N, dd.D, dd.Dr, i8);
   if (pl.mt1 == 1) {
-    if (i8) stream_k1k3<true, 1>(pl, s, d, p); else stream_k1k3<false, 1>(pl, s, d, p);
+    if (i8) packed_launch<true, 1>(pl, s, d, p, g, q8, mark);
+    else packed_launch<false, 1>(pl, s, d, p, g, q8, mark);
   } else {
-    if (i8) stream_k1k3<true, 2>(pl, s, d, p); else stream_k1k3<false, 2>(pl, s, d, p);
+    if (i8) packed_launch<true, 2>(pl, s, d, p, g, q8, mark);
+    else packed_launch<false, 2>(pl, s, d, p, g, q8, mark);
   }
-  mark(1);
-  mark(2);
-  if (pl.mt1 == 1) {
-    if (i8) stream_k3<true, 1>(s, d, p); else stream_k3<false, 1>(s, d, p);
-  } else {
-    if (i8) stream_k3<true, 2>(s, d, p); else stream_k3<false, 2>(s, d, p);
-  }
-  mark(3);
-  if (pl.mt1 == 1) stream_k4<1>(s, d, p, q8); else stream_k4<2>(s, d, p, q8);
-  mark(4);
 }
 
 }  // namespace
@@ -1319,6 +1187,45 @@ mla_status mla_prolog_validate(const mla_prolog_desc* desc, const mla_prolog_ten
 size_t mla_prolog_workspace_bytes(const mla_prolog_desc* desc) {
   if (check_desc(desc) != MLA_OK) return 0;
   return layout(*desc).total;
+}
+
+size_t mla_prolog_packed_weights_bytes(const mla_prolog_desc* desc) {
+  if (check_desc(desc) != MLA_OK) return 0;
+  return size_t(pack_geo(desc->He, desc->Hcq, desc->Hckv, desc->N, desc->D, desc->Dr,
+                         desc->in_dtype == MLA_INT8).total);
+}
+
+mla_status mla_prolog_pack_weights(mla_prolog_t h, const mla_prolog_tensors* t, void* packed,
+                                   void* stream) {
+  if (!h || !t || !packed) return MLA_ERR_NULLPTR;
+  const mla_prolog_desc& dd = h->desc;
+  const void* w[4] = {t->weight_dq, t->weight_uq_qr, t->weight_uk, t->weight_dkv_kr};
+  for (const void* q : w)
+    if (!q) return MLA_ERR_NULLPTR;
+  for (const void* q : w)
+    if (!aligned16(q)) return MLA_ERR_PARAM_INVALID;
+  if (reinterpret_cast<uintptr_t>(packed) & 255u) return MLA_ERR_PARAM_INVALID;
+  const PackGeo g = pack_geo(dd.He, dd.Hcq, dd.Hckv, dd.N, dd.D, dd.Dr, dd.in_dtype == MLA_INT8);
+  if (g.total >= int64_t(kOOB)) return MLA_ERR_UNSUPPORTED;
+  int prev = 0;
+  if (hipGetDevice(&prev) != hipSuccess) return MLA_ERR_RUNTIME;
+  if (prev != dd.device && hipSetDevice(dd.device) != hipSuccess) return MLA_ERR_RUNTIME;
+  (void)hipGetLastError();
+  Dims d;
+  d.T = 0; d.He = int(dd.He); d.Hcq = int(dd.Hcq); d.Hckv = int(dd.Hckv); d.N = int(dd.N);
+  d.D = int(dd.D); d.Dr = int(dd.Dr); d.slots = 0; d.eps_cq = d.eps_ckv = 0.0;
+  Ptrs p;
+  std::memset(&p, 0, sizeof p);
+  p.w_dq = static_cast<const uint8_t*>(t->weight_dq);
+  p.w_uq_qr = static_cast<const uint8_t*>(t->weight_uq_qr);
+  p.w_uk = static_cast<const uint16_t*>(t->weight_uk);
+  p.w_dkv_kr = static_cast<const uint8_t*>(t->weight_dkv_kr);
+  const int64_t chunks = g.total / 16;
+  k_pack<<<dim3(unsigned((chunks + 255) / 256)), 256, 0, static_cast<hipStream_t>(stream)>>>(
+      d, p, g, dd.in_dtype == MLA_INT8, static_cast<uint8_t*>(packed));
+  const hipError_t e = hipGetLastError();
+  if (prev != dd.device) (void)hipSetDevice(prev);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_RUNTIME;
 }
 
 mla_status mla_prolog_create(const mla_prolog_desc* desc, mla_prolog_t* out) {
@@ -1341,14 +1248,7 @@ mla_status mla_prolog_create(const mla_prolog_desc* desc, mla_prolog_t* out) {
     (void)hipSetDevice(prev);
     return MLA_ERR_RUNTIME;
   }
-  // split-K arrival counters start at zero; every run leaves them at zero
-  if (hipMemset(h->ws + h->lay.ticket, 0, h->lay.total - h->lay.ticket) != hipSuccess ||
-      hipDeviceSynchronize() != hipSuccess) {
-    (void)hipFree(h->ws);
-    delete h;
-    (void)hipSetDevice(prev);
-    return MLA_ERR_RUNTIME;
-  }
+
   (void)hipSetDevice(prev);
   *out = h;
   return MLA_OK;
@@ -1371,7 +1271,7 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   d.T = int(T); d.He = int(dd.He); d.Hcq = int(dd.Hcq); d.Hckv = int(dd.Hckv); d.N = int(dd.N);
   d.D = int(dd.D); d.Dr = int(dd.Dr);
   d.slots = dd.block_num * dd.block_size;
-  d.eps_cq = float(dd.eps_cq); d.eps_ckv = float(dd.eps_ckv);
+  d.eps_cq = dd.eps_cq; d.eps_ckv = dd.eps_ckv;
   Ptrs p;
   p.x = static_cast<const uint8_t*>(t->token_x);
   p.w_dq = static_cast<const uint8_t*>(t->weight_dq);
@@ -1394,10 +1294,6 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   p.cq = h->ws + h->lay.cq;
   p.cq_scale = reinterpret_cast<float*>(h->ws + h->lay.cq_scale);
   p.qc = reinterpret_cast<uint16_t*>(h->ws + h->lay.qc);
-  p.y = reinterpret_cast<float*>(h->ws + h->lay.y);
-  p.ssq = reinterpret_cast<float*>(h->ws + h->lay.ssq);
-  p.amax = reinterpret_cast<float*>(h->ws + h->lay.amax);
-  p.ticket = reinterpret_cast<unsigned*>(h->ws + h->lay.ticket);
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   hipEvent_t* ev = nullptr;
@@ -1409,8 +1305,9 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
     if (ev) (void)hipEventRecord(ev[i], s);
   };
   mark(0);
-  if (pl.stream) {
-    launch_stream(pl, s, d, p, i8, q8, mark);
+  p.packed = static_cast<const uint8_t*>(t->packed_weights);
+  if (pl.stream && p.packed && k34_fits(dd, pl.mt1)) {
+    launch_packed(pl, s, d, p, dd, i8, q8, mark);
     const hipError_t e = hipGetLastError();
     if (prev != dd.device) (void)hipSetDevice(prev);
     return e == hipSuccess ? MLA_OK : MLA_ERR_RUNTIME;
@@ -1422,9 +1319,9 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   else launch_k1<false>(pl.mt1, g1, s, d, p, tiles_q, pl.kps);
   mark(1);
 
-  const size_t y_bytes = size_t(d.Hcq + d.Hckv + d.Dr) * sizeof(float);
-  if (i8) k_norm_rope_cache<true><<<dim3(d.T), kThreads, y_bytes, s>>>(d, p, pl.S);
-  else k_norm_rope_cache<false><<<dim3(d.T), kThreads, y_bytes, s>>>(d, p, pl.S);
+  const size_t y_bytes = size_t(d.Hcq + d.Hckv + d.Dr) * sizeof(double);
+  if (i8) k2_norm<true><<<dim3(d.T), 1024, y_bytes, s>>>(d, p, pl.S);
+  else k2_norm<false><<<dim3(d.T), 1024, y_bytes, s>>>(d, p, pl.S);
   mark(2);
 
   const int nope_tiles = ceil_div(d.D, 64);

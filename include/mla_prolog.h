@@ -100,6 +100,12 @@ typedef struct {
  *   query_out        (T, N, Hckv)       bf16, or int8 when query_dtype is INT8
  *   query_rope_out   (T, N, Dr)         bf16
  *   dequant_scale_q_nope (T, N)         fp32 when query_dtype is INT8, else NULL
+ *   packed_weights                      optional (NULL = none): the output of
+ *                                       mla_prolog_pack_weights for these
+ *                                       four weights, 256-byte aligned.  When
+ *                                       given, small-T runs (T <= 32) stream
+ *                                       the weights from it; the row-major
+ *                                       weights stay required.
  * Outputs must not alias inputs.
  */
 typedef struct {
@@ -122,6 +128,7 @@ typedef struct {
   void* query_out;
   void* query_rope_out;
   float* dequant_scale_q_nope;
+  const void* packed_weights; /* optional: the four weights in the library's packed layout */
 } mla_prolog_tensors;
 
 typedef struct mla_prolog* mla_prolog_t;
@@ -134,6 +141,21 @@ mla_status mla_prolog_validate(const mla_prolog_desc* desc, const mla_prolog_ten
 
 /* Bytes of device workspace a handle for desc owns (0 if desc is invalid). */
 size_t mla_prolog_workspace_bytes(const mla_prolog_desc* desc);
+
+/* Bytes of the packed-weight buffer for desc (0 if desc is invalid). */
+size_t mla_prolog_packed_weights_bytes(const mla_prolog_desc* desc);
+
+/* Writes weight_dq, weight_uq_qr, weight_uk and weight_dkv_kr of tensors
+ * (row-major, as for mla_prolog_run) into packed, a caller-owned device
+ * buffer of mla_prolog_packed_weights_bytes bytes, 256-byte aligned, in the
+ * library's packed layout: per matrix, windows of 64 columns, each stored as
+ * its k-stages (32 bf16 or 64 int8 rows, 4 KB) in MFMA operand order, so that
+ * a run streams every window as one contiguous region.  Like the operator
+ * page's weights, which its API takes in a pre-tiled format, this is a
+ * one-time conversion per weight set.  Stream-ordered; the other tensor
+ * fields are ignored. */
+mla_status mla_prolog_pack_weights(mla_prolog_t handle, const mla_prolog_tensors* tensors,
+                                   void* packed, void* stream);
 
 /* Validates desc, allocates the handle and its device workspace on
  * desc->device (the caller's current device is restored).  On error *out is

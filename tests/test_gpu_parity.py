@@ -27,12 +27,18 @@ def say(msg):
     sys.stdout.flush()
 
 
-def run_gpu(inp, query_int8=None, max_tokens=None, T=None, repeat=1):
-    """Upload, run through the C ABI, download.  Returns host arrays."""
+def run_gpu(inp, query_int8=None, max_tokens=None, T=None, repeat=1, packed=False):
+    """Upload, run through the C ABI, download.  Returns host arrays.  With
+    ``packed`` the weights are first converted by mla_prolog_pack_weights
+    and the run reads the packed copy."""
     T = int(inp["T"]) if T is None else T
     t = dev.upload(inp, query_int8=query_int8)
     desc = mla.make_desc(**dev.desc_args(inp, max_tokens=max_tokens, query_int8=query_int8))
     with mla.MlaProlog(desc) as h:
+        if packed:
+            buf = torch.empty(mla.packed_weights_bytes(desc), dtype=torch.uint8, device="cuda")
+            h.pack_weights(t, buf)
+            t["packed_weights"] = buf
         for _ in range(repeat):
             h.run(t, T)
         torch.cuda.synchronize()
@@ -40,11 +46,11 @@ def run_gpu(inp, query_int8=None, max_tokens=None, T=None, repeat=1):
             if k in ("query_out", "query_rope_out", "dequant_scale_q_nope", "kv_cache", "kr_cache")}
 
 
-def full_check(inp, query_int8=None, rows=None):
+def full_check(inp, query_int8=None, rows=None, packed=False):
     q8 = bool(inp["quant"]) if query_int8 is None else bool(query_int8)
     rows = np.arange(int(inp["T"])) if rows is None else np.asarray(rows)
-    say(f"case {inp['workload']} T={inp['T']} dims={inp['dims']} q8={q8} rows={len(rows)}")
-    got = run_gpu(inp, query_int8=query_int8)
+    say(f"case {inp['workload']} T={inp['T']} dims={inp['dims']} q8={q8} rows={len(rows)} packed={packed}")
+    got = run_gpu(inp, query_int8=query_int8, packed=packed)
     ref = oracle.run(inp, tokens=rows, query_int8=query_int8, caches=False)
     check_queries(got, ref, rows, q8)
     check_caches(inp, got["kv_cache"], got["kr_cache"], ref, rows)
@@ -155,3 +161,79 @@ def test_full_size_sampled(name):
     T = int(inp["T"])
     rows = np.arange(T) if T <= 32 else sample_rows(T)
     full_check(inp, rows=rows)
+
+
+# ---- packed weights -----------------------------------------------------------
+def packed_reference(inp):
+    """The packed layout restated with numpy: per matrix, 64-column windows,
+    each as k-stages of 4 column tiles x 64 lanes x 16 bytes; lane l of tile
+    ct holds rows KL*(l//16)+i of column 16*ct + l%16."""
+    d = inp["dims"]
+    i8 = bool(inp["quant"])
+
+    def windows_of(W, cols, K, kl):
+        out = []
+        ks = 4 * kl
+        nst = -(-K // ks)
+        for col0, width in cols:
+            blk = np.zeros((nst * ks, 64), dtype=W.dtype)
+            blk[:K, :width] = W[:, col0:col0 + width]
+            st = blk.reshape(nst, 4, kl, 64)                    # stage, lane group, i, column
+            st = st.reshape(nst, 4, kl, 4, 16)                  # .., column tile, column in tile
+            st = st.transpose(0, 3, 1, 4, 2)                    # stage, ct, group, col, i
+            out.append(np.ascontiguousarray(st).view(np.uint8).ravel())
+        return out
+
+    kl = 16 if i8 else 8
+    parts = []
+    wdq = np.asarray(inp["weight_dq"])
+    parts += windows_of(wdq, [(c, min(64, d.Hcq - c)) for c in range(0, d.Hcq, 64)], d.He, kl)
+    wkr = np.asarray(inp["weight_dkv_kr"])
+    nkr = d.Hckv + d.Dr
+    parts += windows_of(wkr, [(c, min(64, nkr - c)) for c in range(0, nkr, 64)], d.He, kl)
+    wuq = np.asarray(inp["weight_uq_qr"])
+    cols = []
+    for h in range(d.N):
+        base = h * (d.D + d.Dr)
+        cols += [(base + c, min(64, d.D - c)) for c in range(0, d.D, 64)] + [(base + d.D, d.Dr)]
+    parts += windows_of(wuq, cols, d.Hcq, kl)
+    wuk = np.asarray(inp["weight_uk"])
+    for h in range(d.N):
+        parts += windows_of(wuk[h], [(c, min(64, d.Hckv - c)) for c in range(0, d.Hckv, 64)], d.D, 8)
+    return np.concatenate(parts)
+
+
+@pytest.mark.parametrize("name", ["tiny_t4", "ragged_t5_wide"])
+def test_packed_layout(name):
+    inp = synth.make_inputs(SMALL[name])
+    say(f"case pack layout {name}")
+    t = dev.upload(inp)
+    desc = mla.make_desc(**dev.desc_args(inp))
+    with mla.MlaProlog(desc) as h:
+        buf = torch.zeros(mla.packed_weights_bytes(desc), dtype=torch.uint8, device="cuda")
+        h.pack_weights(t, buf)
+        torch.cuda.synchronize()
+    ref = packed_reference(inp)
+    assert buf.numel() == ref.size
+    assert np.array_equal(buf.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("name", ["tiny_t4", "ragged_t5_wide"])
+def test_small_bf16_packed(name):
+    full_check(synth.make_inputs(SMALL[name]), packed=True)
+
+
+def test_small_int8_packed():
+    full_check(synth.make_inputs(INT8_SMALL["q8_t9"]), packed=True)
+    full_check(synth.make_inputs(INT8_SMALL["q8_t9"]), query_int8=False, packed=True)
+
+
+def test_full_size_decode_packed():
+    inp = synth.make_inputs(synth.workload("decode_t32"))
+    full_check(inp, packed=True)
+
+
+def test_int8_decode_t32_packed():
+    # the int8 decode workload at 32 tokens runs on the packed small-T kernels
+    inp = synth.make_inputs(synth.workload("int8_decode_t128"), T=32)
+    full_check(inp, packed=True)
