@@ -762,183 +762,153 @@ __global__ __launch_bounds__(1024) void k2_norm(Dims d, Ptrs p, int S) {
   }
 }
 
-// A fragments from a bf16 tile in LDS (rows of ld elements).
-template <int MT>
-struct ALds {
-  static constexpr int NR = MT;
-  const uint16_t* base;
-  int ld;
-  __device__ __forceinline__ void load(uint4 (&r)[NR], int m0, int ka, int ke) const {
+// K3p: grid (head windows of W^UqQr: per head the nope windows, then the rope
+// window), NW waves splitting the Hcq stages of one window; the waves are
+// summed in LDS, then the nope columns are rounded to bf16 q^C (workspace)
+// and the rope columns go through RoPE to queryRopeOut.
+template <bool I8, int MT, int NW, int D>
+__global__ __launch_bounds__(64 * NW) void k3_packed(Dims d, Ptrs p, PackGeo pg) {
+  using St = Stage<I8>;
+  constexpr int RED = (NW / 2) * MT * 16 * 64 * 4, EPI = 16 * MT * 65 * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[RED > EPI ? RED : EPI];
+  const int P = pg.nope_w + 1;
+  const int h = blockIdx.x / P, part = blockIdx.x % P;
+  const bool rope = part == pg.nope_w;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col0 = h * (d.D + d.Dr) + (rope ? d.D : 64 * part);
+  const int width = rope ? d.Dr : min(64, d.D - 64 * part);
+  const int ns = w < pg.nst_cq ? (pg.nst_cq - w + NW - 1) / NW : 0;
+  typename St::Acc acc[MT][4];
+  const APlain<I8, MT> ap{make_rsrc(p.cq, int64_t(d.T) * d.Hcq * St::EB), uint32_t(d.Hcq * St::EB), d.T};
+  const int64_t wbase = pg.off_uq + int64_t(blockIdx.x) * pg.nst_cq * 4096;
+  stream_packed<I8, MT, D>(ap, 0, make_rsrc(p.packed, pg.total), uint32_t(wbase), w, NW, ns, d.Hcq, acc);
+  reduce_waves<NW, MT>(acc, reinterpret_cast<uint32_t*>(lds));
+  float* E = reinterpret_cast<float*>(lds);   // [16*MT][65]
+  if (w == 0) {
+    const int g = lane >> 4, c = lane & 15;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-      r[mt] = ka < ke ? *reinterpret_cast<const uint4*>(base + (m0 + 16 * mt) * ld + ka)
-                      : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ml = 16 * mt + 4 * g + i, col = 16 * ct + c;
+          float v;
+          if constexpr (I8)
+            v = (ml < d.T && col < width)
+                    ? static_cast<float>(acc[mt][ct][i]) * p.cq_scale[ml] * p.sw_uq_qr[col0 + col]
+                    : 0.0f;
+          else
+            v = acc[mt][ct][i];
+          E[ml * 65 + col] = v;
+        }
   }
-  __device__ __forceinline__ bf16x8 frag(const uint4 (&r)[NR], int mt, int) const {
-    return __builtin_bit_cast(bf16x8, r[mt]);
-  }
-};
-
-// LDS carve of K34p (bytes): partial accumulators of the up-projection waves,
-// the u tile (fp32), q^C (bf16) and the row maxima.
-struct K34Lds {
-  int red, u, qc, rmax, total, qc_ld, u_ld;
-};
-constexpr int kK34Waves = 12;
-constexpr int kK34LdsBytes = 152 * 1024;
-
-K34Lds k34_lds(int MT, int P, int D) {
-  K34Lds L;
+  __syncthreads();
   const int BM = 16 * MT;
-  L.u_ld = P * 64;
-  L.qc_ld = D + 8;
-  L.red = 0;
-  L.u = L.red + kK34Waves * MT * 16 * 64 * 4;
-  L.qc = L.u + BM * L.u_ld * 4;
-  L.rmax = L.qc + ((BM * L.qc_ld * 2 + 15) / 16) * 16;
-  L.total = L.rmax + 8 * BM * 4;
-  return L;
-}
-
-// K34p: one block per head, 12 waves.  Phase A: u = c^Q [W^UQ | W^QR] for
-// the head's P windows, the waves splitting windows and k; the partial
-// accumulators are summed in LDS in a fixed order, the rope window goes
-// through RoPE to queryRopeOut and the nope windows are rounded to bf16 q^C
-// in LDS.  Phase B: q^N = q^C W^UK[h], one wave per 64-column window of
-// Hckv, stored as bf16 or as per-(token, head) int8 with its scale.
-template <bool I8, bool Q8, int MT, int DA>
-__global__ __launch_bounds__(64 * kK34Waves) void k34_packed(Dims d, Ptrs p, PackGeo pg, K34Lds L,
-                                                             int KP) {
-  using St = Stage<I8>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kK34LdsBytes];
-  const int h = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 4, c = lane & 15;
-  const int P = pg.nope_w + 1, BM = 16 * MT;
-  uint32_t* red = reinterpret_cast<uint32_t*>(lds + L.red);
-  float* U = reinterpret_cast<float*>(lds + L.u);
-  uint16_t* QC = reinterpret_cast<uint16_t*>(lds + L.qc);
-  float* rmax = reinterpret_cast<float*>(lds + L.rmax);
-  const rsrc_t Wp = make_rsrc(p.packed, pg.total);
-
-  // phase A
-  {
-    typename St::Acc acc[MT][4];
-    const int pw = w % P, kpart = w / P;
-    if (kpart < KP) {
-      const int ns = kpart < pg.nst_cq ? (pg.nst_cq - kpart + KP - 1) / KP : 0;
-      const int64_t wbase = pg.off_uq + int64_t(h * P + pw) * pg.nst_cq * 4096;
-      const APlain<I8, MT> ap{make_rsrc(p.cq, int64_t(d.T) * d.Hcq * St::EB), uint32_t(d.Hcq * St::EB), d.T};
-      stream_packed<I8, MT, DA>(ap, 0, Wp, uint32_t(wbase), kpart, KP, ns, d.Hcq, acc);
-      uint32_t* r = red + w * (MT * 16 * 64);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const auto e = acc[mt][ct][i];
-            r[((mt * 4 + ct) * 4 + i) * 64 + lane] = __builtin_bit_cast(uint32_t, e);
-          }
+  if (!rope) {
+    for (int idx = tid; idx < BM * width; idx += 64 * NW) {
+      const int ml = idx / width, cc = idx % width;
+      if (ml < d.T) p.qc[(int64_t(ml) * d.N + h) * d.D + 64 * part + cc] = f2bf(E[ml * 65 + cc]);
     }
-  }
-  __syncthreads();
-  // u = sum over k parts (in order), dequantised in int8 mode
-  for (int idx = tid; idx < BM * P * 64; idx += 64 * kK34Waves) {
-    const int m = idx / (P * 64), pc = idx % (P * 64), pw = pc / 64, col = pc % 64;
-    const int mt = m / 16, mr = m % 16, ct = col / 16;
-    const int e = ((mt * 4 + ct) * 4 + (mr % 4)) * 64 + (col % 16) + 16 * (mr / 4);
-    float v;
-    if constexpr (I8) {
-      int32_t a = 0;
-      for (int kp = 0; kp < KP; ++kp) a += static_cast<int32_t>(red[(kp * P + pw) * (MT * 16 * 64) + e]);
-      const int width = pw < pg.nope_w ? min(64, d.D - 64 * pw) : d.Dr;
-      const int gcol = h * (d.D + d.Dr) + (pw < pg.nope_w ? 64 * pw : d.D) + col;
-      v = (m < d.T && col < width) ? static_cast<float>(a) * p.cq_scale[m] * p.sw_uq_qr[gcol] : 0.0f;
-    } else {
-      v = 0.0f;
-      for (int kp = 0; kp < KP; ++kp) v += __builtin_bit_cast(float, red[(kp * P + pw) * (MT * 16 * 64) + e]);
-    }
-    U[m * L.u_ld + pc] = v;
-  }
-  __syncthreads();
-  // q^C (bf16, LDS) and q^R (RoPE, global)
-  for (int idx = tid; idx < BM * d.D; idx += 64 * kK34Waves) {
-    const int m = idx / d.D, k = idx % d.D;
-    QC[m * L.qc_ld + k] = f2bf(U[m * L.u_ld + 64 * (k / 64) + k % 64]);
-  }
-  {
-    const int hf = d.Dr / 2, rc = 64 * pg.nope_w;
-    for (int idx = tid; idx < BM * hf; idx += 64 * kK34Waves) {
-      const int m = idx / hf, i = idx % hf;
-      if (m >= d.T) continue;
-      const float a = U[m * L.u_ld + rc + i], b = U[m * L.u_ld + rc + i + hf];
-      const uint16_t* cs = p.cos + int64_t(m) * d.Dr;
-      const uint16_t* sn = p.sin + int64_t(m) * d.Dr;
-      uint16_t* o = p.qr_out + (int64_t(m) * d.N + h) * d.Dr;
+  } else {
+    const int hf = d.Dr / 2;
+    for (int idx = tid; idx < BM * hf; idx += 64 * NW) {
+      const int ml = idx / hf, i = idx % hf;
+      if (ml >= d.T) continue;
+      const float a = E[ml * 65 + i], b = E[ml * 65 + i + hf];
+      const uint16_t* cs = p.cos + int64_t(ml) * d.Dr;
+      const uint16_t* sn = p.sin + int64_t(ml) * d.Dr;
+      uint16_t* o = p.qr_out + (int64_t(ml) * d.N + h) * d.Dr;
       o[i] = f2bf(a * bf2f(cs[i]) - b * bf2f(sn[i]));
       o[i + hf] = f2bf(b * bf2f(cs[i + hf]) + a * bf2f(sn[i + hf]));
     }
   }
-  __syncthreads();
+}
 
-  // phase B
-  typename Stage<false>::Acc acc[MT][4];
-  const bool active = w < pg.uk_w;
-  const int c0 = 64 * w, width = active ? min(64, d.Hckv - c0) : 0;
-  if (active) {
-    const int64_t wbase = pg.off_uk + int64_t(h * pg.uk_w + w) * pg.nst_d * 4096;
-    const ALds<MT> ap{QC, L.qc_ld};
-    stream_packed<false, MT, 2>(ap, 0, Wp, uint32_t(wbase), 0, 1, pg.nst_d, d.D, acc);
-  }
-  if constexpr (!Q8) {
-    if (!active) return;
-    uint16_t* qo = static_cast<uint16_t*>(p.q_out);
+// K4p, bf16 query: grid (head x 64-column window of Hckv); NW waves split
+// the D stages; the tile is staged through LDS for 16-byte stores.
+template <int MT, int NW, int D>
+__global__ __launch_bounds__(64 * NW) void k4_packed(Dims d, Ptrs p, PackGeo pg) {
+  using St = Stage<false>;
+  constexpr int RED = (NW / 2) * MT * 16 * 64 * 4, EPI = 16 * MT * 64 * 2;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[RED > EPI ? RED : EPI];
+  const int h = blockIdx.x / pg.uk_w, win = blockIdx.x % pg.uk_w;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c0 = 64 * win, width = min(64, d.Hckv - c0);
+  const int ns = w < pg.nst_d ? (pg.nst_d - w + NW - 1) / NW : 0;
+  typename St::Acc acc[MT][4];
+  const APlain<false, MT> ap{make_rsrc(p.qc + int64_t(h) * d.D, (int64_t(d.T) * d.N - h) * d.D * 2),
+                             uint32_t(d.N * d.D * 2), d.T};
+  const int64_t wbase = pg.off_uk + int64_t(blockIdx.x) * pg.nst_d * 4096;
+  stream_packed<false, MT, D>(ap, 0, make_rsrc(p.packed, pg.total), uint32_t(wbase), w, NW, ns, d.D, acc);
+  reduce_waves<NW, MT>(acc, reinterpret_cast<uint32_t*>(lds));
+  uint16_t* E = reinterpret_cast<uint16_t*>(lds);  // [16*MT][64]
+  if (w == 0) {
+    const int g = lane >> 4, c = lane & 15;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) E[(16 * mt + 4 * g + i) * 64 + 16 * ct + c] = f2bf(acc[mt][ct][i]);
+  }
+  __syncthreads();
+  uint16_t* qo = static_cast<uint16_t*>(p.q_out);
+  for (int idx = tid; idx < 16 * MT * 8; idx += 64 * NW) {
+    const int ml = idx / 8, ch = idx % 8;
+    if (ml < d.T && 8 * ch < width)
+      *reinterpret_cast<uint4*>(qo + (int64_t(ml) * d.N + h) * d.Hckv + c0 + 8 * ch) =
+          *reinterpret_cast<const uint4*>(E + ml * 64 + 8 * ch);
+  }
+}
+
+// K4p, int8 query: grid (head); wave w owns the 64-column window w of Hckv
+// over the whole D reduction; the row maximum is taken across the waves.
+template <int MT, int D>
+__global__ __launch_bounds__(512) void k4_packed_q8(Dims d, Ptrs p, PackGeo pg) {
+  __shared__ float rmax[8][16 * MT];
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const bool active = w < pg.uk_w;
+  const int c0 = 64 * w, width = active ? min(64, d.Hckv - c0) : 0;
+  typename Stage<false>::Acc acc[MT][4];
+  const APlain<false, MT> ap{make_rsrc(p.qc + int64_t(h) * d.D, (int64_t(d.T) * d.N - h) * d.D * 2),
+                             uint32_t(d.N * d.D * 2), d.T};
+  const int64_t wbase = pg.off_uk + int64_t(h * pg.uk_w + (active ? w : 0)) * pg.nst_d * 4096;
+  stream_packed<false, MT, D>(ap, 0, make_rsrc(p.packed, pg.total), uint32_t(wbase), 0, 1,
+                              active ? pg.nst_d : 0, d.D, acc);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float mx = 0.0f;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        if (16 * ct + c < width) mx = fmaxf(mx, fabsf(acc[mt][ct][i]));
+      for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+      if (c == 0) rmax[w][16 * mt + 4 * g + i] = mx;
+    }
+  __syncthreads();
+  if (!active) return;
+  int8_t* qo = static_cast<int8_t*>(p.q_out);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ml = 16 * mt + 4 * g + i;
+      if (ml >= d.T) continue;
+      float amax = rmax[0][ml];
+      for (int ww = 1; ww < pg.uk_w; ++ww) amax = fmaxf(amax, rmax[ww][ml]);
+      const float sc = amax / 127.0f;
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
         const int col = 16 * ct + c;
-        if (col >= width) continue;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = 16 * mt + 4 * g + i;
-          if (m < d.T) qo[(int64_t(m) * d.N + h) * d.Hckv + c0 + col] = f2bf(acc[mt][ct][i]);
-        }
+        if (col < width)
+          qo[(int64_t(ml) * d.N + h) * d.Hckv + c0 + col] = sc > 0.0f ? quant_code(acc[mt][ct][i], sc) : 0;
       }
-  } else {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float mx = 0.0f;
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-          if (16 * ct + c < width) mx = fmaxf(mx, fabsf(acc[mt][ct][i]));
-        for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-        if (active && c == 0) rmax[w * BM + 16 * mt + 4 * g + i] = mx;
-      }
-    __syncthreads();
-    if (!active) return;
-    int8_t* qo = static_cast<int8_t*>(p.q_out);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 16 * mt + 4 * g + i;
-        if (m >= d.T) continue;
-        float amax = rmax[m];
-        for (int ww = 1; ww < pg.uk_w; ++ww) amax = fmaxf(amax, rmax[ww * BM + m]);
-        const float sc = amax / 127.0f;
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          const int col = 16 * ct + c;
-          if (col < width)
-            qo[(int64_t(m) * d.N + h) * d.Hckv + c0 + col] = sc > 0.0f ? quant_code(acc[mt][ct][i], sc) : 0;
-        }
-        if (w == 0 && c == 0) p.q_scale[int64_t(m) * d.N + h] = sc;
-      }
-  }
+      if (w == 0 && c == 0) p.q_scale[int64_t(ml) * d.N + h] = sc;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -950,7 +920,6 @@ constexpr int kStreamMaxT = 32;
 struct Plan {
   bool packed;       // small-T path on packed weights (set by the run)
   int Sp, sps;       // packed K1: split count, stages per split
-  int kp34;          // packed K34: k parts per window
   bool stream;       // T small enough for the packed kernels
   int mt1, S, kps;   // K1 rows per tile (16*mt1), split count, k per split
   int mt3;           // K3
@@ -976,7 +945,6 @@ Plan make_plan(const mla_prolog_desc& d, int64_t T) {
     int Sp = std::max(1, std::min(g.nst_he, (512 + ptiles / 2) / ptiles));
     pl.sps = ceil_div(g.nst_he, Sp);
     pl.Sp = ceil_div(g.nst_he, pl.sps);
-    pl.kp34 = std::max(1, kK34Waves / (g.nope_w + 1));
   }
   const int bk = i8 ? 128 : 64;
   pl.mt1 = mt_for(T, 16);
@@ -1135,28 +1103,25 @@ void launch_k4(int ntw, dim3 grid, hipStream_t s, const Dims& d, const Ptrs& p) 
   }
 }
 
-bool k34_fits(const mla_prolog_desc& dd, int mt) {
-  const PackGeo g = pack_geo(dd.He, dd.Hcq, dd.Hckv, dd.N, dd.D, dd.Dr, dd.in_dtype == MLA_INT8);
-  return g.uk_w <= kK34Waves && k34_lds(mt, g.nope_w + 1, int(dd.D)).total <= kK34LdsBytes;
-}
+// The int8-query W^UK kernel gives one wave to each 64-column window of Hckv.
+bool packed_fits(const mla_prolog_desc& dd) { return (dd.Hckv + 63) / 64 <= 8; }
 
-// Small-T run on packed weights: K1p, K2, K34p.  Profiling marks: after
-// K1p, after K2, after K34p (which holds both the up-projection and the
-// W^UK product), and an empty last interval.
+// Small-T run on packed weights: K1p (down-projection, split partials), K2
+// (norms, c^Q, caches), K3p (up-projection, q-RoPE, q^C), K4p (W^UK).
+// Profiling marks follow the kernels.
 template <bool I8, int MT, class Mark>
 void packed_launch(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g,
                    bool q8, Mark& mark) {
-  constexpr int D1 = I8 ? 3 : 4;
   const int tiles = g.win_dq + g.win_kr;
-  k1_packed<I8, MT, 4, D1><<<dim3(tiles * pl.Sp), 256, 0, s>>>(d, p, g, pl.Sp, pl.sps);
+  k1_packed<I8, MT, 4, 2><<<dim3(tiles * pl.Sp), 256, 0, s>>>(d, p, g, pl.Sp, pl.sps);
   mark(1);
   const size_t y_bytes = size_t(d.Hcq + d.Hckv + d.Dr) * sizeof(double);
   k2_norm<I8><<<dim3(d.T), 1024, y_bytes, s>>>(d, p, pl.Sp);
   mark(2);
-  const K34Lds L = k34_lds(MT, g.nope_w + 1, d.D);
-  if (q8) k34_packed<I8, true, MT, 3><<<dim3(d.N), 64 * kK34Waves, 0, s>>>(d, p, g, L, pl.kp34);
-  else k34_packed<I8, false, MT, 3><<<dim3(d.N), 64 * kK34Waves, 0, s>>>(d, p, g, L, pl.kp34);
+  k3_packed<I8, MT, 8, 2><<<dim3(d.N * (g.nope_w + 1)), 512, 0, s>>>(d, p, g);
   mark(3);
+  if (q8) k4_packed_q8<MT, 4><<<dim3(d.N), 512, 0, s>>>(d, p, g);
+  else k4_packed<MT, 4, 1><<<dim3(d.N * g.uk_w), 256, 0, s>>>(d, p, g);
   mark(4);
 }
 
@@ -1306,7 +1271,7 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   };
   mark(0);
   p.packed = static_cast<const uint8_t*>(t->packed_weights);
-  if (pl.stream && p.packed && k34_fits(dd, pl.mt1)) {
+  if (pl.stream && p.packed && packed_fits(dd)) {
     launch_packed(pl, s, d, p, dd, i8, q8, mark);
     const hipError_t e = hipGetLastError();
     if (prev != dd.device) (void)hipSetDevice(prev);
