@@ -912,6 +912,326 @@ __global__ __launch_bounds__(512) void k4_packed_q8(Dims d, Ptrs p, PackGeo pg) 
 }
 
 // ---------------------------------------------------------------------------
+// Tiled path for larger token counts.  Every wave owns a 16*MT-token x
+// 64*NWW-column output tile and streams the packed k-stages of its NWW
+// windows against MT activation fragments per stage; 16-byte loads land in
+// the registers the MFMAs read, and the waves of a block that share a
+// window or a token range share those loads through L1.  The MFMA takes the
+// weight fragment as its first operand, so the 16x16 result is the
+// transposed tile: lane l holds token l%16 and columns 4*(l/16) + r, r < 4 --
+// four consecutive output columns of one token, stored as one 8- or 16-byte
+// vector.
+// ---------------------------------------------------------------------------
+template <bool I8, int MT, int NWW, int D, class AP>
+__device__ __forceinline__ void tile_mma(const AP& ap, rsrc_t Wp, const uint32_t (&wb)[NWW], int s0,
+                                         int ns, int ke,
+                                         typename Stage<I8>::Acc (&acc)[MT][NWW * 4]) {
+  using S = Stage<I8>;
+  const int lane = threadIdx.x & 63, ml = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < NWW * 4; ++j) acc[mt][j] = typename S::Acc{0, 0, 0, 0};
+  uint4 bq[D][NWW * 4];
+  uint4 aq[D][AP::NR];
+  auto issue = [&](uint4 (&b)[NWW * 4], uint4 (&a)[AP::NR], int j) {
+    const bool ok = j < ns;
+    const uint32_t st = uint32_t(s0 + j);
+#pragma unroll
+    for (int w = 0; w < NWW; ++w)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        b[w * 4 + ct] = bload16(Wp, ok && wb[w] != kOOB
+                                        ? wb[w] + st * 4096u + uint32_t(ct * 1024 + lane * 16)
+                                        : kOOB);
+    ap.load(a, ml, ok ? int(st) * S::KS + S::KL * g : ke, ke);
+  };
+#pragma unroll
+  for (int q = 0; q < D; ++q) issue(bq[q], aq[q], q);
+  const int nsr = (ns + D - 1) / D * D;
+  for (int j0 = 0; j0 < nsr; j0 += D) {
+#pragma unroll
+    for (int q = 0; q < D; ++q) {
+      typename S::Frag af[MT], bf[NWW * 4];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) af[mt] = ap.frag(aq[q], mt, 16 * mt + ml);
+#pragma unroll
+      for (int j = 0; j < NWW * 4; ++j) bf[j] = __builtin_bit_cast(typename S::Frag, bq[q][j]);
+      issue(bq[q], aq[q], j0 + q + D);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < NWW * 4; ++j) acc[mt][j] = mfma(bf[j], af[mt], acc[mt][j]);
+    }
+  }
+}
+
+// Activation operand of a wave whose first token is m0: rows m0.. of a
+// row-major [T][ld] matrix (element size EB) starting at column col.
+template <bool I8, int MT>
+__device__ __forceinline__ APlain<I8, MT> rows_from(const void* base, int64_t ld, int64_t col, int m0,
+                                                    int T) {
+  constexpr int EB = Stage<I8>::EB;
+  const int rows = m0 < T ? T - m0 : 0;
+  const uint8_t* b = static_cast<const uint8_t*>(base) + (int64_t(m0 < T ? m0 : 0) * ld + col) * EB;
+  return APlain<I8, MT>{make_rsrc(b, rows > 0 ? (int64_t(rows) * ld - col) * EB : 0),
+                        uint32_t(ld * EB), rows};
+}
+
+__device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float e) {
+  return make_uint2(uint32_t(f2bf(a)) | (uint32_t(f2bf(b)) << 16),
+                    uint32_t(f2bf(c)) | (uint32_t(f2bf(e)) << 16));
+}
+
+// K1t: grid (token tiles fastest, then window groups, then k splits).  Wave
+// (wm, wn) takes tokens 16*MT*wm.. of the block's token tile and windows
+// NWW*wn.. of its group of [W^DQ | W^DkvKr] windows; the split's stages go
+// into fp32 (int32) partials, one 16-byte store per 4 columns.
+template <bool I8, int MT, int NWW, int WM, int WN, int D>
+__global__ __launch_bounds__(64 * WM * WN) void k1_tiled(Dims d, Ptrs p, PackGeo pg, int sps, int mtiles,
+                                                      int ngrp) {
+  using St = Stage<I8>;
+  constexpr int BM = 16 * MT * WM, GW = NWW * WN;
+  const int mtile = blockIdx.x % mtiles, rest = blockIdx.x / mtiles;
+  const int grp = rest % ngrp, split = rest / ngrp;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w % WM, wn = w / WM;
+  const int m0 = mtile * BM + 16 * MT * wm;
+  const int tiles = pg.win_dq + pg.win_kr;
+  const int Nkr = d.Hckv + d.Dr, Ntot = d.Hcq + Nkr;
+  uint32_t wb[NWW];
+#pragma unroll
+  for (int i = 0; i < NWW; ++i) {
+    const int j = grp * GW + wn * NWW + i;
+    wb[i] = j < tiles ? uint32_t(pg.off_dq + int64_t(j) * pg.nst_he * 4096) : kOOB;
+  }
+  const int s0 = split * sps;
+  const int ns = m0 < d.T ? max(0, min(pg.nst_he, s0 + sps) - s0) : 0;
+  const auto ap = rows_from<I8, MT>(p.x, d.He, 0, m0, d.T);
+  typename St::Acc acc[MT][NWW * 4];
+  tile_mma<I8, MT, NWW, D>(ap, make_rsrc(p.packed, pg.total), wb, s0, ns, d.He, acc);
+  if (m0 >= d.T) return;
+  const int g = lane >> 4, c = lane & 15;
+#pragma unroll
+  for (int i = 0; i < NWW; ++i) {
+    const int j = grp * GW + wn * NWW + i;
+    if (j >= tiles) break;
+    const int width = j < pg.win_dq ? min(64, d.Hcq - 64 * j) : min(64, Nkr - 64 * (j - pg.win_dq));
+    const int outc = j < pg.win_dq ? 64 * j : d.Hcq + 64 * (j - pg.win_dq);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = m0 + 16 * mt + c;
+      if (m >= d.T) continue;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int col = 16 * ct + 4 * g;
+        if (col >= width) continue;
+        const auto& a = acc[mt][i * 4 + ct];
+        const uint4 v = make_uint4(__builtin_bit_cast(uint32_t, a[0] + 0), __builtin_bit_cast(uint32_t, a[1] + 0),
+                                   __builtin_bit_cast(uint32_t, a[2] + 0), __builtin_bit_cast(uint32_t, a[3] + 0));
+        *reinterpret_cast<uint4*>(static_cast<uint32_t*>(p.part) + (int64_t(split) * d.T + m) * Ntot +
+                                  outc + col) = v;
+      }
+    }
+  }
+}
+
+// K3t: grid (token tiles fastest, then groups of W^UqQr windows).  Nope
+// windows go to q^C (bf16, workspace); a rope window goes through a per-wave
+// LDS tile of 16 tokens x 64 columns to RoPE and queryRopeOut.
+template <bool I8, int MT, int NWW, int WM, int WN, int D>
+__global__ __launch_bounds__(64 * WM * WN) void k3_tiled(Dims d, Ptrs p, PackGeo pg, int mtiles) {
+  using St = Stage<I8>;
+  constexpr int BM = 16 * MT * WM, GW = NWW * WN;
+  __shared__ float E[WM * WN][16 * 65];
+  const int mtile = blockIdx.x % mtiles, grp = blockIdx.x / mtiles;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w % WM, wn = w / WM;
+  const int m0 = mtile * BM + 16 * MT * wm;
+  uint32_t wb[NWW];
+#pragma unroll
+  for (int i = 0; i < NWW; ++i) {
+    const int j = grp * GW + wn * NWW + i;
+    wb[i] = j < pg.win_uq ? uint32_t(pg.off_uq + int64_t(j) * pg.nst_cq * 4096) : kOOB;
+  }
+  const int ns = m0 < d.T ? pg.nst_cq : 0;
+  const auto ap = rows_from<I8, MT>(p.cq, d.Hcq, 0, m0, d.T);
+  typename St::Acc acc[MT][NWW * 4];
+  tile_mma<I8, MT, NWW, D>(ap, make_rsrc(p.packed, pg.total), wb, 0, ns, d.Hcq, acc);
+  if (m0 >= d.T) return;
+  const int g = lane >> 4, c = lane & 15;
+  const int P = pg.nope_w + 1, hf = d.Dr / 2;
+  float* e = E[w];
+#pragma unroll
+  for (int i = 0; i < NWW; ++i) {
+    const int j = grp * GW + wn * NWW + i;
+    if (j >= pg.win_uq) break;
+    const int h = j / P, part = j % P;
+    const bool rope = part == pg.nope_w;
+    const int col0 = h * (d.D + d.Dr) + (rope ? d.D : 64 * part);
+    const int width = rope ? d.Dr : min(64, d.D - 64 * part);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = m0 + 16 * mt + c;
+      float v[4][4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int col = 16 * ct + 4 * g + r;
+          if constexpr (I8)
+            v[ct][r] = (m < d.T && col < width)
+                           ? static_cast<float>(acc[mt][i * 4 + ct][r]) * p.cq_scale[m] * p.sw_uq_qr[col0 + col]
+                           : 0.0f;
+          else
+            v[ct][r] = acc[mt][i * 4 + ct][r];
+        }
+      if (!rope) {
+        if (m < d.T) {
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) {
+            const int col = 16 * ct + 4 * g;
+            if (col < width)
+              *reinterpret_cast<uint2*>(p.qc + (int64_t(m) * d.N + h) * d.D + 64 * part + col) =
+                  pack_bf16x4(v[ct][0], v[ct][1], v[ct][2], v[ct][3]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) e[c * 65 + 16 * ct + 4 * g + r] = v[ct][r];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // lane: token c, pair groups of 4 starting at 4*g, stepping by 16
+        const int64_t mrow = int64_t(m0 + 16 * mt + c);
+        if (mrow < d.T) {
+          const uint16_t* cs = p.cos + mrow * d.Dr;
+          const uint16_t* sn = p.sin + mrow * d.Dr;
+          uint16_t* o = p.qr_out + (mrow * d.N + h) * d.Dr;
+          for (int i0 = 4 * g; i0 < hf; i0 += 16) {
+            float lo[4], hi[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int ii = i0 + r;
+              const float a = e[c * 65 + ii], b = e[c * 65 + ii + hf];
+              lo[r] = a * bf2f(cs[ii]) - b * bf2f(sn[ii]);
+              hi[r] = b * bf2f(cs[ii + hf]) + a * bf2f(sn[ii + hf]);
+            }
+            *reinterpret_cast<uint2*>(o + i0) = pack_bf16x4(lo[0], lo[1], lo[2], lo[3]);
+            *reinterpret_cast<uint2*>(o + i0 + hf) = pack_bf16x4(hi[0], hi[1], hi[2], hi[3]);
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+    }
+  }
+}
+
+// K4t: grid (token tiles fastest, then column groups, then heads).  q^N =
+// q^C[., h, .] W^UK[h]; bf16 stores, or (one column group holding the whole
+// Hckv row) the per-(token, head) int8 quantisation with the row maximum
+// taken across the WN waves of a token range.
+template <int MT, int NWW, int WM, int WN, int D, bool Q8>
+__global__ __launch_bounds__(64 * WM * WN) void k4_tiled(Dims d, Ptrs p, PackGeo pg, int mtiles,
+                                                      int cgroups) {
+  constexpr int BM = 16 * MT * WM, GW = NWW * WN;
+  __shared__ float rmax[Q8 ? WN : 1][Q8 ? BM : 1];
+  const int mtile = blockIdx.x % mtiles, rest = blockIdx.x / mtiles;
+  const int cg = rest % cgroups, h = rest / cgroups;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w % WM, wn = w / WM;
+  const int m0 = mtile * BM + 16 * MT * wm;
+  uint32_t wb[NWW];
+#pragma unroll
+  for (int i = 0; i < NWW; ++i) {
+    const int jw = cg * GW + wn * NWW + i;
+    wb[i] = jw < pg.uk_w ? uint32_t(pg.off_uk + int64_t(h * pg.uk_w + jw) * pg.nst_d * 4096) : kOOB;
+  }
+  const int ns = m0 < d.T ? pg.nst_d : 0;
+  const auto ap = rows_from<false, MT>(p.qc, int64_t(d.N) * d.D, int64_t(h) * d.D, m0, d.T);
+  typename Stage<false>::Acc acc[MT][NWW * 4];
+  tile_mma<false, MT, NWW, D>(ap, make_rsrc(p.packed, pg.total), wb, 0, ns, d.D, acc);
+  const int g = lane >> 4, c = lane & 15;
+  if constexpr (!Q8) {
+    if (m0 >= d.T) return;
+    uint16_t* qo = static_cast<uint16_t*>(p.q_out);
+#pragma unroll
+    for (int i = 0; i < NWW; ++i) {
+      const int jw = cg * GW + wn * NWW + i;
+      if (jw >= pg.uk_w) break;
+      const int width = min(64, d.Hckv - 64 * jw);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = m0 + 16 * mt + c;
+        if (m >= d.T) continue;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const int col = 16 * ct + 4 * g;
+          if (col >= width) continue;
+          const auto& a = acc[mt][i * 4 + ct];
+          *reinterpret_cast<uint2*>(qo + (int64_t(m) * d.N + h) * d.Hckv + 64 * jw + col) =
+              pack_bf16x4(a[0], a[1], a[2], a[3]);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      float mx = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NWW; ++i) {
+        const int width = min(64, d.Hckv - 64 * (wn * NWW + i));
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+          if (16 * ct + 4 * g < width)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(acc[mt][i * 4 + ct][r]));
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      if (g == 0) rmax[wn][16 * MT * wm + 16 * mt + c] = mx;
+    }
+    __syncthreads();
+    if (m0 >= d.T) return;
+    int8_t* qo = static_cast<int8_t*>(p.q_out);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = m0 + 16 * mt + c;
+      if (m >= d.T) continue;
+      float amax = rmax[0][16 * MT * wm + 16 * mt + c];
+#pragma unroll
+      for (int k = 1; k < WN; ++k) amax = fmaxf(amax, rmax[k][16 * MT * wm + 16 * mt + c]);
+      const float sc = amax / 127.0f;
+#pragma unroll
+      for (int i = 0; i < NWW; ++i) {
+        const int jw = wn * NWW + i;
+        if (jw >= pg.uk_w) break;
+        const int width = min(64, d.Hckv - 64 * jw);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const int col = 16 * ct + 4 * g;
+          if (col >= width) continue;
+          const auto& a = acc[mt][i * 4 + ct];
+          uint32_t q = 0;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float x = a[r];
+            const int8_t code = sc > 0.0f ? quant_code(x, sc) : int8_t(0);
+            q |= uint32_t(uint8_t(code)) << (8 * r);
+          }
+          *reinterpret_cast<uint32_t*>(qo + (int64_t(m) * d.N + h) * d.Hckv + 64 * jw + col) = q;
+        }
+      }
+      if (wn == 0 && g == 0) p.q_scale[int64_t(m) * d.N + h] = sc;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 // Token counts up to this run on the streaming kernels.
@@ -967,6 +1287,48 @@ Plan make_plan(const mla_prolog_desc& d, int64_t T) {
   return pl;
 }
 
+// Tiled path (token counts above the streaming range, packed weights).
+// Shape classes: large (T >= 512) uses 256-token x 256-column blocks of four
+// 128x128 waves; medium uses one 16*mt-token wave per 64-column window (K1,
+// K3) or per 128 columns (K4, two waves stacked along tokens above 128
+// tokens).  K1 splits the He stages so that about kTiledK1Blocks blocks run.
+constexpr int kTiledLargeT = 2048;
+constexpr int kTiledK1Blocks = 512;   // medium: one-wave blocks
+constexpr int kTiledK1BlocksLarge = 256;
+
+struct TiledPlan {
+  bool large;
+  int mt, wm;              // medium: 16-token tiles per wave, waves along tokens (K3, K4)
+  int m1, ngrp1, S, sps;   // K1: token tiles, window groups, splits, stages per split
+  int m3, ngrp3;           // K3
+  int m4, cg4;             // K4 bf16
+  int m4q;                 // K4 int8 query: token tiles of 64
+};
+
+TiledPlan tiled_plan(const mla_prolog_desc& d, int64_t T) {
+  TiledPlan tp;
+  const PackGeo g = pack_geo(d.He, d.Hcq, d.Hckv, d.N, d.D, d.Dr, d.in_dtype == MLA_INT8);
+  const int tiles = g.win_dq + g.win_kr;
+  tp.large = T >= kTiledLargeT;
+  tp.mt = T <= 64 ? 4 : 8;
+  tp.wm = (!tp.large && T > 128) ? 2 : 1;
+  if (tp.large) {
+    tp.m1 = ceil_div(T, 256); tp.ngrp1 = ceil_div(tiles, 4);
+    tp.m3 = ceil_div(T, 256); tp.ngrp3 = ceil_div(g.win_uq, 4);
+    tp.m4 = ceil_div(T, 256); tp.cg4 = ceil_div(g.uk_w, 4);
+  } else {
+    tp.m1 = ceil_div(T, 16 * tp.mt); tp.ngrp1 = tiles;
+    tp.m3 = ceil_div(T, 16 * tp.mt * tp.wm); tp.ngrp3 = g.win_uq;
+    tp.m4 = ceil_div(T, 16 * tp.mt * tp.wm); tp.cg4 = ceil_div(g.uk_w, 2);
+  }
+  const int target = tp.large ? kTiledK1BlocksLarge : kTiledK1Blocks;
+  int S = std::max(1, std::min(g.nst_he, target / std::max(1, tp.m1 * tp.ngrp1)));
+  tp.sps = ceil_div(g.nst_he, S);
+  tp.S = ceil_div(g.nst_he, tp.sps);
+  tp.m4q = ceil_div(T, 64);
+  return tp;
+}
+
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Layout {
@@ -977,12 +1339,12 @@ Layout layout(const mla_prolog_desc& d) {
   Layout L;
   const int64_t Ntot = d.Hcq + d.Hckv + d.Dr;
   int64_t part_rows = 0;
-  // the largest S*T over all T <= max_tokens
+  // the largest S*T over all T <= max_tokens (plans are cheap host arithmetic)
   for (int64_t T = 1; T <= d.max_tokens; ++T) {
     const Plan pl = make_plan(d, T);
     part_rows = std::max<int64_t>(part_rows, int64_t(pl.S) * T);
     if (pl.stream) part_rows = std::max<int64_t>(part_rows, int64_t(pl.Sp) * T);
-    if (T >= 512) { part_rows = std::max<int64_t>(part_rows, d.max_tokens); break; }
+    else part_rows = std::max<int64_t>(part_rows, int64_t(tiled_plan(d, T).S) * T);
   }
   L.part = 0;
   L.cq = align256(L.part + size_t(part_rows) * Ntot * 4);
@@ -1138,6 +1500,60 @@ void launch_packed(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p,
   }
 }
 
+// Tiled run on packed weights (token counts above the streaming range).
+template <bool I8, int MT, int WM, class Mark>
+void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g,
+                  bool q8, Mark& mark) {
+  k1_tiled<I8, MT, 1, 1, 1, 2><<<dim3(tp.m1 * tp.ngrp1 * tp.S), 64, 0, s>>>(d, p, g, tp.sps, tp.m1,
+                                                                           tp.ngrp1);
+  mark(1);
+  const size_t y_bytes = size_t(d.Hcq + d.Hckv + d.Dr) * sizeof(double);
+  k2_norm<I8><<<dim3(d.T), 1024, y_bytes, s>>>(d, p, tp.S);
+  mark(2);
+  k3_tiled<I8, MT, 1, WM, 1, 2><<<dim3(tp.m3 * tp.ngrp3), 64 * WM, 0, s>>>(d, p, g, tp.m3);
+  mark(3);
+  if (q8) k4_tiled<4, 2, 1, 4, 2, true><<<dim3(tp.m4q * d.N), 256, 0, s>>>(d, p, g, tp.m4q, 1);
+  else k4_tiled<MT, 2, WM, 1, 2, false><<<dim3(tp.m4 * tp.cg4 * d.N), 64 * WM, 0, s>>>(d, p, g, tp.m4,
+                                                                                     tp.cg4);
+  mark(4);
+}
+
+template <bool I8, class Mark>
+void tiled_large(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g,
+                 bool q8, Mark& mark) {
+  k1_tiled<I8, 8, 2, 2, 2, 2><<<dim3(tp.m1 * tp.ngrp1 * tp.S), 256, 0, s>>>(d, p, g, tp.sps, tp.m1,
+                                                                           tp.ngrp1);
+  mark(1);
+  const size_t y_bytes = size_t(d.Hcq + d.Hckv + d.Dr) * sizeof(double);
+  k2_norm<I8><<<dim3(d.T), 1024, y_bytes, s>>>(d, p, tp.S);
+  mark(2);
+  k3_tiled<I8, 8, 2, 2, 2, 2><<<dim3(tp.m3 * tp.ngrp3), 256, 0, s>>>(d, p, g, tp.m3);
+  mark(3);
+  if (q8) k4_tiled<4, 2, 1, 4, 2, true><<<dim3(tp.m4q * d.N), 256, 0, s>>>(d, p, g, tp.m4q, 1);
+  else k4_tiled<8, 2, 2, 2, 2, false><<<dim3(tp.m4 * tp.cg4 * d.N), 256, 0, s>>>(d, p, g, tp.m4, tp.cg4);
+  mark(4);
+}
+
+template <class Mark>
+void launch_tiled(hipStream_t s, const Dims& d, const Ptrs& p, const mla_prolog_desc& dd, bool i8,
+                  bool q8, Mark& mark) {
+  const PackGeo g = pack_geo(dd.He, dd.Hcq, dd.Hckv, dd.N, dd.D, dd.Dr, i8);
+  const TiledPlan tp = tiled_plan(dd, d.T);
+  if (tp.large) {
+    if (i8) tiled_large<true>(tp, s, d, p, g, q8, mark);
+    else tiled_large<false>(tp, s, d, p, g, q8, mark);
+  } else if (tp.mt == 4) {
+    if (i8) tiled_medium<true, 4, 1>(tp, s, d, p, g, q8, mark);
+    else tiled_medium<false, 4, 1>(tp, s, d, p, g, q8, mark);
+  } else if (tp.wm == 1) {
+    if (i8) tiled_medium<true, 8, 1>(tp, s, d, p, g, q8, mark);
+    else tiled_medium<false, 8, 1>(tp, s, d, p, g, q8, mark);
+  } else {
+    if (i8) tiled_medium<true, 8, 2>(tp, s, d, p, g, q8, mark);
+    else tiled_medium<false, 8, 2>(tp, s, d, p, g, q8, mark);
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -1271,8 +1687,9 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   };
   mark(0);
   p.packed = static_cast<const uint8_t*>(t->packed_weights);
-  if (pl.stream && p.packed && packed_fits(dd)) {
-    launch_packed(pl, s, d, p, dd, i8, q8, mark);
+  if (p.packed && (!pl.stream || packed_fits(dd))) {
+    if (pl.stream) launch_packed(pl, s, d, p, dd, i8, q8, mark);
+    else launch_tiled(s, d, p, dd, i8, q8, mark);
     const hipError_t e = hipGetLastError();
     if (prev != dd.device) (void)hipSetDevice(prev);
     return e == hipSuccess ? MLA_OK : MLA_ERR_RUNTIME;

@@ -237,3 +237,40 @@ def test_int8_decode_t32_packed():
     # the int8 decode workload at 32 tokens runs on the packed small-T kernels
     inp = synth.make_inputs(synth.workload("int8_decode_t128"), T=32)
     full_check(inp, packed=True)
+
+
+# ---- packed weights, tiled kernels (token counts above 32) -------------------
+TILED = {
+    "ragged_t37": SMALL["ragged_t37"],
+    "mid_t70": SMALL["mid_t70"],
+    "ragged_t150_wide": custom_workload("ragged_t150_wide", T=150,
+                                        dims=Dims(He=520, Hcq=200, Hckv=136, N=5, D=136, Dr=64),
+                                        block_num=16, block_size=16, seed=35),
+    "t600": SMALL["t300_split1"],
+    "t2100_large": custom_workload("t2100_large", T=2100,
+                                   dims=Dims(He=264, Hcq=72, Hckv=40, N=3, D=24, Dr=16),
+                                   block_num=160, block_size=16, seed=36),
+}
+
+
+@pytest.mark.parametrize("name", list(TILED))
+def test_tiled_bf16_packed(name):
+    full_check(synth.make_inputs(TILED[name]), packed=True)
+
+
+def test_tiled_int8_packed():
+    inp = synth.make_inputs(INT8_SMALL["q8_t130"])
+    full_check(inp, packed=True)
+    full_check(inp, query_int8=False, packed=True)
+
+
+def test_tiled_int8_large_packed():
+    wl = custom_workload("q8_t2100", T=2100, dims=Dims(He=512, Hcq=128, Hckv=96, N=3, D=32, Dr=32),
+                         block_num=160, block_size=16, seed=37, quant=True)
+    full_check(synth.make_inputs(wl), packed=True)
+
+
+@pytest.mark.parametrize("name", ["decode_t256", "int8_decode_t128", "prefill_t8192"])
+def test_full_size_tiled_packed(name):
+    inp = synth.make_inputs(synth.workload(name))
+    full_check(inp, rows=sample_rows(int(inp["T"])), packed=True)
