@@ -18,8 +18,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCE = os.path.join(HERE, "csrc", "mla_prolog.hip")
 LIBRARY = os.path.join(HERE, "libmla_prolog.so")
+# MFMA accumulators in VGPRs: with the default AGPR form the register
+# allocator rotates the accumulators of the software-pipelined loops through
+# copies on every iteration.
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
 MLA_OK = 0
 MLA_ERR_NULLPTR = 161001

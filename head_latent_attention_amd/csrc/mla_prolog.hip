@@ -406,7 +406,7 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr uint32_t kOOB = 0x80000000u;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int n = static_cast<int>(bytes < int64_t(kOOB) ? bytes : int64_t(kOOB) - 1);
+  const int n = static_cast<int>(bytes <= 0 ? 0 : bytes < int64_t(kOOB) ? bytes : int64_t(kOOB) - 1);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
 }
 __device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t off) {
@@ -421,28 +421,61 @@ __device__ __forceinline__ i32x4 mfma(i32x4 a, i32x4 b, i32x4 c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-// Activation operands.  A policy loads the raw 16-byte registers of the MT
-// fragments of one stage (load) and turns them into MFMA A fragments (frag).
-// This one reads them as stored (bf16 or int8, k-contiguous rows); rows are
-// relative to the buffer base.
+// Activation operands.  A policy loads the calling lane's 16-byte registers
+// of the MT fragments (16 rows each) of one k-stage (load) and turns them
+// into MFMA fragments (frag).
+//
+// APlain reads row-major rows (bf16 or int8, k-contiguous), counted from the
+// buffer base: a wave's load touches 16 rows.
 template <bool I8, int MT>
 struct APlain {
   static constexpr int NR = MT;  // 16-byte registers per stage
   rsrc_t A;
   uint32_t lda;  // bytes per row
   int M;         // valid rows from the base
-  __device__ __forceinline__ void load(uint4 (&r)[NR], int m0, int ka, int ke) const {
+  int ke;        // valid k
+  __device__ __forceinline__ void load(uint4 (&r)[NR], int st, bool ok) const {
+    const int lane = threadIdx.x & 63, ml = lane & 15, g = lane >> 4;
+    const int ka = st * Stage<I8>::KS + Stage<I8>::KL * g;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int m = m0 + 16 * mt;
-      const bool ok = m < M && ka < ke;
-      r[mt] = bload16(A, ok ? uint32_t(m) * lda + uint32_t(ka) * Stage<I8>::EB : kOOB);
+      const int m = ml + 16 * mt;
+      r[mt] = bload16(A, ok && m < M && ka < ke ? uint32_t(m) * lda + uint32_t(ka) * Stage<I8>::EB
+                                                : kOOB);
     }
   }
-  __device__ __forceinline__ typename Stage<I8>::Frag frag(const uint4 (&r)[NR], int mt, int) const {
+  __device__ __forceinline__ typename Stage<I8>::Frag frag(const uint4 (&r)[NR], int mt) const {
     return __builtin_bit_cast(typename Stage<I8>::Frag, r[mt]);
   }
 };
+
+// APacked reads fragment-packed activations: every 16-row tile stores its
+// k-stages one after the other, 1 KB each, in MFMA fragment order (lane l:
+// row l%16, k-run KL*(l/16) of the stage), so a wave's load is one
+// contiguous kilobyte.  Tiles are `tile` bytes apart from the base.
+template <bool I8, int MT>
+struct APacked {
+  static constexpr int NR = MT;
+  rsrc_t A;
+  uint32_t tile;
+  __device__ __forceinline__ void load(uint4 (&r)[NR], int st, bool ok) const {
+    const uint32_t lane = threadIdx.x & 63;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      r[mt] = bload16(A, ok ? uint32_t(mt) * tile + uint32_t(st) * 1024u + lane * 16u : kOOB);
+  }
+  __device__ __forceinline__ typename Stage<I8>::Frag frag(const uint4 (&r)[NR], int mt) const {
+    return __builtin_bit_cast(typename Stage<I8>::Frag, r[mt]);
+  }
+};
+
+// Byte offset of element (row t, k) in a fragment-packed activation buffer
+// whose 16-row tiles are `tile` bytes apart.
+__device__ __forceinline__ int64_t packed_offset(int64_t t, int k, int64_t tile, bool i8) {
+  const int ks = i8 ? 64 : 32, kl = i8 ? 16 : 8, eb = i8 ? 1 : 2;
+  const int st = k / ks, g = (k % ks) / kl, i = k % kl;
+  return (t >> 4) * tile + int64_t(st) * 1024 + ((g * 16 + (t & 15)) * 16) + i * eb;
+}
 
 // Sum of the NW waves' accumulators into wave 0, in a fixed pairing order.
 // red: (NW/2) * MT * 16 * 64 words of LDS.  Ends with a block barrier.
@@ -578,12 +611,10 @@ __global__ __launch_bounds__(256) void k_pack(Dims d, Ptrs p, PackGeo g, int i8,
 // at byte wbase against MT activation fragments; all loads go through one
 // register ring D stages deep.
 template <bool I8, int MT, int D, class AP>
-__device__ __forceinline__ void stream_packed(const AP& ap, int m0, rsrc_t Wp, uint32_t wbase,
-                                              int sfirst, int sstep, int ns, int ke,
-                                              typename Stage<I8>::Acc (&acc)[MT][4]) {
+__device__ __forceinline__ void stream_packed(const AP& ap, rsrc_t Wp, uint32_t wbase, int sfirst,
+                                              int sstep, int ns, typename Stage<I8>::Acc (&acc)[MT][4]) {
   using S = Stage<I8>;
   const int lane = threadIdx.x & 63;
-  const int ml = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -596,24 +627,29 @@ __device__ __forceinline__ void stream_packed(const AP& ap, int m0, rsrc_t Wp, u
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct)
       b[ct] = bload16(Wp, ok ? wbase + uint32_t(st) * 4096u + uint32_t(ct * 1024 + lane * 16) : kOOB);
-    ap.load(a, m0 + ml, ok ? st * S::KS + S::KL * g : ke, ke);
+    ap.load(a, st, ok);
   };
 #pragma unroll
-  for (int q = 0; q < D; ++q) issue(bq[q], aq[q], q);
+  for (int q = 0; q < D; ++q) {
+    issue(bq[q], aq[q], q);
+    __builtin_amdgcn_sched_barrier(0);   // the loop expects the slots in this order
+  }
+  // each slot is refilled right after the MFMAs that read it; the
+  // scheduling barriers keep the refills in slot order, so every wait is
+  // for the oldest slot only
   const int nsr = (ns + D - 1) / D * D;
   for (int j0 = 0; j0 < nsr; j0 += D) {
 #pragma unroll
     for (int q = 0; q < D; ++q) {
-      typename S::Frag af[MT], bf[4];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) af[mt] = ap.frag(aq[q], mt, 16 * mt + ml);
+      for (int mt = 0; mt < MT; ++mt) {
+        const typename S::Frag af = ap.frag(aq[q], mt);
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) bf[ct] = __builtin_bit_cast(typename S::Frag, bq[q][ct]);
+        for (int ct = 0; ct < 4; ++ct)
+          acc[mt][ct] = mfma(af, __builtin_bit_cast(typename S::Frag, bq[q][ct]), acc[mt][ct]);
+      }
       issue(bq[q], aq[q], j0 + q + D);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) acc[mt][ct] = mfma(af[mt], bf[ct], acc[mt][ct]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -638,9 +674,9 @@ __global__ __launch_bounds__(64 * NW) void k1_packed(Dims d, Ptrs p, PackGeo pg,
   const int s0 = split * sps, s1 = min(pg.nst_he, s0 + sps);
   const int ns = s0 + w < s1 ? (s1 - s0 - w + NW - 1) / NW : 0;
   typename St::Acc acc[MT][4];
-  const APlain<I8, MT> ap{make_rsrc(p.x, int64_t(d.T) * d.He * St::EB), uint32_t(d.He * St::EB), d.T};
-  stream_packed<I8, MT, D>(ap, 0, make_rsrc(p.packed, pg.total), uint32_t(wbase), s0 + w, NW, ns,
-                           d.He, acc);
+  const APlain<I8, MT> ap{make_rsrc(p.x, int64_t(d.T) * d.He * St::EB), uint32_t(d.He * St::EB), d.T,
+                          d.He};
+  stream_packed<I8, MT, D>(ap, make_rsrc(p.packed, pg.total), uint32_t(wbase), s0 + w, NW, ns, acc);
   reduce_waves<NW, MT>(acc, reinterpret_cast<uint32_t*>(lds));
   if (w != 0) return;
   const int g = lane >> 4, c = lane & 15;
@@ -666,7 +702,9 @@ __global__ __launch_bounds__(64 * NW) void k1_packed(Dims d, Ptrs p, PackGeo pg,
 // writes c^Q (bf16, or per-token int8 + scale) to the workspace and the
 // c^KV / RoPE(k^R) rows to the token's cacheIndex slot.  y, the RMS factors
 // and c are computed in double (a few thousand values per token), so the
-// per-token int8 decision of c^Q sees c rounded once to fp32.
+// per-token int8 decision of c^Q sees c rounded once to fp32.  With cq_nst
+// > 0, c^Q is stored fragment-packed (cq_nst k-stages per 16-token tile, k
+// padding as zeros) for the packed-weight kernels; with 0, row-major.
 __device__ double block_sum_f64(double v, double* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -679,7 +717,7 @@ __device__ double block_sum_f64(double v, double* red) {
 }
 
 template <bool I8>
-__global__ __launch_bounds__(1024) void k2_norm(Dims d, Ptrs p, int S) {
+__global__ __launch_bounds__(1024) void k2_norm(Dims d, Ptrs p, int S, int cq_nst) {
   extern __shared__ double y[];  // Hcq + Hckv + Dr
   __shared__ double red[16];
   __shared__ float redf[16];
@@ -737,13 +775,27 @@ __global__ __launch_bounds__(1024) void k2_norm(Dims d, Ptrs p, int S) {
     amax = redf[0];
     for (int w = 1; w < 16; ++w) amax = fmaxf(amax, redf[w]);
     const float sc = amax / 127.0f;
-    int8_t* cq = reinterpret_cast<int8_t*>(p.cq) + int64_t(t) * d.Hcq;
-    for (int n = tid; n < d.Hcq; n += 1024) cq[n] = sc > 0.0f ? quant_code(float(y[n]), sc) : 0;
+    if (cq_nst) {
+      const int64_t tile = int64_t(cq_nst) * 1024;
+      for (int n = tid; n < cq_nst * 64; n += 1024)
+        reinterpret_cast<int8_t*>(p.cq)[packed_offset(t, n, tile, true)] =
+            (n < d.Hcq && sc > 0.0f) ? quant_code(float(y[n]), sc) : int8_t(0);
+    } else {
+      int8_t* cq = reinterpret_cast<int8_t*>(p.cq) + int64_t(t) * d.Hcq;
+      for (int n = tid; n < d.Hcq; n += 1024) cq[n] = sc > 0.0f ? quant_code(float(y[n]), sc) : 0;
+    }
     if (tid == 0) p.cq_scale[t] = sc;
   } else {
-    uint16_t* cq = reinterpret_cast<uint16_t*>(p.cq) + int64_t(t) * d.Hcq;
-    for (int n = tid; n < d.Hcq; n += 1024)
-      cq[n] = f2bf(float(double(bf2f(p.gamma_cq[n])) * y[n] / rms_q));
+    if (cq_nst) {
+      const int64_t tile = int64_t(cq_nst) * 1024;
+      for (int n = tid; n < cq_nst * 32; n += 1024)
+        *reinterpret_cast<uint16_t*>(p.cq + packed_offset(t, n, tile, false)) =
+            n < d.Hcq ? f2bf(float(double(bf2f(p.gamma_cq[n])) * y[n] / rms_q)) : uint16_t(0);
+    } else {
+      uint16_t* cq = reinterpret_cast<uint16_t*>(p.cq) + int64_t(t) * d.Hcq;
+      for (int n = tid; n < d.Hcq; n += 1024)
+        cq[n] = f2bf(float(double(bf2f(p.gamma_cq[n])) * y[n] / rms_q));
+    }
   }
   const int64_t slot = p.cache_index[t];
   if (slot < 0 || slot >= d.slots) return;
@@ -779,9 +831,10 @@ __global__ __launch_bounds__(64 * NW) void k3_packed(Dims d, Ptrs p, PackGeo pg)
   const int width = rope ? d.Dr : min(64, d.D - 64 * part);
   const int ns = w < pg.nst_cq ? (pg.nst_cq - w + NW - 1) / NW : 0;
   typename St::Acc acc[MT][4];
-  const APlain<I8, MT> ap{make_rsrc(p.cq, int64_t(d.T) * d.Hcq * St::EB), uint32_t(d.Hcq * St::EB), d.T};
+  const int64_t ctile = int64_t(pg.nst_cq) * 1024;
+  const APacked<I8, MT> ap{make_rsrc(p.cq, int64_t((d.T + 15) / 16) * ctile), uint32_t(ctile)};
   const int64_t wbase = pg.off_uq + int64_t(blockIdx.x) * pg.nst_cq * 4096;
-  stream_packed<I8, MT, D>(ap, 0, make_rsrc(p.packed, pg.total), uint32_t(wbase), w, NW, ns, d.Hcq, acc);
+  stream_packed<I8, MT, D>(ap, make_rsrc(p.packed, pg.total), uint32_t(wbase), w, NW, ns, acc);
   reduce_waves<NW, MT>(acc, reinterpret_cast<uint32_t*>(lds));
   float* E = reinterpret_cast<float*>(lds);   // [16*MT][65]
   if (w == 0) {
@@ -806,9 +859,15 @@ __global__ __launch_bounds__(64 * NW) void k3_packed(Dims d, Ptrs p, PackGeo pg)
   __syncthreads();
   const int BM = 16 * MT;
   if (!rope) {
-    for (int idx = tid; idx < BM * width; idx += 64 * NW) {
-      const int ml = idx / width, cc = idx % width;
-      if (ml < d.T) p.qc[(int64_t(ml) * d.N + h) * d.D + 64 * part + cc] = f2bf(E[ml * 65 + cc]);
+    // q^C goes out fragment-packed for the W^UK product, its k padding as zeros
+    const int wq = min(64, 32 * pg.nst_d - 64 * part);
+    const int64_t qtile = int64_t(d.N) * pg.nst_d * 1024;
+    uint8_t* qcb = reinterpret_cast<uint8_t*>(p.qc) + int64_t(h) * pg.nst_d * 1024;
+    for (int idx = tid; idx < BM * wq; idx += 64 * NW) {
+      const int ml = idx / wq, cc = idx % wq;
+      if (ml < d.T)
+        *reinterpret_cast<uint16_t*>(qcb + packed_offset(ml, 64 * part + cc, qtile, false)) =
+            f2bf(E[ml * 65 + cc]);
     }
   } else {
     const int hf = d.Dr / 2;
@@ -837,10 +896,12 @@ __global__ __launch_bounds__(64 * NW) void k4_packed(Dims d, Ptrs p, PackGeo pg)
   const int c0 = 64 * win, width = min(64, d.Hckv - c0);
   const int ns = w < pg.nst_d ? (pg.nst_d - w + NW - 1) / NW : 0;
   typename St::Acc acc[MT][4];
-  const APlain<false, MT> ap{make_rsrc(p.qc + int64_t(h) * d.D, (int64_t(d.T) * d.N - h) * d.D * 2),
-                             uint32_t(d.N * d.D * 2), d.T};
+  const int64_t qtile = int64_t(d.N) * pg.nst_d * 1024, qh = int64_t(h) * pg.nst_d * 1024;
+  const APacked<false, MT> ap{make_rsrc(reinterpret_cast<const uint8_t*>(p.qc) + qh,
+                                        int64_t((d.T + 15) / 16) * qtile - qh),
+                              uint32_t(qtile)};
   const int64_t wbase = pg.off_uk + int64_t(blockIdx.x) * pg.nst_d * 4096;
-  stream_packed<false, MT, D>(ap, 0, make_rsrc(p.packed, pg.total), uint32_t(wbase), w, NW, ns, d.D, acc);
+  stream_packed<false, MT, D>(ap, make_rsrc(p.packed, pg.total), uint32_t(wbase), w, NW, ns, acc);
   reduce_waves<NW, MT>(acc, reinterpret_cast<uint32_t*>(lds));
   uint16_t* E = reinterpret_cast<uint16_t*>(lds);  // [16*MT][64]
   if (w == 0) {
@@ -873,11 +934,13 @@ __global__ __launch_bounds__(512) void k4_packed_q8(Dims d, Ptrs p, PackGeo pg) 
   const bool active = w < pg.uk_w;
   const int c0 = 64 * w, width = active ? min(64, d.Hckv - c0) : 0;
   typename Stage<false>::Acc acc[MT][4];
-  const APlain<false, MT> ap{make_rsrc(p.qc + int64_t(h) * d.D, (int64_t(d.T) * d.N - h) * d.D * 2),
-                             uint32_t(d.N * d.D * 2), d.T};
+  const int64_t qtile = int64_t(d.N) * pg.nst_d * 1024, qh = int64_t(h) * pg.nst_d * 1024;
+  const APacked<false, MT> ap{make_rsrc(reinterpret_cast<const uint8_t*>(p.qc) + qh,
+                                        int64_t((d.T + 15) / 16) * qtile - qh),
+                              uint32_t(qtile)};
   const int64_t wbase = pg.off_uk + int64_t(h * pg.uk_w + (active ? w : 0)) * pg.nst_d * 4096;
-  stream_packed<false, MT, D>(ap, 0, make_rsrc(p.packed, pg.total), uint32_t(wbase), 0, 1,
-                              active ? pg.nst_d : 0, d.D, acc);
+  stream_packed<false, MT, D>(ap, make_rsrc(p.packed, pg.total), uint32_t(wbase), 0, 1,
+                              active ? pg.nst_d : 0, acc);
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -924,10 +987,9 @@ __global__ __launch_bounds__(512) void k4_packed_q8(Dims d, Ptrs p, PackGeo pg) 
 // ---------------------------------------------------------------------------
 template <bool I8, int MT, int NWW, int D, class AP>
 __device__ __forceinline__ void tile_mma(const AP& ap, rsrc_t Wp, const uint32_t (&wb)[NWW], int s0,
-                                         int ns, int ke,
-                                         typename Stage<I8>::Acc (&acc)[MT][NWW * 4]) {
+                                         int ns, typename Stage<I8>::Acc (&acc)[MT][NWW * 4]) {
   using S = Stage<I8>;
-  const int lane = threadIdx.x & 63, ml = lane & 15, g = lane >> 4;
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -944,24 +1006,31 @@ __device__ __forceinline__ void tile_mma(const AP& ap, rsrc_t Wp, const uint32_t
         b[w * 4 + ct] = bload16(Wp, ok && wb[w] != kOOB
                                         ? wb[w] + st * 4096u + uint32_t(ct * 1024 + lane * 16)
                                         : kOOB);
-    ap.load(a, ml, ok ? int(st) * S::KS + S::KL * g : ke, ke);
+    ap.load(a, int(st), ok);
   };
 #pragma unroll
-  for (int q = 0; q < D; ++q) issue(bq[q], aq[q], q);
+  for (int q = 0; q < D; ++q) {
+    issue(bq[q], aq[q], q);
+    __builtin_amdgcn_sched_barrier(0);   // the loop expects the slots in this order
+  }
+  // a slot is refilled right after the MFMAs that read it, so the ring
+  // needs no spare registers and no copies on the loop's back edge
   const int nsr = (ns + D - 1) / D * D;
   for (int j0 = 0; j0 < nsr; j0 += D) {
 #pragma unroll
     for (int q = 0; q < D; ++q) {
-      typename S::Frag af[MT], bf[NWW * 4];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) af[mt] = ap.frag(aq[q], mt, 16 * mt + ml);
+      for (int mt = 0; mt < MT; ++mt) {
+        const typename S::Frag af = ap.frag(aq[q], mt);
 #pragma unroll
-      for (int j = 0; j < NWW * 4; ++j) bf[j] = __builtin_bit_cast(typename S::Frag, bq[q][j]);
+        for (int j = 0; j < NWW * 4; ++j)
+          acc[mt][j] = mfma(__builtin_bit_cast(typename S::Frag, bq[q][j]), af, acc[mt][j]);
+      }
       issue(bq[q], aq[q], j0 + q + D);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int j = 0; j < NWW * 4; ++j) acc[mt][j] = mfma(bf[j], af[mt], acc[mt][j]);
+      // keep each slot's MFMAs after its own wait and before the next
+      // slot's: the scheduler would otherwise gather every refill at the end
+      // of the iteration and wait for all of them at its top
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -969,13 +1038,22 @@ __device__ __forceinline__ void tile_mma(const AP& ap, rsrc_t Wp, const uint32_t
 // Activation operand of a wave whose first token is m0: rows m0.. of a
 // row-major [T][ld] matrix (element size EB) starting at column col.
 template <bool I8, int MT>
-__device__ __forceinline__ APlain<I8, MT> rows_from(const void* base, int64_t ld, int64_t col, int m0,
-                                                    int T) {
+__device__ __forceinline__ APlain<I8, MT> rows_from(const void* base, int64_t ld, int m0, int T) {
   constexpr int EB = Stage<I8>::EB;
   const int rows = m0 < T ? T - m0 : 0;
-  const uint8_t* b = static_cast<const uint8_t*>(base) + (int64_t(m0 < T ? m0 : 0) * ld + col) * EB;
-  return APlain<I8, MT>{make_rsrc(b, rows > 0 ? (int64_t(rows) * ld - col) * EB : 0),
-                        uint32_t(ld * EB), rows};
+  const uint8_t* b = static_cast<const uint8_t*>(base) + int64_t(m0 < T ? m0 : 0) * ld * EB;
+  return APlain<I8, MT>{make_rsrc(b, int64_t(rows) * ld * EB), uint32_t(ld * EB), rows, int(ld)};
+}
+
+// Fragment-packed activations from the 16-row tile holding row m0 (a
+// multiple of 16) on; `tile` bytes per tile, `tiles` tiles in the buffer.
+template <bool I8, int MT>
+__device__ __forceinline__ APacked<I8, MT> tiles_from(const void* base, int64_t tile, int64_t tiles,
+                                                      int m0) {
+  const int64_t t0 = m0 / 16;
+  return APacked<I8, MT>{make_rsrc(static_cast<const uint8_t*>(base) + (t0 < tiles ? t0 : 0) * tile,
+                                   (tiles - t0) * tile),
+                         uint32_t(tile)};
 }
 
 __device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float e) {
@@ -1007,9 +1085,9 @@ __global__ __launch_bounds__(64 * WM * WN) void k1_tiled(Dims d, Ptrs p, PackGeo
   }
   const int s0 = split * sps;
   const int ns = m0 < d.T ? max(0, min(pg.nst_he, s0 + sps) - s0) : 0;
-  const auto ap = rows_from<I8, MT>(p.x, d.He, 0, m0, d.T);
+  const auto ap = rows_from<I8, MT>(p.x, d.He, m0, d.T);
   typename St::Acc acc[MT][NWW * 4];
-  tile_mma<I8, MT, NWW, D>(ap, make_rsrc(p.packed, pg.total), wb, s0, ns, d.He, acc);
+  tile_mma<I8, MT, NWW, D>(ap, make_rsrc(p.packed, pg.total), wb, s0, ns, acc);
   if (m0 >= d.T) return;
   const int g = lane >> 4, c = lane & 15;
 #pragma unroll
@@ -1055,9 +1133,9 @@ __global__ __launch_bounds__(64 * WM * WN) void k3_tiled(Dims d, Ptrs p, PackGeo
     wb[i] = j < pg.win_uq ? uint32_t(pg.off_uq + int64_t(j) * pg.nst_cq * 4096) : kOOB;
   }
   const int ns = m0 < d.T ? pg.nst_cq : 0;
-  const auto ap = rows_from<I8, MT>(p.cq, d.Hcq, 0, m0, d.T);
+  const auto ap = tiles_from<I8, MT>(p.cq, int64_t(pg.nst_cq) * 1024, (d.T + 15) / 16, m0);
   typename St::Acc acc[MT][NWW * 4];
-  tile_mma<I8, MT, NWW, D>(ap, make_rsrc(p.packed, pg.total), wb, 0, ns, d.Hcq, acc);
+  tile_mma<I8, MT, NWW, D>(ap, make_rsrc(p.packed, pg.total), wb, 0, ns, acc);
   if (m0 >= d.T) return;
   const int g = lane >> 4, c = lane & 15;
   const int P = pg.nope_w + 1, hf = d.Dr / 2;
@@ -1087,12 +1165,17 @@ __global__ __launch_bounds__(64 * WM * WN) void k3_tiled(Dims d, Ptrs p, PackGeo
             v[ct][r] = acc[mt][i * 4 + ct][r];
         }
       if (!rope) {
+        // q^C goes out fragment-packed for the W^UK product, its k padding
+        // as zeros (the padded weight columns give exact zeros)
         if (m < d.T) {
+          const int wq = min(64, 32 * pg.nst_d - 64 * part);
+          const int64_t qtile = int64_t(d.N) * pg.nst_d * 1024;
+          uint8_t* qcb = reinterpret_cast<uint8_t*>(p.qc) + int64_t(h) * pg.nst_d * 1024;
 #pragma unroll
           for (int ct = 0; ct < 4; ++ct) {
             const int col = 16 * ct + 4 * g;
-            if (col < width)
-              *reinterpret_cast<uint2*>(p.qc + (int64_t(m) * d.N + h) * d.D + 64 * part + col) =
+            if (col < wq)
+              *reinterpret_cast<uint2*>(qcb + packed_offset(m, 64 * part + col, qtile, false)) =
                   pack_bf16x4(v[ct][0], v[ct][1], v[ct][2], v[ct][3]);
           }
         }
@@ -1152,9 +1235,11 @@ __global__ __launch_bounds__(64 * WM * WN) void k4_tiled(Dims d, Ptrs p, PackGeo
     wb[i] = jw < pg.uk_w ? uint32_t(pg.off_uk + int64_t(h * pg.uk_w + jw) * pg.nst_d * 4096) : kOOB;
   }
   const int ns = m0 < d.T ? pg.nst_d : 0;
-  const auto ap = rows_from<false, MT>(p.qc, int64_t(d.N) * d.D, int64_t(h) * d.D, m0, d.T);
+  const int64_t qtile = int64_t(d.N) * pg.nst_d * 1024, qh = int64_t(h) * pg.nst_d * 1024;
+  const auto ap = tiles_from<false, MT>(reinterpret_cast<const uint8_t*>(p.qc) + qh, qtile,
+                                        (d.T + 15) / 16, m0);
   typename Stage<false>::Acc acc[MT][NWW * 4];
-  tile_mma<false, MT, NWW, D>(ap, make_rsrc(p.packed, pg.total), wb, 0, ns, d.D, acc);
+  tile_mma<false, MT, NWW, D>(ap, make_rsrc(p.packed, pg.total), wb, 0, ns, acc);
   const int g = lane >> 4, c = lane & 15;
   if constexpr (!Q8) {
     if (m0 >= d.T) return;
@@ -1346,11 +1431,17 @@ Layout layout(const mla_prolog_desc& d) {
     if (pl.stream) part_rows = std::max<int64_t>(part_rows, int64_t(pl.Sp) * T);
     else part_rows = std::max<int64_t>(part_rows, int64_t(tiled_plan(d, T).S) * T);
   }
+  // c^Q and q^C are row-major on the row-major-weight path and
+  // fragment-packed (16-token tiles of 1 KB k-stages) on the packed path
+  const PackGeo g = pack_geo(d.He, d.Hcq, d.Hckv, d.N, d.D, d.Dr, d.in_dtype == MLA_INT8);
+  const size_t tiles = size_t((d.max_tokens + 15) / 16);
+  const size_t cq_bytes = std::max(size_t(d.max_tokens) * d.Hcq * 2, tiles * g.nst_cq * 1024);
+  const size_t qc_bytes = std::max(size_t(d.max_tokens) * d.N * d.D * 2, tiles * d.N * g.nst_d * 1024);
   L.part = 0;
   L.cq = align256(L.part + size_t(part_rows) * Ntot * 4);
-  L.cq_scale = align256(L.cq + size_t(d.max_tokens) * d.Hcq * 2);
+  L.cq_scale = align256(L.cq + cq_bytes);
   L.qc = align256(L.cq_scale + size_t(d.max_tokens) * 4);
-  L.total = align256(L.qc + size_t(d.max_tokens) * d.N * d.D * 2);
+  L.total = align256(L.qc + qc_bytes);
   return L;
 }
 
@@ -1478,7 +1569,7 @@ void packed_launch(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p, 
   k1_packed<I8, MT, 4, 2><<<dim3(tiles * pl.Sp), 256, 0, s>>>(d, p, g, pl.Sp, pl.sps);
   mark(1);
   const size_t y_bytes = size_t(d.Hcq + d.Hckv + d.Dr) * sizeof(double);
-  k2_norm<I8><<<dim3(d.T), 1024, y_bytes, s>>>(d, p, pl.Sp);
+  k2_norm<I8><<<dim3(d.T), 1024, y_bytes, s>>>(d, p, pl.Sp, g.nst_cq);
   mark(2);
   k3_packed<I8, MT, 8, 2><<<dim3(d.N * (g.nope_w + 1)), 512, 0, s>>>(d, p, g);
   mark(3);
@@ -1508,7 +1599,7 @@ void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs&
                                                                            tp.ngrp1);
   mark(1);
   const size_t y_bytes = size_t(d.Hcq + d.Hckv + d.Dr) * sizeof(double);
-  k2_norm<I8><<<dim3(d.T), 1024, y_bytes, s>>>(d, p, tp.S);
+  k2_norm<I8><<<dim3(d.T), 1024, y_bytes, s>>>(d, p, tp.S, g.nst_cq);
   mark(2);
   k3_tiled<I8, MT, 1, WM, 1, 2><<<dim3(tp.m3 * tp.ngrp3), 64 * WM, 0, s>>>(d, p, g, tp.m3);
   mark(3);
@@ -1525,7 +1616,7 @@ void tiled_large(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs& 
                                                                            tp.ngrp1);
   mark(1);
   const size_t y_bytes = size_t(d.Hcq + d.Hckv + d.Dr) * sizeof(double);
-  k2_norm<I8><<<dim3(d.T), 1024, y_bytes, s>>>(d, p, tp.S);
+  k2_norm<I8><<<dim3(d.T), 1024, y_bytes, s>>>(d, p, tp.S, g.nst_cq);
   mark(2);
   k3_tiled<I8, 8, 2, 2, 2, 2><<<dim3(tp.m3 * tp.ngrp3), 256, 0, s>>>(d, p, g, tp.m3);
   mark(3);
@@ -1702,8 +1793,8 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   mark(1);
 
   const size_t y_bytes = size_t(d.Hcq + d.Hckv + d.Dr) * sizeof(double);
-  if (i8) k2_norm<true><<<dim3(d.T), 1024, y_bytes, s>>>(d, p, pl.S);
-  else k2_norm<false><<<dim3(d.T), 1024, y_bytes, s>>>(d, p, pl.S);
+  if (i8) k2_norm<true><<<dim3(d.T), 1024, y_bytes, s>>>(d, p, pl.S, 0);
+  else k2_norm<false><<<dim3(d.T), 1024, y_bytes, s>>>(d, p, pl.S, 0);
   mark(2);
 
   const int nope_tiles = ceil_div(d.D, 64);
