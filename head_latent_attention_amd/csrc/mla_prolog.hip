@@ -54,6 +54,12 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// four floats -> four bf16 (RNE) in 8 bytes, first value lowest
+__device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float e) {
+  return make_uint2(uint32_t(f2bf(a)) | (uint32_t(f2bf(b)) << 16),
+                    uint32_t(f2bf(c)) | (uint32_t(f2bf(e)) << 16));
+}
+
 // symmetric int8 code of v for scale s > 0: nearest integer (ties to even)
 // of v / s, kept within [-127, 127]
 __device__ __forceinline__ int8_t quant_code(float v, float s) {
@@ -697,117 +703,189 @@ __global__ __launch_bounds__(64 * NW) void k1_packed(Dims d, Ptrs p, PackGeo pg,
     }
 }
 
-// K2: one block per token, 1024 threads.  Sums the S split partials (in
-// split order) of x [W^DQ | W^DkvKr] into y, then applies both RmsNorms,
-// writes c^Q (bf16, or per-token int8 + scale) to the workspace and the
-// c^KV / RoPE(k^R) rows to the token's cacheIndex slot.  y, the RMS factors
-// and c are computed in double (a few thousand values per token), so the
-// per-token int8 decision of c^Q sees c rounded once to fp32.  With cq_nst
-// > 0, c^Q is stored fragment-packed (cq_nst k-stages per 16-token tile, k
-// padding as zeros) for the packed-weight kernels; with 0, row-major.
-__device__ double block_sum_f64(double v, double* red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+// K2: NWT waves per token, TPB tokens per block.  y is the split-order sum
+// of the token's S partials of x [W^DQ | W^DkvKr] (in double; in int8 mode
+// the exact int32 sum times the token and column scales).  A first pass sums
+// the squares of the c^Q and c^KV parts (and, in int8 mode, finds the
+// largest |gamma y| of the c^Q part), keeping each lane's first CPL 8-column
+// chunks of y in registers; a second pass writes c^Q (bf16, or per-token
+// int8 + scale), the c^KV row at the token's cacheIndex slot and, through a
+// small LDS row, the RoPE'd k^R row, reloading only the chunks beyond CPL.  The norms are computed in
+// double, so the per-token int8 decision of c^Q sees c rounded once to fp32.
+// With cq_nst > 0, c^Q is stored fragment-packed (cq_nst k-stages per
+// 16-token tile, the k padding as zeros); with 0, row-major.
+__device__ __forceinline__ double wave_sum_f64(double v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  double r = red[0];
-  for (int w = 1; w < nw; ++w) r += red[w];
-  return r;
+  return v;
+}
+__device__ __forceinline__ double wave_max_f64(double v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
+  return v;
 }
 
-template <bool I8>
-__global__ __launch_bounds__(1024) void k2_norm(Dims d, Ptrs p, int S, int cq_nst) {
-  extern __shared__ double y[];  // Hcq + Hckv + Dr
-  __shared__ double red[16];
-  __shared__ float redf[16];
-  const int t = blockIdx.x, tid = threadIdx.x;
-  const int Nkr = d.Hckv + d.Dr, Ntot = d.Hcq + Nkr, n4 = Ntot / 4;
+template <bool I8, int NWT, int TPB, int CPL>
+__global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S, int cq_nst) {
+  __shared__ double red[NWT * TPB][3];
+  __shared__ double ry[TPB][64];   // the token's y of the k^R columns (Dr <= 64)
+  const int w = threadIdx.x >> 6;
+  const int lane = (w % NWT) * 64 + (threadIdx.x & 63);   // lane among the token's waves
+  constexpr int L = 64 * NWT;
+  const int t = blockIdx.x * TPB + w / NWT;
+  const bool active = t < d.T;
+  const int Ntot = d.Hcq + d.Hckv + d.Dr;
+  const int cq_c = d.Hcq / 8, kv_c = d.Hckv / 8, chunks = cq_c + kv_c + d.Dr / 8;
   const rsrc_t P = make_rsrc(p.part, int64_t(S) * d.T * Ntot * 4);
-  for (int c4 = tid; c4 < n4; c4 += 1024) {
-    double v[4] = {0.0, 0.0, 0.0, 0.0};
-    int32_t iv[4] = {0, 0, 0, 0};
-    for (int s0 = 0; s0 < S; s0 += 16) {
+  const double sx = (I8 && active) ? double(p.sx[t]) : 1.0;
+  // y of the eight columns 8j .. 8j+7; the loads of eight splits at a time
+  // are issued together (a missing split reads as zeros, an exact no-op)
+  auto y8 = [&](int j, double (&v)[8]) {
+    double f[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int32_t iv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int s0 = 0; s0 < S; s0 += 8) {
       uint4 r[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        r[e] = bload16(P, s0 + e < S ? uint32_t(((int64_t(s0 + e) * d.T + t) * Ntot + 4 * c4) * 4) : kOOB);
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t o = uint32_t(((int64_t(s0 + e) * d.T + t) * Ntot + 8 * j) * 4);
+        r[2 * e] = bload16(P, s0 + e < S ? o : kOOB);
+        r[2 * e + 1] = bload16(P, s0 + e < S ? o + 16 : kOOB);
+      }
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        if constexpr (I8) {
-          const int4 q = __builtin_bit_cast(int4, r[e]);
-          iv[0] += q.x; iv[1] += q.y; iv[2] += q.z; iv[3] += q.w;
-        } else {
-          const float4 q = __builtin_bit_cast(float4, r[e]);
-          v[0] += q.x; v[1] += q.y; v[2] += q.z; v[3] += q.w;
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w8[8] = {r[2 * e].x, r[2 * e].y, r[2 * e].z, r[2 * e].w,
+                                r[2 * e + 1].x, r[2 * e + 1].y, r[2 * e + 1].z, r[2 * e + 1].w};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          if constexpr (I8) iv[c] += int32_t(w8[c]);
+          else f[c] += double(__uint_as_float(w8[c]));
         }
       }
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int n = 4 * c4 + e;
+    for (int e = 0; e < 8; ++e) {
       if constexpr (I8) {
+        const int n = 8 * j + e;
         const double sw = n < d.Hcq ? p.sw_dq[n] : p.sw_dkv_kr[n - d.Hcq];
-        v[e] = double(iv[e]) * double(p.sx[t]) * sw;
+        v[e] = double(iv[e]) * sx * sw;
+      } else {
+        v[e] = f[e];
       }
-      y[n] = v[e];
+    }
+  };
+
+  double sq = 0.0, skv = 0.0, gmax = 0.0;
+  auto sums = [&](int j, const double (&v)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (j < cq_c) {
+        sq += v[e] * v[e];
+        if constexpr (I8) gmax = fmax(gmax, fabs(double(bf2f(p.gamma_cq[8 * j + e])) * v[e]));
+      } else if (j < cq_c + kv_c) {
+        skv += v[e] * v[e];
+      }
+    }
+  };
+  double yv[CPL][8];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int j = lane + c * L;
+    if (active && j < chunks) {
+      y8(j, yv[c]);
+      sums(j, yv[c]);
     }
   }
-  __syncthreads();
-  double sq = 0.0, skv = 0.0;
-  for (int n = tid; n < d.Hcq; n += 1024) sq += y[n] * y[n];
-  for (int n = tid; n < d.Hckv; n += 1024) skv += y[d.Hcq + n] * y[d.Hcq + n];
-  sq = block_sum_f64(sq, red);
-  skv = block_sum_f64(skv, red);
+  for (int j = lane + CPL * L; active && j < chunks; j += L) {
+    double v[8];
+    y8(j, v);
+    sums(j, v);
+  }
+  sq = wave_sum_f64(sq);
+  skv = wave_sum_f64(skv);
+  gmax = wave_max_f64(gmax);
+  if constexpr (NWT > 1) {
+    if ((threadIdx.x & 63) == 0) { red[w][0] = sq; red[w][1] = skv; red[w][2] = gmax; }
+    __syncthreads();
+    const int w0 = w - w % NWT;
+    sq = red[w0][0]; skv = red[w0][1]; gmax = red[w0][2];
+#pragma unroll
+    for (int k = 1; k < NWT; ++k) {
+      sq += red[w0 + k][0]; skv += red[w0 + k][1]; gmax = fmax(gmax, red[w0 + k][2]);
+    }
+  }
+  if (!active) return;
   const double rms_q = sqrt(sq / double(d.Hcq) + d.eps_cq);
   const double rms_kv = sqrt(skv / double(d.Hckv) + d.eps_ckv);
-  if constexpr (I8) {
-    float amax = 0.0f;
-    for (int n = tid; n < d.Hcq; n += 1024) {
-      const float c = float(double(bf2f(p.gamma_cq[n])) * y[n] / rms_q);
-      y[n] = c;
-      amax = fmaxf(amax, fabsf(c));
-    }
-    for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-    __syncthreads();
-    if ((tid & 63) == 0) redf[tid >> 6] = amax;
-    __syncthreads();
-    amax = redf[0];
-    for (int w = 1; w < 16; ++w) amax = fmaxf(amax, redf[w]);
-    const float sc = amax / 127.0f;
-    if (cq_nst) {
-      const int64_t tile = int64_t(cq_nst) * 1024;
-      for (int n = tid; n < cq_nst * 64; n += 1024)
-        reinterpret_cast<int8_t*>(p.cq)[packed_offset(t, n, tile, true)] =
-            (n < d.Hcq && sc > 0.0f) ? quant_code(float(y[n]), sc) : int8_t(0);
-    } else {
-      int8_t* cq = reinterpret_cast<int8_t*>(p.cq) + int64_t(t) * d.Hcq;
-      for (int n = tid; n < d.Hcq; n += 1024) cq[n] = sc > 0.0f ? quant_code(float(y[n]), sc) : 0;
-    }
-    if (tid == 0) p.cq_scale[t] = sc;
-  } else {
-    if (cq_nst) {
-      const int64_t tile = int64_t(cq_nst) * 1024;
-      for (int n = tid; n < cq_nst * 32; n += 1024)
-        *reinterpret_cast<uint16_t*>(p.cq + packed_offset(t, n, tile, false)) =
-            n < d.Hcq ? f2bf(float(double(bf2f(p.gamma_cq[n])) * y[n] / rms_q)) : uint16_t(0);
-    } else {
-      uint16_t* cq = reinterpret_cast<uint16_t*>(p.cq) + int64_t(t) * d.Hcq;
-      for (int n = tid; n < d.Hcq; n += 1024)
-        cq[n] = f2bf(float(double(bf2f(p.gamma_cq[n])) * y[n] / rms_q));
-    }
-  }
+  float sc = 0.0f;
+  if constexpr (I8) sc = float(gmax / rms_q) / 127.0f;
   const int64_t slot = p.cache_index[t];
-  if (slot < 0 || slot >= d.slots) return;
-  uint16_t* kv = p.kv_cache + slot * d.Hckv;
-  for (int n = tid; n < d.Hckv; n += 1024)
-    kv[n] = f2bf(float(double(bf2f(p.gamma_ckv[n])) * y[d.Hcq + n] / rms_kv));
+  const bool cache = slot >= 0 && slot < d.slots;
+  const int64_t tile = int64_t(cq_nst) * 1024;
+
+  auto store_cq = [&](int j, const float (&c)[8]) {
+    if constexpr (I8) {
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t code = uint8_t(sc > 0.0f ? quant_code(c[e], sc) : int8_t(0));
+        if (e < 4) lo |= code << (8 * e);
+        else hi |= code << (8 * (e - 4));
+      }
+      const int64_t o = cq_nst ? packed_offset(t, 8 * j, tile, true) : int64_t(t) * d.Hcq + 8 * j;
+      *reinterpret_cast<uint2*>(p.cq + o) = make_uint2(lo, hi);
+    } else {
+      const uint2 a = pack_bf16x4(c[0], c[1], c[2], c[3]), b = pack_bf16x4(c[4], c[5], c[6], c[7]);
+      const int64_t o = cq_nst ? packed_offset(t, 8 * j, tile, false) : (int64_t(t) * d.Hcq + 8 * j) * 2;
+      *reinterpret_cast<uint4*>(p.cq + o) = make_uint4(a.x, a.y, b.x, b.y);
+    }
+  };
+  auto emit = [&](int j, const double (&v)[8]) {
+    float c[8];
+    if (j < cq_c) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) c[e] = float(double(bf2f(p.gamma_cq[8 * j + e])) * v[e] / rms_q);
+      store_cq(j, c);
+    } else if (j >= cq_c + kv_c) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ry[w / NWT][8 * (j - cq_c - kv_c) + e] = v[e];
+    } else if (cache) {
+      const int jk = j - cq_c;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) c[e] = float(double(bf2f(p.gamma_ckv[8 * jk + e])) * v[e] / rms_kv);
+      const uint2 a = pack_bf16x4(c[0], c[1], c[2], c[3]), b = pack_bf16x4(c[4], c[5], c[6], c[7]);
+      *reinterpret_cast<uint4*>(p.kv_cache + slot * d.Hckv + 8 * jk) = make_uint4(a.x, a.y, b.x, b.y);
+    }
+  };
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int j = lane + c * L;
+    if (j < chunks) emit(j, yv[c]);
+  }
+  for (int j = lane + CPL * L; j < chunks; j += L) {
+    if (j >= cq_c && !cache) break;
+    double v[8];
+    y8(j, v);
+    emit(j, v);
+  }
+  // the zero k padding of packed c^Q
+  const int cq_chunks = cq_nst ? cq_nst * (I8 ? 8 : 4) : cq_c;
+  for (int j = cq_c + lane; j < cq_chunks; j += L) {
+    const float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    store_cq(j, z);
+  }
+  if (I8 && lane == 0) p.cq_scale[t] = sc;
+  if (!cache) return;   // the same for every wave of the token
+  if constexpr (NWT > 1) {
+    __syncthreads();
+  } else {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
   const int h = d.Dr / 2;
-  const double* yr = y + d.Hcq + d.Hckv;
+  const double* yr = ry[w / NWT];
   const uint16_t* cs = p.cos + int64_t(t) * d.Dr;
   const uint16_t* sn = p.sin + int64_t(t) * d.Dr;
   uint16_t* kr = p.kr_cache + slot * d.Dr;
-  for (int i = tid; i < h; i += 1024) {
+  for (int i = lane; i < h; i += L) {
     const double a = yr[i], b = yr[i + h];
     kr[i] = f2bf(float(a * bf2f(cs[i]) - b * bf2f(sn[i])));
     kr[i + h] = f2bf(float(b * bf2f(cs[i + h]) + a * bf2f(sn[i + h])));
@@ -1054,11 +1132,6 @@ __device__ __forceinline__ APacked<I8, MT> tiles_from(const void* base, int64_t 
   return APacked<I8, MT>{make_rsrc(static_cast<const uint8_t*>(base) + (t0 < tiles ? t0 : 0) * tile,
                                    (tiles - t0) * tile),
                          uint32_t(tile)};
-}
-
-__device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float e) {
-  return make_uint2(uint32_t(f2bf(a)) | (uint32_t(f2bf(b)) << 16),
-                    uint32_t(f2bf(c)) | (uint32_t(f2bf(e)) << 16));
 }
 
 // K1t: grid (token tiles fastest, then window groups, then k splits).  Wave
@@ -1470,14 +1543,15 @@ mla_status check_desc(const mla_prolog_desc* d) {
   for (int64_t v : vec_dims)
     if (v % 8) return MLA_ERR_UNSUPPORTED;
   if (d->Dr > 64 || d->Hckv > 512 || d->D > 512 || d->He > 65536) return MLA_ERR_UNSUPPORTED;
-  // the norm kernel keeps one token's Hcq + Hckv + Dr values in 64 KB of LDS
-  if (d->Hcq + d->Hckv + d->Dr > 8192) return MLA_ERR_UNSUPPORTED;
   // int8 operands move in 16-byte (16-element) chunks that must not cross a
   // row or column-block end
   if (d->in_dtype == MLA_INT8 &&
       (d->He % 16 || d->Hcq % 16 || (d->Hckv + d->Dr) % 16 || d->D % 16 || d->Dr % 16))
     return MLA_ERR_UNSUPPORTED;
   if (d->N * (d->D + d->Dr) > (1 << 24)) return MLA_ERR_UNSUPPORTED;
+  // the norm kernel addresses the split partials with 32-bit offsets
+  const Layout L = layout(*d);
+  if (L.cq - L.part >= size_t(kOOB)) return MLA_ERR_UNSUPPORTED;
   return MLA_OK;
 }
 
@@ -1556,6 +1630,13 @@ void launch_k4(int ntw, dim3 grid, hipStream_t s, const Dims& d, const Ptrs& p) 
   }
 }
 
+// K2 with eight waves per token when there are few tokens, one otherwise.
+template <bool I8>
+void launch_norm(hipStream_t s, const Dims& d, const Ptrs& p, int S, int cq_nst) {
+  if (d.T <= 512) k2_norm<I8, 8, 1, 1><<<dim3(d.T), 512, 0, s>>>(d, p, S, cq_nst);
+  else k2_norm<I8, 1, 4, 1><<<dim3((d.T + 3) / 4), 256, 0, s>>>(d, p, S, cq_nst);
+}
+
 // The int8-query W^UK kernel gives one wave to each 64-column window of Hckv.
 bool packed_fits(const mla_prolog_desc& dd) { return (dd.Hckv + 63) / 64 <= 8; }
 
@@ -1568,8 +1649,7 @@ void packed_launch(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p, 
   const int tiles = g.win_dq + g.win_kr;
   k1_packed<I8, MT, 4, 2><<<dim3(tiles * pl.Sp), 256, 0, s>>>(d, p, g, pl.Sp, pl.sps);
   mark(1);
-  const size_t y_bytes = size_t(d.Hcq + d.Hckv + d.Dr) * sizeof(double);
-  k2_norm<I8><<<dim3(d.T), 1024, y_bytes, s>>>(d, p, pl.Sp, g.nst_cq);
+  launch_norm<I8>(s, d, p, pl.Sp, g.nst_cq);
   mark(2);
   k3_packed<I8, MT, 8, 2><<<dim3(d.N * (g.nope_w + 1)), 512, 0, s>>>(d, p, g);
   mark(3);
@@ -1598,8 +1678,7 @@ void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs&
   k1_tiled<I8, MT, 1, 1, 1, 2><<<dim3(tp.m1 * tp.ngrp1 * tp.S), 64, 0, s>>>(d, p, g, tp.sps, tp.m1,
                                                                            tp.ngrp1);
   mark(1);
-  const size_t y_bytes = size_t(d.Hcq + d.Hckv + d.Dr) * sizeof(double);
-  k2_norm<I8><<<dim3(d.T), 1024, y_bytes, s>>>(d, p, tp.S, g.nst_cq);
+  launch_norm<I8>(s, d, p, tp.S, g.nst_cq);
   mark(2);
   k3_tiled<I8, MT, 1, WM, 1, 2><<<dim3(tp.m3 * tp.ngrp3), 64 * WM, 0, s>>>(d, p, g, tp.m3);
   mark(3);
@@ -1615,8 +1694,7 @@ void tiled_large(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs& 
   k1_tiled<I8, 8, 2, 2, 2, 2><<<dim3(tp.m1 * tp.ngrp1 * tp.S), 256, 0, s>>>(d, p, g, tp.sps, tp.m1,
                                                                            tp.ngrp1);
   mark(1);
-  const size_t y_bytes = size_t(d.Hcq + d.Hckv + d.Dr) * sizeof(double);
-  k2_norm<I8><<<dim3(d.T), 1024, y_bytes, s>>>(d, p, tp.S, g.nst_cq);
+  launch_norm<I8>(s, d, p, tp.S, g.nst_cq);
   mark(2);
   k3_tiled<I8, 8, 2, 2, 2, 2><<<dim3(tp.m3 * tp.ngrp3), 256, 0, s>>>(d, p, g, tp.m3);
   mark(3);
@@ -1792,9 +1870,8 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   else launch_k1<false>(pl.mt1, g1, s, d, p, tiles_q, pl.kps);
   mark(1);
 
-  const size_t y_bytes = size_t(d.Hcq + d.Hckv + d.Dr) * sizeof(double);
-  if (i8) k2_norm<true><<<dim3(d.T), 1024, y_bytes, s>>>(d, p, pl.S, 0);
-  else k2_norm<false><<<dim3(d.T), 1024, y_bytes, s>>>(d, p, pl.S, 0);
+  if (i8) launch_norm<true>(s, d, p, pl.S, 0);
+  else launch_norm<false>(s, d, p, pl.S, 0);
   mark(2);
 
   const int nope_tiles = ceil_div(d.D, 64);
