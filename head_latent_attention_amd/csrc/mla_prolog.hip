@@ -453,6 +453,12 @@ struct APlain {
   __device__ __forceinline__ typename Stage<I8>::Frag frag(const uint4 (&r)[NR], int mt) const {
     return __builtin_bit_cast(typename Stage<I8>::Frag, r[mt]);
   }
+  // the calling lane's 16 bytes of fragment tile c (rows 16c..) of stage st
+  __device__ __forceinline__ uint4 load1(int c, int st, bool ok) const {
+    const int lane = threadIdx.x & 63;
+    const int m = 16 * c + (lane & 15), ka = st * Stage<I8>::KS + Stage<I8>::KL * (lane >> 4);
+    return bload16(A, ok && m < M && ka < ke ? uint32_t(m) * lda + uint32_t(ka) * Stage<I8>::EB : kOOB);
+  }
 };
 
 // APacked reads fragment-packed activations: every 16-row tile stores its
@@ -472,6 +478,10 @@ struct APacked {
   }
   __device__ __forceinline__ typename Stage<I8>::Frag frag(const uint4 (&r)[NR], int mt) const {
     return __builtin_bit_cast(typename Stage<I8>::Frag, r[mt]);
+  }
+  __device__ __forceinline__ uint4 load1(int c, int st, bool ok) const {
+    const uint32_t lane = threadIdx.x & 63;
+    return bload16(A, ok ? uint32_t(c) * tile + uint32_t(st) * 1024u + lane * 16u : kOOB);
   }
 };
 
@@ -741,7 +751,17 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
   auto y8 = [&](int j, double (&v)[8]) {
     double f[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     int32_t iv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int s0 = 0; s0 < S; s0 += 8) {
+    if (S == 1) {
+      const uint32_t o = uint32_t((int64_t(t) * Ntot + 8 * j) * 4);
+      const uint4 a = bload16(P, o), b = bload16(P, o + 16);
+      const uint32_t w8[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        if constexpr (I8) iv[c] = int32_t(w8[c]);
+        else f[c] = double(__uint_as_float(w8[c]));
+      }
+    }
+    for (int s0 = 0; S > 1 && s0 < S; s0 += 8) {
       uint4 r[16];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -1052,6 +1072,250 @@ __global__ __launch_bounds__(512) void k4_packed_q8(Dims d, Ptrs p, PackGeo pg) 
     }
 }
 
+// Sum of the accumulators of each group of G consecutive waves into the
+// group's first wave, in wave order, for the first `groups` groups.
+// red: groups * (G - 1) * MT * 16 * 64 words of LDS.  Starts and ends with a
+// block barrier.
+template <int MT, class Acc>
+__device__ __forceinline__ void reduce_groups(Acc (&acc)[MT][4], uint32_t* red, int G, int groups) {
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = w / G, r = w % G;
+  constexpr int W = MT * 16 * 64;
+  __syncthreads();
+  if (grp < groups && r > 0) {
+    uint32_t* o = red + (grp * (G - 1) + r - 1) * W;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const auto e = acc[mt][ct][i];
+          o[((mt * 4 + ct) * 4 + i) * 64 + lane] = __builtin_bit_cast(uint32_t, e);
+        }
+  }
+  __syncthreads();
+  if (grp < groups && r == 0) {
+    for (int k = 1; k < G; ++k) {
+      const uint32_t* o = red + (grp * (G - 1) + k - 1) * W;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            using E = decltype(acc[mt][ct][i] + 0);
+            acc[mt][ct][i] += __builtin_bit_cast(E, o[((mt * 4 + ct) * 4 + i) * 64 + lane]);
+          }
+    }
+  }
+  __syncthreads();
+}
+
+// Fragment-packed activations held in LDS (tiles `tile` bytes apart).
+template <int MT>
+struct ALds {
+  static constexpr int NR = MT;
+  const uint8_t* base;
+  uint32_t tile;
+  __device__ __forceinline__ void load(uint4 (&r)[NR], int st, bool ok) const {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      r[mt] = ok ? *reinterpret_cast<const uint4*>(base + mt * tile + st * 1024 + lane * 16)
+                 : make_uint4(0, 0, 0, 0);
+  }
+};
+
+// K34s: the up-projection and the W^UK product of one head in one block, for
+// small token counts (T <= 16 * MT).  Blocks [0, N): head h.  Its W^UK
+// fragments are loaded first (one wave group per 64-column window of Hckv,
+// the groups splitting the D stages), so their latency hides under the first
+// phase; then one wave group per nope window of W^UqQr splits the Hcq stages,
+// the groups are summed, and q^C is rounded to bf16 straight into LDS,
+// fragment-packed (it never goes to HBM); then q^C W^UK[h] gives q^N (bf16,
+// or the per-(token, head) int8 quantisation with the row maximum taken over
+// the window groups).  Blocks [N, 2N): head h's rope window through RoPE to
+// queryRopeOut.  512 threads.
+constexpr int kK34Waves = 8, kK34Stages = 4;
+
+template <bool I8, int MT, int D, bool Q8>
+__global__ __launch_bounds__(512) void k34_stream(Dims d, Ptrs p, PackGeo pg) {
+  using St = Stage<I8>;
+  constexpr int NW = kK34Waves, NS2 = kK34Stages, W = MT * 16 * 64;
+  constexpr int RED = (NW - 1) * W * 4, QCL = 16 * MT * 4 * 32 * 2;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[RED + QCL + NW * 16 * MT * 4];
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const bool rope_blk = int(blockIdx.x) >= d.N;
+  const int h = rope_blk ? blockIdx.x - d.N : blockIdx.x;
+  const int P = pg.nope_w;
+  const rsrc_t Wp = make_rsrc(p.packed, pg.total);
+  const int64_t ctile = int64_t(pg.nst_cq) * 1024;
+  const APacked<I8, MT> ap{make_rsrc(p.cq, int64_t((d.T + 15) / 16) * ctile), uint32_t(ctile)};
+  uint32_t* red = reinterpret_cast<uint32_t*>(lds);
+  typename St::Acc acc[MT][4];
+
+  if (rope_blk) {
+    const int col0 = h * (d.D + d.Dr) + d.D;
+    const int ns = w < pg.nst_cq ? (pg.nst_cq - w + NW - 1) / NW : 0;
+    const int64_t wbase = pg.off_uq + int64_t(h * (P + 1) + P) * pg.nst_cq * 4096;
+    stream_packed<I8, MT, D>(ap, Wp, uint32_t(wbase), w, NW, ns, acc);
+    reduce_groups<MT>(acc, red, NW, 1);
+    float* E = reinterpret_cast<float*>(lds);  // [16*MT][65], over the reduction area
+    if (w == 0) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int ml = 16 * mt + 4 * g + i, col = 16 * ct + c;
+            float v;
+            if constexpr (I8)
+              v = (ml < d.T && col < d.Dr)
+                      ? static_cast<float>(acc[mt][ct][i]) * p.cq_scale[ml] * p.sw_uq_qr[col0 + col]
+                      : 0.0f;
+            else
+              v = acc[mt][ct][i];
+            E[ml * 65 + col] = v;
+          }
+    }
+    __syncthreads();
+    const int hf = d.Dr / 2;
+    for (int idx = threadIdx.x; idx < 16 * MT * hf; idx += 64 * NW) {
+      const int ml = idx / hf, i = idx % hf;
+      if (ml >= d.T) continue;
+      const float a = E[ml * 65 + i], b = E[ml * 65 + i + hf];
+      const uint16_t* cs = p.cos + int64_t(ml) * d.Dr;
+      const uint16_t* sn = p.sin + int64_t(ml) * d.Dr;
+      uint16_t* o = p.qr_out + (int64_t(ml) * d.N + h) * d.Dr;
+      o[i] = f2bf(a * bf2f(cs[i]) - b * bf2f(sn[i]));
+      o[i + hf] = f2bf(b * bf2f(cs[i + hf]) + a * bf2f(sn[i + hf]));
+    }
+    return;
+  }
+
+  // W^UK[h] fragments of this wave's stages
+  const int uk_w = pg.uk_w, nst_d = pg.nst_d;
+  const int G2 = NW / uk_w, jw = w / G2, r2 = w % G2;
+  const bool act2 = jw < uk_w && r2 < nst_d;
+  const int ns2 = act2 ? (nst_d - r2 + G2 - 1) / G2 : 0;
+  const uint32_t wb2 = uint32_t(pg.off_uk + int64_t(h * uk_w + (jw < uk_w ? jw : 0)) * nst_d * 4096);
+  uint4 bk[NS2][4];
+#pragma unroll
+  for (int j = 0; j < NS2; ++j)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+      bk[j][ct] = bload16(Wp, j < ns2 ? wb2 + uint32_t(r2 + j * G2) * 4096u + uint32_t(ct * 1024 + lane * 16)
+                                      : kOOB);
+
+  // phase 1: the nope windows
+  const int G1 = NW / P, p1 = w / G1, r1 = w % G1;
+  const bool act1 = p1 < P && r1 < pg.nst_cq;
+  const int ns1 = act1 ? (pg.nst_cq - r1 + G1 - 1) / G1 : 0;
+  const uint32_t wb1 = uint32_t(pg.off_uq + int64_t(h * (P + 1) + (p1 < P ? p1 : 0)) * pg.nst_cq * 4096);
+  stream_packed<I8, MT, D>(ap, Wp, wb1, r1, G1, ns1, acc);
+  reduce_groups<MT>(acc, red, G1, P);
+  uint8_t* qcl = lds + RED;
+  const int64_t qt = int64_t(nst_d) * 1024;
+  if (p1 < P && r1 == 0) {
+    const int col0 = h * (d.D + d.Dr) + 64 * p1;
+    const int width = min(64, d.D - 64 * p1), wq = min(64, 32 * nst_d - 64 * p1);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * mt + 4 * g + i, col = 16 * ct + c;
+          if (col >= wq) continue;
+          float v;
+          if constexpr (I8)
+            v = (row < d.T && col < width)
+                    ? static_cast<float>(acc[mt][ct][i]) * p.cq_scale[row] * p.sw_uq_qr[col0 + col]
+                    : 0.0f;
+          else
+            v = acc[mt][ct][i];
+          *reinterpret_cast<uint16_t*>(qcl + packed_offset(row, 64 * p1 + col, qt, false)) = f2bf(v);
+        }
+  }
+  __syncthreads();
+
+  // phase 2: q^N = q^C W^UK[h]
+  const ALds<MT> al{qcl, uint32_t(qt)};
+  typename Stage<false>::Acc acc2[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) acc2[mt][ct] = f32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int j = 0; j < NS2; ++j) {
+    if (j >= ns2) break;
+    uint4 a[MT];
+    al.load(a, r2 + j * G2, true);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const bf16x8 af = __builtin_bit_cast(bf16x8, a[mt]);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) acc2[mt][ct] = mfma(af, __builtin_bit_cast(bf16x8, bk[j][ct]), acc2[mt][ct]);
+    }
+  }
+  reduce_groups<MT>(acc2, red, G2, uk_w);
+  const bool lead = jw < uk_w && r2 == 0;
+  const int width2 = lead ? min(64, d.Hckv - 64 * jw) : 0;
+  if constexpr (!Q8) {
+    if (!lead) return;
+    uint16_t* qo = static_cast<uint16_t*>(p.q_out);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * mt + 4 * g + i;
+        if (row >= d.T) continue;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const int col = 16 * ct + c;
+          if (col < width2) qo[(int64_t(row) * d.N + h) * d.Hckv + 64 * jw + col] = f2bf(acc2[mt][ct][i]);
+        }
+      }
+  } else {
+    float* rmax = reinterpret_cast<float*>(lds + RED + QCL);   // [NW][16*MT]
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float mx = 0.0f;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+          if (16 * ct + c < width2) mx = fmaxf(mx, fabsf(acc2[mt][ct][i]));
+        for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        if (lead && c == 0) rmax[jw * 16 * MT + 16 * mt + 4 * g + i] = mx;
+      }
+    __syncthreads();
+    if (!lead) return;
+    int8_t* qo = static_cast<int8_t*>(p.q_out);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * mt + 4 * g + i;
+        if (row >= d.T) continue;
+        float amax = rmax[16 * mt + 4 * g + i];
+        for (int k = 1; k < uk_w; ++k) amax = fmaxf(amax, rmax[k * 16 * MT + 16 * mt + 4 * g + i]);
+        const float sc = amax / 127.0f;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const int col = 16 * ct + c;
+          if (col < width2)
+            qo[(int64_t(row) * d.N + h) * d.Hckv + 64 * jw + col] =
+                sc > 0.0f ? quant_code(acc2[mt][ct][i], sc) : int8_t(0);
+        }
+        if (jw == 0 && c == 0) p.q_scale[int64_t(row) * d.N + h] = sc;
+      }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Tiled path for larger token counts.  Every wave owns a 16*MT-token x
 // 64*NWW-column output tile and streams the packed k-stages of its NWW
@@ -1134,11 +1398,90 @@ __device__ __forceinline__ APacked<I8, MT> tiles_from(const void* base, int64_t 
                          uint32_t(tile)};
 }
 
+// Block-cooperative tile product for large token counts.  The block's WM*MT
+// activation tiles and its WN*NWW weight windows (consecutive in the packed
+// buffer, `wstride` bytes apart, the first at wbase, nwin of them valid) of
+// each k-stage are copied, 1 KB per wave load, into a two-buffer LDS ring;
+// every wave then reads its fragments with conflict-free 16-byte LDS reads.
+// The global loads run three stages ahead of the MFMAs through two register
+// sets.  ns must be the same for the whole block.
+template <bool I8, int MT, int NWW, int WM, int WN, class AP>
+__device__ __forceinline__ void tile_mma_lds(const AP& ap, rsrc_t Wp, uint32_t wbase, uint32_t wstride,
+                                             int nwin, int s0, int ns, uint8_t* lds,
+                                             typename Stage<I8>::Acc (&acc)[MT][NWW * 4]) {
+  using S = Stage<I8>;
+  constexpr int NW = WM * WN, AT = MT * WM, BC = NWW * WN * 4, CH = (AT + BC) / NW;
+  static_assert(AT % NW == 0 && BC % NW == 0, "the stage chunks must split evenly over the waves");
+  constexpr int BUF = (AT + BC) * 1024;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w % WM, wn = w / WM;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < NWW * 4; ++j) acc[mt][j] = typename S::Acc{0, 0, 0, 0};
+  auto gload = [&](uint4 (&r)[CH], int j) {
+    const bool ok = j < ns;
+    const int st = s0 + j;
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      const int c = w + q * NW;   // chunk c: activation tile c, then weight chunk c - AT
+      if (q < AT / NW) {
+        r[q] = ap.load1(c, st, ok);
+      } else {
+        const int b = c - AT, v = b >> 2;
+        r[q] = bload16(Wp, ok && v < nwin ? wbase + uint32_t(v) * wstride + uint32_t(st) * 4096u +
+                                                uint32_t((b & 3) * 1024 + lane * 16)
+                                          : kOOB);
+      }
+    }
+  };
+  auto lwrite = [&](const uint4 (&r)[CH], int buf) {
+#pragma unroll
+    for (int q = 0; q < CH; ++q)
+      *reinterpret_cast<uint4*>(lds + buf * BUF + (w + q * NW) * 1024 + lane * 16) = r[q];
+  };
+  auto compute = [&](int buf) {
+    const uint8_t* L = lds + buf * BUF;
+    typename S::Frag bf[NWW * 4];
+#pragma unroll
+    for (int j = 0; j < NWW * 4; ++j)
+      bf[j] = *reinterpret_cast<const typename S::Frag*>(L + (AT + wn * NWW * 4 + j) * 1024 + lane * 16);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const typename S::Frag af =
+          *reinterpret_cast<const typename S::Frag*>(L + (wm * MT + mt) * 1024 + lane * 16);
+#pragma unroll
+      for (int j = 0; j < NWW * 4; ++j) acc[mt][j] = mfma(bf[j], af, acc[mt][j]);
+    }
+  };
+  uint4 R0[CH], R1[CH];   // stage k waits in R(k % 2)
+  gload(R0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  gload(R1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  lwrite(R0, 0);
+  gload(R0, 2);
+  __syncthreads();
+  for (int j = 0; j < ns; j += 2) {
+    compute(0);                      // stage j
+    __builtin_amdgcn_sched_barrier(0);
+    if (j + 1 < ns) lwrite(R1, 1);   // stage j + 1
+    gload(R1, j + 3);
+    __syncthreads();
+    if (j + 1 >= ns) break;
+    compute(1);                      // stage j + 1
+    __builtin_amdgcn_sched_barrier(0);
+    if (j + 2 < ns) lwrite(R0, 0);   // stage j + 2
+    gload(R0, j + 4);
+    __syncthreads();
+  }
+}
+
 // K1t: grid (token tiles fastest, then window groups, then k splits).  Wave
 // (wm, wn) takes tokens 16*MT*wm.. of the block's token tile and windows
 // NWW*wn.. of its group of [W^DQ | W^DkvKr] windows; the split's stages go
 // into fp32 (int32) partials, one 16-byte store per 4 columns.
-template <bool I8, int MT, int NWW, int WM, int WN, int D>
+template <bool I8, int MT, int NWW, int WM, int WN, int D, bool LC = false>
 __global__ __launch_bounds__(64 * WM * WN) void k1_tiled(Dims d, Ptrs p, PackGeo pg, int sps, int mtiles,
                                                       int ngrp) {
   using St = Stage<I8>;
@@ -1157,10 +1500,20 @@ __global__ __launch_bounds__(64 * WM * WN) void k1_tiled(Dims d, Ptrs p, PackGeo
     wb[i] = j < tiles ? uint32_t(pg.off_dq + int64_t(j) * pg.nst_he * 4096) : kOOB;
   }
   const int s0 = split * sps;
-  const int ns = m0 < d.T ? max(0, min(pg.nst_he, s0 + sps) - s0) : 0;
-  const auto ap = rows_from<I8, MT>(p.x, d.He, m0, d.T);
   typename St::Acc acc[MT][NWW * 4];
-  tile_mma<I8, MT, NWW, D>(ap, make_rsrc(p.packed, pg.total), wb, s0, ns, acc);
+  if constexpr (LC) {
+    __shared__ __attribute__((aligned(16))) uint8_t ring[2 * (MT * WM + NWW * WN * 4) * 1024];
+    const int mb = mtile * BM, j0 = grp * GW;
+    const int nsb = mb < d.T ? max(0, min(pg.nst_he, s0 + sps) - s0) : 0;
+    tile_mma_lds<I8, MT, NWW, WM, WN>(rows_from<I8, MT * WM>(p.x, d.He, mb, d.T),
+                                      make_rsrc(p.packed, pg.total),
+                                      uint32_t(pg.off_dq + int64_t(j0) * pg.nst_he * 4096),
+                                      uint32_t(pg.nst_he * 4096), tiles - j0, s0, nsb, ring, acc);
+  } else {
+    const int ns = m0 < d.T ? max(0, min(pg.nst_he, s0 + sps) - s0) : 0;
+    const auto ap = rows_from<I8, MT>(p.x, d.He, m0, d.T);
+    tile_mma<I8, MT, NWW, D>(ap, make_rsrc(p.packed, pg.total), wb, s0, ns, acc);
+  }
   if (m0 >= d.T) return;
   const int g = lane >> 4, c = lane & 15;
 #pragma unroll
@@ -1190,7 +1543,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k1_tiled(Dims d, Ptrs p, PackGeo
 // K3t: grid (token tiles fastest, then groups of W^UqQr windows).  Nope
 // windows go to q^C (bf16, workspace); a rope window goes through a per-wave
 // LDS tile of 16 tokens x 64 columns to RoPE and queryRopeOut.
-template <bool I8, int MT, int NWW, int WM, int WN, int D>
+template <bool I8, int MT, int NWW, int WM, int WN, int D, bool LC = false>
 __global__ __launch_bounds__(64 * WM * WN) void k3_tiled(Dims d, Ptrs p, PackGeo pg, int mtiles) {
   using St = Stage<I8>;
   constexpr int BM = 16 * MT * WM, GW = NWW * WN;
@@ -1205,10 +1558,19 @@ __global__ __launch_bounds__(64 * WM * WN) void k3_tiled(Dims d, Ptrs p, PackGeo
     const int j = grp * GW + wn * NWW + i;
     wb[i] = j < pg.win_uq ? uint32_t(pg.off_uq + int64_t(j) * pg.nst_cq * 4096) : kOOB;
   }
-  const int ns = m0 < d.T ? pg.nst_cq : 0;
-  const auto ap = tiles_from<I8, MT>(p.cq, int64_t(pg.nst_cq) * 1024, (d.T + 15) / 16, m0);
   typename St::Acc acc[MT][NWW * 4];
-  tile_mma<I8, MT, NWW, D>(ap, make_rsrc(p.packed, pg.total), wb, 0, ns, acc);
+  if constexpr (LC) {
+    __shared__ __attribute__((aligned(16))) uint8_t ring[2 * (MT * WM + NWW * WN * 4) * 1024];
+    const int mb = mtile * BM, j0 = grp * GW;
+    tile_mma_lds<I8, MT, NWW, WM, WN>(
+        tiles_from<I8, MT * WM>(p.cq, int64_t(pg.nst_cq) * 1024, (d.T + 15) / 16, mb),
+        make_rsrc(p.packed, pg.total), uint32_t(pg.off_uq + int64_t(j0) * pg.nst_cq * 4096),
+        uint32_t(pg.nst_cq * 4096), pg.win_uq - j0, 0, mb < d.T ? pg.nst_cq : 0, ring, acc);
+  } else {
+    const int ns = m0 < d.T ? pg.nst_cq : 0;
+    const auto ap = tiles_from<I8, MT>(p.cq, int64_t(pg.nst_cq) * 1024, (d.T + 15) / 16, m0);
+    tile_mma<I8, MT, NWW, D>(ap, make_rsrc(p.packed, pg.total), wb, 0, ns, acc);
+  }
   if (m0 >= d.T) return;
   const int g = lane >> 4, c = lane & 15;
   const int P = pg.nope_w + 1, hf = d.Dr / 2;
@@ -1291,7 +1653,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k3_tiled(Dims d, Ptrs p, PackGeo
 // q^C[., h, .] W^UK[h]; bf16 stores, or (one column group holding the whole
 // Hckv row) the per-(token, head) int8 quantisation with the row maximum
 // taken across the WN waves of a token range.
-template <int MT, int NWW, int WM, int WN, int D, bool Q8>
+template <int MT, int NWW, int WM, int WN, int D, bool Q8, bool LC = false>
 __global__ __launch_bounds__(64 * WM * WN) void k4_tiled(Dims d, Ptrs p, PackGeo pg, int mtiles,
                                                       int cgroups) {
   constexpr int BM = 16 * MT * WM, GW = NWW * WN;
@@ -1307,12 +1669,21 @@ __global__ __launch_bounds__(64 * WM * WN) void k4_tiled(Dims d, Ptrs p, PackGeo
     const int jw = cg * GW + wn * NWW + i;
     wb[i] = jw < pg.uk_w ? uint32_t(pg.off_uk + int64_t(h * pg.uk_w + jw) * pg.nst_d * 4096) : kOOB;
   }
-  const int ns = m0 < d.T ? pg.nst_d : 0;
   const int64_t qtile = int64_t(d.N) * pg.nst_d * 1024, qh = int64_t(h) * pg.nst_d * 1024;
-  const auto ap = tiles_from<false, MT>(reinterpret_cast<const uint8_t*>(p.qc) + qh, qtile,
-                                        (d.T + 15) / 16, m0);
   typename Stage<false>::Acc acc[MT][NWW * 4];
-  tile_mma<false, MT, NWW, D>(ap, make_rsrc(p.packed, pg.total), wb, 0, ns, acc);
+  if constexpr (LC) {
+    __shared__ __attribute__((aligned(16))) uint8_t ring[2 * (MT * WM + NWW * WN * 4) * 1024];
+    const int mb = mtile * BM, j0 = cg * GW;
+    tile_mma_lds<false, MT, NWW, WM, WN>(
+        tiles_from<false, MT * WM>(reinterpret_cast<const uint8_t*>(p.qc) + qh, qtile, (d.T + 15) / 16, mb),
+        make_rsrc(p.packed, pg.total), uint32_t(pg.off_uk + int64_t(h * pg.uk_w + j0) * pg.nst_d * 4096),
+        uint32_t(pg.nst_d * 4096), pg.uk_w - j0, 0, mb < d.T ? pg.nst_d : 0, ring, acc);
+  } else {
+    const int ns = m0 < d.T ? pg.nst_d : 0;
+    const auto ap = tiles_from<false, MT>(reinterpret_cast<const uint8_t*>(p.qc) + qh, qtile,
+                                          (d.T + 15) / 16, m0);
+    tile_mma<false, MT, NWW, D>(ap, make_rsrc(p.packed, pg.total), wb, 0, ns, acc);
+  }
   const int g = lane >> 4, c = lane & 15;
   if constexpr (!Q8) {
     if (m0 >= d.T) return;
@@ -1594,6 +1965,7 @@ struct mla_prolog {
   Layout lay;
   uint8_t* ws;
   hipEvent_t* events;  // kProfileRing x kProfileEvents when profiling, else NULL
+  bool* fused;         // per recorded run: up_proj and uk ran as one kernel
   int64_t recorded;    // runs recorded since the last read
 };
 
@@ -1651,6 +2023,14 @@ void packed_launch(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p, 
   mark(1);
   launch_norm<I8>(s, d, p, pl.Sp, g.nst_cq);
   mark(2);
+  if (g.nope_w <= kK34Waves && g.uk_w <= kK34Waves && g.nst_d <= kK34Stages) {
+    // up-projection and W^UK fused; the profile books both to the first
+    if (q8) k34_stream<I8, MT, 2, true><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g);
+    else k34_stream<I8, MT, 2, false><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g);
+    mark(3);
+    mark(-1);
+    return;
+  }
   k3_packed<I8, MT, 8, 2><<<dim3(d.N * (g.nope_w + 1)), 512, 0, s>>>(d, p, g);
   mark(3);
   if (q8) k4_packed_q8<MT, 4><<<dim3(d.N), 512, 0, s>>>(d, p, g);
@@ -1792,6 +2172,7 @@ mla_status mla_prolog_create(const mla_prolog_desc* desc, mla_prolog_t* out) {
   h->lay = layout(*desc);
   h->ws = nullptr;
   h->events = nullptr;
+  h->fused = nullptr;
   h->recorded = 0;
   if (hipMalloc(&h->ws, h->lay.total) != hipSuccess) {
     delete h;
@@ -1847,12 +2228,19 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   hipEvent_t* ev = nullptr;
+  bool* fused = nullptr;
   if (h->events) {
     ev = h->events + (h->recorded % kProfileRing) * kProfileEvents;
+    fused = h->fused + (h->recorded % kProfileRing);
+    *fused = false;
     ++h->recorded;
   }
+  // mark(i): event i (after kernel i); mark(-1): the last event of a run
+  // whose up_proj and uk were one kernel
   auto mark = [&](int i) {
-    if (ev) (void)hipEventRecord(ev[i], s);
+    if (!ev) return;
+    if (i < 0) *fused = true;
+    (void)hipEventRecord(ev[i < 0 ? kProfileEvents - 1 : i], s);
   };
   mark(0);
   p.packed = static_cast<const uint8_t*>(t->packed_weights);
@@ -1891,11 +2279,13 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
 }
 
 static void destroy_events(mla_prolog* h) {
-  if (!h->events) return;
-  for (int i = 0; i < kProfileRing * kProfileEvents; ++i)
-    if (h->events[i]) (void)hipEventDestroy(h->events[i]);
+  if (h->events)
+    for (int i = 0; i < kProfileRing * kProfileEvents; ++i)
+      if (h->events[i]) (void)hipEventDestroy(h->events[i]);
   delete[] h->events;
+  delete[] h->fused;
   h->events = nullptr;
+  h->fused = nullptr;
   h->recorded = 0;
 }
 
@@ -1909,7 +2299,8 @@ mla_status mla_prolog_profile_enable(mla_prolog_t h, int enable) {
   destroy_events(h);
   if (st == MLA_OK && enable) {
     h->events = new (std::nothrow) hipEvent_t[kProfileRing * kProfileEvents]();
-    if (!h->events) st = MLA_ERR_RUNTIME;
+    h->fused = new (std::nothrow) bool[kProfileRing]();
+    if (!h->events || !h->fused) st = MLA_ERR_RUNTIME;
     for (int i = 0; st == MLA_OK && i < kProfileRing * kProfileEvents; ++i)
       if (hipEventCreate(&h->events[i]) != hipSuccess) st = MLA_ERR_RUNTIME;
     if (st != MLA_OK) destroy_events(h);
@@ -1929,6 +2320,7 @@ mla_status mla_prolog_profile_read(mla_prolog_t h, double* kernel_ms, int64_t* r
     hipEvent_t* ev = h->events + r * kProfileEvents;
     if (hipEventSynchronize(ev[kProfileEvents - 1]) != hipSuccess) return MLA_ERR_RUNTIME;
     for (int k = 0; k < kProfileEvents - 1; ++k) {
+      if (h->fused[r] && k == kProfileEvents - 2) continue;   // uk ran inside up_proj
       float ms = 0.0f;
       if (hipEventElapsedTime(&ms, ev[k], ev[k + 1]) != hipSuccess) return MLA_ERR_RUNTIME;
       kernel_ms[k] += ms;

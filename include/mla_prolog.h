@@ -177,7 +177,9 @@ mla_status mla_prolog_destroy(mla_prolog_t handle);
 /* Kernel timing with HIP events, for benchmarks.  After
  * mla_prolog_profile_enable(h, 1) every run of h records HIP events on its
  * stream before its first kernel and after each of its four kernels
- * (down_proj, norm_rope_cache, up_proj, uk).  mla_prolog_profile_read waits
+ * (down_proj, norm_rope_cache, up_proj, uk; where one kernel does both
+ * up_proj and uk, its time is booked to up_proj and uk reads 0).
+ * mla_prolog_profile_read waits
  * for the recorded events and returns, per kernel, the elapsed milliseconds
  * summed over the runs since the previous read (kernel_ms[4]) and the number
  * of those runs; at most 2048 runs are kept between reads (more is an
