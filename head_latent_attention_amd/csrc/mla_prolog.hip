@@ -1817,13 +1817,14 @@ Plan make_plan(const mla_prolog_desc& d, int64_t T) {
 }
 
 // Tiled path (token counts above the streaming range, packed weights).
-// Shape classes: large (T >= 512) uses 256-token x 256-column blocks of four
-// 128x128 waves; medium uses one 16*mt-token wave per 64-column window (K1,
-// K3) or per 128 columns (K4, two waves stacked along tokens above 128
-// tokens).  K1 splits the He stages so that about kTiledK1Blocks blocks run.
+// Shape classes.  Large (T >= kTiledLargeT): K1 in LDS-staged 256-token x
+// 128-column blocks of eight 64x64 waves, split in two along He; K3 and K4
+// in 256 x 256 blocks of four 128x128 waves.  Medium: K1 with one 16*mt-token
+// wave per 64-column window, He split so that about kTiledK1Blocks blocks
+// run; K3 likewise up to 128 tokens, LDS-staged 256 x 128 blocks above; K4
+// with waves of 128 columns (two stacked along tokens above 128 tokens).
 constexpr int kTiledLargeT = 2048;
 constexpr int kTiledK1Blocks = 512;   // medium: one-wave blocks
-constexpr int kTiledK1BlocksLarge = 256;
 
 struct TiledPlan {
   bool large;
@@ -1842,15 +1843,17 @@ TiledPlan tiled_plan(const mla_prolog_desc& d, int64_t T) {
   tp.mt = T <= 64 ? 4 : 8;
   tp.wm = (!tp.large && T > 128) ? 2 : 1;
   if (tp.large) {
-    tp.m1 = ceil_div(T, 256); tp.ngrp1 = ceil_div(tiles, 4);
+    tp.m1 = ceil_div(T, 256); tp.ngrp1 = ceil_div(tiles, 2);      // LDS-staged 256 x 128
     tp.m3 = ceil_div(T, 256); tp.ngrp3 = ceil_div(g.win_uq, 4);
     tp.m4 = ceil_div(T, 256); tp.cg4 = ceil_div(g.uk_w, 4);
   } else {
     tp.m1 = ceil_div(T, 16 * tp.mt); tp.ngrp1 = tiles;
-    tp.m3 = ceil_div(T, 16 * tp.mt * tp.wm); tp.ngrp3 = g.win_uq;
+    if (tp.wm == 2) { tp.m3 = ceil_div(T, 256); tp.ngrp3 = ceil_div(g.win_uq, 2); }   // LDS-staged
+    else { tp.m3 = ceil_div(T, 16 * tp.mt); tp.ngrp3 = g.win_uq; }
     tp.m4 = ceil_div(T, 16 * tp.mt * tp.wm); tp.cg4 = ceil_div(g.uk_w, 2);
   }
-  const int target = tp.large ? kTiledK1BlocksLarge : kTiledK1Blocks;
+  // large: two k splits, so that the 1-block-per-CU grid fills whole rounds
+  const int target = tp.large ? 2 * tp.m1 * tp.ngrp1 : kTiledK1Blocks;
   int S = std::max(1, std::min(g.nst_he, target / std::max(1, tp.m1 * tp.ngrp1)));
   tp.sps = ceil_div(g.nst_he, S);
   tp.S = ceil_div(g.nst_he, tp.sps);
@@ -2060,7 +2063,8 @@ void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs&
   mark(1);
   launch_norm<I8>(s, d, p, tp.S, g.nst_cq);
   mark(2);
-  k3_tiled<I8, MT, 1, WM, 1, 2><<<dim3(tp.m3 * tp.ngrp3), 64 * WM, 0, s>>>(d, p, g, tp.m3);
+  if (WM == 2) k3_tiled<I8, 4, 1, 4, 2, 2, true><<<dim3(tp.m3 * tp.ngrp3), 512, 0, s>>>(d, p, g, tp.m3);
+  else k3_tiled<I8, MT, 1, WM, 1, 2><<<dim3(tp.m3 * tp.ngrp3), 64 * WM, 0, s>>>(d, p, g, tp.m3);
   mark(3);
   if (q8) k4_tiled<4, 2, 1, 4, 2, true><<<dim3(tp.m4q * d.N), 256, 0, s>>>(d, p, g, tp.m4q, 1);
   else k4_tiled<MT, 2, WM, 1, 2, false><<<dim3(tp.m4 * tp.cg4 * d.N), 64 * WM, 0, s>>>(d, p, g, tp.m4,
@@ -2071,8 +2075,8 @@ void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs&
 template <bool I8, class Mark>
 void tiled_large(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g,
                  bool q8, Mark& mark) {
-  k1_tiled<I8, 8, 2, 2, 2, 2><<<dim3(tp.m1 * tp.ngrp1 * tp.S), 256, 0, s>>>(d, p, g, tp.sps, tp.m1,
-                                                                           tp.ngrp1);
+  k1_tiled<I8, 4, 1, 4, 2, 2, true><<<dim3(tp.m1 * tp.ngrp1 * tp.S), 512, 0, s>>>(d, p, g, tp.sps,
+                                                                                 tp.m1, tp.ngrp1);
   mark(1);
   launch_norm<I8>(s, d, p, tp.S, g.nst_cq);
   mark(2);
