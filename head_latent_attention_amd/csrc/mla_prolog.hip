@@ -245,6 +245,7 @@ struct Ptrs {
   uint8_t* cq;       // [T][Hcq] bf16 (int8 in int8 mode)
   float* cq_scale;   // [T]
   uint16_t* qc;      // [T][N][D] bf16
+  uint8_t* xp;       // x fragment-packed (tiled path, medium T)
   const uint8_t* packed;  // weights in the packed layout, or NULL
 };
 
@@ -1481,7 +1482,25 @@ __device__ __forceinline__ void tile_mma_lds(const AP& ap, rsrc_t Wp, uint32_t w
 // (wm, wn) takes tokens 16*MT*wm.. of the block's token tile and windows
 // NWW*wn.. of its group of [W^DQ | W^DkvKr] windows; the split's stages go
 // into fp32 (int32) partials, one 16-byte store per 4 columns.
-template <bool I8, int MT, int NWW, int WM, int WN, int D, bool LC = false>
+// x into the fragment-packed layout of the activations (16-token tiles of
+// 1 KB k-stages; k padding and rows past T as zeros), one 16-byte chunk per
+// thread.
+template <bool I8>
+__global__ __launch_bounds__(256) void k_pack_x(Dims d, Ptrs p, int nst) {
+  using St = Stage<I8>;
+  const int64_t q = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t tiles = (d.T + 15) / 16;
+  if (q >= tiles * nst * 64) return;
+  const int lane = int(q % 64), st = int((q / 64) % nst);
+  const int64_t t = (q / (64 * nst)) * 16 + (lane & 15);
+  const int k = st * St::KS + St::KL * (lane >> 4);
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (t < d.T && k < d.He) v = *reinterpret_cast<const uint4*>(p.x + (t * d.He + k) * St::EB);
+  *reinterpret_cast<uint4*>(p.xp + q * 16) = v;
+}
+
+// XP: x is read fragment-packed from p.xp instead of row-major.
+template <bool I8, int MT, int NWW, int WM, int WN, int D, bool LC = false, bool XP = false>
 __global__ __launch_bounds__(64 * WM * WN) void k1_tiled(Dims d, Ptrs p, PackGeo pg, int sps, int mtiles,
                                                       int ngrp) {
   using St = Stage<I8>;
@@ -1511,8 +1530,13 @@ __global__ __launch_bounds__(64 * WM * WN) void k1_tiled(Dims d, Ptrs p, PackGeo
                                       uint32_t(pg.nst_he * 4096), tiles - j0, s0, nsb, ring, acc);
   } else {
     const int ns = m0 < d.T ? max(0, min(pg.nst_he, s0 + sps) - s0) : 0;
-    const auto ap = rows_from<I8, MT>(p.x, d.He, m0, d.T);
-    tile_mma<I8, MT, NWW, D>(ap, make_rsrc(p.packed, pg.total), wb, s0, ns, acc);
+    if constexpr (XP) {
+      const auto ap = tiles_from<I8, MT>(p.xp, int64_t(pg.nst_he) * 1024, (d.T + 15) / 16, m0);
+      tile_mma<I8, MT, NWW, D>(ap, make_rsrc(p.packed, pg.total), wb, s0, ns, acc);
+    } else {
+      const auto ap = rows_from<I8, MT>(p.x, d.He, m0, d.T);
+      tile_mma<I8, MT, NWW, D>(ap, make_rsrc(p.packed, pg.total), wb, s0, ns, acc);
+    }
   }
   if (m0 >= d.T) return;
   const int g = lane >> 4, c = lane & 15;
@@ -1821,8 +1845,9 @@ Plan make_plan(const mla_prolog_desc& d, int64_t T) {
 // 128-column blocks of eight 64x64 waves, split in two along He; K3 and K4
 // in 256 x 256 blocks of four 128x128 waves.  Medium: K1 with one 16*mt-token
 // wave per 64-column window, He split so that about kTiledK1Blocks blocks
-// run; K3 likewise up to 128 tokens, LDS-staged 256 x 128 blocks above; K4
-// with waves of 128 columns (two stacked along tokens above 128 tokens).
+// run; K3 with one 64-token wave per window up to 128 tokens, LDS-staged
+// 256 x 128 blocks above; K4 with eight 64-column waves per 16*mt tokens.
+// The int8-query K4 always takes 64 tokens x the whole Hckv row per block.
 constexpr int kTiledLargeT = 2048;
 constexpr int kTiledK1Blocks = 512;   // medium: one-wave blocks
 
@@ -1849,8 +1874,8 @@ TiledPlan tiled_plan(const mla_prolog_desc& d, int64_t T) {
   } else {
     tp.m1 = ceil_div(T, 16 * tp.mt); tp.ngrp1 = tiles;
     if (tp.wm == 2) { tp.m3 = ceil_div(T, 256); tp.ngrp3 = ceil_div(g.win_uq, 2); }   // LDS-staged
-    else { tp.m3 = ceil_div(T, 16 * tp.mt); tp.ngrp3 = g.win_uq; }
-    tp.m4 = ceil_div(T, 16 * tp.mt * tp.wm); tp.cg4 = ceil_div(g.uk_w, 2);
+    else { tp.m3 = ceil_div(T, 64); tp.ngrp3 = g.win_uq; }                            // 64-token waves
+    tp.m4 = ceil_div(T, 16 * tp.mt); tp.cg4 = ceil_div(g.uk_w, 8);
   }
   // large: two k splits, so that the 1-block-per-CU grid fills whole rounds
   const int target = tp.large ? 2 * tp.m1 * tp.ngrp1 : kTiledK1Blocks;
@@ -2064,11 +2089,10 @@ void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs&
   launch_norm<I8>(s, d, p, tp.S, g.nst_cq);
   mark(2);
   if (WM == 2) k3_tiled<I8, 4, 1, 4, 2, 2, true><<<dim3(tp.m3 * tp.ngrp3), 512, 0, s>>>(d, p, g, tp.m3);
-  else k3_tiled<I8, MT, 1, WM, 1, 2><<<dim3(tp.m3 * tp.ngrp3), 64 * WM, 0, s>>>(d, p, g, tp.m3);
+  else k3_tiled<I8, 4, 1, 1, 1, 2><<<dim3(tp.m3 * tp.ngrp3), 64, 0, s>>>(d, p, g, tp.m3);
   mark(3);
-  if (q8) k4_tiled<4, 2, 1, 4, 2, true><<<dim3(tp.m4q * d.N), 256, 0, s>>>(d, p, g, tp.m4q, 1);
-  else k4_tiled<MT, 2, WM, 1, 2, false><<<dim3(tp.m4 * tp.cg4 * d.N), 64 * WM, 0, s>>>(d, p, g, tp.m4,
-                                                                                     tp.cg4);
+  if (q8) k4_tiled<4, 1, 1, 8, 2, true><<<dim3(tp.m4q * d.N), 512, 0, s>>>(d, p, g, tp.m4q, 1);
+  else k4_tiled<MT, 1, 1, 8, 2, false><<<dim3(tp.m4 * tp.cg4 * d.N), 512, 0, s>>>(d, p, g, tp.m4, tp.cg4);
   mark(4);
 }
 
@@ -2082,7 +2106,7 @@ void tiled_large(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs& 
   mark(2);
   k3_tiled<I8, 8, 2, 2, 2, 2><<<dim3(tp.m3 * tp.ngrp3), 256, 0, s>>>(d, p, g, tp.m3);
   mark(3);
-  if (q8) k4_tiled<4, 2, 1, 4, 2, true><<<dim3(tp.m4q * d.N), 256, 0, s>>>(d, p, g, tp.m4q, 1);
+  if (q8) k4_tiled<4, 1, 1, 8, 2, true><<<dim3(tp.m4q * d.N), 512, 0, s>>>(d, p, g, tp.m4q, 1);
   else k4_tiled<8, 2, 2, 2, 2, false><<<dim3(tp.m4 * tp.cg4 * d.N), 256, 0, s>>>(d, p, g, tp.m4, tp.cg4);
   mark(4);
 }
@@ -2229,6 +2253,7 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   p.cq = h->ws + h->lay.cq;
   p.cq_scale = reinterpret_cast<float*>(h->ws + h->lay.cq_scale);
   p.qc = reinterpret_cast<uint16_t*>(h->ws + h->lay.qc);
+  p.xp = nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   hipEvent_t* ev = nullptr;
