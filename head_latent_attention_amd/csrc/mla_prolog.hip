@@ -1677,13 +1677,24 @@ __global__ __launch_bounds__(64 * WM * WN) void k3_tiled(Dims d, Ptrs p, PackGeo
 // q^C[., h, .] W^UK[h]; bf16 stores, or (one column group holding the whole
 // Hckv row) the per-(token, head) int8 quantisation with the row maximum
 // taken across the WN waves of a token range.
-template <int MT, int NWW, int WM, int WN, int D, bool Q8, bool LC = false>
+// HF: heads vary fastest along the grid, so blocks running together write
+// neighbouring heads of the same tokens (one contiguous q^N row per token).
+template <int MT, int NWW, int WM, int WN, int D, bool Q8, bool LC = false, bool HF = false>
 __global__ __launch_bounds__(64 * WM * WN) void k4_tiled(Dims d, Ptrs p, PackGeo pg, int mtiles,
                                                       int cgroups) {
   constexpr int BM = 16 * MT * WM, GW = NWW * WN;
   __shared__ float rmax[Q8 ? WN : 1][Q8 ? BM : 1];
-  const int mtile = blockIdx.x % mtiles, rest = blockIdx.x / mtiles;
-  const int cg = rest % cgroups, h = rest / cgroups;
+  __shared__ __attribute__((aligned(16))) uint8_t stage[Q8 ? 16 : WM * WN * 16 * 144];
+  int mtile, cg, h;
+  if constexpr (HF) {
+    h = blockIdx.x % d.N;
+    const int rest = blockIdx.x / d.N;
+    cg = rest % cgroups; mtile = rest / cgroups;
+  } else {
+    mtile = blockIdx.x % mtiles;
+    const int rest = blockIdx.x / mtiles;
+    cg = rest % cgroups; h = rest / cgroups;
+  }
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = w % WM, wn = w / WM;
   const int m0 = mtile * BM + 16 * MT * wm;
@@ -1710,8 +1721,12 @@ __global__ __launch_bounds__(64 * WM * WN) void k4_tiled(Dims d, Ptrs p, PackGeo
   }
   const int g = lane >> 4, c = lane & 15;
   if constexpr (!Q8) {
+    // each 16-token x 64-column piece goes through the wave's LDS tile
+    // (rows 144 bytes apart, which spreads the 8-byte writes over the banks)
+    // and out as 16-byte stores, eight whole 128-byte row pieces per store
     if (m0 >= d.T) return;
     uint16_t* qo = static_cast<uint16_t*>(p.q_out);
+    uint8_t* tile = stage + w * 16 * 144;
 #pragma unroll
     for (int i = 0; i < NWW; ++i) {
       const int jw = cg * GW + wn * NWW + i;
@@ -1719,16 +1734,25 @@ __global__ __launch_bounds__(64 * WM * WN) void k4_tiled(Dims d, Ptrs p, PackGeo
       const int width = min(64, d.Hckv - 64 * jw);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const int m = m0 + 16 * mt + c;
-        if (m >= d.T) continue;
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
-          const int col = 16 * ct + 4 * g;
-          if (col >= width) continue;
           const auto& a = acc[mt][i * 4 + ct];
-          *reinterpret_cast<uint2*>(qo + (int64_t(m) * d.N + h) * d.Hckv + 64 * jw + col) =
-              pack_bf16x4(a[0], a[1], a[2], a[3]);
+          *reinterpret_cast<uint2*>(tile + c * 144 + (16 * ct + 4 * g) * 2) = pack_bf16x4(a[0], a[1], a[2], a[3]);
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int k = lane + 64 * half, row = k >> 3, col = 8 * (k & 7);
+          const int m = m0 + 16 * mt + row;
+          if (m < d.T && col < width)
+            *reinterpret_cast<uint4*>(qo + (int64_t(m) * d.N + h) * d.Hckv + 64 * jw + col) =
+                *reinterpret_cast<const uint4*>(tile + row * 144 + col * 2);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
     }
   } else {
@@ -1870,7 +1894,7 @@ TiledPlan tiled_plan(const mla_prolog_desc& d, int64_t T) {
   if (tp.large) {
     tp.m1 = ceil_div(T, 256); tp.ngrp1 = ceil_div(tiles, 2);      // LDS-staged 256 x 128
     tp.m3 = ceil_div(T, 256); tp.ngrp3 = ceil_div(g.win_uq, 4);
-    tp.m4 = ceil_div(T, 256); tp.cg4 = ceil_div(g.uk_w, 4);
+    tp.m4 = ceil_div(T, 128); tp.cg4 = ceil_div(g.uk_w, 8);
   } else {
     tp.m1 = ceil_div(T, 16 * tp.mt); tp.ngrp1 = tiles;
     if (tp.wm == 2) { tp.m3 = ceil_div(T, 256); tp.ngrp3 = ceil_div(g.win_uq, 2); }   // LDS-staged
@@ -2091,8 +2115,9 @@ void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs&
   if (WM == 2) k3_tiled<I8, 4, 1, 4, 2, 2, true><<<dim3(tp.m3 * tp.ngrp3), 512, 0, s>>>(d, p, g, tp.m3);
   else k3_tiled<I8, 4, 1, 1, 1, 2><<<dim3(tp.m3 * tp.ngrp3), 64, 0, s>>>(d, p, g, tp.m3);
   mark(3);
-  if (q8) k4_tiled<4, 1, 1, 8, 2, true><<<dim3(tp.m4q * d.N), 512, 0, s>>>(d, p, g, tp.m4q, 1);
-  else k4_tiled<MT, 1, 1, 8, 2, false><<<dim3(tp.m4 * tp.cg4 * d.N), 512, 0, s>>>(d, p, g, tp.m4, tp.cg4);
+  if (q8) k4_tiled<4, 1, 1, 8, 2, true, false, true><<<dim3(tp.m4q * d.N), 512, 0, s>>>(d, p, g, tp.m4q, 1);
+  else k4_tiled<MT, 1, 1, 8, 2, false, false, true><<<dim3(tp.m4 * tp.cg4 * d.N), 512, 0, s>>>(d, p, g, tp.m4,
+                                                                                           tp.cg4);
   mark(4);
 }
 
@@ -2106,8 +2131,9 @@ void tiled_large(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs& 
   mark(2);
   k3_tiled<I8, 8, 2, 2, 2, 2><<<dim3(tp.m3 * tp.ngrp3), 256, 0, s>>>(d, p, g, tp.m3);
   mark(3);
-  if (q8) k4_tiled<4, 1, 1, 8, 2, true><<<dim3(tp.m4q * d.N), 512, 0, s>>>(d, p, g, tp.m4q, 1);
-  else k4_tiled<8, 2, 2, 2, 2, false><<<dim3(tp.m4 * tp.cg4 * d.N), 256, 0, s>>>(d, p, g, tp.m4, tp.cg4);
+  if (q8) k4_tiled<4, 1, 1, 8, 2, true, false, true><<<dim3(tp.m4q * d.N), 512, 0, s>>>(d, p, g, tp.m4q, 1);
+  else k4_tiled<8, 1, 1, 8, 2, false, false, true><<<dim3(tp.m4 * tp.cg4 * d.N), 512, 0, s>>>(d, p, g, tp.m4,
+                                                                                          tp.cg4);
   mark(4);
 }
 
