@@ -752,17 +752,20 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
   auto y8 = [&](int j, double (&v)[8]) {
     double f[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     int32_t iv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (S == 1) {
+    if (S <= 2) {
       const uint32_t o = uint32_t((int64_t(t) * Ntot + 8 * j) * 4);
+      const uint32_t o2 = uint32_t(((int64_t(d.T) + t) * Ntot + 8 * j) * 4);
       const uint4 a = bload16(P, o), b = bload16(P, o + 16);
+      const uint4 a2 = bload16(P, S == 2 ? o2 : kOOB), b2 = bload16(P, S == 2 ? o2 + 16 : kOOB);
       const uint32_t w8[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      const uint32_t v8[8] = {a2.x, a2.y, a2.z, a2.w, b2.x, b2.y, b2.z, b2.w};
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        if constexpr (I8) iv[c] = int32_t(w8[c]);
-        else f[c] = double(__uint_as_float(w8[c]));
+        if constexpr (I8) iv[c] = int32_t(w8[c]) + int32_t(v8[c]);
+        else f[c] = double(__uint_as_float(w8[c])) + double(__uint_as_float(v8[c]));
       }
     }
-    for (int s0 = 0; S > 1 && s0 < S; s0 += 8) {
+    for (int s0 = 0; S > 2 && s0 < S; s0 += 8) {
       uint4 r[16];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -1406,7 +1409,7 @@ __device__ __forceinline__ APacked<I8, MT> tiles_from(const void* base, int64_t 
 // every wave then reads its fragments with conflict-free 16-byte LDS reads.
 // The global loads run three stages ahead of the MFMAs through two register
 // sets.  ns must be the same for the whole block.
-template <bool I8, int MT, int NWW, int WM, int WN, class AP>
+template <bool I8, int MT, int NWW, int WM, int WN, class AP, int RS = 2>
 __device__ __forceinline__ void tile_mma_lds(const AP& ap, rsrc_t Wp, uint32_t wbase, uint32_t wstride,
                                              int nwin, int s0, int ns, uint8_t* lds,
                                              typename Stage<I8>::Acc (&acc)[MT][NWW * 4]) {
@@ -1455,6 +1458,30 @@ __device__ __forceinline__ void tile_mma_lds(const AP& ap, rsrc_t Wp, uint32_t w
       for (int j = 0; j < NWW * 4; ++j) acc[mt][j] = mfma(bf[j], af, acc[mt][j]);
     }
   };
+  if constexpr (RS == 1) {
+    // one register set: stage k + 2 is loaded while stage k is computed and
+    // written to LDS one iteration later
+    uint4 R[CH];
+    gload(R, 0);
+    lwrite(R, 0);
+    gload(R, 1);
+    __syncthreads();
+    // stages past ns load as zeros, so an odd ns costs one zero stage
+    // but keeps the loop free of an exit between the two halves
+    for (int j = 0; j < ns; j += 2) {
+      compute(0);                      // stage j
+      __builtin_amdgcn_sched_barrier(0);
+      lwrite(R, 1);                    // stage j + 1
+      gload(R, j + 2);
+      __syncthreads();
+      compute(1);                      // stage j + 1
+      __builtin_amdgcn_sched_barrier(0);
+      lwrite(R, 0);                    // stage j + 2
+      gload(R, j + 3);
+      __syncthreads();
+    }
+    return;
+  }
   uint4 R0[CH], R1[CH];   // stage k waits in R(k % 2)
   gload(R0, 0);
   __builtin_amdgcn_sched_barrier(0);
@@ -1463,16 +1490,15 @@ __device__ __forceinline__ void tile_mma_lds(const AP& ap, rsrc_t Wp, uint32_t w
   lwrite(R0, 0);
   gload(R0, 2);
   __syncthreads();
-  for (int j = 0; j < ns; j += 2) {
+  for (int j = 0; j < ns; j += 2) {   // as above, an odd ns adds one zero stage
     compute(0);                      // stage j
     __builtin_amdgcn_sched_barrier(0);
-    if (j + 1 < ns) lwrite(R1, 1);   // stage j + 1
+    lwrite(R1, 1);                   // stage j + 1
     gload(R1, j + 3);
     __syncthreads();
-    if (j + 1 >= ns) break;
     compute(1);                      // stage j + 1
     __builtin_amdgcn_sched_barrier(0);
-    if (j + 2 < ns) lwrite(R0, 0);   // stage j + 2
+    lwrite(R0, 0);                   // stage j + 2
     gload(R0, j + 4);
     __syncthreads();
   }
@@ -1500,7 +1526,7 @@ __global__ __launch_bounds__(256) void k_pack_x(Dims d, Ptrs p, int nst) {
 }
 
 // XP: x is read fragment-packed from p.xp instead of row-major.
-template <bool I8, int MT, int NWW, int WM, int WN, int D, bool LC = false, bool XP = false>
+template <bool I8, int MT, int NWW, int WM, int WN, int D, bool LC = false, bool XP = false, int RS = 2>
 __global__ __launch_bounds__(64 * WM * WN) void k1_tiled(Dims d, Ptrs p, PackGeo pg, int sps, int mtiles,
                                                       int ngrp) {
   using St = Stage<I8>;
@@ -1524,7 +1550,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k1_tiled(Dims d, Ptrs p, PackGeo
     __shared__ __attribute__((aligned(16))) uint8_t ring[2 * (MT * WM + NWW * WN * 4) * 1024];
     const int mb = mtile * BM, j0 = grp * GW;
     const int nsb = mb < d.T ? max(0, min(pg.nst_he, s0 + sps) - s0) : 0;
-    tile_mma_lds<I8, MT, NWW, WM, WN>(rows_from<I8, MT * WM>(p.x, d.He, mb, d.T),
+    tile_mma_lds<I8, MT, NWW, WM, WN, APlain<I8, MT * WM>, RS>(rows_from<I8, MT * WM>(p.x, d.He, mb, d.T),
                                       make_rsrc(p.packed, pg.total),
                                       uint32_t(pg.off_dq + int64_t(j0) * pg.nst_he * 4096),
                                       uint32_t(pg.nst_he * 4096), tiles - j0, s0, nsb, ring, acc);
@@ -1567,7 +1593,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k1_tiled(Dims d, Ptrs p, PackGeo
 // K3t: grid (token tiles fastest, then groups of W^UqQr windows).  Nope
 // windows go to q^C (bf16, workspace); a rope window goes through a per-wave
 // LDS tile of 16 tokens x 64 columns to RoPE and queryRopeOut.
-template <bool I8, int MT, int NWW, int WM, int WN, int D, bool LC = false>
+template <bool I8, int MT, int NWW, int WM, int WN, int D, bool LC = false, int RS = 2>
 __global__ __launch_bounds__(64 * WM * WN) void k3_tiled(Dims d, Ptrs p, PackGeo pg, int mtiles) {
   using St = Stage<I8>;
   constexpr int BM = 16 * MT * WM, GW = NWW * WN;
@@ -1586,7 +1612,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k3_tiled(Dims d, Ptrs p, PackGeo
   if constexpr (LC) {
     __shared__ __attribute__((aligned(16))) uint8_t ring[2 * (MT * WM + NWW * WN * 4) * 1024];
     const int mb = mtile * BM, j0 = grp * GW;
-    tile_mma_lds<I8, MT, NWW, WM, WN>(
+    tile_mma_lds<I8, MT, NWW, WM, WN, APacked<I8, MT * WM>, RS>(
         tiles_from<I8, MT * WM>(p.cq, int64_t(pg.nst_cq) * 1024, (d.T + 15) / 16, mb),
         make_rsrc(p.packed, pg.total), uint32_t(pg.off_uq + int64_t(j0) * pg.nst_cq * 4096),
         uint32_t(pg.nst_cq * 4096), pg.win_uq - j0, 0, mb < d.T ? pg.nst_cq : 0, ring, acc);
@@ -1865,9 +1891,9 @@ Plan make_plan(const mla_prolog_desc& d, int64_t T) {
 }
 
 // Tiled path (token counts above the streaming range, packed weights).
-// Shape classes.  Large (T >= kTiledLargeT): K1 in LDS-staged 256-token x
-// 128-column blocks of eight 64x64 waves, split in two along He; K3 and K4
-// in 256 x 256 blocks of four 128x128 waves.  Medium: K1 with one 16*mt-token
+// Shape classes.  Large (T >= kTiledLargeT): K1 and K3 in LDS-staged
+// 256-token x 256-column blocks of eight 128x64 waves, K1 split in two
+// along He; K4 in 128-token x 512-column blocks of eight 128x64 waves.  Medium: K1 with one 16*mt-token
 // wave per 64-column window, He split so that about kTiledK1Blocks blocks
 // run; K3 with one 64-token wave per window up to 128 tokens, LDS-staged
 // 256 x 128 blocks above; K4 with eight 64-column waves per 16*mt tokens.
@@ -1892,7 +1918,7 @@ TiledPlan tiled_plan(const mla_prolog_desc& d, int64_t T) {
   tp.mt = T <= 64 ? 4 : 8;
   tp.wm = (!tp.large && T > 128) ? 2 : 1;
   if (tp.large) {
-    tp.m1 = ceil_div(T, 256); tp.ngrp1 = ceil_div(tiles, 2);      // LDS-staged 256 x 128
+    tp.m1 = ceil_div(T, 256); tp.ngrp1 = ceil_div(tiles, 4);      // LDS-staged 256 x 256
     tp.m3 = ceil_div(T, 256); tp.ngrp3 = ceil_div(g.win_uq, 4);
     tp.m4 = ceil_div(T, 128); tp.cg4 = ceil_div(g.uk_w, 8);
   } else {
@@ -2112,7 +2138,7 @@ void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs&
   mark(1);
   launch_norm<I8>(s, d, p, tp.S, g.nst_cq);
   mark(2);
-  if (WM == 2) k3_tiled<I8, 4, 1, 4, 2, 2, true><<<dim3(tp.m3 * tp.ngrp3), 512, 0, s>>>(d, p, g, tp.m3);
+  if (WM == 2) k3_tiled<I8, 4, 1, 4, 2, 2, true, 1><<<dim3(tp.m3 * tp.ngrp3), 512, 0, s>>>(d, p, g, tp.m3);
   else k3_tiled<I8, 4, 1, 1, 1, 2><<<dim3(tp.m3 * tp.ngrp3), 64, 0, s>>>(d, p, g, tp.m3);
   mark(3);
   if (q8) k4_tiled<4, 1, 1, 8, 2, true, false, true><<<dim3(tp.m4q * d.N), 512, 0, s>>>(d, p, g, tp.m4q, 1);
@@ -2124,12 +2150,12 @@ void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs&
 template <bool I8, class Mark>
 void tiled_large(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g,
                  bool q8, Mark& mark) {
-  k1_tiled<I8, 4, 1, 4, 2, 2, true><<<dim3(tp.m1 * tp.ngrp1 * tp.S), 512, 0, s>>>(d, p, g, tp.sps,
+  k1_tiled<I8, 8, 1, 2, 4, 2, true><<<dim3(tp.m1 * tp.ngrp1 * tp.S), 512, 0, s>>>(d, p, g, tp.sps,
                                                                                  tp.m1, tp.ngrp1);
   mark(1);
   launch_norm<I8>(s, d, p, tp.S, g.nst_cq);
   mark(2);
-  k3_tiled<I8, 8, 2, 2, 2, 2><<<dim3(tp.m3 * tp.ngrp3), 256, 0, s>>>(d, p, g, tp.m3);
+  k3_tiled<I8, 8, 1, 2, 4, 2, true><<<dim3(tp.m3 * tp.ngrp3), 512, 0, s>>>(d, p, g, tp.m3);
   mark(3);
   if (q8) k4_tiled<4, 1, 1, 8, 2, true, false, true><<<dim3(tp.m4q * d.N), 512, 0, s>>>(d, p, g, tp.m4q, 1);
   else k4_tiled<8, 1, 1, 8, 2, false, false, true><<<dim3(tp.m4 * tp.cg4 * d.N), 512, 0, s>>>(d, p, g, tp.m4,
