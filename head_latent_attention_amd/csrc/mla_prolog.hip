@@ -1143,10 +1143,10 @@ struct ALds {
 // queryRopeOut.  512 threads.
 constexpr int kK34Waves = 8, kK34Stages = 4;
 
-template <bool I8, int MT, int D, bool Q8>
-__global__ __launch_bounds__(512) void k34_stream(Dims d, Ptrs p, PackGeo pg) {
+template <bool I8, int MT, int D, bool Q8, int NW = kK34Waves, int NS2 = kK34Stages>
+__global__ __launch_bounds__(64 * NW) void k34_stream(Dims d, Ptrs p, PackGeo pg) {
   using St = Stage<I8>;
-  constexpr int NW = kK34Waves, NS2 = kK34Stages, W = MT * 16 * 64;
+  constexpr int W = MT * 16 * 64;
   constexpr int RED = (NW - 1) * W * 4, QCL = 16 * MT * 4 * 32 * 2;
   __shared__ __attribute__((aligned(16))) uint8_t lds[RED + QCL + NW * 16 * MT * 4];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1895,7 +1895,8 @@ Plan make_plan(const mla_prolog_desc& d, int64_t T) {
 // 256-token x 256-column blocks of eight 128x64 waves, K1 split in two
 // along He; K4 in 128-token x 512-column blocks of eight 128x64 waves.  Medium: K1 with one 16*mt-token
 // wave per 64-column window, He split so that about kTiledK1Blocks blocks
-// run; K3 with one 64-token wave per window up to 128 tokens, LDS-staged
+// run (above 128 tokens: LDS-staged 256 x 128 blocks, about one per CU);
+// K3 with one 64-token wave per window up to 128 tokens, LDS-staged
 // 256 x 128 blocks above; K4 with eight 64-column waves per 16*mt tokens.
 // The int8-query K4 always takes 64 tokens x the whole Hckv row per block.
 constexpr int kTiledLargeT = 2048;
@@ -1922,13 +1923,15 @@ TiledPlan tiled_plan(const mla_prolog_desc& d, int64_t T) {
     tp.m3 = ceil_div(T, 256); tp.ngrp3 = ceil_div(g.win_uq, 4);
     tp.m4 = ceil_div(T, 128); tp.cg4 = ceil_div(g.uk_w, 8);
   } else {
-    tp.m1 = ceil_div(T, 16 * tp.mt); tp.ngrp1 = tiles;
+    if (tp.wm == 2) { tp.m1 = ceil_div(T, 256); tp.ngrp1 = ceil_div(tiles, 2); }     // LDS-staged
+    else { tp.m1 = ceil_div(T, 16 * tp.mt); tp.ngrp1 = tiles; }
     if (tp.wm == 2) { tp.m3 = ceil_div(T, 256); tp.ngrp3 = ceil_div(g.win_uq, 2); }   // LDS-staged
     else { tp.m3 = ceil_div(T, 64); tp.ngrp3 = g.win_uq; }                            // 64-token waves
     tp.m4 = ceil_div(T, 16 * tp.mt); tp.cg4 = ceil_div(g.uk_w, 8);
   }
-  // large: two k splits, so that the 1-block-per-CU grid fills whole rounds
-  const int target = tp.large ? 2 * tp.m1 * tp.ngrp1 : kTiledK1Blocks;
+  // large: two k splits, so that the 1-block-per-CU grid fills whole rounds;
+  // medium LDS-staged: about one block per CU
+  const int target = tp.large ? 2 * tp.m1 * tp.ngrp1 : tp.wm == 2 ? 256 : kTiledK1Blocks;
   int S = std::max(1, std::min(g.nst_he, target / std::max(1, tp.m1 * tp.ngrp1)));
   tp.sps = ceil_div(g.nst_he, S);
   tp.S = ceil_div(g.nst_he, tp.sps);
@@ -2133,8 +2136,12 @@ void launch_packed(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p,
 template <bool I8, int MT, int WM, class Mark>
 void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g,
                   bool q8, Mark& mark) {
-  k1_tiled<I8, MT, 1, 1, 1, 2><<<dim3(tp.m1 * tp.ngrp1 * tp.S), 64, 0, s>>>(d, p, g, tp.sps, tp.m1,
-                                                                           tp.ngrp1);
+  if (WM == 2)
+    k1_tiled<I8, 4, 1, 4, 2, 2, true><<<dim3(tp.m1 * tp.ngrp1 * tp.S), 512, 0, s>>>(d, p, g, tp.sps, tp.m1,
+                                                                                  tp.ngrp1);
+  else
+    k1_tiled<I8, MT, 1, 1, 1, 2><<<dim3(tp.m1 * tp.ngrp1 * tp.S), 64, 0, s>>>(d, p, g, tp.sps, tp.m1,
+                                                                             tp.ngrp1);
   mark(1);
   launch_norm<I8>(s, d, p, tp.S, g.nst_cq);
   mark(2);
