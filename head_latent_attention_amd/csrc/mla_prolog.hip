@@ -1409,80 +1409,92 @@ __device__ __forceinline__ APacked<I8, MT> tiles_from(const void* base, int64_t 
 // every wave then reads its fragments with conflict-free 16-byte LDS reads.
 // The global loads run three stages ahead of the MFMAs through two register
 // sets.  ns must be the same for the whole block.
-template <bool I8, int MT, int NWW, int WM, int WN, class AP, int RS = 2>
+template <bool I8, int MT, int NWW, int WM, int WN, class AP, int RS = 2, int KPB = 1>
 __device__ __forceinline__ void tile_mma_lds(const AP& ap, rsrc_t Wp, uint32_t wbase, uint32_t wstride,
                                              int nwin, int s0, int ns, uint8_t* lds,
                                              typename Stage<I8>::Acc (&acc)[MT][NWW * 4]) {
   using S = Stage<I8>;
   constexpr int NW = WM * WN, AT = MT * WM, BC = NWW * WN * 4, CH = (AT + BC) / NW;
   static_assert(AT % NW == 0 && BC % NW == 0, "the stage chunks must split evenly over the waves");
-  constexpr int BUF = (AT + BC) * 1024;
+  constexpr int BUF = (AT + BC) * 1024;   // one k-stage; a ring slot holds KPB of them
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = w % WM, wn = w / WM;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int j = 0; j < NWW * 4; ++j) acc[mt][j] = typename S::Acc{0, 0, 0, 0};
-  auto gload = [&](uint4 (&r)[CH], int j) {
-    const bool ok = j < ns;
-    const int st = s0 + j;
+  using Regs = uint4[KPB][CH];
+  // group g = stages s0 + g*KPB .. s0 + g*KPB + KPB - 1
+  auto gload = [&](Regs& r, int g) {
 #pragma unroll
-    for (int q = 0; q < CH; ++q) {
-      const int c = w + q * NW;   // chunk c: activation tile c, then weight chunk c - AT
-      if (q < AT / NW) {
-        r[q] = ap.load1(c, st, ok);
-      } else {
-        const int b = c - AT, v = b >> 2;
-        r[q] = bload16(Wp, ok && v < nwin ? wbase + uint32_t(v) * wstride + uint32_t(st) * 4096u +
-                                                uint32_t((b & 3) * 1024 + lane * 16)
-                                          : kOOB);
+    for (int kk = 0; kk < KPB; ++kk) {
+      const int j = g * KPB + kk;
+      const bool ok = j < ns;
+      const int st = s0 + j;
+#pragma unroll
+      for (int q = 0; q < CH; ++q) {
+        const int c = w + q * NW;   // chunk c: activation tile c, then weight chunk c - AT
+        if (q < AT / NW) {
+          r[kk][q] = ap.load1(c, st, ok);
+        } else {
+          const int b = c - AT, v = b >> 2;
+          r[kk][q] = bload16(Wp, ok && v < nwin ? wbase + uint32_t(v) * wstride + uint32_t(st) * 4096u +
+                                                      uint32_t((b & 3) * 1024 + lane * 16)
+                                                : kOOB);
+        }
       }
     }
   };
-  auto lwrite = [&](const uint4 (&r)[CH], int buf) {
+  auto lwrite = [&](const Regs& r, int slot) {
 #pragma unroll
-    for (int q = 0; q < CH; ++q)
-      *reinterpret_cast<uint4*>(lds + buf * BUF + (w + q * NW) * 1024 + lane * 16) = r[q];
+    for (int kk = 0; kk < KPB; ++kk)
+#pragma unroll
+      for (int q = 0; q < CH; ++q)
+        *reinterpret_cast<uint4*>(lds + (slot * KPB + kk) * BUF + (w + q * NW) * 1024 + lane * 16) = r[kk][q];
   };
-  auto compute = [&](int buf) {
-    const uint8_t* L = lds + buf * BUF;
-    typename S::Frag bf[NWW * 4];
+  auto compute = [&](int slot) {
 #pragma unroll
-    for (int j = 0; j < NWW * 4; ++j)
-      bf[j] = *reinterpret_cast<const typename S::Frag*>(L + (AT + wn * NWW * 4 + j) * 1024 + lane * 16);
+    for (int kk = 0; kk < KPB; ++kk) {
+      const uint8_t* L = lds + (slot * KPB + kk) * BUF;
+      typename S::Frag bf[NWW * 4];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const typename S::Frag af =
-          *reinterpret_cast<const typename S::Frag*>(L + (wm * MT + mt) * 1024 + lane * 16);
+      for (int j = 0; j < NWW * 4; ++j)
+        bf[j] = *reinterpret_cast<const typename S::Frag*>(L + (AT + wn * NWW * 4 + j) * 1024 + lane * 16);
 #pragma unroll
-      for (int j = 0; j < NWW * 4; ++j) acc[mt][j] = mfma(bf[j], af, acc[mt][j]);
+      for (int mt = 0; mt < MT; ++mt) {
+        const typename S::Frag af =
+            *reinterpret_cast<const typename S::Frag*>(L + (wm * MT + mt) * 1024 + lane * 16);
+#pragma unroll
+        for (int j = 0; j < NWW * 4; ++j) acc[mt][j] = mfma(bf[j], af, acc[mt][j]);
+      }
     }
   };
+  const int ngr = (ns + KPB - 1) / KPB;
+  // groups past ngr load as zeros, so an odd count costs one zero group but
+  // keeps the loop free of an exit between its two halves
   if constexpr (RS == 1) {
-    // one register set: stage k + 2 is loaded while stage k is computed and
+    // one register set: group k + 2 is loaded while group k is computed and
     // written to LDS one iteration later
-    uint4 R[CH];
+    Regs R;
     gload(R, 0);
     lwrite(R, 0);
     gload(R, 1);
     __syncthreads();
-    // stages past ns load as zeros, so an odd ns costs one zero stage
-    // but keeps the loop free of an exit between the two halves
-    for (int j = 0; j < ns; j += 2) {
-      compute(0);                      // stage j
+    for (int j = 0; j < ngr; j += 2) {
+      compute(0);                      // group j
       __builtin_amdgcn_sched_barrier(0);
-      lwrite(R, 1);                    // stage j + 1
+      lwrite(R, 1);                    // group j + 1
       gload(R, j + 2);
       __syncthreads();
-      compute(1);                      // stage j + 1
+      compute(1);                      // group j + 1
       __builtin_amdgcn_sched_barrier(0);
-      lwrite(R, 0);                    // stage j + 2
+      lwrite(R, 0);                    // group j + 2
       gload(R, j + 3);
       __syncthreads();
     }
     return;
   }
-  uint4 R0[CH], R1[CH];   // stage k waits in R(k % 2)
+  Regs R0, R1;   // group k waits in R(k % 2)
   gload(R0, 0);
   __builtin_amdgcn_sched_barrier(0);
   gload(R1, 1);
@@ -1490,15 +1502,15 @@ __device__ __forceinline__ void tile_mma_lds(const AP& ap, rsrc_t Wp, uint32_t w
   lwrite(R0, 0);
   gload(R0, 2);
   __syncthreads();
-  for (int j = 0; j < ns; j += 2) {   // as above, an odd ns adds one zero stage
-    compute(0);                      // stage j
+  for (int j = 0; j < ngr; j += 2) {
+    compute(0);                      // group j
     __builtin_amdgcn_sched_barrier(0);
-    lwrite(R1, 1);                   // stage j + 1
+    lwrite(R1, 1);                   // group j + 1
     gload(R1, j + 3);
     __syncthreads();
-    compute(1);                      // stage j + 1
+    compute(1);                      // group j + 1
     __builtin_amdgcn_sched_barrier(0);
-    lwrite(R0, 0);                   // stage j + 2
+    lwrite(R0, 0);                   // group j + 2
     gload(R0, j + 4);
     __syncthreads();
   }
@@ -1526,7 +1538,8 @@ __global__ __launch_bounds__(256) void k_pack_x(Dims d, Ptrs p, int nst) {
 }
 
 // XP: x is read fragment-packed from p.xp instead of row-major.
-template <bool I8, int MT, int NWW, int WM, int WN, int D, bool LC = false, bool XP = false, int RS = 2>
+template <bool I8, int MT, int NWW, int WM, int WN, int D, bool LC = false, bool XP = false, int RS = 2,
+          int KPB = 1>
 __global__ __launch_bounds__(64 * WM * WN) void k1_tiled(Dims d, Ptrs p, PackGeo pg, int sps, int mtiles,
                                                       int ngrp) {
   using St = Stage<I8>;
@@ -1547,10 +1560,10 @@ __global__ __launch_bounds__(64 * WM * WN) void k1_tiled(Dims d, Ptrs p, PackGeo
   const int s0 = split * sps;
   typename St::Acc acc[MT][NWW * 4];
   if constexpr (LC) {
-    __shared__ __attribute__((aligned(16))) uint8_t ring[2 * (MT * WM + NWW * WN * 4) * 1024];
+    __shared__ __attribute__((aligned(16))) uint8_t ring[2 * KPB * (MT * WM + NWW * WN * 4) * 1024];
     const int mb = mtile * BM, j0 = grp * GW;
     const int nsb = mb < d.T ? max(0, min(pg.nst_he, s0 + sps) - s0) : 0;
-    tile_mma_lds<I8, MT, NWW, WM, WN, APlain<I8, MT * WM>, RS>(rows_from<I8, MT * WM>(p.x, d.He, mb, d.T),
+    tile_mma_lds<I8, MT, NWW, WM, WN, APlain<I8, MT * WM>, RS, KPB>(rows_from<I8, MT * WM>(p.x, d.He, mb, d.T),
                                       make_rsrc(p.packed, pg.total),
                                       uint32_t(pg.off_dq + int64_t(j0) * pg.nst_he * 4096),
                                       uint32_t(pg.nst_he * 4096), tiles - j0, s0, nsb, ring, acc);
@@ -1593,11 +1606,16 @@ __global__ __launch_bounds__(64 * WM * WN) void k1_tiled(Dims d, Ptrs p, PackGeo
 // K3t: grid (token tiles fastest, then groups of W^UqQr windows).  Nope
 // windows go to q^C (bf16, workspace); a rope window goes through a per-wave
 // LDS tile of 16 tokens x 64 columns to RoPE and queryRopeOut.
-template <bool I8, int MT, int NWW, int WM, int WN, int D, bool LC = false, int RS = 2>
+template <bool I8, int MT, int NWW, int WM, int WN, int D, bool LC = false, int RS = 2, int KPB = 1>
 __global__ __launch_bounds__(64 * WM * WN) void k3_tiled(Dims d, Ptrs p, PackGeo pg, int mtiles) {
   using St = Stage<I8>;
   constexpr int BM = 16 * MT * WM, GW = NWW * WN;
-  __shared__ float E[WM * WN][16 * 65];
+  // per-wave RoPE tiles; with the LDS-staged core they reuse its ring,
+  // which is idle once the main loop has ended with a barrier
+  constexpr int ERING = 2 * KPB * (MT * WM + NWW * WN * 4) * 1024;
+  constexpr int EBYTES = WM * WN * 16 * 65 * 4;
+  static_assert(!LC || EBYTES <= ERING, "the RoPE tiles must fit in the ring");
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k3[LC ? ERING : EBYTES];
   const int mtile = blockIdx.x % mtiles, grp = blockIdx.x / mtiles;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = w % WM, wn = w / WM;
@@ -1610,9 +1628,9 @@ __global__ __launch_bounds__(64 * WM * WN) void k3_tiled(Dims d, Ptrs p, PackGeo
   }
   typename St::Acc acc[MT][NWW * 4];
   if constexpr (LC) {
-    __shared__ __attribute__((aligned(16))) uint8_t ring[2 * (MT * WM + NWW * WN * 4) * 1024];
+    uint8_t* ring = lds_k3;
     const int mb = mtile * BM, j0 = grp * GW;
-    tile_mma_lds<I8, MT, NWW, WM, WN, APacked<I8, MT * WM>, RS>(
+    tile_mma_lds<I8, MT, NWW, WM, WN, APacked<I8, MT * WM>, RS, KPB>(
         tiles_from<I8, MT * WM>(p.cq, int64_t(pg.nst_cq) * 1024, (d.T + 15) / 16, mb),
         make_rsrc(p.packed, pg.total), uint32_t(pg.off_uq + int64_t(j0) * pg.nst_cq * 4096),
         uint32_t(pg.nst_cq * 4096), pg.win_uq - j0, 0, mb < d.T ? pg.nst_cq : 0, ring, acc);
@@ -1624,7 +1642,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k3_tiled(Dims d, Ptrs p, PackGeo
   if (m0 >= d.T) return;
   const int g = lane >> 4, c = lane & 15;
   const int P = pg.nope_w + 1, hf = d.Dr / 2;
-  float* e = E[w];
+  float* e = reinterpret_cast<float*>(lds_k3) + w * 16 * 65;
 #pragma unroll
   for (int i = 0; i < NWW; ++i) {
     const int j = grp * GW + wn * NWW + i;
