@@ -53,6 +53,26 @@ def algorithmic(inp, T):
                 step_bytes=step_bytes, step_flop=k1_flop + k3_flop + k4_flop)
 
 
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary profiles/traffic_<workload>.json (FETCH_SIZE and WRITE_SIZE per
+    dispatch, each scaled by what the counter reads for a plain copy of known
+    size), or None when there is none or the kernel source has changed since
+    the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    src = os.path.join(ROOT, "head_latent_attention_amd", "csrc", "mla_prolog.hip")
+    with open(src, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    if t.get("source_sha256") != digest or t.get("bench_kernel") != kernel:
+        return None
+    return t["traffic_bytes"]
+
+
 def cpu_baseline(inp, seconds):
     """The oracle, as it is, over repeated passes of the workload's first
     tokens until about ``seconds`` of host time are spent."""
@@ -88,7 +108,21 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--row-major", action="store_true",
                     help="run on the row-major weights only (no packed copy)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run five device-to-device copies of MIB MiB (the known-size copy "
+                         "that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration << 20
+        a = torch.full((n,), 1, dtype=torch.uint8, device="cuda:0")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "copies": 5}), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the prolog shards by tokens or heads with no exchange; see the design notes)",
@@ -184,6 +218,8 @@ def main():
                 "unit": "TFLOP/s", "frac": path_ach / BF16_PEAK_TFLOPS,
                 "flop_per_step": alg["step_flop"]}
     roof["kernel"] = "up_proj+uk (fused)" if fused else "up_proj"
+    if not args.row_major:
+        roof["traffic"] = measured_traffic(wl.name, roof["kernel"])
     roof["per_launch"] = (f"{alg['k3_bytes']} B" if decode else f"{alg['k3_flop']} FLOP")
 
     out = {
