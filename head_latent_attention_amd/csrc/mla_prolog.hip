@@ -1452,21 +1452,24 @@ __device__ __forceinline__ void tile_mma_lds(const AP& ap, rsrc_t Wp, uint32_t w
       for (int q = 0; q < CH; ++q)
         *reinterpret_cast<uint4*>(lds + (slot * KPB + kk) * BUF + (w + q * NW) * 1024 + lane * 16) = r[kk][q];
   };
+  // all of a stage's fragment reads are issued before its MFMAs, so the
+  // LDS latency is paid once per stage rather than once per token tile
   auto compute = [&](int slot) {
 #pragma unroll
     for (int kk = 0; kk < KPB; ++kk) {
       const uint8_t* L = lds + (slot * KPB + kk) * BUF;
-      typename S::Frag bf[NWW * 4];
+      typename S::Frag bf[NWW * 4], af[MT];
 #pragma unroll
       for (int j = 0; j < NWW * 4; ++j)
         bf[j] = *reinterpret_cast<const typename S::Frag*>(L + (AT + wn * NWW * 4 + j) * 1024 + lane * 16);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const typename S::Frag af =
-            *reinterpret_cast<const typename S::Frag*>(L + (wm * MT + mt) * 1024 + lane * 16);
+      for (int mt = 0; mt < MT; ++mt)
+        af[mt] = *reinterpret_cast<const typename S::Frag*>(L + (wm * MT + mt) * 1024 + lane * 16);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < NWW * 4; ++j) acc[mt][j] = mfma(bf[j], af, acc[mt][j]);
-      }
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < NWW * 4; ++j) acc[mt][j] = mfma(bf[j], af[mt], acc[mt][j]);
     }
   };
   const int ngr = (ns + KPB - 1) / KPB;
