@@ -274,3 +274,21 @@ def test_tiled_int8_large_packed():
 def test_full_size_tiled_packed(name):
     inp = synth.make_inputs(synth.workload(name))
     full_check(inp, rows=sample_rows(int(inp["T"])), packed=True)
+
+
+# ---- the token counts where the launch shapes change --------------------------
+BOUNDARY_DIMS = Dims(He=512, Hcq=128, Hckv=64, N=2, D=32, Dr=16)
+
+
+@pytest.mark.parametrize("T", [32, 33, 64, 65, 128, 129, 256, 257, 2047, 2048])
+def test_shape_boundaries_bf16_packed(T):
+    wl = custom_workload(f"boundary_t{T}", T=T, dims=BOUNDARY_DIMS, block_num=(T + 15) // 16 + 1,
+                         block_size=16, seed=50 + T)
+    full_check(synth.make_inputs(wl), packed=True)
+
+
+@pytest.mark.parametrize("T", [32, 33, 128, 129])
+def test_shape_boundaries_int8_packed(T):
+    wl = custom_workload(f"boundary_q8_t{T}", T=T, dims=Dims(He=512, Hcq=128, Hckv=96, N=2, D=32, Dr=32),
+                         block_num=(T + 15) // 16 + 1, block_size=16, quant=True, seed=60 + T)
+    full_check(synth.make_inputs(wl), packed=True)
