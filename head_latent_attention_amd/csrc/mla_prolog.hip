@@ -1617,8 +1617,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k3_tiled(Dims d, Ptrs p, PackGeo
   // which is idle once the main loop has ended with a barrier
   constexpr int ERING = 2 * KPB * (MT * WM + NWW * WN * 4) * 1024;
   constexpr int EBYTES = WM * WN * 16 * 65 * 4;
-  static_assert(!LC || EBYTES <= ERING, "the RoPE tiles must fit in the ring");
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k3[LC ? ERING : EBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k3[LC && ERING > EBYTES ? ERING : EBYTES];
   const int mtile = blockIdx.x % mtiles, grp = blockIdx.x / mtiles;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = w % WM, wn = w / WM;
@@ -1913,8 +1912,10 @@ Plan make_plan(const mla_prolog_desc& d, int64_t T) {
 
 // Tiled path (token counts above the streaming range, packed weights).
 // Shape classes.  Large (T >= kTiledLargeT): K1 and K3 in LDS-staged
-// 256-token x 256-column blocks of eight 128x64 waves, K1 split in two
-// along He; K4 in 128-token x 512-column blocks of eight 128x64 waves.  Medium: K1 with one 16*mt-token
+// 256-token x 256-column blocks of sixteen 64x64 waves (four per SIMD, which
+// hides the LDS and barrier latency better than eight 128x64 waves), K1
+// split in two along He; K4 in 128-token x 512-column blocks of eight
+// 128x64 waves.  Medium: K1 with one 16*mt-token
 // wave per 64-column window, He split so that about kTiledK1Blocks blocks
 // run (above 128 tokens: LDS-staged 256 x 128 blocks, about one per CU);
 // K3 with one 64-token wave per window up to 128 tokens, LDS-staged
@@ -2178,12 +2179,12 @@ void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs&
 template <bool I8, class Mark>
 void tiled_large(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g,
                  bool q8, Mark& mark) {
-  k1_tiled<I8, 8, 1, 2, 4, 2, true><<<dim3(tp.m1 * tp.ngrp1 * tp.S), 512, 0, s>>>(d, p, g, tp.sps,
-                                                                                 tp.m1, tp.ngrp1);
+  k1_tiled<I8, 4, 1, 4, 4, 2, true><<<dim3(tp.m1 * tp.ngrp1 * tp.S), 1024, 0, s>>>(d, p, g, tp.sps,
+                                                                                  tp.m1, tp.ngrp1);
   mark(1);
   launch_norm<I8>(s, d, p, tp.S, g.nst_cq);
   mark(2);
-  k3_tiled<I8, 8, 1, 2, 4, 2, true><<<dim3(tp.m3 * tp.ngrp3), 512, 0, s>>>(d, p, g, tp.m3);
+  k3_tiled<I8, 4, 1, 4, 4, 2, true><<<dim3(tp.m3 * tp.ngrp3), 1024, 0, s>>>(d, p, g, tp.m3);
   mark(3);
   if (q8) k4_tiled<4, 1, 1, 8, 2, true, false, true><<<dim3(tp.m4q * d.N), 512, 0, s>>>(d, p, g, tp.m4q, 1);
   else k4_tiled<8, 1, 1, 8, 2, false, false, true><<<dim3(tp.m4 * tp.cg4 * d.N), 512, 0, s>>>(d, p, g, tp.m4,
