@@ -1914,8 +1914,7 @@ Plan make_plan(const mla_prolog_desc& d, int64_t T) {
 // Shape classes.  Large (T >= kTiledLargeT): K1 and K3 in LDS-staged
 // 256-token x 256-column blocks of sixteen 64x64 waves (four per SIMD, which
 // hides the LDS and barrier latency better than eight 128x64 waves), K1
-// split in two along He; K4 in 128-token x 512-column blocks of eight
-// 128x64 waves.  Medium: K1 with one 16*mt-token
+// split in two along He; K4 likewise (bf16 query), heads fastest.  Medium: K1 with one 16*mt-token
 // wave per 64-column window, He split so that about kTiledK1Blocks blocks
 // run (above 128 tokens: LDS-staged 256 x 128 blocks, about one per CU);
 // K3 with one 64-token wave per window up to 128 tokens, LDS-staged
@@ -1943,7 +1942,7 @@ TiledPlan tiled_plan(const mla_prolog_desc& d, int64_t T) {
   if (tp.large) {
     tp.m1 = ceil_div(T, 256); tp.ngrp1 = ceil_div(tiles, 4);      // LDS-staged 256 x 256
     tp.m3 = ceil_div(T, 256); tp.ngrp3 = ceil_div(g.win_uq, 4);
-    tp.m4 = ceil_div(T, 128); tp.cg4 = ceil_div(g.uk_w, 8);
+    tp.m4 = ceil_div(T, 256); tp.cg4 = ceil_div(g.uk_w, 4);      // LDS-staged 256 x 256
   } else {
     if (tp.wm == 2) { tp.m1 = ceil_div(T, 256); tp.ngrp1 = ceil_div(tiles, 2); }     // LDS-staged
     else { tp.m1 = ceil_div(T, 16 * tp.mt); tp.ngrp1 = tiles; }
@@ -2187,7 +2186,7 @@ void tiled_large(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs& 
   k3_tiled<I8, 4, 1, 4, 4, 2, true><<<dim3(tp.m3 * tp.ngrp3), 1024, 0, s>>>(d, p, g, tp.m3);
   mark(3);
   if (q8) k4_tiled<4, 1, 1, 8, 2, true, false, true><<<dim3(tp.m4q * d.N), 512, 0, s>>>(d, p, g, tp.m4q, 1);
-  else k4_tiled<8, 1, 1, 8, 2, false, false, true><<<dim3(tp.m4 * tp.cg4 * d.N), 512, 0, s>>>(d, p, g, tp.m4,
+  else k4_tiled<4, 1, 4, 4, 2, false, true, true><<<dim3(tp.m4 * tp.cg4 * d.N), 1024, 0, s>>>(d, p, g, tp.m4,
                                                                                           tp.cg4);
   mark(4);
 }
