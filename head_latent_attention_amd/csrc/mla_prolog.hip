@@ -1414,8 +1414,10 @@ __device__ __forceinline__ void tile_mma_lds(const AP& ap, rsrc_t Wp, uint32_t w
                                              int nwin, int s0, int ns, uint8_t* lds,
                                              typename Stage<I8>::Acc (&acc)[MT][NWW * 4]) {
   using S = Stage<I8>;
-  constexpr int NW = WM * WN, AT = MT * WM, BC = NWW * WN * 4, CH = (AT + BC) / NW;
-  static_assert(AT % NW == 0 && BC % NW == 0, "the stage chunks must split evenly over the waves");
+  // chunks of a stage: AT activation tiles, then BC weight chunks; wave w
+  // takes activation tiles w, w + NW, ... and weight chunks w, w + NW, ...
+  constexpr int NW = WM * WN, AT = MT * WM, BC = NWW * WN * 4;
+  constexpr int CA = (AT + NW - 1) / NW, CB = (BC + NW - 1) / NW, CH = CA + CB;
   constexpr int BUF = (AT + BC) * 1024;   // one k-stage; a ring slot holds KPB of them
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = w % WM, wn = w / WM;
@@ -1432,25 +1434,31 @@ __device__ __forceinline__ void tile_mma_lds(const AP& ap, rsrc_t Wp, uint32_t w
       const bool ok = j < ns;
       const int st = s0 + j;
 #pragma unroll
-      for (int q = 0; q < CH; ++q) {
-        const int c = w + q * NW;   // chunk c: activation tile c, then weight chunk c - AT
-        if (q < AT / NW) {
-          r[kk][q] = ap.load1(c, st, ok);
-        } else {
-          const int b = c - AT, v = b >> 2;
-          r[kk][q] = bload16(Wp, ok && v < nwin ? wbase + uint32_t(v) * wstride + uint32_t(st) * 4096u +
-                                                      uint32_t((b & 3) * 1024 + lane * 16)
-                                                : kOOB);
-        }
+      for (int q = 0; q < CA; ++q) {
+        const int c = w + q * NW;
+        r[kk][q] = ap.load1(c < AT ? c : 0, st, ok && c < AT);
+      }
+#pragma unroll
+      for (int q = 0; q < CB; ++q) {
+        const int b = w + q * NW, v = b >> 2;
+        r[kk][CA + q] = bload16(Wp, ok && b < BC && v < nwin ? wbase + uint32_t(v) * wstride + uint32_t(st) * 4096u +
+                                                                   uint32_t((b & 3) * 1024 + lane * 16)
+                                                             : kOOB);
       }
     }
   };
   auto lwrite = [&](const Regs& r, int slot) {
 #pragma unroll
-    for (int kk = 0; kk < KPB; ++kk)
+    for (int kk = 0; kk < KPB; ++kk) {
+      uint8_t* L = lds + (slot * KPB + kk) * BUF;
 #pragma unroll
-      for (int q = 0; q < CH; ++q)
-        *reinterpret_cast<uint4*>(lds + (slot * KPB + kk) * BUF + (w + q * NW) * 1024 + lane * 16) = r[kk][q];
+      for (int q = 0; q < CA; ++q)
+        if (w + q * NW < AT) *reinterpret_cast<uint4*>(L + (w + q * NW) * 1024 + lane * 16) = r[kk][q];
+#pragma unroll
+      for (int q = 0; q < CB; ++q)
+        if (w + q * NW < BC)
+          *reinterpret_cast<uint4*>(L + (AT + w + q * NW) * 1024 + lane * 16) = r[kk][CA + q];
+    }
   };
   // all of a stage's fragment reads are issued before its MFMAs, so the
   // LDS latency is paid once per stage rather than once per token tile
@@ -1925,7 +1933,8 @@ constexpr int kTiledK1Blocks = 512;   // medium: one-wave blocks
 
 struct TiledPlan {
   bool large;
-  int mt, wm;              // medium: 16-token tiles per wave, waves along tokens (K3, K4)
+  int mt;                  // medium: 16-token tiles per K4 wave (and per direct K1 wave)
+  int k1v, k3v;            // medium kernel shapes: 0 direct, 1 LDS-staged 256-token, 2 LDS-staged 128-token
   int m1, ngrp1, S, sps;   // K1: token tiles, window groups, splits, stages per split
   int m3, ngrp3;           // K3
   int m4, cg4;             // K4 bf16
@@ -1938,21 +1947,25 @@ TiledPlan tiled_plan(const mla_prolog_desc& d, int64_t T) {
   const int tiles = g.win_dq + g.win_kr;
   tp.large = T >= kTiledLargeT;
   tp.mt = T <= 64 ? 4 : 8;
-  tp.wm = (!tp.large && T > 128) ? 2 : 1;
+  // medium shapes: LDS-staged blocks above 128 tokens; for int8 inputs also
+  // from 65 tokens on, in 128-token blocks (the int8 k-stages are twice as deep)
+  const bool i8 = d.in_dtype == MLA_INT8;
+  tp.k1v = tp.k3v = T > 128 ? 1 : (i8 && T > 64) ? 2 : 0;
   if (tp.large) {
     tp.m1 = ceil_div(T, 256); tp.ngrp1 = ceil_div(tiles, 4);      // LDS-staged 256 x 256
     tp.m3 = ceil_div(T, 256); tp.ngrp3 = ceil_div(g.win_uq, 4);
     tp.m4 = ceil_div(T, 256); tp.cg4 = ceil_div(g.uk_w, 4);      // LDS-staged 256 x 256
   } else {
-    if (tp.wm == 2) { tp.m1 = ceil_div(T, 256); tp.ngrp1 = ceil_div(tiles, 2); }     // LDS-staged
+    const int bm = tp.k1v == 1 ? 256 : 128;                                         // LDS-staged block rows
+    if (tp.k1v) { tp.m1 = ceil_div(T, bm); tp.ngrp1 = ceil_div(tiles, 2); }
     else { tp.m1 = ceil_div(T, 16 * tp.mt); tp.ngrp1 = tiles; }
-    if (tp.wm == 2) { tp.m3 = ceil_div(T, 256); tp.ngrp3 = ceil_div(g.win_uq, 2); }   // LDS-staged
+    if (tp.k3v) { tp.m3 = ceil_div(T, bm); tp.ngrp3 = ceil_div(g.win_uq, 2); }
     else { tp.m3 = ceil_div(T, 64); tp.ngrp3 = g.win_uq; }                            // 64-token waves
     tp.m4 = ceil_div(T, 16 * tp.mt); tp.cg4 = ceil_div(g.uk_w, 8);
   }
   // large: two k splits, so that the 1-block-per-CU grid fills whole rounds;
   // medium LDS-staged: about one block per CU
-  const int target = tp.large ? 2 * tp.m1 * tp.ngrp1 : tp.wm == 2 ? 256 : kTiledK1Blocks;
+  const int target = tp.large ? 2 * tp.m1 * tp.ngrp1 : tp.k1v ? 256 : kTiledK1Blocks;
   int S = std::max(1, std::min(g.nst_he, target / std::max(1, tp.m1 * tp.ngrp1)));
   tp.sps = ceil_div(g.nst_he, S);
   tp.S = ceil_div(g.nst_he, tp.sps);
@@ -2154,20 +2167,20 @@ void launch_packed(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p,
 }
 
 // Tiled run on packed weights (token counts above the streaming range).
-template <bool I8, int MT, int WM, class Mark>
+template <bool I8, int MT, class Mark>
 void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g,
                   bool q8, Mark& mark) {
-  if (WM == 2)
-    k1_tiled<I8, 4, 1, 4, 2, 2, true><<<dim3(tp.m1 * tp.ngrp1 * tp.S), 512, 0, s>>>(d, p, g, tp.sps, tp.m1,
-                                                                                  tp.ngrp1);
-  else
-    k1_tiled<I8, MT, 1, 1, 1, 2><<<dim3(tp.m1 * tp.ngrp1 * tp.S), 64, 0, s>>>(d, p, g, tp.sps, tp.m1,
-                                                                             tp.ngrp1);
+  const dim3 g1(tp.m1 * tp.ngrp1 * tp.S), g3(tp.m3 * tp.ngrp3);
+  if (tp.k1v == 1) k1_tiled<I8, 4, 1, 4, 2, 2, true><<<g1, 512, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
+  else if (I8 && tp.k1v == 2)
+    k1_tiled<I8, 2, 1, 4, 2, 2, true><<<g1, 512, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
+  else k1_tiled<I8, MT, 1, 1, 1, 2><<<g1, 64, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
   mark(1);
   launch_norm<I8>(s, d, p, tp.S, g.nst_cq);
   mark(2);
-  if (WM == 2) k3_tiled<I8, 4, 1, 4, 2, 2, true, 1><<<dim3(tp.m3 * tp.ngrp3), 512, 0, s>>>(d, p, g, tp.m3);
-  else k3_tiled<I8, 4, 1, 1, 1, 2><<<dim3(tp.m3 * tp.ngrp3), 64, 0, s>>>(d, p, g, tp.m3);
+  if (tp.k3v == 1) k3_tiled<I8, 2, 1, 8, 2, 2, true, 2><<<g3, 1024, 0, s>>>(d, p, g, tp.m3);
+  else if (I8 && tp.k3v == 2) k3_tiled<I8, 1, 1, 8, 2, 2, true, 1><<<g3, 1024, 0, s>>>(d, p, g, tp.m3);
+  else k3_tiled<I8, 4, 1, 1, 1, 2><<<g3, 64, 0, s>>>(d, p, g, tp.m3);
   mark(3);
   if (q8) k4_tiled<4, 1, 1, 8, 2, true, false, true><<<dim3(tp.m4q * d.N), 512, 0, s>>>(d, p, g, tp.m4q, 1);
   else k4_tiled<MT, 1, 1, 8, 2, false, false, true><<<dim3(tp.m4 * tp.cg4 * d.N), 512, 0, s>>>(d, p, g, tp.m4,
@@ -2200,14 +2213,11 @@ void launch_tiled(hipStream_t s, const Dims& d, const Ptrs& p, const mla_prolog_
     if (i8) tiled_large<true>(tp, s, d, p, g, q8, mark);
     else tiled_large<false>(tp, s, d, p, g, q8, mark);
   } else if (tp.mt == 4) {
-    if (i8) tiled_medium<true, 4, 1>(tp, s, d, p, g, q8, mark);
-    else tiled_medium<false, 4, 1>(tp, s, d, p, g, q8, mark);
-  } else if (tp.wm == 1) {
-    if (i8) tiled_medium<true, 8, 1>(tp, s, d, p, g, q8, mark);
-    else tiled_medium<false, 8, 1>(tp, s, d, p, g, q8, mark);
+    if (i8) tiled_medium<true, 4>(tp, s, d, p, g, q8, mark);
+    else tiled_medium<false, 4>(tp, s, d, p, g, q8, mark);
   } else {
-    if (i8) tiled_medium<true, 8, 2>(tp, s, d, p, g, q8, mark);
-    else tiled_medium<false, 8, 2>(tp, s, d, p, g, q8, mark);
+    if (i8) tiled_medium<true, 8>(tp, s, d, p, g, q8, mark);
+    else tiled_medium<false, 8>(tp, s, d, p, g, q8, mark);
   }
 }
 

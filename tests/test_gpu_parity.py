@@ -287,7 +287,7 @@ def test_shape_boundaries_bf16_packed(T):
     full_check(synth.make_inputs(wl), packed=True)
 
 
-@pytest.mark.parametrize("T", [32, 33, 128, 129])
+@pytest.mark.parametrize("T", [32, 33, 64, 65, 100, 128, 129])
 def test_shape_boundaries_int8_packed(T):
     wl = custom_workload(f"boundary_q8_t{T}", T=T, dims=Dims(He=512, Hcq=128, Hckv=96, N=2, D=32, Dr=32),
                          block_num=(T + 15) // 16 + 1, block_size=16, quant=True, seed=60 + T)
