@@ -246,6 +246,9 @@ struct Ptrs {
   float* cq_scale;   // [T]
   uint16_t* qc;      // [T][N][D] bf16
   uint8_t* xp;       // x fragment-packed (tiled path, medium T)
+  uint8_t* xq;       // [N] q^C exchange of the paired small-T kernel, kPairXq bytes a head
+  uint32_t* xflag;   // [N][4] its exchange flags, then one error word; zero between runs
+  float* xmax;       // [N][2][32] its per-token row maxima
   const uint8_t* packed;  // weights in the packed layout, or NULL
 };
 
@@ -1320,6 +1323,311 @@ __global__ __launch_bounds__(64 * NW) void k34_stream(Dims d, Ptrs p, PackGeo pg
   }
 }
 
+// K34p: the up-projection and the W^UK product for small token counts
+// (T <= 16 * MT) with two blocks per head, for heads of two nope windows and
+// Dr = 64.  Half p of head h streams nope window p (q^C columns 64p ..),
+// the rope column tiles p and p + 2 (the RoPE pairs i, i + 32 stay in one
+// lane) and the W^UK windows of its half of Hckv, so every block moves the
+// same bytes.  The halves trade their q^C columns (bf16, 4 KB) through a
+// per-head exchange buffer: each block publishes its half with a release
+// flag and waits for its partner's, which is already running (a head's two
+// blocks are on the same XCD when N % 8 == 0); the wait is bounded and a
+// block that gives up marks an error word.  The consumer clears the flag, so
+// every run starts from zero flags.  Products use swapped MFMA operands
+// (weights as the A operand), so a lane's accumulator holds four adjacent
+// columns of one token: q^C goes to the exchange buffer in 8-byte pieces,
+// q^N and q^R leave in 8-byte stores.  With the int8 query the two halves
+// also trade their per-token row maxima.  The wave partial sums are added in
+// wave order, so the result is deterministic.  512 threads.
+constexpr int kPairSpin = 1 << 20;
+
+// The exchanged words are written and read with agent-scope relaxed atomics,
+// which bypass the caches that are not coherent across XCDs, so no L2
+// writeback or invalidation (an agent-scope fence) is needed: a wave waits
+// for its own exchange stores to complete, the block meets at a barrier, and
+// one lane raises the flag.
+__device__ __forceinline__ void xstore64(void* p, uint2 v) {
+  __hip_atomic_store(static_cast<uint64_t*>(p), (uint64_t(v.y) << 32) | v.x, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint4 xload128(const void* p) {
+  const uint64_t a = __hip_atomic_load(static_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t b =
+      __hip_atomic_load(static_cast<const uint64_t*>(p) + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_uint4(uint32_t(a), uint32_t(a >> 32), uint32_t(b), uint32_t(b >> 32));
+}
+
+__device__ __forceinline__ void pair_publish(uint32_t* flag) {
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's exchange stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void pair_wait(uint32_t* flag, uint32_t* err) {
+  if (threadIdx.x == 0) {
+    int n = 0;
+    while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+      if (++n > kPairSpin) {
+        __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    __hip_atomic_store(flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+}
+
+constexpr int kPairXq = 8192;   // exchange bytes per head: 2 token tiles x 4 D stages x 1 KB
+
+template <bool I8, int MT, bool Q8, int D = 2>
+__global__ __launch_bounds__(512) void k34_pair(Dims d, Ptrs p, PackGeo pg) {
+  using St = Stage<I8>;
+  using Acc = typename St::Acc;
+  using Frag = typename St::Frag;
+  constexpr int NW = 8, NT = 6 * MT;   // parked tiles per wave: nope MT x 4, rope MT x 2
+  __shared__ uint4 red[NW * NT * 64];
+  __shared__ float rmw[NW][32];
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int b = blockIdx.x;
+  const int h = d.N % 8 == 0 ? (b / 16) * 8 + b % 8 : b / 2;
+  const int half = d.N % 8 == 0 ? (b / 8) % 2 : b % 2;
+  const int P = pg.nope_w, DDr = d.D + d.Dr;
+  const rsrc_t Wp = make_rsrc(p.packed, pg.total);
+  const int64_t ctile = int64_t(pg.nst_cq) * 1024;
+  const APacked<I8, MT> ap{make_rsrc(p.cq, int64_t((d.T + 15) / 16) * ctile), uint32_t(ctile)};
+  uint8_t* xq = p.xq + int64_t(h) * kPairXq;
+
+  // W^UK fragments first: window j of this half, column tiles 2 (w % 2) + k,
+  // every D stage; their latency hides under the stream
+  const int ja = (pg.uk_w + 1) / 2, jlo = half ? ja : 0, jhi = half ? pg.uk_w : ja;
+  const int j = jlo + w / 2, ctu = 2 * (w % 2);
+  const bool ukact = j < jhi;
+  const uint32_t ukb = uint32_t(pg.off_uk + int64_t(h * pg.uk_w + (ukact ? j : 0)) * pg.nst_d * 4096);
+  uint4 bu[4][2];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      bu[s][k] = bload16(Wp, ukact && s < pg.nst_d ? ukb + uint32_t(s * 4096 + (ctu + k) * 1024 + lane * 16)
+                                                   : kOOB);
+
+  // the stream: stages w, w + 8, ... of nope window `half` (4 column tiles)
+  // and of the rope window (column tiles half, half + 2), one activation load
+  // for both
+  const uint32_t nb = uint32_t(pg.off_uq + int64_t(h * (P + 1) + half) * pg.nst_cq * 4096);
+  const uint32_t rb = uint32_t(pg.off_uq + int64_t(h * (P + 1) + P) * pg.nst_cq * 4096);
+  const int ns = w < pg.nst_cq ? (pg.nst_cq - w + NW - 1) / NW : 0;
+  Acc an[MT][4], ar[MT][2];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) an[mt][ct] = Acc{0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < 2; ++k) ar[mt][k] = Acc{0, 0, 0, 0};
+  }
+  uint4 qb[D][6], qa[D][MT];
+  auto issue = [&](int q, int jj) {
+    const int st = w + jj * NW;
+    const bool ok = jj < ns;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+      qb[q][ct] = bload16(Wp, ok ? nb + uint32_t(st) * 4096u + uint32_t(ct * 1024 + lane * 16) : kOOB);
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      qb[q][4 + k] = bload16(Wp, ok ? rb + uint32_t(st) * 4096u + uint32_t((half + 2 * k) * 1024 + lane * 16)
+                                    : kOOB);
+    ap.load(qa[q], st, ok);
+  };
+  auto consume = [&](int q) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const Frag af = ap.frag(qa[q], mt);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) an[mt][ct] = mfma(__builtin_bit_cast(Frag, qb[q][ct]), af, an[mt][ct]);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) ar[mt][k] = mfma(__builtin_bit_cast(Frag, qb[q][4 + k]), af, ar[mt][k]);
+    }
+  };
+#pragma unroll
+  for (int q = 0; q < D; ++q) {
+    issue(q, q);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // the last round issues no refills, so no load is left in flight
+  const int nsr = (ns + D - 1) / D * D;
+  for (int j0 = 0; j0 < nsr - D; j0 += D) {
+#pragma unroll
+    for (int q = 0; q < D; ++q) {
+      consume(q);
+      issue(q, j0 + q + D);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < D; ++q) {
+    consume(q);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // every wave parks its tiles; tile q is summed in wave order by its owner
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) red[(w * NT + mt * 4 + ct) * 64 + lane] = __builtin_bit_cast(uint4, an[mt][ct]);
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      red[(w * NT + 4 * MT + mt * 2 + k) * 64 + lane] = __builtin_bit_cast(uint4, ar[mt][k]);
+  }
+  __syncthreads();
+  auto sum_tile = [&](int q) {
+    Acc s = __builtin_bit_cast(Acc, red[q * 64 + lane]);
+#pragma unroll
+    for (int w2 = 1; w2 < NW; ++w2) s += __builtin_bit_cast(Acc, red[(w2 * NT + q) * 64 + lane]);
+    return s;
+  };
+
+  // q^C tile (mt, ct) of this half -> bf16 -> exchange buffer, in the
+  // fragment order of the W^UK product's activation operand
+  if (w < 4 * MT) {
+    const int mt = w / 4, ct = w % 4, t = 16 * mt + c;
+    const Acc s = sum_tile(w);
+    const int col = 64 * half + 16 * ct + 4 * g;   // q^C column of element 0
+    float v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (I8)
+        v[r] = (t < d.T && col + r < d.D)
+                   ? static_cast<float>(s[r]) * p.cq_scale[t] * p.sw_uq_qr[h * DDr + col + r]
+                   : 0.0f;
+      else
+        v[r] = s[r];
+    }
+    const int st = 2 * half + ct / 2;
+    if (st < pg.nst_d)
+      xstore64(xq + (mt * 4 + st) * 1024 + (16 * (2 * (ct % 2) + g / 2) + c) * 16 + 8 * (g % 2),
+               pack_bf16x4(v[0], v[1], v[2], v[3]));
+  }
+  pair_publish(p.xflag + 4 * h + half);
+
+  // q^R: the owner of token tile mt holds both tiles of every RoPE pair
+  if (w >= NW - MT) {
+    const int mt = NW - 1 - w, t = 16 * mt + c;
+    const Acc a0 = sum_tile(4 * MT + 2 * mt), a1 = sum_tile(4 * MT + 2 * mt + 1);
+    if (t < d.T) {
+      const int i0 = 16 * half + 4 * g, hf = d.Dr / 2;
+      const uint2 c0 = *reinterpret_cast<const uint2*>(p.cos + int64_t(t) * d.Dr + i0);
+      const uint2 c1 = *reinterpret_cast<const uint2*>(p.cos + int64_t(t) * d.Dr + i0 + hf);
+      const uint2 s0 = *reinterpret_cast<const uint2*>(p.sin + int64_t(t) * d.Dr + i0);
+      const uint2 s1 = *reinterpret_cast<const uint2*>(p.sin + int64_t(t) * d.Dr + i0 + hf);
+      const uint16_t* cs0 = reinterpret_cast<const uint16_t*>(&c0);
+      const uint16_t* cs1 = reinterpret_cast<const uint16_t*>(&c1);
+      const uint16_t* sn0 = reinterpret_cast<const uint16_t*>(&s0);
+      const uint16_t* sn1 = reinterpret_cast<const uint16_t*>(&s1);
+      float o0[4], o1[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float a, bb;
+        if constexpr (I8) {
+          a = static_cast<float>(a0[r]) * p.cq_scale[t] * p.sw_uq_qr[h * DDr + d.D + i0 + r];
+          bb = static_cast<float>(a1[r]) * p.cq_scale[t] * p.sw_uq_qr[h * DDr + d.D + i0 + hf + r];
+        } else {
+          a = a0[r];
+          bb = a1[r];
+        }
+        o0[r] = a * bf2f(cs0[r]) - bb * bf2f(sn0[r]);
+        o1[r] = bb * bf2f(cs1[r]) + a * bf2f(sn1[r]);
+      }
+      uint16_t* o = p.qr_out + (int64_t(t) * d.N + h) * d.Dr + i0;
+      *reinterpret_cast<uint2*>(o) = pack_bf16x4(o0[0], o0[1], o0[2], o0[3]);
+      *reinterpret_cast<uint2*>(o + hf) = pack_bf16x4(o1[0], o1[1], o1[2], o1[3]);
+    }
+  }
+
+  // q^N = q^C W^UK[h] over this half's columns, all of D
+  pair_wait(p.xflag + 4 * h + (1 - half), p.xflag + 4 * d.N);
+  uint4 aq[4][MT];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      aq[s][mt] = s < pg.nst_d ? xload128(xq + (mt * 4 + s) * 1024 + lane * 16) : make_uint4(0, 0, 0, 0);
+  f32x4 au[MT][2];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      au[mt][k] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        au[mt][k] = mfma(__builtin_bit_cast(bf16x8, bu[s][k]), __builtin_bit_cast(bf16x8, aq[s][mt]), au[mt][k]);
+    }
+  const int col0 = 64 * j + 16 * ctu + 4 * g;   // q^N column of element 0 of tile k = 0
+  if constexpr (!Q8) {
+    if (!ukact) return;
+    uint16_t* qo = static_cast<uint16_t*>(p.q_out);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int t = 16 * mt + c;
+      if (t >= d.T) continue;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int col = col0 + 16 * k;
+        if (col < d.Hckv)
+          *reinterpret_cast<uint2*>(qo + (int64_t(t) * d.N + h) * d.Hckv + col) =
+              pack_bf16x4(au[mt][k][0], au[mt][k][1], au[mt][k][2], au[mt][k][3]);
+      }
+    }
+  } else {
+    // per-token max |q^N| of this block, then of the head
+    float* xm = p.xmax + int64_t(h) * 64;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      float m = 0.0f;
+      if (ukact)
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+          if (col0 + 16 * k < d.Hckv)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(au[mt][k][r]));
+      m = fmaxf(m, __shfl_xor(m, 16, 64));
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      if (g == 0) rmw[w][16 * mt + c] = m;
+    }
+    __syncthreads();
+    if (w == 0 && lane < 16 * MT) {
+      float m = rmw[0][lane];
+#pragma unroll
+      for (int w2 = 1; w2 < NW; ++w2) m = fmaxf(m, rmw[w2][lane]);
+      __hip_atomic_store(xm + 32 * half + lane, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    pair_publish(p.xflag + 4 * h + 2 + half);
+    pair_wait(p.xflag + 4 * h + 2 + (1 - half), p.xflag + 4 * d.N);
+    if (!ukact) return;
+    int8_t* qo = static_cast<int8_t*>(p.q_out);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int t = 16 * mt + c;
+      if (t >= d.T) continue;
+      const float amax = fmaxf(__hip_atomic_load(xm + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                               __hip_atomic_load(xm + 32 + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      const float sc = amax / 127.0f;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int col = col0 + 16 * k;
+        if (col >= d.Hckv) continue;
+        uint32_t u = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          u |= uint32_t(uint8_t(sc > 0.0f ? quant_code(au[mt][k][r], sc) : 0)) << (8 * r);
+        *reinterpret_cast<uint32_t*>(qo + (int64_t(t) * d.N + h) * d.Hckv + col) = u;
+      }
+      if (half == 0 && w == 0 && g == 0) p.q_scale[int64_t(t) * d.N + h] = sc;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Tiled path for larger token counts.  Every wave owns a 16*MT-token x
 // 64*NWW-column output tile and streams the packed k-stages of its NWW
@@ -1976,7 +2284,7 @@ TiledPlan tiled_plan(const mla_prolog_desc& d, int64_t T) {
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t part, cq, cq_scale, qc, total;
+  size_t part, cq, cq_scale, qc, xq, xflag, xmax, total;
 };
 
 Layout layout(const mla_prolog_desc& d) {
@@ -2000,7 +2308,10 @@ Layout layout(const mla_prolog_desc& d) {
   L.cq = align256(L.part + size_t(part_rows) * Ntot * 4);
   L.cq_scale = align256(L.cq + cq_bytes);
   L.qc = align256(L.cq_scale + size_t(d.max_tokens) * 4);
-  L.total = align256(L.qc + qc_bytes);
+  L.xq = align256(L.qc + qc_bytes);
+  L.xflag = align256(L.xq + size_t(d.N) * kPairXq);
+  L.xmax = align256(L.xflag + size_t(4 * d.N + 1) * 4);
+  L.total = align256(L.xmax + size_t(d.N) * 64 * 4);
   return L;
 }
 
@@ -2138,6 +2449,14 @@ void packed_launch(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p, 
   mark(1);
   launch_norm<I8>(s, d, p, pl.Sp, g.nst_cq);
   mark(2);
+  if (g.nope_w == 2 && d.Dr == 64 && g.uk_w <= 8) {
+    // two balanced blocks per head; the profile books both products to the first
+    if (q8) k34_pair<I8, MT, true><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g);
+    else k34_pair<I8, MT, false><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g);
+    mark(3);
+    mark(-1);
+    return;
+  }
   if (g.nope_w <= kK34Waves && g.uk_w <= kK34Waves && g.nst_d <= kK34Stages) {
     // up-projection and W^UK fused; the profile books both to the first
     if (q8) k34_stream<I8, MT, 2, true><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g);
@@ -2297,6 +2616,13 @@ mla_status mla_prolog_create(const mla_prolog_desc* desc, mla_prolog_t* out) {
     (void)hipSetDevice(prev);
     return MLA_ERR_RUNTIME;
   }
+  // the exchange flags start at zero; every run leaves them at zero
+  if (hipMemset(h->ws + h->lay.xflag, 0, size_t(4 * desc->N + 1) * 4) != hipSuccess) {
+    (void)hipFree(h->ws);
+    delete h;
+    (void)hipSetDevice(prev);
+    return MLA_ERR_RUNTIME;
+  }
 
   (void)hipSetDevice(prev);
   *out = h;
@@ -2344,6 +2670,9 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   p.cq_scale = reinterpret_cast<float*>(h->ws + h->lay.cq_scale);
   p.qc = reinterpret_cast<uint16_t*>(h->ws + h->lay.qc);
   p.xp = nullptr;
+  p.xq = h->ws + h->lay.xq;
+  p.xflag = reinterpret_cast<uint32_t*>(h->ws + h->lay.xflag);
+  p.xmax = reinterpret_cast<float*>(h->ws + h->lay.xmax);
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   hipEvent_t* ev = nullptr;

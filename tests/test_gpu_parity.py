@@ -27,10 +27,12 @@ def say(msg):
     sys.stdout.flush()
 
 
-def run_gpu(inp, query_int8=None, max_tokens=None, T=None, repeat=1, packed=False):
+def run_gpu(inp, query_int8=None, max_tokens=None, T=None, repeat=1, packed=False, prerun_negated=False):
     """Upload, run through the C ABI, download.  Returns host arrays.  With
     ``packed`` the weights are first converted by mla_prolog_pack_weights
-    and the run reads the packed copy."""
+    and the run reads the packed copy.  With ``prerun_negated`` the handle
+    first runs once on -x (every intermediate differs), so that a result
+    left in the workspace by an earlier run cannot pass for this one's."""
     T = int(inp["T"]) if T is None else T
     t = dev.upload(inp, query_int8=query_int8)
     desc = mla.make_desc(**dev.desc_args(inp, max_tokens=max_tokens, query_int8=query_int8))
@@ -39,6 +41,8 @@ def run_gpu(inp, query_int8=None, max_tokens=None, T=None, repeat=1, packed=Fals
             buf = torch.empty(mla.packed_weights_bytes(desc), dtype=torch.uint8, device="cuda")
             h.pack_weights(t, buf)
             t["packed_weights"] = buf
+        if prerun_negated:
+            h.run(dict(t, token_x=-t["token_x"]), T)
         for _ in range(repeat):
             h.run(t, T)
         torch.cuda.synchronize()
@@ -46,11 +50,11 @@ def run_gpu(inp, query_int8=None, max_tokens=None, T=None, repeat=1, packed=Fals
             if k in ("query_out", "query_rope_out", "dequant_scale_q_nope", "kv_cache", "kr_cache")}
 
 
-def full_check(inp, query_int8=None, rows=None, packed=False):
+def full_check(inp, query_int8=None, rows=None, packed=False, repeat=1, prerun_negated=False):
     q8 = bool(inp["quant"]) if query_int8 is None else bool(query_int8)
     rows = np.arange(int(inp["T"])) if rows is None else np.asarray(rows)
     say(f"case {inp['workload']} T={inp['T']} dims={inp['dims']} q8={q8} rows={len(rows)} packed={packed}")
-    got = run_gpu(inp, query_int8=query_int8, packed=packed)
+    got = run_gpu(inp, query_int8=query_int8, packed=packed, repeat=repeat, prerun_negated=prerun_negated)
     ref = oracle.run(inp, tokens=rows, query_int8=query_int8, caches=False)
     check_queries(got, ref, rows, q8)
     check_caches(inp, got["kv_cache"], got["kr_cache"], ref, rows)
@@ -237,6 +241,42 @@ def test_int8_decode_t32_packed():
     # the int8 decode workload at 32 tokens runs on the packed small-T kernels
     inp = synth.make_inputs(synth.workload("int8_decode_t128"), T=32)
     full_check(inp, packed=True)
+
+
+# ---- packed weights, two blocks per head (two nope windows, Dr = 64) ---------
+# The halves of a head trade q^C (and, for the int8 query, the row maxima)
+# through flags that every run must leave at zero: each case runs on -x
+# first and then three times on x, on one handle.  Head counts with N % 8 == 0 and without take the two
+# block-to-head mappings; Hckv = 320 leaves the second half one W^UK window
+# short; D = 96 leaves the second nope window half empty.
+PAIR = {
+    "pair_t5_n4": custom_workload("pair_t5_n4", T=5, dims=Dims(He=512, Hcq=256, Hckv=128, N=4, D=128, Dr=64),
+                                  block_num=2, block_size=16, seed=70),
+    "pair_t32_n8": custom_workload("pair_t32_n8", T=32, dims=Dims(He=256, Hcq=192, Hckv=320, N=8, D=96, Dr=64),
+                                   block_num=4, block_size=16, seed=71),
+    "pair_t16_n16": custom_workload("pair_t16_n16", T=16, dims=Dims(He=384, Hcq=128, Hckv=512, N=16, D=128, Dr=64),
+                                    block_num=2, block_size=16, seed=72),
+    "pair_t27_n3": custom_workload("pair_t27_n3", T=27, dims=Dims(He=256, Hcq=160, Hckv=64, N=3, D=72, Dr=64),
+                                   block_num=3, block_size=16, seed=73),
+}
+PAIR_INT8 = {
+    "pair_q8_t17_n16": custom_workload("pair_q8_t17_n16", T=17, dims=Dims(He=512, Hcq=256, Hckv=256, N=16, D=128, Dr=64),
+                                       block_num=2, block_size=16, seed=74, quant=True),
+    "pair_q8_t3_n3": custom_workload("pair_q8_t3_n3", T=3, dims=Dims(He=256, Hcq=128, Hckv=320, N=3, D=96, Dr=64),
+                                     block_num=1, block_size=16, seed=75, quant=True),
+}
+
+
+@pytest.mark.parametrize("name", list(PAIR))
+def test_pair_bf16_packed(name):
+    full_check(synth.make_inputs(PAIR[name]), packed=True, repeat=3, prerun_negated=True)
+
+
+@pytest.mark.parametrize("name", list(PAIR_INT8))
+def test_pair_int8_packed(name):
+    inp = synth.make_inputs(PAIR_INT8[name])
+    full_check(inp, packed=True, repeat=3, prerun_negated=True)
+    full_check(inp, query_int8=False, packed=True, repeat=3, prerun_negated=True)
 
 
 # ---- packed weights, tiled kernels (token counts above 32) -------------------
