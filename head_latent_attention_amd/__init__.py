@@ -37,7 +37,7 @@ MLA_INT8 = 1
 EXPORTS = ("mla_prolog_validate", "mla_prolog_workspace_bytes", "mla_prolog_packed_weights_bytes",
            "mla_prolog_pack_weights", "mla_prolog_create",
            "mla_prolog_run", "mla_prolog_destroy", "mla_prolog_profile_enable",
-           "mla_prolog_profile_read", "mla_prolog_status_string")
+           "mla_prolog_profile_read", "mla_prolog_check", "mla_prolog_status_string")
 #: kernel order of mla_prolog_profile_read
 KERNELS = ("down_proj", "norm_rope_cache", "up_proj", "uk")
 
@@ -107,6 +107,8 @@ def lib() -> ctypes.CDLL:
         L.mla_prolog_profile_read.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_double),
                                               ctypes.POINTER(ctypes.c_int64)]
         L.mla_prolog_profile_read.restype = ctypes.c_int
+        L.mla_prolog_check.argtypes = [ctypes.c_void_p]
+        L.mla_prolog_check.restype = ctypes.c_int
         L.mla_prolog_status_string.argtypes = [ctypes.c_int]
         L.mla_prolog_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -205,10 +207,22 @@ class MlaProlog:
             raise MlaError(st, "mla_prolog_profile_read")
         return dict(zip(KERNELS, list(ms))), int(n.value)
 
+    def check(self) -> None:
+        """Wait for the device and raise if an earlier run of this handle gave
+        up waiting for another block of its launch (its outputs are then not
+        to be trusted)."""
+        st = lib().mla_prolog_check(self._h)
+        if st != MLA_OK:
+            raise MlaError(st, "mla_prolog_check")
+
     def close(self) -> None:
+        """check(), then free the handle."""
         if self._h:
+            chk = lib().mla_prolog_check(self._h)
             st = lib().mla_prolog_destroy(self._h)
             self._h = None
+            if chk != MLA_OK:
+                raise MlaError(chk, "mla_prolog_check")
             if st != MLA_OK:
                 raise MlaError(st, "mla_prolog_destroy")
 

@@ -249,6 +249,10 @@ struct Ptrs {
   uint8_t* xq;       // [N] q^C exchange of the paired small-T kernel, kPairXq bytes a head
   uint32_t* xflag;   // [N][4] its exchange flags, then one error word; zero between runs
   float* xmax;       // [N][2][32] its per-token row maxima
+  uint32_t* fpart;   // fused kernel: [phase-1 blocks][32][64] (fp32 split partial, run tag) words
+  uint32_t* fss;     // fused kernel: [windows][32] (fp32 sum of squares, run tag) words
+  float* fykr;       // fused kernel: [32][Hckv + Dr] y of the c^KV and k^R columns
+  uint32_t* fcnt;    // fused kernel: [2N] flags, 64 bytes apart, then an error word
   const uint8_t* packed;  // weights in the packed layout, or NULL
 };
 
@@ -1629,6 +1633,549 @@ __global__ __launch_bounds__(512) void k34_pair(Dims d, Ptrs p, PackGeo pg) {
 }
 
 // ---------------------------------------------------------------------------
+// Fused small-T kernel: the whole prolog (bf16) in one launch of 2N blocks,
+// two per head, 512 threads, all resident on the device at once (the host
+// checks the occupancy before it picks this kernel).
+//
+// Phase 1.  Blocks 0 .. P1-1 each take a split of the He k-stages of one
+// 64-column window of [W^DQ | W^DkvKr] (at most eight splits a window, the
+// blocks spread over the windows).  Every wave streams its stages straight
+// into MFMA, the waves are summed in LDS, and wave 0 publishes the block's
+// [16 MT][64] fp32 partial.
+//
+// Window sum.  Each 8-byte word of a partial carries the run number next
+// to its value, so the split blocks of a window need no counter: each polls
+// the window's partials for its own rows until every word holds this run's
+// tag, then sums them in split order (the bits do not depend on which block
+// finishes first).  It publishes each row's sum of y^2 over the window (over
+// the c^KV columns in the c^KV / k^R windows), tagged the same way; the
+// c^KV / k^R blocks also publish y as fp32 rows.  A c^Q block then polls the
+// tagged window sums of its rows, adds them in a fixed order (the same bits
+// in every block) and writes c^Q = bf16(gamma_cq y / rms), fragment-packed
+// like c^Q on the packed path: the rounding point of the row-by-row
+// RmsNorm.  Every split block raises its own flag once its stores are
+// complete, and every block waits for all flags of the run.
+//
+// Phase 3 is the paired up-projection and W^UK product of k34_pair.  One
+// wave per block also writes one 64-column chunk of a c^KV row (and, for
+// chunk 0, the RoPE'd k^R row) to the token's cache slot.
+//
+// Data that crosses blocks moves through agent-scope atomic loads and stores
+// (coherent across the XCDs' L2 caches; aligned 8-byte words are
+// single-copy atomic), and a wave waits for its stores before it raises a
+// flag; no cache writeback or invalidation is needed.  Tags and flags hold
+// the run number the host passes (1, 2, ...), so nothing is reset between
+// runs.  Polling the data itself instead of counting arrivals keeps atomics
+// off the critical path: many same-address atomics arriving together
+// serialise.  Every wait is bounded and marks the error word when it gives
+// up.
+//
+// The memory counter of a wave completes in order, so a wave that waits on
+// another block must not have loads of its own in flight: wave 0 does all the
+// waiting and takes no phase-3 k-stages, while waves 1..7 share the Hcq
+// stages and issue their phase-3 weight loads (W^UK and the first kFusedPF
+// k-stages) once their phase-1 loads are in, holding them in registers
+// through the wait.  All waves run the same load instructions (wave 0's
+// fall outside the buffer, cost no memory access and return at once),
+// because the compiler counts outstanding loads along the code, not per
+// wave: a load issued only by some waves would make the others wait for it.
+// ---------------------------------------------------------------------------
+constexpr int kFusedP1 = 4;       // phase-1 k-stages a wave may have
+constexpr int kFusedPF = 4;       // phase-3 register ring: k-stages a wave has in flight
+constexpr int kFusedPE = 2;       // of those, the ones issued before the wait
+constexpr int kFusedStages = 7;   // phase-3 k-stages a wave may have (waves 1..7)
+constexpr int kFusedMaxSplits = 8;
+constexpr int kFusedFlagStride = 16;   // uint32 words between the fused kernel's flags
+constexpr int kFusedSpin = 1 << 20;
+
+struct FusedGeo {
+  int nwin;            // windows of [W^DQ | W^DkvKr]
+  int hi_win, hi_s;    // windows below hi_win take hi_s splits, the others hi_s - 1
+  int p1;              // blocks with phase-1 work (the sum of the splits)
+  uint32_t run;        // this run's number (1, 2, ...; never 0, modulo 2^32)
+};
+
+__device__ __forceinline__ void xstore32(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void xstored(double* p, double v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double xloadd(const double* p) {
+  return __builtin_bit_cast(double, __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ float xloadf(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// a 16-byte buffer load coherent at agent scope (the sc1 cache policy of an
+// agent-scope atomic load)
+__device__ __forceinline__ uint4 bload16c(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16));
+}
+__device__ __forceinline__ float bload4c(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 16));
+}
+__device__ __forceinline__ double bload8c(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 16));
+}
+__device__ __forceinline__ uint2 bload8u(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 16));
+}
+// one step of a bounded wave-wide poll: true once every lane's `ok` holds;
+// after kFusedSpin steps it marks the error word and gives up
+__device__ __forceinline__ bool fused_poll_done(bool ok, int& n, uint32_t* err) {
+  if (__builtin_amdgcn_ballot_w64(!ok) == 0) return true;
+  if (++n > kFusedSpin) {
+    if ((threadIdx.x & 63) == 0) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+  }
+  __builtin_amdgcn_s_sleep(2);
+  return false;
+}
+
+template <int MT>
+__global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, FusedGeo fg) {
+  using Acc = f32x4;
+  constexpr int NW = 8, NT = 6 * MT, R = 16 * MT;
+  __shared__ __attribute__((aligned(16))) uint4 red[NW * NT * 64];
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int b = blockIdx.x, G = gridDim.x;
+  const rsrc_t Wp = make_rsrc(p.packed, pg.total);
+  // flags of the split blocks, one per 64-byte line, then the error word
+  uint32_t* const flag = p.fcnt;
+  uint32_t* const err = p.fcnt + G * kFusedFlagStride;
+
+  // ---- the block's head and half in phase 3 (as in k34_pair)
+  const int h = d.N % 8 == 0 ? (b / 16) * 8 + b % 8 : b / 2;
+  const int half = d.N % 8 == 0 ? (b / 8) % 2 : b % 2;
+  const int P = pg.nope_w, DDr = d.D + d.Dr;
+  const int ja = (pg.uk_w + 1) / 2, jlo = half ? ja : 0, jhi = half ? pg.uk_w : ja;
+  const int jw = jlo + w / 2, ctu = 2 * (w % 2);
+  const bool ukact = jw < jhi;
+  const uint32_t ukb = uint32_t(pg.off_uk + int64_t(h * pg.uk_w + (ukact ? jw : 0)) * pg.nst_d * 4096);
+  const uint32_t nb = uint32_t(pg.off_uq + int64_t(h * (P + 1) + half) * pg.nst_cq * 4096);
+  const uint32_t rb = uint32_t(pg.off_uq + int64_t(h * (P + 1) + P) * pg.nst_cq * 4096);
+  // phase-3 k-stages: wave w >= 1 takes stages w - 1, w + 6, ...
+  const int ns3 = w >= 1 && w - 1 < pg.nst_cq ? (pg.nst_cq - (w - 1) + NW - 2) / (NW - 1) : 0;
+  uint4 bu[4][2];
+  uint4 pre[kFusedPF][6];
+  auto issue_uk = [&](bool ok) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        bu[s][k] = bload16(Wp, ok && ukact && s < pg.nst_d
+                                   ? ukb + uint32_t(s * 4096 + (ctu + k) * 1024 + lane * 16)
+                                   : kOOB);
+  };
+  // weights of the wave's q-th phase-3 k-stage: the four column tiles of
+  // nope window `half`, rope column tiles half and half + 2
+  auto issue_w3 = [&](uint4 (&r)[6], int q) {
+    const int st = w - 1 + q * (NW - 1);
+    const bool ok = q < ns3;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+      r[ct] = bload16(Wp, ok ? nb + uint32_t(st) * 4096u + uint32_t(ct * 1024 + lane * 16) : kOOB);
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      r[4 + k] = bload16(Wp, ok ? rb + uint32_t(st) * 4096u + uint32_t((half + 2 * k) * 1024 + lane * 16) : kOOB);
+  };
+
+  // ---- phase 1: block -> split s of S of window j
+  int j = 0, s = 0, S = 0, jfirst = 0;
+  if (b < fg.p1) {
+    const int nhi = fg.hi_win * fg.hi_s;
+    if (b < nhi) {
+      j = b / fg.hi_s; s = b % fg.hi_s; S = fg.hi_s; jfirst = j * fg.hi_s;
+    } else {
+      S = fg.hi_s - 1;
+      j = fg.hi_win + (b - nhi) / S; s = (b - nhi) % S; jfirst = nhi + (j - fg.hi_win) * S;
+    }
+  }
+  const int st0 = S ? s * pg.nst_he / S : 0, st1 = S ? (s + 1) * pg.nst_he / S : 0;
+  const int ns1 = st0 + w < st1 ? (st1 - st0 - w + NW - 1) / NW : 0;
+  const uint32_t w1b = uint32_t(j < pg.win_dq ? pg.off_dq + int64_t(j) * pg.nst_he * 4096
+                                              : pg.off_kr + int64_t(j - pg.win_dq) * pg.nst_he * 4096);
+  const APlain<false, MT> ax{make_rsrc(p.x, int64_t(d.T) * d.He * 2), uint32_t(d.He * 2), d.T, d.He};
+  uint4 b1[kFusedP1][4], a1[kFusedP1][MT];
+#pragma unroll
+  for (int q = 0; q < kFusedP1; ++q) {
+    const int st = st0 + w + q * NW;
+    const bool ok = q < ns1;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+      b1[q][ct] = bload16(Wp, ok ? w1b + uint32_t(st) * 4096u + uint32_t(ct * 1024 + lane * 16) : kOOB);
+    ax.load(a1[q], st, ok);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  Acc acc1[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) acc1[mt][ct] = Acc{0, 0, 0, 0};
+#pragma unroll
+  for (int q = 0; q < kFusedP1; ++q)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const bf16x8 af = __builtin_bit_cast(bf16x8, a1[q][mt]);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) acc1[mt][ct] = mfma(af, __builtin_bit_cast(bf16x8, b1[q][ct]), acc1[mt][ct]);
+    }
+  reduce_waves<NW, MT>(acc1, reinterpret_cast<uint32_t*>(red));
+
+  // wave 0 of a split block publishes the block's partial before any
+  // prefetch is issued (its memory pipeline is then free of other loads).
+  // Its rows of the window are summed below: lane -> row 2 pass + lane / 32,
+  // columns 2 (lane % 32) and + 1.
+  const int r0 = S ? s * R / S : 0, r1 = S ? (s + 1) * R / S : 0, q2 = lane & 31;
+  const bool qwin = j < pg.win_dq;
+  const int col0 = (qwin ? 64 * j : 64 * (j - pg.win_dq)) + 2 * q2;   // column in W^DQ or W^DkvKr
+  const uint32_t run = fg.run;
+  uint32_t gq = 0;
+  if (w == 0 && S) {
+    gq = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(p.gamma_cq, int64_t(d.Hcq) * 2),
+                                              qwin && col0 < d.Hcq ? col0 * 2u : kOOB, 0, 0);
+    // the block's partial, rows 16 mt + 4 g + i, columns 16 ct + c, each
+    // value next to this run's tag
+    uint32_t* mine = p.fpart + int64_t(b) * R * 64 * 2;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = acc1[mt][ct][i];
+          xstore64(mine + ((16 * mt + 4 * g + i) * 64 + 16 * ct + c) * 2, make_uint2(__float_as_uint(v), run));
+        }
+  }
+  // the phase-3 prefetch goes out once phase 1's loads are in (so that it
+  // does not delay them) and wave 0's stores are issued (the waves share the
+  // CU's memory pipeline); the barrier orders LDS only
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  issue_uk(w != 0);
+#pragma unroll
+  for (int q = 0; q < kFusedPE; ++q) issue_w3(pre[q], q);
+  __builtin_amdgcn_sched_barrier(0);
+
+  if (w == 0) {
+    if (S) {
+      float* ylds = reinterpret_cast<float*>(red);   // [R][64] y of the c^Q window rows
+      const rsrc_t Fp = make_rsrc(p.fpart, int64_t(fg.p1) * R * 64 * 8);
+      for (int rb = r0; rb < r1; rb += 2) {
+        const int r = rb + (lane >> 5);
+        const bool act = r < r1;
+        // S <= kFusedMaxSplits; the words past S are not waited for
+        uint2 v[kFusedMaxSplits][2];
+        int n = 0;
+        for (;;) {
+#pragma unroll
+          for (int k = 0; k < kFusedMaxSplits; ++k)
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+              v[k][e] = bload8u(Fp, act && k < S ? uint32_t(((jfirst + k) * R + r) * 64 + 2 * q2 + e) * 8u : kOOB);
+          bool ok = true;
+#pragma unroll
+          for (int k = 0; k < kFusedMaxSplits; ++k)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) ok &= !(act && k < S) || v[k][e].y == run;
+          if (fused_poll_done(ok, n, err)) break;
+        }
+        float y[2] = {0, 0};
+#pragma unroll
+        for (int k = 0; k < kFusedMaxSplits; ++k)
+#pragma unroll
+          for (int e = 0; e < 2; ++e) y[e] += __uint_as_float(v[k][e].x);   // words past S read zeros
+        // the row's sum of squares over the window (c^KV columns only in the
+        // c^KV / k^R windows), tagged
+        double ss = 0.0;
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          if (qwin || col0 + e < d.Hckv) ss += double(y[e]) * double(y[e]);
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) ss += __shfl_xor(ss, o, 64);
+        if (act && q2 == 0) xstore64(p.fss + (j * 32 + r) * 2, make_uint2(__float_as_uint(float(ss)), run));
+        if (!act) continue;
+        if (qwin) {
+          ylds[r * 64 + 2 * q2] = y[0];
+          ylds[r * 64 + 2 * q2 + 1] = y[1];
+        } else if (col0 < d.Hckv + d.Dr) {
+          // Hckv + Dr is even: the lane's 2 columns are both in the row
+          xstore64(p.fykr + r * (d.Hckv + d.Dr) + col0, make_uint2(__float_as_uint(y[0]), __float_as_uint(y[1])));
+        }
+      }
+      if (qwin) {
+        // c^Q = bf16(gamma y / rms) once every window sum of the rows is out
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const rsrc_t Sp = make_rsrc(p.fss, int64_t(pg.win_dq) * 32 * 8);
+        for (int rb = r0; rb < r1; rb += 2) {
+          const int r = rb + (lane >> 5);
+          const bool act = r < r1;
+          // lane q2 adds windows q2, q2 + 32, ..., then the row's 32 lanes are
+          // added: a fixed order, the same in every block
+          double ss = 0.0;
+          for (int j0 = q2; j0 < pg.win_dq; j0 += 128) {
+            uint2 v[4];
+            int n = 0;
+            for (;;) {
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                const int jj = j0 + 32 * k;
+                v[k] = bload8u(Sp, act && jj < pg.win_dq ? uint32_t(jj * 32 + r) * 8u : kOOB);
+              }
+              bool ok = true;
+#pragma unroll
+              for (int k = 0; k < 4; ++k) ok &= !(act && j0 + 32 * k < pg.win_dq) || v[k].y == run;
+              if (fused_poll_done(ok, n, err)) break;
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) ss += double(__uint_as_float(v[k].x));   // zeros past win_dq
+          }
+#pragma unroll
+          for (int o = 1; o < 32; o <<= 1) ss += __shfl_xor(ss, o, 64);
+          const int stg = col0 / 32;
+          if (act && stg < pg.nst_cq) {
+            const double rms = sqrt(ss / double(d.Hcq) + d.eps_cq);
+            const float c0 = float(double(bf2f(uint16_t(gq))) * double(ylds[r * 64 + 2 * q2]) / rms);
+            const float c1 = float(double(bf2f(uint16_t(gq >> 16))) * double(ylds[r * 64 + 2 * q2 + 1]) / rms);
+            uint32_t* dst = reinterpret_cast<uint32_t*>(p.cq + int64_t(r >> 4) * pg.nst_cq * 1024 + stg * 1024 +
+                                                        ((((col0 % 32) / 8) * 16 + (r & 15)) * 16) + (col0 % 8) * 2);
+            __hip_atomic_store(dst, uint32_t(f2bf(c0)) | (uint32_t(f2bf(c1)) << 16), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+      }
+      // the block's outputs are complete: raise its flag
+      __builtin_amdgcn_s_waitcnt(0);
+      if (lane == 0) __hip_atomic_store(flag + b * kFusedFlagStride, run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // wait for the flags of every split block of this run
+    int n = 0;
+    for (;;) {
+      bool ok = true;
+      for (int i0 = 0; i0 < fg.p1; i0 += 256) {
+        uint32_t v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int i = i0 + lane + 64 * k;
+          v[k] = i < fg.p1 ? __hip_atomic_load(flag + i * kFusedFlagStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                           : run;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) ok &= v[k] == run;
+      }
+      if (fused_poll_done(ok, n, err)) break;
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 3 (wave 0's W^UK fragments are only read at the very end)
+  if (w == 0) issue_uk(true);
+  // cache jobs: job jb = (token jb / cj, 64-column chunk jb % cj of c^KV;
+  // chunk 0 also writes k^R).  Wave 7 takes jobs b, b + G, ...; the loads of
+  // the first are issued now and used after the stream.
+  const int cj = (d.Hckv + 63) / 64, W2 = d.Hckv + d.Dr;
+  // the loads are predicated buffer loads (no branches), so that their
+  // waits come only where the values are used
+  struct CacheJob {
+    int t, ch;
+    float y, a, b2;
+    uint32_t gam;
+    double ss;
+    int64_t slot;
+  };
+  const rsrc_t Yp = make_rsrc(p.fykr, int64_t(d.T) * W2 * 4);
+  const rsrc_t Sk = make_rsrc(p.fss, int64_t(pg.win_dq + pg.win_kr) * 32 * 8);
+  const rsrc_t Gk = make_rsrc(p.gamma_ckv, int64_t(d.Hckv) * 2);
+  auto job_load = [&](int jb) {
+    CacheJob cjb;
+    cjb.t = jb / cj; cjb.ch = jb % cj;
+    const int col = 64 * cjb.ch + lane;
+    const bool kv = col < d.Hckv, kr = cjb.ch == 0 && lane < d.Dr / 2;
+    cjb.y = bload4c(Yp, kv ? uint32_t(cjb.t * W2 + col) * 4u : kOOB);
+    cjb.gam = __builtin_amdgcn_raw_buffer_load_b16(Gk, kv ? uint32_t(col) * 2u : kOOB, 0, 0);
+    cjb.a = bload4c(Yp, kr ? uint32_t(cjb.t * W2 + d.Hckv + lane) * 4u : kOOB);
+    cjb.b2 = bload4c(Yp, kr ? uint32_t(cjb.t * W2 + d.Hckv + lane + d.Dr / 2) * 4u : kOOB);
+    cjb.ss = double(__uint_as_float(
+        bload8u(Sk, lane < pg.win_kr ? uint32_t((pg.win_dq + lane) * 32 + cjb.t) * 8u : kOOB).x));   // (float, tag)
+    cjb.slot = p.cache_index[cjb.t];
+    return cjb;
+  };
+  // c^KV = gamma y / rms, k^R = RoPE(y_kr), bf16, at the token's slot
+  auto job_store = [&](const CacheJob& cjb) {
+    double ssk = cjb.ss;
+    for (int o = 32; o > 0; o >>= 1) ssk += __shfl_xor(ssk, o, 64);
+    if (cjb.slot < 0 || cjb.slot >= d.slots) return;
+    const double rms = sqrt(ssk / double(d.Hckv) + d.eps_ckv);
+    const int col = 64 * cjb.ch + lane;
+    if (col < d.Hckv)
+      p.kv_cache[cjb.slot * d.Hckv + col] = f2bf(float(double(bf2f(uint16_t(cjb.gam))) * double(cjb.y) / rms));
+    if (cjb.ch == 0 && lane < d.Dr / 2) {
+      const int hf = d.Dr / 2;
+      const uint16_t* cs = p.cos + int64_t(cjb.t) * d.Dr;
+      const uint16_t* sn = p.sin + int64_t(cjb.t) * d.Dr;
+      uint16_t* kr = p.kr_cache + cjb.slot * d.Dr;
+      kr[lane] = f2bf(float(double(cjb.a) * bf2f(cs[lane]) - double(cjb.b2) * bf2f(sn[lane])));
+      kr[lane + hf] = f2bf(float(double(cjb.b2) * bf2f(cs[lane + hf]) + double(cjb.a) * bf2f(sn[lane + hf])));
+    }
+  };
+  const bool cjob = w == NW - 1 && b < d.T * cj;
+  CacheJob job0{};
+  if (cjob) job0 = job_load(b);
+
+  const int64_t ctile = int64_t(pg.nst_cq) * 1024;
+  const rsrc_t Cq = make_rsrc(p.cq, int64_t((d.T + 15) / 16) * ctile);
+  uint4 aq[kFusedPF][MT];
+  auto issue_a = [&](uint4 (&r)[MT], int q) {
+    const int st = w - 1 + q * (NW - 1);
+    const bool ok = q < ns3;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      r[mt] = bload16c(Cq, ok ? uint32_t(mt * ctile + st * 1024 + lane * 16) : kOOB);
+  };
+  // the ring's stages that were not prefetched, then the activation operand
+#pragma unroll
+  for (int q = kFusedPE; q < kFusedPF; ++q) issue_w3(pre[q], q);
+#pragma unroll
+  for (int q = 0; q < kFusedPF; ++q) issue_a(aq[q], q);
+  __builtin_amdgcn_sched_barrier(0);
+  Acc an[MT][4], ar[MT][2];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) an[mt][ct] = Acc{0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < 2; ++k) ar[mt][k] = Acc{0, 0, 0, 0};
+  }
+  auto consume = [&](const uint4 (&wq)[6], const uint4 (&a)[MT]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const bf16x8 af = __builtin_bit_cast(bf16x8, a[mt]);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) an[mt][ct] = mfma(__builtin_bit_cast(bf16x8, wq[ct]), af, an[mt][ct]);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) ar[mt][k] = mfma(__builtin_bit_cast(bf16x8, wq[4 + k]), af, ar[mt][k]);
+    }
+  };
+  // a register ring of kFusedPF stages: stage q + kFusedPF refills the slot
+  // of stage q once that is consumed
+#pragma unroll
+  for (int q = 0; q < kFusedStages; ++q) {
+    consume(pre[q % kFusedPF], aq[q % kFusedPF]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (q + kFusedPF < kFusedStages) {
+      issue_w3(pre[q % kFusedPF], q + kFusedPF);
+      issue_a(aq[q % kFusedPF], q + kFusedPF);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // every wave parks its tiles; tile q is summed in wave order by its owner
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) red[(w * NT + mt * 4 + ct) * 64 + lane] = __builtin_bit_cast(uint4, an[mt][ct]);
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      red[(w * NT + 4 * MT + mt * 2 + k) * 64 + lane] = __builtin_bit_cast(uint4, ar[mt][k]);
+  }
+  __syncthreads();
+  auto sum_tile = [&](int q) {
+    Acc sm = __builtin_bit_cast(Acc, red[q * 64 + lane]);
+#pragma unroll
+    for (int w2 = 1; w2 < NW; ++w2) sm += __builtin_bit_cast(Acc, red[(w2 * NT + q) * 64 + lane]);
+    return sm;
+  };
+  uint8_t* xq = p.xq + int64_t(h) * kPairXq;
+
+  // q^C tile (mt, ct) of this half -> bf16 -> exchange buffer, in the
+  // fragment order of the W^UK product's activation operand
+  if (w < 4 * MT) {
+    const int mt = w / 4, ct = w % 4;
+    const Acc sm = sum_tile(w);
+    const int st = 2 * half + ct / 2;
+    if (st < pg.nst_d)
+      xstore64(xq + (mt * 4 + st) * 1024 + (16 * (2 * (ct % 2) + g / 2) + c) * 16 + 8 * (g % 2),
+               pack_bf16x4(sm[0], sm[1], sm[2], sm[3]));
+  }
+  pair_publish(p.xflag + 4 * h + half);
+
+  // the cache rows and q^R leave after the exchange is published (its wait
+  // for the exchange stores then does not wait for these)
+  if (cjob) {
+    job_store(job0);
+    for (int jb = b + G; jb < d.T * cj; jb += G) job_store(job_load(jb));
+  }
+
+  // q^R: the owner of token tile mt holds both tiles of every RoPE pair
+  if (w >= NW - MT) {
+    const int mt = NW - 1 - w, t = 16 * mt + c;
+    const Acc a0 = sum_tile(4 * MT + 2 * mt), a1v = sum_tile(4 * MT + 2 * mt + 1);
+    if (t < d.T) {
+      const int i0 = 16 * half + 4 * g, hf = d.Dr / 2;
+      const uint2 c0 = *reinterpret_cast<const uint2*>(p.cos + int64_t(t) * d.Dr + i0);
+      const uint2 c1 = *reinterpret_cast<const uint2*>(p.cos + int64_t(t) * d.Dr + i0 + hf);
+      const uint2 s0 = *reinterpret_cast<const uint2*>(p.sin + int64_t(t) * d.Dr + i0);
+      const uint2 s1 = *reinterpret_cast<const uint2*>(p.sin + int64_t(t) * d.Dr + i0 + hf);
+      const uint16_t* cs0 = reinterpret_cast<const uint16_t*>(&c0);
+      const uint16_t* cs1 = reinterpret_cast<const uint16_t*>(&c1);
+      const uint16_t* sn0 = reinterpret_cast<const uint16_t*>(&s0);
+      const uint16_t* sn1 = reinterpret_cast<const uint16_t*>(&s1);
+      float o0[4], o1[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float a = a0[r], bb = a1v[r];
+        o0[r] = a * bf2f(cs0[r]) - bb * bf2f(sn0[r]);
+        o1[r] = bb * bf2f(cs1[r]) + a * bf2f(sn1[r]);
+      }
+      uint16_t* o = p.qr_out + (int64_t(t) * d.N + h) * d.Dr + i0;
+      *reinterpret_cast<uint2*>(o) = pack_bf16x4(o0[0], o0[1], o0[2], o0[3]);
+      *reinterpret_cast<uint2*>(o + hf) = pack_bf16x4(o1[0], o1[1], o1[2], o1[3]);
+    }
+  }
+
+  // q^N = q^C W^UK[h] over this half's columns, all of D
+  pair_wait(p.xflag + 4 * h + (1 - half), p.xflag + 4 * d.N);
+  uint4 aqc[4][MT];
+#pragma unroll
+  for (int st = 0; st < 4; ++st)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      aqc[st][mt] = st < pg.nst_d ? xload128(xq + (mt * 4 + st) * 1024 + lane * 16) : make_uint4(0, 0, 0, 0);
+  f32x4 au[MT][2];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      au[mt][k] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        au[mt][k] = mfma(__builtin_bit_cast(bf16x8, bu[st][k]), __builtin_bit_cast(bf16x8, aqc[st][mt]), au[mt][k]);
+    }
+  if (!ukact) return;
+  const int qcol0 = 64 * jw + 16 * ctu + 4 * g;   // q^N column of element 0 of tile k = 0
+  uint16_t* qo = static_cast<uint16_t*>(p.q_out);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int t = 16 * mt + c;
+    if (t >= d.T) continue;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int col = qcol0 + 16 * k;
+      if (col < d.Hckv)
+        *reinterpret_cast<uint2*>(qo + (int64_t(t) * d.N + h) * d.Hckv + col) =
+            pack_bf16x4(au[mt][k][0], au[mt][k][1], au[mt][k][2], au[mt][k][3]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Tiled path for larger token counts.  Every wave owns a 16*MT-token x
 // 64*NWW-column output tile and streams the packed k-stages of its NWW
 // windows against MT activation fragments per stage; 16-byte loads land in
@@ -2284,7 +2831,7 @@ TiledPlan tiled_plan(const mla_prolog_desc& d, int64_t T) {
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t part, cq, cq_scale, qc, xq, xflag, xmax, total;
+  size_t part, cq, cq_scale, qc, xq, xflag, xmax, fpart, fss, fykr, fcnt, total;
 };
 
 Layout layout(const mla_prolog_desc& d) {
@@ -2311,7 +2858,14 @@ Layout layout(const mla_prolog_desc& d) {
   L.xq = align256(L.qc + qc_bytes);
   L.xflag = align256(L.xq + size_t(d.N) * kPairXq);
   L.xmax = align256(L.xflag + size_t(4 * d.N + 1) * 4);
-  L.total = align256(L.xmax + size_t(d.N) * 64 * 4);
+  // the fused small-T kernel: 2N blocks' partials, per-window sums of
+  // squares, the c^KV / k^R rows, counters
+  const size_t nwin = size_t(g.win_dq + g.win_kr);
+  L.fpart = align256(L.xmax + size_t(d.N) * 64 * 4);
+  L.fss = align256(L.fpart + size_t(2 * d.N) * 32 * 64 * 8);
+  L.fykr = align256(L.fss + nwin * 32 * 8);
+  L.fcnt = align256(L.fykr + size_t(32) * (d.Hckv + d.Dr) * 4);
+  L.total = align256(L.fcnt + (size_t(2 * d.N) * kFusedFlagStride + 1) * 4);
   return L;
 }
 
@@ -2391,8 +2945,10 @@ struct mla_prolog {
   Layout lay;
   uint8_t* ws;
   hipEvent_t* events;  // kProfileRing x kProfileEvents when profiling, else NULL
-  bool* fused;         // per recorded run: up_proj and uk ran as one kernel
+  uint8_t* fused;      // per recorded run: 0 four kernels, 1 up_proj and uk as one, 2 one kernel
   int64_t recorded;    // runs recorded since the last read
+  bool fused_fit[2];   // the fused kernel (16 or 32 tokens) has all 2N blocks resident at once
+  uint32_t fused_run;  // fused runs launched so far
 };
 
 namespace {
@@ -2470,6 +3026,31 @@ void packed_launch(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p, 
   if (q8) k4_packed_q8<MT, 4><<<dim3(d.N), 512, 0, s>>>(d, p, g);
   else k4_packed<MT, 4, 1><<<dim3(d.N * g.uk_w), 256, 0, s>>>(d, p, g);
   mark(4);
+}
+
+// The fused small-T kernel (bf16, two nope windows, Dr = 64): the split of
+// the phase-1 windows over the 2N blocks, or false when the shapes are
+// outside what the kernel holds in registers.
+bool fused_geo(const mla_prolog_desc& dd, FusedGeo* fg) {
+  if (dd.in_dtype != MLA_BF16 || dd.query_dtype != MLA_BF16) return false;
+  const PackGeo g = pack_geo(dd.He, dd.Hcq, dd.Hckv, dd.N, dd.D, dd.Dr, false);
+  if (g.nope_w != 2 || dd.Dr != 64 || g.uk_w > 8 || g.nst_d > 4) return false;
+  const int G = int(2 * dd.N), W = g.win_dq + g.win_kr;
+  if (G < W || (g.nst_cq + 6) / 7 > kFusedStages) return false;
+  const int base = G / W;
+  if (base >= kFusedMaxSplits) {
+    fg->hi_win = W; fg->hi_s = kFusedMaxSplits;
+  } else if (G % W == 0) {
+    fg->hi_win = W; fg->hi_s = base;
+  } else {
+    fg->hi_win = G % W; fg->hi_s = base + 1;
+  }
+  fg->nwin = W;
+  fg->p1 = fg->hi_win * fg->hi_s + (W - fg->hi_win) * (fg->hi_s - 1);
+  const int smin = fg->hi_win < W ? fg->hi_s - 1 : fg->hi_s;
+  if ((ceil_div(g.nst_he, smin) + 7) / 8 > kFusedP1) return false;
+  fg->run = 0;
+  return true;
 }
 
 template <class Mark>
@@ -2616,12 +3197,34 @@ mla_status mla_prolog_create(const mla_prolog_desc* desc, mla_prolog_t* out) {
     (void)hipSetDevice(prev);
     return MLA_ERR_RUNTIME;
   }
-  // the exchange flags start at zero; every run leaves them at zero
-  if (hipMemset(h->ws + h->lay.xflag, 0, size_t(4 * desc->N + 1) * 4) != hipSuccess) {
+  // the exchange flags start at zero and every run leaves them at zero; the
+  // fused kernel's tags and flags start at zero (no run is numbered 0)
+  if (hipMemset(h->ws + h->lay.xflag, 0, size_t(4 * desc->N + 1) * 4) != hipSuccess ||
+      hipMemset(h->ws + h->lay.fpart, 0, h->lay.total - h->lay.fpart) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess) {
     (void)hipFree(h->ws);
     delete h;
     (void)hipSetDevice(prev);
     return MLA_ERR_RUNTIME;
+  }
+  // the fused kernel's blocks wait for one another, so all 2N of them must
+  // be resident at once; MLA_PROLOG_FUSED=0 in the environment turns it off
+  h->fused_run = 0;
+  h->fused_fit[0] = h->fused_fit[1] = false;
+  {
+    FusedGeo fg;
+    const char* env = std::getenv("MLA_PROLOG_FUSED");
+    int cus = 0, nb1 = 0, nb2 = 0;
+    if (!(env && env[0] == '0') && fused_geo(*desc, &fg) &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, desc->device) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb1, reinterpret_cast<const void*>(k_fused<1>), 512, 0) ==
+            hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb2, reinterpret_cast<const void*>(k_fused<2>), 512, 0) ==
+            hipSuccess) {
+      h->fused_fit[0] = int64_t(nb1) * cus >= 2 * desc->N;
+      h->fused_fit[1] = int64_t(nb2) * cus >= 2 * desc->N;
+    }
+    (void)hipGetLastError();
   }
 
   (void)hipSetDevice(prev);
@@ -2673,25 +3276,42 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   p.xq = h->ws + h->lay.xq;
   p.xflag = reinterpret_cast<uint32_t*>(h->ws + h->lay.xflag);
   p.xmax = reinterpret_cast<float*>(h->ws + h->lay.xmax);
+  p.fpart = reinterpret_cast<uint32_t*>(h->ws + h->lay.fpart);
+  p.fss = reinterpret_cast<uint32_t*>(h->ws + h->lay.fss);
+  p.fykr = reinterpret_cast<float*>(h->ws + h->lay.fykr);
+  p.fcnt = reinterpret_cast<uint32_t*>(h->ws + h->lay.fcnt);
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   hipEvent_t* ev = nullptr;
-  bool* fused = nullptr;
+  uint8_t* fused = nullptr;
   if (h->events) {
     ev = h->events + (h->recorded % kProfileRing) * kProfileEvents;
     fused = h->fused + (h->recorded % kProfileRing);
-    *fused = false;
+    *fused = 0;
     ++h->recorded;
   }
   // mark(i): event i (after kernel i); mark(-1): the last event of a run
-  // whose up_proj and uk were one kernel
+  // whose up_proj and uk were one kernel; mark(-2): the last event of a run
+  // that was one kernel
   auto mark = [&](int i) {
     if (!ev) return;
-    if (i < 0) *fused = true;
+    if (i < 0) *fused = uint8_t(-i);
     (void)hipEventRecord(ev[i < 0 ? kProfileEvents - 1 : i], s);
   };
   mark(0);
   p.packed = static_cast<const uint8_t*>(t->packed_weights);
+  FusedGeo fg;
+  if (p.packed && pl.stream && h->fused_fit[pl.mt1 == 1 ? 0 : 1] && fused_geo(dd, &fg)) {
+    fg.run = ++h->fused_run;
+    const PackGeo g = pack_geo(dd.He, dd.Hcq, dd.Hckv, dd.N, dd.D, dd.Dr, false);
+    if (pl.mt1 == 1) k_fused<1><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g, fg);
+    else k_fused<2><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g, fg);
+    mark(-2);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) --h->fused_run;
+    if (prev != dd.device) (void)hipSetDevice(prev);
+    return e == hipSuccess ? MLA_OK : MLA_ERR_RUNTIME;
+  }
   if (p.packed && (!pl.stream || packed_fits(dd))) {
     if (pl.stream) launch_packed(pl, s, d, p, dd, i8, q8, mark);
     else launch_tiled(s, d, p, dd, i8, q8, mark);
@@ -2747,7 +3367,7 @@ mla_status mla_prolog_profile_enable(mla_prolog_t h, int enable) {
   destroy_events(h);
   if (st == MLA_OK && enable) {
     h->events = new (std::nothrow) hipEvent_t[kProfileRing * kProfileEvents]();
-    h->fused = new (std::nothrow) bool[kProfileRing]();
+    h->fused = new (std::nothrow) uint8_t[kProfileRing]();
     if (!h->events || !h->fused) st = MLA_ERR_RUNTIME;
     for (int i = 0; st == MLA_OK && i < kProfileRing * kProfileEvents; ++i)
       if (hipEventCreate(&h->events[i]) != hipSuccess) st = MLA_ERR_RUNTIME;
@@ -2767,6 +3387,12 @@ mla_status mla_prolog_profile_read(mla_prolog_t h, double* kernel_ms, int64_t* r
   for (int64_t r = 0; r < n; ++r) {
     hipEvent_t* ev = h->events + r * kProfileEvents;
     if (hipEventSynchronize(ev[kProfileEvents - 1]) != hipSuccess) return MLA_ERR_RUNTIME;
+    if (h->fused[r] == 2) {   // one kernel, booked to up_proj
+      float ms = 0.0f;
+      if (hipEventElapsedTime(&ms, ev[0], ev[kProfileEvents - 1]) != hipSuccess) return MLA_ERR_RUNTIME;
+      kernel_ms[2] += ms;
+      continue;
+    }
     for (int k = 0; k < kProfileEvents - 1; ++k) {
       if (h->fused[r] && k == kProfileEvents - 2) continue;   // uk ran inside up_proj
       float ms = 0.0f;
@@ -2790,6 +3416,31 @@ mla_status mla_prolog_destroy(mla_prolog_t h) {
     (void)hipSetDevice(prev);
   }
   delete h;
+  return st;
+}
+
+mla_status mla_prolog_check(mla_prolog_t h) {
+  if (!h) return MLA_ERR_NULLPTR;
+  int prev = 0;
+  if (hipGetDevice(&prev) != hipSuccess || hipSetDevice(h->desc.device) != hipSuccess)
+    return MLA_ERR_RUNTIME;
+  // the paired kernel's error word follows its 4N exchange flags; the fused
+  // kernel's follows its window counters and done counter
+  const PackGeo g = pack_geo(h->desc.He, h->desc.Hcq, h->desc.Hckv, h->desc.N, h->desc.D, h->desc.Dr,
+                             h->desc.in_dtype == MLA_INT8);
+  uint32_t* words[2] = {reinterpret_cast<uint32_t*>(h->ws + h->lay.xflag) + 4 * h->desc.N,
+                        reinterpret_cast<uint32_t*>(h->ws + h->lay.fcnt) + 2 * h->desc.N * kFusedFlagStride};
+  mla_status st = hipDeviceSynchronize() == hipSuccess ? MLA_OK : MLA_ERR_RUNTIME;
+  for (uint32_t* wd : words) {
+    uint32_t v = 0;
+    if (st == MLA_OK && hipMemcpy(&v, wd, 4, hipMemcpyDeviceToHost) != hipSuccess) st = MLA_ERR_RUNTIME;
+    if (st == MLA_OK && v != 0) {
+      st = MLA_ERR_RUNTIME;
+      const uint32_t zero = 0;
+      (void)hipMemcpy(wd, &zero, 4, hipMemcpyHostToDevice);
+    }
+  }
+  (void)hipSetDevice(prev);
   return st;
 }
 

@@ -174,11 +174,22 @@ mla_status mla_prolog_run(mla_prolog_t handle, const mla_prolog_tensors* tensors
 /* Frees the workspace and the handle (after synchronising its device). */
 mla_status mla_prolog_destroy(mla_prolog_t handle);
 
+/* Waits for the handle's device and reports whether any earlier run gave up
+ * waiting for another block of its own launch (MLA_ERR_RUNTIME; then the
+ * outputs of those runs are not to be trusted), else MLA_OK; clears the
+ * record.  On the small-T kernels the blocks of one launch hand data to one
+ * another and wait, with a bounded spin, for it; that can only fail when
+ * the launch does not get the whole device (the library checks at create
+ * time that all of its blocks fit on the device at once). */
+mla_status mla_prolog_check(mla_prolog_t handle);
+
 /* Kernel timing with HIP events, for benchmarks.  After
  * mla_prolog_profile_enable(h, 1) every run of h records HIP events on its
  * stream before its first kernel and after each of its four kernels
  * (down_proj, norm_rope_cache, up_proj, uk; where one kernel does both
- * up_proj and uk, its time is booked to up_proj and uk reads 0).
+ * up_proj and uk, its time is booked to up_proj and uk reads 0; where one
+ * kernel does the whole run, its time is booked to up_proj and the other
+ * three read 0).
  * mla_prolog_profile_read waits
  * for the recorded events and returns, per kernel, the elapsed milliseconds
  * summed over the runs since the previous read (kernel_ms[4]) and the number

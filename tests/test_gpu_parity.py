@@ -272,6 +272,38 @@ def test_pair_bf16_packed(name):
     full_check(synth.make_inputs(PAIR[name]), packed=True, repeat=3, prerun_negated=True)
 
 
+@pytest.mark.parametrize("name", ["pair_t5_n4", "pair_t32_n8"])
+def test_pair_bf16_packed_unfused(name, monkeypatch):
+    # the bf16 cases above run on the one-kernel path; this keeps the paired
+    # kernel that serves when not all blocks of that launch fit on the device
+    monkeypatch.setenv("MLA_PROLOG_FUSED", "0")
+    full_check(synth.make_inputs(PAIR[name]), packed=True, repeat=2, prerun_negated=True)
+
+
+def test_fused_mixed_token_counts():
+    # one handle, runs of 32, 7, 16 and 32 tokens: the one-kernel path's
+    # counters only grow, and each run must wait for its own arrivals
+    wl = PAIR["pair_t32_n8"]
+    desc_inp = synth.make_inputs(wl)
+    desc = mla.make_desc(**dev.desc_args(desc_inp))
+    with mla.MlaProlog(desc) as h:
+        t0 = dev.upload(desc_inp)
+        buf = torch.empty(mla.packed_weights_bytes(desc), dtype=torch.uint8, device="cuda")
+        h.pack_weights(t0, buf)
+        for T in (32, 7, 16, 32):
+            inp = synth.make_inputs(wl, T=T)
+            say(f"case fused mixed T={T}")
+            t = dev.upload(inp)
+            t["packed_weights"] = buf
+            h.run(t, T)
+            torch.cuda.synchronize()
+            h.check()
+            got = {k: dev.bits(v) for k, v in t.items() if k != "packed_weights"}
+            ref = oracle.run(inp, caches=False)
+            check_queries(got, ref, np.arange(T), False)
+            check_caches(inp, got["kv_cache"], got["kr_cache"], ref, np.arange(T))
+
+
 @pytest.mark.parametrize("name", list(PAIR_INT8))
 def test_pair_int8_packed(name):
     inp = synth.make_inputs(PAIR_INT8[name])
