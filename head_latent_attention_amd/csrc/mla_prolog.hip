@@ -1673,12 +1673,12 @@ __global__ __launch_bounds__(512) void k34_pair(Dims d, Ptrs p, PackGeo pg) {
 // The memory counter of a wave completes in order, so a wave that waits on
 // another block must not have loads of its own in flight: wave 0 does all the
 // waiting and takes no phase-3 k-stages, while waves 1..7 share the Hcq
-// stages and issue their phase-3 weight loads (W^UK and the first kFusedPF
-// k-stages) once their phase-1 loads are in, holding them in registers
-// through the wait.  All waves run the same load instructions (wave 0's
-// fall outside the buffer, cost no memory access and return at once),
-// because the compiler counts outstanding loads along the code, not per
-// wave: a load issued only by some waves would make the others wait for it.
+// stages and issue their phase-3 weight loads (W^UK and the first kFusedPE
+// k-stages) once wave 0 has summed its window rows, holding them in
+// registers through the rest of the wait.  Wave 0 issues no load that spans
+// that point (the compiler merges outstanding-load counts where the waves'
+// paths join, so a load older than the prefetch would make wave 0 wait for
+// loads it never issued).
 // ---------------------------------------------------------------------------
 constexpr int kFusedP1 = 4;       // phase-1 k-stages a wave may have
 constexpr int kFusedPF = 4;       // phase-3 register ring: k-stages a wave has in flight
@@ -1762,6 +1762,10 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
   const int ns3 = w >= 1 && w - 1 < pg.nst_cq ? (pg.nst_cq - (w - 1) + NW - 2) / (NW - 1) : 0;
   uint4 bu[4][2];
   uint4 pre[kFusedPF][6];
+#pragma unroll
+  for (int q = 0; q < kFusedPF; ++q)
+#pragma unroll
+    for (int i = 0; i < 6; ++i) pre[q][i] = make_uint4(0, 0, 0, 0);
   auto issue_uk = [&](bool ok) {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -1834,10 +1838,7 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
   const bool qwin = j < pg.win_dq;
   const int col0 = (qwin ? 64 * j : 64 * (j - pg.win_dq)) + 2 * q2;   // column in W^DQ or W^DkvKr
   const uint32_t run = fg.run;
-  uint32_t gq = 0;
   if (w == 0 && S) {
-    gq = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(p.gamma_cq, int64_t(d.Hcq) * 2),
-                                              qwin && col0 < d.Hcq ? col0 * 2u : kOOB, 0, 0);
     // the block's partial, rows 16 mt + 4 g + i, columns 16 ct + c, each
     // value next to this run's tag
     uint32_t* mine = p.fpart + int64_t(b) * R * 64 * 2;
@@ -1851,20 +1852,9 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
           xstore64(mine + ((16 * mt + 4 * g + i) * 64 + 16 * ct + c) * 2, make_uint2(__float_as_uint(v), run));
         }
   }
-  // the phase-3 prefetch goes out once phase 1's loads are in (so that it
-  // does not delay them) and wave 0's stores are issued (the waves share the
-  // CU's memory pipeline); the barrier orders LDS only
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-  issue_uk(w != 0);
-#pragma unroll
-  for (int q = 0; q < kFusedPE; ++q) issue_w3(pre[q], q);
-  __builtin_amdgcn_sched_barrier(0);
-
-  if (w == 0) {
-    if (S) {
-      float* ylds = reinterpret_cast<float*>(red);   // [R][64] y of the c^Q window rows
+  float* const ylds = reinterpret_cast<float*>(red);   // [R][64] y of the c^Q window rows
+  if (w == 0 && S) {
+    {
       const rsrc_t Fp = make_rsrc(p.fpart, int64_t(fg.p1) * R * 64 * 8);
       for (int rb = r0; rb < r1; rb += 2) {
         const int r = rb + (lane >> 5);
@@ -1908,8 +1898,27 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
           xstore64(p.fykr + r * (d.Hckv + d.Dr) + col0, make_uint2(__float_as_uint(y[0]), __float_as_uint(y[1])));
         }
       }
+    }
+  }
+  // the phase-3 prefetch goes out once phase 1's loads are in (so that it
+  // does not delay them) and wave 0 has summed its window rows (the partials
+  // land far faster while HBM is quiet); the barrier orders LDS only
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  if (w != 0) {
+    issue_uk(true);
+#pragma unroll
+    for (int q = 0; q < kFusedPE; ++q) issue_w3(pre[q], q);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  if (w == 0) {
+    if (S) {
       if (qwin) {
         // c^Q = bf16(gamma y / rms) once every window sum of the rows is out
+        const uint32_t gq = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(p.gamma_cq, int64_t(d.Hcq) * 2),
+                                                                 col0 < d.Hcq ? col0 * 2u : kOOB, 0, 0);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -1988,46 +1997,46 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
     float y, a, b2;
     uint32_t gam;
     double ss;
-    int64_t slot;
   };
   const rsrc_t Yp = make_rsrc(p.fykr, int64_t(d.T) * W2 * 4);
   const rsrc_t Sk = make_rsrc(p.fss, int64_t(pg.win_dq + pg.win_kr) * 32 * 8);
   const rsrc_t Gk = make_rsrc(p.gamma_ckv, int64_t(d.Hckv) * 2);
-  auto job_load = [&](int jb) {
+  auto job_load = [&](int jb, bool on) {
     CacheJob cjb;
-    cjb.t = jb / cj; cjb.ch = jb % cj;
+    cjb.t = on ? jb / cj : 0; cjb.ch = on ? jb % cj : 1;
     const int col = 64 * cjb.ch + lane;
-    const bool kv = col < d.Hckv, kr = cjb.ch == 0 && lane < d.Dr / 2;
+    const bool kv = on && col < d.Hckv, kr = on && cjb.ch == 0 && lane < d.Dr / 2;
     cjb.y = bload4c(Yp, kv ? uint32_t(cjb.t * W2 + col) * 4u : kOOB);
     cjb.gam = __builtin_amdgcn_raw_buffer_load_b16(Gk, kv ? uint32_t(col) * 2u : kOOB, 0, 0);
     cjb.a = bload4c(Yp, kr ? uint32_t(cjb.t * W2 + d.Hckv + lane) * 4u : kOOB);
     cjb.b2 = bload4c(Yp, kr ? uint32_t(cjb.t * W2 + d.Hckv + lane + d.Dr / 2) * 4u : kOOB);
     cjb.ss = double(__uint_as_float(
-        bload8u(Sk, lane < pg.win_kr ? uint32_t((pg.win_dq + lane) * 32 + cjb.t) * 8u : kOOB).x));   // (float, tag)
-    cjb.slot = p.cache_index[cjb.t];
+        bload8u(Sk, on && lane < pg.win_kr ? uint32_t((pg.win_dq + lane) * 32 + cjb.t) * 8u : kOOB).x));   // (float, tag)
     return cjb;
   };
   // c^KV = gamma y / rms, k^R = RoPE(y_kr), bf16, at the token's slot
   auto job_store = [&](const CacheJob& cjb) {
     double ssk = cjb.ss;
     for (int o = 32; o > 0; o >>= 1) ssk += __shfl_xor(ssk, o, 64);
-    if (cjb.slot < 0 || cjb.slot >= d.slots) return;
+    const int64_t slot = p.cache_index[cjb.t];
+    if (slot < 0 || slot >= d.slots) return;
     const double rms = sqrt(ssk / double(d.Hckv) + d.eps_ckv);
     const int col = 64 * cjb.ch + lane;
     if (col < d.Hckv)
-      p.kv_cache[cjb.slot * d.Hckv + col] = f2bf(float(double(bf2f(uint16_t(cjb.gam))) * double(cjb.y) / rms));
+      p.kv_cache[slot * d.Hckv + col] = f2bf(float(double(bf2f(uint16_t(cjb.gam))) * double(cjb.y) / rms));
     if (cjb.ch == 0 && lane < d.Dr / 2) {
       const int hf = d.Dr / 2;
       const uint16_t* cs = p.cos + int64_t(cjb.t) * d.Dr;
       const uint16_t* sn = p.sin + int64_t(cjb.t) * d.Dr;
-      uint16_t* kr = p.kr_cache + cjb.slot * d.Dr;
+      uint16_t* kr = p.kr_cache + slot * d.Dr;
       kr[lane] = f2bf(float(double(cjb.a) * bf2f(cs[lane]) - double(cjb.b2) * bf2f(sn[lane])));
       kr[lane + hf] = f2bf(float(double(cjb.b2) * bf2f(cs[lane + hf]) + double(cjb.a) * bf2f(sn[lane + hf])));
     }
   };
+  // predicated loads rather than a branch: a select between loaded and
+  // default values would wait for the loads right here
   const bool cjob = w == NW - 1 && b < d.T * cj;
-  CacheJob job0{};
-  if (cjob) job0 = job_load(b);
+  const CacheJob job0 = job_load(b, cjob);
 
   const int64_t ctile = int64_t(pg.nst_cq) * 1024;
   const rsrc_t Cq = make_rsrc(p.cq, int64_t((d.T + 15) / 16) * ctile);
@@ -2110,7 +2119,7 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
   // for the exchange stores then does not wait for these)
   if (cjob) {
     job_store(job0);
-    for (int jb = b + G; jb < d.T * cj; jb += G) job_store(job_load(jb));
+    for (int jb = b + G; jb < d.T * cj; jb += G) job_store(job_load(jb, true));
   }
 
   // q^R: the owner of token tile mt holds both tiles of every RoPE pair
