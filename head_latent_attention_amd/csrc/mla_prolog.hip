@@ -1686,13 +1686,14 @@ constexpr int kFusedPE = 2;       // of those, the ones issued before the wait
 constexpr int kFusedStages = 7;   // phase-3 k-stages a wave may have (waves 1..7)
 constexpr int kFusedMaxSplits = 8;
 constexpr int kFusedFlagStride = 16;   // uint32 words between the fused kernel's flags
-constexpr int kFusedSpin = 1 << 20;
+constexpr int kFusedSpin = 1 << 20;   // poll steps before a wait gives up (about a second)
 
 struct FusedGeo {
   int nwin;            // windows of [W^DQ | W^DkvKr]
   int hi_win, hi_s;    // windows below hi_win take hi_s splits, the others hi_s - 1
   int p1;              // blocks with phase-1 work (the sum of the splits)
   uint32_t run;        // this run's number (1, 2, ...; never 0, modulo 2^32)
+  int spin;            // poll steps a wait makes before it gives up
 };
 
 __device__ __forceinline__ void xstore32(float* p, float v) {
@@ -1724,10 +1725,10 @@ __device__ __forceinline__ uint2 bload8u(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 16));
 }
 // one step of a bounded wave-wide poll: true once every lane's `ok` holds;
-// after kFusedSpin steps it marks the error word and gives up
-__device__ __forceinline__ bool fused_poll_done(bool ok, int& n, uint32_t* err) {
+// after `spin` steps it marks the error word and gives up
+__device__ __forceinline__ bool fused_poll_done(bool ok, int& n, int spin, uint32_t* err) {
   if (__builtin_amdgcn_ballot_w64(!ok) == 0) return true;
-  if (++n > kFusedSpin) {
+  if (++n > spin) {
     if ((threadIdx.x & 63) == 0) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return true;
   }
@@ -1873,7 +1874,7 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
           for (int k = 0; k < kFusedMaxSplits; ++k)
 #pragma unroll
             for (int e = 0; e < 2; ++e) ok &= !(act && k < S) || v[k][e].y == run;
-          if (fused_poll_done(ok, n, err)) break;
+          if (fused_poll_done(ok, n, fg.spin, err)) break;
         }
         float y[2] = {0, 0};
 #pragma unroll
@@ -1941,7 +1942,7 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
               bool ok = true;
 #pragma unroll
               for (int k = 0; k < 4; ++k) ok &= !(act && j0 + 32 * k < pg.win_dq) || v[k].y == run;
-              if (fused_poll_done(ok, n, err)) break;
+              if (fused_poll_done(ok, n, fg.spin, err)) break;
             }
 #pragma unroll
             for (int k = 0; k < 4; ++k) ss += double(__uint_as_float(v[k].x));   // zeros past win_dq
@@ -1979,7 +1980,7 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
 #pragma unroll
         for (int k = 0; k < 4; ++k) ok &= v[k] == run;
       }
-      if (fused_poll_done(ok, n, err)) break;
+      if (fused_poll_done(ok, n, fg.spin, err)) break;
     }
   }
   __syncthreads();
@@ -2951,6 +2952,7 @@ constexpr int kProfileEvents = 5;
 
 struct mla_prolog {
   mla_prolog_desc desc;
+  int fused_spin;      // poll steps of the fused kernel's waits
   Layout lay;
   uint8_t* ws;
   hipEvent_t* events;  // kProfileRing x kProfileEvents when profiling, else NULL
@@ -3059,6 +3061,7 @@ bool fused_geo(const mla_prolog_desc& dd, FusedGeo* fg) {
   const int smin = fg->hi_win < W ? fg->hi_s - 1 : fg->hi_s;
   if ((ceil_div(g.nst_he, smin) + 7) / 8 > kFusedP1) return false;
   fg->run = 0;
+  fg->spin = kFusedSpin;
   return true;
 }
 
@@ -3220,6 +3223,13 @@ mla_status mla_prolog_create(const mla_prolog_desc* desc, mla_prolog_t* out) {
   // be resident at once; MLA_PROLOG_FUSED=0 in the environment turns it off
   h->fused_run = 0;
   h->fused_fit[0] = h->fused_fit[1] = false;
+  // MLA_PROLOG_FUSED_SPIN overrides the poll steps a wait makes before it
+  // gives up (a test of the failure report sets it to 1)
+  h->fused_spin = kFusedSpin;
+  if (const char* sp = std::getenv("MLA_PROLOG_FUSED_SPIN")) {
+    const long v = std::strtol(sp, nullptr, 10);
+    if (v > 0 && v <= kFusedSpin) h->fused_spin = int(v);
+  }
   {
     FusedGeo fg;
     const char* env = std::getenv("MLA_PROLOG_FUSED");
@@ -3312,6 +3322,7 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   FusedGeo fg;
   if (p.packed && pl.stream && h->fused_fit[pl.mt1 == 1 ? 0 : 1] && fused_geo(dd, &fg)) {
     fg.run = ++h->fused_run;
+    fg.spin = h->fused_spin;
     const PackGeo g = pack_geo(dd.He, dd.Hcq, dd.Hckv, dd.N, dd.D, dd.Dr, false);
     if (pl.mt1 == 1) k_fused<1><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g, fg);
     else k_fused<2><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g, fg);

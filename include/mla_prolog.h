@@ -159,7 +159,10 @@ mla_status mla_prolog_pack_weights(mla_prolog_t handle, const mla_prolog_tensors
 
 /* Validates desc, allocates the handle and its device workspace on
  * desc->device (the caller's current device is restored).  On error *out is
- * set to NULL. */
+ * set to NULL.  Two environment variables, read here, are for diagnosis:
+ * MLA_PROLOG_FUSED=0 keeps small-T runs off the one-launch kernel, and
+ * MLA_PROLOG_FUSED_SPIN=n (1..2^20) caps the poll steps of that kernel's
+ * waits (see mla_prolog_check). */
 mla_status mla_prolog_create(const mla_prolog_desc* desc, mla_prolog_t* out);
 
 /* Enqueues one prolog over T tokens on stream (a hipStream_t; NULL = the

@@ -304,6 +304,29 @@ def test_fused_mixed_token_counts():
             check_caches(inp, got["kv_cache"], got["kr_cache"], ref, np.arange(T))
 
 
+def test_fused_gave_up_is_reported(monkeypatch):
+    # a poll limit of one step makes the one-kernel path's waits give up
+    # (every access stays in bounds and the kernel ends normally); the
+    # handle must report it, and a fresh handle must not
+    inp = synth.make_inputs(PAIR["pair_t16_n16"])
+    say("case fused wait gives up")
+    monkeypatch.setenv("MLA_PROLOG_FUSED_SPIN", "1")
+    t = dev.upload(inp)
+    desc = mla.make_desc(**dev.desc_args(inp))
+    h = mla.MlaProlog(desc)
+    buf = torch.empty(mla.packed_weights_bytes(desc), dtype=torch.uint8, device="cuda")
+    h.pack_weights(t, buf)
+    t["packed_weights"] = buf
+    for _ in range(3):
+        h.run(t, int(inp["T"]))
+    with pytest.raises(mla.MlaError):
+        h.check()
+    h.check()   # the record was cleared
+    h.close()
+    monkeypatch.delenv("MLA_PROLOG_FUSED_SPIN")
+    full_check(inp, packed=True)
+
+
 @pytest.mark.parametrize("name", list(PAIR_INT8))
 def test_pair_int8_packed(name):
     inp = synth.make_inputs(PAIR_INT8[name])
