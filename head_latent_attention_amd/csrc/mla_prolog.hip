@@ -39,6 +39,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;  // 4 waves of 64
 
@@ -2642,7 +2643,10 @@ __global__ __launch_bounds__(64 * WM * WN) void k4_tiled(Dims d, Ptrs p, PackGeo
   if constexpr (!Q8) {
     // each 16-token x 64-column piece goes through the wave's LDS tile
     // (rows 144 bytes apart, which spreads the 8-byte writes over the banks)
-    // and out as 16-byte stores, eight whole 128-byte row pieces per store
+    // and out as 16-byte stores, eight whole 128-byte row pieces per store;
+    // the stores are non-temporal (queryOut is written once and not read
+    // back here, and the streaming hint keeps it from displacing the
+    // operands in the caches)
     if (m0 >= d.T) return;
     uint16_t* qo = static_cast<uint16_t*>(p.q_out);
     uint8_t* tile = stage + w * 16 * 144;
@@ -2666,8 +2670,8 @@ __global__ __launch_bounds__(64 * WM * WN) void k4_tiled(Dims d, Ptrs p, PackGeo
           const int k = lane + 64 * half, row = k >> 3, col = 8 * (k & 7);
           const int m = m0 + 16 * mt + row;
           if (m < d.T && col < width)
-            *reinterpret_cast<uint4*>(qo + (int64_t(m) * d.N + h) * d.Hckv + 64 * jw + col) =
-                *reinterpret_cast<const uint4*>(tile + row * 144 + col * 2);
+            __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(tile + row * 144 + col * 2),
+                                        reinterpret_cast<u32x4*>(qo + (int64_t(m) * d.N + h) * d.Hckv + 64 * jw + col));
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
