@@ -429,6 +429,11 @@ __device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, v);
 }
 
+// a 16-byte buffer load with the streaming hint, for data read once
+__device__ __forceinline__ uint4 bload16s(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+}
+
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -1773,7 +1778,7 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int k = 0; k < 2; ++k)
-        bu[s][k] = bload16(Wp, ok && ukact && s < pg.nst_d
+        bu[s][k] = bload16s(Wp, ok && ukact && s < pg.nst_d
                                    ? ukb + uint32_t(s * 4096 + (ctu + k) * 1024 + lane * 16)
                                    : kOOB);
   };
@@ -1784,10 +1789,10 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
     const bool ok = q < ns3;
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct)
-      r[ct] = bload16(Wp, ok ? nb + uint32_t(st) * 4096u + uint32_t(ct * 1024 + lane * 16) : kOOB);
+      r[ct] = bload16s(Wp, ok ? nb + uint32_t(st) * 4096u + uint32_t(ct * 1024 + lane * 16) : kOOB);
 #pragma unroll
     for (int k = 0; k < 2; ++k)
-      r[4 + k] = bload16(Wp, ok ? rb + uint32_t(st) * 4096u + uint32_t((half + 2 * k) * 1024 + lane * 16) : kOOB);
+      r[4 + k] = bload16s(Wp, ok ? rb + uint32_t(st) * 4096u + uint32_t((half + 2 * k) * 1024 + lane * 16) : kOOB);
   };
 
   // ---- phase 1: block -> split s of S of window j
@@ -1813,7 +1818,7 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
     const bool ok = q < ns1;
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct)
-      b1[q][ct] = bload16(Wp, ok ? w1b + uint32_t(st) * 4096u + uint32_t(ct * 1024 + lane * 16) : kOOB);
+      b1[q][ct] = bload16s(Wp, ok ? w1b + uint32_t(st) * 4096u + uint32_t(ct * 1024 + lane * 16) : kOOB);
     ax.load(a1[q], st, ok);
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -2275,7 +2280,10 @@ __device__ __forceinline__ APacked<I8, MT> tiles_from(const void* base, int64_t 
 // every wave then reads its fragments with conflict-free 16-byte LDS reads.
 // The global loads run three stages ahead of the MFMAs through two register
 // sets.  ns must be the same for the whole block.
-template <bool I8, int MT, int NWW, int WM, int WN, class AP, int RS = 2, int KPB = 1>
+// SH: weight loads carry the streaming hint; set where each weight byte is
+// read once per step (few token tiles), left off where token tiles re-read
+// the weights and want them kept in the caches
+template <bool I8, int MT, int NWW, int WM, int WN, class AP, int RS = 2, int KPB = 1, bool SH = false>
 __device__ __forceinline__ void tile_mma_lds(const AP& ap, rsrc_t Wp, uint32_t wbase, uint32_t wstride,
                                              int nwin, int s0, int ns, uint8_t* lds,
                                              typename Stage<I8>::Acc (&acc)[MT][NWW * 4]) {
@@ -2307,9 +2315,10 @@ __device__ __forceinline__ void tile_mma_lds(const AP& ap, rsrc_t Wp, uint32_t w
 #pragma unroll
       for (int q = 0; q < CB; ++q) {
         const int b = w + q * NW, v = b >> 2;
-        r[kk][CA + q] = bload16(Wp, ok && b < BC && v < nwin ? wbase + uint32_t(v) * wstride + uint32_t(st) * 4096u +
-                                                                   uint32_t((b & 3) * 1024 + lane * 16)
-                                                             : kOOB);
+        const uint32_t off = ok && b < BC && v < nwin ? wbase + uint32_t(v) * wstride + uint32_t(st) * 4096u +
+                                                            uint32_t((b & 3) * 1024 + lane * 16)
+                                                      : kOOB;
+        r[kk][CA + q] = SH ? bload16s(Wp, off) : bload16(Wp, off);
       }
     }
   };
@@ -2416,7 +2425,7 @@ __global__ __launch_bounds__(256) void k_pack_x(Dims d, Ptrs p, int nst) {
 
 // XP: x is read fragment-packed from p.xp instead of row-major.
 template <bool I8, int MT, int NWW, int WM, int WN, int D, bool LC = false, bool XP = false, int RS = 2,
-          int KPB = 1>
+          int KPB = 1, bool SH = false>
 __global__ __launch_bounds__(64 * WM * WN) void k1_tiled(Dims d, Ptrs p, PackGeo pg, int sps, int mtiles,
                                                       int ngrp) {
   using St = Stage<I8>;
@@ -2440,7 +2449,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k1_tiled(Dims d, Ptrs p, PackGeo
     __shared__ __attribute__((aligned(16))) uint8_t ring[2 * KPB * (MT * WM + NWW * WN * 4) * 1024];
     const int mb = mtile * BM, j0 = grp * GW;
     const int nsb = mb < d.T ? max(0, min(pg.nst_he, s0 + sps) - s0) : 0;
-    tile_mma_lds<I8, MT, NWW, WM, WN, APlain<I8, MT * WM>, RS, KPB>(rows_from<I8, MT * WM>(p.x, d.He, mb, d.T),
+    tile_mma_lds<I8, MT, NWW, WM, WN, APlain<I8, MT * WM>, RS, KPB, SH>(rows_from<I8, MT * WM>(p.x, d.He, mb, d.T),
                                       make_rsrc(p.packed, pg.total),
                                       uint32_t(pg.off_dq + int64_t(j0) * pg.nst_he * 4096),
                                       uint32_t(pg.nst_he * 4096), tiles - j0, s0, nsb, ring, acc);
@@ -2483,7 +2492,8 @@ __global__ __launch_bounds__(64 * WM * WN) void k1_tiled(Dims d, Ptrs p, PackGeo
 // K3t: grid (token tiles fastest, then groups of W^UqQr windows).  Nope
 // windows go to q^C (bf16, workspace); a rope window goes through a per-wave
 // LDS tile of 16 tokens x 64 columns to RoPE and queryRopeOut.
-template <bool I8, int MT, int NWW, int WM, int WN, int D, bool LC = false, int RS = 2, int KPB = 1>
+template <bool I8, int MT, int NWW, int WM, int WN, int D, bool LC = false, int RS = 2, int KPB = 1,
+          bool SH = false>
 __global__ __launch_bounds__(64 * WM * WN) void k3_tiled(Dims d, Ptrs p, PackGeo pg, int mtiles) {
   using St = Stage<I8>;
   constexpr int BM = 16 * MT * WM, GW = NWW * WN;
@@ -2506,7 +2516,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k3_tiled(Dims d, Ptrs p, PackGeo
   if constexpr (LC) {
     uint8_t* ring = lds_k3;
     const int mb = mtile * BM, j0 = grp * GW;
-    tile_mma_lds<I8, MT, NWW, WM, WN, APacked<I8, MT * WM>, RS, KPB>(
+    tile_mma_lds<I8, MT, NWW, WM, WN, APacked<I8, MT * WM>, RS, KPB, SH>(
         tiles_from<I8, MT * WM>(p.cq, int64_t(pg.nst_cq) * 1024, (d.T + 15) / 16, mb),
         make_rsrc(p.packed, pg.total), uint32_t(pg.off_uq + int64_t(j0) * pg.nst_cq * 4096),
         uint32_t(pg.nst_cq * 4096), pg.win_uq - j0, 0, mb < d.T ? pg.nst_cq : 0, ring, acc);
@@ -3087,15 +3097,16 @@ template <bool I8, int MT, class Mark>
 void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g,
                   bool q8, Mark& mark) {
   const dim3 g1(tp.m1 * tp.ngrp1 * tp.S), g3(tp.m3 * tp.ngrp3);
-  if (tp.k1v == 1) k1_tiled<I8, 4, 1, 4, 2, 2, true><<<g1, 512, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
+  if (tp.k1v == 1)
+    k1_tiled<I8, 4, 1, 4, 2, 2, true, false, 2, 1, true><<<g1, 512, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
   else if (I8 && tp.k1v == 2)
-    k1_tiled<I8, 2, 1, 4, 2, 2, true><<<g1, 512, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
+    k1_tiled<I8, 2, 1, 4, 2, 2, true, false, 2, 1, true><<<g1, 512, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
   else k1_tiled<I8, MT, 1, 1, 1, 2><<<g1, 64, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
   mark(1);
   launch_norm<I8>(s, d, p, tp.S, g.nst_cq);
   mark(2);
-  if (tp.k3v == 1) k3_tiled<I8, 2, 1, 8, 2, 2, true, 2><<<g3, 1024, 0, s>>>(d, p, g, tp.m3);
-  else if (I8 && tp.k3v == 2) k3_tiled<I8, 1, 1, 8, 2, 2, true, 1><<<g3, 1024, 0, s>>>(d, p, g, tp.m3);
+  if (tp.k3v == 1) k3_tiled<I8, 2, 1, 8, 2, 2, true, 2, 1, true><<<g3, 1024, 0, s>>>(d, p, g, tp.m3);
+  else if (I8 && tp.k3v == 2) k3_tiled<I8, 1, 1, 8, 2, 2, true, 1, 1, true><<<g3, 1024, 0, s>>>(d, p, g, tp.m3);
   else k3_tiled<I8, 4, 1, 1, 1, 2><<<g3, 64, 0, s>>>(d, p, g, tp.m3);
   mark(3);
   if (q8) k4_tiled<4, 1, 1, 8, 2, true, false, true><<<dim3(tp.m4q * d.N), 512, 0, s>>>(d, p, g, tp.m4q, 1);
