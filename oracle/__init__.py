@@ -39,11 +39,12 @@ class Problem(ctypes.Structure):
         ("eps_cq", ctypes.c_double), ("eps_ckv", ctypes.c_double),
         ("quant_in", ctypes.c_int32), ("query_int8", ctypes.c_int32),
         ("round_intermediates", ctypes.c_int32), ("mutation", ctypes.c_int32),
+        ("quant_uq", ctypes.c_int32), ("pad_", ctypes.c_int32),
         ("x", _P), ("w_dq", _P), ("w_uq_qr", _P), ("w_uk", _P), ("w_dkv_kr", _P),
         ("gamma_cq", _P), ("gamma_ckv", _P), ("rope_sin", _P), ("rope_cos", _P),
         ("cache_index", _P), ("kv_cache", _P), ("kr_cache", _P),
         ("scale_x", _P), ("scale_w_dq", _P), ("scale_w_uq_qr", _P), ("scale_w_dkv_kr", _P),
-        ("tokens", _P), ("n_tokens", _I64),
+        ("smooth_cq", _P), ("tokens", _P), ("n_tokens", _I64),
         ("query_out", _P), ("query_rope_out", _P), ("dequant_scale_q_nope", _P),
         ("kv_rows", _P), ("kr_rows", _P),
         ("y_out", _P), ("cq_out", _P), ("u_out", _P), ("qn_out", _P),
@@ -123,7 +124,9 @@ def run(inp: Dict[str, object], tokens: Optional[Sequence[int]] = None,
         nthreads: int = 0) -> Dict[str, np.ndarray]:
     """Run the oracle on the host arrays of ``synth.make_inputs``.
 
-    ``tokens`` selects the rows to compute (tokens are independent); row r of
+    ``inp["quant"]`` is the int8 full-quantisation scenario, ``inp["partial"]``
+    the partial one (only weightUqQr int8); ``inp["smooth_scales_cq"]``, when
+    present, is smoothScalesCq.  ``tokens`` selects the rows to compute (tokens are independent); row r of
     every output holds token ``tokens[r]``.  With ``caches`` the returned
     ``kv_cache``/``kr_cache`` are copies of the input caches with the computed
     rows written at their cacheIndex slots.
@@ -131,6 +134,7 @@ def run(inp: Dict[str, object], tokens: Optional[Sequence[int]] = None,
     d = inp["dims"]
     T = int(inp["T"])
     quant = bool(inp["quant"])
+    quant_uq = quant or bool(inp.get("partial", False))
     q8 = quant if query_int8 is None else bool(query_int8)
     keep = []
 
@@ -141,7 +145,7 @@ def run(inp: Dict[str, object], tokens: Optional[Sequence[int]] = None,
 
     x = arr(inp["token_x"], np.int8 if quant else np.uint16)
     wdq = arr(inp["weight_dq"], np.int8 if quant else np.uint16)
-    wuq = arr(inp["weight_uq_qr"], np.int8 if quant else np.uint16)
+    wuq = arr(inp["weight_uq_qr"], np.int8 if quant_uq else np.uint16)
     wdkv = arr(inp["weight_dkv_kr"], np.int8 if quant else np.uint16)
     wuk = arr(inp["weight_uk"], np.uint16)
     gcq = arr(inp["rmsnorm_gamma_cq"], np.uint16)
@@ -178,7 +182,7 @@ def run(inp: Dict[str, object], tokens: Optional[Sequence[int]] = None,
     p.T, p.He, p.Hcq, p.Hckv, p.N, p.D, p.Dr = T, d.He, Hcq, Hckv, N, D, Dr
     p.block_num, p.block_size = int(inp["block_num"]), int(inp["block_size"])
     p.eps_cq, p.eps_ckv = float(inp["eps_cq"]), float(inp["eps_ckv"])
-    p.quant_in, p.query_int8 = int(quant), int(q8)
+    p.quant_in, p.query_int8, p.quant_uq = int(quant), int(q8), int(quant_uq)
     p.round_intermediates, p.mutation = int(bool(round_intermediates)), int(mutation)
     p.x, p.w_dq, p.w_uq_qr, p.w_uk, p.w_dkv_kr = _ptr(x), _ptr(wdq), _ptr(wuq), _ptr(wuk), _ptr(wdkv)
     p.gamma_cq, p.gamma_ckv, p.rope_sin, p.rope_cos = _ptr(gcq), _ptr(gckv), _ptr(sin), _ptr(cos)
@@ -188,6 +192,10 @@ def run(inp: Dict[str, object], tokens: Optional[Sequence[int]] = None,
         p.scale_w_dq = _ptr(arr(inp["dequant_scale_w_dq"], np.float32))
         p.scale_w_uq_qr = _ptr(arr(inp["dequant_scale_w_uq_qr"], np.float32))
         p.scale_w_dkv_kr = _ptr(arr(inp["dequant_scale_w_dkv_kr"], np.float32))
+    elif quant_uq:
+        p.scale_w_uq_qr = _ptr(arr(inp["dequant_scale_w_uq_qr"], np.float32))
+    if inp.get("smooth_scales_cq") is not None:
+        p.smooth_cq = _ptr(arr(inp["smooth_scales_cq"], np.float32))
     p.tokens, p.n_tokens = _ptr(rows), n
     p.query_out, p.query_rope_out = _ptr(out["query_out"]), _ptr(out["query_rope_out"])
     p.dequant_scale_q_nope = _ptr(out.get("dequant_scale_q_nope"))

@@ -27,11 +27,25 @@
 // matrix product (the readings R1..R7):
 //   R1 kvCache row = bf16(c^KV)          R2 krCache row = bf16(k^R)
 //   R3 bf16 operand bf16(c^Q)            R3' int8 operand: per-token dynamic
-//                                            int8 of c^Q, decided in float32
+//                                            int8 of c^Q (times the optional
+//                                            smoothScalesCq), decided in float32
 //   R4 queryRopeOut = bf16(q^R)          R5 W^UK operand bf16(q^C)
 //   R6 queryOut = bf16(q^N)              R7 int8 queryOut: per-(token, head)
 //                                            dynamic int8, decided in float32
 // round_intermediates = 0 skips R3 and R5 (used by the composition pin).
+//
+// The partial-quantisation scenario (same page, scenario table) takes tokenX,
+// weightDq and weightDkvKr in bf16 and only weightUqQr in int8, with its
+// per-channel dequantisation scale; the up-projection then runs on R3' as in
+// full quantisation.  smoothScalesCq (1, Hcq), optional in both int8
+// scenarios, multiplies c^Q element-wise before R3' decides the codes (the
+// page's parameter table: a parameter of the dynamic quantisation of the
+// RmsNorm output).  The product is not divided back: the caller's int8
+// weightUqQr carries the inverse smoothing, as is usual for smoothing
+// factors.  Here c^Q * m is formed as RmsNorm with gamma * m for its weight:
+// gamma (bf16) times m (fp32) is exact in double, and the result is the
+// same real number, so only the double-rounding order is a choice (the one
+// the device uses, so that both take the same int8 decisions).
 //
 // Every function here is pinned by the CPU tests (closed forms, invariants,
 // special cases, brute force on tiny shapes, planted mistakes); none is
@@ -142,6 +156,8 @@ typedef struct {
   int32_t query_int8;           // 1: q^N as int8 + per-(token, head) scale
   int32_t round_intermediates;  // 0: skip R3 and R5
   int32_t mutation;             // planted mistake for the pin tests, 0 = none
+  int32_t quant_uq;             // 1: int8 W^UqQr + fp32 scale and R3' (implied by quant_in)
+  int32_t pad_;
   const void* x;                // uint16 bf16 bits, or int8
   const void* w_dq;
   const void* w_uq_qr;
@@ -158,6 +174,7 @@ typedef struct {
   const float* scale_w_dq;      // (Hcq)
   const float* scale_w_uq_qr;   // (N*(D+Dr))
   const float* scale_w_dkv_kr;  // (Hckv+Dr)
+  const float* smooth_cq;       // (Hcq) smoothScalesCq, int8 W^UqQr only; NULL = none
   const int64_t* tokens;        // rows to compute; NULL = 0..T-1
   int64_t n_tokens;
   // outputs, row r of each holds token tokens[r]
@@ -252,10 +269,21 @@ static void one_token(const mla_oracle_problem* p, int64_t r, int64_t t) {
 
   // up-projection u = c^Q [W^UQ | W^QR]
   std::vector<double> u(Wuq, 0.0);
-  if (q8in) {  // R3'
+  if (q8in || p->quant_uq) {  // R3'
+    std::vector<double> cm(c_q);
+    if (p->smooth_cq) {
+      // c^Q * m: the RmsNorm of y_q with weight gamma * m (exact products)
+      for (int64_t i = 0; i < Hcq; ++i) {
+        double m = p->smooth_cq[i];
+        if (mut == 6) m = 1.0 / m;   // planted: smoothing divided out
+        if (mut == 7) m = 1.0;       // planted: smoothing ignored
+        g[i] = bf16_value(p->gamma_cq[i]) * m;
+      }
+      rmsnorm(y_q.data(), g.data(), Hcq, p->eps_cq, cm.data(), mut);
+    }
     std::vector<int8_t> c8(Hcq);
     float s_cq;
-    quant_int8(c_q.data(), Hcq, c8.data(), &s_cq);
+    quant_int8(cm.data(), Hcq, c8.data(), &s_cq);
     const int8_t* w = static_cast<const int8_t*>(p->w_uq_qr);
     std::vector<int64_t> acc(Wuq, 0);
     for (int64_t k = 0; k < Hcq; ++k) {
@@ -315,6 +343,8 @@ int mla_oracle_run(mla_oracle_problem* p, int nthreads) {
     return -1;
   if (p->quant_in && (!p->scale_x || !p->scale_w_dq || !p->scale_w_uq_qr || !p->scale_w_dkv_kr))
     return -1;
+  if (p->quant_uq && !p->scale_w_uq_qr) return -1;
+  if (p->smooth_cq && !p->quant_in && !p->quant_uq) return -1;
   if (p->query_int8 && !p->dequant_scale_q_nope) return -1;
   const int64_t n = p->tokens ? p->n_tokens : p->T;
   for (int64_t r = 0; r < n; ++r) {

@@ -31,6 +31,10 @@ def upload(inp: Dict[str, object], device="cuda:0", query_int8=None) -> Dict[str
         names.update({"dequant_scale_x": "scale_x", "dequant_scale_w_dq": "scale_w_dq",
                       "dequant_scale_w_uq_qr": "scale_w_uq_qr",
                       "dequant_scale_w_dkv_kr": "scale_w_dkv_kr"})
+    elif inp.get("partial", False):
+        names["dequant_scale_w_uq_qr"] = "scale_w_uq_qr"
+    if inp.get("smooth_scales_cq") is not None:
+        names["smooth_scales_cq"] = "smooth_scales_cq"
     out = {lib_name: _tensor(np.asarray(inp[key]), device) for key, lib_name in names.items()
            if key in inp}
     out["query_out"] = torch.zeros((T, d.N, d.Hckv), dtype=torch.int8 if q8 else torch.bfloat16,
@@ -50,7 +54,8 @@ def bits(t: torch.Tensor) -> np.ndarray:
 
 
 def desc_args(inp: Dict[str, object], max_tokens=None, query_int8=None) -> Dict[str, object]:
-    """Keyword arguments of ``make_desc`` for these inputs."""
+    """Keyword arguments of ``make_desc`` for these inputs (in_dtype 0 bf16,
+    1 int8 full quantisation, 2 partial quantisation)."""
     d = inp["dims"]
     quant = bool(inp["quant"])
     q8 = quant if query_int8 is None else bool(query_int8)
@@ -58,4 +63,4 @@ def desc_args(inp: Dict[str, object], max_tokens=None, query_int8=None) -> Dict[
                 block_num=int(inp["block_num"]), block_size=int(inp["block_size"]),
                 max_tokens=int(inp["T"]) if max_tokens is None else int(max_tokens),
                 eps_cq=float(inp["eps_cq"]), eps_ckv=float(inp["eps_ckv"]),
-                in_dtype=int(quant), query_dtype=int(q8))
+                in_dtype=2 if inp.get("partial", False) else int(quant), query_dtype=int(q8))

@@ -39,7 +39,7 @@ SENTINEL_BF16 = np.uint16(0x7FA5)
 _STREAM = {
     "x": 1, "w_dq": 2, "w_uq": 3, "w_qr": 4, "w_uk": 5, "w_dkv": 6, "w_kr": 7,
     "gamma_cq": 8, "gamma_ckv": 9, "pos": 10, "slots": 11, "sx": 12,
-    "sw_dq": 13, "sw_uq_qr": 14, "sw_dkv_kr": 15, "blocks": 16,
+    "sw_dq": 13, "sw_uq_qr": 14, "sw_dkv_kr": 15, "blocks": 16, "smooth_cq": 17,
 }
 
 
@@ -154,6 +154,8 @@ class Workload:
     positions: str        # "uniform:<P>" or "prefill:<seqs>x<len>"
     seed: int
     eps: float = 1e-6
+    partial: bool = False  # partial quantisation: only weightUqQr int8 (+ its scale)
+    smooth: bool = False   # draw smoothScalesCq (int8 weightUqQr scenarios only)
 
     def with_tokens(self, T: int) -> "Workload":
         return replace(self, T=T)
@@ -165,6 +167,10 @@ WORKLOADS: Dict[str, Workload] = {
     "decode_t256": Workload("decode_t256", 256, MODEL, 4096, 128, False, "uniform:32768", 20262),
     "prefill_t8192": Workload("prefill_t8192", 8192, MODEL, 1024, 128, False, "prefill:2x4096", 20263),
     "int8_decode_t128": Workload("int8_decode_t128", 128, MODEL, 1024, 128, True, "uniform:32768", 20264),
+    "tiny_partial_t4": Workload("tiny_partial_t4", 4, TINY, 4, 16, False, "uniform:64", 20265,
+                                partial=True, smooth=True),
+    "partial_decode_t32": Workload("partial_decode_t32", 32, MODEL, 1024, 128, False, "uniform:32768",
+                                   20266, partial=True, smooth=True),
 }
 
 
@@ -229,7 +235,12 @@ def make_inputs(wl: Workload, T: Optional[int] = None, with_caches: bool = True,
     He, Hcq, Hckv, N, D, Dr = d.He, d.Hcq, d.Hckv, d.N, d.D, d.Dr
     out: Dict[str, object] = {"workload": wl.name, "T": T, "dims": d,
                               "block_num": wl.block_num, "block_size": wl.block_size,
-                              "quant": wl.quant, "eps_cq": wl.eps, "eps_ckv": wl.eps}
+                              "quant": wl.quant, "partial": wl.partial,
+                              "eps_cq": wl.eps, "eps_ckv": wl.eps}
+    if wl.partial and wl.quant:
+        raise ValueError("a workload is either fully or partially quantised")
+    if wl.smooth and not (wl.quant or wl.partial):
+        raise ValueError("smoothScalesCq belongs to the int8 weightUqQr scenarios")
 
     pos, slots = _positions_and_slots(wl)
     pos, slots = pos[:T], slots[:T]
@@ -251,8 +262,13 @@ def make_inputs(wl: Workload, T: Optional[int] = None, with_caches: bool = True,
     if not wl.quant:
         out["token_x"] = _to_bf16_bits(_normal(s, "x", full_T * He)[:T * He]).reshape(T, He)
         w_dq = _to_bf16_bits(_normal(s, "w_dq", He * Hcq) / np.sqrt(He)).reshape(He, Hcq)
-        w_uq = _to_bf16_bits(_normal(s, "w_uq", Hcq * N * D) / np.sqrt(Hcq)).reshape(Hcq, N * D)
-        w_qr = _to_bf16_bits(_normal(s, "w_qr", Hcq * N * Dr) / np.sqrt(Hcq)).reshape(Hcq, N * Dr)
+        if wl.partial:
+            w_uq = _int8_uniform(s, "w_uq", Hcq * N * D).reshape(Hcq, N * D)
+            w_qr = _int8_uniform(s, "w_qr", Hcq * N * Dr).reshape(Hcq, N * Dr)
+            out["dequant_scale_w_uq_qr"] = (0.001 + 0.009 * _uniform(s, "sw_uq_qr", N * (D + Dr))).astype(np.float32)
+        else:
+            w_uq = _to_bf16_bits(_normal(s, "w_uq", Hcq * N * D) / np.sqrt(Hcq)).reshape(Hcq, N * D)
+            w_qr = _to_bf16_bits(_normal(s, "w_qr", Hcq * N * Dr) / np.sqrt(Hcq)).reshape(Hcq, N * Dr)
         w_dkv = _to_bf16_bits(_normal(s, "w_dkv", He * Hckv) / np.sqrt(He)).reshape(He, Hckv)
         w_kr = _to_bf16_bits(_normal(s, "w_kr", He * Dr) / np.sqrt(He)).reshape(He, Dr)
     else:
@@ -266,6 +282,9 @@ def make_inputs(wl: Workload, T: Optional[int] = None, with_caches: bool = True,
         out["dequant_scale_w_dq"] = (0.001 + 0.009 * _uniform(s, "sw_dq", Hcq)).astype(np.float32)
         out["dequant_scale_w_uq_qr"] = (0.001 + 0.009 * _uniform(s, "sw_uq_qr", N * (D + Dr))).astype(np.float32)
         out["dequant_scale_w_dkv_kr"] = (0.001 + 0.009 * _uniform(s, "sw_dkv_kr", Hckv + Dr)).astype(np.float32)
+    if wl.smooth:
+        # per-channel smoothing factors in [0.5, 2)
+        out["smooth_scales_cq"] = (0.5 + 1.5 * _uniform(s, "smooth_cq", Hcq)).astype(np.float32)
     out["weight_dq"] = np.ascontiguousarray(w_dq)
     out["weight_uq_qr"] = head_interleave(w_uq, w_qr)
     out["weight_dkv_kr"] = np.ascontiguousarray(np.concatenate([w_dkv, w_kr], axis=1))
@@ -284,9 +303,9 @@ def make_inputs(wl: Workload, T: Optional[int] = None, with_caches: bool = True,
 
 def custom_workload(name: str, T: int, dims: Dims, block_num: int, block_size: int,
                     quant: bool = False, seed: int = 7, positions: str = "uniform:4096",
-                    eps: float = 1e-6) -> Workload:
+                    eps: float = 1e-6, partial: bool = False, smooth: bool = False) -> Workload:
     """A workload with arbitrary (small) sizes for tests of ragged shapes."""
-    return Workload(name, T, dims, block_num, block_size, quant, positions, seed, eps)
+    return Workload(name, T, dims, block_num, block_size, quant, positions, seed, eps, partial, smooth)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:

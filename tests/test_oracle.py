@@ -384,6 +384,90 @@ def test_thread_count_does_not_change_results():
         assert np.array_equal(a[k], b[k])
 
 
+# ---------------------------------------------------------------------------
+# partial quantisation (int8 weightUqQr only) and smoothScalesCq
+# ---------------------------------------------------------------------------
+PARTIAL = synth.workload("tiny_partial_t4")
+RAGGED_PARTIAL = custom_workload("ragged_partial", T=5, dims=Dims(He=40, Hcq=24, Hckv=12, N=3, D=6, Dr=4),
+                                 block_num=3, block_size=16, seed=13, partial=True, smooth=True)
+RAGGED_Q8_SMOOTH = custom_workload("ragged_q8_smooth", T=6, dims=Dims(He=48, Hcq=16, Hckv=8, N=2, D=4, Dr=6),
+                                   block_num=2, block_size=16, quant=True, seed=14, smooth=True)
+
+
+def _with(inp, **kw):
+    out = dict(inp)
+    out.update(kw)
+    return out
+
+
+@pytest.mark.parametrize("wl", [PARTIAL, RAGGED_PARTIAL], ids=["tiny_partial", "ragged_partial"])
+def test_partial_scenario_keeps_the_bf16_cache_path(wl):
+    # only weightUqQr is int8: y, c^Q and the cache rows are those of the
+    # scalar formulas on the bf16 inputs, whatever weightUqQr holds
+    inp = synth.make_inputs(wl, unpacked=True)
+    d = inp["dims"]
+    o = oracle.run(inp, intermediates=True)
+    bf = brute_force(inp)
+    assert np.allclose(o["y"][:, :d.Hcq], bf["y_q"], rtol=1e-12, atol=1e-12)
+    assert np.allclose(o["c_q"], bf["c_q"], rtol=1e-12, atol=1e-12)
+    assert near_bf16(o["kv_rows"], bf["c_kv"])
+    assert near_bf16(o["kr_rows"], bf["k_r"])
+    other = oracle.run(_with(inp, weight_uq_qr=np.zeros_like(inp["weight_uq_qr"])))
+    assert np.array_equal(other["kv_cache"], o["kv_cache"])
+    assert np.array_equal(other["kr_cache"], o["kr_cache"])
+
+
+def _smooth_bound_holds(inp, o):
+    """u = c8 W8 s_cq s_w approximates (c^Q * m) W8 s_w within the int8
+    rounding of c^Q * m: each code is off by at most half a step s_cq (plus
+    the float32 rounding of c^Q * m before the decision)."""
+    w8 = np.asarray(inp["weight_uq_qr"]).astype(np.float64)
+    sw = inp["dequant_scale_w_uq_qr"].astype(np.float64)
+    m = inp.get("smooth_scales_cq")
+    m = np.ones(inp["dims"].Hcq) if m is None else m.astype(np.float64)
+    for t in range(inp["T"]):
+        cm = o["c_q"][t] * m
+        s = np.max(np.abs(cm)) / 127 * (1 + 1e-6)
+        ref = (cm @ w8) * sw
+        err = ((s / 2 + np.abs(cm) * 2.0 ** -24) @ np.abs(w8)) * sw
+        if not np.all(np.abs(o["u"][t] - ref) <= err * (1 + 1e-9) + 1e-300):
+            return False
+    return True
+
+
+@pytest.mark.parametrize("wl", [PARTIAL, RAGGED_PARTIAL, RAGGED_Q8_SMOOTH],
+                         ids=["tiny_partial", "ragged_partial", "ragged_q8_smooth"])
+def test_smoothed_up_projection_within_the_quantisation_bound(wl):
+    inp = synth.make_inputs(wl)
+    o = oracle.run(inp, intermediates=True, query_int8=False)
+    assert _smooth_bound_holds(inp, o)
+    # the smoothing is not a no-op on these inputs: the same bound around the
+    # unsmoothed product fails
+    assert not _smooth_bound_holds(_with(inp, smooth_scales_cq=None), o)
+
+
+@pytest.mark.parametrize("wl", [PARTIAL, RAGGED_Q8_SMOOTH], ids=["tiny_partial", "ragged_q8_smooth"])
+def test_unit_smoothing_is_no_smoothing(wl):
+    inp = synth.make_inputs(wl)
+    a = oracle.run(_with(inp, smooth_scales_cq=np.ones(inp["dims"].Hcq, dtype=np.float32)))
+    b = oracle.run(_with(inp, smooth_scales_cq=None))
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("wl", [PARTIAL, RAGGED_Q8_SMOOTH], ids=["tiny_partial", "ragged_q8_smooth"])
+def test_power_of_two_smoothing_scales_the_product_exactly(wl):
+    # m = 4 everywhere: c^Q * 4 has the same int8 codes with a 4x scale, so
+    # u is exactly 4x the unsmoothed u (every rounding commutes with 4)
+    inp = synth.make_inputs(wl)
+    d = inp["dims"]
+    four = oracle.run(_with(inp, smooth_scales_cq=np.full(d.Hcq, 4.0, dtype=np.float32)),
+                      intermediates=True, query_int8=False)
+    one = oracle.run(_with(inp, smooth_scales_cq=None), intermediates=True, query_int8=False)
+    assert np.array_equal(four["u"], 4.0 * one["u"])
+    assert np.array_equal(four["c_q"], one["c_q"])
+
+
 def _whole_pins_hold(mutation):
     """All whole-prolog pins above, as one predicate, for the planted mistakes."""
     try:
@@ -403,6 +487,27 @@ def _whole_pins_hold(mutation):
 
 def test_pins_hold_without_planted_mistake():
     assert _whole_pins_hold(0)
+
+
+def _smooth_pins_hold(mutation):
+    try:
+        ok = True
+        for wl in (PARTIAL, RAGGED_Q8_SMOOTH):
+            inp = synth.make_inputs(wl)
+            o = oracle.run(inp, intermediates=True, query_int8=False, mutation=mutation)
+            ok = ok and _smooth_bound_holds(inp, o)
+        return bool(ok)
+    except Exception:
+        return False
+
+
+def test_smooth_pins_hold_without_planted_mistake():
+    assert _smooth_pins_hold(0)
+
+
+@pytest.mark.parametrize("mutation", [6, 7], ids=["smooth_divided", "smooth_ignored"])
+def test_planted_smoothing_mistakes_fail_a_pin(mutation):
+    assert not _smooth_pins_hold(mutation)
 
 
 @pytest.mark.parametrize("mutation", [1, 2, 3, 4, 5],
