@@ -33,23 +33,28 @@ MALL_BYTES = 256 << 20
 def algorithmic(inp, T):
     """Bytes and flops each kernel must move / do at minimum for T tokens."""
     d = inp["dims"]
-    q8 = bool(inp["quant"])
-    eb = 1 if q8 else 2                       # x and the three int8-able weights
+    q8 = bool(inp["quant"])                   # int8 x, W^DQ, W^DkvKr (and W^UqQr)
+    u8 = q8 or bool(inp.get("partial", False))   # int8 W^UqQr and c^Q
+    sm = inp.get("smooth_scales_cq") is not None
+    ed = 1 if q8 else 2                       # bytes of x, W^DQ, W^DkvKr elements
+    eu = 1 if u8 else 2                       # bytes of W^UqQr and c^Q elements
     W = d.N * (d.D + d.Dr)
     Nkr = d.Hckv + d.Dr
     qo = 1 if q8 else 2
-    k1_bytes = d.He * (d.Hcq + Nkr) * eb + T * d.He * eb + (q8 and (d.Hcq + Nkr + T) * 4)
+    k1_bytes = d.He * (d.Hcq + Nkr) * ed + T * d.He * ed + (q8 and (d.Hcq + Nkr + T) * 4)
     k1_flop = 2 * T * d.He * (d.Hcq + Nkr)
-    k2_bytes = T * (d.Hckv + d.Dr) * 2 + T * d.Hcq * (1 if q8 else 2) + T * 2 * d.Dr * 2 + T * 8
-    k3_bytes = (d.Hcq * W * eb + T * d.Hcq * (1 if q8 else 2) + T * d.N * d.D * 2
-                + T * d.N * d.Dr * 2 + T * 2 * d.Dr * 2 + (q8 and W * 4 + T * 4))
+    k2_bytes = (T * (d.Hckv + d.Dr) * 2 + T * d.Hcq * eu + T * 2 * d.Dr * 2 + T * 8
+                + (u8 and T * 4) + (sm and d.Hcq * 4))
+    k3_bytes = (d.Hcq * W * eu + T * d.Hcq * eu + T * d.N * d.D * 2
+                + T * d.N * d.Dr * 2 + T * 2 * d.Dr * 2 + (u8 and W * 4 + T * 4))
     k3_flop = 2 * T * d.Hcq * W
     k4_bytes = d.N * d.D * d.Hckv * 2 + T * d.N * d.D * 2 + T * d.N * d.Hckv * qo + (q8 and T * d.N * 4)
     k4_flop = 2 * T * d.N * d.D * d.Hckv
-    weights = d.He * (d.Hcq + Nkr) * eb + d.Hcq * W * eb + d.N * d.D * d.Hckv * 2
-    step_bytes = (weights + T * d.He * eb + T * 2 * d.Dr * 2 + T * 8 + T * d.N * d.Hckv * qo
+    weights = d.He * (d.Hcq + Nkr) * ed + d.Hcq * W * eu + d.N * d.D * d.Hckv * 2
+    # inputs read once, outputs written once, the scales of the scenario
+    step_bytes = (weights + T * d.He * ed + T * 2 * d.Dr * 2 + T * 8 + T * d.N * d.Hckv * qo
                   + T * d.N * d.Dr * 2 + T * (d.Hckv + d.Dr) * 2
-                  + (q8 and (T + d.Hcq + Nkr + W + T * d.N) * 4))
+                  + (q8 and (T + d.Hcq + Nkr + T * d.N) * 4) + (u8 and W * 4) + (sm and d.Hcq * 4))
     return dict(k1_bytes=k1_bytes, k1_flop=k1_flop, k2_bytes=k2_bytes, k3_bytes=k3_bytes,
                 k3_flop=k3_flop, k4_bytes=k4_bytes, k4_flop=k4_flop, weights=weights,
                 step_bytes=step_bytes, step_flop=k1_flop + k3_flop + k4_flop)
@@ -103,7 +108,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_t32",
                     choices=["decode_t32", "decode_t256", "prefill_t8192", "int8_decode_t128",
-                             "tiny_t4"])
+                             "partial_decode_t32", "tiny_t4"])
     ap.add_argument("--replicas", type=int, default=0, help="weight replicas (0 = enough to "
                     "exceed twice the Infinity Cache)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -220,7 +225,7 @@ def main():
         path = {"bound": "hbm", "achieved": path_ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": path_ach / HBM_PEAK_GBS, "bytes_per_step": alg["step_bytes"]}
     else:
-        peak = INT8_PEAK_TOPS if inp["quant"] else BF16_PEAK_TFLOPS
+        peak = INT8_PEAK_TOPS if (inp["quant"] or inp.get("partial", False)) else BF16_PEAK_TFLOPS
         achieved = alg["k3_flop"] / (k3_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                 "frac": achieved / peak, "traffic": None}
@@ -237,7 +242,8 @@ def main():
         "metric": METRIC, "value": T * args.steps / (ms_total * 1e-3), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int8" if inp["quant"] else "bf16", "data": "synthetic",
+        "dtype": "int8" if inp["quant"] else "bf16+int8" if inp.get("partial", False) else "bf16",
+        "data": "synthetic",
         "config": {"workload": wl.name, "T": T, "He": d.He, "Hcq": d.Hcq, "Hckv": d.Hckv,
                    "N": d.N, "D": d.D, "Dr": d.Dr, "block_num": wl.block_num,
                    "block_size": wl.block_size, "weight_replicas": R,

@@ -32,6 +32,7 @@ MLA_ERR_RUNTIME = 361001
 MLA_ERR_UNSUPPORTED = 561002
 MLA_BF16 = 0
 MLA_INT8 = 1
+MLA_INT8_PARTIAL = 2   # in_dtype only: int8 weightUqQr, every other input bf16
 
 #: the symbols include/mla_prolog.h declares
 EXPORTS = ("mla_prolog_validate", "mla_prolog_workspace_bytes", "mla_prolog_packed_weights_bytes",
@@ -63,7 +64,7 @@ TENSOR_FIELDS = ("token_x", "weight_dq", "weight_uq_qr", "weight_uk", "weight_dk
                  "gamma_cq", "gamma_ckv", "rope_sin", "rope_cos", "cache_index",
                  "kv_cache", "kr_cache", "scale_x", "scale_w_dq", "scale_w_uq_qr",
                  "scale_w_dkv_kr", "query_out", "query_rope_out", "dequant_scale_q_nope",
-                 "packed_weights")
+                 "packed_weights", "smooth_scales_cq")
 
 
 class Tensors(ctypes.Structure):

@@ -238,6 +238,7 @@ struct Ptrs {
   const float* sw_dq;
   const float* sw_uq_qr;
   const float* sw_dkv_kr;
+  const float* smooth_cq;   // smoothScalesCq (Hcq), or NULL (int8 W^UqQr only)
   void* q_out;
   uint16_t* qr_out;
   float* q_scale;
@@ -567,11 +568,14 @@ struct PackGeo {
   int nope_w, uk_w;                               // nope windows per head, W^UK windows per head
 };
 
-PackGeo pack_geo(int64_t He, int64_t Hcq, int64_t Hckv, int64_t N, int64_t D, int64_t Dr, bool i8) {
+// i8d: W^DQ and W^DkvKr are int8 (k-stages of 64 rows, else 32); i8u:
+// W^UqQr is int8.  W^UK is bf16 in every scenario.
+PackGeo pack_geo(int64_t He, int64_t Hcq, int64_t Hckv, int64_t N, int64_t D, int64_t Dr, bool i8d,
+                 bool i8u) {
   PackGeo g;
-  const int ks = i8 ? 64 : 32;
-  g.nst_he = int((He + ks - 1) / ks);
-  g.nst_cq = int((Hcq + ks - 1) / ks);
+  const int ksd = i8d ? 64 : 32, ksu = i8u ? 64 : 32;
+  g.nst_he = int((He + ksd - 1) / ksd);
+  g.nst_cq = int((Hcq + ksu - 1) / ksu);
   g.nst_d = int((D + 31) / 32);
   g.nope_w = int((D + 63) / 64);
   g.uk_w = int((Hckv + 63) / 64);
@@ -589,7 +593,7 @@ PackGeo pack_geo(int64_t He, int64_t Hcq, int64_t Hckv, int64_t N, int64_t D, in
 
 // One 16-byte chunk per thread: (window, stage, column tile, lane) of one
 // matrix, gathered from the row-major source.
-__global__ __launch_bounds__(256) void k_pack(Dims d, Ptrs p, PackGeo g, int i8, uint8_t* out) {
+__global__ __launch_bounds__(256) void k_pack(Dims d, Ptrs p, PackGeo g, int i8d, int i8u, uint8_t* out) {
   const int64_t q = int64_t(blockIdx.x) * 256 + threadIdx.x;
   const int64_t off = q * 16;
   if (off >= g.total) return;
@@ -601,18 +605,18 @@ __global__ __launch_bounds__(256) void k_pack(Dims d, Ptrs p, PackGeo g, int i8,
   if (off < g.off_kr) {
     rel = off - g.off_dq; nst = g.nst_he; win = int(rel / (int64_t(nst) * 4096));
     src = p.w_dq; ld = d.Hcq; K = d.He; col0 = 64 * win; width = min(64, d.Hcq - col0);
-    eb = i8 ? 1 : 2;
+    eb = i8d ? 1 : 2;
   } else if (off < g.off_uq) {
     rel = off - g.off_kr; nst = g.nst_he; win = int(rel / (int64_t(nst) * 4096));
     src = p.w_dkv_kr; ld = d.Hckv + d.Dr; K = d.He; col0 = 64 * win; width = min(64, d.Hckv + d.Dr - col0);
-    eb = i8 ? 1 : 2;
+    eb = i8d ? 1 : 2;
   } else if (off < g.off_uk) {
     rel = off - g.off_uq; nst = g.nst_cq; win = int(rel / (int64_t(nst) * 4096));
     const int h = win / (g.nope_w + 1), part = win % (g.nope_w + 1);
     src = p.w_uq_qr; ld = int64_t(d.N) * (d.D + d.Dr); K = d.Hcq;
     col0 = h * (d.D + d.Dr) + (part < g.nope_w ? 64 * part : d.D);
     width = part < g.nope_w ? min(64, d.D - 64 * part) : d.Dr;
-    eb = i8 ? 1 : 2;
+    eb = i8u ? 1 : 2;
   } else {
     rel = off - g.off_uk; nst = g.nst_d; win = int(rel / (int64_t(nst) * 4096));
     const int h = win / g.uk_w, part = win % g.uk_w;
@@ -728,14 +732,17 @@ __global__ __launch_bounds__(64 * NW) void k1_packed(Dims d, Ptrs p, PackGeo pg,
 }
 
 // K2: NWT waves per token, TPB tokens per block.  y is the split-order sum
-// of the token's S partials of x [W^DQ | W^DkvKr] (in double; in int8 mode
-// the exact int32 sum times the token and column scales).  A first pass sums
-// the squares of the c^Q and c^KV parts (and, in int8 mode, finds the
-// largest |gamma y| of the c^Q part), keeping each lane's first CPL 8-column
-// chunks of y in registers; a second pass writes c^Q (bf16, or per-token
-// int8 + scale), the c^KV row at the token's cacheIndex slot and, through a
-// small LDS row, the RoPE'd k^R row, reloading only the chunks beyond CPL.  The norms are computed in
-// double, so the per-token int8 decision of c^Q sees c rounded once to fp32.
+// of the token's S partials of x [W^DQ | W^DkvKr] (in double; with int8
+// down-projection inputs, I8D, the exact int32 sum times the token and
+// column scales).  A first pass sums the squares of the c^Q and c^KV parts
+// (and, for an int8 c^Q, I8U, finds the largest |gamma m y| of the c^Q part,
+// m the optional smoothScalesCq), keeping each lane's first CPL 8-column
+// chunks of y in registers; a second pass writes c^Q (bf16, or the
+// per-token int8 of c^Q * m + scale), the c^KV row at the token's cacheIndex
+// slot and, through a small LDS row, the RoPE'd k^R row, reloading only the
+// chunks beyond CPL.  The norms are computed in double, so the per-token
+// int8 decision of c^Q sees c rounded once to fp32; c^Q * m is formed as
+// (gamma m) y / rms, gamma m being exact in double.
 // With cq_nst > 0, c^Q is stored fragment-packed (cq_nst k-stages per
 // 16-token tile, the k padding as zeros); with 0, row-major.
 __device__ __forceinline__ double wave_sum_f64(double v) {
@@ -747,7 +754,7 @@ __device__ __forceinline__ double wave_max_f64(double v) {
   return v;
 }
 
-template <bool I8, int NWT, int TPB, int CPL>
+template <bool I8D, bool I8U, int NWT, int TPB, int CPL>
 __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S, int cq_nst) {
   __shared__ double red[NWT * TPB][3];
   __shared__ double ry[TPB][64];   // the token's y of the k^R columns (Dr <= 64)
@@ -759,7 +766,7 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
   const int Ntot = d.Hcq + d.Hckv + d.Dr;
   const int cq_c = d.Hcq / 8, kv_c = d.Hckv / 8, chunks = cq_c + kv_c + d.Dr / 8;
   const rsrc_t P = make_rsrc(p.part, int64_t(S) * d.T * Ntot * 4);
-  const double sx = (I8 && active) ? double(p.sx[t]) : 1.0;
+  const double sx = (I8D && active) ? double(p.sx[t]) : 1.0;
   // y of the eight columns 8j .. 8j+7; the loads of eight splits at a time
   // are issued together (a missing split reads as zeros, an exact no-op)
   auto y8 = [&](int j, double (&v)[8]) {
@@ -774,7 +781,7 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
       const uint32_t v8[8] = {a2.x, a2.y, a2.z, a2.w, b2.x, b2.y, b2.z, b2.w};
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        if constexpr (I8) iv[c] = int32_t(w8[c]) + int32_t(v8[c]);
+        if constexpr (I8D) iv[c] = int32_t(w8[c]) + int32_t(v8[c]);
         else f[c] = double(__uint_as_float(w8[c])) + double(__uint_as_float(v8[c]));
       }
     }
@@ -792,14 +799,14 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
                                 r[2 * e + 1].x, r[2 * e + 1].y, r[2 * e + 1].z, r[2 * e + 1].w};
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          if constexpr (I8) iv[c] += int32_t(w8[c]);
+          if constexpr (I8D) iv[c] += int32_t(w8[c]);
           else f[c] += double(__uint_as_float(w8[c]));
         }
       }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      if constexpr (I8) {
+      if constexpr (I8D) {
         const int n = 8 * j + e;
         const double sw = n < d.Hcq ? p.sw_dq[n] : p.sw_dkv_kr[n - d.Hcq];
         v[e] = double(iv[e]) * sx * sw;
@@ -809,13 +816,19 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
     }
   };
 
+  // the c^Q weight: gamma, times smoothScalesCq for an int8 c^Q when given
+  auto gq = [&](int n) {
+    const double g = double(bf2f(p.gamma_cq[n]));
+    if constexpr (I8U) return p.smooth_cq ? g * double(p.smooth_cq[n]) : g;
+    return g;
+  };
   double sq = 0.0, skv = 0.0, gmax = 0.0;
   auto sums = [&](int j, const double (&v)[8]) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       if (j < cq_c) {
         sq += v[e] * v[e];
-        if constexpr (I8) gmax = fmax(gmax, fabs(double(bf2f(p.gamma_cq[8 * j + e])) * v[e]));
+        if constexpr (I8U) gmax = fmax(gmax, fabs(gq(8 * j + e) * v[e]));
       } else if (j < cq_c + kv_c) {
         skv += v[e] * v[e];
       }
@@ -852,13 +865,13 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
   const double rms_q = sqrt(sq / double(d.Hcq) + d.eps_cq);
   const double rms_kv = sqrt(skv / double(d.Hckv) + d.eps_ckv);
   float sc = 0.0f;
-  if constexpr (I8) sc = float(gmax / rms_q) / 127.0f;
+  if constexpr (I8U) sc = float(gmax / rms_q) / 127.0f;
   const int64_t slot = p.cache_index[t];
   const bool cache = slot >= 0 && slot < d.slots;
   const int64_t tile = int64_t(cq_nst) * 1024;
 
   auto store_cq = [&](int j, const float (&c)[8]) {
-    if constexpr (I8) {
+    if constexpr (I8U) {
       uint32_t lo = 0, hi = 0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -878,7 +891,7 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
     float c[8];
     if (j < cq_c) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) c[e] = float(double(bf2f(p.gamma_cq[8 * j + e])) * v[e] / rms_q);
+      for (int e = 0; e < 8; ++e) c[e] = float(gq(8 * j + e) * v[e] / rms_q);
       store_cq(j, c);
     } else if (j >= cq_c + kv_c) {
 #pragma unroll
@@ -903,12 +916,12 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
     emit(j, v);
   }
   // the zero k padding of packed c^Q
-  const int cq_chunks = cq_nst ? cq_nst * (I8 ? 8 : 4) : cq_c;
+  const int cq_chunks = cq_nst ? cq_nst * (I8U ? 8 : 4) : cq_c;
   for (int j = cq_c + lane; j < cq_chunks; j += L) {
     const float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     store_cq(j, z);
   }
-  if (I8 && lane == 0) p.cq_scale[t] = sc;
+  if (I8U && lane == 0) p.cq_scale[t] = sc;
   if (!cache) return;   // the same for every wave of the token
   if constexpr (NWT > 1) {
     __syncthreads();
@@ -2758,6 +2771,14 @@ struct Plan {
 
 int ceil_div(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
 
+// int8 down-projection operands (x, W^DQ, W^DkvKr): full quantisation only;
+// int8 W^UqQr (and an int8 c^Q): full and partial quantisation
+bool down_i8(const mla_prolog_desc& d) { return d.in_dtype == MLA_INT8; }
+bool up_i8(const mla_prolog_desc& d) { return d.in_dtype == MLA_INT8 || d.in_dtype == MLA_INT8_PARTIAL; }
+PackGeo geo_of(const mla_prolog_desc& d) {
+  return pack_geo(d.He, d.Hcq, d.Hckv, d.N, d.D, d.Dr, down_i8(d), up_i8(d));
+}
+
 int mt_for(int64_t T, int cap) {
   int mt = 1;
   while (mt < cap && 16 * mt < T) mt *= 2;
@@ -2766,11 +2787,11 @@ int mt_for(int64_t T, int cap) {
 
 Plan make_plan(const mla_prolog_desc& d, int64_t T) {
   Plan pl;
-  const bool i8 = d.in_dtype == MLA_INT8;
+  const bool i8 = down_i8(d);
   pl.packed = false;
   pl.stream = T <= kStreamMaxT;
   {
-    const PackGeo g = pack_geo(d.He, d.Hcq, d.Hckv, d.N, d.D, d.Dr, i8);
+    const PackGeo g = geo_of(d);
     const int ptiles = g.win_dq + g.win_kr;
     int Sp = std::max(1, std::min(g.nst_he, (512 + ptiles / 2) / ptiles));
     pl.sps = ceil_div(g.nst_he, Sp);
@@ -2822,23 +2843,25 @@ struct TiledPlan {
 
 TiledPlan tiled_plan(const mla_prolog_desc& d, int64_t T) {
   TiledPlan tp;
-  const PackGeo g = pack_geo(d.He, d.Hcq, d.Hckv, d.N, d.D, d.Dr, d.in_dtype == MLA_INT8);
+  const PackGeo g = geo_of(d);
   const int tiles = g.win_dq + g.win_kr;
   tp.large = T >= kTiledLargeT;
   tp.mt = T <= 64 ? 4 : 8;
-  // medium shapes: LDS-staged blocks above 128 tokens; for int8 inputs also
-  // from 65 tokens on, in 128-token blocks (the int8 k-stages are twice as deep)
-  const bool i8 = d.in_dtype == MLA_INT8;
-  tp.k1v = tp.k3v = T > 128 ? 1 : (i8 && T > 64) ? 2 : 0;
+  // medium shapes: LDS-staged blocks above 128 tokens; for an int8 product
+  // also from 65 tokens on, in 128-token blocks (the int8 k-stages are twice
+  // as deep)
+  tp.k1v = T > 128 ? 1 : (down_i8(d) && T > 64) ? 2 : 0;
+  tp.k3v = T > 128 ? 1 : (up_i8(d) && T > 64) ? 2 : 0;
   if (tp.large) {
     tp.m1 = ceil_div(T, 256); tp.ngrp1 = ceil_div(tiles, 4);      // LDS-staged 256 x 256
     tp.m3 = ceil_div(T, 256); tp.ngrp3 = ceil_div(g.win_uq, 4);
     tp.m4 = ceil_div(T, 256); tp.cg4 = ceil_div(g.uk_w, 4);      // LDS-staged 256 x 256
   } else {
-    const int bm = tp.k1v == 1 ? 256 : 128;                                         // LDS-staged block rows
-    if (tp.k1v) { tp.m1 = ceil_div(T, bm); tp.ngrp1 = ceil_div(tiles, 2); }
+    // LDS-staged block rows
+    const int bm1 = tp.k1v == 1 ? 256 : 128, bm3 = tp.k3v == 1 ? 256 : 128;
+    if (tp.k1v) { tp.m1 = ceil_div(T, bm1); tp.ngrp1 = ceil_div(tiles, 2); }
     else { tp.m1 = ceil_div(T, 16 * tp.mt); tp.ngrp1 = tiles; }
-    if (tp.k3v) { tp.m3 = ceil_div(T, bm); tp.ngrp3 = ceil_div(g.win_uq, 2); }
+    if (tp.k3v) { tp.m3 = ceil_div(T, bm3); tp.ngrp3 = ceil_div(g.win_uq, 2); }
     else { tp.m3 = ceil_div(T, 64); tp.ngrp3 = g.win_uq; }                            // 64-token waves
     tp.m4 = ceil_div(T, 16 * tp.mt); tp.cg4 = ceil_div(g.uk_w, 8);
   }
@@ -2871,7 +2894,7 @@ Layout layout(const mla_prolog_desc& d) {
   }
   // c^Q and q^C are row-major on the row-major-weight path and
   // fragment-packed (16-token tiles of 1 KB k-stages) on the packed path
-  const PackGeo g = pack_geo(d.He, d.Hcq, d.Hckv, d.N, d.D, d.Dr, d.in_dtype == MLA_INT8);
+  const PackGeo g = geo_of(d);
   const size_t tiles = size_t((d.max_tokens + 15) / 16);
   const size_t cq_bytes = std::max(size_t(d.max_tokens) * d.Hcq * 2, tiles * g.nst_cq * 1024);
   const size_t qc_bytes = std::max(size_t(d.max_tokens) * d.N * d.D * 2, tiles * d.N * g.nst_d * 1024);
@@ -2903,7 +2926,7 @@ mla_status check_desc(const mla_prolog_desc* d) {
     if (v <= 0 || v > (1 << 20)) return MLA_ERR_PARAM_INVALID;
   // the page's dtype table has an int8 queryOut only in the int8
   // full-quantisation scenario
-  if ((d->in_dtype != MLA_BF16 && d->in_dtype != MLA_INT8) ||
+  if ((d->in_dtype != MLA_BF16 && d->in_dtype != MLA_INT8 && d->in_dtype != MLA_INT8_PARTIAL) ||
       (d->query_dtype != MLA_BF16 && d->query_dtype != MLA_INT8))
     return MLA_ERR_PARAM_INVALID;
   if (d->query_dtype == MLA_INT8 && d->in_dtype != MLA_INT8) return MLA_ERR_PARAM_INVALID;
@@ -2922,6 +2945,8 @@ mla_status check_desc(const mla_prolog_desc* d) {
   // row or column-block end
   if (d->in_dtype == MLA_INT8 &&
       (d->He % 16 || d->Hcq % 16 || (d->Hckv + d->Dr) % 16 || d->D % 16 || d->Dr % 16))
+    return MLA_ERR_UNSUPPORTED;
+  if (d->in_dtype == MLA_INT8_PARTIAL && (d->Hcq % 16 || d->D % 16 || d->Dr % 16))
     return MLA_ERR_UNSUPPORTED;
   if (d->N * (d->D + d->Dr) > (1 << 24)) return MLA_ERR_UNSUPPORTED;
   // the norm kernel addresses the split partials with 32-bit offsets
@@ -2945,12 +2970,17 @@ mla_status check_tensors(const mla_prolog_desc* d, const mla_prolog_tensors* t, 
     if (!t->kv_cache || !t->kr_cache) return MLA_ERR_NULLPTR;
     if (!aligned16(t->kv_cache) || !aligned16(t->kr_cache)) return MLA_ERR_PARAM_INVALID;
   }
+  // the scales each scenario takes: all four in full quantisation, that of
+  // weightUqQr alone in partial quantisation, none without quantisation
   const float* sc[] = {t->scale_x, t->scale_w_dq, t->scale_w_uq_qr, t->scale_w_dkv_kr};
-  for (const float* q : sc) {
-    if (d->in_dtype == MLA_INT8 && !q) return MLA_ERR_NULLPTR;
-    if (d->in_dtype == MLA_BF16 && q) return MLA_ERR_PARAM_INVALID;
-    if (q && !aligned4(q)) return MLA_ERR_PARAM_INVALID;
+  const bool need[] = {down_i8(*d), down_i8(*d), up_i8(*d), down_i8(*d)};
+  for (int i = 0; i < 4; ++i) {
+    if (need[i] && !sc[i]) return MLA_ERR_NULLPTR;
+    if (!need[i] && sc[i]) return MLA_ERR_PARAM_INVALID;
+    if (sc[i] && !aligned4(sc[i])) return MLA_ERR_PARAM_INVALID;
   }
+  // smoothScalesCq: optional with an int8 weightUqQr, absent otherwise
+  if (t->smooth_scales_cq && (!up_i8(*d) || !aligned4(t->smooth_scales_cq))) return MLA_ERR_PARAM_INVALID;
   if (t->packed_weights && (reinterpret_cast<uintptr_t>(t->packed_weights) & 255u))
     return MLA_ERR_PARAM_INVALID;
   if (d->query_dtype == MLA_INT8 && !t->dequant_scale_q_nope) return MLA_ERR_NULLPTR;
@@ -3010,10 +3040,10 @@ void launch_k4(int ntw, dim3 grid, hipStream_t s, const Dims& d, const Ptrs& p) 
 }
 
 // K2 with eight waves per token when there are few tokens, one otherwise.
-template <bool I8>
+template <bool I8D, bool I8U>
 void launch_norm(hipStream_t s, const Dims& d, const Ptrs& p, int S, int cq_nst) {
-  if (d.T <= 512) k2_norm<I8, 8, 1, 1><<<dim3(d.T), 512, 0, s>>>(d, p, S, cq_nst);
-  else k2_norm<I8, 1, 4, 1><<<dim3((d.T + 3) / 4), 256, 0, s>>>(d, p, S, cq_nst);
+  if (d.T <= 512) k2_norm<I8D, I8U, 8, 1, 1><<<dim3(d.T), 512, 0, s>>>(d, p, S, cq_nst);
+  else k2_norm<I8D, I8U, 1, 4, 1><<<dim3((d.T + 3) / 4), 256, 0, s>>>(d, p, S, cq_nst);
 }
 
 // The int8-query W^UK kernel gives one wave to each 64-column window of Hckv.
@@ -3021,14 +3051,16 @@ bool packed_fits(const mla_prolog_desc& dd) { return (dd.Hckv + 63) / 64 <= 8; }
 
 // Small-T run on packed weights: K1p (down-projection, split partials), K2
 // (norms, c^Q, caches), K3p (up-projection, q-RoPE, q^C), K4p (W^UK).
-// Profiling marks follow the kernels.
-template <bool I8, int MT, class Mark>
+// Profiling marks follow the kernels.  I8D: int8 down-projection operands;
+// I8U: int8 c^Q and W^UqQr.
+template <bool I8D, bool I8U, int MT, class Mark>
 void packed_launch(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g,
                    bool q8, Mark& mark) {
+  constexpr bool I8 = I8U;   // the up-projection kernels below
   const int tiles = g.win_dq + g.win_kr;
-  k1_packed<I8, MT, 4, 2><<<dim3(tiles * pl.Sp), 256, 0, s>>>(d, p, g, pl.Sp, pl.sps);
+  k1_packed<I8D, MT, 4, 2><<<dim3(tiles * pl.Sp), 256, 0, s>>>(d, p, g, pl.Sp, pl.sps);
   mark(1);
-  launch_norm<I8>(s, d, p, pl.Sp, g.nst_cq);
+  launch_norm<I8D, I8U>(s, d, p, pl.Sp, g.nst_cq);
   mark(2);
   if (g.nope_w == 2 && d.Dr == 64 && g.uk_w <= 8) {
     // two balanced blocks per head; the profile books both products to the first
@@ -3058,7 +3090,7 @@ void packed_launch(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p, 
 // outside what the kernel holds in registers.
 bool fused_geo(const mla_prolog_desc& dd, FusedGeo* fg) {
   if (dd.in_dtype != MLA_BF16 || dd.query_dtype != MLA_BF16) return false;
-  const PackGeo g = pack_geo(dd.He, dd.Hcq, dd.Hckv, dd.N, dd.D, dd.Dr, false);
+  const PackGeo g = geo_of(dd);
   if (g.nope_w != 2 || dd.Dr != 64 || g.uk_w > 8 || g.nst_d > 4) return false;
   const int G = int(2 * dd.N), W = g.win_dq + g.win_kr;
   if (G < W || (g.nst_cq + 6) / 7 > kFusedStages) return false;
@@ -3079,35 +3111,38 @@ bool fused_geo(const mla_prolog_desc& dd, FusedGeo* fg) {
   return true;
 }
 
+template <int MT, class Mark>
+void packed_launch_mt(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g,
+                      bool i8d, bool i8u, bool q8, Mark& mark) {
+  if (i8d) packed_launch<true, true, MT>(pl, s, d, p, g, q8, mark);
+  else if (i8u) packed_launch<false, true, MT>(pl, s, d, p, g, q8, mark);
+  else packed_launch<false, false, MT>(pl, s, d, p, g, q8, mark);
+}
+
 template <class Mark>
 void launch_packed(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p,
-                   const mla_prolog_desc& dd, bool i8, bool q8, Mark& mark) {
-  const PackGeo g = pack_geo(dd.He, dd.Hcq, dd.Hckv, dd.N, dd.D, dd.Dr, i8);
-  if (pl.mt1 == 1) {
-    if (i8) packed_launch<true, 1>(pl, s, d, p, g, q8, mark);
-    else packed_launch<false, 1>(pl, s, d, p, g, q8, mark);
-  } else {
-    if (i8) packed_launch<true, 2>(pl, s, d, p, g, q8, mark);
-    else packed_launch<false, 2>(pl, s, d, p, g, q8, mark);
-  }
+                   const mla_prolog_desc& dd, bool q8, Mark& mark) {
+  const PackGeo g = geo_of(dd);
+  if (pl.mt1 == 1) packed_launch_mt<1>(pl, s, d, p, g, down_i8(dd), up_i8(dd), q8, mark);
+  else packed_launch_mt<2>(pl, s, d, p, g, down_i8(dd), up_i8(dd), q8, mark);
 }
 
 // Tiled run on packed weights (token counts above the streaming range).
-template <bool I8, int MT, class Mark>
+template <bool I8D, bool I8U, int MT, class Mark>
 void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g,
                   bool q8, Mark& mark) {
   const dim3 g1(tp.m1 * tp.ngrp1 * tp.S), g3(tp.m3 * tp.ngrp3);
   if (tp.k1v == 1)
-    k1_tiled<I8, 4, 1, 4, 2, 2, true, false, 2, 1, true><<<g1, 512, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
-  else if (I8 && tp.k1v == 2)
-    k1_tiled<I8, 2, 1, 4, 2, 2, true, false, 2, 1, true><<<g1, 512, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
-  else k1_tiled<I8, MT, 1, 1, 1, 2><<<g1, 64, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
+    k1_tiled<I8D, 4, 1, 4, 2, 2, true, false, 2, 1, true><<<g1, 512, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
+  else if (I8D && tp.k1v == 2)
+    k1_tiled<I8D, 2, 1, 4, 2, 2, true, false, 2, 1, true><<<g1, 512, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
+  else k1_tiled<I8D, MT, 1, 1, 1, 2><<<g1, 64, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
   mark(1);
-  launch_norm<I8>(s, d, p, tp.S, g.nst_cq);
+  launch_norm<I8D, I8U>(s, d, p, tp.S, g.nst_cq);
   mark(2);
-  if (tp.k3v == 1) k3_tiled<I8, 2, 1, 8, 2, 2, true, 2, 1, true><<<g3, 1024, 0, s>>>(d, p, g, tp.m3);
-  else if (I8 && tp.k3v == 2) k3_tiled<I8, 1, 1, 8, 2, 2, true, 1, 1, true><<<g3, 1024, 0, s>>>(d, p, g, tp.m3);
-  else k3_tiled<I8, 4, 1, 1, 1, 2><<<g3, 64, 0, s>>>(d, p, g, tp.m3);
+  if (tp.k3v == 1) k3_tiled<I8U, 2, 1, 8, 2, 2, true, 2, 1, true><<<g3, 1024, 0, s>>>(d, p, g, tp.m3);
+  else if (I8U && tp.k3v == 2) k3_tiled<I8U, 1, 1, 8, 2, 2, true, 1, 1, true><<<g3, 1024, 0, s>>>(d, p, g, tp.m3);
+  else k3_tiled<I8U, 4, 1, 1, 1, 2><<<g3, 64, 0, s>>>(d, p, g, tp.m3);
   mark(3);
   if (q8) k4_tiled<4, 1, 1, 8, 2, true, false, true><<<dim3(tp.m4q * d.N), 512, 0, s>>>(d, p, g, tp.m4q, 1);
   else k4_tiled<MT, 1, 1, 8, 2, false, false, true><<<dim3(tp.m4 * tp.cg4 * d.N), 512, 0, s>>>(d, p, g, tp.m4,
@@ -3115,15 +3150,15 @@ void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs&
   mark(4);
 }
 
-template <bool I8, class Mark>
+template <bool I8D, bool I8U, class Mark>
 void tiled_large(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g,
                  bool q8, Mark& mark) {
-  k1_tiled<I8, 4, 1, 4, 4, 2, true><<<dim3(tp.m1 * tp.ngrp1 * tp.S), 1024, 0, s>>>(d, p, g, tp.sps,
-                                                                                  tp.m1, tp.ngrp1);
+  k1_tiled<I8D, 4, 1, 4, 4, 2, true><<<dim3(tp.m1 * tp.ngrp1 * tp.S), 1024, 0, s>>>(d, p, g, tp.sps,
+                                                                                   tp.m1, tp.ngrp1);
   mark(1);
-  launch_norm<I8>(s, d, p, tp.S, g.nst_cq);
+  launch_norm<I8D, I8U>(s, d, p, tp.S, g.nst_cq);
   mark(2);
-  k3_tiled<I8, 4, 1, 4, 4, 2, true><<<dim3(tp.m3 * tp.ngrp3), 1024, 0, s>>>(d, p, g, tp.m3);
+  k3_tiled<I8U, 4, 1, 4, 4, 2, true><<<dim3(tp.m3 * tp.ngrp3), 1024, 0, s>>>(d, p, g, tp.m3);
   mark(3);
   if (q8) k4_tiled<4, 1, 1, 8, 2, true, false, true><<<dim3(tp.m4q * d.N), 512, 0, s>>>(d, p, g, tp.m4q, 1);
   else k4_tiled<4, 1, 4, 4, 2, false, true, true><<<dim3(tp.m4 * tp.cg4 * d.N), 1024, 0, s>>>(d, p, g, tp.m4,
@@ -3131,21 +3166,22 @@ void tiled_large(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs& 
   mark(4);
 }
 
+template <bool I8D, bool I8U, class Mark>
+void tiled_run(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g,
+               bool q8, Mark& mark) {
+  if (tp.large) tiled_large<I8D, I8U>(tp, s, d, p, g, q8, mark);
+  else if (tp.mt == 4) tiled_medium<I8D, I8U, 4>(tp, s, d, p, g, q8, mark);
+  else tiled_medium<I8D, I8U, 8>(tp, s, d, p, g, q8, mark);
+}
+
 template <class Mark>
-void launch_tiled(hipStream_t s, const Dims& d, const Ptrs& p, const mla_prolog_desc& dd, bool i8,
-                  bool q8, Mark& mark) {
-  const PackGeo g = pack_geo(dd.He, dd.Hcq, dd.Hckv, dd.N, dd.D, dd.Dr, i8);
+void launch_tiled(hipStream_t s, const Dims& d, const Ptrs& p, const mla_prolog_desc& dd, bool q8,
+                  Mark& mark) {
+  const PackGeo g = geo_of(dd);
   const TiledPlan tp = tiled_plan(dd, d.T);
-  if (tp.large) {
-    if (i8) tiled_large<true>(tp, s, d, p, g, q8, mark);
-    else tiled_large<false>(tp, s, d, p, g, q8, mark);
-  } else if (tp.mt == 4) {
-    if (i8) tiled_medium<true, 4>(tp, s, d, p, g, q8, mark);
-    else tiled_medium<false, 4>(tp, s, d, p, g, q8, mark);
-  } else {
-    if (i8) tiled_medium<true, 8>(tp, s, d, p, g, q8, mark);
-    else tiled_medium<false, 8>(tp, s, d, p, g, q8, mark);
-  }
+  if (down_i8(dd)) tiled_run<true, true>(tp, s, d, p, g, q8, mark);
+  else if (up_i8(dd)) tiled_run<false, true>(tp, s, d, p, g, q8, mark);
+  else tiled_run<false, false>(tp, s, d, p, g, q8, mark);
 }
 
 }  // namespace
@@ -3166,8 +3202,7 @@ size_t mla_prolog_workspace_bytes(const mla_prolog_desc* desc) {
 
 size_t mla_prolog_packed_weights_bytes(const mla_prolog_desc* desc) {
   if (check_desc(desc) != MLA_OK) return 0;
-  return size_t(pack_geo(desc->He, desc->Hcq, desc->Hckv, desc->N, desc->D, desc->Dr,
-                         desc->in_dtype == MLA_INT8).total);
+  return size_t(geo_of(*desc).total);
 }
 
 mla_status mla_prolog_pack_weights(mla_prolog_t h, const mla_prolog_tensors* t, void* packed,
@@ -3180,7 +3215,7 @@ mla_status mla_prolog_pack_weights(mla_prolog_t h, const mla_prolog_tensors* t, 
   for (const void* q : w)
     if (!aligned16(q)) return MLA_ERR_PARAM_INVALID;
   if (reinterpret_cast<uintptr_t>(packed) & 255u) return MLA_ERR_PARAM_INVALID;
-  const PackGeo g = pack_geo(dd.He, dd.Hcq, dd.Hckv, dd.N, dd.D, dd.Dr, dd.in_dtype == MLA_INT8);
+  const PackGeo g = geo_of(dd);
   if (g.total >= int64_t(kOOB)) return MLA_ERR_UNSUPPORTED;
   int prev = 0;
   if (hipGetDevice(&prev) != hipSuccess) return MLA_ERR_RUNTIME;
@@ -3197,7 +3232,7 @@ mla_status mla_prolog_pack_weights(mla_prolog_t h, const mla_prolog_tensors* t, 
   p.w_dkv_kr = static_cast<const uint8_t*>(t->weight_dkv_kr);
   const int64_t chunks = g.total / 16;
   k_pack<<<dim3(unsigned((chunks + 255) / 256)), 256, 0, static_cast<hipStream_t>(stream)>>>(
-      d, p, g, dd.in_dtype == MLA_INT8, static_cast<uint8_t*>(packed));
+      d, p, g, int(down_i8(dd)), int(up_i8(dd)), static_cast<uint8_t*>(packed));
   const hipError_t e = hipGetLastError();
   if (prev != dd.device) (void)hipSetDevice(prev);
   return e == hipSuccess ? MLA_OK : MLA_ERR_RUNTIME;
@@ -3277,7 +3312,7 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   if (prev != dd.device && hipSetDevice(dd.device) != hipSuccess) return MLA_ERR_RUNTIME;
   (void)hipGetLastError();
 
-  const bool i8 = dd.in_dtype == MLA_INT8, q8 = dd.query_dtype == MLA_INT8;
+  const bool i8d = down_i8(dd), i8u = up_i8(dd), q8 = dd.query_dtype == MLA_INT8;
   const Plan pl = make_plan(dd, T);
   Dims d;
   d.T = int(T); d.He = int(dd.He); d.Hcq = int(dd.Hcq); d.Hckv = int(dd.Hckv); d.N = int(dd.N);
@@ -3299,6 +3334,7 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   p.kr_cache = static_cast<uint16_t*>(t->kr_cache);
   p.sx = t->scale_x; p.sw_dq = t->scale_w_dq; p.sw_uq_qr = t->scale_w_uq_qr;
   p.sw_dkv_kr = t->scale_w_dkv_kr;
+  p.smooth_cq = t->smooth_scales_cq;
   p.q_out = t->query_out;
   p.qr_out = static_cast<uint16_t*>(t->query_rope_out);
   p.q_scale = t->dequant_scale_q_nope;
@@ -3338,7 +3374,7 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   if (p.packed && pl.stream && h->fused_fit[pl.mt1 == 1 ? 0 : 1] && fused_geo(dd, &fg)) {
     fg.run = ++h->fused_run;
     fg.spin = h->fused_spin;
-    const PackGeo g = pack_geo(dd.He, dd.Hcq, dd.Hckv, dd.N, dd.D, dd.Dr, false);
+    const PackGeo g = geo_of(dd);
     if (pl.mt1 == 1) k_fused<1><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g, fg);
     else k_fused<2><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g, fg);
     mark(-2);
@@ -3348,8 +3384,8 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
     return e == hipSuccess ? MLA_OK : MLA_ERR_RUNTIME;
   }
   if (p.packed && (!pl.stream || packed_fits(dd))) {
-    if (pl.stream) launch_packed(pl, s, d, p, dd, i8, q8, mark);
-    else launch_tiled(s, d, p, dd, i8, q8, mark);
+    if (pl.stream) launch_packed(pl, s, d, p, dd, q8, mark);
+    else launch_tiled(s, d, p, dd, q8, mark);
     const hipError_t e = hipGetLastError();
     if (prev != dd.device) (void)hipSetDevice(prev);
     return e == hipSuccess ? MLA_OK : MLA_ERR_RUNTIME;
@@ -3357,17 +3393,18 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   const int tiles_q = ceil_div(d.Hcq, 64);
   const int tiles_kr = ceil_div(d.Hckv + d.Dr, 64);
   dim3 g1(tiles_q + tiles_kr, pl.S, ceil_div(T, 16 * pl.mt1));
-  if (i8) launch_k1<true>(pl.mt1, g1, s, d, p, tiles_q, pl.kps);
+  if (i8d) launch_k1<true>(pl.mt1, g1, s, d, p, tiles_q, pl.kps);
   else launch_k1<false>(pl.mt1, g1, s, d, p, tiles_q, pl.kps);
   mark(1);
 
-  if (i8) launch_norm<true>(s, d, p, pl.S, 0);
-  else launch_norm<false>(s, d, p, pl.S, 0);
+  if (i8d) launch_norm<true, true>(s, d, p, pl.S, 0);
+  else if (i8u) launch_norm<false, true>(s, d, p, pl.S, 0);
+  else launch_norm<false, false>(s, d, p, pl.S, 0);
   mark(2);
 
   const int nope_tiles = ceil_div(d.D, 64);
   dim3 g3(d.N * (nope_tiles + 1), 1, ceil_div(T, 16 * pl.mt3));
-  if (i8) launch_k3<true>(pl.mt3, g3, s, d, p, nope_tiles);
+  if (i8u) launch_k3<true>(pl.mt3, g3, s, d, p, nope_tiles);
   else launch_k3<false>(pl.mt3, g3, s, d, p, nope_tiles);
   mark(3);
 
@@ -3460,9 +3497,7 @@ mla_status mla_prolog_check(mla_prolog_t h) {
   if (hipGetDevice(&prev) != hipSuccess || hipSetDevice(h->desc.device) != hipSuccess)
     return MLA_ERR_RUNTIME;
   // the paired kernel's error word follows its 4N exchange flags; the fused
-  // kernel's follows its window counters and done counter
-  const PackGeo g = pack_geo(h->desc.He, h->desc.Hcq, h->desc.Hckv, h->desc.N, h->desc.D, h->desc.Dr,
-                             h->desc.in_dtype == MLA_INT8);
+  // kernel's follows its 2N block flags
   uint32_t* words[2] = {reinterpret_cast<uint32_t*>(h->ws + h->lay.xflag) + 4 * h->desc.N,
                         reinterpret_cast<uint32_t*>(h->ws + h->lay.fcnt) + 2 * h->desc.N * kFusedFlagStride};
   mla_status st = hipDeviceSynchronize() == hipSuccess ? MLA_OK : MLA_ERR_RUNTIME;

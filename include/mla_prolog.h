@@ -42,7 +42,7 @@ typedef enum {
   MLA_ERR_UNSUPPORTED = 561002    /* legal on the page but no kernel tiling for it here */
 } mla_status;
 
-typedef enum { MLA_BF16 = 0, MLA_INT8 = 1 } mla_dtype;
+typedef enum { MLA_BF16 = 0, MLA_INT8 = 1, MLA_INT8_PARTIAL = 2 } mla_dtype;
 
 /*
  * Problem description, fixed at create time (the page's "Shape format field
@@ -59,6 +59,14 @@ typedef enum { MLA_BF16 = 0, MLA_INT8 = 1 } mla_dtype;
  *   gammas, sin/cos and both caches bf16.  The RmsNorm output c^Q is
  *   quantised per token (scale RowMax(|c^Q|)/127) before the int8 W^UqQr
  *   product.
+ * in_dtype MLA_INT8_PARTIAL: the partial-quantisation scenario with a bf16
+ *   cache (same tables): weightUqQr int8 with its per-output-channel fp32
+ *   scale, every other tensor bf16; c^Q is quantised per token as above.
+ *   In both int8 scenarios the optional smoothScalesCq m (Hcq, fp32)
+ *   multiplies c^Q element-wise before that quantisation (scale
+ *   RowMax(|c^Q * m|)/127); the product is not divided back by m, so the
+ *   int8 weightUqQr is expected to carry 1/m.  Only in_dtype takes this
+ *   value.
  * query_dtype MLA_INT8: queryOut is int8 with one fp32 dequantisation scale
  *   per (token, head), RowMax(|q^N|)/127 ("Dequant Scale Query Nope
  *   calculation formula"); MLA_BF16: queryOut is bf16.  As in the page's
@@ -96,7 +104,9 @@ typedef struct {
  *                                       slots only; may be NULL iff block_num
  *                                       is 0 (no cache update)
  *   scale_x (T), scale_w_dq (Hcq), scale_w_uq_qr (N*(D+Dr)),
- *   scale_w_dkv_kr (Hckv+Dr)            fp32, int8 mode only, else NULL
+ *   scale_w_dkv_kr (Hckv+Dr)            fp32, int8 mode only, else NULL;
+ *                                       partial quantisation takes
+ *                                       scale_w_uq_qr alone
  *   query_out        (T, N, Hckv)       bf16, or int8 when query_dtype is INT8
  *   query_rope_out   (T, N, Dr)         bf16
  *   dequant_scale_q_nope (T, N)         fp32 when query_dtype is INT8, else NULL
@@ -106,6 +116,9 @@ typedef struct {
  *                                       given, small-T runs (T <= 32) stream
  *                                       the weights from it; the row-major
  *                                       weights stay required.
+ *   smooth_scales_cq (Hcq)              fp32 smoothScalesCq, optional (NULL =
+ *                                       none) with an int8 weightUqQr, NULL
+ *                                       otherwise
  * Outputs must not alias inputs.
  */
 typedef struct {
@@ -129,6 +142,7 @@ typedef struct {
   void* query_rope_out;
   float* dequant_scale_q_nope;
   const void* packed_weights; /* optional: the four weights in the library's packed layout */
+  const float* smooth_scales_cq;
 } mla_prolog_tensors;
 
 typedef struct mla_prolog* mla_prolog_t;

@@ -141,6 +141,8 @@ class Dims:
 
 MODEL = Dims(He=7168, Hcq=1536, Hckv=512, N=128, D=128, Dr=64)
 TINY = Dims(He=256, Hcq=64, Hckv=32, N=2, D=16, Dr=8)
+# the tiny shape with Dr = 16: an int8 weightUqQr moves in 16-column chunks
+TINY_Q = Dims(He=256, Hcq=64, Hckv=32, N=2, D=16, Dr=16)
 
 
 @dataclass(frozen=True)
@@ -167,7 +169,7 @@ WORKLOADS: Dict[str, Workload] = {
     "decode_t256": Workload("decode_t256", 256, MODEL, 4096, 128, False, "uniform:32768", 20262),
     "prefill_t8192": Workload("prefill_t8192", 8192, MODEL, 1024, 128, False, "prefill:2x4096", 20263),
     "int8_decode_t128": Workload("int8_decode_t128", 128, MODEL, 1024, 128, True, "uniform:32768", 20264),
-    "tiny_partial_t4": Workload("tiny_partial_t4", 4, TINY, 4, 16, False, "uniform:64", 20265,
+    "tiny_partial_t4": Workload("tiny_partial_t4", 4, TINY_Q, 4, 16, False, "uniform:64", 20265,
                                 partial=True, smooth=True),
     "partial_decode_t32": Workload("partial_decode_t32", 32, MODEL, 1024, 128, False, "uniform:32768",
                                    20266, partial=True, smooth=True),

@@ -35,13 +35,17 @@ def model_desc(**kw):
 FAKE = 1 << 40   # an aligned address; validate never dereferences it
 
 
-def fake_tensors(q8=False, in8=False):
+def fake_tensors(q8=False, in8=False, partial=False, smooth=False):
     t = {f: FAKE for f in mla.TENSOR_FIELDS}
     if not in8:
-        for f in ("scale_x", "scale_w_dq", "scale_w_uq_qr", "scale_w_dkv_kr"):
+        for f in ("scale_x", "scale_w_dq", "scale_w_dkv_kr"):
             t[f] = None
+        if not partial:
+            t["scale_w_uq_qr"] = None
     if not q8:
         t["dequant_scale_q_nope"] = None
+    if not smooth:
+        t["smooth_scales_cq"] = None
     return t
 
 
@@ -49,6 +53,12 @@ def test_valid_descriptions():
     assert mla.validate(model_desc()) == mla.MLA_OK
     assert mla.validate(model_desc(), fake_tensors(), 32) == mla.MLA_OK
     assert mla.validate(model_desc(in_dtype=1, query_dtype=1), fake_tensors(True, True), 128) == mla.MLA_OK
+    assert mla.validate(model_desc(in_dtype=1), fake_tensors(in8=True, smooth=True), 128) == mla.MLA_OK
+    part = model_desc(in_dtype=mla.MLA_INT8_PARTIAL)
+    assert mla.validate(part, fake_tensors(partial=True), 32) == mla.MLA_OK
+    assert mla.validate(part, fake_tensors(partial=True, smooth=True), 32) == mla.MLA_OK
+    # the bf16 down-projection of partial quantisation keeps the bf16 size rules
+    assert mla.validate(model_desc(in_dtype=mla.MLA_INT8_PARTIAL, He=7176, Hckv=504)) == mla.MLA_OK
     tiny = mla.make_desc(256, 64, 32, 2, 16, 8, 4, 16, 4)
     assert mla.validate(tiny, fake_tensors(), 4) == mla.MLA_OK
     assert mla.workspace_bytes(model_desc()) > 0
@@ -68,6 +78,9 @@ def test_valid_descriptions():
     (dict(in_dtype=1, Hcq=1544), mla.MLA_ERR_UNSUPPORTED),
     (dict(in_dtype=1, Hckv=504), mla.MLA_ERR_UNSUPPORTED),
     (dict(in_dtype=1, Dr=56), mla.MLA_ERR_UNSUPPORTED),
+    (dict(in_dtype=2, query_dtype=1), mla.MLA_ERR_PARAM_INVALID),   # int8 q^N: full quantisation only
+    (dict(in_dtype=2, Hcq=1544), mla.MLA_ERR_UNSUPPORTED),
+    (dict(in_dtype=2, D=120), mla.MLA_ERR_UNSUPPORTED),
 ])
 def test_bad_descriptions(kw, code):
     assert mla.validate(model_desc(**kw)) == code
@@ -89,6 +102,16 @@ def test_bad_run_arguments():
     d8 = model_desc(in_dtype=1, query_dtype=1)
     assert mla.validate(d8, fake_tensors(q8=False, in8=True), 8) == mla.MLA_ERR_NULLPTR
     assert mla.validate(d8, fake_tensors(q8=True, in8=False), 8) == mla.MLA_ERR_NULLPTR
+    # smoothScalesCq belongs to the int8 weightUqQr scenarios
+    assert mla.validate(d, fake_tensors(smooth=True), 8) == mla.MLA_ERR_PARAM_INVALID
+    t = fake_tensors(q8=True, in8=True, smooth=True); t["smooth_scales_cq"] = FAKE + 2
+    assert mla.validate(d8, t, 8) == mla.MLA_ERR_PARAM_INVALID                 # misaligned
+    # partial quantisation: the weightUqQr scale alone
+    dp = model_desc(in_dtype=mla.MLA_INT8_PARTIAL)
+    t = fake_tensors(partial=True); t["scale_w_uq_qr"] = None
+    assert mla.validate(dp, t, 8) == mla.MLA_ERR_NULLPTR
+    t = fake_tensors(partial=True); t["scale_x"] = FAKE
+    assert mla.validate(dp, t, 8) == mla.MLA_ERR_PARAM_INVALID
 
 
 def test_empty_run_needs_no_tensors():

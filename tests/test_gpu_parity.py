@@ -14,7 +14,7 @@ import oracle
 import synth
 from synth import device as dev
 from synth.generate import Dims, custom_workload
-from parity import check_caches, check_queries
+from parity import check_caches, check_queries, tie_allowance
 
 pytestmark = pytest.mark.gpu
 
@@ -55,8 +55,15 @@ def full_check(inp, query_int8=None, rows=None, packed=False, repeat=1, prerun_n
     rows = np.arange(int(inp["T"])) if rows is None else np.asarray(rows)
     say(f"case {inp['workload']} T={inp['T']} dims={inp['dims']} q8={q8} rows={len(rows)} packed={packed}")
     got = run_gpu(inp, query_int8=query_int8, packed=packed, repeat=repeat, prerun_negated=prerun_negated)
-    ref = oracle.run(inp, tokens=rows, query_int8=query_int8, caches=False)
-    check_queries(got, ref, rows, q8)
+    partial = bool(inp.get("partial", False))
+    ref = oracle.run(inp, tokens=rows, query_int8=query_int8, caches=False, intermediates=partial)
+    allow = None
+    if partial:
+        # int8 c^Q from a float y: codes at a rounding tie may go either way
+        aqr, aqn, namb = tie_allowance(inp, ref, rows)
+        allow = (aqr, aqn)
+        say(f"  c^Q codes within the tie band: {namb}")
+    check_queries(got, ref, rows, q8, allow)
     check_caches(inp, got["kv_cache"], got["kr_cache"], ref, rows)
     return got
 
@@ -173,7 +180,8 @@ def packed_reference(inp):
     each as k-stages of 4 column tiles x 64 lanes x 16 bytes; lane l of tile
     ct holds rows KL*(l//16)+i of column 16*ct + l%16."""
     d = inp["dims"]
-    i8 = bool(inp["quant"])
+    i8 = bool(inp["quant"])                        # W^DQ, W^DkvKr
+    i8u = i8 or bool(inp.get("partial", False))    # W^UqQr
 
     def windows_of(W, cols, K, kl):
         out = []
@@ -189,6 +197,7 @@ def packed_reference(inp):
         return out
 
     kl = 16 if i8 else 8
+    klu = 16 if i8u else 8
     parts = []
     wdq = np.asarray(inp["weight_dq"])
     parts += windows_of(wdq, [(c, min(64, d.Hcq - c)) for c in range(0, d.Hcq, 64)], d.He, kl)
@@ -200,16 +209,16 @@ def packed_reference(inp):
     for h in range(d.N):
         base = h * (d.D + d.Dr)
         cols += [(base + c, min(64, d.D - c)) for c in range(0, d.D, 64)] + [(base + d.D, d.Dr)]
-    parts += windows_of(wuq, cols, d.Hcq, kl)
+    parts += windows_of(wuq, cols, d.Hcq, klu)
     wuk = np.asarray(inp["weight_uk"])
     for h in range(d.N):
         parts += windows_of(wuk[h], [(c, min(64, d.Hckv - c)) for c in range(0, d.Hckv, 64)], d.D, 8)
     return np.concatenate(parts)
 
 
-@pytest.mark.parametrize("name", ["tiny_t4", "ragged_t5_wide"])
+@pytest.mark.parametrize("name", ["tiny_t4", "ragged_t5_wide", "partial_t37"])
 def test_packed_layout(name):
-    inp = synth.make_inputs(SMALL[name])
+    inp = synth.make_inputs(SMALL[name] if name in SMALL else PARTIAL[name])
     say(f"case pack layout {name}")
     t = dev.upload(inp)
     desc = mla.make_desc(**dev.desc_args(inp))
@@ -387,3 +396,70 @@ def test_shape_boundaries_int8_packed(T):
     wl = custom_workload(f"boundary_q8_t{T}", T=T, dims=Dims(He=512, Hcq=128, Hckv=96, N=2, D=32, Dr=32),
                          block_num=(T + 15) // 16 + 1, block_size=16, quant=True, seed=60 + T)
     full_check(synth.make_inputs(wl), packed=True)
+
+
+# ---- partial quantisation (int8 weightUqQr only) and smoothScalesCq -----------
+# The down-projection, norms and caches run the bf16 kernels; c^Q is quantised
+# per token (times the smoothing factors) for the int8 up-projection kernels.
+PARTIAL = {
+    "tiny_partial_t4": synth.workload("tiny_partial_t4"),
+    "partial_t37": custom_workload("partial_t37", T=37, dims=Dims(He=264, Hcq=80, Hckv=40, N=3, D=32, Dr=16),
+                                   block_num=4, block_size=16, seed=81, partial=True, smooth=True),
+    "partial_t6_nosmooth": custom_workload("partial_t6", T=6, dims=Dims(He=264, Hcq=64, Hckv=40, N=2, D=16, Dr=16),
+                                           block_num=2, block_size=16, seed=82, partial=True),
+    "pair_partial_t5_n4": custom_workload("pair_partial_t5_n4", T=5,
+                                          dims=Dims(He=512, Hcq=256, Hckv=128, N=4, D=128, Dr=64),
+                                          block_num=2, block_size=16, seed=83, partial=True, smooth=True),
+    "pair_partial_t32_n8": custom_workload("pair_partial_t32_n8", T=32,
+                                           dims=Dims(He=264, Hcq=192, Hckv=320, N=8, D=96, Dr=64),
+                                           block_num=4, block_size=16, seed=84, partial=True, smooth=True),
+    "partial_t130": custom_workload("partial_t130", T=130, dims=Dims(He=1032, Hcq=192, Hckv=504, N=3, D=128, Dr=64),
+                                    block_num=16, block_size=16, seed=85, partial=True, smooth=True),
+    "partial_t300": custom_workload("partial_t300", T=300, dims=Dims(He=520, Hcq=128, Hckv=64, N=2, D=32, Dr=16),
+                                    block_num=20, block_size=16, seed=86, partial=True, smooth=True),
+    "partial_t2100_large": custom_workload("partial_t2100", T=2100,
+                                           dims=Dims(He=264, Hcq=64, Hckv=40, N=3, D=32, Dr=16),
+                                           block_num=160, block_size=16, seed=87, partial=True, smooth=True),
+}
+
+
+@pytest.mark.parametrize("name", ["tiny_partial_t4", "partial_t37", "partial_t6_nosmooth"])
+def test_partial_row_major(name):
+    full_check(synth.make_inputs(PARTIAL[name]))
+
+
+@pytest.mark.parametrize("name", list(PARTIAL))
+def test_partial_packed(name):
+    inp = synth.make_inputs(PARTIAL[name])
+    full_check(inp, packed=True, repeat=2, prerun_negated=True)
+
+
+@pytest.mark.parametrize("T", [32, 33, 64, 65, 100, 128, 129])
+def test_shape_boundaries_partial_packed(T):
+    wl = custom_workload(f"boundary_partial_t{T}", T=T, dims=Dims(He=520, Hcq=128, Hckv=88, N=2, D=32, Dr=32),
+                         block_num=(T + 15) // 16 + 1, block_size=16, partial=True, smooth=True, seed=90 + T)
+    full_check(synth.make_inputs(wl), packed=True)
+
+
+def test_full_size_partial_decode_packed():
+    inp = synth.make_inputs(synth.workload("partial_decode_t32"))
+    full_check(inp, packed=True)
+
+
+SMOOTH_Q8 = {
+    "q8_smooth_t9": custom_workload("q8_smooth_t9", T=9, dims=Dims(He=256, Hcq=64, Hckv=32, N=2, D=16, Dr=16),
+                                    block_num=2, block_size=16, quant=True, smooth=True, seed=95),
+    "q8_smooth_pair_t16": custom_workload("q8_smooth_pair_t16", T=16,
+                                          dims=Dims(He=512, Hcq=256, Hckv=128, N=4, D=128, Dr=64),
+                                          block_num=2, block_size=16, quant=True, smooth=True, seed=96),
+    "q8_smooth_t130": custom_workload("q8_smooth_t130", T=130, dims=Dims(He=1024, Hcq=192, Hckv=512, N=3, D=128, Dr=64),
+                                      block_num=16, block_size=16, quant=True, smooth=True, seed=97),
+}
+
+
+@pytest.mark.parametrize("name", list(SMOOTH_Q8))
+def test_int8_smoothed(name):
+    inp = synth.make_inputs(SMOOTH_Q8[name])
+    full_check(inp)
+    full_check(inp, packed=True)
+    full_check(inp, query_int8=False, packed=True)
