@@ -247,7 +247,6 @@ struct Ptrs {
   uint8_t* cq;       // [T][Hcq] bf16 (int8 in int8 mode)
   float* cq_scale;   // [T]
   uint16_t* qc;      // [T][N][D] bf16
-  uint8_t* xp;       // x fragment-packed (tiled path, medium T)
   uint8_t* xq;       // [N] q^C exchange of the paired small-T kernel, kPairXq bytes a head
   uint32_t* xflag;   // [N][4] its exchange flags, then one error word; zero between runs
   float* xmax;       // [N][2][32] its per-token row maxima
@@ -2291,12 +2290,12 @@ __device__ __forceinline__ APacked<I8, MT> tiles_from(const void* base, int64_t 
 // buffer, `wstride` bytes apart, the first at wbase, nwin of them valid) of
 // each k-stage are copied, 1 KB per wave load, into a two-buffer LDS ring;
 // every wave then reads its fragments with conflict-free 16-byte LDS reads.
-// The global loads run three stages ahead of the MFMAs through two register
-// sets.  ns must be the same for the whole block.
+// The global loads run two groups of KPB stages ahead of the MFMAs through
+// two register sets.  ns must be the same for the whole block.
 // SH: weight loads carry the streaming hint; set where each weight byte is
 // read once per step (few token tiles), left off where token tiles re-read
 // the weights and want them kept in the caches
-template <bool I8, int MT, int NWW, int WM, int WN, class AP, int RS = 2, int KPB = 1, bool SH = false>
+template <bool I8, int MT, int NWW, int WM, int WN, class AP, int KPB = 1, bool SH = false>
 __device__ __forceinline__ void tile_mma_lds(const AP& ap, rsrc_t Wp, uint32_t wbase, uint32_t wstride,
                                              int nwin, int s0, int ns, uint8_t* lds,
                                              typename Stage<I8>::Acc (&acc)[MT][NWW * 4]) {
@@ -2371,28 +2370,6 @@ __device__ __forceinline__ void tile_mma_lds(const AP& ap, rsrc_t Wp, uint32_t w
   const int ngr = (ns + KPB - 1) / KPB;
   // groups past ngr load as zeros, so an odd count costs one zero group but
   // keeps the loop free of an exit between its two halves
-  if constexpr (RS == 1) {
-    // one register set: group k + 2 is loaded while group k is computed and
-    // written to LDS one iteration later
-    Regs R;
-    gload(R, 0);
-    lwrite(R, 0);
-    gload(R, 1);
-    __syncthreads();
-    for (int j = 0; j < ngr; j += 2) {
-      compute(0);                      // group j
-      __builtin_amdgcn_sched_barrier(0);
-      lwrite(R, 1);                    // group j + 1
-      gload(R, j + 2);
-      __syncthreads();
-      compute(1);                      // group j + 1
-      __builtin_amdgcn_sched_barrier(0);
-      lwrite(R, 0);                    // group j + 2
-      gload(R, j + 3);
-      __syncthreads();
-    }
-    return;
-  }
   Regs R0, R1;   // group k waits in R(k % 2)
   gload(R0, 0);
   __builtin_amdgcn_sched_barrier(0);
@@ -2419,26 +2396,7 @@ __device__ __forceinline__ void tile_mma_lds(const AP& ap, rsrc_t Wp, uint32_t w
 // (wm, wn) takes tokens 16*MT*wm.. of the block's token tile and windows
 // NWW*wn.. of its group of [W^DQ | W^DkvKr] windows; the split's stages go
 // into fp32 (int32) partials, one 16-byte store per 4 columns.
-// x into the fragment-packed layout of the activations (16-token tiles of
-// 1 KB k-stages; k padding and rows past T as zeros), one 16-byte chunk per
-// thread.
-template <bool I8>
-__global__ __launch_bounds__(256) void k_pack_x(Dims d, Ptrs p, int nst) {
-  using St = Stage<I8>;
-  const int64_t q = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t tiles = (d.T + 15) / 16;
-  if (q >= tiles * nst * 64) return;
-  const int lane = int(q % 64), st = int((q / 64) % nst);
-  const int64_t t = (q / (64 * nst)) * 16 + (lane & 15);
-  const int k = st * St::KS + St::KL * (lane >> 4);
-  uint4 v = make_uint4(0, 0, 0, 0);
-  if (t < d.T && k < d.He) v = *reinterpret_cast<const uint4*>(p.x + (t * d.He + k) * St::EB);
-  *reinterpret_cast<uint4*>(p.xp + q * 16) = v;
-}
-
-// XP: x is read fragment-packed from p.xp instead of row-major.
-template <bool I8, int MT, int NWW, int WM, int WN, int D, bool LC = false, bool XP = false, int RS = 2,
-          int KPB = 1, bool SH = false>
+template <bool I8, int MT, int NWW, int WM, int WN, int D, bool LC = false, int KPB = 1, bool SH = false>
 __global__ __launch_bounds__(64 * WM * WN) void k1_tiled(Dims d, Ptrs p, PackGeo pg, int sps, int mtiles,
                                                       int ngrp) {
   using St = Stage<I8>;
@@ -2462,19 +2420,14 @@ __global__ __launch_bounds__(64 * WM * WN) void k1_tiled(Dims d, Ptrs p, PackGeo
     __shared__ __attribute__((aligned(16))) uint8_t ring[2 * KPB * (MT * WM + NWW * WN * 4) * 1024];
     const int mb = mtile * BM, j0 = grp * GW;
     const int nsb = mb < d.T ? max(0, min(pg.nst_he, s0 + sps) - s0) : 0;
-    tile_mma_lds<I8, MT, NWW, WM, WN, APlain<I8, MT * WM>, RS, KPB, SH>(rows_from<I8, MT * WM>(p.x, d.He, mb, d.T),
+    tile_mma_lds<I8, MT, NWW, WM, WN, APlain<I8, MT * WM>, KPB, SH>(rows_from<I8, MT * WM>(p.x, d.He, mb, d.T),
                                       make_rsrc(p.packed, pg.total),
                                       uint32_t(pg.off_dq + int64_t(j0) * pg.nst_he * 4096),
                                       uint32_t(pg.nst_he * 4096), tiles - j0, s0, nsb, ring, acc);
   } else {
     const int ns = m0 < d.T ? max(0, min(pg.nst_he, s0 + sps) - s0) : 0;
-    if constexpr (XP) {
-      const auto ap = tiles_from<I8, MT>(p.xp, int64_t(pg.nst_he) * 1024, (d.T + 15) / 16, m0);
-      tile_mma<I8, MT, NWW, D>(ap, make_rsrc(p.packed, pg.total), wb, s0, ns, acc);
-    } else {
-      const auto ap = rows_from<I8, MT>(p.x, d.He, m0, d.T);
-      tile_mma<I8, MT, NWW, D>(ap, make_rsrc(p.packed, pg.total), wb, s0, ns, acc);
-    }
+    const auto ap = rows_from<I8, MT>(p.x, d.He, m0, d.T);
+    tile_mma<I8, MT, NWW, D>(ap, make_rsrc(p.packed, pg.total), wb, s0, ns, acc);
   }
   if (m0 >= d.T) return;
   const int g = lane >> 4, c = lane & 15;
@@ -2505,8 +2458,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k1_tiled(Dims d, Ptrs p, PackGeo
 // K3t: grid (token tiles fastest, then groups of W^UqQr windows).  Nope
 // windows go to q^C (bf16, workspace); a rope window goes through a per-wave
 // LDS tile of 16 tokens x 64 columns to RoPE and queryRopeOut.
-template <bool I8, int MT, int NWW, int WM, int WN, int D, bool LC = false, int RS = 2, int KPB = 1,
-          bool SH = false>
+template <bool I8, int MT, int NWW, int WM, int WN, int D, bool LC = false, int KPB = 1, bool SH = false>
 __global__ __launch_bounds__(64 * WM * WN) void k3_tiled(Dims d, Ptrs p, PackGeo pg, int mtiles) {
   using St = Stage<I8>;
   constexpr int BM = 16 * MT * WM, GW = NWW * WN;
@@ -2529,7 +2481,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k3_tiled(Dims d, Ptrs p, PackGeo
   if constexpr (LC) {
     uint8_t* ring = lds_k3;
     const int mb = mtile * BM, j0 = grp * GW;
-    tile_mma_lds<I8, MT, NWW, WM, WN, APacked<I8, MT * WM>, RS, KPB, SH>(
+    tile_mma_lds<I8, MT, NWW, WM, WN, APacked<I8, MT * WM>, KPB, SH>(
         tiles_from<I8, MT * WM>(p.cq, int64_t(pg.nst_cq) * 1024, (d.T + 15) / 16, mb),
         make_rsrc(p.packed, pg.total), uint32_t(pg.off_uq + int64_t(j0) * pg.nst_cq * 4096),
         uint32_t(pg.nst_cq * 4096), pg.win_uq - j0, 0, mb < d.T ? pg.nst_cq : 0, ring, acc);
@@ -3133,15 +3085,15 @@ void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs&
                   bool q8, Mark& mark) {
   const dim3 g1(tp.m1 * tp.ngrp1 * tp.S), g3(tp.m3 * tp.ngrp3);
   if (tp.k1v == 1)
-    k1_tiled<I8D, 4, 1, 4, 2, 2, true, false, 2, 1, true><<<g1, 512, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
+    k1_tiled<I8D, 4, 1, 4, 2, 2, true, 1, true><<<g1, 512, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
   else if (I8D && tp.k1v == 2)
-    k1_tiled<I8D, 2, 1, 4, 2, 2, true, false, 2, 1, true><<<g1, 512, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
+    k1_tiled<I8D, 2, 1, 4, 2, 2, true, 1, true><<<g1, 512, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
   else k1_tiled<I8D, MT, 1, 1, 1, 2><<<g1, 64, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
   mark(1);
   launch_norm<I8D, I8U>(s, d, p, tp.S, g.nst_cq);
   mark(2);
-  if (tp.k3v == 1) k3_tiled<I8U, 2, 1, 8, 2, 2, true, 2, 1, true><<<g3, 1024, 0, s>>>(d, p, g, tp.m3);
-  else if (I8U && tp.k3v == 2) k3_tiled<I8U, 1, 1, 8, 2, 2, true, 1, 1, true><<<g3, 1024, 0, s>>>(d, p, g, tp.m3);
+  if (tp.k3v == 1) k3_tiled<I8U, 2, 1, 8, 2, 2, true, 1, true><<<g3, 1024, 0, s>>>(d, p, g, tp.m3);
+  else if (I8U && tp.k3v == 2) k3_tiled<I8U, 1, 1, 8, 2, 2, true, 1, true><<<g3, 1024, 0, s>>>(d, p, g, tp.m3);
   else k3_tiled<I8U, 4, 1, 1, 1, 2><<<g3, 64, 0, s>>>(d, p, g, tp.m3);
   mark(3);
   if (q8) k4_tiled<4, 1, 1, 8, 2, true, false, true><<<dim3(tp.m4q * d.N), 512, 0, s>>>(d, p, g, tp.m4q, 1);
@@ -3342,7 +3294,6 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   p.cq = h->ws + h->lay.cq;
   p.cq_scale = reinterpret_cast<float*>(h->ws + h->lay.cq_scale);
   p.qc = reinterpret_cast<uint16_t*>(h->ws + h->lay.qc);
-  p.xp = nullptr;
   p.xq = h->ws + h->lay.xq;
   p.xflag = reinterpret_cast<uint32_t*>(h->ws + h->lay.xflag);
   p.xmax = reinterpret_cast<float*>(h->ws + h->lay.xmax);
