@@ -48,6 +48,8 @@ class Problem(ctypes.Structure):
         ("query_out", _P), ("query_rope_out", _P), ("dequant_scale_q_nope", _P),
         ("kv_rows", _P), ("kr_rows", _P),
         ("y_out", _P), ("cq_out", _P), ("u_out", _P), ("qn_out", _P),
+        ("kv_int8", ctypes.c_int32), ("kr_int8", ctypes.c_int32),
+        ("quant_scale_ckv", _P), ("quant_scale_ckr", _P), ("ckv_out", _P), ("kr_out", _P),
     ]
 
 
@@ -126,7 +128,9 @@ def run(inp: Dict[str, object], tokens: Optional[Sequence[int]] = None,
 
     ``inp["quant"]`` is the int8 full-quantisation scenario, ``inp["partial"]``
     the partial one (only weightUqQr int8); ``inp["smooth_scales_cq"]``, when
-    present, is smoothScalesCq.  ``tokens`` selects the rows to compute (tokens are independent); row r of
+    present, is smoothScalesCq; ``inp["kv_quant"]`` quantises the kv cache
+    (and, with partial quantisation, the kr cache) with quantScaleCkv /
+    quantScaleCkr.  ``tokens`` selects the rows to compute (tokens are independent); row r of
     every output holds token ``tokens[r]``.  With ``caches`` the returned
     ``kv_cache``/``kr_cache`` are copies of the input caches with the computed
     rows written at their cacheIndex slots.
@@ -136,6 +140,8 @@ def run(inp: Dict[str, object], tokens: Optional[Sequence[int]] = None,
     quant = bool(inp["quant"])
     quant_uq = quant or bool(inp.get("partial", False))
     q8 = quant if query_int8 is None else bool(query_int8)
+    kv8 = bool(inp.get("kv_quant", False))
+    kr8 = kv8 and not quant
     keep = []
 
     def arr(a, dtype):
@@ -163,8 +169,8 @@ def run(inp: Dict[str, object], tokens: Optional[Sequence[int]] = None,
     out = {
         "query_out": np.zeros((n, N, Hckv), dtype=np.int8 if q8 else np.uint16),
         "query_rope_out": np.zeros((n, N, Dr), dtype=np.uint16),
-        "kv_rows": np.zeros((n, Hckv), dtype=np.uint16),
-        "kr_rows": np.zeros((n, Dr), dtype=np.uint16),
+        "kv_rows": np.zeros((n, Hckv), dtype=np.int8 if kv8 else np.uint16),
+        "kr_rows": np.zeros((n, Dr), dtype=np.int8 if kr8 else np.uint16),
     }
     if q8:
         out["dequant_scale_q_nope"] = np.zeros((n, N), dtype=np.float32)
@@ -173,10 +179,12 @@ def run(inp: Dict[str, object], tokens: Optional[Sequence[int]] = None,
         out["c_q"] = np.zeros((n, Hcq))
         out["u"] = np.zeros((n, N * (D + Dr)))
         out["q_n"] = np.zeros((n, N, Hckv))
+        out["c_kv"] = np.zeros((n, Hckv))
+        out["k_r"] = np.zeros((n, Dr))
     kv = kr = None
     if caches and "kv_cache" in inp:
-        kv = np.array(inp["kv_cache"], dtype=np.uint16, copy=True)
-        kr = np.array(inp["kr_cache"], dtype=np.uint16, copy=True)
+        kv = np.array(inp["kv_cache"], dtype=np.int8 if kv8 else np.uint16, copy=True)
+        kr = np.array(inp["kr_cache"], dtype=np.int8 if kr8 else np.uint16, copy=True)
 
     p = Problem()
     p.T, p.He, p.Hcq, p.Hckv, p.N, p.D, p.Dr = T, d.He, Hcq, Hckv, N, D, Dr
@@ -196,6 +204,11 @@ def run(inp: Dict[str, object], tokens: Optional[Sequence[int]] = None,
         p.scale_w_uq_qr = _ptr(arr(inp["dequant_scale_w_uq_qr"], np.float32))
     if inp.get("smooth_scales_cq") is not None:
         p.smooth_cq = _ptr(arr(inp["smooth_scales_cq"], np.float32))
+    p.kv_int8, p.kr_int8 = int(kv8), int(kr8)
+    if kv8:
+        p.quant_scale_ckv = _ptr(arr(inp["quant_scale_ckv"], np.float32))
+    if kr8:
+        p.quant_scale_ckr = _ptr(arr(inp["quant_scale_ckr"], np.float32))
     p.tokens, p.n_tokens = _ptr(rows), n
     p.query_out, p.query_rope_out = _ptr(out["query_out"]), _ptr(out["query_rope_out"])
     p.dequant_scale_q_nope = _ptr(out.get("dequant_scale_q_nope"))
@@ -203,6 +216,7 @@ def run(inp: Dict[str, object], tokens: Optional[Sequence[int]] = None,
     if intermediates:
         p.y_out, p.cq_out, p.u_out, p.qn_out = (_ptr(out["y"]), _ptr(out["c_q"]),
                                                 _ptr(out["u"]), _ptr(out["q_n"]))
+        p.ckv_out, p.kr_out = _ptr(out["c_kv"]), _ptr(out["k_r"])
     rc = lib().mla_oracle_run(ctypes.byref(p), int(nthreads))
     if rc != 0:
         raise ValueError("oracle rejected the problem")

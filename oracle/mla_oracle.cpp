@@ -34,6 +34,15 @@
 //                                            dynamic int8, decided in float32
 // round_intermediates = 0 skips R3 and R5 (used by the composition pin).
 //
+// KV-cache quantisation (same page: quantScaleCkv / quantScaleCkr and the
+// "kv_cache quantized" columns of the scenario and dtype tables) replaces R1
+// and R2 by static int8 codes (R1', R2'): the value times its channel's
+// scale, rounded half to even and saturated to [-128, 127], decided in
+// float32.  The page gives the scales' shapes and scenarios but no formula;
+// multiplying is the reading taken (the preprocess page's quantising norm
+// multiplies by its scale).  Full quantisation quantises the kv cache only;
+// partial quantisation quantises both caches.
+//
 // The partial-quantisation scenario (same page, scenario table) takes tokenX,
 // weightDq and weightDkvKr in bf16 and only weightUqQr in int8, with its
 // per-channel dequantisation scale; the up-projection then runs on R3' as in
@@ -136,6 +145,15 @@ void quant_int8(const double* v, int64_t n, int8_t* q, float* scale) {
   }
 }
 
+// Static int8 code of v with a given scale (R1', R2'): v times the scale,
+// rounded half to even, saturated to [-128, 127], decided in float32.
+int8_t quant_static(double v, float scale, int mutation) {
+  const float f = static_cast<float>(v);
+  float r = std::nearbyint(mutation == 8 ? f / scale : f * scale);  // planted 8: divided
+  r = std::min(127.0f, std::max(-128.0f, r));
+  return static_cast<int8_t>(r);
+}
+
 }  // namespace
 
 extern "C" {
@@ -168,8 +186,8 @@ typedef struct {
   const uint16_t* rope_sin;
   const uint16_t* rope_cos;
   const int64_t* cache_index;
-  uint16_t* kv_cache;           // updated in place; NULL = no cache writes
-  uint16_t* kr_cache;
+  void* kv_cache;               // updated in place (bf16 bits, or int8); NULL = no cache writes
+  void* kr_cache;
   const float* scale_x;         // (T)
   const float* scale_w_dq;      // (Hcq)
   const float* scale_w_uq_qr;   // (N*(D+Dr))
@@ -181,12 +199,18 @@ typedef struct {
   void* query_out;              // (n, N, Hckv) bf16 bits or int8
   uint16_t* query_rope_out;     // (n, N, Dr)
   float* dequant_scale_q_nope;  // (n, N), int8 query only
-  uint16_t* kv_rows;            // optional (n, Hckv): the row written to kvCache
-  uint16_t* kr_rows;            // optional (n, Dr)
+  void* kv_rows;                // optional (n, Hckv): the row written to kvCache (bf16 bits or int8)
+  void* kr_rows;                // optional (n, Dr)
   double* y_out;                // optional (n, Hcq+Hckv+Dr): x W^DQ | x W^DKV | x W^KR
   double* cq_out;               // optional (n, Hcq): c^Q before rounding
   double* u_out;                // optional (n, N*(D+Dr)): c^Q W^UqQr
   double* qn_out;               // optional (n, N, Hckv): q^N before rounding
+  int32_t kv_int8;              // 1: kvCache rows are R1' codes with quant_scale_ckv
+  int32_t kr_int8;              // 1: krCache rows are R2' codes with quant_scale_ckr
+  const float* quant_scale_ckv; // (Hckv)
+  const float* quant_scale_ckr; // (Dr)
+  double* ckv_out;              // optional (n, Hckv): c^KV before rounding
+  double* kr_out;               // optional (n, Dr): k^R before rounding
 } mla_oracle_problem;
 
 double mla_oracle_bf16_value(uint16_t bits) { return bf16_value(bits); }
@@ -262,10 +286,26 @@ static void one_token(const mla_oracle_problem* p, int64_t r, int64_t t) {
   rope(y_kvr.data() + Hckv, cosv.data(), sinv.data(), Dr, k_r.data(), mut);
   if (p->cq_out)
     for (int64_t i = 0; i < Hcq; ++i) p->cq_out[r * Hcq + i] = c_q[i];
-  if (p->kv_rows)
-    for (int64_t i = 0; i < Hckv; ++i) p->kv_rows[r * Hckv + i] = bf16_bits(c_kv[i]);  // R1
-  if (p->kr_rows)
-    for (int64_t i = 0; i < Dr; ++i) p->kr_rows[r * Dr + i] = bf16_bits(k_r[i]);      // R2
+  if (p->ckv_out)
+    for (int64_t i = 0; i < Hckv; ++i) p->ckv_out[r * Hckv + i] = c_kv[i];
+  if (p->kr_out)
+    for (int64_t i = 0; i < Dr; ++i) p->kr_out[r * Dr + i] = k_r[i];
+  if (p->kv_rows) {
+    for (int64_t i = 0; i < Hckv; ++i) {
+      if (p->kv_int8)   // R1'
+        static_cast<int8_t*>(p->kv_rows)[r * Hckv + i] = quant_static(c_kv[i], p->quant_scale_ckv[i], mut);
+      else              // R1
+        static_cast<uint16_t*>(p->kv_rows)[r * Hckv + i] = bf16_bits(c_kv[i]);
+    }
+  }
+  if (p->kr_rows) {
+    for (int64_t i = 0; i < Dr; ++i) {
+      if (p->kr_int8)   // R2'
+        static_cast<int8_t*>(p->kr_rows)[r * Dr + i] = quant_static(k_r[i], p->quant_scale_ckr[i], mut);
+      else              // R2
+        static_cast<uint16_t*>(p->kr_rows)[r * Dr + i] = bf16_bits(k_r[i]);
+    }
+  }
 
   // up-projection u = c^Q [W^UQ | W^QR]
   std::vector<double> u(Wuq, 0.0);
@@ -346,12 +386,14 @@ int mla_oracle_run(mla_oracle_problem* p, int nthreads) {
   if (p->quant_uq && !p->scale_w_uq_qr) return -1;
   if (p->smooth_cq && !p->quant_in && !p->quant_uq) return -1;
   if (p->query_int8 && !p->dequant_scale_q_nope) return -1;
+  if ((p->kv_int8 && !p->quant_scale_ckv) || (p->kr_int8 && !p->quant_scale_ckr)) return -1;
   const int64_t n = p->tokens ? p->n_tokens : p->T;
   for (int64_t r = 0; r < n; ++r) {
     int64_t t = p->tokens ? p->tokens[r] : r;
     if (t < 0 || t >= p->T) return -1;
   }
   // cache rows are always produced (into caller buffers or scratch)
+  const size_t kv_eb = p->kv_int8 ? 1 : 2, kr_eb = p->kr_int8 ? 1 : 2;
   std::vector<uint16_t> kv_tmp, kr_tmp;
   mla_oracle_problem q = *p;
   if (!q.kv_rows) { kv_tmp.resize(static_cast<size_t>(n * p->Hckv)); q.kv_rows = kv_tmp.data(); }
@@ -377,10 +419,11 @@ int mla_oracle_run(mla_oracle_problem* p, int nthreads) {
       int64_t s = p->cache_index[t];
       if (s < 0 || s >= slots) continue;
       int64_t blk = s / p->block_size, off = s % p->block_size;
-      uint16_t* kv = p->kv_cache + (blk * p->block_size + off) * p->Hckv;
-      uint16_t* kr = p->kr_cache + (blk * p->block_size + off) * p->Dr;
-      std::memcpy(kv, q.kv_rows + r * p->Hckv, sizeof(uint16_t) * p->Hckv);
-      std::memcpy(kr, q.kr_rows + r * p->Dr, sizeof(uint16_t) * p->Dr);
+      const int64_t slot = blk * p->block_size + off;
+      std::memcpy(static_cast<uint8_t*>(p->kv_cache) + slot * p->Hckv * kv_eb,
+                  static_cast<const uint8_t*>(q.kv_rows) + r * p->Hckv * kv_eb, kv_eb * p->Hckv);
+      std::memcpy(static_cast<uint8_t*>(p->kr_cache) + slot * p->Dr * kr_eb,
+                  static_cast<const uint8_t*>(q.kr_rows) + r * p->Dr * kr_eb, kr_eb * p->Dr);
     }
   }
   return 0;

@@ -34,12 +34,15 @@ _CHUNK = 1 << 20
 #: bf16 bit pattern every cache slot starts with (a quiet NaN whose payload no
 #: arithmetic produces), so that untouched slots can be checked bitwise.
 SENTINEL_BF16 = np.uint16(0x7FA5)
+#: the byte an int8 (quantised) cache slot starts with
+SENTINEL_I8 = np.int8(-77)
 
 # one random stream per tensor
 _STREAM = {
     "x": 1, "w_dq": 2, "w_uq": 3, "w_qr": 4, "w_uk": 5, "w_dkv": 6, "w_kr": 7,
     "gamma_cq": 8, "gamma_ckv": 9, "pos": 10, "slots": 11, "sx": 12,
     "sw_dq": 13, "sw_uq_qr": 14, "sw_dkv_kr": 15, "blocks": 16, "smooth_cq": 17,
+    "qs_ckv": 18, "qs_ckr": 19,
 }
 
 
@@ -158,6 +161,7 @@ class Workload:
     eps: float = 1e-6
     partial: bool = False  # partial quantisation: only weightUqQr int8 (+ its scale)
     smooth: bool = False   # draw smoothScalesCq (int8 weightUqQr scenarios only)
+    kv_quant: bool = False  # int8 kv cache (and, partially quantised, int8 kr cache)
 
     def with_tokens(self, T: int) -> "Workload":
         return replace(self, T=T)
@@ -173,6 +177,8 @@ WORKLOADS: Dict[str, Workload] = {
                                 partial=True, smooth=True),
     "partial_decode_t32": Workload("partial_decode_t32", 32, MODEL, 1024, 128, False, "uniform:32768",
                                    20266, partial=True, smooth=True),
+    "int8_kvq_decode_t128": Workload("int8_kvq_decode_t128", 128, MODEL, 1024, 128, True, "uniform:32768",
+                                     20267, kv_quant=True),
 }
 
 
@@ -237,12 +243,14 @@ def make_inputs(wl: Workload, T: Optional[int] = None, with_caches: bool = True,
     He, Hcq, Hckv, N, D, Dr = d.He, d.Hcq, d.Hckv, d.N, d.D, d.Dr
     out: Dict[str, object] = {"workload": wl.name, "T": T, "dims": d,
                               "block_num": wl.block_num, "block_size": wl.block_size,
-                              "quant": wl.quant, "partial": wl.partial,
+                              "quant": wl.quant, "partial": wl.partial, "kv_quant": wl.kv_quant,
                               "eps_cq": wl.eps, "eps_ckv": wl.eps}
     if wl.partial and wl.quant:
         raise ValueError("a workload is either fully or partially quantised")
     if wl.smooth and not (wl.quant or wl.partial):
         raise ValueError("smoothScalesCq belongs to the int8 weightUqQr scenarios")
+    if wl.kv_quant and not (wl.quant or wl.partial):
+        raise ValueError("cache quantisation belongs to the int8 scenarios")
 
     pos, slots = _positions_and_slots(wl)
     pos, slots = pos[:T], slots[:T]
@@ -295,19 +303,30 @@ def make_inputs(wl: Workload, T: Optional[int] = None, with_caches: bool = True,
         out["weight_dkv"], out["weight_kr"] = w_dkv, w_kr
     out["weight_uk"] = _to_bf16_bits(_normal(s, "w_uk", N * D * Hckv) / np.sqrt(D)).reshape(N, D, Hckv)
 
+    kr8 = wl.kv_quant and wl.partial
+    if wl.kv_quant:
+        # per-channel quantScaleCkv in [16, 48): c^KV is O(1), so codes spread
+        # over the int8 range and the largest saturate
+        out["quant_scale_ckv"] = (16.0 + 32.0 * _uniform(s, "qs_ckv", Hckv)).astype(np.float32)
+    if kr8:
+        out["quant_scale_ckr"] = (16.0 + 32.0 * _uniform(s, "qs_ckr", Dr)).astype(np.float32)
     out["kv_cache_shape"] = (wl.block_num, wl.block_size, 1, Hckv)
     out["kr_cache_shape"] = (wl.block_num, wl.block_size, 1, Dr)
     if with_caches:
-        out["kv_cache"] = np.full(out["kv_cache_shape"], SENTINEL_BF16, dtype=np.uint16)
-        out["kr_cache"] = np.full(out["kr_cache_shape"], SENTINEL_BF16, dtype=np.uint16)
+        out["kv_cache"] = (np.full(out["kv_cache_shape"], SENTINEL_I8, dtype=np.int8) if wl.kv_quant
+                           else np.full(out["kv_cache_shape"], SENTINEL_BF16, dtype=np.uint16))
+        out["kr_cache"] = (np.full(out["kr_cache_shape"], SENTINEL_I8, dtype=np.int8) if kr8
+                           else np.full(out["kr_cache_shape"], SENTINEL_BF16, dtype=np.uint16))
     return out
 
 
 def custom_workload(name: str, T: int, dims: Dims, block_num: int, block_size: int,
                     quant: bool = False, seed: int = 7, positions: str = "uniform:4096",
-                    eps: float = 1e-6, partial: bool = False, smooth: bool = False) -> Workload:
+                    eps: float = 1e-6, partial: bool = False, smooth: bool = False,
+                    kv_quant: bool = False) -> Workload:
     """A workload with arbitrary (small) sizes for tests of ragged shapes."""
-    return Workload(name, T, dims, block_num, block_size, quant, positions, seed, eps, partial, smooth)
+    return Workload(name, T, dims, block_num, block_size, quant, positions, seed, eps, partial, smooth,
+                    kv_quant)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:

@@ -468,6 +468,84 @@ def test_power_of_two_smoothing_scales_the_product_exactly(wl):
     assert np.array_equal(four["c_q"], one["c_q"])
 
 
+# ---------------------------------------------------------------------------
+# KV-cache quantisation (quantScaleCkv / quantScaleCkr): R1', R2'
+# ---------------------------------------------------------------------------
+KVQ_PARTIAL = custom_workload("kvq_partial", T=5, dims=Dims(He=40, Hcq=32, Hckv=24, N=3, D=16, Dr=16),
+                              block_num=3, block_size=16, seed=15, partial=True, smooth=True, kv_quant=True)
+KVQ_FULL = custom_workload("kvq_full", T=6, dims=Dims(He=48, Hcq=16, Hckv=16, N=2, D=16, Dr=16),
+                           block_num=2, block_size=16, quant=True, seed=16, kv_quant=True)
+
+
+def _codes_within_half_step(codes, v, scale):
+    """Each code is v * scale to within half a step (plus the float32
+    roundings of v and of the product), or the saturated end of the int8
+    range on the side v * scale lies."""
+    x = np.asarray(v, np.float64) * np.asarray(scale, np.float64)
+    c = np.asarray(codes).astype(np.float64)
+    slack = 0.5 + np.abs(x) * 2.0 ** -22
+    inner = (c > -128) & (c < 127)
+    ok = np.where(inner, np.abs(c - x) <= slack, False)
+    ok |= (c == 127) & (x >= 126.5 - np.abs(x) * 2.0 ** -22)
+    ok |= (c == -128) & (x <= -127.5 + np.abs(x) * 2.0 ** -22)
+    return bool(ok.all())
+
+
+def _kvq_pins_hold(wl, mutation=0):
+    try:
+        inp = synth.make_inputs(wl)
+        o = oracle.run(inp, intermediates=True, mutation=mutation, query_int8=False)
+        ok = _codes_within_half_step(o["kv_rows"], o["c_kv"], inp["quant_scale_ckv"])
+        # the same codes from the bf16 rows of the unquantised cache path
+        plain = oracle.run(dict(inp, kv_quant=False, kv_cache=None, kr_cache=None), caches=False,
+                           query_int8=False, mutation=mutation)
+        bf = lib_bf16_to_f64(plain["kv_rows"])
+        x = bf * inp["quant_scale_ckv"].astype(np.float64)
+        inner = (o["kv_rows"] > -128) & (o["kv_rows"] < 127)
+        ok = ok and bool(np.all(np.abs(o["kv_rows"][inner] - x[inner]) <= 0.5 + np.abs(x[inner]) * 2.0 ** -8))
+        if wl.partial:
+            ok = ok and _codes_within_half_step(o["kr_rows"], o["k_r"], inp["quant_scale_ckr"])
+        return ok
+    except Exception:
+        return False
+
+
+@pytest.mark.parametrize("wl", [KVQ_PARTIAL, KVQ_FULL], ids=["partial", "full"])
+def test_cache_codes_are_the_scaled_rows(wl):
+    assert _kvq_pins_hold(wl)
+
+
+def test_cache_codes_saturate():
+    inp = synth.make_inputs(KVQ_PARTIAL)
+    big = dict(inp, quant_scale_ckv=np.full(inp["dims"].Hckv, 1e4, np.float32),
+               quant_scale_ckr=np.full(inp["dims"].Dr, 1e4, np.float32))
+    o = oracle.run(big, intermediates=True)
+    for codes, v in ((o["kv_rows"], o["c_kv"]), (o["kr_rows"], o["k_r"])):
+        x = v * 1e4
+        out = np.abs(x) >= 128          # beyond the int8 range: saturated on its side
+        assert out.mean() > 0.9
+        assert np.all(np.where(x[out] > 0, codes[out] == 127, codes[out] == -128))
+
+
+@pytest.mark.parametrize("wl", [KVQ_PARTIAL, KVQ_FULL], ids=["partial", "full"])
+def test_cache_quantisation_leaves_the_queries_alone(wl):
+    inp = synth.make_inputs(wl)
+    a = oracle.run(inp)
+    b = oracle.run(dict(inp, kv_quant=False, kv_cache=None, kr_cache=None), caches=False)
+    for k in ("query_out", "query_rope_out"):
+        assert np.array_equal(a[k], b[k])
+    if not wl.partial:   # full quantisation keeps a bf16 kr cache
+        assert a["kr_rows"].dtype == np.uint16 and np.array_equal(a["kr_rows"], b["kr_rows"])
+    else:
+        assert a["kr_rows"].dtype == np.int8
+    # the int8 caches change only at the named slots
+    kv = a["kv_cache"].reshape(-1, inp["dims"].Hckv)
+    named = np.zeros(kv.shape[0], bool)
+    named[inp["cache_index"]] = True
+    assert np.all(kv[~named] == synth.SENTINEL_I8)
+    assert np.array_equal(kv[inp["cache_index"]], a["kv_rows"])
+
+
 def _whole_pins_hold(mutation):
     """All whole-prolog pins above, as one predicate, for the planted mistakes."""
     try:
@@ -508,6 +586,13 @@ def test_smooth_pins_hold_without_planted_mistake():
 @pytest.mark.parametrize("mutation", [6, 7], ids=["smooth_divided", "smooth_ignored"])
 def test_planted_smoothing_mistakes_fail_a_pin(mutation):
     assert not _smooth_pins_hold(mutation)
+
+
+def test_planted_cache_scale_mistake_fails_a_pin():
+    # planted mistake 8: the cache value divided by its scale instead of multiplied
+    assert _kvq_pins_hold(KVQ_PARTIAL) and _kvq_pins_hold(KVQ_FULL)
+    assert not _kvq_pins_hold(KVQ_PARTIAL, mutation=8)
+    assert not _kvq_pins_hold(KVQ_FULL, mutation=8)
 
 
 @pytest.mark.parametrize("mutation", [1, 2, 3, 4, 5],
