@@ -36,6 +36,9 @@ def algorithmic(inp, T):
     q8 = bool(inp["quant"])                   # int8 x, W^DQ, W^DkvKr (and W^UqQr)
     u8 = q8 or bool(inp.get("partial", False))   # int8 W^UqQr and c^Q
     sm = inp.get("smooth_scales_cq") is not None
+    kv8 = bool(inp.get("kv_quant", False))            # int8 kv cache rows
+    kr8 = kv8 and bool(inp.get("partial", False))    # int8 kr cache rows
+    cache = T * (d.Hckv * (1 if kv8 else 2) + d.Dr * (1 if kr8 else 2)) + (kv8 and d.Hckv * 4) + (kr8 and d.Dr * 4)
     ed = 1 if q8 else 2                       # bytes of x, W^DQ, W^DkvKr elements
     eu = 1 if u8 else 2                       # bytes of W^UqQr and c^Q elements
     W = d.N * (d.D + d.Dr)
@@ -43,7 +46,7 @@ def algorithmic(inp, T):
     qo = 1 if q8 else 2
     k1_bytes = d.He * (d.Hcq + Nkr) * ed + T * d.He * ed + (q8 and (d.Hcq + Nkr + T) * 4)
     k1_flop = 2 * T * d.He * (d.Hcq + Nkr)
-    k2_bytes = (T * (d.Hckv + d.Dr) * 2 + T * d.Hcq * eu + T * 2 * d.Dr * 2 + T * 8
+    k2_bytes = (cache + T * d.Hcq * eu + T * 2 * d.Dr * 2 + T * 8
                 + (u8 and T * 4) + (sm and d.Hcq * 4))
     k3_bytes = (d.Hcq * W * eu + T * d.Hcq * eu + T * d.N * d.D * 2
                 + T * d.N * d.Dr * 2 + T * 2 * d.Dr * 2 + (u8 and W * 4 + T * 4))
@@ -53,7 +56,7 @@ def algorithmic(inp, T):
     weights = d.He * (d.Hcq + Nkr) * ed + d.Hcq * W * eu + d.N * d.D * d.Hckv * 2
     # inputs read once, outputs written once, the scales of the scenario
     step_bytes = (weights + T * d.He * ed + T * 2 * d.Dr * 2 + T * 8 + T * d.N * d.Hckv * qo
-                  + T * d.N * d.Dr * 2 + T * (d.Hckv + d.Dr) * 2
+                  + T * d.N * d.Dr * 2 + cache
                   + (q8 and (T + d.Hcq + Nkr + T * d.N) * 4) + (u8 and W * 4) + (sm and d.Hcq * 4))
     return dict(k1_bytes=k1_bytes, k1_flop=k1_flop, k2_bytes=k2_bytes, k3_bytes=k3_bytes,
                 k3_flop=k3_flop, k4_bytes=k4_bytes, k4_flop=k4_flop, weights=weights,
@@ -108,7 +111,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_t32",
                     choices=["decode_t32", "decode_t256", "prefill_t8192", "int8_decode_t128",
-                             "partial_decode_t32", "tiny_t4"])
+                             "partial_decode_t32", "int8_kvq_decode_t128", "tiny_t4"])
     ap.add_argument("--replicas", type=int, default=0, help="weight replicas (0 = enough to "
                     "exceed twice the Infinity Cache)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -248,6 +251,7 @@ def main():
                    "N": d.N, "D": d.D, "Dr": d.Dr, "block_num": wl.block_num,
                    "block_size": wl.block_size, "weight_replicas": R,
                    "query_out": "int8" if inp["quant"] else "bf16",
+                   "kv_cache": "int8" if inp.get("kv_quant", False) else "bf16",
                    "weights": "row-major" if args.row_major else "packed"},
         "roofline": roof,
         "path_roofline": path,

@@ -57,14 +57,14 @@ class Desc(ctypes.Structure):
                 ("max_tokens", ctypes.c_int64),
                 ("eps_cq", ctypes.c_double), ("eps_ckv", ctypes.c_double),
                 ("in_dtype", ctypes.c_int32), ("query_dtype", ctypes.c_int32),
-                ("device", ctypes.c_int32)]
+                ("device", ctypes.c_int32), ("cache_dtype", ctypes.c_int32)]
 
 
 TENSOR_FIELDS = ("token_x", "weight_dq", "weight_uq_qr", "weight_uk", "weight_dkv_kr",
                  "gamma_cq", "gamma_ckv", "rope_sin", "rope_cos", "cache_index",
                  "kv_cache", "kr_cache", "scale_x", "scale_w_dq", "scale_w_uq_qr",
                  "scale_w_dkv_kr", "query_out", "query_rope_out", "dequant_scale_q_nope",
-                 "packed_weights", "smooth_scales_cq")
+                 "packed_weights", "smooth_scales_cq", "quant_scale_ckv", "quant_scale_ckr")
 
 
 class Tensors(ctypes.Structure):
@@ -121,9 +121,10 @@ def status_string(status: int) -> str:
 
 
 def make_desc(He, Hcq, Hckv, N, D, Dr, block_num, block_size, max_tokens, eps_cq=1e-5,
-              eps_ckv=1e-5, in_dtype=MLA_BF16, query_dtype=MLA_BF16, device=0) -> Desc:
+              eps_ckv=1e-5, in_dtype=MLA_BF16, query_dtype=MLA_BF16, device=0,
+              cache_dtype=MLA_BF16) -> Desc:
     return Desc(He, Hcq, Hckv, N, D, Dr, block_num, block_size, max_tokens, eps_cq, eps_ckv,
-                in_dtype, query_dtype, device)
+                in_dtype, query_dtype, device, cache_dtype)
 
 
 def _address(v) -> Optional[int]:

@@ -69,6 +69,13 @@ __device__ __forceinline__ int8_t quant_code(float v, float s) {
   return static_cast<int8_t>(r);
 }
 
+// static int8 code of a cache value: v times its channel's scale, rounded
+// half to even, saturated to [-128, 127] (quantScaleCkv / quantScaleCkr)
+__device__ __forceinline__ uint32_t cache_code(float v, float s) {
+  const float r = fminf(127.0f, fmaxf(-128.0f, rintf(v * s)));
+  return uint32_t(uint8_t(int8_t(r)));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
@@ -232,8 +239,10 @@ struct Ptrs {
   const uint16_t* sin;
   const uint16_t* cos;
   const int64_t* cache_index;
-  uint16_t* kv_cache;
-  uint16_t* kr_cache;
+  uint16_t* kv_cache;        // bf16 rows, or int8 rows when qs_ckv is set
+  uint16_t* kr_cache;        // bf16 rows, or int8 rows when qs_ckr is set
+  const float* qs_ckv;       // quantScaleCkv (Hckv), or NULL
+  const float* qs_ckr;       // quantScaleCkr (Dr), or NULL
   const float* sx;
   const float* sw_dq;
   const float* sw_uq_qr;
@@ -899,8 +908,19 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
       const int jk = j - cq_c;
 #pragma unroll
       for (int e = 0; e < 8; ++e) c[e] = float(double(bf2f(p.gamma_ckv[8 * jk + e])) * v[e] / rms_kv);
-      const uint2 a = pack_bf16x4(c[0], c[1], c[2], c[3]), b = pack_bf16x4(c[4], c[5], c[6], c[7]);
-      *reinterpret_cast<uint4*>(p.kv_cache + slot * d.Hckv + 8 * jk) = make_uint4(a.x, a.y, b.x, b.y);
+      if (p.qs_ckv) {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lo |= cache_code(c[e], p.qs_ckv[8 * jk + e]) << (8 * e);
+          hi |= cache_code(c[e + 4], p.qs_ckv[8 * jk + e + 4]) << (8 * e);
+        }
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(p.kv_cache) + slot * d.Hckv + 8 * jk) =
+            make_uint2(lo, hi);
+      } else {
+        const uint2 a = pack_bf16x4(c[0], c[1], c[2], c[3]), b = pack_bf16x4(c[4], c[5], c[6], c[7]);
+        *reinterpret_cast<uint4*>(p.kv_cache + slot * d.Hckv + 8 * jk) = make_uint4(a.x, a.y, b.x, b.y);
+      }
     }
   };
 #pragma unroll
@@ -934,10 +954,18 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
   const uint16_t* cs = p.cos + int64_t(t) * d.Dr;
   const uint16_t* sn = p.sin + int64_t(t) * d.Dr;
   uint16_t* kr = p.kr_cache + slot * d.Dr;
+  uint8_t* kr8 = reinterpret_cast<uint8_t*>(p.kr_cache) + slot * d.Dr;
   for (int i = lane; i < h; i += L) {
     const double a = yr[i], b = yr[i + h];
-    kr[i] = f2bf(float(a * bf2f(cs[i]) - b * bf2f(sn[i])));
-    kr[i + h] = f2bf(float(b * bf2f(cs[i + h]) + a * bf2f(sn[i + h])));
+    const float r0 = float(a * bf2f(cs[i]) - b * bf2f(sn[i]));
+    const float r1 = float(b * bf2f(cs[i + h]) + a * bf2f(sn[i + h]));
+    if (p.qs_ckr) {
+      kr8[i] = uint8_t(cache_code(r0, p.qs_ckr[i]));
+      kr8[i + h] = uint8_t(cache_code(r1, p.qs_ckr[i + h]));
+    } else {
+      kr[i] = f2bf(r0);
+      kr[i + h] = f2bf(r1);
+    }
   }
 }
 
@@ -2882,6 +2910,10 @@ mla_status check_desc(const mla_prolog_desc* d) {
       (d->query_dtype != MLA_BF16 && d->query_dtype != MLA_INT8))
     return MLA_ERR_PARAM_INVALID;
   if (d->query_dtype == MLA_INT8 && d->in_dtype != MLA_INT8) return MLA_ERR_PARAM_INVALID;
+  // quantised caches: only in the two int8 scenarios (the tables' "kv_cache
+  // quantized" columns)
+  if (d->cache_dtype != MLA_BF16 && d->cache_dtype != MLA_INT8) return MLA_ERR_PARAM_INVALID;
+  if (d->cache_dtype == MLA_INT8 && d->in_dtype == MLA_BF16) return MLA_ERR_PARAM_INVALID;
   if (d->block_num < 0 || d->max_tokens < 0 || d->max_tokens > (1 << 20))
     return MLA_ERR_PARAM_INVALID;
   if (d->block_num > 0 && (d->block_size < 16 || d->block_size > 1024 || d->block_size % 16))
@@ -2933,6 +2965,14 @@ mla_status check_tensors(const mla_prolog_desc* d, const mla_prolog_tensors* t, 
   }
   // smoothScalesCq: optional with an int8 weightUqQr, absent otherwise
   if (t->smooth_scales_cq && (!up_i8(*d) || !aligned4(t->smooth_scales_cq))) return MLA_ERR_PARAM_INVALID;
+  // quantScaleCkv with an int8 kv cache; quantScaleCkr with an int8 kr
+  // cache, which partial quantisation has and full quantisation does not
+  const bool kv8 = d->cache_dtype == MLA_INT8, kr8 = kv8 && d->in_dtype == MLA_INT8_PARTIAL;
+  if (kv8 && !t->quant_scale_ckv) return MLA_ERR_NULLPTR;
+  if (kr8 && !t->quant_scale_ckr) return MLA_ERR_NULLPTR;
+  if ((!kv8 && t->quant_scale_ckv) || (!kr8 && t->quant_scale_ckr)) return MLA_ERR_PARAM_INVALID;
+  if ((t->quant_scale_ckv && !aligned4(t->quant_scale_ckv)) || (t->quant_scale_ckr && !aligned4(t->quant_scale_ckr)))
+    return MLA_ERR_PARAM_INVALID;
   if (t->packed_weights && (reinterpret_cast<uintptr_t>(t->packed_weights) & 255u))
     return MLA_ERR_PARAM_INVALID;
   if (d->query_dtype == MLA_INT8 && !t->dequant_scale_q_nope) return MLA_ERR_NULLPTR;
@@ -3041,7 +3081,7 @@ void packed_launch(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p, 
 // the phase-1 windows over the 2N blocks, or false when the shapes are
 // outside what the kernel holds in registers.
 bool fused_geo(const mla_prolog_desc& dd, FusedGeo* fg) {
-  if (dd.in_dtype != MLA_BF16 || dd.query_dtype != MLA_BF16) return false;
+  if (dd.in_dtype != MLA_BF16 || dd.query_dtype != MLA_BF16 || dd.cache_dtype != MLA_BF16) return false;
   const PackGeo g = geo_of(dd);
   if (g.nope_w != 2 || dd.Dr != 64 || g.uk_w > 8 || g.nst_d > 4) return false;
   const int G = int(2 * dd.N), W = g.win_dq + g.win_kr;
@@ -3284,6 +3324,8 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   p.cache_index = t->cache_index;
   p.kv_cache = static_cast<uint16_t*>(t->kv_cache);
   p.kr_cache = static_cast<uint16_t*>(t->kr_cache);
+  p.qs_ckv = t->quant_scale_ckv;
+  p.qs_ckr = t->quant_scale_ckr;
   p.sx = t->scale_x; p.sw_dq = t->scale_w_dq; p.sw_uq_qr = t->scale_w_uq_qr;
   p.sw_dkv_kr = t->scale_w_dkv_kr;
   p.smooth_cq = t->smooth_scales_cq;

@@ -72,6 +72,13 @@ typedef enum { MLA_BF16 = 0, MLA_INT8 = 1, MLA_INT8_PARTIAL = 2 } mla_dtype;
  *   calculation formula"); MLA_BF16: queryOut is bf16.  As in the page's
  *   dtype table, an int8 queryOut needs in_dtype MLA_INT8 (otherwise
  *   MLA_ERR_PARAM_INVALID); int8 inputs with a bf16 queryOut are allowed.
+ * cache_dtype MLA_INT8: quantised caches (the "kv_cache quantized" columns
+ *   of the scenario and dtype tables), only with in_dtype MLA_INT8 or
+ *   MLA_INT8_PARTIAL.  The kv cache holds int8 codes of c^KV with
+ *   quant_scale_ckv; with partial quantisation the kr cache holds int8
+ *   codes of k^R with quant_scale_ckr, while full quantisation keeps a bf16
+ *   kr cache.  A code is the value times its channel's scale, rounded half
+ *   to even and saturated to [-128, 127].  MLA_BF16: bf16 caches.
  * max_tokens bounds T of every run; it sizes the handle's workspace.
  * eps_cq / eps_ckv: the two RmsNorm epsilons (the page recommends 1e-5).
  */
@@ -83,6 +90,7 @@ typedef struct {
   int32_t in_dtype;    /* mla_dtype */
   int32_t query_dtype; /* mla_dtype */
   int32_t device;      /* HIP device ordinal the handle and all tensors live on */
+  int32_t cache_dtype; /* mla_dtype: MLA_BF16, or MLA_INT8 (quantised caches) */
 } mla_prolog_desc;
 
 /*
@@ -100,9 +108,10 @@ typedef struct {
  *                                       entries outside [0, block_num*block_size)
  *                                       are skipped; duplicates are undefined
  *   kv_cache (block_num, block_size, 1, Hckv), kr_cache (.., Dr)
- *                                       bf16, updated in place at the named
- *                                       slots only; may be NULL iff block_num
- *                                       is 0 (no cache update)
+ *                                       bf16 (or int8, see cache_dtype),
+ *                                       updated in place at the named slots
+ *                                       only; may be NULL iff block_num is 0
+ *                                       (no cache update)
  *   scale_x (T), scale_w_dq (Hcq), scale_w_uq_qr (N*(D+Dr)),
  *   scale_w_dkv_kr (Hckv+Dr)            fp32, int8 mode only, else NULL;
  *                                       partial quantisation takes
@@ -119,6 +128,10 @@ typedef struct {
  *   smooth_scales_cq (Hcq)              fp32 smoothScalesCq, optional (NULL =
  *                                       none) with an int8 weightUqQr, NULL
  *                                       otherwise
+ *   quant_scale_ckv (Hckv), quant_scale_ckr (Dr)
+ *                                       fp32 quantScaleCkv / quantScaleCkr:
+ *                                       each given exactly when its cache is
+ *                                       int8 (see cache_dtype), else NULL
  * Outputs must not alias inputs.
  */
 typedef struct {
@@ -143,6 +156,8 @@ typedef struct {
   float* dequant_scale_q_nope;
   const void* packed_weights; /* optional: the four weights in the library's packed layout */
   const float* smooth_scales_cq;
+  const float* quant_scale_ckv;
+  const float* quant_scale_ckr;
 } mla_prolog_tensors;
 
 typedef struct mla_prolog* mla_prolog_t;

@@ -35,6 +35,9 @@ def upload(inp: Dict[str, object], device="cuda:0", query_int8=None) -> Dict[str
         names["dequant_scale_w_uq_qr"] = "scale_w_uq_qr"
     if inp.get("smooth_scales_cq") is not None:
         names["smooth_scales_cq"] = "smooth_scales_cq"
+    for k in ("quant_scale_ckv", "quant_scale_ckr"):
+        if inp.get(k) is not None:
+            names[k] = k
     out = {lib_name: _tensor(np.asarray(inp[key]), device) for key, lib_name in names.items()
            if key in inp}
     out["query_out"] = torch.zeros((T, d.N, d.Hckv), dtype=torch.int8 if q8 else torch.bfloat16,
@@ -63,4 +66,5 @@ def desc_args(inp: Dict[str, object], max_tokens=None, query_int8=None) -> Dict[
                 block_num=int(inp["block_num"]), block_size=int(inp["block_size"]),
                 max_tokens=int(inp["T"]) if max_tokens is None else int(max_tokens),
                 eps_cq=float(inp["eps_cq"]), eps_ckv=float(inp["eps_ckv"]),
-                in_dtype=2 if inp.get("partial", False) else int(quant), query_dtype=int(q8))
+                in_dtype=2 if inp.get("partial", False) else int(quant), query_dtype=int(q8),
+                cache_dtype=int(bool(inp.get("kv_quant", False))))

@@ -3,7 +3,10 @@
 bf16 outputs: |gpu - ref| <= 1e-2 + 1e-2 |ref| per element.  int8 q^N: at most
 1 LSB apart, on at most 0.1% of the elements.  Dequantisation scales: relative
 error <= 1e-2.  Cache slots: every slot not named by cacheIndex keeps its bits
-exactly; named slots hold the row within the bf16 tolerance.
+exactly; named slots hold the row within the bf16 tolerance.  int8 (quantised)
+cache rows: every code equals the oracle's, except that a value v * scale
+within TIE_BAND of a rounding tie may round either way (the same reasoning as
+for c^Q below: y's summation order is not fixed).
 
 An int8 c^Q taken from a floating-point down-projection (partial
 quantisation) is decided from y summed in fp32 on the device and in double
@@ -116,9 +119,24 @@ def check_queries(got, ref, rows, int8_query, allow=None):
         assert_bf16_close(got["query_out"][rows], ref["query_out"], "query_out", allow_qn)
 
 
+def assert_cache_codes(got, ref_codes, v, scale, what):
+    """int8 cache codes against the oracle's: equal, or one apart where the
+    float32 value v * scale lies within TIE_BAND of a rounding tie."""
+    g = np.asarray(got).astype(np.int32)
+    r = np.asarray(ref_codes).astype(np.int32)
+    x = np.abs(np.asarray(v, np.float64).astype(np.float32) * np.asarray(scale, np.float32)).astype(np.float64)
+    tie = np.abs(x - np.floor(x) - 0.5) < TIE_BAND
+    ok = (g == r) | (tie & (np.abs(g - r) == 1))
+    if not ok.all():
+        i = np.argwhere(~ok)[0]
+        raise AssertionError(f"{what}: {np.count_nonzero(~ok)} of {ok.size} codes differ; first at {tuple(i)}: "
+                             f"gpu {g[tuple(i)]} ref {r[tuple(i)]}")
+
+
 def check_caches(inp, kv_after, kr_after, ref, rows):
     """Untouched slots bit-exact; slots of ``rows`` within tolerance of the
-    oracle's rows; every in-range named slot written."""
+    oracle's rows (int8 rows: assert_cache_codes, with the oracle's c_kv and
+    k_r intermediates in ``ref``); every in-range named slot written."""
     d = inp["dims"]
     nslots = int(inp["block_num"]) * int(inp["block_size"])
     kv0 = np.asarray(inp["kv_cache"]).reshape(nslots, d.Hckv)
@@ -131,10 +149,20 @@ def check_caches(inp, kv_after, kr_after, ref, rows):
     named[valid] = True
     assert np.array_equal(kv1[~named], kv0[~named]), "kv cache changed outside the named slots"
     assert np.array_equal(kr1[~named], kr0[~named]), "kr cache changed outside the named slots"
+    kv8 = bool(inp.get("kv_quant", False))
+    kr8 = kv8 and bool(inp.get("partial", False))
     for r, t in enumerate(rows):
         s = int(idx[t])
         if 0 <= s < nslots:
-            assert_bf16_close(kv1[s], ref["kv_rows"][r], f"kv cache slot {s} (token {t})")
-            assert_bf16_close(kr1[s], ref["kr_rows"][r], f"kr cache slot {s} (token {t})")
+            if kv8:
+                assert_cache_codes(kv1[s], ref["kv_rows"][r], ref["c_kv"][r], inp["quant_scale_ckv"],
+                                   f"kv cache slot {s} (token {t})")
+            else:
+                assert_bf16_close(kv1[s], ref["kv_rows"][r], f"kv cache slot {s} (token {t})")
+            if kr8:
+                assert_cache_codes(kr1[s], ref["kr_rows"][r], ref["k_r"][r], inp["quant_scale_ckr"],
+                                   f"kr cache slot {s} (token {t})")
+            else:
+                assert_bf16_close(kr1[s], ref["kr_rows"][r], f"kr cache slot {s} (token {t})")
     if valid.size:
         assert not np.all(kv1[valid] == kv0[valid], axis=1).any(), "a named kv slot was not written"

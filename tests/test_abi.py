@@ -35,8 +35,12 @@ def model_desc(**kw):
 FAKE = 1 << 40   # an aligned address; validate never dereferences it
 
 
-def fake_tensors(q8=False, in8=False, partial=False, smooth=False):
+def fake_tensors(q8=False, in8=False, partial=False, smooth=False, kvq=False):
     t = {f: FAKE for f in mla.TENSOR_FIELDS}
+    if not kvq:
+        t["quant_scale_ckv"] = None
+    if not (kvq and partial):
+        t["quant_scale_ckr"] = None
     if not in8:
         for f in ("scale_x", "scale_w_dq", "scale_w_dkv_kr"):
             t[f] = None
@@ -57,6 +61,11 @@ def test_valid_descriptions():
     part = model_desc(in_dtype=mla.MLA_INT8_PARTIAL)
     assert mla.validate(part, fake_tensors(partial=True), 32) == mla.MLA_OK
     assert mla.validate(part, fake_tensors(partial=True, smooth=True), 32) == mla.MLA_OK
+    # quantised caches: kv (full quantisation), kv and kr (partial)
+    assert mla.validate(model_desc(in_dtype=1, query_dtype=1, cache_dtype=1),
+                        fake_tensors(True, True, kvq=True), 128) == mla.MLA_OK
+    assert mla.validate(model_desc(in_dtype=2, cache_dtype=1),
+                        fake_tensors(partial=True, kvq=True), 32) == mla.MLA_OK
     # the bf16 down-projection of partial quantisation keeps the bf16 size rules
     assert mla.validate(model_desc(in_dtype=mla.MLA_INT8_PARTIAL, He=7176, Hckv=504)) == mla.MLA_OK
     tiny = mla.make_desc(256, 64, 32, 2, 16, 8, 4, 16, 4)
@@ -81,6 +90,8 @@ def test_valid_descriptions():
     (dict(in_dtype=2, query_dtype=1), mla.MLA_ERR_PARAM_INVALID),   # int8 q^N: full quantisation only
     (dict(in_dtype=2, Hcq=1544), mla.MLA_ERR_UNSUPPORTED),
     (dict(in_dtype=2, D=120), mla.MLA_ERR_UNSUPPORTED),
+    (dict(cache_dtype=1), mla.MLA_ERR_PARAM_INVALID),             # quantised caches: int8 scenarios only
+    (dict(in_dtype=1, cache_dtype=2), mla.MLA_ERR_PARAM_INVALID),
 ])
 def test_bad_descriptions(kw, code):
     assert mla.validate(model_desc(**kw)) == code
@@ -111,6 +122,16 @@ def test_bad_run_arguments():
     t = fake_tensors(partial=True); t["scale_w_uq_qr"] = None
     assert mla.validate(dp, t, 8) == mla.MLA_ERR_NULLPTR
     t = fake_tensors(partial=True); t["scale_x"] = FAKE
+    assert mla.validate(dp, t, 8) == mla.MLA_ERR_PARAM_INVALID
+    # cache scales: exactly those of the int8 caches
+    dk = model_desc(in_dtype=1, cache_dtype=1)
+    assert mla.validate(dk, fake_tensors(in8=True), 8) == mla.MLA_ERR_NULLPTR          # no quantScaleCkv
+    t = fake_tensors(in8=True, kvq=True); t["quant_scale_ckr"] = FAKE                 # kr stays bf16 here
+    assert mla.validate(dk, t, 8) == mla.MLA_ERR_PARAM_INVALID
+    dpk = model_desc(in_dtype=2, cache_dtype=1)
+    t = fake_tensors(partial=True, kvq=True); t["quant_scale_ckr"] = None
+    assert mla.validate(dpk, t, 8) == mla.MLA_ERR_NULLPTR
+    t = fake_tensors(partial=True); t["quant_scale_ckv"] = FAKE                       # bf16 caches
     assert mla.validate(dp, t, 8) == mla.MLA_ERR_PARAM_INVALID
 
 

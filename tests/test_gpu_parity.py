@@ -56,7 +56,8 @@ def full_check(inp, query_int8=None, rows=None, packed=False, repeat=1, prerun_n
     say(f"case {inp['workload']} T={inp['T']} dims={inp['dims']} q8={q8} rows={len(rows)} packed={packed}")
     got = run_gpu(inp, query_int8=query_int8, packed=packed, repeat=repeat, prerun_negated=prerun_negated)
     partial = bool(inp.get("partial", False))
-    ref = oracle.run(inp, tokens=rows, query_int8=query_int8, caches=False, intermediates=partial)
+    ref = oracle.run(inp, tokens=rows, query_int8=query_int8, caches=False,
+                     intermediates=partial or bool(inp.get("kv_quant", False)))
     allow = None
     if partial:
         # int8 c^Q from a float y: codes at a rounding tie may go either way
@@ -463,3 +464,67 @@ def test_int8_smoothed(name):
     full_check(inp)
     full_check(inp, packed=True)
     full_check(inp, query_int8=False, packed=True)
+
+
+# ---- KV-cache quantisation (quantScaleCkv / quantScaleCkr) --------------------
+# int8 kv cache in full quantisation (kr stays bf16); int8 kv and kr caches in
+# partial quantisation.  The cache rows are written by the norm kernel on
+# every path; the cases cover the row-major, paired, tiled medium and tiled
+# large launches, empty caches and skipped slots.
+KVQ = {
+    "kvq_full_t9": custom_workload("kvq_full_t9", T=9, dims=Dims(He=256, Hcq=64, Hckv=32, N=2, D=16, Dr=16),
+                                   block_num=2, block_size=16, quant=True, kv_quant=True, seed=101),
+    "kvq_full_pair_t16": custom_workload("kvq_full_pair_t16", T=16,
+                                         dims=Dims(He=512, Hcq=256, Hckv=128, N=4, D=128, Dr=64),
+                                         block_num=2, block_size=16, quant=True, kv_quant=True, seed=102),
+    "kvq_full_t130": custom_workload("kvq_full_t130", T=130,
+                                     dims=Dims(He=1024, Hcq=192, Hckv=512, N=3, D=128, Dr=64),
+                                     block_num=16, block_size=16, quant=True, kv_quant=True, smooth=True, seed=103),
+    "kvq_partial_t5": custom_workload("kvq_partial_t5", T=5, dims=Dims(He=512, Hcq=256, Hckv=128, N=4, D=128, Dr=64),
+                                      block_num=2, block_size=16, partial=True, smooth=True, kv_quant=True, seed=104),
+    "kvq_partial_t37": custom_workload("kvq_partial_t37", T=37, dims=Dims(He=264, Hcq=80, Hckv=40, N=3, D=32, Dr=16),
+                                       block_num=4, block_size=16, partial=True, kv_quant=True, seed=105),
+    "kvq_partial_t300": custom_workload("kvq_partial_t300", T=300, dims=Dims(He=520, Hcq=128, Hckv=64, N=2, D=32, Dr=16),
+                                        block_num=20, block_size=16, partial=True, smooth=True, kv_quant=True, seed=106),
+    "kvq_partial_t2100": custom_workload("kvq_partial_t2100", T=2100,
+                                         dims=Dims(He=264, Hcq=64, Hckv=40, N=3, D=32, Dr=16),
+                                         block_num=160, block_size=16, partial=True, kv_quant=True, seed=107),
+}
+
+
+@pytest.mark.parametrize("name", ["kvq_full_t9", "kvq_partial_t37"])
+def test_quantised_cache_row_major(name):
+    full_check(synth.make_inputs(KVQ[name]))
+
+
+@pytest.mark.parametrize("name", list(KVQ))
+def test_quantised_cache_packed(name):
+    inp = synth.make_inputs(KVQ[name])
+    full_check(inp, packed=True, repeat=2, prerun_negated=True)
+
+
+def test_quantised_cache_skipped_slots_and_no_blocks():
+    inp = synth.make_inputs(KVQ["kvq_partial_t5"])
+    n = inp["block_num"] * inp["block_size"]
+    inp["cache_index"] = np.array([-1, n, 0, n + 3, 1], dtype=np.int64)
+    full_check(inp, packed=True)
+    # no cache blocks: the queries are still computed and nothing is written
+    wl = custom_workload("kvq_noblocks", T=5, dims=Dims(He=512, Hcq=256, Hckv=128, N=4, D=128, Dr=64),
+                         block_num=1, block_size=16, partial=True, kv_quant=True, seed=108)
+    inp0 = synth.make_inputs(wl)
+    say("case kvq block_num=0")
+    t = dev.upload(inp0)
+    t.pop("kv_cache"), t.pop("kr_cache")
+    args = dev.desc_args(inp0)
+    args["block_num"] = 0
+    with mla.MlaProlog(mla.make_desc(**args)) as h:
+        h.run(t, 5)
+        torch.cuda.synchronize()
+    ref = oracle.run(inp0, caches=False, intermediates=True)
+    rows = np.arange(5)
+    check_queries({k: dev.bits(v) for k, v in t.items()}, ref, rows, False, tie_allowance(inp0, ref, rows)[:2])
+
+
+def test_full_size_int8_quantised_cache_packed():
+    inp = synth.make_inputs(synth.workload("int8_kvq_decode_t128"))
+    full_check(inp, rows=sample_rows(int(inp["T"])), packed=True)
