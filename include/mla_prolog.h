@@ -199,7 +199,14 @@ mla_status mla_prolog_create(const mla_prolog_desc* desc, mla_prolog_t* out);
  * ready when the stream reaches this point.  T = 0 enqueues nothing.  A
  * handle's workspace is shared by its runs: runs of one handle on different
  * streams must be ordered by the caller.  The result is deterministic: the
- * same inputs give bit-identical outputs. */
+ * same inputs give bit-identical outputs.
+ * Small-T runs on packed weights (T <= 32) launch kernels whose blocks wait
+ * for data from other blocks of the same launch, so such a run needs those
+ * blocks resident on the device together: kernels from other streams or
+ * processes must not occupy the device while it runs.  Otherwise a bounded
+ * wait gives up and mla_prolog_check reports the run; MLA_PROLOG_FUSED=0
+ * (see mla_prolog_create) keeps small-T runs on kernels that wait only
+ * between the two blocks of a head. */
 mla_status mla_prolog_run(mla_prolog_t handle, const mla_prolog_tensors* tensors, int64_t T,
                           void* stream);
 
