@@ -2806,8 +2806,10 @@ Plan make_plan(const mla_prolog_desc& d, int64_t T) {
 // wave per 64-column window, He split so that about kTiledK1Blocks blocks
 // run (above 128 tokens: LDS-staged 256 x 128 blocks, about one per CU);
 // K3 with one 64-token wave per window up to 128 tokens, LDS-staged
-// 256 x 128 blocks above; K4 with eight 64-column waves per 16*mt tokens.
-// The int8-query K4 always takes 64 tokens x the whole Hckv row per block.
+// 256 x 128 blocks above; an int8 K1 or K3 switches to LDS-staged
+// 128 x 128 blocks from 65 tokens on.  K4 with eight 64-column waves per
+// 16*mt tokens.  The int8-query K4 always takes 64 tokens x the whole Hckv
+// row per block.
 constexpr int kTiledLargeT = 2048;
 constexpr int kTiledK1Blocks = 512;   // medium: one-wave blocks
 
