@@ -1728,7 +1728,7 @@ __global__ __launch_bounds__(512) void k34_pair(Dims d, Ptrs p, PackGeo pg) {
 // ---------------------------------------------------------------------------
 constexpr int kFusedP1 = 4;       // phase-1 k-stages a wave may have
 constexpr int kFusedPF = 4;       // phase-3 register ring: k-stages a wave has in flight
-constexpr int kFusedPE = 2;       // of those, the ones issued before the wait
+constexpr int kFusedPE = 3;       // of those, the ones issued before the wait
 constexpr int kFusedStages = 7;   // phase-3 k-stages a wave may have (waves 1..7)
 constexpr int kFusedMaxSplits = 8;
 constexpr int kFusedFlagStride = 16;   // uint32 words between the fused kernel's flags
