@@ -528,3 +528,27 @@ def test_quantised_cache_skipped_slots_and_no_blocks():
 def test_full_size_int8_quantised_cache_packed():
     inp = synth.make_inputs(synth.workload("int8_kvq_decode_t128"))
     full_check(inp, rows=sample_rows(int(inp["T"])), packed=True)
+
+
+# ---- the largest head dimensions the library takes (D = Hckv = 512, Dr = 64) --
+# At small T these shapes run the per-window up-projection and W^UK kernels
+# (16 D-stages, eight 64-column windows per head); above 32 tokens the tiled
+# kernels.
+MAXD = Dims(He=256, Hcq=128, Hckv=512, N=2, D=512, Dr=64)
+
+
+@pytest.mark.parametrize("T", [5, 40])
+def test_max_head_dims_bf16(T):
+    wl = custom_workload(f"maxd_t{T}", T=T, dims=MAXD, block_num=4, block_size=16, seed=110 + T)
+    inp = synth.make_inputs(wl)
+    full_check(inp)
+    full_check(inp, packed=True)
+
+
+@pytest.mark.parametrize("T", [5, 40])
+def test_max_head_dims_int8(T):
+    wl = custom_workload(f"maxd_q8_t{T}", T=T, dims=MAXD, block_num=4, block_size=16, quant=True,
+                         kv_quant=True, seed=120 + T)
+    inp = synth.make_inputs(wl)
+    full_check(inp, packed=True)
+    full_check(inp, query_int8=False, packed=True)
