@@ -3,25 +3,33 @@
 // The operation is the Multi-Head Latent Attention prolog of the Ascend
 // operator page aclnnMlaPrologV2WeightNz ("Function", formula block); the
 // rotate-half RoPE is the mode the aclnnMlaPreprocess page fixes
-// (constraints, rope mode).  Four stream-ordered kernels:
+// (constraints, rope mode).  Its steps:
 //
-//   K1 down_proj        y = x [W^DQ | W^DKV | W^KR], split-K partials (fp32,
-//                       or exact int32 in int8 mode) into the workspace
-//   K2 norm             fixed-order split-K sum, both RmsNorms (in double),
-//                       k^R RoPE, kv/kr rows scattered at cacheIndex, c^Q
-//                       emitted as bf16 (or per-token int8 + scale)
-//   K3 up_proj          u = c^Q [W^UQ | W^QR] per head; nope columns -> q^C
-//                       (bf16, workspace), rope columns -> RoPE -> queryRopeOut
-//   K4 uk               q^N = q^C W^UK[h] per head; bf16 store, or per-(token,
-//                       head) dynamic int8 with its dequantisation scale
+//   down-projection   y = x [W^DQ | W^DKV | W^KR] (fp32 accumulation, or
+//                     exact int32 with int8 inputs)
+//   norms             both RmsNorms (in double), c^Q as bf16 or per-token
+//                     int8 (+ smoothScalesCq), c^KV and RoPE(k^R) scattered
+//                     to the cacheIndex slots (bf16, or static int8 codes)
+//   up-projection     u = c^Q [W^UQ | W^QR] per head; nope columns -> q^C
+//                     (bf16), rope columns -> RoPE -> queryRopeOut
+//   W^UK product      q^N = q^C W^UK[h] per head; bf16, or per-(token, head)
+//                     dynamic int8 with its dequantisation scale
+//
+// Execution paths, by token count and weight layout:
+//   - packed weights (mla_prolog_pack_weights: 64-column windows stored as
+//     4 KB k-stages in MFMA operand order), T <= 32, bf16: one launch
+//     (k_fused) whose blocks hand partial results to one another through
+//     agent-scope tagged words and flags;
+//   - packed weights, T <= 32 otherwise: k1_packed, k2_norm, then the
+//     up-projection and W^UK product (k34_pair, k34_stream, or k3_packed
+//     and k4_packed);
+//   - packed weights, T > 32: k1_tiled, k2_norm, k3_tiled, k4_tiled
+//     (direct or LDS-staged tiles, by shape class);
+//   - row-major weights only: k_down_proj, k2_norm, k_up_proj, k_uk.
 //
 // All matrix products run on MFMA (v_mfma_f32_16x16x32_bf16,
-// v_mfma_i32_16x16x64_i8).  Weights are (k, n) row-major, so a weight tile is
-// staged through LDS with an odd dword row stride and read back column-wise
-// (one k-run of 8 or 16 elements per lane) without bank conflicts; activation
-// fragments are k-contiguous and come straight from global memory.
-// There are no float atomics: every reduction has a fixed order, so a run is
-// deterministic.
+// v_mfma_i32_16x16x64_i8).  There are no float atomics: every reduction has
+// a fixed order, so a run is deterministic.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -1742,20 +1750,6 @@ struct FusedGeo {
   int spin;            // poll steps a wait makes before it gives up
 };
 
-__device__ __forceinline__ void xstore32(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void xstored(double* p, double v) {
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ double xloadd(const double* p) {
-  return __builtin_bit_cast(double, __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT));
-}
-__device__ __forceinline__ float xloadf(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 // a 16-byte buffer load coherent at agent scope (the sc1 cache policy of an
 // agent-scope atomic load)
 __device__ __forceinline__ uint4 bload16c(rsrc_t r, uint32_t off) {
@@ -1763,9 +1757,6 @@ __device__ __forceinline__ uint4 bload16c(rsrc_t r, uint32_t off) {
 }
 __device__ __forceinline__ float bload4c(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 16));
-}
-__device__ __forceinline__ double bload8c(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 16));
 }
 __device__ __forceinline__ uint2 bload8u(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 16));
@@ -2741,7 +2732,6 @@ __global__ __launch_bounds__(64 * WM * WN) void k4_tiled(Dims d, Ptrs p, PackGeo
 constexpr int kStreamMaxT = 32;
 
 struct Plan {
-  bool packed;       // small-T path on packed weights (set by the run)
   int Sp, sps;       // packed K1: split count, stages per split
   bool stream;       // T small enough for the packed kernels
   int mt1, S, kps;   // K1 rows per tile (16*mt1), split count, k per split
@@ -2768,7 +2758,6 @@ int mt_for(int64_t T, int cap) {
 Plan make_plan(const mla_prolog_desc& d, int64_t T) {
   Plan pl;
   const bool i8 = down_i8(d);
-  pl.packed = false;
   pl.stream = T <= kStreamMaxT;
   {
     const PackGeo g = geo_of(d);
