@@ -3356,14 +3356,18 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   p.packed = static_cast<const uint8_t*>(t->packed_weights);
   FusedGeo fg;
   if (p.packed && pl.stream && h->fused_fit[pl.mt1 == 1 ? 0 : 1] && fused_geo(dd, &fg)) {
-    fg.run = ++h->fused_run;
+    // run numbers 1, 2, ...: 0 is what the workspace starts with, so a wrap
+    // of the counter skips it
+    const uint32_t last = h->fused_run;
+    if (++h->fused_run == 0) h->fused_run = 1;
+    fg.run = h->fused_run;
     fg.spin = h->fused_spin;
     const PackGeo g = geo_of(dd);
     if (pl.mt1 == 1) k_fused<1><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g, fg);
     else k_fused<2><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g, fg);
     mark(-2);
     const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) --h->fused_run;
+    if (e != hipSuccess) h->fused_run = last;
     if (prev != dd.device) (void)hipSetDevice(prev);
     return e == hipSuccess ? MLA_OK : MLA_ERR_RUNTIME;
   }
