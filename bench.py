@@ -135,7 +135,8 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the prolog shards by tokens or heads with no exchange; see the design notes)",
+              "(the prolog shards by tokens, or by heads, with no exchange between GPUs, so one "
+              "GPU's share at the full shapes is what is measured)",
               file=sys.stderr)
         sys.exit(2)
 
