@@ -1739,6 +1739,7 @@ constexpr int kFusedPF = 4;       // phase-3 register ring: k-stages a wave has 
 constexpr int kFusedPE = 3;       // of those, the ones issued before the wait
 constexpr int kFusedStages = 7;   // phase-3 k-stages a wave may have (waves 1..7)
 constexpr int kFusedMaxSplits = 8;
+constexpr int kFusedRowSets = 2;  // rows per lane polled together in the handoffs (two per pass)
 constexpr int kFusedFlagStride = 16;   // uint32 words between the fused kernel's flags
 constexpr int kFusedSpin = 1 << 20;   // poll steps before a wait gives up (about a second)
 
@@ -1894,46 +1895,62 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
   if (w == 0 && S) {
     {
       const rsrc_t Fp = make_rsrc(p.fpart, int64_t(fg.p1) * R * 64 * 8);
-      for (int rb = r0; rb < r1; rb += 2) {
-        const int r = rb + (lane >> 5);
-        const bool act = r < r1;
+      // kFusedRowSets row pairs per poll: the rows of a block are published
+      // together, so one round trip serves them all
+      for (int rb = r0; rb < r1; rb += 2 * kFusedRowSets) {
+        int rr[kFusedRowSets];
+        bool act[kFusedRowSets];
+#pragma unroll
+        for (int u = 0; u < kFusedRowSets; ++u) {
+          rr[u] = rb + 2 * u + (lane >> 5);
+          act[u] = rr[u] < r1;
+        }
         // S <= kFusedMaxSplits; the words past S are not waited for
-        uint2 v[kFusedMaxSplits][2];
+        uint2 v[kFusedRowSets][kFusedMaxSplits][2];
         int n = 0;
         for (;;) {
 #pragma unroll
-          for (int k = 0; k < kFusedMaxSplits; ++k)
+          for (int u = 0; u < kFusedRowSets; ++u)
 #pragma unroll
-            for (int e = 0; e < 2; ++e)
-              v[k][e] = bload8u(Fp, act && k < S ? uint32_t(((jfirst + k) * R + r) * 64 + 2 * q2 + e) * 8u : kOOB);
+            for (int k = 0; k < kFusedMaxSplits; ++k)
+#pragma unroll
+              for (int e = 0; e < 2; ++e)
+                v[u][k][e] = bload8u(Fp, act[u] && k < S ? uint32_t(((jfirst + k) * R + rr[u]) * 64 + 2 * q2 + e) * 8u
+                                                       : kOOB);
           bool ok = true;
 #pragma unroll
-          for (int k = 0; k < kFusedMaxSplits; ++k)
+          for (int u = 0; u < kFusedRowSets; ++u)
 #pragma unroll
-            for (int e = 0; e < 2; ++e) ok &= !(act && k < S) || v[k][e].y == run;
+            for (int k = 0; k < kFusedMaxSplits; ++k)
+#pragma unroll
+              for (int e = 0; e < 2; ++e) ok &= !(act[u] && k < S) || v[u][k][e].y == run;
           if (fused_poll_done(ok, n, fg.spin, err)) break;
         }
-        float y[2] = {0, 0};
 #pragma unroll
-        for (int k = 0; k < kFusedMaxSplits; ++k)
+        for (int u = 0; u < kFusedRowSets; ++u) {
+          const int r = rr[u];
+          float y[2] = {0, 0};
 #pragma unroll
-          for (int e = 0; e < 2; ++e) y[e] += __uint_as_float(v[k][e].x);   // words past S read zeros
-        // the row's sum of squares over the window (c^KV columns only in the
-        // c^KV / k^R windows), tagged
-        double ss = 0.0;
+          for (int k = 0; k < kFusedMaxSplits; ++k)
 #pragma unroll
-        for (int e = 0; e < 2; ++e)
-          if (qwin || col0 + e < d.Hckv) ss += double(y[e]) * double(y[e]);
+            for (int e = 0; e < 2; ++e) y[e] += __uint_as_float(v[u][k][e].x);   // words past S read zeros
+          // the row's sum of squares over the window (c^KV columns only in
+          // the c^KV / k^R windows), tagged
+          double ss = 0.0;
 #pragma unroll
-        for (int o = 1; o < 32; o <<= 1) ss += __shfl_xor(ss, o, 64);
-        if (act && q2 == 0) xstore64(p.fss + (j * 32 + r) * 2, make_uint2(__float_as_uint(float(ss)), run));
-        if (!act) continue;
-        if (qwin) {
-          ylds[r * 64 + 2 * q2] = y[0];
-          ylds[r * 64 + 2 * q2 + 1] = y[1];
-        } else if (col0 < d.Hckv + d.Dr) {
-          // Hckv + Dr is even: the lane's 2 columns are both in the row
-          xstore64(p.fykr + r * (d.Hckv + d.Dr) + col0, make_uint2(__float_as_uint(y[0]), __float_as_uint(y[1])));
+          for (int e = 0; e < 2; ++e)
+            if (qwin || col0 + e < d.Hckv) ss += double(y[e]) * double(y[e]);
+#pragma unroll
+          for (int o = 1; o < 32; o <<= 1) ss += __shfl_xor(ss, o, 64);
+          if (act[u] && q2 == 0) xstore64(p.fss + (j * 32 + r) * 2, make_uint2(__float_as_uint(float(ss)), run));
+          if (!act[u]) continue;
+          if (qwin) {
+            ylds[r * 64 + 2 * q2] = y[0];
+            ylds[r * 64 + 2 * q2 + 1] = y[1];
+          } else if (col0 < d.Hckv + d.Dr) {
+            // Hckv + Dr is even: the lane's 2 columns are both in the row
+            xstore64(p.fykr + r * (d.Hckv + d.Dr) + col0, make_uint2(__float_as_uint(y[0]), __float_as_uint(y[1])));
+          }
         }
       }
     }
@@ -1961,40 +1978,57 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         const rsrc_t Sp = make_rsrc(p.fss, int64_t(pg.win_dq) * 32 * 8);
-        for (int rb = r0; rb < r1; rb += 2) {
-          const int r = rb + (lane >> 5);
-          const bool act = r < r1;
-          // lane q2 adds windows q2, q2 + 32, ..., then the row's 32 lanes are
-          // added: a fixed order, the same in every block
-          double ss = 0.0;
+        for (int rb = r0; rb < r1; rb += 2 * kFusedRowSets) {
+          int rr[kFusedRowSets];
+          bool act[kFusedRowSets];
+          double ss[kFusedRowSets];
+#pragma unroll
+          for (int u = 0; u < kFusedRowSets; ++u) {
+            rr[u] = rb + 2 * u + (lane >> 5);
+            act[u] = rr[u] < r1;
+            ss[u] = 0.0;
+          }
+          // lane q2 adds windows q2, q2 + 32, ..., then the row's 32 lanes
+          // are added: a fixed order, the same in every block; the row sets
+          // are polled together
           for (int j0 = q2; j0 < pg.win_dq; j0 += 128) {
-            uint2 v[4];
+            uint2 v[kFusedRowSets][4];
             int n = 0;
             for (;;) {
 #pragma unroll
-              for (int k = 0; k < 4; ++k) {
-                const int jj = j0 + 32 * k;
-                v[k] = bload8u(Sp, act && jj < pg.win_dq ? uint32_t(jj * 32 + r) * 8u : kOOB);
-              }
+              for (int u = 0; u < kFusedRowSets; ++u)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                  const int jj = j0 + 32 * k;
+                  v[u][k] = bload8u(Sp, act[u] && jj < pg.win_dq ? uint32_t(jj * 32 + rr[u]) * 8u : kOOB);
+                }
               bool ok = true;
 #pragma unroll
-              for (int k = 0; k < 4; ++k) ok &= !(act && j0 + 32 * k < pg.win_dq) || v[k].y == run;
+              for (int u = 0; u < kFusedRowSets; ++u)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) ok &= !(act[u] && j0 + 32 * k < pg.win_dq) || v[u][k].y == run;
               if (fused_poll_done(ok, n, fg.spin, err)) break;
             }
 #pragma unroll
-            for (int k = 0; k < 4; ++k) ss += double(__uint_as_float(v[k].x));   // zeros past win_dq
+            for (int u = 0; u < kFusedRowSets; ++u)
+#pragma unroll
+              for (int k = 0; k < 4; ++k) ss[u] += double(__uint_as_float(v[u][k].x));   // zeros past win_dq
           }
 #pragma unroll
-          for (int o = 1; o < 32; o <<= 1) ss += __shfl_xor(ss, o, 64);
-          const int stg = col0 / 32;
-          if (act && stg < pg.nst_cq) {
-            const double rms = sqrt(ss / double(d.Hcq) + d.eps_cq);
-            const float c0 = float(double(bf2f(uint16_t(gq))) * double(ylds[r * 64 + 2 * q2]) / rms);
-            const float c1 = float(double(bf2f(uint16_t(gq >> 16))) * double(ylds[r * 64 + 2 * q2 + 1]) / rms);
-            uint32_t* dst = reinterpret_cast<uint32_t*>(p.cq + int64_t(r >> 4) * pg.nst_cq * 1024 + stg * 1024 +
-                                                        ((((col0 % 32) / 8) * 16 + (r & 15)) * 16) + (col0 % 8) * 2);
-            __hip_atomic_store(dst, uint32_t(f2bf(c0)) | (uint32_t(f2bf(c1)) << 16), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+          for (int u = 0; u < kFusedRowSets; ++u) {
+            const int r = rr[u];
+#pragma unroll
+            for (int o = 1; o < 32; o <<= 1) ss[u] += __shfl_xor(ss[u], o, 64);
+            const int stg = col0 / 32;
+            if (act[u] && stg < pg.nst_cq) {
+              const double rms = sqrt(ss[u] / double(d.Hcq) + d.eps_cq);
+              const float c0 = float(double(bf2f(uint16_t(gq))) * double(ylds[r * 64 + 2 * q2]) / rms);
+              const float c1 = float(double(bf2f(uint16_t(gq >> 16))) * double(ylds[r * 64 + 2 * q2 + 1]) / rms);
+              uint32_t* dst = reinterpret_cast<uint32_t*>(p.cq + int64_t(r >> 4) * pg.nst_cq * 1024 + stg * 1024 +
+                                                          ((((col0 % 32) / 8) * 16 + (r & 15)) * 16) + (col0 % 8) * 2);
+              __hip_atomic_store(dst, uint32_t(f2bf(c0)) | (uint32_t(f2bf(c1)) << 16), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+            }
           }
         }
       }
