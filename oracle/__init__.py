@@ -50,6 +50,11 @@ class Problem(ctypes.Structure):
         ("y_out", _P), ("cq_out", _P), ("u_out", _P), ("qn_out", _P),
         ("kv_int8", ctypes.c_int32), ("kr_int8", ctypes.c_int32),
         ("quant_scale_ckv", _P), ("quant_scale_ckr", _P), ("ckv_out", _P), ("kr_out", _P),
+        ("static_quant", ctypes.c_int32), ("x_norm", ctypes.c_int32), ("concat", ctypes.c_int32),
+        ("weight_nk", ctypes.c_int32), ("eps_x", ctypes.c_double),
+        ("gamma_x", _P), ("beta_x", _P), ("quant_scale_x", _P), ("quant_offset_x", _P),
+        ("bias_dqkv", _P), ("beta_cq", _P), ("quant_scale_cq", _P), ("quant_offset_cq", _P),
+        ("bias_uq_qr", _P),
     ]
 
 
@@ -71,6 +76,7 @@ def lib() -> ctypes.CDLL:
         L.mla_oracle_rmsnorm.argtypes = [_P, _P, _I64, ctypes.c_double, _P]
         L.mla_oracle_rope.argtypes = [_P, _P, _P, _I64, _P]
         L.mla_oracle_quant_int8.argtypes = [_P, _I64, _P, _P]
+        L.mla_oracle_quant_static_asym.argtypes = [_P, _I64, ctypes.c_float, ctypes.c_int, _P]
         _lib = L
     return _lib
 
@@ -119,6 +125,14 @@ def quant_int8(v):
     return q, float(s[0])
 
 
+def quant_static_asym(v, scale: float, offset: int) -> np.ndarray:
+    """The preprocess page's static asymmetric int8 codes of v."""
+    v = _f64(v)
+    q = np.empty(v.size, dtype=np.int8)
+    lib().mla_oracle_quant_static_asym(_ptr(v), v.size, float(scale), int(offset), _ptr(q))
+    return q.reshape(v.shape)
+
+
 # ---- the whole prolog ---------------------------------------------------------
 def run(inp: Dict[str, object], tokens: Optional[Sequence[int]] = None,
         round_intermediates: bool = True, query_int8: Optional[bool] = None,
@@ -130,7 +144,12 @@ def run(inp: Dict[str, object], tokens: Optional[Sequence[int]] = None,
     the partial one (only weightUqQr int8); ``inp["smooth_scales_cq"]``, when
     present, is smoothScalesCq; ``inp["kv_quant"]`` quantises the kv cache
     (and, with partial quantisation, the kr cache) with quantScaleCkv /
-    quantScaleCkr.  ``tokens`` selects the rows to compute (tokens are independent); row r of
+    quantScaleCkr.  ``inp["preprocess"]`` is the MLA preprocess page's static
+    scenario (bf16 x quantised by RmsNormQuant, int8 weights with deScale and
+    bias, c^Q quantised the same way; ``inp["x_norm"]`` False quantises x
+    without its norm); ``inp["concat"]`` its concatenated layout (queryOut
+    rows q^N | q^R, kvCache rows c^KV | k^R, no query_rope_out / kr_cache);
+    ``inp["weight_nk"]`` weights given (n, k).  ``tokens`` selects the rows to compute (tokens are independent); row r of
     every output holds token ``tokens[r]``.  With ``caches`` the returned
     ``kv_cache``/``kr_cache`` are copies of the input caches with the computed
     rows written at their cacheIndex slots.
@@ -138,6 +157,8 @@ def run(inp: Dict[str, object], tokens: Optional[Sequence[int]] = None,
     d = inp["dims"]
     T = int(inp["T"])
     quant = bool(inp["quant"])
+    static = bool(inp.get("preprocess", False))
+    concat = bool(inp.get("concat", False))
     quant_uq = quant or bool(inp.get("partial", False))
     q8 = quant if query_int8 is None else bool(query_int8)
     kv8 = bool(inp.get("kv_quant", False))
@@ -150,9 +171,9 @@ def run(inp: Dict[str, object], tokens: Optional[Sequence[int]] = None,
         return a
 
     x = arr(inp["token_x"], np.int8 if quant else np.uint16)
-    wdq = arr(inp["weight_dq"], np.int8 if quant else np.uint16)
-    wuq = arr(inp["weight_uq_qr"], np.int8 if quant_uq else np.uint16)
-    wdkv = arr(inp["weight_dkv_kr"], np.int8 if quant else np.uint16)
+    wdq = arr(inp["weight_dq"], np.int8 if quant or static else np.uint16)
+    wuq = arr(inp["weight_uq_qr"], np.int8 if quant_uq or static else np.uint16)
+    wdkv = arr(inp["weight_dkv_kr"], np.int8 if quant or static else np.uint16)
     wuk = arr(inp["weight_uk"], np.uint16)
     gcq = arr(inp["rmsnorm_gamma_cq"], np.uint16)
     gckv = arr(inp["rmsnorm_gamma_ckv"], np.uint16)
@@ -167,11 +188,12 @@ def run(inp: Dict[str, object], tokens: Optional[Sequence[int]] = None,
         n = rows.size
     N, Hckv, Dr, Hcq, D = d.N, d.Hckv, d.Dr, d.Hcq, d.D
     out = {
-        "query_out": np.zeros((n, N, Hckv), dtype=np.int8 if q8 else np.uint16),
-        "query_rope_out": np.zeros((n, N, Dr), dtype=np.uint16),
+        "query_out": np.zeros((n, N, Hckv + Dr if concat else Hckv), dtype=np.int8 if q8 else np.uint16),
         "kv_rows": np.zeros((n, Hckv), dtype=np.int8 if kv8 else np.uint16),
         "kr_rows": np.zeros((n, Dr), dtype=np.int8 if kr8 else np.uint16),
     }
+    if not concat:
+        out["query_rope_out"] = np.zeros((n, N, Dr), dtype=np.uint16)
     if q8:
         out["dequant_scale_q_nope"] = np.zeros((n, N), dtype=np.float32)
     if intermediates:
@@ -184,7 +206,7 @@ def run(inp: Dict[str, object], tokens: Optional[Sequence[int]] = None,
     kv = kr = None
     if caches and "kv_cache" in inp:
         kv = np.array(inp["kv_cache"], dtype=np.int8 if kv8 else np.uint16, copy=True)
-        kr = np.array(inp["kr_cache"], dtype=np.int8 if kr8 else np.uint16, copy=True)
+        kr = None if concat else np.array(inp["kr_cache"], dtype=np.int8 if kr8 else np.uint16, copy=True)
 
     p = Problem()
     p.T, p.He, p.Hcq, p.Hckv, p.N, p.D, p.Dr = T, d.He, Hcq, Hckv, N, D, Dr
@@ -200,8 +222,23 @@ def run(inp: Dict[str, object], tokens: Optional[Sequence[int]] = None,
         p.scale_w_dq = _ptr(arr(inp["dequant_scale_w_dq"], np.float32))
         p.scale_w_uq_qr = _ptr(arr(inp["dequant_scale_w_uq_qr"], np.float32))
         p.scale_w_dkv_kr = _ptr(arr(inp["dequant_scale_w_dkv_kr"], np.float32))
-    elif quant_uq:
+    elif quant_uq or static:
         p.scale_w_uq_qr = _ptr(arr(inp["dequant_scale_w_uq_qr"], np.float32))
+    if static:
+        p.static_quant, p.x_norm = 1, int(bool(inp.get("x_norm", True)))
+        p.scale_w_dq = _ptr(arr(inp["dequant_scale_w_dq"], np.float32))
+        p.scale_w_dkv_kr = _ptr(arr(inp["dequant_scale_w_dkv_kr"], np.float32))
+        p.eps_x = float(inp["eps_x"])
+        for f, key, dt in (("gamma_x", "rmsnorm_gamma_x", np.uint16), ("beta_x", "rmsnorm_beta_x", np.uint16),
+                           ("quant_scale_x", "quant_scale_x", np.uint16),
+                           ("quant_offset_x", "quant_offset_x", np.int8),
+                           ("bias_dqkv", "bias_dqkv", np.int32), ("beta_cq", "rmsnorm_beta_cq", np.uint16),
+                           ("quant_scale_cq", "quant_scale_cq", np.uint16),
+                           ("quant_offset_cq", "quant_offset_cq", np.int8),
+                           ("bias_uq_qr", "bias_uq_qr", np.int32)):
+            if inp.get(key) is not None:
+                setattr(p, f, _ptr(arr(inp[key], dt)))
+    p.concat, p.weight_nk = int(concat), int(bool(inp.get("weight_nk", False)))
     if inp.get("smooth_scales_cq") is not None:
         p.smooth_cq = _ptr(arr(inp["smooth_scales_cq"], np.float32))
     p.kv_int8, p.kr_int8 = int(kv8), int(kr8)
@@ -210,7 +247,7 @@ def run(inp: Dict[str, object], tokens: Optional[Sequence[int]] = None,
     if kr8:
         p.quant_scale_ckr = _ptr(arr(inp["quant_scale_ckr"], np.float32))
     p.tokens, p.n_tokens = _ptr(rows), n
-    p.query_out, p.query_rope_out = _ptr(out["query_out"]), _ptr(out["query_rope_out"])
+    p.query_out, p.query_rope_out = _ptr(out["query_out"]), _ptr(out.get("query_rope_out"))
     p.dequant_scale_q_nope = _ptr(out.get("dequant_scale_q_nope"))
     p.kv_rows, p.kr_rows = _ptr(out["kv_rows"]), _ptr(out["kr_rows"])
     if intermediates:
@@ -221,5 +258,7 @@ def run(inp: Dict[str, object], tokens: Optional[Sequence[int]] = None,
     if rc != 0:
         raise ValueError("oracle rejected the problem")
     if kv is not None:
-        out["kv_cache"], out["kr_cache"] = kv, kr
+        out["kv_cache"] = kv
+        if kr is not None:
+            out["kr_cache"] = kr
     return out

@@ -56,6 +56,22 @@
 // same real number, so only the double-rounding order is a choice (the one
 // the device uses, so that both take the same int8 decisions).
 //
+// The static scenario follows the MLA preprocess page (aclnnMlaPreprocess,
+// "Function" formulas and parameter table, quantMode 0: per-tensor static
+// asymmetric int8).  Its RmsNormQuant is read as
+//   code = saturate[-128, 127](round-half-even(f32(v) * scale) + offset),
+//   v = gamma * x / RMS(x) + beta,
+// with the scale (quantScale, one value) multiplying as the page's formula
+// writes it and the int8 offset (quantOffset) added to the rounded product;
+// the code is decided in float32.  It is applied to the bf16 input x (gamma0,
+// beta0, quantScale0, quantOffset0; without the norm when doRmsNorm is false:
+// v = x) and to y_q (gamma1, beta1, quantScale1, quantOffset1).  The products
+// with the int8 weights are exact integer sums, biased and dequantised per
+// output channel: y = (acc + bias[n]) * deScale[n].  c^KV is the plain
+// RmsNorm of y_kv with gamma2.  The page's cacheMode 0 concatenates the
+// outputs: each queryOut row holds q^N then q^R (Hckv + Dr values) and each
+// kvCache row c^KV then k^R; its weights come transposed, (n, k) row-major.
+//
 // Every function here is pinned by the CPU tests (closed forms, invariants,
 // special cases, brute force on tiny shapes, planted mistakes); none is
 // unpinned.
@@ -145,6 +161,17 @@ void quant_int8(const double* v, int64_t n, int8_t* q, float* scale) {
   }
 }
 
+// Static asymmetric int8 code of the preprocess page's RmsNormQuant:
+// round-half-even(v * scale) + offset, saturated to [-128, 127], decided in
+// float32.
+int8_t quant_static_asym(double v, float scale, int offset, int mutation) {
+  const float f = static_cast<float>(v);
+  float r = std::nearbyint(f * scale);
+  if (mutation != 9) r += static_cast<float>(offset);  // planted 9: offset ignored
+  r = std::min(127.0f, std::max(-128.0f, r));
+  return static_cast<int8_t>(r);
+}
+
 // Static int8 code of v with a given scale (R1', R2'): v times the scale,
 // rounded half to even, saturated to [-128, 127], decided in float32.
 int8_t quant_static(double v, float scale, int mutation) {
@@ -211,6 +238,21 @@ typedef struct {
   const float* quant_scale_ckr; // (Dr)
   double* ckv_out;              // optional (n, Hckv): c^KV before rounding
   double* kr_out;               // optional (n, Dr): k^R before rounding
+  // the preprocess page's static scenario (see the file header)
+  int32_t static_quant;         // 1: bf16 x quantised here; int8 W^DQ, W^UqQr, W^DkvKr
+  int32_t x_norm;               // static only: 1 = RmsNormQuant of x, 0 = quantise x as is
+  int32_t concat;               // 1: queryOut (n, N, Hckv+Dr) and kvCache rows Hckv+Dr; kr unused
+  int32_t weight_nk;            // 1: W^DQ (Hcq, He), W^DkvKr (Hckv+Dr, He), W^UqQr (N*(D+Dr), Hcq)
+  double eps_x;                 // the RmsNorm of x
+  const uint16_t* gamma_x;      // (He) gamma0
+  const uint16_t* beta_x;       // (He) beta0
+  const uint16_t* quant_scale_x;   // (1) quantScale0, bf16
+  const int8_t* quant_offset_x;    // (1) quantOffset0
+  const int32_t* bias_dqkv;        // (Hcq+Hckv+Dr) bias0, or NULL for zeros
+  const uint16_t* beta_cq;         // (Hcq) beta1
+  const uint16_t* quant_scale_cq;  // (1) quantScale1, bf16
+  const int8_t* quant_offset_cq;   // (1) quantOffset1
+  const int32_t* bias_uq_qr;       // (N*(D+Dr)) bias1, or NULL for zeros
 } mla_oracle_problem;
 
 double mla_oracle_bf16_value(uint16_t bits) { return bf16_value(bits); }
@@ -230,9 +272,19 @@ void mla_oracle_quant_int8(const double* v, int64_t n, int8_t* q, float* scale) 
   quant_int8(v, n, q, scale);
 }
 
+void mla_oracle_quant_static_asym(const double* v, int64_t n, float scale, int offset, int8_t* q) {
+  for (int64_t i = 0; i < n; ++i) q[i] = quant_static_asym(v[i], scale, offset, 0);
+}
+
 static double load(const void* base, int64_t i, int32_t is_int8) {
   if (is_int8) return static_cast<double>(static_cast<const int8_t*>(base)[i]);
   return bf16_value(static_cast<const uint16_t*>(base)[i]);
+}
+
+// Element (k, n) of a weight with K rows of reduction and Nc output columns:
+// stored (k, n) row-major, or (n, k) with weight_nk.
+static int64_t widx(const mla_oracle_problem* p, int64_t k, int64_t n, int64_t K, int64_t Nc) {
+  return p->weight_nk ? n * K + k : k * Nc + n;
 }
 
 // The whole prolog for row r (token t) of the problem.
@@ -244,15 +296,46 @@ static void one_token(const mla_oracle_problem* p, int64_t r, int64_t t) {
 
   // down-projections: y_q = x W^DQ (Hcq), y_kvr = x [W^DKV | W^KR] (Hckv+Dr)
   std::vector<double> y_q(Hcq, 0.0), y_kvr(Wkr, 0.0);
-  if (q8in) {
+  if (p->static_quant) {
+    // x to int8 codes: RmsNormQuant(x) = code(gamma0 x / RMS(x) + beta0)
+    std::vector<double> xv(He), v(He), g0(He);
+    for (int64_t k = 0; k < He; ++k) xv[k] = bf16_value(static_cast<const uint16_t*>(p->x)[t * He + k]);
+    if (p->x_norm) {
+      for (int64_t k = 0; k < He; ++k) g0[k] = bf16_value(p->gamma_x[k]);
+      rmsnorm(xv.data(), g0.data(), He, p->eps_x, v.data(), mut);
+      for (int64_t k = 0; k < He; ++k)
+        if (mut != 10) v[k] += bf16_value(p->beta_x[k]);  // planted 10: beta dropped
+    } else {
+      v = xv;
+    }
+    const float qs = static_cast<float>(bf16_value(p->quant_scale_x[0]));
+    std::vector<int64_t> x8(He);
+    for (int64_t k = 0; k < He; ++k) x8[k] = quant_static_asym(v[k], qs, p->quant_offset_x[0], mut);
+    const int8_t* wq = static_cast<const int8_t*>(p->w_dq);
+    const int8_t* wk = static_cast<const int8_t*>(p->w_dkv_kr);
+    std::vector<int64_t> aq(Hcq, 0), ak(Wkr, 0);
+    for (int64_t k = 0; k < He; ++k) {
+      for (int64_t n = 0; n < Hcq; ++n) aq[n] += x8[k] * wq[widx(p, k, n, He, Hcq)];
+      for (int64_t n = 0; n < Wkr; ++n) ak[n] += x8[k] * wk[widx(p, k, n, He, Wkr)];
+    }
+    // y = (acc + bias0) * deScale0; planted 11 subtracts the bias
+    auto bias = [&](int64_t n) -> int64_t {
+      const int64_t b = p->bias_dqkv ? p->bias_dqkv[n] : 0;
+      return mut == 11 ? -b : b;
+    };
+    for (int64_t n = 0; n < Hcq; ++n)
+      y_q[n] = static_cast<double>(aq[n] + bias(n)) * p->scale_w_dq[n];
+    for (int64_t n = 0; n < Wkr; ++n)
+      y_kvr[n] = static_cast<double>(ak[n] + bias(Hcq + n)) * p->scale_w_dkv_kr[n];
+  } else if (q8in) {
     const int8_t* x = static_cast<const int8_t*>(p->x) + t * He;
     const int8_t* wq = static_cast<const int8_t*>(p->w_dq);
     const int8_t* wk = static_cast<const int8_t*>(p->w_dkv_kr);
     std::vector<int64_t> aq(Hcq, 0), ak(Wkr, 0);
     for (int64_t k = 0; k < He; ++k) {
       int64_t xv = x[k];
-      for (int64_t n = 0; n < Hcq; ++n) aq[n] += xv * wq[k * Hcq + n];
-      for (int64_t n = 0; n < Wkr; ++n) ak[n] += xv * wk[k * Wkr + n];
+      for (int64_t n = 0; n < Hcq; ++n) aq[n] += xv * wq[widx(p, k, n, He, Hcq)];
+      for (int64_t n = 0; n < Wkr; ++n) ak[n] += xv * wk[widx(p, k, n, He, Wkr)];
     }
     double sx = p->scale_x[t];
     for (int64_t n = 0; n < Hcq; ++n) y_q[n] = static_cast<double>(aq[n]) * sx * p->scale_w_dq[n];
@@ -260,8 +343,8 @@ static void one_token(const mla_oracle_problem* p, int64_t r, int64_t t) {
   } else {
     for (int64_t k = 0; k < He; ++k) {
       double xv = load(p->x, t * He + k, 0);
-      for (int64_t n = 0; n < Hcq; ++n) y_q[n] += xv * load(p->w_dq, k * Hcq + n, 0);
-      for (int64_t n = 0; n < Wkr; ++n) y_kvr[n] += xv * load(p->w_dkv_kr, k * Wkr + n, 0);
+      for (int64_t n = 0; n < Hcq; ++n) y_q[n] += xv * load(p->w_dq, widx(p, k, n, He, Hcq), 0);
+      for (int64_t n = 0; n < Wkr; ++n) y_kvr[n] += xv * load(p->w_dkv_kr, widx(p, k, n, He, Wkr), 0);
     }
   }
   if (p->y_out) {
@@ -309,7 +392,24 @@ static void one_token(const mla_oracle_problem* p, int64_t r, int64_t t) {
 
   // up-projection u = c^Q [W^UQ | W^QR]
   std::vector<double> u(Wuq, 0.0);
-  if (q8in || p->quant_uq) {  // R3'
+  if (p->static_quant) {
+    // c^Q to int8 codes: RmsNormQuant(y_q) = code(gamma1 y_q / RMS + beta1)
+    std::vector<double> w(c_q);
+    for (int64_t i = 0; i < Hcq; ++i)
+      if (mut != 10) w[i] += bf16_value(p->beta_cq[i]);
+    const float qs = static_cast<float>(bf16_value(p->quant_scale_cq[0]));
+    std::vector<int64_t> c8(Hcq);
+    for (int64_t i = 0; i < Hcq; ++i) c8[i] = quant_static_asym(w[i], qs, p->quant_offset_cq[0], mut);
+    const int8_t* wu = static_cast<const int8_t*>(p->w_uq_qr);
+    std::vector<int64_t> acc(Wuq, 0);
+    for (int64_t k = 0; k < Hcq; ++k)
+      for (int64_t n = 0; n < Wuq; ++n) acc[n] += c8[k] * wu[widx(p, k, n, Hcq, Wuq)];
+    for (int64_t n = 0; n < Wuq; ++n) {
+      int64_t b = p->bias_uq_qr ? p->bias_uq_qr[n] : 0;
+      if (mut == 11) b = -b;
+      u[n] = static_cast<double>(acc[n] + b) * p->scale_w_uq_qr[n];
+    }
+  } else if (q8in || p->quant_uq) {  // R3'
     std::vector<double> cm(c_q);
     if (p->smooth_cq) {
       // c^Q * m: the RmsNorm of y_q with weight gamma * m (exact products)
@@ -328,14 +428,14 @@ static void one_token(const mla_oracle_problem* p, int64_t r, int64_t t) {
     std::vector<int64_t> acc(Wuq, 0);
     for (int64_t k = 0; k < Hcq; ++k) {
       int64_t cv = c8[k];
-      for (int64_t n = 0; n < Wuq; ++n) acc[n] += cv * w[k * Wuq + n];
+      for (int64_t n = 0; n < Wuq; ++n) acc[n] += cv * w[widx(p, k, n, Hcq, Wuq)];
     }
     for (int64_t n = 0; n < Wuq; ++n)
       u[n] = static_cast<double>(acc[n]) * static_cast<double>(s_cq) * p->scale_w_uq_qr[n];
   } else {
     for (int64_t k = 0; k < Hcq; ++k) {
       double cv = p->round_intermediates ? bf16_round(c_q[k]) : c_q[k];  // R3
-      for (int64_t n = 0; n < Wuq; ++n) u[n] += cv * load(p->w_uq_qr, k * Wuq + n, 0);
+      for (int64_t n = 0; n < Wuq; ++n) u[n] += cv * load(p->w_uq_qr, widx(p, k, n, Hcq, Wuq), 0);
     }
   }
   if (p->u_out)
@@ -343,13 +443,20 @@ static void one_token(const mla_oracle_problem* p, int64_t r, int64_t t) {
 
   // per head: split, q^R = RoPE(rope part), q^N = bf16(nope part) W^UK[h]
   std::vector<double> qc(D), qr(Dr), qn(Hckv);
+  // queryOut row of (token, head): Hckv values, or Hckv + Dr with q^R after
+  // q^N in the concatenated layout
+  const int64_t qrow = p->concat ? Hckv + Dr : Hckv;
   for (int64_t h = 0; h < N; ++h) {
     // column offsets of head h inside weightUqQr
     int64_t nope0 = h * (D + Dr), rope0 = h * (D + Dr) + D;
     if (mut == 3) { nope0 = h * D; rope0 = N * D + h * Dr; }  // planted: blocked, not interleaved
     rope(u.data() + rope0, cosv.data(), sinv.data(), Dr, qr.data(), mut);
-    for (int64_t i = 0; i < Dr; ++i)
-      p->query_rope_out[(r * N + h) * Dr + i] = bf16_bits(qr[i]);  // R4
+    for (int64_t i = 0; i < Dr; ++i) {  // R4
+      if (p->concat)
+        static_cast<uint16_t*>(p->query_out)[(r * N + h) * qrow + Hckv + i] = bf16_bits(qr[i]);
+      else
+        p->query_rope_out[(r * N + h) * Dr + i] = bf16_bits(qr[i]);
+    }
     for (int64_t d = 0; d < D; ++d)
       qc[d] = p->round_intermediates ? bf16_round(u[nope0 + d]) : u[nope0 + d];  // R5
     for (int64_t j = 0; j < Hckv; ++j) qn[j] = 0.0;
@@ -366,7 +473,7 @@ static void one_token(const mla_oracle_problem* p, int64_t r, int64_t t) {
       quant_int8(qn.data(), Hckv, static_cast<int8_t*>(p->query_out) + (r * N + h) * Hckv,
                  p->dequant_scale_q_nope + r * N + h);
     } else {              // R6
-      uint16_t* qo = static_cast<uint16_t*>(p->query_out) + (r * N + h) * Hckv;
+      uint16_t* qo = static_cast<uint16_t*>(p->query_out) + (r * N + h) * qrow;
       for (int64_t j = 0; j < Hckv; ++j) qo[j] = bf16_bits(qn[j]);
     }
   }
@@ -377,8 +484,17 @@ static void one_token(const mla_oracle_problem* p, int64_t r, int64_t t) {
 // outside [0, BlockNum*BlockSize).  Returns 0, or -1 on a bad argument.
 int mla_oracle_run(mla_oracle_problem* p, int nthreads) {
   if (!p || !p->x || !p->w_dq || !p->w_uq_qr || !p->w_uk || !p->w_dkv_kr || !p->gamma_cq ||
-      !p->gamma_ckv || !p->rope_sin || !p->rope_cos || !p->query_out || !p->query_rope_out)
+      !p->gamma_ckv || !p->rope_sin || !p->rope_cos || !p->query_out ||
+      (!p->concat && !p->query_rope_out))
     return -1;
+  if (p->static_quant) {
+    if (p->quant_in || p->quant_uq || p->smooth_cq || p->kv_int8 || p->kr_int8 || p->query_int8) return -1;
+    if (!p->scale_w_dq || !p->scale_w_dkv_kr || !p->scale_w_uq_qr || !p->quant_scale_x ||
+        !p->quant_offset_x || !p->beta_cq || !p->quant_scale_cq || !p->quant_offset_cq)
+      return -1;
+    if (p->x_norm && (!p->gamma_x || !p->beta_x)) return -1;
+  }
+  if (p->concat && (p->query_int8 || p->kv_int8 || p->kr_int8)) return -1;
   if (p->Dr % 2 != 0 || p->Hcq <= 0 || p->Hckv <= 0 || p->N <= 0 || p->D <= 0 || p->Dr <= 0)
     return -1;
   if (p->quant_in && (!p->scale_x || !p->scale_w_dq || !p->scale_w_uq_qr || !p->scale_w_dkv_kr))
@@ -412,7 +528,7 @@ int mla_oracle_run(mla_oracle_problem* p, int nthreads) {
 
   // scatter (aclnnMlaPrologV2WeightNz, parameters cacheIndex / kvCacheRef /
   // krCacheRef): flat slot s is block s / BlockSize, offset s % BlockSize
-  if (p->kv_cache && p->kr_cache && p->cache_index) {
+  if (p->kv_cache && (p->kr_cache || p->concat) && p->cache_index) {
     const int64_t slots = p->block_num * p->block_size;
     for (int64_t r = 0; r < n; ++r) {
       int64_t t = p->tokens ? p->tokens[r] : r;
@@ -420,6 +536,12 @@ int mla_oracle_run(mla_oracle_problem* p, int nthreads) {
       if (s < 0 || s >= slots) continue;
       int64_t blk = s / p->block_size, off = s % p->block_size;
       const int64_t slot = blk * p->block_size + off;
+      if (p->concat) {  // one row: c^KV then k^R
+        uint16_t* row = static_cast<uint16_t*>(p->kv_cache) + slot * (p->Hckv + p->Dr);
+        std::memcpy(row, static_cast<const uint16_t*>(q.kv_rows) + r * p->Hckv, 2 * p->Hckv);
+        std::memcpy(row + p->Hckv, static_cast<const uint16_t*>(q.kr_rows) + r * p->Dr, 2 * p->Dr);
+        continue;
+      }
       std::memcpy(static_cast<uint8_t*>(p->kv_cache) + slot * p->Hckv * kv_eb,
                   static_cast<const uint8_t*>(q.kv_rows) + r * p->Hckv * kv_eb, kv_eb * p->Hckv);
       std::memcpy(static_cast<uint8_t*>(p->kr_cache) + slot * p->Dr * kr_eb,

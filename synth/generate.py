@@ -42,7 +42,8 @@ _STREAM = {
     "x": 1, "w_dq": 2, "w_uq": 3, "w_qr": 4, "w_uk": 5, "w_dkv": 6, "w_kr": 7,
     "gamma_cq": 8, "gamma_ckv": 9, "pos": 10, "slots": 11, "sx": 12,
     "sw_dq": 13, "sw_uq_qr": 14, "sw_dkv_kr": 15, "blocks": 16, "smooth_cq": 17,
-    "qs_ckv": 18, "qs_ckr": 19,
+    "qs_ckv": 18, "qs_ckr": 19, "gamma_x": 20, "beta_x": 21, "qs_x": 22, "qo_x": 23,
+    "bias_dqkv": 24, "beta_cq": 25, "qs_cq": 26, "qo_cq": 27, "bias_uq": 28,
 }
 
 
@@ -162,6 +163,13 @@ class Workload:
     partial: bool = False  # partial quantisation: only weightUqQr int8 (+ its scale)
     smooth: bool = False   # draw smoothScalesCq (int8 weightUqQr scenarios only)
     kv_quant: bool = False  # int8 kv cache (and, partially quantised, int8 kr cache)
+    # the MLA preprocess page's static scenario: bf16 x quantised by
+    # RmsNormQuant (x_norm False: quantised as is), int8 weights with
+    # per-channel deScale and int32 bias, c^Q quantised the same way
+    preprocess: bool = False
+    x_norm: bool = True
+    concat: bool = False     # cacheMode 0: queryOut q^N | q^R, kvCache c^KV | k^R
+    weight_nk: bool = False  # weights given transposed, (n, k) row-major
 
     def with_tokens(self, T: int) -> "Workload":
         return replace(self, T=T)
@@ -179,6 +187,10 @@ WORKLOADS: Dict[str, Workload] = {
                                    20266, partial=True, smooth=True),
     "int8_kvq_decode_t128": Workload("int8_kvq_decode_t128", 128, MODEL, 1024, 128, True, "uniform:32768",
                                      20267, kv_quant=True),
+    "tiny_pre_t4": Workload("tiny_pre_t4", 4, TINY_Q, 4, 16, False, "uniform:64", 20268,
+                            preprocess=True, concat=True, weight_nk=True),
+    "pre_decode_t32": Workload("pre_decode_t32", 32, MODEL, 1024, 128, False, "uniform:32768", 20269,
+                               preprocess=True, concat=True, weight_nk=True),
 }
 
 
@@ -244,13 +256,19 @@ def make_inputs(wl: Workload, T: Optional[int] = None, with_caches: bool = True,
     out: Dict[str, object] = {"workload": wl.name, "T": T, "dims": d,
                               "block_num": wl.block_num, "block_size": wl.block_size,
                               "quant": wl.quant, "partial": wl.partial, "kv_quant": wl.kv_quant,
-                              "eps_cq": wl.eps, "eps_ckv": wl.eps}
+                              "preprocess": wl.preprocess, "x_norm": wl.x_norm, "concat": wl.concat,
+                              "weight_nk": wl.weight_nk,
+                              "eps_cq": wl.eps, "eps_ckv": wl.eps, "eps_x": wl.eps}
     if wl.partial and wl.quant:
         raise ValueError("a workload is either fully or partially quantised")
     if wl.smooth and not (wl.quant or wl.partial):
         raise ValueError("smoothScalesCq belongs to the int8 weightUqQr scenarios")
     if wl.kv_quant and not (wl.quant or wl.partial):
         raise ValueError("cache quantisation belongs to the int8 scenarios")
+    if wl.preprocess and (wl.quant or wl.partial or wl.smooth or wl.kv_quant):
+        raise ValueError("the static scenario has its own quantisation")
+    if wl.concat and (wl.quant or wl.kv_quant):
+        raise ValueError("the concatenated layout holds bf16 rows")
 
     pos, slots = _positions_and_slots(wl)
     pos, slots = pos[:T], slots[:T]
@@ -269,7 +287,46 @@ def make_inputs(wl: Workload, T: Optional[int] = None, with_caches: bool = True,
         b = wqr.reshape(Hcq, N, Dr)
         return np.ascontiguousarray(np.concatenate([a, b], axis=2).reshape(Hcq, N * (D + Dr)))
 
-    if not wl.quant:
+    def static_scale(stream):
+        # one bf16 quantScale in [12, 24): the normalised values are O(1), so
+        # codes reach about +-100 and the largest saturate
+        return _to_bf16_bits(12.0 + 12.0 * _uniform(s, stream, 1))
+
+    def static_offset(stream):
+        return np.floor(-4.0 + 9.0 * _uniform(s, stream, 1)).astype(np.int8)
+
+    def descale(stream, n, K):
+        # y = (acc + bias) * deScale is O(1): the codes are ~18 rms, the
+        # weights ~73, so acc is about sqrt(K) * 1300
+        return ((0.5 + _uniform(s, stream, n)) / (np.sqrt(K) * 1300.0)).astype(np.float32)
+
+    def bias(stream, w_kn, offset):
+        # the offset's share, -offset * sum_k W[k, n], plus a small term
+        comp = -int(offset[0]) * w_kn.astype(np.int64).sum(axis=0)
+        extra = np.floor(-2000.0 + 4000.0 * _uniform(s, stream, w_kn.shape[1])).astype(np.int64)
+        return (comp + extra).astype(np.int32)
+
+    if wl.preprocess:
+        out["token_x"] = _to_bf16_bits(_normal(s, "x", full_T * He)[:T * He]).reshape(T, He)
+        out["rmsnorm_gamma_x"] = gamma("gamma_x", He)
+        out["rmsnorm_beta_x"] = _to_bf16_bits(-0.1 + 0.2 * _uniform(s, "beta_x", He))
+        out["quant_scale_x"] = static_scale("qs_x")
+        out["quant_offset_x"] = static_offset("qo_x")
+        out["rmsnorm_beta_cq"] = _to_bf16_bits(-0.1 + 0.2 * _uniform(s, "beta_cq", Hcq))
+        out["quant_scale_cq"] = static_scale("qs_cq")
+        out["quant_offset_cq"] = static_offset("qo_cq")
+        w_dq = _int8_uniform(s, "w_dq", He * Hcq).reshape(He, Hcq)
+        w_uq = _int8_uniform(s, "w_uq", Hcq * N * D).reshape(Hcq, N * D)
+        w_qr = _int8_uniform(s, "w_qr", Hcq * N * Dr).reshape(Hcq, N * Dr)
+        w_dkv = _int8_uniform(s, "w_dkv", He * Hckv).reshape(He, Hckv)
+        w_kr = _int8_uniform(s, "w_kr", He * Dr).reshape(He, Dr)
+        out["dequant_scale_w_dq"] = descale("sw_dq", Hcq, He)
+        out["dequant_scale_w_dkv_kr"] = descale("sw_dkv_kr", Hckv + Dr, He)
+        out["dequant_scale_w_uq_qr"] = descale("sw_uq_qr", N * (D + Dr), Hcq)
+        w_cat = np.concatenate([w_dq, w_dkv, w_kr], axis=1)
+        out["bias_dqkv"] = bias("bias_dqkv", w_cat, out["quant_offset_x"])
+        out["bias_uq_qr"] = bias("bias_uq", head_interleave(w_uq, w_qr), out["quant_offset_cq"])
+    elif not wl.quant:
         out["token_x"] = _to_bf16_bits(_normal(s, "x", full_T * He)[:T * He]).reshape(T, He)
         w_dq = _to_bf16_bits(_normal(s, "w_dq", He * Hcq) / np.sqrt(He)).reshape(He, Hcq)
         if wl.partial:
@@ -298,6 +355,9 @@ def make_inputs(wl: Workload, T: Optional[int] = None, with_caches: bool = True,
     out["weight_dq"] = np.ascontiguousarray(w_dq)
     out["weight_uq_qr"] = head_interleave(w_uq, w_qr)
     out["weight_dkv_kr"] = np.ascontiguousarray(np.concatenate([w_dkv, w_kr], axis=1))
+    if wl.weight_nk:
+        for k in ("weight_dq", "weight_uq_qr", "weight_dkv_kr"):
+            out[k] = np.ascontiguousarray(out[k].T)
     if unpacked:
         out["weight_uq"], out["weight_qr"] = w_uq, w_qr
         out["weight_dkv"], out["weight_kr"] = w_dkv, w_kr
@@ -310,9 +370,11 @@ def make_inputs(wl: Workload, T: Optional[int] = None, with_caches: bool = True,
         out["quant_scale_ckv"] = (16.0 + 32.0 * _uniform(s, "qs_ckv", Hckv)).astype(np.float32)
     if kr8:
         out["quant_scale_ckr"] = (16.0 + 32.0 * _uniform(s, "qs_ckr", Dr)).astype(np.float32)
-    out["kv_cache_shape"] = (wl.block_num, wl.block_size, 1, Hckv)
+    out["kv_cache_shape"] = (wl.block_num, wl.block_size, 1, Hckv + Dr if wl.concat else Hckv)
     out["kr_cache_shape"] = (wl.block_num, wl.block_size, 1, Dr)
-    if with_caches:
+    if with_caches and wl.concat:
+        out["kv_cache"] = np.full(out["kv_cache_shape"], SENTINEL_BF16, dtype=np.uint16)
+    elif with_caches:
         out["kv_cache"] = (np.full(out["kv_cache_shape"], SENTINEL_I8, dtype=np.int8) if wl.kv_quant
                            else np.full(out["kv_cache_shape"], SENTINEL_BF16, dtype=np.uint16))
         out["kr_cache"] = (np.full(out["kr_cache_shape"], SENTINEL_I8, dtype=np.int8) if kr8
@@ -323,10 +385,11 @@ def make_inputs(wl: Workload, T: Optional[int] = None, with_caches: bool = True,
 def custom_workload(name: str, T: int, dims: Dims, block_num: int, block_size: int,
                     quant: bool = False, seed: int = 7, positions: str = "uniform:4096",
                     eps: float = 1e-6, partial: bool = False, smooth: bool = False,
-                    kv_quant: bool = False) -> Workload:
+                    kv_quant: bool = False, preprocess: bool = False, x_norm: bool = True,
+                    concat: bool = False, weight_nk: bool = False) -> Workload:
     """A workload with arbitrary (small) sizes for tests of ragged shapes."""
     return Workload(name, T, dims, block_num, block_size, quant, positions, seed, eps, partial, smooth,
-                    kv_quant)
+                    kv_quant, preprocess, x_norm, concat, weight_nk)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:

@@ -600,3 +600,160 @@ def test_planted_cache_scale_mistake_fails_a_pin():
                               "gamma_dropped"])
 def test_planted_mistakes_fail_a_pin(mutation):
     assert not _whole_pins_hold(mutation)
+
+
+# ---------------------------------------------------------------------------
+# the MLA preprocess page's static scenario (aclnnMlaPreprocess, "Function"
+# formulas and parameter table, quantMode 0) and its concatenated layout
+# ---------------------------------------------------------------------------
+PRE = synth.workload("tiny_pre_t4")
+RAGGED_PRE = custom_workload("ragged_pre", T=5, dims=Dims(He=48, Hcq=32, Hckv=16, N=3, D=16, Dr=16),
+                             block_num=2, block_size=16, seed=14, preprocess=True)
+
+
+def test_static_quant_hand_worked():
+    # round-half-even(v * 4) + 3, saturated to [-128, 127]
+    v = [0.25, -0.3, 10.0, -10.0, 0.125, 0.625, 0.875, 100.0, -100.0, -31.5]
+    want = [4, 2, 43, -37, 3, 5, 7, 127, -128, -123]
+    assert oracle.quant_static_asym(v, 4.0, 3).tolist() == want
+    # without an offset the codes are the symmetric rounding, clipped to -128
+    assert oracle.quant_static_asym([-40.0, 40.0, 0.375], 4.0, 0).tolist() == [-128, 127, 2]
+
+
+def _kn(inp, key):
+    """A weight as (k, n), whichever way the inputs hold it."""
+    w = np.asarray(inp[key]).astype(np.int64)
+    return w.T if inp.get("weight_nk") else w
+
+
+def _codes(v, scale_bits, offset):
+    """Static codes written with numpy: float32 product, rint (half to even)."""
+    s = np.float32(lib_bf16_to_f64(np.asarray(scale_bits))[0])
+    r = np.rint(np.asarray(v, np.float64).astype(np.float32) * s).astype(np.float64) + int(offset[0])
+    return np.clip(r, -128, 127).astype(np.int64)
+
+
+def brute_force_static(inp):
+    """The static scenario with numpy in float64 (decisions in float32), written
+    without the oracle: returns y, c_q (the norm before beta1), u, c_kv, k_r,
+    q_r and q_n, the last four before their bf16 rounding."""
+    d = inp["dims"]
+    T, half = inp["T"], d.Dr // 2
+    x = lib_bf16_to_f64(inp["token_x"])
+    if inp.get("x_norm", True):
+        rms = np.sqrt((x * x).mean(axis=1, keepdims=True) + inp["eps_x"])
+        v = values(inp, "rmsnorm_gamma_x") * x / rms + values(inp, "rmsnorm_beta_x")
+    else:
+        v = x
+    x8 = _codes(v, inp["quant_scale_x"], inp["quant_offset_x"])
+    wcat = np.concatenate([_kn(inp, "weight_dq"), _kn(inp, "weight_dkv_kr")], axis=1)
+    ds = np.concatenate([inp["dequant_scale_w_dq"], inp["dequant_scale_w_dkv_kr"]]).astype(np.float64)
+    y = (x8 @ wcat + np.asarray(inp["bias_dqkv"], np.int64)).astype(np.float64) * ds
+    yq, ykv, ykr = y[:, :d.Hcq], y[:, d.Hcq:d.Hcq + d.Hckv], y[:, d.Hcq + d.Hckv:]
+
+    def norm(a, g, eps):
+        return g * a / np.sqrt((a * a).mean(axis=1, keepdims=True) + eps)
+
+    def rot(a, c, s):
+        lo, hi = a[..., :half], a[..., half:]
+        return np.concatenate([lo * c[..., :half] - hi * s[..., :half],
+                               hi * c[..., half:] + lo * s[..., half:]], axis=-1)
+
+    cq = norm(yq, values(inp, "rmsnorm_gamma_cq"), inp["eps_cq"])
+    c8 = _codes(cq + values(inp, "rmsnorm_beta_cq"), inp["quant_scale_cq"], inp["quant_offset_cq"])
+    u = ((c8 @ _kn(inp, "weight_uq_qr") + np.asarray(inp["bias_uq_qr"], np.int64)).astype(np.float64)
+         * inp["dequant_scale_w_uq_qr"].astype(np.float64))
+    cos, sin = values(inp, "rope_cos"), values(inp, "rope_sin")
+    uh = u.reshape(T, d.N, d.D + d.Dr)
+    q_r = rot(uh[:, :, d.D:], cos[:, None, :], sin[:, None, :])
+    qc = lib_bf16_to_f64(oracle.bf16_bits(uh[:, :, :d.D]))
+    q_n = np.einsum("thd,hdc->thc", qc, values(inp, "weight_uk"))
+    return {"y": y, "c_q": cq, "u": u, "c_kv": norm(ykv, values(inp, "rmsnorm_gamma_ckv"), inp["eps_ckv"]),
+            "k_r": rot(ykr, cos, sin), "q_r": q_r, "q_n": q_n}
+
+
+def _static_pins_hold(inp, mutation=0):
+    d = inp["dims"]
+    o = oracle.run(inp, intermediates=True, mutation=mutation)
+    bf = brute_force_static(inp)
+    q = o["query_out"]
+    qn, qr = (q[..., :d.Hckv], q[..., d.Hckv:]) if inp.get("concat") else (q, o["query_rope_out"])
+    return bool(np.allclose(o["y"], bf["y"], rtol=1e-15, atol=0)
+                and np.allclose(o["c_q"], bf["c_q"], rtol=1e-13, atol=1e-14)
+                and np.allclose(o["u"], bf["u"], rtol=1e-15, atol=0)
+                and near_bf16(o["kv_rows"], bf["c_kv"]) and near_bf16(o["kr_rows"], bf["k_r"])
+                and near_bf16(qr, bf["q_r"]) and near_bf16(qn, bf["q_n"]))
+
+
+@pytest.mark.parametrize("wl", [PRE, RAGGED_PRE], ids=["tiny_pre", "ragged_pre"])
+def test_static_scenario_matches_brute_force(wl):
+    assert _static_pins_hold(synth.make_inputs(wl))
+
+
+def test_static_scenario_without_the_input_norm():
+    # doRmsNorm false: x is quantised as it is
+    inp = synth.make_inputs(RAGGED_PRE)
+    inp["x_norm"] = False
+    assert _static_pins_hold(inp)
+    a = oracle.run(synth.make_inputs(RAGGED_PRE), intermediates=True)
+    assert not np.allclose(oracle.run(inp, intermediates=True)["y"], a["y"])
+
+
+def test_bias_carries_the_offset():
+    # with bias = -offset * sum_k W[k, n] + e, the codes' offset cancels
+    # exactly: the result equals offset 0 with bias e, as long as no code
+    # saturates (a small quantScale keeps the codes within +-60)
+    base = synth.make_inputs(RAGGED_PRE)
+    for k in ("quant_scale_x", "quant_scale_cq"):
+        base[k] = oracle.bf16_bits(np.array([8.0]))
+    zero = dict(base)
+    for off, b, w in (("quant_offset_x", "bias_dqkv", None), ("quant_offset_cq", "bias_uq_qr", "weight_uq_qr")):
+        o = int(base[off][0])
+        assert o != 0
+        wkn = (np.concatenate([_kn(base, "weight_dq"), _kn(base, "weight_dkv_kr")], axis=1) if w is None
+               else _kn(base, w))
+        zero[off] = np.zeros(1, np.int8)
+        zero[b] = (np.asarray(base[b], np.int64) + o * wkn.sum(axis=0)).astype(np.int32)
+    a = oracle.run(base, intermediates=True)
+    z = oracle.run(zero, intermediates=True)
+    assert np.array_equal(a["y"], z["y"]) and np.array_equal(a["u"], z["u"])
+    assert np.array_equal(a["query_out"], z["query_out"])
+
+
+def test_concatenated_layout_is_the_split_layout_side_by_side():
+    inp = synth.make_inputs(PRE)
+    d = inp["dims"]
+    assert inp["concat"]
+    c = oracle.run(inp)
+    split = dict(inp, concat=False)
+    split["kv_cache"] = np.full((inp["block_num"], inp["block_size"], 1, d.Hckv), synth.SENTINEL_BF16, np.uint16)
+    split["kr_cache"] = np.full((inp["block_num"], inp["block_size"], 1, d.Dr), synth.SENTINEL_BF16, np.uint16)
+    s = oracle.run(split)
+    assert np.array_equal(c["query_out"], np.concatenate([s["query_out"], s["query_rope_out"]], axis=2))
+    assert np.array_equal(c["kv_cache"], np.concatenate([s["kv_cache"], s["kr_cache"]], axis=3))
+    assert "query_rope_out" not in c and "kr_cache" not in c
+
+
+@pytest.mark.parametrize("wl", [PRE, RAGGED_Q8, TINY], ids=["tiny_pre", "ragged_q8", "tiny_bf16"])
+def test_transposed_weights_give_the_same_result(wl):
+    inp = synth.make_inputs(wl)
+    flip = dict(inp, weight_nk=not inp.get("weight_nk", False))
+    for k in ("weight_dq", "weight_uq_qr", "weight_dkv_kr"):
+        flip[k] = np.ascontiguousarray(np.asarray(inp[k]).T)
+    a, b = oracle.run(inp), oracle.run(flip)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_static_pins_hold_without_planted_mistake():
+    assert _static_pins_hold(synth.make_inputs(RAGGED_PRE))
+
+
+@pytest.mark.parametrize("mutation", [9, 10, 11], ids=["offset_ignored", "beta_dropped", "bias_subtracted"])
+def test_planted_static_mistakes_fail_a_pin(mutation):
+    inp = synth.make_inputs(RAGGED_PRE)
+    try:
+        held = _static_pins_hold(inp, mutation)
+    except Exception:
+        held = False
+    assert not held
