@@ -34,30 +34,37 @@ def algorithmic(inp, T):
     """Bytes and flops each kernel must move / do at minimum for T tokens."""
     d = inp["dims"]
     q8 = bool(inp["quant"])                   # int8 x, W^DQ, W^DkvKr (and W^UqQr)
-    u8 = q8 or bool(inp.get("partial", False))   # int8 W^UqQr and c^Q
+    st = bool(inp.get("preprocess", False))   # bf16 x quantised here, int8 weights, biases
+    u8 = q8 or st or bool(inp.get("partial", False))   # int8 W^UqQr and c^Q
     sm = inp.get("smooth_scales_cq") is not None
     kv8 = bool(inp.get("kv_quant", False))            # int8 kv cache rows
     kr8 = kv8 and bool(inp.get("partial", False))    # int8 kr cache rows
     cache = T * (d.Hckv * (1 if kv8 else 2) + d.Dr * (1 if kr8 else 2)) + (kv8 and d.Hckv * 4) + (kr8 and d.Dr * 4)
-    ed = 1 if q8 else 2                       # bytes of x, W^DQ, W^DkvKr elements
+    ed = 1 if q8 or st else 2                 # bytes of W^DQ, W^DkvKr elements
+    ex = 1 if q8 else 2                       # bytes of x elements
     eu = 1 if u8 else 2                       # bytes of W^UqQr and c^Q elements
     W = d.N * (d.D + d.Dr)
     Nkr = d.Hckv + d.Dr
     qo = 1 if q8 else 2
-    k1_bytes = d.He * (d.Hcq + Nkr) * ed + T * d.He * ed + (q8 and (d.Hcq + Nkr + T) * 4)
+    # the static scenario's extra parameters: deScale0 + bias0, deScale1 +
+    # bias1, gamma0 + beta0, beta1
+    st_dq = st and (d.Hcq + Nkr) * 8 + d.He * 4
+    st_uq = st and W * 8
+    k1_bytes = d.He * (d.Hcq + Nkr) * ed + T * d.He * ex + (q8 and (d.Hcq + Nkr + T) * 4) + st_dq
     k1_flop = 2 * T * d.He * (d.Hcq + Nkr)
     k2_bytes = (cache + T * d.Hcq * eu + T * 2 * d.Dr * 2 + T * 8
-                + (u8 and T * 4) + (sm and d.Hcq * 4))
+                + (u8 and T * 4) + (sm and d.Hcq * 4) + (st and d.Hcq * 2))
     k3_bytes = (d.Hcq * W * eu + T * d.Hcq * eu + T * d.N * d.D * 2
-                + T * d.N * d.Dr * 2 + T * 2 * d.Dr * 2 + (u8 and W * 4 + T * 4))
+                + T * d.N * d.Dr * 2 + T * 2 * d.Dr * 2 + (u8 and W * 4 + T * 4) + (st and W * 4))
     k3_flop = 2 * T * d.Hcq * W
     k4_bytes = d.N * d.D * d.Hckv * 2 + T * d.N * d.D * 2 + T * d.N * d.Hckv * qo + (q8 and T * d.N * 4)
     k4_flop = 2 * T * d.N * d.D * d.Hckv
     weights = d.He * (d.Hcq + Nkr) * ed + d.Hcq * W * eu + d.N * d.D * d.Hckv * 2
     # inputs read once, outputs written once, the scales of the scenario
-    step_bytes = (weights + T * d.He * ed + T * 2 * d.Dr * 2 + T * 8 + T * d.N * d.Hckv * qo
+    step_bytes = (weights + T * d.He * ex + T * 2 * d.Dr * 2 + T * 8 + T * d.N * d.Hckv * qo
                   + T * d.N * d.Dr * 2 + cache
-                  + (q8 and (T + d.Hcq + Nkr + T * d.N) * 4) + (u8 and W * 4) + (sm and d.Hcq * 4))
+                  + (q8 and (T + d.Hcq + Nkr + T * d.N) * 4) + (u8 and not st and W * 4)
+                  + (sm and d.Hcq * 4) + st_dq + st_uq + (st and d.Hcq * 2))
     return dict(k1_bytes=k1_bytes, k1_flop=k1_flop, k2_bytes=k2_bytes, k3_bytes=k3_bytes,
                 k3_flop=k3_flop, k4_bytes=k4_bytes, k4_flop=k4_flop, weights=weights,
                 step_bytes=step_bytes, step_flop=k1_flop + k3_flop + k4_flop)
@@ -111,7 +118,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_t32",
                     choices=["decode_t32", "decode_t256", "prefill_t8192", "int8_decode_t128",
-                             "partial_decode_t32", "int8_kvq_decode_t128", "tiny_t4"])
+                             "partial_decode_t32", "int8_kvq_decode_t128", "pre_decode_t32", "tiny_t4"])
     ap.add_argument("--replicas", type=int, default=0, help="weight replicas (0 = enough to "
                     "exceed twice the Infinity Cache)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -246,14 +253,20 @@ def main():
         "metric": METRIC, "value": T * args.steps / (ms_total * 1e-3), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int8" if inp["quant"] else "bf16+int8" if inp.get("partial", False) else "bf16",
+        "dtype": ("int8" if inp["quant"] or inp.get("preprocess", False)
+                  else "bf16+int8" if inp.get("partial", False) else "bf16"),
         "data": "synthetic",
         "config": {"workload": wl.name, "T": T, "He": d.He, "Hcq": d.Hcq, "Hckv": d.Hckv,
                    "N": d.N, "D": d.D, "Dr": d.Dr, "block_num": wl.block_num,
                    "block_size": wl.block_size, "weight_replicas": R,
                    "query_out": "int8" if inp["quant"] else "bf16",
                    "kv_cache": "int8" if inp.get("kv_quant", False) else "bf16",
-                   "weights": "row-major" if args.row_major else "packed"},
+                   "weights": "row-major" if args.row_major else "packed",
+                   "scenario": ("static int8 (preprocess)" if inp.get("preprocess", False) else
+                                "int8" if inp["quant"] else "partial int8" if inp.get("partial", False)
+                                else "bf16"),
+                   "layout": "concatenated" if inp.get("concat", False) else "separate",
+                   "weights_given": "(n, k)" if inp.get("weight_nk", False) else "(k, n)"},
         "roofline": roof,
         "path_roofline": path,
         "kernel_us": kernel_us,

@@ -33,6 +33,7 @@ MLA_ERR_UNSUPPORTED = 561002
 MLA_BF16 = 0
 MLA_INT8 = 1
 MLA_INT8_PARTIAL = 2   # in_dtype only: int8 weightUqQr, every other input bf16
+MLA_INT8_STATIC = 3    # in_dtype only: the preprocess page's static int8 scenario
 
 #: the symbols include/mla_prolog.h declares
 EXPORTS = ("mla_prolog_validate", "mla_prolog_workspace_bytes", "mla_prolog_packed_weights_bytes",
@@ -57,14 +58,19 @@ class Desc(ctypes.Structure):
                 ("max_tokens", ctypes.c_int64),
                 ("eps_cq", ctypes.c_double), ("eps_ckv", ctypes.c_double),
                 ("in_dtype", ctypes.c_int32), ("query_dtype", ctypes.c_int32),
-                ("device", ctypes.c_int32), ("cache_dtype", ctypes.c_int32)]
+                ("device", ctypes.c_int32), ("cache_dtype", ctypes.c_int32),
+                ("concat", ctypes.c_int32), ("weights_nk", ctypes.c_int32),
+                ("x_quant_only", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("eps_x", ctypes.c_double)]
 
 
 TENSOR_FIELDS = ("token_x", "weight_dq", "weight_uq_qr", "weight_uk", "weight_dkv_kr",
                  "gamma_cq", "gamma_ckv", "rope_sin", "rope_cos", "cache_index",
                  "kv_cache", "kr_cache", "scale_x", "scale_w_dq", "scale_w_uq_qr",
                  "scale_w_dkv_kr", "query_out", "query_rope_out", "dequant_scale_q_nope",
-                 "packed_weights", "smooth_scales_cq", "quant_scale_ckv", "quant_scale_ckr")
+                 "packed_weights", "smooth_scales_cq", "quant_scale_ckv", "quant_scale_ckr",
+                 "gamma_x", "beta_x", "quant_scale_x", "quant_offset_x", "bias_dqkv", "beta_cq",
+                 "quant_scale_cq", "quant_offset_cq", "bias_uq_qr")
 
 
 class Tensors(ctypes.Structure):
@@ -122,9 +128,10 @@ def status_string(status: int) -> str:
 
 def make_desc(He, Hcq, Hckv, N, D, Dr, block_num, block_size, max_tokens, eps_cq=1e-5,
               eps_ckv=1e-5, in_dtype=MLA_BF16, query_dtype=MLA_BF16, device=0,
-              cache_dtype=MLA_BF16) -> Desc:
+              cache_dtype=MLA_BF16, concat=0, weights_nk=0, x_quant_only=0, eps_x=1e-5) -> Desc:
     return Desc(He, Hcq, Hckv, N, D, Dr, block_num, block_size, max_tokens, eps_cq, eps_ckv,
-                in_dtype, query_dtype, device, cache_dtype)
+                in_dtype, query_dtype, device, cache_dtype, int(concat), int(weights_nk),
+                int(x_quant_only), 0, eps_x)
 
 
 def _address(v) -> Optional[int]:

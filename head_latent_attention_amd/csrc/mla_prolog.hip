@@ -15,6 +15,14 @@
 //   W^UK product      q^N = q^C W^UK[h] per head; bf16, or per-(token, head)
 //                     dynamic int8 with its dequantisation scale
 //
+// The static int8 scenario of the aclnnMlaPreprocess page ("Function",
+// parameter table, quantMode 0) puts k0_xquant in front: x is quantised by
+// RmsNormQuant (static, per tensor, asymmetric); the int8 products add a
+// per-channel int32 bias before their deScale; c^Q takes the same static
+// codes.  Every path writes the separate outputs and caches, or the same
+// rows concatenated (that page's cacheMode 0), through per-output row
+// strides; the packer also takes (n, k) transposed weights.
+//
 // Execution paths, by token count and weight layout:
 //   - packed weights (mla_prolog_pack_weights: 64-column windows stored as
 //     4 KB k-stages in MFMA operand order), T <= 32, bf16: one launch
@@ -84,12 +92,28 @@ __device__ __forceinline__ uint32_t cache_code(float v, float s) {
   return uint32_t(uint8_t(int8_t(r)));
 }
 
+// static asymmetric int8 code of the MLA preprocess page's RmsNormQuant
+// (quantMode 0): v times the scale, rounded half to even, plus the offset,
+// saturated to [-128, 127]
+__device__ __forceinline__ uint32_t static_code(float v, float s, float off) {
+  const float r = fminf(127.0f, fmaxf(-128.0f, rintf(v * s) + off));
+  return uint32_t(uint8_t(int8_t(r)));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ double wave_max_f64(double v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
   return v;
 }
 
@@ -234,6 +258,11 @@ struct Dims {
   int T, He, Hcq, Hckv, N, D, Dr;
   int64_t slots;  // block_num * block_size
   double eps_cq, eps_ckv;
+  // row strides, in elements, of queryOut (per token and head), of the q^R
+  // rows, and of the kv and kr cache slots: Hckv, Dr, Hckv, Dr, or all
+  // Hckv + Dr in the concatenated layout (q^R and k^R then start Hckv
+  // elements into the queryOut row and the kv slot)
+  int qs, qrs, kvs, krs;
 };
 
 struct Ptrs {
@@ -256,6 +285,12 @@ struct Ptrs {
   const float* sw_uq_qr;
   const float* sw_dkv_kr;
   const float* smooth_cq;   // smoothScalesCq (Hcq), or NULL (int8 W^UqQr only)
+  // the static int8 scenario (MLA preprocess page, quantMode 0)
+  const int32_t* bias_dq;   // bias0 (Hcq + Hckv + Dr), or NULL (zeros)
+  const int32_t* bias_uq;   // bias1 (N*(D+Dr)), or NULL (zeros)
+  const uint16_t* beta_cq;  // beta1 (Hcq): set exactly when c^Q takes static codes
+  const uint16_t* qsc_cq;   // quantScale1 (one bf16)
+  const int8_t* qo_cq;      // quantOffset1
   void* q_out;
   uint16_t* qr_out;
   float* q_scale;
@@ -273,6 +308,92 @@ struct Ptrs {
   uint32_t* fcnt;    // fused kernel: [2N] flags, 64 bytes apart, then an error word
   const uint8_t* packed;  // weights in the packed layout, or NULL
 };
+
+// int8 up-projection output of column n for token t: (acc + bias1[n]) *
+// s_cq[t] * scaleW[n] in fp32 (bias1 only in the static scenario, whose
+// s_cq is 1).  The biased sum is an int32, like the accumulator.
+__device__ __forceinline__ float udq(const Ptrs& p, int32_t acc, int t, int n) {
+  const int32_t b = p.bias_uq ? p.bias_uq[n] : 0;
+  return static_cast<float>(acc + b) * p.cq_scale[t] * p.sw_uq_qr[n];
+}
+
+// K0 (static scenario) -------------------------------------------------------
+// One 1024-thread block per token: x (bf16) to int8 codes with the MLA
+// preprocess page's RmsNormQuant, v = gamma0 x / sqrt(mean(x^2) + eps) +
+// beta0 (v = x without the norm), code = static_code(v, quantScale0,
+// quantOffset0).  The sum of squares is taken in double (each square is
+// exact), so the codes see v rounded once to fp32.  Each thread keeps its
+// first 8-element chunk of x (and its gamma0 / beta0) in registers, loaded
+// before the reduction; chunks beyond the first 1024 are read again.
+struct XQuant {
+  const uint16_t* x;      // (T, He) bf16
+  const uint16_t* gamma;  // (He) bf16, NULL without the norm
+  const uint16_t* beta;   // (He) bf16
+  const uint16_t* scale;  // one bf16
+  const int8_t* offset;   // one int8
+  uint8_t* out;           // (T, He) int8 codes
+  int T, He;
+  double eps;
+};
+constexpr int kXqThreads = 1024;
+
+__device__ __forceinline__ void unpack_bf16x8(const uint4& u, double (&v)[8]) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = bf2f(uint16_t(w[e / 2] >> (16 * (e & 1))));
+}
+
+__global__ __launch_bounds__(kXqThreads) void k0_xquant(XQuant a) {
+  __shared__ double red[kXqThreads / 64];
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int chunks = a.He / 8;
+  const uint4* row = reinterpret_cast<const uint4*>(a.x + int64_t(t) * a.He);
+  const uint4* g4 = reinterpret_cast<const uint4*>(a.gamma);
+  const uint4* b4 = reinterpret_cast<const uint4*>(a.beta);
+  const bool mine = tid < chunks;
+  const uint4 x0 = mine ? row[tid] : make_uint4(0, 0, 0, 0);
+  uint4 g0 = make_uint4(0, 0, 0, 0), b0 = g0;
+  double rms = 1.0;
+  if (a.gamma) {
+    if (mine) { g0 = g4[tid]; b0 = b4[tid]; }
+    double v[8], ss = 0.0;
+    unpack_bf16x8(x0, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+    for (int j = tid + kXqThreads; j < chunks; j += kXqThreads) {
+      unpack_bf16x8(row[j], v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+    }
+    ss = wave_sum_f64(ss);
+    if (lane == 0) red[w] = ss;
+    __syncthreads();
+    double tot = 0.0;
+#pragma unroll
+    for (int k = 0; k < kXqThreads / 64; ++k) tot += red[k];
+    rms = sqrt(tot / double(a.He) + a.eps);
+  }
+  const float qs = bf2f(*a.scale), off = float(*a.offset);
+  uint2* out = reinterpret_cast<uint2*>(a.out + int64_t(t) * a.He);
+  auto emit = [&](int j, const uint4& xu, const uint4& gu, const uint4& bu) {
+    double v[8];
+    unpack_bf16x8(xu, v);
+    if (a.gamma) {
+      double g[8], b[8];
+      unpack_bf16x8(gu, g);
+      unpack_bf16x8(bu, b);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = g[e] * v[e] / rms + b[e];
+    }
+    uint32_t code[2] = {0, 0};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) code[e / 4] |= static_code(float(v[e]), qs, off) << (8 * (e % 4));
+    out[j] = make_uint2(code[0], code[1]);
+  };
+  if (mine) emit(tid, x0, g0, b0);
+  for (int j = tid + kXqThreads; j < chunks; j += kXqThreads)
+    emit(j, row[j], a.gamma ? g4[j] : x0, a.gamma ? b4[j] : x0);
+}
 
 // K1 ------------------------------------------------------------------------
 // grid (column tiles of [W^DQ | W^DkvKr], split, token tile)
@@ -333,7 +454,7 @@ __global__ __launch_bounds__(kThreads) void k_up_proj(Dims d, Ptrs p, int nope_t
         const int ml = 16 * mt + 4 * g + i, m = m0 + ml;
         float v;
         if constexpr (I8) {
-          v = (m < d.T) ? static_cast<float>(acc[mt][0][i]) * p.cq_scale[m] * p.sw_uq_qr[col0 + col]
+          v = (m < d.T) ? udq(p, acc[mt][0][i], m, col0 + col)
                         : 0.0f;
         } else {
           v = acc[mt][0][i];
@@ -355,7 +476,7 @@ __global__ __launch_bounds__(kThreads) void k_up_proj(Dims d, Ptrs p, int nope_t
       const float a = E[ml][i], b = E[ml][i + hf];
       const uint16_t* cs = p.cos + int64_t(m) * d.Dr;
       const uint16_t* sn = p.sin + int64_t(m) * d.Dr;
-      uint16_t* o = p.qr_out + (int64_t(m) * d.N + h) * d.Dr;
+      uint16_t* o = p.qr_out + (int64_t(m) * d.N + h) * d.qrs;
       o[i] = f2bf(a * bf2f(cs[i]) - b * bf2f(sn[i]));
       o[i + hf] = f2bf(b * bf2f(cs[i + hf]) + a * bf2f(sn[i + hf]));
     }
@@ -385,7 +506,7 @@ __global__ __launch_bounds__(kThreads) void k_uk(Dims d, Ptrs p) {
         if (col >= width) continue;
         for (int i = 0; i < 4; ++i) {
           const int m = m0 + 16 * mt + 4 * g + i;
-          if (m < d.T) qo[(int64_t(m) * d.N + h) * d.Hckv + c0 + col] = f2bf(acc[mt][j][i]);
+          if (m < d.T) qo[(int64_t(m) * d.N + h) * d.qs + c0 + col] = f2bf(acc[mt][j][i]);
         }
       }
   } else {
@@ -411,7 +532,7 @@ __global__ __launch_bounds__(kThreads) void k_uk(Dims d, Ptrs p) {
         for (int j = 0; j < NTW; ++j) {
           const int col = 16 * (wave * NTW + j) + c;
           if (col < width)
-            qo[(int64_t(m) * d.N + h) * d.Hckv + col] = s > 0.0f ? quant_code(acc[mt][j][i], s) : 0;
+            qo[(int64_t(m) * d.N + h) * d.qs + col] = s > 0.0f ? quant_code(acc[mt][j][i], s) : 0;
         }
         if (wave == 0 && c == 0) p.q_scale[int64_t(m) * d.N + h] = s;
       }
@@ -609,7 +730,8 @@ PackGeo pack_geo(int64_t He, int64_t Hcq, int64_t Hckv, int64_t N, int64_t D, in
 
 // One 16-byte chunk per thread: (window, stage, column tile, lane) of one
 // matrix, gathered from the row-major source.
-__global__ __launch_bounds__(256) void k_pack(Dims d, Ptrs p, PackGeo g, int i8d, int i8u, uint8_t* out) {
+__global__ __launch_bounds__(256) void k_pack(Dims d, Ptrs p, PackGeo g, int i8d, int i8u, int nk,
+                                              uint8_t* out) {
   const int64_t q = int64_t(blockIdx.x) * 256 + threadIdx.x;
   const int64_t off = q * 16;
   if (off >= g.total) return;
@@ -639,6 +761,7 @@ __global__ __launch_bounds__(256) void k_pack(Dims d, Ptrs p, PackGeo g, int i8d
     src = reinterpret_cast<const uint8_t*>(p.w_uk + int64_t(h) * d.D * d.Hckv);
     ld = d.Hckv; K = d.D; col0 = 64 * part; width = min(64, d.Hckv - col0);
     eb = 2;
+    nk = 0;   // W^UK is always (N, D, Hckv)
   }
   const int in_win = int(rel % (int64_t(nst) * 4096));
   const int stage = in_win / 4096, ct = (in_win % 4096) / 1024, lane = (in_win % 1024) / 16;
@@ -650,7 +773,8 @@ __global__ __launch_bounds__(256) void k_pack(Dims d, Ptrs p, PackGeo g, int i8d
   for (int i = 0; i < kl; ++i) {
     const int k = stage * ks + kl * (lane >> 4) + i;
     if (k >= K || c >= width) continue;
-    const int64_t e = int64_t(k) * ld + col0 + c;
+    // element (k, n): row k of a (k, n) weight, or row n of an (n, k) one
+    const int64_t e = nk ? int64_t(col0 + c) * K + k : int64_t(k) * ld + col0 + c;
     if (eb == 1) u.b[i] = src[e];
     else u.h[i] = reinterpret_cast<const uint16_t*>(src)[e];
   }
@@ -750,7 +874,8 @@ __global__ __launch_bounds__(64 * NW) void k1_packed(Dims d, Ptrs p, PackGeo pg,
 // K2: NWT waves per token, TPB tokens per block.  y is the split-order sum
 // of the token's S partials of x [W^DQ | W^DkvKr] (in double; with int8
 // down-projection inputs, I8D, the exact int32 sum times the token and
-// column scales).  A first pass sums the squares of the c^Q and c^KV parts
+// column scales; in the static scenario, ST, the sum plus bias0 times the
+// column's deScale0, and c^Q + beta1 takes static codes with scale 1).  A first pass sums the squares of the c^Q and c^KV parts
 // (and, for an int8 c^Q, I8U, finds the largest |gamma m y| of the c^Q part,
 // m the optional smoothScalesCq), keeping each lane's first CPL 8-column
 // chunks of y in registers; a second pass writes c^Q (bf16, or the
@@ -761,17 +886,10 @@ __global__ __launch_bounds__(64 * NW) void k1_packed(Dims d, Ptrs p, PackGeo pg,
 // (gamma m) y / rms, gamma m being exact in double.
 // With cq_nst > 0, c^Q is stored fragment-packed (cq_nst k-stages per
 // 16-token tile, the k padding as zeros); with 0, row-major.
-__device__ __forceinline__ double wave_sum_f64(double v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-__device__ __forceinline__ double wave_max_f64(double v) {
-  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
-  return v;
-}
 
-template <bool I8D, bool I8U, int NWT, int TPB, int CPL>
+template <bool I8D, bool I8U, bool ST, int NWT, int TPB, int CPL>
 __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S, int cq_nst) {
+  static_assert(!ST || (I8D && I8U), "the static scenario is int8 throughout");
   __shared__ double red[NWT * TPB][3];
   __shared__ double ry[TPB][64];   // the token's y of the k^R columns (Dr <= 64)
   const int w = threadIdx.x >> 6;
@@ -782,7 +900,7 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
   const int Ntot = d.Hcq + d.Hckv + d.Dr;
   const int cq_c = d.Hcq / 8, kv_c = d.Hckv / 8, chunks = cq_c + kv_c + d.Dr / 8;
   const rsrc_t P = make_rsrc(p.part, int64_t(S) * d.T * Ntot * 4);
-  const double sx = (I8D && active) ? double(p.sx[t]) : 1.0;
+  const double sx = (I8D && !ST && active) ? double(p.sx[t]) : 1.0;
   // y of the eight columns 8j .. 8j+7; the loads of eight splits at a time
   // are issued together (a missing split reads as zeros, an exact no-op)
   auto y8 = [&](int j, double (&v)[8]) {
@@ -825,7 +943,8 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
       if constexpr (I8D) {
         const int n = 8 * j + e;
         const double sw = n < d.Hcq ? p.sw_dq[n] : p.sw_dkv_kr[n - d.Hcq];
-        v[e] = double(iv[e]) * sx * sw;
+        const int32_t b = (ST && p.bias_dq) ? p.bias_dq[n] : 0;
+        v[e] = double(iv[e] + b) * sx * sw;
       } else {
         v[e] = f[e];
       }
@@ -880,18 +999,25 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
   if (!active) return;
   const double rms_q = sqrt(sq / double(d.Hcq) + d.eps_cq);
   const double rms_kv = sqrt(skv / double(d.Hckv) + d.eps_ckv);
+  // the static scenario quantises c^Q + beta1 with quantScale1 and
+  // quantOffset1 and its dequantisation scale is 1 (the per-channel deScale1
+  // does the rest)
+  constexpr bool stq = ST;
+  const float st_s = stq ? bf2f(*p.qsc_cq) : 0.0f, st_o = stq ? float(*p.qo_cq) : 0.0f;
   float sc = 0.0f;
-  if constexpr (I8U) sc = float(gmax / rms_q) / 127.0f;
+  if constexpr (I8U) sc = stq ? 1.0f : float(gmax / rms_q) / 127.0f;
   const int64_t slot = p.cache_index[t];
   const bool cache = slot >= 0 && slot < d.slots;
   const int64_t tile = int64_t(cq_nst) * 1024;
 
-  auto store_cq = [&](int j, const float (&c)[8]) {
+  auto store_cq = [&](int j, const float (&c)[8], bool pad) {
     if constexpr (I8U) {
       uint32_t lo = 0, hi = 0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t code = uint8_t(sc > 0.0f ? quant_code(c[e], sc) : int8_t(0));
+        const uint32_t code = pad   ? 0u
+                              : stq ? static_code(c[e], st_s, st_o)
+                                    : uint8_t(sc > 0.0f ? quant_code(c[e], sc) : int8_t(0));
         if (e < 4) lo |= code << (8 * e);
         else hi |= code << (8 * (e - 4));
       }
@@ -907,8 +1033,12 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
     float c[8];
     if (j < cq_c) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) c[e] = float(gq(8 * j + e) * v[e] / rms_q);
-      store_cq(j, c);
+      for (int e = 0; e < 8; ++e) {
+        double w = gq(8 * j + e) * v[e] / rms_q;
+        if (stq) w += double(bf2f(p.beta_cq[8 * j + e]));
+        c[e] = float(w);
+      }
+      store_cq(j, c, false);
     } else if (j >= cq_c + kv_c) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) ry[w / NWT][8 * (j - cq_c - kv_c) + e] = v[e];
@@ -923,11 +1053,11 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
           lo |= cache_code(c[e], p.qs_ckv[8 * jk + e]) << (8 * e);
           hi |= cache_code(c[e + 4], p.qs_ckv[8 * jk + e + 4]) << (8 * e);
         }
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(p.kv_cache) + slot * d.Hckv + 8 * jk) =
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(p.kv_cache) + slot * d.kvs + 8 * jk) =
             make_uint2(lo, hi);
       } else {
         const uint2 a = pack_bf16x4(c[0], c[1], c[2], c[3]), b = pack_bf16x4(c[4], c[5], c[6], c[7]);
-        *reinterpret_cast<uint4*>(p.kv_cache + slot * d.Hckv + 8 * jk) = make_uint4(a.x, a.y, b.x, b.y);
+        *reinterpret_cast<uint4*>(p.kv_cache + slot * d.kvs + 8 * jk) = make_uint4(a.x, a.y, b.x, b.y);
       }
     }
   };
@@ -946,7 +1076,7 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
   const int cq_chunks = cq_nst ? cq_nst * (I8U ? 8 : 4) : cq_c;
   for (int j = cq_c + lane; j < cq_chunks; j += L) {
     const float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    store_cq(j, z);
+    store_cq(j, z, true);
   }
   if (I8U && lane == 0) p.cq_scale[t] = sc;
   if (!cache) return;   // the same for every wave of the token
@@ -961,8 +1091,8 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
   const double* yr = ry[w / NWT];
   const uint16_t* cs = p.cos + int64_t(t) * d.Dr;
   const uint16_t* sn = p.sin + int64_t(t) * d.Dr;
-  uint16_t* kr = p.kr_cache + slot * d.Dr;
-  uint8_t* kr8 = reinterpret_cast<uint8_t*>(p.kr_cache) + slot * d.Dr;
+  uint16_t* kr = p.kr_cache + slot * d.krs;
+  uint8_t* kr8 = reinterpret_cast<uint8_t*>(p.kr_cache) + slot * d.krs;
   for (int i = lane; i < h; i += L) {
     const double a = yr[i], b = yr[i + h];
     const float r0 = float(a * bf2f(cs[i]) - b * bf2f(sn[i]));
@@ -1012,7 +1142,7 @@ __global__ __launch_bounds__(64 * NW) void k3_packed(Dims d, Ptrs p, PackGeo pg)
           float v;
           if constexpr (I8)
             v = (ml < d.T && col < width)
-                    ? static_cast<float>(acc[mt][ct][i]) * p.cq_scale[ml] * p.sw_uq_qr[col0 + col]
+                    ? udq(p, acc[mt][ct][i], ml, col0 + col)
                     : 0.0f;
           else
             v = acc[mt][ct][i];
@@ -1040,7 +1170,7 @@ __global__ __launch_bounds__(64 * NW) void k3_packed(Dims d, Ptrs p, PackGeo pg)
       const float a = E[ml * 65 + i], b = E[ml * 65 + i + hf];
       const uint16_t* cs = p.cos + int64_t(ml) * d.Dr;
       const uint16_t* sn = p.sin + int64_t(ml) * d.Dr;
-      uint16_t* o = p.qr_out + (int64_t(ml) * d.N + h) * d.Dr;
+      uint16_t* o = p.qr_out + (int64_t(ml) * d.N + h) * d.qrs;
       o[i] = f2bf(a * bf2f(cs[i]) - b * bf2f(sn[i]));
       o[i + hf] = f2bf(b * bf2f(cs[i + hf]) + a * bf2f(sn[i + hf]));
     }
@@ -1081,7 +1211,7 @@ __global__ __launch_bounds__(64 * NW) void k4_packed(Dims d, Ptrs p, PackGeo pg)
   for (int idx = tid; idx < 16 * MT * 8; idx += 64 * NW) {
     const int ml = idx / 8, ch = idx % 8;
     if (ml < d.T && 8 * ch < width)
-      *reinterpret_cast<uint4*>(qo + (int64_t(ml) * d.N + h) * d.Hckv + c0 + 8 * ch) =
+      *reinterpret_cast<uint4*>(qo + (int64_t(ml) * d.N + h) * d.qs + c0 + 8 * ch) =
           *reinterpret_cast<const uint4*>(E + ml * 64 + 8 * ch);
   }
 }
@@ -1131,7 +1261,7 @@ __global__ __launch_bounds__(512) void k4_packed_q8(Dims d, Ptrs p, PackGeo pg) 
       for (int ct = 0; ct < 4; ++ct) {
         const int col = 16 * ct + c;
         if (col < width)
-          qo[(int64_t(ml) * d.N + h) * d.Hckv + c0 + col] = sc > 0.0f ? quant_code(acc[mt][ct][i], sc) : 0;
+          qo[(int64_t(ml) * d.N + h) * d.qs + c0 + col] = sc > 0.0f ? quant_code(acc[mt][ct][i], sc) : 0;
       }
       if (w == 0 && c == 0) p.q_scale[int64_t(ml) * d.N + h] = sc;
     }
@@ -1239,7 +1369,7 @@ __global__ __launch_bounds__(64 * NW) void k34_stream(Dims d, Ptrs p, PackGeo pg
             float v;
             if constexpr (I8)
               v = (ml < d.T && col < d.Dr)
-                      ? static_cast<float>(acc[mt][ct][i]) * p.cq_scale[ml] * p.sw_uq_qr[col0 + col]
+                      ? udq(p, acc[mt][ct][i], ml, col0 + col)
                       : 0.0f;
             else
               v = acc[mt][ct][i];
@@ -1254,7 +1384,7 @@ __global__ __launch_bounds__(64 * NW) void k34_stream(Dims d, Ptrs p, PackGeo pg
       const float a = E[ml * 65 + i], b = E[ml * 65 + i + hf];
       const uint16_t* cs = p.cos + int64_t(ml) * d.Dr;
       const uint16_t* sn = p.sin + int64_t(ml) * d.Dr;
-      uint16_t* o = p.qr_out + (int64_t(ml) * d.N + h) * d.Dr;
+      uint16_t* o = p.qr_out + (int64_t(ml) * d.N + h) * d.qrs;
       o[i] = f2bf(a * bf2f(cs[i]) - b * bf2f(sn[i]));
       o[i + hf] = f2bf(b * bf2f(cs[i + hf]) + a * bf2f(sn[i + hf]));
     }
@@ -1298,7 +1428,7 @@ __global__ __launch_bounds__(64 * NW) void k34_stream(Dims d, Ptrs p, PackGeo pg
           float v;
           if constexpr (I8)
             v = (row < d.T && col < width)
-                    ? static_cast<float>(acc[mt][ct][i]) * p.cq_scale[row] * p.sw_uq_qr[col0 + col]
+                    ? udq(p, acc[mt][ct][i], row, col0 + col)
                     : 0.0f;
           else
             v = acc[mt][ct][i];
@@ -1341,7 +1471,7 @@ __global__ __launch_bounds__(64 * NW) void k34_stream(Dims d, Ptrs p, PackGeo pg
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
           const int col = 16 * ct + c;
-          if (col < width2) qo[(int64_t(row) * d.N + h) * d.Hckv + 64 * jw + col] = f2bf(acc2[mt][ct][i]);
+          if (col < width2) qo[(int64_t(row) * d.N + h) * d.qs + 64 * jw + col] = f2bf(acc2[mt][ct][i]);
         }
       }
   } else {
@@ -1373,7 +1503,7 @@ __global__ __launch_bounds__(64 * NW) void k34_stream(Dims d, Ptrs p, PackGeo pg
         for (int ct = 0; ct < 4; ++ct) {
           const int col = 16 * ct + c;
           if (col < width2)
-            qo[(int64_t(row) * d.N + h) * d.Hckv + 64 * jw + col] =
+            qo[(int64_t(row) * d.N + h) * d.qs + 64 * jw + col] =
                 sc > 0.0f ? quant_code(acc2[mt][ct][i], sc) : int8_t(0);
         }
         if (jw == 0 && c == 0) p.q_scale[int64_t(row) * d.N + h] = sc;
@@ -1557,7 +1687,7 @@ __global__ __launch_bounds__(512) void k34_pair(Dims d, Ptrs p, PackGeo pg) {
     for (int r = 0; r < 4; ++r) {
       if constexpr (I8)
         v[r] = (t < d.T && col + r < d.D)
-                   ? static_cast<float>(s[r]) * p.cq_scale[t] * p.sw_uq_qr[h * DDr + col + r]
+                   ? udq(p, s[r], t, h * DDr + col + r)
                    : 0.0f;
       else
         v[r] = s[r];
@@ -1588,8 +1718,8 @@ __global__ __launch_bounds__(512) void k34_pair(Dims d, Ptrs p, PackGeo pg) {
       for (int r = 0; r < 4; ++r) {
         float a, bb;
         if constexpr (I8) {
-          a = static_cast<float>(a0[r]) * p.cq_scale[t] * p.sw_uq_qr[h * DDr + d.D + i0 + r];
-          bb = static_cast<float>(a1[r]) * p.cq_scale[t] * p.sw_uq_qr[h * DDr + d.D + i0 + hf + r];
+          a = udq(p, a0[r], t, h * DDr + d.D + i0 + r);
+          bb = udq(p, a1[r], t, h * DDr + d.D + i0 + hf + r);
         } else {
           a = a0[r];
           bb = a1[r];
@@ -1597,7 +1727,7 @@ __global__ __launch_bounds__(512) void k34_pair(Dims d, Ptrs p, PackGeo pg) {
         o0[r] = a * bf2f(cs0[r]) - bb * bf2f(sn0[r]);
         o1[r] = bb * bf2f(cs1[r]) + a * bf2f(sn1[r]);
       }
-      uint16_t* o = p.qr_out + (int64_t(t) * d.N + h) * d.Dr + i0;
+      uint16_t* o = p.qr_out + (int64_t(t) * d.N + h) * d.qrs + i0;
       *reinterpret_cast<uint2*>(o) = pack_bf16x4(o0[0], o0[1], o0[2], o0[3]);
       *reinterpret_cast<uint2*>(o + hf) = pack_bf16x4(o1[0], o1[1], o1[2], o1[3]);
     }
@@ -1633,7 +1763,7 @@ __global__ __launch_bounds__(512) void k34_pair(Dims d, Ptrs p, PackGeo pg) {
       for (int k = 0; k < 2; ++k) {
         const int col = col0 + 16 * k;
         if (col < d.Hckv)
-          *reinterpret_cast<uint2*>(qo + (int64_t(t) * d.N + h) * d.Hckv + col) =
+          *reinterpret_cast<uint2*>(qo + (int64_t(t) * d.N + h) * d.qs + col) =
               pack_bf16x4(au[mt][k][0], au[mt][k][1], au[mt][k][2], au[mt][k][3]);
       }
     }
@@ -1679,7 +1809,7 @@ __global__ __launch_bounds__(512) void k34_pair(Dims d, Ptrs p, PackGeo pg) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           u |= uint32_t(uint8_t(sc > 0.0f ? quant_code(au[mt][k][r], sc) : 0)) << (8 * r);
-        *reinterpret_cast<uint32_t*>(qo + (int64_t(t) * d.N + h) * d.Hckv + col) = u;
+        *reinterpret_cast<uint32_t*>(qo + (int64_t(t) * d.N + h) * d.qs + col) = u;
       }
       if (half == 0 && w == 0 && g == 0) p.q_scale[int64_t(t) * d.N + h] = sc;
     }
@@ -2095,12 +2225,12 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
     const double rms = sqrt(ssk / double(d.Hckv) + d.eps_ckv);
     const int col = 64 * cjb.ch + lane;
     if (col < d.Hckv)
-      p.kv_cache[slot * d.Hckv + col] = f2bf(float(double(bf2f(uint16_t(cjb.gam))) * double(cjb.y) / rms));
+      p.kv_cache[slot * d.kvs + col] = f2bf(float(double(bf2f(uint16_t(cjb.gam))) * double(cjb.y) / rms));
     if (cjb.ch == 0 && lane < d.Dr / 2) {
       const int hf = d.Dr / 2;
       const uint16_t* cs = p.cos + int64_t(cjb.t) * d.Dr;
       const uint16_t* sn = p.sin + int64_t(cjb.t) * d.Dr;
-      uint16_t* kr = p.kr_cache + slot * d.Dr;
+      uint16_t* kr = p.kr_cache + slot * d.krs;
       kr[lane] = f2bf(float(double(cjb.a) * bf2f(cs[lane]) - double(cjb.b2) * bf2f(sn[lane])));
       kr[lane + hf] = f2bf(float(double(cjb.b2) * bf2f(cs[lane + hf]) + double(cjb.a) * bf2f(sn[lane + hf])));
     }
@@ -2215,7 +2345,7 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
         o0[r] = a * bf2f(cs0[r]) - bb * bf2f(sn0[r]);
         o1[r] = bb * bf2f(cs1[r]) + a * bf2f(sn1[r]);
       }
-      uint16_t* o = p.qr_out + (int64_t(t) * d.N + h) * d.Dr + i0;
+      uint16_t* o = p.qr_out + (int64_t(t) * d.N + h) * d.qrs + i0;
       *reinterpret_cast<uint2*>(o) = pack_bf16x4(o0[0], o0[1], o0[2], o0[3]);
       *reinterpret_cast<uint2*>(o + hf) = pack_bf16x4(o1[0], o1[1], o1[2], o1[3]);
     }
@@ -2250,7 +2380,7 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
     for (int k = 0; k < 2; ++k) {
       const int col = qcol0 + 16 * k;
       if (col < d.Hckv)
-        *reinterpret_cast<uint2*>(qo + (int64_t(t) * d.N + h) * d.Hckv + col) =
+        *reinterpret_cast<uint2*>(qo + (int64_t(t) * d.N + h) * d.qs + col) =
             pack_bf16x4(au[mt][k][0], au[mt][k][1], au[mt][k][2], au[mt][k][3]);
     }
   }
@@ -2566,7 +2696,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k3_tiled(Dims d, Ptrs p, PackGeo
           const int col = 16 * ct + 4 * g + r;
           if constexpr (I8)
             v[ct][r] = (m < d.T && col < width)
-                           ? static_cast<float>(acc[mt][i * 4 + ct][r]) * p.cq_scale[m] * p.sw_uq_qr[col0 + col]
+                           ? udq(p, acc[mt][i * 4 + ct][r], m, col0 + col)
                            : 0.0f;
           else
             v[ct][r] = acc[mt][i * 4 + ct][r];
@@ -2599,7 +2729,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k3_tiled(Dims d, Ptrs p, PackGeo
         if (mrow < d.T) {
           const uint16_t* cs = p.cos + mrow * d.Dr;
           const uint16_t* sn = p.sin + mrow * d.Dr;
-          uint16_t* o = p.qr_out + (mrow * d.N + h) * d.Dr;
+          uint16_t* o = p.qr_out + (mrow * d.N + h) * d.qrs;
           for (int i0 = 4 * g; i0 < hf; i0 += 16) {
             float lo[4], hi[4];
 #pragma unroll
@@ -2699,7 +2829,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k4_tiled(Dims d, Ptrs p, PackGeo
           const int m = m0 + 16 * mt + row;
           if (m < d.T && col < width)
             __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(tile + row * 144 + col * 2),
-                                        reinterpret_cast<u32x4*>(qo + (int64_t(m) * d.N + h) * d.Hckv + 64 * jw + col));
+                                        reinterpret_cast<u32x4*>(qo + (int64_t(m) * d.N + h) * d.qs + 64 * jw + col));
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -2751,7 +2881,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k4_tiled(Dims d, Ptrs p, PackGeo
             const int8_t code = sc > 0.0f ? quant_code(x, sc) : int8_t(0);
             q |= uint32_t(uint8_t(code)) << (8 * r);
           }
-          *reinterpret_cast<uint32_t*>(qo + (int64_t(m) * d.N + h) * d.Hckv + 64 * jw + col) = q;
+          *reinterpret_cast<uint32_t*>(qo + (int64_t(m) * d.N + h) * d.qs + 64 * jw + col) = q;
         }
       }
       if (wn == 0 && g == 0) p.q_scale[int64_t(m) * d.N + h] = sc;
@@ -2777,8 +2907,9 @@ int ceil_div(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
 
 // int8 down-projection operands (x, W^DQ, W^DkvKr): full quantisation only;
 // int8 W^UqQr (and an int8 c^Q): full and partial quantisation
-bool down_i8(const mla_prolog_desc& d) { return d.in_dtype == MLA_INT8; }
-bool up_i8(const mla_prolog_desc& d) { return d.in_dtype == MLA_INT8 || d.in_dtype == MLA_INT8_PARTIAL; }
+bool is_static(const mla_prolog_desc& d) { return d.in_dtype == MLA_INT8_STATIC; }
+bool down_i8(const mla_prolog_desc& d) { return d.in_dtype == MLA_INT8 || is_static(d); }
+bool up_i8(const mla_prolog_desc& d) { return down_i8(d) || d.in_dtype == MLA_INT8_PARTIAL; }
 PackGeo geo_of(const mla_prolog_desc& d) {
   return pack_geo(d.He, d.Hcq, d.Hckv, d.N, d.D, d.Dr, down_i8(d), up_i8(d));
 }
@@ -2796,7 +2927,7 @@ Plan make_plan(const mla_prolog_desc& d, int64_t T) {
   {
     const PackGeo g = geo_of(d);
     const int ptiles = g.win_dq + g.win_kr;
-    int Sp = std::max(1, std::min(g.nst_he, (512 + ptiles / 2) / ptiles));
+    int Sp = std::max(1, std::min(g.nst_he, ((i8 ? 256 : 512) + ptiles / 2) / ptiles));
     pl.sps = ceil_div(g.nst_he, Sp);
     pl.Sp = ceil_div(g.nst_he, pl.sps);
   }
@@ -2883,7 +3014,7 @@ TiledPlan tiled_plan(const mla_prolog_desc& d, int64_t T) {
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t part, cq, cq_scale, qc, xq, xflag, xmax, fpart, fss, fykr, fcnt, total;
+  size_t part, cq, cq_scale, qc, xq, xflag, xmax, x8, fpart, fss, fykr, fcnt, total;
 };
 
 Layout layout(const mla_prolog_desc& d) {
@@ -2913,7 +3044,10 @@ Layout layout(const mla_prolog_desc& d) {
   // the fused small-T kernel: 2N blocks' partials, per-window sums of
   // squares, the c^KV / k^R rows, counters
   const size_t nwin = size_t(g.win_dq + g.win_kr);
-  L.fpart = align256(L.xmax + size_t(d.N) * 64 * 4);
+  // the static scenario's int8 codes of x
+  L.x8 = align256(L.xmax + size_t(d.N) * 64 * 4);
+  const size_t x8_bytes = d.in_dtype == MLA_INT8_STATIC ? size_t(d.max_tokens) * d.He : 0;
+  L.fpart = align256(L.x8 + x8_bytes);
   L.fss = align256(L.fpart + size_t(2 * d.N) * 32 * 64 * 8);
   L.fykr = align256(L.fss + nwin * 32 * 8);
   L.fcnt = align256(L.fykr + size_t(32) * (d.Hckv + d.Dr) * 4);
@@ -2931,14 +3065,25 @@ mla_status check_desc(const mla_prolog_desc* d) {
     if (v <= 0 || v > (1 << 20)) return MLA_ERR_PARAM_INVALID;
   // the page's dtype table has an int8 queryOut only in the int8
   // full-quantisation scenario
-  if ((d->in_dtype != MLA_BF16 && d->in_dtype != MLA_INT8 && d->in_dtype != MLA_INT8_PARTIAL) ||
+  if ((d->in_dtype != MLA_BF16 && d->in_dtype != MLA_INT8 && d->in_dtype != MLA_INT8_PARTIAL &&
+       d->in_dtype != MLA_INT8_STATIC) ||
       (d->query_dtype != MLA_BF16 && d->query_dtype != MLA_INT8))
     return MLA_ERR_PARAM_INVALID;
   if (d->query_dtype == MLA_INT8 && d->in_dtype != MLA_INT8) return MLA_ERR_PARAM_INVALID;
   // quantised caches: only in the two int8 scenarios (the tables' "kv_cache
   // quantized" columns)
   if (d->cache_dtype != MLA_BF16 && d->cache_dtype != MLA_INT8) return MLA_ERR_PARAM_INVALID;
-  if (d->cache_dtype == MLA_INT8 && d->in_dtype == MLA_BF16) return MLA_ERR_PARAM_INVALID;
+  if (d->cache_dtype == MLA_INT8 && d->in_dtype != MLA_INT8 && d->in_dtype != MLA_INT8_PARTIAL)
+    return MLA_ERR_PARAM_INVALID;
+  // the preprocess page's layout and weight options; its concatenated
+  // layout holds bf16 rows only
+  if ((d->concat != 0 && d->concat != 1) || (d->weights_nk != 0 && d->weights_nk != 1) ||
+      (d->x_quant_only != 0 && d->x_quant_only != 1) || d->reserved != 0)
+    return MLA_ERR_PARAM_INVALID;
+  if (d->concat && (d->query_dtype != MLA_BF16 || d->cache_dtype != MLA_BF16)) return MLA_ERR_PARAM_INVALID;
+  if (d->x_quant_only && d->in_dtype != MLA_INT8_STATIC) return MLA_ERR_PARAM_INVALID;
+  if (d->in_dtype == MLA_INT8_STATIC && (!(d->eps_x >= 0.0) || !std::isfinite(d->eps_x)))
+    return MLA_ERR_PARAM_INVALID;
   if (d->block_num < 0 || d->max_tokens < 0 || d->max_tokens > (1 << 20))
     return MLA_ERR_PARAM_INVALID;
   if (d->block_num > 0 && (d->block_size < 16 || d->block_size > 1024 || d->block_size % 16))
@@ -2952,7 +3097,7 @@ mla_status check_desc(const mla_prolog_desc* d) {
   if (d->Dr > 64 || d->Hckv > 512 || d->D > 512 || d->He > 65536) return MLA_ERR_UNSUPPORTED;
   // int8 operands move in 16-byte (16-element) chunks that must not cross a
   // row or column-block end
-  if (d->in_dtype == MLA_INT8 &&
+  if (down_i8(*d) &&
       (d->He % 16 || d->Hcq % 16 || (d->Hckv + d->Dr) % 16 || d->D % 16 || d->Dr % 16))
     return MLA_ERR_UNSUPPORTED;
   if (d->in_dtype == MLA_INT8_PARTIAL && (d->Hcq % 16 || d->D % 16 || d->Dr % 16))
@@ -2968,28 +3113,54 @@ mla_status check_tensors(const mla_prolog_desc* d, const mla_prolog_tensors* t, 
   if (T < 0 || T > d->max_tokens) return MLA_ERR_PARAM_INVALID;
   if (!t) return MLA_ERR_NULLPTR;
   if (T == 0) return MLA_OK;
+  // the concatenated layout has no separate q^R output or k^R cache
+  const void* qr_or_q = d->concat ? t->query_out : t->query_rope_out;
   const void* req[] = {t->token_x, t->weight_dq, t->weight_uq_qr, t->weight_uk, t->weight_dkv_kr,
                        t->gamma_cq, t->gamma_ckv, t->rope_sin, t->rope_cos, t->cache_index,
-                       t->query_out, t->query_rope_out};
+                       t->query_out, qr_or_q};
   for (const void* q : req)
     if (!q) return MLA_ERR_NULLPTR;
   for (const void* q : req)
     if (!aligned16(q)) return MLA_ERR_PARAM_INVALID;
+  if (d->concat && (t->query_rope_out || t->kr_cache)) return MLA_ERR_PARAM_INVALID;
   if (d->block_num > 0) {
-    if (!t->kv_cache || !t->kr_cache) return MLA_ERR_NULLPTR;
-    if (!aligned16(t->kv_cache) || !aligned16(t->kr_cache)) return MLA_ERR_PARAM_INVALID;
+    const void* kr = d->concat ? t->kv_cache : t->kr_cache;
+    if (!t->kv_cache || !kr) return MLA_ERR_NULLPTR;
+    if (!aligned16(t->kv_cache) || !aligned16(kr)) return MLA_ERR_PARAM_INVALID;
   }
+  // the static scenario's norm and quantisation parameters, absent elsewhere
+  const bool st = is_static(*d), xn = st && !d->x_quant_only;
+  const void* st_req[] = {t->quant_scale_x, t->quant_offset_x, t->beta_cq, t->quant_scale_cq,
+                          t->quant_offset_cq};
+  for (const void* q : st_req) {
+    if (st && !q) return MLA_ERR_NULLPTR;
+    if (!st && q) return MLA_ERR_PARAM_INVALID;
+  }
+  if (xn && (!t->gamma_x || !t->beta_x)) return MLA_ERR_NULLPTR;
+  if (!xn && (t->gamma_x || t->beta_x)) return MLA_ERR_PARAM_INVALID;
+  if (!st && (t->bias_dqkv || t->bias_uq_qr)) return MLA_ERR_PARAM_INVALID;
+  // gamma0 / beta0 are read in 16-byte chunks; the one-value scales as bf16
+  if ((t->gamma_x && !aligned16(t->gamma_x)) || (t->beta_x && !aligned16(t->beta_x)))
+    return MLA_ERR_PARAM_INVALID;
+  const void* st_bf16[] = {t->quant_scale_x, t->beta_cq, t->quant_scale_cq};
+  for (const void* q : st_bf16)
+    if (reinterpret_cast<uintptr_t>(q) & 1u) return MLA_ERR_PARAM_INVALID;
+  if ((t->bias_dqkv && !aligned4(t->bias_dqkv)) || (t->bias_uq_qr && !aligned4(t->bias_uq_qr)))
+    return MLA_ERR_PARAM_INVALID;
+  // the unpacked kernels read (k, n) weights only
+  if (d->weights_nk && !t->packed_weights) return MLA_ERR_UNSUPPORTED;
   // the scales each scenario takes: all four in full quantisation, that of
   // weightUqQr alone in partial quantisation, none without quantisation
   const float* sc[] = {t->scale_x, t->scale_w_dq, t->scale_w_uq_qr, t->scale_w_dkv_kr};
-  const bool need[] = {down_i8(*d), down_i8(*d), up_i8(*d), down_i8(*d)};
+  const bool need[] = {down_i8(*d) && !st, down_i8(*d), up_i8(*d), down_i8(*d)};
   for (int i = 0; i < 4; ++i) {
     if (need[i] && !sc[i]) return MLA_ERR_NULLPTR;
     if (!need[i] && sc[i]) return MLA_ERR_PARAM_INVALID;
     if (sc[i] && !aligned4(sc[i])) return MLA_ERR_PARAM_INVALID;
   }
   // smoothScalesCq: optional with an int8 weightUqQr, absent otherwise
-  if (t->smooth_scales_cq && (!up_i8(*d) || !aligned4(t->smooth_scales_cq))) return MLA_ERR_PARAM_INVALID;
+  if (t->smooth_scales_cq && (!up_i8(*d) || st || !aligned4(t->smooth_scales_cq)))
+    return MLA_ERR_PARAM_INVALID;
   // quantScaleCkv with an int8 kv cache; quantScaleCkr with an int8 kr
   // cache, which partial quantisation has and full quantisation does not
   const bool kv8 = d->cache_dtype == MLA_INT8, kr8 = kv8 && d->in_dtype == MLA_INT8_PARTIAL;
@@ -3059,8 +3230,15 @@ void launch_k4(int ntw, dim3 grid, hipStream_t s, const Dims& d, const Ptrs& p) 
 // K2 with eight waves per token when there are few tokens, one otherwise.
 template <bool I8D, bool I8U>
 void launch_norm(hipStream_t s, const Dims& d, const Ptrs& p, int S, int cq_nst) {
-  if (d.T <= 512) k2_norm<I8D, I8U, 8, 1, 1><<<dim3(d.T), 512, 0, s>>>(d, p, S, cq_nst);
-  else k2_norm<I8D, I8U, 1, 4, 1><<<dim3((d.T + 3) / 4), 256, 0, s>>>(d, p, S, cq_nst);
+  if constexpr (I8D && I8U) {
+    if (p.beta_cq) {   // the static scenario
+      if (d.T <= 512) k2_norm<true, true, true, 8, 1, 1><<<dim3(d.T), 512, 0, s>>>(d, p, S, cq_nst);
+      else k2_norm<true, true, true, 1, 4, 1><<<dim3((d.T + 3) / 4), 256, 0, s>>>(d, p, S, cq_nst);
+      return;
+    }
+  }
+  if (d.T <= 512) k2_norm<I8D, I8U, false, 8, 1, 1><<<dim3(d.T), 512, 0, s>>>(d, p, S, cq_nst);
+  else k2_norm<I8D, I8U, false, 1, 4, 1><<<dim3((d.T + 3) / 4), 256, 0, s>>>(d, p, S, cq_nst);
 }
 
 // The int8-query W^UK kernel gives one wave to each 64-column window of Hckv.
@@ -3249,7 +3427,7 @@ mla_status mla_prolog_pack_weights(mla_prolog_t h, const mla_prolog_tensors* t, 
   p.w_dkv_kr = static_cast<const uint8_t*>(t->weight_dkv_kr);
   const int64_t chunks = g.total / 16;
   k_pack<<<dim3(unsigned((chunks + 255) / 256)), 256, 0, static_cast<hipStream_t>(stream)>>>(
-      d, p, g, int(down_i8(dd)), int(up_i8(dd)), static_cast<uint8_t*>(packed));
+      d, p, g, int(down_i8(dd)), int(up_i8(dd)), int(dd.weights_nk != 0), static_cast<uint8_t*>(packed));
   const hipError_t e = hipGetLastError();
   if (prev != dd.device) (void)hipSetDevice(prev);
   return e == hipSuccess ? MLA_OK : MLA_ERR_RUNTIME;
@@ -3336,7 +3514,13 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   d.D = int(dd.D); d.Dr = int(dd.Dr);
   d.slots = dd.block_num * dd.block_size;
   d.eps_cq = dd.eps_cq; d.eps_ckv = dd.eps_ckv;
+  const int row = int(dd.Hckv + dd.Dr);
+  d.qs = dd.concat ? row : d.Hckv;
+  d.qrs = dd.concat ? row : d.Dr;
+  d.kvs = dd.concat ? row : d.Hckv;
+  d.krs = dd.concat ? row : d.Dr;
   Ptrs p;
+  std::memset(&p, 0, sizeof p);
   p.x = static_cast<const uint8_t*>(t->token_x);
   p.w_dq = static_cast<const uint8_t*>(t->weight_dq);
   p.w_uq_qr = static_cast<const uint8_t*>(t->weight_uq_qr);
@@ -3349,13 +3533,20 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   p.cache_index = t->cache_index;
   p.kv_cache = static_cast<uint16_t*>(t->kv_cache);
   p.kr_cache = static_cast<uint16_t*>(t->kr_cache);
+  if (dd.concat && p.kv_cache) p.kr_cache = p.kv_cache + dd.Hckv;   // k^R after c^KV in each slot
   p.qs_ckv = t->quant_scale_ckv;
   p.qs_ckr = t->quant_scale_ckr;
   p.sx = t->scale_x; p.sw_dq = t->scale_w_dq; p.sw_uq_qr = t->scale_w_uq_qr;
   p.sw_dkv_kr = t->scale_w_dkv_kr;
   p.smooth_cq = t->smooth_scales_cq;
   p.q_out = t->query_out;
-  p.qr_out = static_cast<uint16_t*>(t->query_rope_out);
+  p.qr_out = dd.concat ? static_cast<uint16_t*>(t->query_out) + dd.Hckv   // q^R after q^N in each row
+                       : static_cast<uint16_t*>(t->query_rope_out);
+  p.bias_dq = t->bias_dqkv;
+  p.bias_uq = t->bias_uq_qr;
+  p.beta_cq = static_cast<const uint16_t*>(t->beta_cq);
+  p.qsc_cq = static_cast<const uint16_t*>(t->quant_scale_cq);
+  p.qo_cq = t->quant_offset_cq;
   p.q_scale = t->dequant_scale_q_nope;
   p.part = h->ws + h->lay.part;
   p.cq = h->ws + h->lay.cq;
@@ -3387,6 +3578,20 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
     (void)hipEventRecord(ev[i < 0 ? kProfileEvents - 1 : i], s);
   };
   mark(0);
+  if (is_static(dd)) {
+    // x to int8 codes first; the down-projection then reads the codes (the
+    // profile books this to the down-projection)
+    XQuant xq;
+    xq.x = static_cast<const uint16_t*>(t->token_x);
+    xq.gamma = static_cast<const uint16_t*>(t->gamma_x);
+    xq.beta = static_cast<const uint16_t*>(t->beta_x);
+    xq.scale = static_cast<const uint16_t*>(t->quant_scale_x);
+    xq.offset = t->quant_offset_x;
+    xq.out = h->ws + h->lay.x8;
+    xq.T = d.T; xq.He = d.He; xq.eps = dd.eps_x;
+    k0_xquant<<<dim3(unsigned(T)), kXqThreads, 0, s>>>(xq);
+    p.x = xq.out;
+  }
   p.packed = static_cast<const uint8_t*>(t->packed_weights);
   FusedGeo fg;
   if (p.packed && pl.stream && h->fused_fit[pl.mt1 == 1 ? 0 : 1] && fused_geo(dd, &fg)) {

@@ -42,7 +42,7 @@ typedef enum {
   MLA_ERR_UNSUPPORTED = 561002    /* legal on the page but no kernel tiling for it here */
 } mla_status;
 
-typedef enum { MLA_BF16 = 0, MLA_INT8 = 1, MLA_INT8_PARTIAL = 2 } mla_dtype;
+typedef enum { MLA_BF16 = 0, MLA_INT8 = 1, MLA_INT8_PARTIAL = 2, MLA_INT8_STATIC = 3 } mla_dtype;
 
 /*
  * Problem description, fixed at create time (the page's "Shape format field
@@ -66,7 +66,7 @@ typedef enum { MLA_BF16 = 0, MLA_INT8 = 1, MLA_INT8_PARTIAL = 2 } mla_dtype;
  *   multiplies c^Q element-wise before that quantisation (scale
  *   RowMax(|c^Q * m|)/127); the product is not divided back by m, so the
  *   int8 weightUqQr is expected to carry 1/m.  Only in_dtype takes this
- *   value.
+ *   value (as it alone takes MLA_INT8_STATIC).
  * query_dtype MLA_INT8: queryOut is int8 with one fp32 dequantisation scale
  *   per (token, head), RowMax(|q^N|)/127 ("Dequant Scale Query Nope
  *   calculation formula"); MLA_BF16: queryOut is bf16.  As in the page's
@@ -79,8 +79,40 @@ typedef enum { MLA_BF16 = 0, MLA_INT8 = 1, MLA_INT8_PARTIAL = 2 } mla_dtype;
  *   codes of k^R with quant_scale_ckr, while full quantisation keeps a bf16
  *   kr cache.  A code is the value times its channel's scale, rounded half
  *   to even and saturated to [-128, 127].  MLA_BF16: bf16 caches.
+ * in_dtype MLA_INT8_STATIC: the static int8 scenario of the MLA preprocess
+ *   page (aclnnMlaPreprocess, "Function" formulas and parameter table,
+ *   quantMode 0: per-tensor static asymmetric quantisation).  tokenX is
+ *   bf16 and the library quantises it by RmsNormQuant:
+ *     code = saturate[-128, 127](round-half-even(f32(v) * quantScale) + quantOffset),
+ *     v = gamma_x * x / sqrt(mean(x^2) + eps_x) + beta_x   (v = x when
+ *     x_quant_only is 1, the page's doRmsNorm false),
+ *   decided in fp32 with the one bf16 quant_scale_x and int8
+ *   quant_offset_x.  weightDq, weightDkvKr and weightUqQr are int8; each
+ *   int8 product is biased and dequantised per output channel,
+ *   y = (acc + bias[n]) * deScale[n] (deScale0 = scale_w_dq | scale_w_dkv_kr,
+ *   bias0 = bias_dqkv; deScale1 = scale_w_uq_qr, bias1 = bias_uq_qr).  c^Q
+ *   is quantised the same way from gamma_cq * y_q / RMS + beta_cq with
+ *   quant_scale_cq / quant_offset_cq; c^KV is RmsNorm(y_kv) with gamma_ckv
+ *   (the page's gamma2).  weightUk and the caches are bf16; queryOut is
+ *   bf16.  Same size rules as in_dtype MLA_INT8.  The scale multiplies, as
+ *   the page's RmsNormQuant formula writes it; the offset is added to the
+ *   rounded product.
+ * concat 1: the preprocess page's cacheMode 0.  queryOut is (T, N, Hckv+Dr),
+ *   each row q^N then q^R, and query_rope_out is NULL; kvCache is
+ *   (block_num, block_size, 1, Hckv+Dr), each row c^KV then k^R, and
+ *   kr_cache is NULL.  bf16 queryOut and caches only.  0: the separate
+ *   outputs and caches of the prolog page (the preprocess page's cacheMode 1).
+ * weights_nk 1: weightDq (Hcq, He), weightDkvKr (Hckv+Dr, He) and weightUqQr
+ *   (N*(D+Dr), Hcq) come transposed, (n, k) row-major, as the preprocess
+ *   page takes its weights (transposeWdq / transposeWuq); its fused
+ *   (Hcq+Hckv+Dr, He) weight is weightDq followed by weightDkvKr.  Runs then
+ *   need packed_weights (the unpacked kernels read (k, n) weights only:
+ *   MLA_ERR_UNSUPPORTED otherwise).  0: (k, n) row-major.
+ * x_quant_only: see MLA_INT8_STATIC; 0 in the other scenarios.
  * max_tokens bounds T of every run; it sizes the handle's workspace.
- * eps_cq / eps_ckv: the two RmsNorm epsilons (the page recommends 1e-5).
+ * eps_cq / eps_ckv: the two RmsNorm epsilons (the page recommends 1e-5);
+ *   eps_x: that of the RmsNorm of x (MLA_INT8_STATIC; the preprocess page
+ *   has one epsilon for its three norms).
  */
 typedef struct {
   int64_t He, Hcq, Hckv, N, D, Dr;
@@ -91,12 +123,17 @@ typedef struct {
   int32_t query_dtype; /* mla_dtype */
   int32_t device;      /* HIP device ordinal the handle and all tensors live on */
   int32_t cache_dtype; /* mla_dtype: MLA_BF16, or MLA_INT8 (quantised caches) */
+  int32_t concat;      /* 0 or 1 */
+  int32_t weights_nk;  /* 0 or 1 */
+  int32_t x_quant_only; /* 0 or 1 */
+  int32_t reserved;    /* 0 */
+  double eps_x;
 } mla_prolog_desc;
 
 /*
  * Tensors of one run (the page's parameter table), all device pointers:
  *   token_x          (T, He)            bf16, or int8
- *   weight_dq        (He, Hcq)          (k, n) row-major, bf16 or int8
+ *   weight_dq        (He, Hcq)          (k, n) row-major (see weights_nk), bf16 or int8
  *   weight_uq_qr     (Hcq, N*(D+Dr))    head-interleaved columns: column
  *                                       h*(D+Dr)+j is W^UQ column h*D+j for
  *                                       j < D, W^QR column h*Dr+j-D otherwise
@@ -115,16 +152,19 @@ typedef struct {
  *   scale_x (T), scale_w_dq (Hcq), scale_w_uq_qr (N*(D+Dr)),
  *   scale_w_dkv_kr (Hckv+Dr)            fp32, int8 mode only, else NULL;
  *                                       partial quantisation takes
- *                                       scale_w_uq_qr alone
+ *                                       scale_w_uq_qr alone; the static
+ *                                       scenario all but scale_x
  *   query_out        (T, N, Hckv)       bf16, or int8 when query_dtype is INT8
- *   query_rope_out   (T, N, Dr)         bf16
+ *                                       ((T, N, Hckv+Dr) with concat)
+ *   query_rope_out   (T, N, Dr)         bf16 (NULL with concat)
  *   dequant_scale_q_nope (T, N)         fp32 when query_dtype is INT8, else NULL
  *   packed_weights                      optional (NULL = none): the output of
  *                                       mla_prolog_pack_weights for these
  *                                       four weights, 256-byte aligned.  When
- *                                       given, small-T runs (T <= 32) stream
- *                                       the weights from it; the row-major
- *                                       weights stay required.
+ *                                       given, every run streams the weights
+ *                                       from it; the unpacked weights stay
+ *                                       required (they are the fallback of
+ *                                       shapes without a packed tiling).
  *   smooth_scales_cq (Hcq)              fp32 smoothScalesCq, optional (NULL =
  *                                       none) with an int8 weightUqQr, NULL
  *                                       otherwise
@@ -132,6 +172,16 @@ typedef struct {
  *                                       fp32 quantScaleCkv / quantScaleCkr:
  *                                       each given exactly when its cache is
  *                                       int8 (see cache_dtype), else NULL
+ * MLA_INT8_STATIC only (NULL otherwise), the preprocess page's names after
+ * the equals sign:
+ *   gamma_x = gamma0, beta_x = beta0   (He) bf16; NULL with x_quant_only
+ *   quant_scale_x = quantScale0 (1) bf16, quant_offset_x = quantOffset0 (1) int8
+ *   bias_dqkv = bias0 (Hcq+Hckv+Dr)     int32, optional (NULL = zeros); each
+ *                                       biased sum acc + bias must fit int32,
+ *                                       like the accumulator (as for bias1)
+ *   beta_cq = beta1 (Hcq)               bf16
+ *   quant_scale_cq = quantScale1 (1) bf16, quant_offset_cq = quantOffset1 (1) int8
+ *   bias_uq_qr = bias1 (N*(D+Dr))       int32, optional (NULL = zeros)
  * Outputs must not alias inputs.
  */
 typedef struct {
@@ -158,6 +208,15 @@ typedef struct {
   const float* smooth_scales_cq;
   const float* quant_scale_ckv;
   const float* quant_scale_ckr;
+  const void* gamma_x;
+  const void* beta_x;
+  const void* quant_scale_x;
+  const int8_t* quant_offset_x;
+  const int32_t* bias_dqkv;
+  const void* beta_cq;
+  const void* quant_scale_cq;
+  const int8_t* quant_offset_cq;
+  const int32_t* bias_uq_qr;
 } mla_prolog_tensors;
 
 typedef struct mla_prolog* mla_prolog_t;

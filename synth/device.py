@@ -33,6 +33,14 @@ def upload(inp: Dict[str, object], device="cuda:0", query_int8=None) -> Dict[str
                       "dequant_scale_w_dkv_kr": "scale_w_dkv_kr"})
     elif inp.get("partial", False):
         names["dequant_scale_w_uq_qr"] = "scale_w_uq_qr"
+    elif inp.get("preprocess", False):
+        names.update({"dequant_scale_w_dq": "scale_w_dq", "dequant_scale_w_uq_qr": "scale_w_uq_qr",
+                      "dequant_scale_w_dkv_kr": "scale_w_dkv_kr", "rmsnorm_beta_cq": "beta_cq",
+                      "quant_scale_x": "quant_scale_x", "quant_offset_x": "quant_offset_x",
+                      "bias_dqkv": "bias_dqkv", "quant_scale_cq": "quant_scale_cq",
+                      "quant_offset_cq": "quant_offset_cq", "bias_uq_qr": "bias_uq_qr"})
+        if inp.get("x_norm", True):
+            names.update({"rmsnorm_gamma_x": "gamma_x", "rmsnorm_beta_x": "beta_x"})
     if inp.get("smooth_scales_cq") is not None:
         names["smooth_scales_cq"] = "smooth_scales_cq"
     for k in ("quant_scale_ckv", "quant_scale_ckr"):
@@ -40,9 +48,11 @@ def upload(inp: Dict[str, object], device="cuda:0", query_int8=None) -> Dict[str
             names[k] = k
     out = {lib_name: _tensor(np.asarray(inp[key]), device) for key, lib_name in names.items()
            if key in inp}
-    out["query_out"] = torch.zeros((T, d.N, d.Hckv), dtype=torch.int8 if q8 else torch.bfloat16,
-                                   device=device)
-    out["query_rope_out"] = torch.zeros((T, d.N, d.Dr), dtype=torch.bfloat16, device=device)
+    concat = bool(inp.get("concat", False))
+    out["query_out"] = torch.zeros((T, d.N, d.Hckv + d.Dr if concat else d.Hckv),
+                                   dtype=torch.int8 if q8 else torch.bfloat16, device=device)
+    if not concat:
+        out["query_rope_out"] = torch.zeros((T, d.N, d.Dr), dtype=torch.bfloat16, device=device)
     if q8:
         out["dequant_scale_q_nope"] = torch.zeros((T, d.N), dtype=torch.float32, device=device)
     return out
@@ -58,7 +68,7 @@ def bits(t: torch.Tensor) -> np.ndarray:
 
 def desc_args(inp: Dict[str, object], max_tokens=None, query_int8=None) -> Dict[str, object]:
     """Keyword arguments of ``make_desc`` for these inputs (in_dtype 0 bf16,
-    1 int8 full quantisation, 2 partial quantisation)."""
+    1 int8 full quantisation, 2 partial quantisation, 3 the static scenario)."""
     d = inp["dims"]
     quant = bool(inp["quant"])
     q8 = quant if query_int8 is None else bool(query_int8)
@@ -66,5 +76,9 @@ def desc_args(inp: Dict[str, object], max_tokens=None, query_int8=None) -> Dict[
                 block_num=int(inp["block_num"]), block_size=int(inp["block_size"]),
                 max_tokens=int(inp["T"]) if max_tokens is None else int(max_tokens),
                 eps_cq=float(inp["eps_cq"]), eps_ckv=float(inp["eps_ckv"]),
-                in_dtype=2 if inp.get("partial", False) else int(quant), query_dtype=int(q8),
-                cache_dtype=int(bool(inp.get("kv_quant", False))))
+                in_dtype=(2 if inp.get("partial", False) else 3 if inp.get("preprocess", False)
+                          else int(quant)),
+                query_dtype=int(q8), cache_dtype=int(bool(inp.get("kv_quant", False))),
+                concat=int(bool(inp.get("concat", False))), weights_nk=int(bool(inp.get("weight_nk", False))),
+                x_quant_only=int(not inp.get("x_norm", True)) if inp.get("preprocess", False) else 0,
+                eps_x=float(inp.get("eps_x", 1e-5)))

@@ -35,17 +35,32 @@ def model_desc(**kw):
 FAKE = 1 << 40   # an aligned address; validate never dereferences it
 
 
-def fake_tensors(q8=False, in8=False, partial=False, smooth=False, kvq=False):
+STATIC_ONLY = ("gamma_x", "beta_x", "quant_scale_x", "quant_offset_x", "bias_dqkv", "beta_cq",
+               "quant_scale_cq", "quant_offset_cq", "bias_uq_qr")
+
+
+def fake_tensors(q8=False, in8=False, partial=False, smooth=False, kvq=False, static=False,
+                 concat=False):
     t = {f: FAKE for f in mla.TENSOR_FIELDS}
+    if not static:
+        for f in STATIC_ONLY:
+            t[f] = None
+    else:
+        t["scale_x"] = None
+    if concat:
+        t["query_rope_out"] = None
+        t["kr_cache"] = None
     if not kvq:
         t["quant_scale_ckv"] = None
     if not (kvq and partial):
         t["quant_scale_ckr"] = None
-    if not in8:
+    if not (in8 or static):
         for f in ("scale_x", "scale_w_dq", "scale_w_dkv_kr"):
             t[f] = None
         if not partial:
             t["scale_w_uq_qr"] = None
+    elif not in8:
+        t["scale_x"] = None
     if not q8:
         t["dequant_scale_q_nope"] = None
     if not smooth:
@@ -68,6 +83,15 @@ def test_valid_descriptions():
                         fake_tensors(partial=True, kvq=True), 32) == mla.MLA_OK
     # the bf16 down-projection of partial quantisation keeps the bf16 size rules
     assert mla.validate(model_desc(in_dtype=mla.MLA_INT8_PARTIAL, He=7176, Hckv=504)) == mla.MLA_OK
+    # the preprocess page's static scenario, its concatenated layout and
+    # transposed weights (which need the packed copy)
+    st = model_desc(in_dtype=mla.MLA_INT8_STATIC, concat=1, weights_nk=1)
+    assert mla.validate(st, fake_tensors(static=True, concat=True), 32) == mla.MLA_OK
+    t = fake_tensors(static=True); t["bias_dqkv"] = None; t["bias_uq_qr"] = None   # biases optional
+    assert mla.validate(model_desc(in_dtype=3), t, 32) == mla.MLA_OK
+    t = fake_tensors(static=True); t["gamma_x"] = None; t["beta_x"] = None
+    assert mla.validate(model_desc(in_dtype=3, x_quant_only=1), t, 32) == mla.MLA_OK
+    assert mla.validate(model_desc(concat=1), fake_tensors(concat=True), 32) == mla.MLA_OK
     tiny = mla.make_desc(256, 64, 32, 2, 16, 8, 4, 16, 4)
     assert mla.validate(tiny, fake_tensors(), 4) == mla.MLA_OK
     assert mla.workspace_bytes(model_desc()) > 0
@@ -79,7 +103,16 @@ def test_valid_descriptions():
     (dict(block_size=24), mla.MLA_ERR_PARAM_INVALID),
     (dict(block_num=-1), mla.MLA_ERR_PARAM_INVALID),
     (dict(eps_cq=-1.0), mla.MLA_ERR_PARAM_INVALID),
-    (dict(in_dtype=3), mla.MLA_ERR_PARAM_INVALID),
+    (dict(in_dtype=4), mla.MLA_ERR_PARAM_INVALID),
+    (dict(in_dtype=3, query_dtype=1), mla.MLA_ERR_PARAM_INVALID),   # the static scenario: bf16 queryOut
+    (dict(in_dtype=3, cache_dtype=1), mla.MLA_ERR_PARAM_INVALID),   # and bf16 caches
+    (dict(in_dtype=3, Hcq=1544), mla.MLA_ERR_UNSUPPORTED),          # int8 size rules
+    (dict(in_dtype=3, eps_x=-1.0), mla.MLA_ERR_PARAM_INVALID),
+    (dict(x_quant_only=1), mla.MLA_ERR_PARAM_INVALID),              # the static scenario's option
+    (dict(concat=2), mla.MLA_ERR_PARAM_INVALID),
+    (dict(weights_nk=-1), mla.MLA_ERR_PARAM_INVALID),
+    (dict(concat=1, in_dtype=1, query_dtype=1), mla.MLA_ERR_PARAM_INVALID),  # concatenated rows are bf16
+    (dict(concat=1, in_dtype=2, cache_dtype=1), mla.MLA_ERR_PARAM_INVALID),
     (dict(query_dtype=1), mla.MLA_ERR_PARAM_INVALID),   # int8 q^N needs int8 inputs
     (dict(He=7164), mla.MLA_ERR_UNSUPPORTED),
     (dict(Dr=128), mla.MLA_ERR_UNSUPPORTED),
@@ -133,6 +166,40 @@ def test_bad_run_arguments():
     assert mla.validate(dpk, t, 8) == mla.MLA_ERR_NULLPTR
     t = fake_tensors(partial=True); t["quant_scale_ckv"] = FAKE                       # bf16 caches
     assert mla.validate(dp, t, 8) == mla.MLA_ERR_PARAM_INVALID
+
+
+def test_bad_static_and_concat_arguments():
+    st = model_desc(in_dtype=mla.MLA_INT8_STATIC)
+    for f in ("quant_scale_x", "quant_offset_x", "beta_cq", "quant_scale_cq", "quant_offset_cq", "gamma_x",
+              "beta_x", "scale_w_dq", "scale_w_uq_qr", "scale_w_dkv_kr"):
+        t = fake_tensors(static=True); t[f] = None
+        assert mla.validate(st, t, 8) == mla.MLA_ERR_NULLPTR, f
+    t = fake_tensors(static=True); t["scale_x"] = FAKE                            # x is quantised here
+    assert mla.validate(st, t, 8) == mla.MLA_ERR_PARAM_INVALID
+    t = fake_tensors(static=True, smooth=True)
+    assert mla.validate(st, t, 8) == mla.MLA_ERR_PARAM_INVALID
+    t = fake_tensors(static=True)                                                 # gamma0 without the norm
+    assert mla.validate(model_desc(in_dtype=3, x_quant_only=1), t, 8) == mla.MLA_ERR_PARAM_INVALID
+    t = fake_tensors(static=True); t["bias_dqkv"] = FAKE + 2
+    assert mla.validate(st, t, 8) == mla.MLA_ERR_PARAM_INVALID
+    t = fake_tensors(static=True); t["gamma_x"] = FAKE + 8                        # read in 16-byte chunks
+    assert mla.validate(st, t, 8) == mla.MLA_ERR_PARAM_INVALID
+    for f in STATIC_ONLY:                                                         # other scenarios
+        t = fake_tensors(); t[f] = FAKE
+        assert mla.validate(model_desc(), t, 8) == mla.MLA_ERR_PARAM_INVALID, f
+    # the concatenated layout has no q^R output or kr cache of its own
+    dc = model_desc(concat=1)
+    for f in ("query_rope_out", "kr_cache"):
+        t = fake_tensors(concat=True); t[f] = FAKE
+        assert mla.validate(dc, t, 8) == mla.MLA_ERR_PARAM_INVALID, f
+    t = fake_tensors(concat=True); t["kv_cache"] = None
+    assert mla.validate(dc, t, 8) == mla.MLA_ERR_NULLPTR
+    t = fake_tensors(); t["query_rope_out"] = None
+    assert mla.validate(model_desc(), t, 8) == mla.MLA_ERR_NULLPTR
+    # transposed weights need the packed copy
+    t = fake_tensors(); t["packed_weights"] = None
+    assert mla.validate(model_desc(weights_nk=1), t, 8) == mla.MLA_ERR_UNSUPPORTED
+    assert mla.validate(model_desc(), t, 8) == mla.MLA_OK
 
 
 def test_empty_run_needs_no_tensors():

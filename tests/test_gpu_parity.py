@@ -50,14 +50,31 @@ def run_gpu(inp, query_int8=None, max_tokens=None, T=None, repeat=1, packed=Fals
             if k in ("query_out", "query_rope_out", "dequant_scale_q_nope", "kv_cache", "kr_cache")}
 
 
+def split_concat(inp, arrays):
+    """queryOut and kvCache of the concatenated layout as the separate
+    outputs (q^N | q^R and c^KV | k^R side by side)."""
+    d = inp["dims"]
+    out = dict(arrays)
+    if arrays.get("query_out") is not None:
+        q = np.asarray(arrays["query_out"])
+        out["query_out"], out["query_rope_out"] = q[..., :d.Hckv], q[..., d.Hckv:]
+    if arrays.get("kv_cache") is not None:
+        kv = np.asarray(arrays["kv_cache"])
+        out["kv_cache"], out["kr_cache"] = kv[..., :d.Hckv], kv[..., d.Hckv:]
+    return out
+
+
 def full_check(inp, query_int8=None, rows=None, packed=False, repeat=1, prerun_negated=False):
     q8 = bool(inp["quant"]) if query_int8 is None else bool(query_int8)
     rows = np.arange(int(inp["T"])) if rows is None else np.asarray(rows)
-    say(f"case {inp['workload']} T={inp['T']} dims={inp['dims']} q8={q8} rows={len(rows)} packed={packed}")
+    say(f"case {inp['workload']} T={inp['T']} dims={inp['dims']} q8={q8} rows={len(rows)} packed={packed} "
+        f"static={inp.get('preprocess', False)} concat={inp.get('concat', False)} nk={inp.get('weight_nk', False)}")
     got = run_gpu(inp, query_int8=query_int8, packed=packed, repeat=repeat, prerun_negated=prerun_negated)
     partial = bool(inp.get("partial", False))
     ref = oracle.run(inp, tokens=rows, query_int8=query_int8, caches=False,
                      intermediates=partial or bool(inp.get("kv_quant", False)))
+    if inp.get("concat", False):
+        got, ref, inp = split_concat(inp, got), split_concat(inp, ref), split_concat(inp, inp)
     allow = None
     if partial:
         # int8 c^Q from a float y: codes at a rounding tie may go either way
@@ -181,8 +198,12 @@ def packed_reference(inp):
     each as k-stages of 4 column tiles x 64 lanes x 16 bytes; lane l of tile
     ct holds rows KL*(l//16)+i of column 16*ct + l%16."""
     d = inp["dims"]
-    i8 = bool(inp["quant"])                        # W^DQ, W^DkvKr
-    i8u = i8 or bool(inp.get("partial", False))    # W^UqQr
+    i8 = bool(inp["quant"]) or bool(inp.get("preprocess", False))   # W^DQ, W^DkvKr
+    i8u = i8 or bool(inp.get("partial", False))                      # W^UqQr
+
+    def kn(key):   # a weight as (k, n)
+        w = np.asarray(inp[key])
+        return w.T if inp.get("weight_nk", False) else w
 
     def windows_of(W, cols, K, kl):
         out = []
@@ -200,12 +221,12 @@ def packed_reference(inp):
     kl = 16 if i8 else 8
     klu = 16 if i8u else 8
     parts = []
-    wdq = np.asarray(inp["weight_dq"])
+    wdq = kn("weight_dq")
     parts += windows_of(wdq, [(c, min(64, d.Hcq - c)) for c in range(0, d.Hcq, 64)], d.He, kl)
-    wkr = np.asarray(inp["weight_dkv_kr"])
+    wkr = kn("weight_dkv_kr")
     nkr = d.Hckv + d.Dr
     parts += windows_of(wkr, [(c, min(64, nkr - c)) for c in range(0, nkr, 64)], d.He, kl)
-    wuq = np.asarray(inp["weight_uq_qr"])
+    wuq = kn("weight_uq_qr")
     cols = []
     for h in range(d.N):
         base = h * (d.D + d.Dr)
@@ -217,9 +238,10 @@ def packed_reference(inp):
     return np.concatenate(parts)
 
 
-@pytest.mark.parametrize("name", ["tiny_t4", "ragged_t5_wide", "partial_t37"])
+@pytest.mark.parametrize("name", ["tiny_t4", "ragged_t5_wide", "partial_t37", "tiny_pre_t4"])
 def test_packed_layout(name):
-    inp = synth.make_inputs(SMALL[name] if name in SMALL else PARTIAL[name])
+    inp = synth.make_inputs(SMALL[name] if name in SMALL else PARTIAL[name] if name in PARTIAL
+                            else synth.workload(name))
     say(f"case pack layout {name}")
     t = dev.upload(inp)
     desc = mla.make_desc(**dev.desc_args(inp))
@@ -552,3 +574,80 @@ def test_max_head_dims_int8(T):
     inp = synth.make_inputs(wl)
     full_check(inp, packed=True)
     full_check(inp, query_int8=False, packed=True)
+
+
+# ---- the MLA preprocess page's static int8 scenario (quantMode 0), its
+# concatenated layout (cacheMode 0) and transposed weights ------------------
+def _pre(name, T, dims, seed, **kw):
+    kw.setdefault("preprocess", True)
+    kw.setdefault("concat", True)
+    kw.setdefault("weight_nk", True)
+    return custom_workload(name, T=T, dims=dims, block_num=max(2, -(-T // 16) + 1), block_size=16,
+                           seed=seed, **kw)
+
+
+MID = Dims(He=1024, Hcq=256, Hckv=512, N=4, D=128, Dr=64)
+STATIC = {
+    "pre_t4": synth.workload("tiny_pre_t4"),
+    "pre_t37": _pre("pre_t37", 37, Dims(He=272, Hcq=80, Hckv=48, N=3, D=32, Dr=16), 91),
+    "pre_t17_pair": _pre("pre_t17_pair", 17, Dims(He=512, Hcq=256, Hckv=256, N=8, D=128, Dr=64), 92),
+    "pre_t70": _pre("pre_t70", 70, MID, 93),
+    "pre_t130": _pre("pre_t130", 130, Dims(He=1024, Hcq=192, Hckv=512, N=3, D=128, Dr=64), 94),
+    "pre_t600": _pre("pre_t600", 600, Dims(He=512, Hcq=128, Hckv=64, N=2, D=32, Dr=16), 95),
+    "pre_t2048": _pre("pre_t2048", 2048, Dims(He=512, Hcq=128, Hckv=64, N=2, D=32, Dr=16), 96),
+}
+
+
+@pytest.mark.parametrize("name", list(STATIC))
+def test_static_packed(name):
+    full_check(synth.make_inputs(STATIC[name]), packed=True, repeat=2, prerun_negated=True)
+
+
+def test_static_without_input_norm_packed():
+    full_check(synth.make_inputs(_pre("pre_xq_t37", 37, Dims(He=272, Hcq=80, Hckv=48, N=3, D=32, Dr=16), 97,
+                                      x_norm=False)), packed=True)
+
+
+@pytest.mark.parametrize("concat", [False, True], ids=["split", "concat"])
+def test_static_row_major(concat):
+    # the unpacked kernels take (k, n) weights
+    full_check(synth.make_inputs(_pre("pre_rm_t9", 9, Dims(He=256, Hcq=64, Hckv=32, N=2, D=16, Dr=16), 98,
+                                      concat=concat, weight_nk=False)))
+
+
+def test_full_size_static_decode_packed():
+    inp = synth.make_inputs(synth.workload("pre_decode_t32"))
+    full_check(inp, rows=sample_rows(32, k=6), packed=True)
+
+
+CONCAT_BF16 = {
+    "cat_t5": _pre("cat_t5", 5, Dims(He=264, Hcq=72, Hckv=40, N=3, D=24, Dr=16), 101, preprocess=False),
+    "cat_t32_pair": _pre("cat_t32_pair", 32, Dims(He=256, Hcq=192, Hckv=320, N=8, D=96, Dr=64), 102,
+                         preprocess=False),
+    "cat_t70": _pre("cat_t70", 70, MID, 103, preprocess=False),
+    "cat_t2048": _pre("cat_t2048", 2048, Dims(He=512, Hcq=128, Hckv=64, N=2, D=32, Dr=16), 104,
+                      preprocess=False),
+}
+
+
+@pytest.mark.parametrize("name", list(CONCAT_BF16))
+def test_concat_bf16_packed(name):
+    # cat_t32_pair runs on the one-kernel path
+    full_check(synth.make_inputs(CONCAT_BF16[name]), packed=True, repeat=2, prerun_negated=True)
+
+
+def test_concat_bf16_packed_unfused(monkeypatch):
+    monkeypatch.setenv("MLA_PROLOG_FUSED", "0")
+    full_check(synth.make_inputs(CONCAT_BF16["cat_t32_pair"]), packed=True)
+
+
+def test_concat_bf16_row_major():
+    wl = _pre("cat_rm_t37", 37, Dims(He=264, Hcq=72, Hckv=40, N=3, D=24, Dr=16), 105, preprocess=False,
+              weight_nk=False)
+    full_check(synth.make_inputs(wl))
+
+
+def test_full_size_concat_decode_packed():
+    from dataclasses import replace
+    wl = replace(synth.workload("decode_t32"), name="decode_t32_concat", concat=True, weight_nk=True)
+    full_check(synth.make_inputs(wl), rows=sample_rows(32, k=6), packed=True)
