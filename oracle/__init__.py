@@ -262,3 +262,57 @@ def run(inp: Dict[str, object], tokens: Optional[Sequence[int]] = None,
         if kr is not None:
             out["kr_cache"] = kr
     return out
+
+
+# ---- the sparse flash attention consumer of the caches ---------------------
+class SfaProblem(ctypes.Structure):
+    _fields_ = [
+        ("T", _I64), ("N", _I64), ("D", _I64), ("Dr", _I64), ("block_num", _I64), ("block_size", _I64),
+        ("K", _I64), ("sparse_block_size", _I64), ("max_blocks", _I64), ("scale", ctypes.c_double),
+        ("concat", ctypes.c_int32), ("mutation", ctypes.c_int32),
+        ("query", _P), ("query_rope", _P), ("kv", _P), ("kr", _P), ("indices", _P),
+        ("block_table", _P), ("seq_lens", _P), ("out", _P), ("softmax_max", _P), ("softmax_sum", _P),
+        ("out_f64", _P), ("tokens", _P), ("n_tokens", _I64),
+    ]
+
+
+def sfa(inp: Dict[str, object], tokens: Optional[Sequence[int]] = None, mutation: int = 0,
+        nthreads: int = 0) -> Dict[str, np.ndarray]:
+    """Sparse flash attention (MLA-absorb, one decode query per batch) on the
+    host arrays of ``synth.sfa.make_sfa_inputs``: attention_out (bf16 bits),
+    softmax_max, softmax_sum and the unrounded out_f64 of the selected rows."""
+    L = lib()
+    if not getattr(L, "_sfa_ready", False):
+        L.mla_oracle_sfa.argtypes = [ctypes.POINTER(SfaProblem), ctypes.c_int]
+        L.mla_oracle_sfa.restype = ctypes.c_int
+        L._sfa_ready = True
+    keep = []
+
+    def arr(a, dtype):
+        a = np.ascontiguousarray(a, dtype=dtype)
+        keep.append(a)
+        return a
+
+    T, N, D, Dr = int(inp["T"]), int(inp["N"]), int(inp["D"]), int(inp["Dr"])
+    rows = None if tokens is None else arr(np.asarray(tokens), np.int64)
+    n = T if rows is None else rows.size
+    out = {"attention_out": np.zeros((n, N, D), np.uint16), "softmax_max": np.zeros((n, N), np.float32),
+           "softmax_sum": np.zeros((n, N), np.float32), "out_f64": np.zeros((n, N, D))}
+    p = SfaProblem()
+    p.T, p.N, p.D, p.Dr = T, N, D, Dr
+    p.block_num, p.block_size = int(inp["block_num"]), int(inp["block_size"])
+    p.K, p.sparse_block_size, p.max_blocks = int(inp["K"]), int(inp["sparse_block_size"]), int(inp["max_blocks"])
+    p.scale, p.concat, p.mutation = float(inp["scale"]), int(bool(inp["concat"])), int(mutation)
+    p.query, p.query_rope = _ptr(arr(inp["query"], np.uint16)), _ptr(arr(inp["query_rope"], np.uint16))
+    p.kv = _ptr(arr(inp["kv_cache"], np.uint16))
+    if not inp["concat"]:
+        p.kr = _ptr(arr(inp["kr_cache"], np.uint16))
+    p.indices, p.block_table = _ptr(arr(inp["indices"], np.int32)), _ptr(arr(inp["block_table"], np.int32))
+    p.seq_lens = _ptr(arr(inp["seq_lens"], np.int32))
+    p.out, p.softmax_max, p.softmax_sum = (_ptr(out["attention_out"]), _ptr(out["softmax_max"]),
+                                           _ptr(out["softmax_sum"]))
+    p.out_f64 = _ptr(out["out_f64"])
+    p.tokens, p.n_tokens = _ptr(rows), n
+    if L.mla_oracle_sfa(ctypes.byref(p), int(nthreads)) != 0:
+        raise ValueError("oracle rejected the problem")
+    return out

@@ -72,6 +72,19 @@
 // outputs: each queryOut row holds q^N then q^R (Hckv + Dr values) and each
 // kvCache row c^KV then k^R; its weights come transposed, (n, k) row-major.
 //
+// The consumer of the caches, mla_oracle_sfa, is the sparse flash attention
+// page (aclnnSparseFlashAttention, "Function" formula, parameter table,
+// attentionMode 2 = MLA-absorb) for one query per batch (decode): per token
+// t and head h, over the cache rows its sparse indices select (index i
+// selects positions i*sparseBlockSize .. +sparseBlockSize-1, those below the
+// batch's kv length, mapped to slots through its block table; negative
+// indices select nothing),
+//   s_j = scaleValue * ([q^N | q^R] . [c^KV_j | k^R_j]),
+//   out = sum_j softmax(s)_j c^KV_j,
+// softmaxMax = max_j s_j and softmaxSum = sum_j exp(s_j - max).  A token
+// with no selected row gets out = 0, max = -inf, sum = 0.  Double
+// arithmetic, out rounded to bf16 once.
+//
 // Every function here is pinned by the CPU tests (closed forms, invariants,
 // special cases, brute force on tiny shapes, planted mistakes); none is
 // unpinned.
@@ -548,6 +561,107 @@ int mla_oracle_run(mla_oracle_problem* p, int nthreads) {
                   static_cast<const uint8_t*>(q.kr_rows) + r * p->Dr * kr_eb, kr_eb * p->Dr);
     }
   }
+  return 0;
+}
+
+
+// ---------------------------------------------------------------------------
+// sparse flash attention, MLA-absorb decode (see the file header)
+// ---------------------------------------------------------------------------
+typedef struct {
+  int64_t T, N, D, Dr;            // D = the latent width (Hckv), Dr the rope width
+  int64_t block_num, block_size, K, sparse_block_size, max_blocks;
+  double scale;
+  int32_t concat;                 // 1: kv rows hold D + Dr values, k^R after c^KV; kr unused
+  int32_t mutation;               // planted mistake for the pin tests, 0 = none
+  const uint16_t* query;          // (T, N, D) bf16
+  const uint16_t* query_rope;     // (T, N, Dr) bf16
+  const uint16_t* kv;             // (block_num, block_size, D or D + Dr) bf16
+  const uint16_t* kr;             // (block_num, block_size, Dr) bf16
+  const int32_t* indices;         // (T, K)
+  const int32_t* block_table;     // (T, max_blocks)
+  const int32_t* seq_lens;        // (T) kv length of each token's batch
+  uint16_t* out;                  // (T, N, D) bf16
+  float* softmax_max;             // (T, N) or NULL
+  float* softmax_sum;             // (T, N) or NULL
+  double* out_f64;                // (T, N, D) before rounding, or NULL
+  const int64_t* tokens;          // rows to compute; NULL = 0..T-1 (row r holds token tokens[r])
+  int64_t n_tokens;
+} mla_oracle_sfa_problem;
+
+static void sfa_token(const mla_oracle_sfa_problem* p, int64_t r, int64_t t) {
+  const int64_t D = p->D, Dr = p->Dr, N = p->N, row = p->concat ? D + Dr : D;
+  const int mut = p->mutation;
+  // the selected slots, in index order
+  std::vector<int64_t> slots;
+  for (int64_t i = 0; i < p->K; ++i) {
+    const int64_t idx = p->indices[t * p->K + i];
+    if (idx < 0) continue;
+    for (int64_t u = 0; u < p->sparse_block_size; ++u) {
+      const int64_t pos = idx * p->sparse_block_size + u;
+      if (pos >= p->seq_lens[t]) continue;
+      const int64_t b = pos / p->block_size;
+      if (b >= p->max_blocks) continue;
+      const int64_t blk = mut == 23 ? b : p->block_table[t * p->max_blocks + b];  // planted 23: table ignored
+      if (blk < 0 || blk >= p->block_num) continue;
+      slots.push_back(blk * p->block_size + pos % p->block_size);
+    }
+  }
+  std::vector<double> s(slots.size()), o(D);
+  for (int64_t h = 0; h < N; ++h) {
+    const uint16_t* q = p->query + (t * N + h) * D;
+    const uint16_t* qr = p->query_rope + (t * N + h) * Dr;
+    double mx = -INFINITY;
+    for (size_t j = 0; j < slots.size(); ++j) {
+      const uint16_t* kv = p->kv + slots[j] * row;
+      const uint16_t* kr = p->concat ? kv + D : p->kr + slots[j] * Dr;
+      double a = 0.0, b = 0.0;
+      for (int64_t d = 0; d < D; ++d) a += bf16_value(q[d]) * bf16_value(kv[d]);
+      for (int64_t d = 0; d < Dr; ++d) b += bf16_value(qr[d]) * bf16_value(kr[d]);
+      if (mut == 21) b = 0.0;                                   // planted 21: rope part dropped
+      s[j] = (mut == 22 ? p->scale * p->scale : p->scale) * (a + b);  // planted 22: scale squared
+      mx = std::max(mx, s[j]);
+    }
+    double sum = 0.0;
+    for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+    for (size_t j = 0; j < slots.size(); ++j) {
+      const double w = std::exp(s[j] - mx);
+      sum += w;
+      const uint16_t* kv = p->kv + slots[j] * row;
+      for (int64_t d = 0; d < D; ++d) o[d] += w * bf16_value(kv[d]);
+    }
+    for (int64_t d = 0; d < D; ++d) {
+      const double v = slots.empty() ? 0.0 : o[d] / sum;
+      if (p->out_f64) p->out_f64[(r * N + h) * D + d] = v;
+      p->out[(r * N + h) * D + d] = bf16_bits(v);
+    }
+    if (p->softmax_max) p->softmax_max[r * N + h] = static_cast<float>(mx);
+    if (p->softmax_sum) p->softmax_sum[r * N + h] = static_cast<float>(sum);
+  }
+}
+
+// Returns 0, or -1 on a bad argument.
+int mla_oracle_sfa(mla_oracle_sfa_problem* p, int nthreads) {
+  if (!p || !p->query || !p->query_rope || !p->kv || (!p->concat && !p->kr) || !p->indices ||
+      !p->block_table || !p->seq_lens || !p->out)
+    return -1;
+  if (p->N <= 0 || p->D <= 0 || p->Dr <= 0 || p->block_size <= 0 || p->K <= 0 ||
+      p->sparse_block_size <= 0 || p->max_blocks <= 0)
+    return -1;
+  const int64_t n = p->tokens ? p->n_tokens : p->T;
+  for (int64_t r = 0; r < n; ++r) {
+    const int64_t t = p->tokens ? p->tokens[r] : r;
+    if (t < 0 || t >= p->T) return -1;
+  }
+  unsigned hw = std::thread::hardware_concurrency();
+  int nt = nthreads > 0 ? nthreads : static_cast<int>(hw ? hw : 1);
+  nt = static_cast<int>(std::min<int64_t>(nt, std::max<int64_t>(n, 1)));
+  std::vector<std::thread> pool;
+  for (int w = 0; w < nt; ++w)
+    pool.emplace_back([p, w, nt, n]() {
+      for (int64_t r = w; r < n; r += nt) sfa_token(p, r, p->tokens ? p->tokens[r] : r);
+    });
+  for (auto& th : pool) th.join();
   return 0;
 }
 

@@ -44,6 +44,9 @@ _STREAM = {
     "sw_dq": 13, "sw_uq_qr": 14, "sw_dkv_kr": 15, "blocks": 16, "smooth_cq": 17,
     "qs_ckv": 18, "qs_ckr": 19, "gamma_x": 20, "beta_x": 21, "qs_x": 22, "qo_x": 23,
     "bias_dqkv": 24, "beta_cq": 25, "qs_cq": 26, "qo_cq": 27, "bias_uq": 28,
+    # the sparse attention consumer
+    "sfa_q": 40, "sfa_qr": 41, "sfa_kv": 42, "sfa_kr": 43, "sfa_len": 44, "sfa_blocks": 45,
+    "sfa_idx": 46,
 }
 
 
