@@ -20,6 +20,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -111,6 +113,104 @@ def cpu_baseline(inp, seconds):
                       f"of {inp['workload']}) in {el:.1f} s"}
 
 
+SFA_METRIC = "sparse flash attention (MLA-absorb) decode tokens/s; % HBM roofline"
+
+
+def sfa_bytes(inp, T):
+    """Bytes a sparse attention step must move at minimum: the selected cache
+    rows (each read once), the queries, the outputs, indices and tables."""
+    N, D, Dr, K, sbs = (int(inp[k]) for k in ("N", "D", "Dr", "K", "sparse_block_size"))
+    return (T * K * sbs * (D + Dr) * 2 + T * N * (D + Dr) * 2 + T * N * D * 2 + T * N * 8
+            + T * K * 4 + T * int(inp["max_blocks"]) * 4 + T * 4)
+
+
+def bench_sfa(args):
+    """One step = one mla_sfa_run over the workload's tokens.  The caches
+    (filled on the device) are several times the Infinity Cache and each
+    step takes the next of several index sets, so the selected rows come
+    from HBM."""
+    import torch
+    import head_latent_attention_amd as mla
+    from dataclasses import replace
+    from synth.sfa import make_sfa_inputs, sfa_workload
+    wl = sfa_workload(args.workload)
+    # longer sequences than the parity workload: a 2 GB cache
+    wl = replace(wl, len_lo=49152, len_hi=65536)
+    sets = 8
+    inps = [make_sfa_inputs(replace(wl, seed=wl.seed + 1000 * r), caches=False) for r in range(sets)]
+    inp = inps[0]
+    T, N, D, Dr = int(inp["T"]), int(inp["N"]), int(inp["D"]), int(inp["Dr"])
+    block_num = max(int(i["block_num"]) for i in inps)
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(wl.seed)
+    kv = torch.randn((block_num, int(inp["block_size"]), 1, D), generator=gen, device="cuda:0").to(torch.bfloat16)
+    kr = torch.randn((block_num, int(inp["block_size"]), 1, Dr), generator=gen, device="cuda:0").to(torch.bfloat16)
+    dev_sets = []
+    for i in inps:
+        dev_sets.append({
+            "query": torch.from_numpy(i["query"].view(np.int16)).to("cuda:0").view(torch.bfloat16),
+            "query_rope": torch.from_numpy(i["query_rope"].view(np.int16)).to("cuda:0").view(torch.bfloat16),
+            "kv_cache": kv, "kr_cache": kr,
+            "sparse_indices": torch.from_numpy(i["indices"]).to("cuda:0"),
+            "block_table": torch.from_numpy(i["block_table"]).to("cuda:0"),
+            "seq_lens_kv": torch.from_numpy(i["seq_lens"]).to("cuda:0")})
+    out = torch.empty((T, N, D), dtype=torch.bfloat16, device="cuda:0")
+    smax = torch.empty((T, N), dtype=torch.float32, device="cuda:0")
+    ssum = torch.empty((T, N), dtype=torch.float32, device="cuda:0")
+    for d in dev_sets:
+        d.update(attention_out=out, softmax_max=smax, softmax_sum=ssum)
+    desc = mla.make_sfa_desc(N=N, D=D, Dr=Dr, block_num=block_num, block_size=int(inp["block_size"]),
+                             max_blocks=int(inp["max_blocks"]), sparse_size=int(inp["K"]),
+                             sparse_block_size=int(inp["sparse_block_size"]), max_tokens=T,
+                             scale=float(inp["scale"]))
+    h = mla.MlaSfa(desc)
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        h.run(dev_sets[i % sets], T, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        h.run(dev_sets[i % sets], T, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    h.close()
+    nbytes = sfa_bytes(inp, T)
+    achieved = nbytes / (ms_step * 1e-3) / 1e9
+    res = {
+        "metric": SFA_METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "T": T, "N": N, "D": D, "Dr": Dr, "sparse_size": int(inp["K"]),
+                   "sparse_block_size": int(inp["sparse_block_size"]), "block_size": int(inp["block_size"]),
+                   "kv_len": [wl.len_lo, wl.len_hi], "cache_bytes": int(kv.numel() * 2 + kr.numel() * 2),
+                   "index_sets": sets},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "k_sfa + k_sfa_combine",
+                     "per_launch": f"{nbytes} B"},
+        "wall_s": wall,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        small = make_sfa_inputs(replace(sfa_workload(args.workload), T=2, len_lo=4096, len_hi=8192))
+        cores = len(os.sched_getaffinity(0))
+        oracle.sfa(small, tokens=[0], nthreads=cores)
+        done, t0 = 0, time.perf_counter()
+        while True:
+            oracle.sfa(small, nthreads=cores)
+            done += 2
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        res["cpu_baseline"] = {"value": done / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+                               "sample": f"{done} tokens (passes over a 2-token instance of the workload's "
+                                         f"shapes, same sparse_size) in {el:.1f} s"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -118,7 +218,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_t32",
                     choices=["decode_t32", "decode_t256", "prefill_t8192", "int8_decode_t128",
-                             "partial_decode_t32", "int8_kvq_decode_t128", "pre_decode_t32", "tiny_t4"])
+                             "partial_decode_t32", "int8_kvq_decode_t128", "pre_decode_t32", "tiny_t4",
+                             "sfa_decode_t32"])
     ap.add_argument("--replicas", type=int, default=0, help="weight replicas (0 = enough to "
                     "exceed twice the Infinity Cache)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -147,6 +248,9 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.workload.startswith("sfa_"):
+        bench_sfa(args)
+        return
     import torch
     import head_latent_attention_amd as mla
     import synth

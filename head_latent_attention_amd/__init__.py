@@ -17,6 +17,8 @@ from typing import Dict, Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCE = os.path.join(HERE, "csrc", "mla_prolog.hip")
+#: every HIP source of the library: the prolog and its cache consumer
+SOURCES = (SOURCE, os.path.join(HERE, "csrc", "mla_sfa.hip"))
 LIBRARY = os.path.join(HERE, "libmla_prolog.so")
 # MFMA accumulators in VGPRs: with the default AGPR form the register
 # allocator rotates the accumulators of the software-pipelined loops through
@@ -39,7 +41,8 @@ MLA_INT8_STATIC = 3    # in_dtype only: the preprocess page's static int8 scenar
 EXPORTS = ("mla_prolog_validate", "mla_prolog_workspace_bytes", "mla_prolog_packed_weights_bytes",
            "mla_prolog_pack_weights", "mla_prolog_create",
            "mla_prolog_run", "mla_prolog_destroy", "mla_prolog_profile_enable",
-           "mla_prolog_profile_read", "mla_prolog_check", "mla_prolog_status_string")
+           "mla_prolog_profile_read", "mla_prolog_check", "mla_prolog_status_string",
+           "mla_sfa_validate", "mla_sfa_create", "mla_sfa_run", "mla_sfa_destroy")
 #: kernel order of mla_prolog_profile_read
 KERNELS = ("down_proj", "norm_rope_cache", "up_proj", "uk")
 
@@ -47,7 +50,7 @@ KERNELS = ("down_proj", "norm_rope_cache", "up_proj", "uk")
 def build() -> str:
     """Compile the HIP library for gfx950 with hipcc (always recompiles)."""
     hipcc = os.environ.get("HIPCC", "hipcc")
-    subprocess.run([hipcc, *HIPCC_FLAGS, "-o", LIBRARY, SOURCE], check=True)
+    subprocess.run([hipcc, *HIPCC_FLAGS, "-o", LIBRARY, *SOURCES], check=True)
     return LIBRARY
 
 
@@ -118,6 +121,14 @@ def lib() -> ctypes.CDLL:
         L.mla_prolog_check.restype = ctypes.c_int
         L.mla_prolog_status_string.argtypes = [ctypes.c_int]
         L.mla_prolog_status_string.restype = ctypes.c_char_p
+        L.mla_sfa_validate.argtypes = [ctypes.POINTER(SfaDesc), ctypes.POINTER(SfaTensors), ctypes.c_int64]
+        L.mla_sfa_validate.restype = ctypes.c_int
+        L.mla_sfa_create.argtypes = [ctypes.POINTER(SfaDesc), ctypes.POINTER(ctypes.c_void_p)]
+        L.mla_sfa_create.restype = ctypes.c_int
+        L.mla_sfa_run.argtypes = [ctypes.c_void_p, ctypes.POINTER(SfaTensors), ctypes.c_int64, ctypes.c_void_p]
+        L.mla_sfa_run.restype = ctypes.c_int
+        L.mla_sfa_destroy.argtypes = [ctypes.c_void_p]
+        L.mla_sfa_destroy.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -234,6 +245,78 @@ class MlaProlog:
                 raise MlaError(chk, "mla_prolog_check")
             if st != MLA_OK:
                 raise MlaError(st, "mla_prolog_destroy")
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ---- sparse flash attention over the caches (include/mla_sfa.h) ------------
+class SfaDesc(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int64), ("D", ctypes.c_int64), ("Dr", ctypes.c_int64),
+                ("block_num", ctypes.c_int64), ("block_size", ctypes.c_int64), ("max_blocks", ctypes.c_int64),
+                ("sparse_size", ctypes.c_int64), ("sparse_block_size", ctypes.c_int64),
+                ("max_tokens", ctypes.c_int64), ("scale", ctypes.c_double),
+                ("concat", ctypes.c_int32), ("device", ctypes.c_int32)]
+
+
+SFA_TENSOR_FIELDS = ("query", "query_rope", "kv_cache", "kr_cache", "sparse_indices", "block_table",
+                     "seq_lens_kv", "attention_out", "softmax_max", "softmax_sum")
+
+
+class SfaTensors(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_void_p) for f in SFA_TENSOR_FIELDS]
+
+
+def make_sfa_desc(N, D, Dr, block_num, block_size, max_blocks, sparse_size, sparse_block_size, max_tokens,
+                  scale, concat=0, device=0) -> SfaDesc:
+    return SfaDesc(N, D, Dr, block_num, block_size, max_blocks, sparse_size, sparse_block_size, max_tokens,
+                   float(scale), int(concat), device)
+
+
+def make_sfa_tensors(tensors: Dict[str, object]) -> SfaTensors:
+    unknown = set(tensors) - set(SFA_TENSOR_FIELDS)
+    if unknown:
+        raise KeyError(f"unknown tensor names {sorted(unknown)}")
+    return SfaTensors(*[_address(tensors.get(f)) for f in SFA_TENSOR_FIELDS])
+
+
+def sfa_validate(desc: SfaDesc, tensors: Optional[Dict[str, object]] = None, T: int = 0) -> int:
+    t = make_sfa_tensors(tensors) if tensors is not None else None
+    return lib().mla_sfa_validate(ctypes.byref(desc), ctypes.byref(t) if t is not None else None, int(T))
+
+
+class MlaSfa:
+    """Sparse flash attention handle: ``MlaSfa(desc)``, then ``run(tensors, T, stream)``."""
+
+    def __init__(self, desc: SfaDesc):
+        self.desc = desc
+        h = ctypes.c_void_p()
+        st = lib().mla_sfa_create(ctypes.byref(desc), ctypes.byref(h))
+        if st != MLA_OK:
+            raise MlaError(st, "mla_sfa_create")
+        self._h = h
+
+    def run(self, tensors: Dict[str, object], T: int, stream=None) -> None:
+        t = make_sfa_tensors(tensors)
+        st = lib().mla_sfa_run(self._h, ctypes.byref(t), int(T), ctypes.c_void_p(_stream_handle(stream)))
+        if st != MLA_OK:
+            raise MlaError(st, "mla_sfa_run")
+
+    def close(self) -> None:
+        if self._h:
+            st = lib().mla_sfa_destroy(self._h)
+            self._h = None
+            if st != MLA_OK:
+                raise MlaError(st, "mla_sfa_destroy")
 
     def __enter__(self):
         return self

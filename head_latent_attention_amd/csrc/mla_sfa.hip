@@ -1,0 +1,469 @@
+// Sparse flash attention, MLA-absorb decode, for MI355X (gfx950): the
+// consumer of the MLA prolog's paged caches (aclnnSparseFlashAttention,
+// "Function" formula, parameter table, attentionMode 2).
+//
+// Per token t and head h, over the cache rows t's sparse indices select:
+//   s_j = scale [q^N | q^R][t, h] . [c^KV_j | k^R_j],
+//   out[t, h] = sum_j softmax(s)_j c^KV_j   (value = key = c^KV).
+//
+// k_sfa: one block per (token, split of the selected rows, group of 64
+// heads); four waves of 16 heads.  The block's heads' queries sit in LDS;
+// 32 selected cache rows at a time are gathered into an LDS tile (the next
+// two tiles' loads in flight in registers), then each wave takes
+// S = Q K^T on MFMA (B fragments are 16-byte row reads of the tile), an
+// online softmax per head row, and O += P V on MFMA, with P through a small
+// per-wave LDS tile and the V fragments read from the same row-major tile
+// by transposing LDS reads (ds_read_b64_tr_b16: lane i of each 16-lane
+// group receives element i%4 of the 8-byte pieces read by lanes 4e + i/4).
+// With more than one split, k_sfa_combine merges the splits' normalised
+// partial outputs by their (max, sum) pairs in split order.  No atomics: a
+// run is deterministic.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "../../include/mla_sfa.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr int kWaves = 4;             // waves per block, 16 heads each
+constexpr int kHeads = 16 * kWaves;   // heads per block
+constexpr int kRows = 32;             // cache rows per tile
+constexpr int kMaxW = 576;            // D + Dr at most
+constexpr int kPitch = kMaxW + 8;     // LDS row pitch (bf16): rows 4 banks apart
+constexpr int kMaxKS = kMaxW / 32;    // MFMA k-steps of S = Q K^T
+constexpr int kMaxDT = 512 / 16;      // 16-column tiles of O
+constexpr int kPer = (kRows * (kMaxW / 8) + 64 * kWaves - 1) / (64 * kWaves);  // 16-byte loads per thread per tile
+constexpr int kMaxRows = 2048;        // selected rows of one block
+constexpr int kPPitch = kRows + 8;    // per-wave P tile pitch (bf16)
+
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// A barrier that orders LDS only: the tile loop keeps the next tiles'
+// global loads in flight across it (a full __syncthreads would wait for them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+struct SfaArgs {
+  const uint16_t* q;      // (T, N, D)
+  const uint16_t* qr;     // (T, N, Dr)
+  const uint16_t* kv;     // slots of kv_row elements
+  const uint16_t* kr;     // slots of kr_row elements (kv + D with the concatenated cache)
+  const int32_t* idx;     // (T, K)
+  const int32_t* table;   // (T, max_blocks)
+  const int32_t* lens;    // (T)
+  uint16_t* out;          // (T, N, D)
+  float* smax;            // (T, N) or NULL
+  float* ssum;            // (T, N) or NULL
+  float* part_o;          // [T][S][N][D] split outputs, each divided by its own sum
+  float* part_ml;         // [T][S][N][2] their (max, sum)
+  int T, N, D, Dr, bs, max_blocks, K, sbs, S, rows_per_split, block_num;
+  int kv_row, kr_row;
+  float scale;
+};
+
+__global__ __launch_bounds__(64 * kWaves) void k_sfa(SfaArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t qs[kHeads * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t kt[kRows * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t pw[kWaves][16 * kPPitch];
+  __shared__ int32_t slots[kMaxRows];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c = lane & 15;
+  // block -> (token, split) and head group: the head groups of one (token,
+  // split) are 8 blocks apart, so they run on the same XCD and share its L2
+  const int HB = (a.N + kHeads - 1) / kHeads;
+  const int b = blockIdx.x;
+  const int flat = (b / (8 * HB)) * 8 + b % 8;
+  const int hb = (b / 8) % HB;
+  if (flat >= a.T * a.S) return;
+  const int t = flat / a.S, s = flat % a.S;
+  const int W = a.D + a.Dr, cpr = W / 8, KS = W / 32, DT = a.D / 16;
+  const int tile_chunks = kRows * cpr;
+
+  // the selected slots of this split (-1: nothing)
+  const int R = a.K * a.sbs;
+  const int r0 = s * a.rows_per_split, nrows = max(0, min(R, r0 + a.rows_per_split) - r0);
+  const int len = a.lens[t];
+  for (int r = tid; r < nrows; r += 64 * kWaves) {
+    const int rr = r0 + r, e = rr / a.sbs, off = rr % a.sbs;
+    const int ix = a.idx[int64_t(t) * a.K + e];
+    int slot = -1;
+    if (ix >= 0) {
+      const int64_t pos = int64_t(ix) * a.sbs + off;
+      if (pos < len && pos / a.bs < a.max_blocks) {
+        const int blk = a.table[int64_t(t) * a.max_blocks + pos / a.bs];
+        if (blk >= 0 && blk < a.block_num) slot = blk * a.bs + int(pos % a.bs);
+      }
+    }
+    slots[r] = slot;
+  }
+  // the block's queries, [q^N | q^R] per head row (zeros past N)
+  for (int q = tid; q < kHeads * cpr; q += 64 * kWaves) {
+    const int hr = q / cpr, cc = q % cpr, h = hb * kHeads + hr;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (h < a.N)
+      v = 8 * cc < a.D ? *reinterpret_cast<const uint4*>(a.q + (int64_t(t) * a.N + h) * a.D + 8 * cc)
+                       : *reinterpret_cast<const uint4*>(a.qr + (int64_t(t) * a.N + h) * a.Dr + 8 * cc - a.D);
+    *reinterpret_cast<uint4*>(&qs[hr * kPitch + 8 * cc]) = v;
+  }
+  __syncthreads();
+
+  const int ntiles = (nrows + kRows - 1) / kRows;
+  uint4 pre[2][kPer];
+  // loads of tile `tile` into register set `set`; rows without a slot read as zeros
+  auto issue = [&](uint4 (&buf)[kPer], int tile) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int q = tid + 64 * kWaves * i;
+      buf[i] = make_uint4(0, 0, 0, 0);
+      if (tile < ntiles && q < tile_chunks) {
+        const int row = q / cpr, cc = q % cpr, r = tile * kRows + row;
+        const int slot = r < nrows ? slots[r] : -1;
+        if (slot >= 0)
+          buf[i] = 8 * cc < a.D ? *reinterpret_cast<const uint4*>(a.kv + int64_t(slot) * a.kv_row + 8 * cc)
+                                : *reinterpret_cast<const uint4*>(a.kr + int64_t(slot) * a.kr_row + 8 * cc - a.D);
+      }
+    }
+  };
+  auto commit = [&](const uint4 (&buf)[kPer]) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int q = tid + 64 * kWaves * i;
+      if (q < tile_chunks) {
+        const int row = q / cpr, cc = q % cpr;
+        *reinterpret_cast<uint4*>(&kt[row * kPitch + 8 * cc]) = buf[i];
+      }
+    }
+  };
+
+  f32x4 acc[kMaxDT];
+#pragma unroll
+  for (int dt = 0; dt < kMaxDT; ++dt) acc[dt] = f32x4{0, 0, 0, 0};
+  float m[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { m[i] = -INFINITY; l[i] = 0.0f; }
+  const uint16_t* qrow = &qs[(16 * w + c) * kPitch + 8 * g];   // A fragments of S: head c, k 8g..
+  uint16_t* pwr = pw[w];
+
+  auto step = [&](int tile) {
+    // S = Q K^T for the tile's two 16-row halves
+    f32x4 sacc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+#pragma unroll
+    for (int ks = 0; ks < kMaxKS; ++ks) {
+      if (ks < KS) {
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&kt[(16 * j + c) * kPitch + 32 * ks + 8 * g]);
+          sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kb, sacc[j], 0, 0, 0);
+        }
+      }
+    }
+    // sacc[j][i]: head 4g+i of the wave, row 16j + c of the tile
+    bool ok[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = tile * kRows + 16 * j + c;
+      ok[j] = r < nrows && slots[r] >= 0;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float s0 = ok[0] ? sacc[0][i] * a.scale : -INFINITY;
+      const float s1 = ok[1] ? sacc[1][i] * a.scale : -INFINITY;
+      float mx = fmaxf(s0, s1);
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+      const float mn = fmaxf(m[i], mx);
+      const bool none = mn == -INFINITY;
+      const float alpha = none ? 1.0f : __expf(m[i] - mn);
+      const float p0 = none ? 0.0f : __expf(s0 - mn), p1 = none ? 0.0f : __expf(s1 - mn);
+      float ps = p0 + p1;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) ps += __shfl_xor(ps, o, 64);
+      l[i] = l[i] * alpha + ps;
+      m[i] = mn;
+#pragma unroll
+      for (int dt = 0; dt < kMaxDT; ++dt) acc[dt][i] *= alpha;
+      pwr[(4 * g + i) * kPPitch + c] = f2bf(p0);
+      pwr[(4 * g + i) * kPPitch + 16 + c] = f2bf(p1);
+    }
+    // P is read back by other lanes of the wave
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const bf16x8 pa = *reinterpret_cast<const bf16x8*>(&pwr[c * kPPitch + 8 * g]);   // head c, rows 8g..
+    // O += P V: the B fragment (rows 8g..8g+7, column 16dt + c) from two
+    // transposing reads of 4 rows x 4 columns pieces of the row-major tile
+    const int vr = 8 * g + c / 4, vc = 4 * (c % 4);
+    lds_char* kbase = (lds_char*)(kt);
+#pragma unroll
+    for (int dt = 0; dt < kMaxDT; ++dt) {
+      if (dt < DT) {
+        const int o0 = (vr * kPitch + 16 * dt + vc) * 2, o1 = o0 + 4 * kPitch * 2;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(kbase + o0));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(kbase + o1));
+        const v4i16 vv[2] = {lo, hi};
+        bf16x8 vb;
+        __builtin_memcpy(&vb, vv, 16);
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, acc[dt], 0, 0, 0);
+      }
+    }
+  };
+
+  // two tiles' loads in flight ahead of the tile being computed
+  issue(pre[0], 0);
+  issue(pre[1], 1);
+  for (int tile = 0; tile < ntiles; tile += 2) {
+    commit(pre[0]);
+    lds_barrier();
+    issue(pre[0], tile + 2);
+    step(tile);
+    lds_barrier();
+    if (tile + 1 >= ntiles) break;
+    commit(pre[1]);
+    lds_barrier();
+    issue(pre[1], tile + 3);
+    step(tile + 1);
+    lds_barrier();
+  }
+
+  // this split's result, per head row 4g+i of the wave
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = hb * kHeads + 16 * w + 4 * g + i;
+    if (h >= a.N) continue;
+    const float inv = l[i] > 0.0f ? 1.0f / l[i] : 0.0f;
+    if (a.S == 1) {
+      uint16_t* o = a.out + (int64_t(t) * a.N + h) * a.D;
+#pragma unroll
+      for (int dt = 0; dt < kMaxDT; ++dt)
+        if (dt < DT) o[16 * dt + c] = f2bf(acc[dt][i] * inv);
+      if (c == 0) {
+        if (a.smax) a.smax[int64_t(t) * a.N + h] = m[i];
+        if (a.ssum) a.ssum[int64_t(t) * a.N + h] = l[i];
+      }
+    } else {
+      const int64_t row = (int64_t(t) * a.S + s) * a.N + h;
+      float* o = a.part_o + row * a.D;
+#pragma unroll
+      for (int dt = 0; dt < kMaxDT; ++dt)
+        if (dt < DT) o[16 * dt + c] = acc[dt][i] * inv;
+      if (c == 0) { a.part_ml[2 * row] = m[i]; a.part_ml[2 * row + 1] = l[i]; }
+    }
+  }
+}
+
+// Merges the S splits of (token, head) rows: with M = max_s m_s and
+// w_s = l_s exp(m_s - M), out = sum_s w_s o_s / sum_s w_s, softmax_max = M,
+// softmax_sum = sum_s w_s, the splits taken in order.  One wave per row,
+// eight columns per lane.
+__global__ __launch_bounds__(256) void k_sfa_combine(SfaArgs a) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= a.T * a.N) return;
+  const int t = row / a.N, h = row % a.N;
+  float M = -INFINITY;
+  for (int s = 0; s < a.S; ++s) M = fmaxf(M, a.part_ml[2 * ((int64_t(t) * a.S + s) * a.N + h)]);
+  float o[8] = {0, 0, 0, 0, 0, 0, 0, 0}, W = 0.0f;
+  const bool mine = 8 * lane < a.D;   // D is a multiple of 32: whole 8-column pieces
+  if (M != -INFINITY) {
+    for (int s = 0; s < a.S; ++s) {
+      const int64_t pr = (int64_t(t) * a.S + s) * a.N + h;
+      const float ms = a.part_ml[2 * pr], ls = a.part_ml[2 * pr + 1];
+      if (ms == -INFINITY) continue;
+      const float ws = ls * __expf(ms - M);
+      W += ws;
+      if (mine) {
+        const float4* src = reinterpret_cast<const float4*>(a.part_o + pr * a.D + 8 * lane);
+        const float4 u = src[0], v = src[1];
+        o[0] += ws * u.x; o[1] += ws * u.y; o[2] += ws * u.z; o[3] += ws * u.w;
+        o[4] += ws * v.x; o[5] += ws * v.y; o[6] += ws * v.z; o[7] += ws * v.w;
+      }
+    }
+  }
+  const float inv = W > 0.0f ? 1.0f / W : 0.0f;
+  if (mine) {
+    uint32_t pk[4];
+    for (int e = 0; e < 4; ++e)
+      pk[e] = uint32_t(f2bf(o[2 * e] * inv)) | (uint32_t(f2bf(o[2 * e + 1] * inv)) << 16);
+    *reinterpret_cast<uint4*>(a.out + (int64_t(t) * a.N + h) * a.D + 8 * lane) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+  }
+  if (lane == 0) {
+    if (a.smax) a.smax[int64_t(t) * a.N + h] = M;
+    if (a.ssum) a.ssum[int64_t(t) * a.N + h] = W;
+  }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// splits of the selected rows: about one block per CU (one block fills a
+// CU's LDS; at 32 tokens and 128 heads, 4 splits of 512 rows ran 131 us per
+// step against 156 for 8 splits and 224 for 2), at most kMaxRows rows and
+// at least one tile per split
+int splits_for(const mla_sfa_desc& d, int64_t T) {
+  const int64_t R = d.sparse_size * d.sparse_block_size;
+  const int64_t HB = (d.N + kHeads - 1) / kHeads;
+  int64_t S = std::max<int64_t>(1, 256 / std::max<int64_t>(1, T * HB));
+  S = std::min<int64_t>(S, (R + kRows - 1) / kRows);
+  S = std::max<int64_t>(S, (R + kMaxRows - 1) / kMaxRows);
+  return int(S);
+}
+
+int64_t max_splits(const mla_sfa_desc& d) {
+  int64_t best = 1;
+  for (int64_t T = 1; T <= d.max_tokens; T = T < 16 ? T + 1 : T * 2) best = std::max<int64_t>(best, splits_for(d, T));
+  return std::max<int64_t>(best, splits_for(d, d.max_tokens));
+}
+
+mla_status check_desc(const mla_sfa_desc* d) {
+  if (!d) return MLA_ERR_NULLPTR;
+  if (d->N <= 0 || d->D <= 0 || d->Dr <= 0 || d->block_num < 0 || d->block_size <= 0 || d->max_blocks <= 0 ||
+      d->sparse_size <= 0 || d->sparse_block_size <= 0 || d->max_tokens < 0 || d->max_tokens > (1 << 20) ||
+      (d->concat != 0 && d->concat != 1) || !std::isfinite(d->scale))
+    return MLA_ERR_PARAM_INVALID;
+  if (d->D % 32 || d->D > 512 || d->Dr % 32 || d->D + d->Dr > kMaxW || d->N > 128) return MLA_ERR_UNSUPPORTED;
+  if (d->block_num * d->block_size >= (int64_t(1) << 31) || d->max_blocks > (1 << 24) ||
+      d->sparse_size * d->sparse_block_size > (int64_t(1) << 24) || d->block_size > (1 << 20))
+    return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+mla_status check_tensors(const mla_sfa_desc* d, const mla_sfa_tensors* t, int64_t T) {
+  if (T < 0 || T > d->max_tokens) return MLA_ERR_PARAM_INVALID;
+  if (!t) return MLA_ERR_NULLPTR;
+  if (T == 0) return MLA_OK;
+  const void* req[] = {t->query, t->query_rope, t->kv_cache, t->sparse_indices, t->block_table, t->seq_lens_kv,
+                       t->attention_out};
+  for (const void* q : req)
+    if (!q) return MLA_ERR_NULLPTR;
+  for (const void* q : req)
+    if (!aligned16(q)) return MLA_ERR_PARAM_INVALID;
+  if (d->concat ? t->kr_cache != nullptr : t->kr_cache == nullptr)
+    return d->concat ? MLA_ERR_PARAM_INVALID : MLA_ERR_NULLPTR;
+  if (t->kr_cache && !aligned16(t->kr_cache)) return MLA_ERR_PARAM_INVALID;
+  if ((t->softmax_max && (reinterpret_cast<uintptr_t>(t->softmax_max) & 3u)) ||
+      (t->softmax_sum && (reinterpret_cast<uintptr_t>(t->softmax_sum) & 3u)))
+    return MLA_ERR_PARAM_INVALID;
+  return MLA_OK;
+}
+
+}  // namespace
+
+struct mla_sfa {
+  mla_sfa_desc desc;
+  int64_t max_s;
+  float* part_o;
+  float* part_ml;
+};
+
+extern "C" {
+
+mla_status mla_sfa_validate(const mla_sfa_desc* desc, const mla_sfa_tensors* tensors, int64_t T) {
+  mla_status st = check_desc(desc);
+  if (st != MLA_OK || !tensors) return st;
+  return check_tensors(desc, tensors, T);
+}
+
+mla_status mla_sfa_create(const mla_sfa_desc* desc, mla_sfa_t* out) {
+  if (!out) return MLA_ERR_NULLPTR;
+  *out = nullptr;
+  mla_status st = check_desc(desc);
+  if (st != MLA_OK) return st;
+  int prev = 0;
+  if (hipGetDevice(&prev) != hipSuccess) return MLA_ERR_RUNTIME;
+  if (hipSetDevice(desc->device) != hipSuccess) return MLA_ERR_PARAM_INVALID;
+  mla_sfa* h = new (std::nothrow) mla_sfa;
+  if (!h) { (void)hipSetDevice(prev); return MLA_ERR_RUNTIME; }
+  h->desc = *desc;
+  h->max_s = max_splits(*desc);
+  h->part_o = nullptr;
+  h->part_ml = nullptr;
+  const size_t rows = size_t(std::max<int64_t>(1, desc->max_tokens)) * size_t(h->max_s) * size_t(desc->N);
+  if (h->max_s > 1 && (hipMalloc(&h->part_o, rows * desc->D * 4) != hipSuccess ||
+                       hipMalloc(&h->part_ml, rows * 2 * 4) != hipSuccess)) {
+    (void)hipFree(h->part_o);
+    delete h;
+    (void)hipSetDevice(prev);
+    return MLA_ERR_RUNTIME;
+  }
+  (void)hipSetDevice(prev);
+  *out = h;
+  return MLA_OK;
+}
+
+mla_status mla_sfa_run(mla_sfa_t h, const mla_sfa_tensors* t, int64_t T, void* stream) {
+  if (!h) return MLA_ERR_NULLPTR;
+  const mla_sfa_desc& d = h->desc;
+  mla_status st = check_tensors(&d, t, T);
+  if (st != MLA_OK) return st;
+  if (T == 0) return MLA_OK;
+  int prev = 0;
+  if (hipGetDevice(&prev) != hipSuccess) return MLA_ERR_RUNTIME;
+  if (prev != d.device && hipSetDevice(d.device) != hipSuccess) return MLA_ERR_RUNTIME;
+  (void)hipGetLastError();
+  SfaArgs a;
+  a.q = static_cast<const uint16_t*>(t->query);
+  a.qr = static_cast<const uint16_t*>(t->query_rope);
+  a.kv = static_cast<const uint16_t*>(t->kv_cache);
+  a.kv_row = int(d.concat ? d.D + d.Dr : d.D);
+  a.kr = d.concat ? a.kv + d.D : static_cast<const uint16_t*>(t->kr_cache);
+  a.kr_row = int(d.concat ? d.D + d.Dr : d.Dr);
+  a.idx = t->sparse_indices;
+  a.table = t->block_table;
+  a.lens = t->seq_lens_kv;
+  a.out = static_cast<uint16_t*>(t->attention_out);
+  a.smax = t->softmax_max;
+  a.ssum = t->softmax_sum;
+  a.part_o = h->part_o;
+  a.part_ml = h->part_ml;
+  a.T = int(T); a.N = int(d.N); a.D = int(d.D); a.Dr = int(d.Dr); a.bs = int(d.block_size);
+  a.max_blocks = int(d.max_blocks); a.K = int(d.sparse_size); a.sbs = int(d.sparse_block_size);
+  a.block_num = int(d.block_num);
+  a.scale = float(d.scale);
+  const int64_t R = d.sparse_size * d.sparse_block_size;
+  a.S = splits_for(d, T);
+  a.rows_per_split = int((R + a.S - 1) / a.S);
+  const int HB = int((d.N + kHeads - 1) / kHeads);
+  const int64_t flats = T * a.S;
+  const dim3 grid(unsigned(((flats + 7) / 8) * 8 * HB));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  k_sfa<<<grid, 64 * kWaves, 0, s>>>(a);
+  if (a.S > 1) k_sfa_combine<<<dim3(unsigned((T * d.N + 3) / 4)), 256, 0, s>>>(a);
+  const hipError_t e = hipGetLastError();
+  if (prev != d.device) (void)hipSetDevice(prev);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_RUNTIME;
+}
+
+mla_status mla_sfa_destroy(mla_sfa_t h) {
+  if (!h) return MLA_ERR_NULLPTR;
+  int prev = 0;
+  mla_status st = MLA_OK;
+  if (hipGetDevice(&prev) != hipSuccess) st = MLA_ERR_RUNTIME;
+  if (st == MLA_OK && hipSetDevice(h->desc.device) == hipSuccess) {
+    if (hipDeviceSynchronize() != hipSuccess) st = MLA_ERR_RUNTIME;
+    if (h->part_o && hipFree(h->part_o) != hipSuccess) st = MLA_ERR_RUNTIME;
+    if (h->part_ml && hipFree(h->part_ml) != hipSuccess) st = MLA_ERR_RUNTIME;
+    (void)hipSetDevice(prev);
+  }
+  delete h;
+  return st;
+}
+
+}  // extern "C"

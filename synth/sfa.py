@@ -45,7 +45,7 @@ class SfaWorkload:
 
 
 SFA_WORKLOADS: Dict[str, SfaWorkload] = {
-    "sfa_tiny_t3": SfaWorkload("sfa_tiny_t3", 3, 2, 32, 16, 16, 8, 1, 20, 60, 20300),
+    "sfa_tiny_t3": SfaWorkload("sfa_tiny_t3", 3, 2, 32, 32, 16, 8, 1, 20, 60, 20300),
     # decode at the model's head count and widths: 2048 selected tokens
     "sfa_decode_t32": SfaWorkload("sfa_decode_t32", 32, 128, 512, 64, 128, 2048, 1, 12288, 20480, 20301),
 }

@@ -13,8 +13,12 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def header_functions():
-    text = open(os.path.join(ROOT, "include", "mla_prolog.h")).read()
-    return sorted(set(re.findall(r"^\w[\w\s\*]*?\b(mla_prolog_\w+)\s*\(", text, re.M)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", h)).read()
+            names |= set(re.findall(r"^\w[\w\s\*]*?\b(mla_\w+)\s*\(", text, re.M))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol():
@@ -215,3 +219,57 @@ def test_no_cache_blocks_needs_no_caches():
 def test_status_strings():
     for code in (0, 161001, 161002, 361001, 561002):
         assert mla.status_string(code) != "unknown status"
+
+
+# ---- sparse flash attention over the caches --------------------------------
+def sfa_desc(**kw):
+    a = dict(N=128, D=512, Dr=64, block_num=4096, block_size=128, max_blocks=256, sparse_size=2048,
+             sparse_block_size=1, max_tokens=32, scale=1 / 24)
+    a.update(kw)
+    return mla.make_sfa_desc(**a)
+
+
+def sfa_tensors(concat=False, lse=True):
+    t = {f: FAKE for f in mla.SFA_TENSOR_FIELDS}
+    if concat:
+        t["kr_cache"] = None
+    if not lse:
+        t["softmax_max"] = t["softmax_sum"] = None
+    return t
+
+
+def test_sfa_valid():
+    assert mla.sfa_validate(sfa_desc()) == mla.MLA_OK
+    assert mla.sfa_validate(sfa_desc(), sfa_tensors(), 32) == mla.MLA_OK
+    assert mla.sfa_validate(sfa_desc(concat=1), sfa_tensors(concat=True, lse=False), 32) == mla.MLA_OK
+    assert mla.sfa_validate(sfa_desc(N=3, D=64, Dr=32, sparse_block_size=4), sfa_tensors(), 1) == mla.MLA_OK
+    assert mla.sfa_validate(sfa_desc(), {}, 0) == mla.MLA_OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=0), mla.MLA_ERR_PARAM_INVALID),
+    (dict(block_size=0), mla.MLA_ERR_PARAM_INVALID),
+    (dict(sparse_size=0), mla.MLA_ERR_PARAM_INVALID),
+    (dict(concat=2), mla.MLA_ERR_PARAM_INVALID),
+    (dict(scale=float("nan")), mla.MLA_ERR_PARAM_INVALID),
+    (dict(D=520), mla.MLA_ERR_UNSUPPORTED),
+    (dict(D=48), mla.MLA_ERR_UNSUPPORTED),
+    (dict(Dr=16), mla.MLA_ERR_UNSUPPORTED),
+    (dict(Dr=96), mla.MLA_ERR_UNSUPPORTED),
+    (dict(N=129), mla.MLA_ERR_UNSUPPORTED),
+    (dict(block_num=1 << 24, block_size=1024), mla.MLA_ERR_UNSUPPORTED),
+])
+def test_sfa_bad_descriptions(kw, code):
+    assert mla.sfa_validate(sfa_desc(**kw)) == code
+
+
+def test_sfa_bad_run_arguments():
+    d = sfa_desc()
+    assert mla.sfa_validate(d, sfa_tensors(), 33) == mla.MLA_ERR_PARAM_INVALID
+    for f in ("query", "query_rope", "kv_cache", "kr_cache", "sparse_indices", "block_table", "seq_lens_kv",
+              "attention_out"):
+        t = sfa_tensors(); t[f] = None
+        assert mla.sfa_validate(d, t, 8) == mla.MLA_ERR_NULLPTR, f
+    t = sfa_tensors(); t["query"] = FAKE + 8
+    assert mla.sfa_validate(d, t, 8) == mla.MLA_ERR_PARAM_INVALID
+    assert mla.sfa_validate(sfa_desc(concat=1), sfa_tensors(), 8) == mla.MLA_ERR_PARAM_INVALID   # kr given
