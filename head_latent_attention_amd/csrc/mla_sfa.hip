@@ -7,14 +7,17 @@
 //   out[t, h] = sum_j softmax(s)_j c^KV_j   (value = key = c^KV).
 //
 // k_sfa: one block per (token, split of the selected rows, group of 64
-// heads); four waves of 16 heads.  The block's heads' queries sit in LDS;
-// 32 selected cache rows at a time are gathered into an LDS tile (the next
-// two tiles' loads in flight in registers), then each wave takes
-// S = Q K^T on MFMA (B fragments are 16-byte row reads of the tile), an
-// online softmax per head row, and O += P V on MFMA, with P through a small
-// per-wave LDS tile and the V fragments read from the same row-major tile
-// by transposing LDS reads (ds_read_b64_tr_b16: lane i of each 16-lane
-// group receives element i%4 of the 8-byte pieces read by lanes 4e + i/4).
+// heads); eight waves, two per 16 heads, each wave owning half of the
+// output columns (so that a wave's registers hold its heads' queries and
+// two waves share each SIMD).  32 selected cache rows at a time are
+// gathered into an LDS tile (the next tile's loads in flight in
+// registers); each wave takes S = Q K^T on MFMA (queries as A fragments in
+// registers, B fragments 16-byte row reads of the tile), the online softmax
+// of its heads (both waves of a head group compute the same), and its half
+// of O += P V on MFMA, with P through a small per-wave LDS tile and the V
+// fragments read from the same row-major tile by transposing LDS reads
+// (ds_read_b64_tr_b16: lane i of each 16-lane group receives element i%4 of
+// the 8-byte pieces read by lanes 4e + i/4).
 // With more than one split, k_sfa_combine merges the splits' normalised
 // partial outputs by their (max, sum) pairs in split order.  No atomics: a
 // run is deterministic.
@@ -36,13 +39,13 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) char lds_char;
 
-constexpr int kWaves = 4;             // waves per block, 16 heads each
-constexpr int kHeads = 16 * kWaves;   // heads per block
+constexpr int kWaves = 8;             // waves per block: 4 groups of 16 heads x 2 column halves
+constexpr int kHeads = 64;            // heads per block
 constexpr int kRows = 32;             // cache rows per tile
 constexpr int kMaxW = 576;            // D + Dr at most
 constexpr int kPitch = kMaxW + 8;     // LDS row pitch (bf16): rows 4 banks apart
 constexpr int kMaxKS = kMaxW / 32;    // MFMA k-steps of S = Q K^T
-constexpr int kMaxDT = 512 / 16;      // 16-column tiles of O
+constexpr int kMaxDT = 512 / 16 / 2;  // 16-column tiles of O per wave (half of the columns)
 constexpr int kPer = (kRows * (kMaxW / 8) + 64 * kWaves - 1) / (64 * kWaves);  // 16-byte loads per thread per tile
 constexpr int kMaxRows = 2048;        // selected rows of one block
 constexpr int kPPitch = kRows + 8;    // per-wave P tile pitch (bf16)
@@ -61,6 +64,31 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Max and sum over each 16-lane row of the wave with DPP moves (quad
+// permutations, then the half-row and row mirrors); every lane of the row
+// ends with the result.  Cross-lane shuffles through the LDS crossbar would
+// put four round trips per reduction on the tile loop's critical path.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadSwap1 = 0xB1;     // quad_perm [1, 0, 3, 2]
+constexpr int kQuadSwap2 = 0x4E;     // quad_perm [2, 3, 0, 1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp<kQuadSwap1>(v));
+  v = fmaxf(v, dpp<kQuadSwap2>(v));
+  v = fmaxf(v, dpp<kRowHalfMirror>(v));
+  return fmaxf(v, dpp<kRowMirror>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<kQuadSwap1>(v);
+  v += dpp<kQuadSwap2>(v);
+  v += dpp<kRowHalfMirror>(v);
+  return v + dpp<kRowMirror>(v);
 }
 
 struct SfaArgs {
@@ -82,11 +110,11 @@ struct SfaArgs {
 };
 
 __global__ __launch_bounds__(64 * kWaves) void k_sfa(SfaArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t qs[kHeads * kPitch];
   __shared__ __attribute__((aligned(16))) uint16_t kt[kRows * kPitch];
   __shared__ __attribute__((aligned(16))) uint16_t pw[kWaves][16 * kPPitch];
   __shared__ int32_t slots[kMaxRows];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c = lane & 15;
+  const int hg = w % 4, dh = w / 4;   // head group of 16 and column half of this wave
   // block -> (token, split) and head group: the head groups of one (token,
   // split) are 8 blocks apart, so they run on the same XCD and share its L2
   const int HB = (a.N + kHeads - 1) / kHeads;
@@ -95,7 +123,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_sfa(SfaArgs a) {
   const int hb = (b / 8) % HB;
   if (flat >= a.T * a.S) return;
   const int t = flat / a.S, s = flat % a.S;
-  const int W = a.D + a.Dr, cpr = W / 8, KS = W / 32, DT = a.D / 16;
+  const int W = a.D + a.Dr, cpr = W / 8;
   const int tile_chunks = kRows * cpr;
 
   // the selected slots of this split (-1: nothing)
@@ -115,19 +143,32 @@ __global__ __launch_bounds__(64 * kWaves) void k_sfa(SfaArgs a) {
     }
     slots[r] = slot;
   }
-  // the block's queries, [q^N | q^R] per head row (zeros past N)
-  for (int q = tid; q < kHeads * cpr; q += 64 * kWaves) {
-    const int hr = q / cpr, cc = q % cpr, h = hb * kHeads + hr;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (h < a.N)
-      v = 8 * cc < a.D ? *reinterpret_cast<const uint4*>(a.q + (int64_t(t) * a.N + h) * a.D + 8 * cc)
-                       : *reinterpret_cast<const uint4*>(a.qr + (int64_t(t) * a.N + h) * a.Dr + 8 * cc - a.D);
-    *reinterpret_cast<uint4*>(&qs[hr * kPitch + 8 * cc]) = v;
+  // the tile's columns from D + Dr to the widest row stay zero (as do the
+  // queries'), so the MFMA loops below run over the widest row with no
+  // branches (a branch around each step keeps the LDS reads from overlapping)
+  for (int q = tid; q < kRows * (kMaxW / 8 - cpr); q += 64 * kWaves) {
+    const int n = kMaxW / 8 - cpr, r = q / n, cc = cpr + q % n;
+    *reinterpret_cast<uint4*>(&kt[r * kPitch + 8 * cc]) = make_uint4(0, 0, 0, 0);
+  }
+  // this wave's A fragments of S: head 16hg + c, columns 32ks + 8g .. +7 of
+  // [q^N | q^R] (zeros past N and past D + Dr)
+  bf16x8 qa[kMaxKS];
+  {
+    const int h = hb * kHeads + 16 * hg + c;
+#pragma unroll
+    for (int ks = 0; ks < kMaxKS; ++ks) {
+      const int k0 = 32 * ks + 8 * g;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (h < a.N && k0 < W)
+        v = k0 < a.D ? *reinterpret_cast<const uint4*>(a.q + (int64_t(t) * a.N + h) * a.D + k0)
+                     : *reinterpret_cast<const uint4*>(a.qr + (int64_t(t) * a.N + h) * a.Dr + k0 - a.D);
+      __builtin_memcpy(&qa[ks], &v, 16);
+    }
   }
   __syncthreads();
 
   const int ntiles = (nrows + kRows - 1) / kRows;
-  uint4 pre[2][kPer];
+  uint4 pre[1][kPer];
   // loads of tile `tile` into register set `set`; rows without a slot read as zeros
   auto issue = [&](uint4 (&buf)[kPer], int tile) {
 #pragma unroll
@@ -160,7 +201,6 @@ __global__ __launch_bounds__(64 * kWaves) void k_sfa(SfaArgs a) {
   float m[4], l[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) { m[i] = -INFINITY; l[i] = 0.0f; }
-  const uint16_t* qrow = &qs[(16 * w + c) * kPitch + 8 * g];   // A fragments of S: head c, k 8g..
   uint16_t* pwr = pw[w];
 
   auto step = [&](int tile) {
@@ -168,13 +208,10 @@ __global__ __launch_bounds__(64 * kWaves) void k_sfa(SfaArgs a) {
     f32x4 sacc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
 #pragma unroll
     for (int ks = 0; ks < kMaxKS; ++ks) {
-      if (ks < KS) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&kt[(16 * j + c) * kPitch + 32 * ks + 8 * g]);
-          sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kb, sacc[j], 0, 0, 0);
-        }
+      for (int j = 0; j < 2; ++j) {
+        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&kt[(16 * j + c) * kPitch + 32 * ks + 8 * g]);
+        sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb, sacc[j], 0, 0, 0);
       }
     }
     // sacc[j][i]: head 4g+i of the wave, row 16j + c of the tile
@@ -188,16 +225,12 @@ __global__ __launch_bounds__(64 * kWaves) void k_sfa(SfaArgs a) {
     for (int i = 0; i < 4; ++i) {
       const float s0 = ok[0] ? sacc[0][i] * a.scale : -INFINITY;
       const float s1 = ok[1] ? sacc[1][i] * a.scale : -INFINITY;
-      float mx = fmaxf(s0, s1);
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+      const float mx = row16_max(fmaxf(s0, s1));
       const float mn = fmaxf(m[i], mx);
       const bool none = mn == -INFINITY;
       const float alpha = none ? 1.0f : __expf(m[i] - mn);
       const float p0 = none ? 0.0f : __expf(s0 - mn), p1 = none ? 0.0f : __expf(s1 - mn);
-      float ps = p0 + p1;
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) ps += __shfl_xor(ps, o, 64);
+      const float ps = row16_sum(p0 + p1);
       l[i] = l[i] * alpha + ps;
       m[i] = mn;
 #pragma unroll
@@ -210,63 +243,56 @@ __global__ __launch_bounds__(64 * kWaves) void k_sfa(SfaArgs a) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const bf16x8 pa = *reinterpret_cast<const bf16x8*>(&pwr[c * kPPitch + 8 * g]);   // head c, rows 8g..
-    // O += P V: the B fragment (rows 8g..8g+7, column 16dt + c) from two
-    // transposing reads of 4 rows x 4 columns pieces of the row-major tile
-    const int vr = 8 * g + c / 4, vc = 4 * (c % 4);
+    // O += P V over this wave's column half: the B fragment (rows 8g..8g+7,
+    // column 256dh + 16dt + c) from two transposing reads of 4 rows x 4
+    // columns pieces of the row-major tile
+    const int vr = 8 * g + c / 4, vc = 256 * dh + 4 * (c % 4);
     lds_char* kbase = (lds_char*)(kt);
+    // (columns past D land in tiles that are never stored)
 #pragma unroll
     for (int dt = 0; dt < kMaxDT; ++dt) {
-      if (dt < DT) {
-        const int o0 = (vr * kPitch + 16 * dt + vc) * 2, o1 = o0 + 4 * kPitch * 2;
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(kbase + o0));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(kbase + o1));
-        const v4i16 vv[2] = {lo, hi};
-        bf16x8 vb;
-        __builtin_memcpy(&vb, vv, 16);
-        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, acc[dt], 0, 0, 0);
-      }
+      const int o0 = (vr * kPitch + 16 * dt + vc) * 2, o1 = o0 + 4 * kPitch * 2;
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(kbase + o0));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(kbase + o1));
+      const v4i16 vv[2] = {lo, hi};
+      bf16x8 vb;
+      __builtin_memcpy(&vb, vv, 16);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, acc[dt], 0, 0, 0);
     }
   };
 
-  // two tiles' loads in flight ahead of the tile being computed
+  // the next tile's loads in flight while a tile is computed
   issue(pre[0], 0);
-  issue(pre[1], 1);
-  for (int tile = 0; tile < ntiles; tile += 2) {
+  for (int tile = 0; tile < ntiles; ++tile) {
     commit(pre[0]);
     lds_barrier();
-    issue(pre[0], tile + 2);
+    issue(pre[0], tile + 1);
     step(tile);
-    lds_barrier();
-    if (tile + 1 >= ntiles) break;
-    commit(pre[1]);
-    lds_barrier();
-    issue(pre[1], tile + 3);
-    step(tile + 1);
     lds_barrier();
   }
 
-  // this split's result, per head row 4g+i of the wave
+  // this split's result, per head row 4g+i of the wave, its column half
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int h = hb * kHeads + 16 * w + 4 * g + i;
+    const int h = hb * kHeads + 16 * hg + 4 * g + i;
     if (h >= a.N) continue;
     const float inv = l[i] > 0.0f ? 1.0f / l[i] : 0.0f;
     if (a.S == 1) {
-      uint16_t* o = a.out + (int64_t(t) * a.N + h) * a.D;
+      uint16_t* o = a.out + (int64_t(t) * a.N + h) * a.D + 256 * dh;
 #pragma unroll
       for (int dt = 0; dt < kMaxDT; ++dt)
-        if (dt < DT) o[16 * dt + c] = f2bf(acc[dt][i] * inv);
-      if (c == 0) {
+        if (256 * dh + 16 * dt < a.D) o[16 * dt + c] = f2bf(acc[dt][i] * inv);
+      if (c == 0 && dh == 0) {
         if (a.smax) a.smax[int64_t(t) * a.N + h] = m[i];
         if (a.ssum) a.ssum[int64_t(t) * a.N + h] = l[i];
       }
     } else {
       const int64_t row = (int64_t(t) * a.S + s) * a.N + h;
-      float* o = a.part_o + row * a.D;
+      float* o = a.part_o + row * a.D + 256 * dh;
 #pragma unroll
       for (int dt = 0; dt < kMaxDT; ++dt)
-        if (dt < DT) o[16 * dt + c] = acc[dt][i] * inv;
-      if (c == 0) { a.part_ml[2 * row] = m[i]; a.part_ml[2 * row + 1] = l[i]; }
+        if (256 * dh + 16 * dt < a.D) o[16 * dt + c] = acc[dt][i] * inv;
+      if (c == 0 && dh == 0) { a.part_ml[2 * row] = m[i]; a.part_ml[2 * row + 1] = l[i]; }
     }
   }
 }
