@@ -57,7 +57,8 @@ def weighted_abs(inp, rows):
 
 def bf16(bits):
     b = np.asarray(bits, np.uint16).astype(np.uint32) << np.uint32(16)
-    return b.view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):   # unwritten cache slots hold a NaN sentinel
+        return b.view(np.float32).astype(np.float64)
 
 
 def run_gpu(inp, lse=True, repeat=1, T=None):
@@ -166,3 +167,34 @@ def test_model_concatenated_t4():
     wl = replace(sfa_workload("sfa_decode_t32"), name="sfa_decode_t4_concat", T=4, concat=True, len_lo=2500,
                  len_hi=5000)
     check(make_sfa_inputs(wl))
+
+
+def test_consumes_the_prolog_caches():
+    """The prolog writes two sequences' rows into the paged caches; the
+    attention then reads them back through block tables rebuilt from the
+    prolog's cacheIndex, with the prolog's own queries of each sequence's
+    last token.  The oracle runs on host copies of the same device data."""
+    from synth.generate import Dims, custom_workload
+    import synth
+    L, bs = 64, 16
+    wl = custom_workload("prolog_for_sfa", T=2 * L, dims=Dims(He=256, Hcq=64, Hckv=64, N=4, D=32, Dr=32),
+                         block_num=16, block_size=bs, seed=61, positions=f"prefill:2x{L}")
+    pin = synth.make_inputs(wl)
+    say("case the prolog's caches and queries read by the attention")
+    t = dev.upload(pin)
+    with mla.MlaProlog(mla.make_desc(**dev.desc_args(pin))) as h:
+        h.run(t, 2 * L)
+        torch.cuda.synchronize()
+    d = pin["dims"]
+    last = [L - 1, 2 * L - 1]
+    idx = np.asarray(pin["cache_index"])
+    table = np.stack([idx[s * L:(s + 1) * L:bs] // bs for s in range(2)]).astype(np.int32)
+    rng = np.random.default_rng(5)
+    inp = {"workload": "prolog_for_sfa", "T": 2, "N": d.N, "D": d.Hckv, "Dr": d.Dr, "block_size": bs, "K": 40,
+           "sparse_block_size": 1, "concat": False, "scale": 1.0 / np.sqrt(d.Hckv + d.Dr),
+           "seq_lens": np.array([L, L], np.int32), "block_table": table, "max_blocks": table.shape[1],
+           "block_num": int(pin["block_num"]),
+           "indices": np.stack([rng.permutation(L)[:40] for _ in range(2)]).astype(np.int32),
+           "query": dev.bits(t["query_out"])[last], "query_rope": dev.bits(t["query_rope_out"])[last],
+           "kv_cache": dev.bits(t["kv_cache"]), "kr_cache": dev.bits(t["kr_cache"])}
+    check(inp)
