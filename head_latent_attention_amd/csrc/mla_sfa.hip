@@ -46,7 +46,7 @@ constexpr int kMaxW = 576;            // D + Dr at most
 constexpr int kPitch = kMaxW + 8;     // LDS row pitch (bf16): rows 4 banks apart
 constexpr int kMaxKS = kMaxW / 32;    // MFMA k-steps of S = Q K^T
 constexpr int kMaxDT = 512 / 16 / 2;  // 16-column tiles of O per wave (half of the columns)
-constexpr int kPer = (kRows * (kMaxW / 8) + 64 * kWaves - 1) / (64 * kWaves);  // 16-byte loads per thread per tile
+constexpr int kPer = 5;               // 16-byte loads per thread per tile: 32 rows in passes of >= 7 rows
 constexpr int kMaxRows = 2048;        // selected rows of one block
 constexpr int kPPitch = kRows + 8;    // per-wave P tile pitch (bf16)
 
@@ -124,7 +124,6 @@ __global__ __launch_bounds__(64 * kWaves) void k_sfa(SfaArgs a) {
   if (flat >= a.T * a.S) return;
   const int t = flat / a.S, s = flat % a.S;
   const int W = a.D + a.Dr, cpr = W / 8;
-  const int tile_chunks = kRows * cpr;
 
   // the selected slots of this split (-1: nothing)
   const int R = a.K * a.sbs;
@@ -169,29 +168,29 @@ __global__ __launch_bounds__(64 * kWaves) void k_sfa(SfaArgs a) {
 
   const int ntiles = (nrows + kRows - 1) / kRows;
   uint4 pre[1][kPer];
-  // loads of tile `tile` into register set `set`; rows without a slot read as zeros
+  // thread -> (16-byte column cc of a row, first row rbase); rows rbase +
+  // rstep*i, so the per-tile addressing has no division
+  const int rstep = (64 * kWaves) / cpr, cc = tid % cpr, rbase = tid / cpr;
+  const bool mover = rbase < rstep;
+  const uint16_t* src = 8 * cc < a.D ? a.kv + 8 * cc : a.kr + (8 * cc - a.D);
+  const int src_row = 8 * cc < a.D ? a.kv_row : a.kr_row;
+  // loads of tile `tile`; rows without a slot read as zeros
   auto issue = [&](uint4 (&buf)[kPer], int tile) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int q = tid + 64 * kWaves * i;
+      const int row = rbase + rstep * i, r = tile * kRows + row;
       buf[i] = make_uint4(0, 0, 0, 0);
-      if (tile < ntiles && q < tile_chunks) {
-        const int row = q / cpr, cc = q % cpr, r = tile * kRows + row;
+      if (mover && row < kRows && tile < ntiles) {
         const int slot = r < nrows ? slots[r] : -1;
-        if (slot >= 0)
-          buf[i] = 8 * cc < a.D ? *reinterpret_cast<const uint4*>(a.kv + int64_t(slot) * a.kv_row + 8 * cc)
-                                : *reinterpret_cast<const uint4*>(a.kr + int64_t(slot) * a.kr_row + 8 * cc - a.D);
+        if (slot >= 0) buf[i] = *reinterpret_cast<const uint4*>(src + int64_t(slot) * src_row);
       }
     }
   };
   auto commit = [&](const uint4 (&buf)[kPer]) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int q = tid + 64 * kWaves * i;
-      if (q < tile_chunks) {
-        const int row = q / cpr, cc = q % cpr;
-        *reinterpret_cast<uint4*>(&kt[row * kPitch + 8 * cc]) = buf[i];
-      }
+      const int row = rbase + rstep * i;
+      if (mover && row < kRows) *reinterpret_cast<uint4*>(&kt[row * kPitch + 8 * cc]) = buf[i];
     }
   };
 
