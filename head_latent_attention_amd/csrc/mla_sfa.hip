@@ -220,6 +220,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_sfa(SfaArgs a) {
       const int r = tile * kRows + 16 * j + c;
       ok[j] = r < nrows && slots[r] >= 0;
     }
+    float alpha[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float s0 = ok[0] ? sacc[0][i] * a.scale : -INFINITY;
@@ -227,15 +228,21 @@ __global__ __launch_bounds__(64 * kWaves) void k_sfa(SfaArgs a) {
       const float mx = row16_max(fmaxf(s0, s1));
       const float mn = fmaxf(m[i], mx);
       const bool none = mn == -INFINITY;
-      const float alpha = none ? 1.0f : __expf(m[i] - mn);
+      alpha[i] = none ? 1.0f : __expf(m[i] - mn);
       const float p0 = none ? 0.0f : __expf(s0 - mn), p1 = none ? 0.0f : __expf(s1 - mn);
       const float ps = row16_sum(p0 + p1);
-      l[i] = l[i] * alpha + ps;
+      l[i] = l[i] * alpha[i] + ps;
       m[i] = mn;
+      pwr[(4 * g + i) * kPPitch + c] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(p0));
+      pwr[(4 * g + i) * kPPitch + 16 + c] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(p1));
+    }
+    // rescale O only when a running max of the wave moved (once the maxima
+    // settle, most tiles leave them alone)
+    if (__any(alpha[0] != 1.0f || alpha[1] != 1.0f || alpha[2] != 1.0f || alpha[3] != 1.0f)) {
 #pragma unroll
-      for (int dt = 0; dt < kMaxDT; ++dt) acc[dt][i] *= alpha;
-      pwr[(4 * g + i) * kPPitch + c] = f2bf(p0);
-      pwr[(4 * g + i) * kPPitch + 16 + c] = f2bf(p1);
+      for (int dt = 0; dt < kMaxDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[dt][i] *= alpha[i];
     }
     // P is read back by other lanes of the wave
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
