@@ -651,3 +651,52 @@ def test_full_size_concat_decode_packed():
     from dataclasses import replace
     wl = replace(synth.workload("decode_t32"), name="decode_t32_concat", concat=True, weight_nk=True)
     full_check(synth.make_inputs(wl), rows=sample_rows(32, k=6), packed=True)
+
+
+@pytest.mark.parametrize("name", ["pre_t37", "cat_t32_pair"])
+def test_concat_out_of_range_slots_are_skipped(name):
+    # the concatenated rows are written whole or not at all
+    wl = STATIC.get(name) or CONCAT_BF16[name]
+    inp = synth.make_inputs(wl)
+    n = inp["block_num"] * inp["block_size"]
+    idx = np.array(inp["cache_index"])
+    idx[:3] = [-1, n, n + 77]
+    inp["cache_index"] = idx
+    full_check(inp, packed=True)
+
+
+def test_static_no_cache_blocks_still_computes_queries():
+    inp = synth.make_inputs(STATIC["pre_t37"])
+    say("case static, concatenated, block_num=0")
+    t = dev.upload(inp)
+    t.pop("kv_cache")
+    args = dev.desc_args(inp)
+    args["block_num"] = 0
+    desc = mla.make_desc(**args)
+    with mla.MlaProlog(desc) as h:
+        buf = torch.empty(mla.packed_weights_bytes(desc), dtype=torch.uint8, device="cuda")
+        h.pack_weights(t, buf)
+        t["packed_weights"] = buf
+        h.run(t, int(inp["T"]))
+        torch.cuda.synchronize()
+    ref = split_concat(inp, oracle.run(inp, caches=False))
+    got = split_concat(inp, {"query_out": dev.bits(t["query_out"])})
+    check_queries(got, ref, np.arange(int(inp["T"])), False)
+
+
+def test_static_smaller_run_than_max_tokens():
+    say("case static T=23 of max 130")
+    small = synth.make_inputs(STATIC["pre_t130"], T=23)
+    d = small["dims"]
+    t = dev.upload(small)
+    desc = mla.make_desc(**dev.desc_args(small, max_tokens=130))
+    with mla.MlaProlog(desc) as h:
+        buf = torch.empty(mla.packed_weights_bytes(desc), dtype=torch.uint8, device="cuda")
+        h.pack_weights(t, buf)
+        t["packed_weights"] = buf
+        h.run(t, 23)
+        torch.cuda.synchronize()
+    got = split_concat(small, {k: dev.bits(v) for k, v in t.items() if k in ("query_out", "kv_cache")})
+    ref = split_concat(small, oracle.run(small, caches=False))
+    check_queries(got, ref, np.arange(23), False)
+    check_caches(split_concat(small, small), got["kv_cache"], got["kr_cache"], ref, np.arange(23))

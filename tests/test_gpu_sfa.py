@@ -198,3 +198,32 @@ def test_consumes_the_prolog_caches():
            "query": dev.bits(t["query_out"])[last], "query_rope": dev.bits(t["query_rope_out"])[last],
            "kv_cache": dev.bits(t["kv_cache"]), "kr_cache": dev.bits(t["kr_cache"])}
     check(inp)
+
+
+def test_smaller_run_than_max_tokens():
+    # the handle's split workspace is sized for 40 tokens; a run of 7 uses the
+    # first tokens' rows only
+    inp = make_sfa_inputs(SMALL["ragged_t5"])
+    wl = replace(SMALL["ragged_t5"], T=40)
+    big = make_sfa_inputs(wl)
+    say("case sparse attention T=7 of max 40")
+    t = {"query": big["query"], "query_rope": big["query_rope"], "kv_cache": big["kv_cache"],
+         "kr_cache": big["kr_cache"], "sparse_indices": big["indices"], "block_table": big["block_table"],
+         "seq_lens_kv": big["seq_lens"]}
+    g = {k: dev._tensor(np.asarray(v), "cuda:0") for k, v in t.items()}
+    N, D = int(big["N"]), int(big["D"])
+    g["attention_out"] = torch.zeros((40, N, D), dtype=torch.bfloat16, device="cuda:0")
+    desc = mla.make_sfa_desc(N=N, D=D, Dr=int(big["Dr"]), block_num=int(big["block_num"]),
+                             block_size=int(big["block_size"]), max_blocks=int(big["max_blocks"]),
+                             sparse_size=int(big["K"]), sparse_block_size=1, max_tokens=40,
+                             scale=float(big["scale"]))
+    with mla.MlaSfa(desc) as h:
+        h.run(g, 7)
+        torch.cuda.synchronize()
+    out = dev.bits(g["attention_out"])
+    ref = oracle.sfa(big, tokens=list(range(7)))
+    g7, r7 = bf16(out[:7]), bf16(ref["attention_out"])
+    tol = 2.0 ** -8 * (weighted_abs(big, list(range(7))) + np.abs(r7)) + 1e-6
+    assert np.all(np.abs(g7 - r7) <= tol)
+    assert not out[7:].any(), "rows past T were written"
+    del inp
