@@ -345,10 +345,10 @@ __global__ __launch_bounds__(256) void k_sfa_combine(SfaArgs a) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// splits of the selected rows: about one block per CU (one block fills a
-// CU's LDS; at 32 tokens and 128 heads, 4 splits of 512 rows ran 131 us per
-// step against 156 for 8 splits and 224 for 2), at most kMaxRows rows and
-// at least one tile per split
+// splits of the selected rows: about one block per CU (a block's eight
+// waves at up to 256 VGPRs fill a CU; at 32 tokens and 128 heads, 4 splits
+// of 512 rows ran 80 us per step against 96 for 8 splits and 122 for 2), at
+// most kMaxRows rows and at least one tile per split
 int splits_for(const mla_sfa_desc& d, int64_t T) {
   const int64_t R = d.sparse_size * d.sparse_block_size;
   const int64_t HB = (d.N + kHeads - 1) / kHeads;
