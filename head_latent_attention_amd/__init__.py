@@ -19,7 +19,10 @@ ROOT = os.path.dirname(HERE)
 SOURCE = os.path.join(HERE, "csrc", "mla_prolog.hip")
 #: every HIP source of the library: the prolog and its cache consumer
 SOURCES = (SOURCE, os.path.join(HERE, "csrc", "mla_sfa.hip"))
-LIBRARY = os.path.join(HERE, "libmla_prolog.so")
+#: the built library; MLA_PROLOG_LIBRARY names another build of the same
+#: sources (the sanitizer test builds one whose host code carries AddressSanitizer
+#: and UBSan)
+LIBRARY = os.environ.get("MLA_PROLOG_LIBRARY") or os.path.join(HERE, "libmla_prolog.so")
 # MFMA accumulators in VGPRs: with the default AGPR form the register
 # allocator rotates the accumulators of the software-pipelined loops through
 # copies on every iteration.
@@ -41,7 +44,8 @@ MLA_INT8_STATIC = 3    # in_dtype only: the preprocess page's static int8 scenar
 EXPORTS = ("mla_prolog_validate", "mla_prolog_workspace_bytes", "mla_prolog_packed_weights_bytes",
            "mla_prolog_pack_weights", "mla_prolog_create",
            "mla_prolog_run", "mla_prolog_destroy", "mla_prolog_profile_enable",
-           "mla_prolog_profile_read", "mla_prolog_check", "mla_prolog_status_string",
+           "mla_prolog_profile_read", "mla_prolog_check", "mla_prolog_set_poll_limit",
+           "mla_prolog_status_string",
            "mla_sfa_validate", "mla_sfa_create", "mla_sfa_run", "mla_sfa_destroy")
 #: kernel order of mla_prolog_profile_read
 KERNELS = ("down_proj", "norm_rope_cache", "up_proj", "uk")
@@ -63,7 +67,7 @@ class Desc(ctypes.Structure):
                 ("in_dtype", ctypes.c_int32), ("query_dtype", ctypes.c_int32),
                 ("device", ctypes.c_int32), ("cache_dtype", ctypes.c_int32),
                 ("concat", ctypes.c_int32), ("weights_nk", ctypes.c_int32),
-                ("x_quant_only", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("x_quant_only", ctypes.c_int32), ("check_index", ctypes.c_int32),
                 ("eps_x", ctypes.c_double)]
 
 
@@ -119,6 +123,8 @@ def lib() -> ctypes.CDLL:
         L.mla_prolog_profile_read.restype = ctypes.c_int
         L.mla_prolog_check.argtypes = [ctypes.c_void_p]
         L.mla_prolog_check.restype = ctypes.c_int
+        L.mla_prolog_set_poll_limit.argtypes = [ctypes.c_void_p, ctypes.c_int32]
+        L.mla_prolog_set_poll_limit.restype = ctypes.c_int
         L.mla_prolog_status_string.argtypes = [ctypes.c_int]
         L.mla_prolog_status_string.restype = ctypes.c_char_p
         L.mla_sfa_validate.argtypes = [ctypes.POINTER(SfaDesc), ctypes.POINTER(SfaTensors), ctypes.c_int64]
@@ -139,10 +145,11 @@ def status_string(status: int) -> str:
 
 def make_desc(He, Hcq, Hckv, N, D, Dr, block_num, block_size, max_tokens, eps_cq=1e-5,
               eps_ckv=1e-5, in_dtype=MLA_BF16, query_dtype=MLA_BF16, device=0,
-              cache_dtype=MLA_BF16, concat=0, weights_nk=0, x_quant_only=0, eps_x=1e-5) -> Desc:
+              cache_dtype=MLA_BF16, concat=0, weights_nk=0, x_quant_only=0, eps_x=1e-5,
+              check_index=0) -> Desc:
     return Desc(He, Hcq, Hckv, N, D, Dr, block_num, block_size, max_tokens, eps_cq, eps_ckv,
                 in_dtype, query_dtype, device, cache_dtype, int(concat), int(weights_nk),
-                int(x_quant_only), 0, eps_x)
+                int(x_quant_only), int(check_index), eps_x)
 
 
 def _address(v) -> Optional[int]:
@@ -234,6 +241,13 @@ class MlaProlog:
         st = lib().mla_prolog_check(self._h)
         if st != MLA_OK:
             raise MlaError(st, "mla_prolog_check")
+
+    def set_poll_limit(self, steps: int) -> None:
+        """Poll steps after which a bounded wait of the small-T kernels gives
+        up, from the next run on (0 = the default)."""
+        st = lib().mla_prolog_set_poll_limit(self._h, int(steps))
+        if st != MLA_OK:
+            raise MlaError(st, "mla_prolog_set_poll_limit")
 
     def close(self) -> None:
         """check(), then free the handle."""

@@ -263,6 +263,11 @@ struct Dims {
   // Hckv + Dr in the concatenated layout (q^R and k^R then start Hckv
   // elements into the queryOut row and the kv slot)
   int qs, qrs, kvs, krs;
+  // the run's number (1, 2, ...; never 0, modulo 2^32), which the small-T
+  // kernels' flags and tags hold, and the poll steps a bounded wait makes
+  // before it gives up
+  uint32_t run;
+  int spin;
 };
 
 struct Ptrs {
@@ -300,7 +305,7 @@ struct Ptrs {
   float* cq_scale;   // [T]
   uint16_t* qc;      // [T][N][D] bf16
   uint8_t* xq;       // [N] q^C exchange of the paired small-T kernel, kPairXq bytes a head
-  uint32_t* xflag;   // [N][4] its exchange flags, then one error word; zero between runs
+  uint32_t* xflag;   // [N][4] its exchange flags (run numbers), then one error word
   float* xmax;       // [N][2][32] its per-token row maxima
   uint32_t* fpart;   // fused kernel: [phase-1 blocks][32][64] (fp32 split partial, run tag) words
   uint32_t* fss;     // fused kernel: [windows][32] (fp32 sum of squares, run tag) words
@@ -1520,14 +1525,15 @@ __global__ __launch_bounds__(64 * NW) void k34_stream(Dims d, Ptrs p, PackGeo pg
 // per-head exchange buffer: each block publishes its half with a release
 // flag and waits for its partner's, which is already running (a head's two
 // blocks are on the same XCD when N % 8 == 0); the wait is bounded and a
-// block that gives up marks an error word.  The consumer clears the flag, so
-// every run starts from zero flags.  Products use swapped MFMA operands
+// block that gives up marks an error word.  A flag holds the number of the
+// run that raised it, so a flag left by an earlier run (also one whose wait
+// gave up) never passes for this run's, and nothing is reset between runs.
+// Products use swapped MFMA operands
 // (weights as the A operand), so a lane's accumulator holds four adjacent
 // columns of one token: q^C goes to the exchange buffer in 8-byte pieces,
 // q^N and q^R leave in 8-byte stores.  With the int8 query the two halves
 // also trade their per-token row maxima.  The wave partial sums are added in
 // wave order, so the result is deterministic.  512 threads.
-constexpr int kPairSpin = 1 << 20;
 
 // The exchanged words are written and read with agent-scope relaxed atomics,
 // which bypass the caches that are not coherent across XCDs, so no L2
@@ -1545,23 +1551,24 @@ __device__ __forceinline__ uint4 xload128(const void* p) {
   return make_uint4(uint32_t(a), uint32_t(a >> 32), uint32_t(b), uint32_t(b >> 32));
 }
 
-__device__ __forceinline__ void pair_publish(uint32_t* flag) {
+__device__ __forceinline__ void pair_publish(uint32_t* flag, uint32_t run) {
   __builtin_amdgcn_s_waitcnt(0);   // this wave's exchange stores have completed
   __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) __hip_atomic_store(flag, run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void pair_wait(uint32_t* flag, uint32_t* err) {
+// waits (at most `spin` poll steps) until the partner's flag holds this run's
+// number; the flag is left as it is
+__device__ __forceinline__ void pair_wait(const uint32_t* flag, uint32_t* err, uint32_t run, int spin) {
   if (threadIdx.x == 0) {
     int n = 0;
-    while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-      if (++n > kPairSpin) {
+    while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != run) {
+      if (++n > spin) {
         __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
       __builtin_amdgcn_s_sleep(2);
     }
-    __hip_atomic_store(flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
 }
@@ -1697,7 +1704,7 @@ __global__ __launch_bounds__(512) void k34_pair(Dims d, Ptrs p, PackGeo pg) {
       xstore64(xq + (mt * 4 + st) * 1024 + (16 * (2 * (ct % 2) + g / 2) + c) * 16 + 8 * (g % 2),
                pack_bf16x4(v[0], v[1], v[2], v[3]));
   }
-  pair_publish(p.xflag + 4 * h + half);
+  pair_publish(p.xflag + 4 * h + half, d.run);
 
   // q^R: the owner of token tile mt holds both tiles of every RoPE pair
   if (w >= NW - MT) {
@@ -1734,7 +1741,7 @@ __global__ __launch_bounds__(512) void k34_pair(Dims d, Ptrs p, PackGeo pg) {
   }
 
   // q^N = q^C W^UK[h] over this half's columns, all of D
-  pair_wait(p.xflag + 4 * h + (1 - half), p.xflag + 4 * d.N);
+  pair_wait(p.xflag + 4 * h + (1 - half), p.xflag + 4 * d.N, d.run, d.spin);
   uint4 aq[4][MT];
 #pragma unroll
   for (int s = 0; s < 4; ++s)
@@ -1790,8 +1797,8 @@ __global__ __launch_bounds__(512) void k34_pair(Dims d, Ptrs p, PackGeo pg) {
       for (int w2 = 1; w2 < NW; ++w2) m = fmaxf(m, rmw[w2][lane]);
       __hip_atomic_store(xm + 32 * half + lane, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    pair_publish(p.xflag + 4 * h + 2 + half);
-    pair_wait(p.xflag + 4 * h + 2 + (1 - half), p.xflag + 4 * d.N);
+    pair_publish(p.xflag + 4 * h + 2 + half, d.run);
+    pair_wait(p.xflag + 4 * h + 2 + (1 - half), p.xflag + 4 * d.N, d.run, d.spin);
     if (!ukact) return;
     int8_t* qo = static_cast<int8_t*>(p.q_out);
 #pragma unroll
@@ -1877,8 +1884,6 @@ struct FusedGeo {
   int nwin;            // windows of [W^DQ | W^DkvKr]
   int hi_win, hi_s;    // windows below hi_win take hi_s splits, the others hi_s - 1
   int p1;              // blocks with phase-1 work (the sum of the splits)
-  uint32_t run;        // this run's number (1, 2, ...; never 0, modulo 2^32)
-  int spin;            // poll steps a wait makes before it gives up
 };
 
 // a 16-byte buffer load coherent at agent scope (the sc1 cache policy of an
@@ -2006,7 +2011,7 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
   const int r0 = S ? s * R / S : 0, r1 = S ? (s + 1) * R / S : 0, q2 = lane & 31;
   const bool qwin = j < pg.win_dq;
   const int col0 = (qwin ? 64 * j : 64 * (j - pg.win_dq)) + 2 * q2;   // column in W^DQ or W^DkvKr
-  const uint32_t run = fg.run;
+  const uint32_t run = d.run;
   if (w == 0 && S) {
     // the block's partial, rows 16 mt + 4 g + i, columns 16 ct + c, each
     // value next to this run's tag
@@ -2054,7 +2059,7 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
             for (int k = 0; k < kFusedMaxSplits; ++k)
 #pragma unroll
               for (int e = 0; e < 2; ++e) ok &= !(act[u] && k < S) || v[u][k][e].y == run;
-          if (fused_poll_done(ok, n, fg.spin, err)) break;
+          if (fused_poll_done(ok, n, d.spin, err)) break;
         }
 #pragma unroll
         for (int u = 0; u < kFusedRowSets; ++u) {
@@ -2137,7 +2142,7 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
               for (int u = 0; u < kFusedRowSets; ++u)
 #pragma unroll
                 for (int k = 0; k < 4; ++k) ok &= !(act[u] && j0 + 32 * k < pg.win_dq) || v[u][k].y == run;
-              if (fused_poll_done(ok, n, fg.spin, err)) break;
+              if (fused_poll_done(ok, n, d.spin, err)) break;
             }
 #pragma unroll
             for (int u = 0; u < kFusedRowSets; ++u)
@@ -2162,8 +2167,13 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
           }
         }
       }
-      // the block's outputs are complete: raise its flag
+      // the block's outputs are complete: raise its flag.  The stores above
+      // and the flag are relaxed atomics to different addresses; the wait
+      // for every outstanding memory operation orders them on the device,
+      // and the signal fence keeps the compiler from moving the flag store
+      // above that wait
       __builtin_amdgcn_s_waitcnt(0);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
       if (lane == 0) __hip_atomic_store(flag + b * kFusedFlagStride, run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     // wait for the flags of every split block of this run
@@ -2181,7 +2191,7 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
 #pragma unroll
         for (int k = 0; k < 4; ++k) ok &= v[k] == run;
       }
-      if (fused_poll_done(ok, n, fg.spin, err)) break;
+      if (fused_poll_done(ok, n, d.spin, err)) break;
     }
   }
   __syncthreads();
@@ -2315,7 +2325,7 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
       xstore64(xq + (mt * 4 + st) * 1024 + (16 * (2 * (ct % 2) + g / 2) + c) * 16 + 8 * (g % 2),
                pack_bf16x4(sm[0], sm[1], sm[2], sm[3]));
   }
-  pair_publish(p.xflag + 4 * h + half);
+  pair_publish(p.xflag + 4 * h + half, d.run);
 
   // the cache rows and q^R leave after the exchange is published (its wait
   // for the exchange stores then does not wait for these)
@@ -2352,7 +2362,7 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
   }
 
   // q^N = q^C W^UK[h] over this half's columns, all of D
-  pair_wait(p.xflag + 4 * h + (1 - half), p.xflag + 4 * d.N);
+  pair_wait(p.xflag + 4 * h + (1 - half), p.xflag + 4 * d.N, d.run, d.spin);
   uint4 aqc[4][MT];
 #pragma unroll
   for (int st = 0; st < 4; ++st)
@@ -3078,7 +3088,7 @@ mla_status check_desc(const mla_prolog_desc* d) {
   // the preprocess page's layout and weight options; its concatenated
   // layout holds bf16 rows only
   if ((d->concat != 0 && d->concat != 1) || (d->weights_nk != 0 && d->weights_nk != 1) ||
-      (d->x_quant_only != 0 && d->x_quant_only != 1) || d->reserved != 0)
+      (d->x_quant_only != 0 && d->x_quant_only != 1) || (d->check_index != 0 && d->check_index != 1))
     return MLA_ERR_PARAM_INVALID;
   if (d->concat && (d->query_dtype != MLA_BF16 || d->cache_dtype != MLA_BF16)) return MLA_ERR_PARAM_INVALID;
   if (d->x_quant_only && d->in_dtype != MLA_INT8_STATIC) return MLA_ERR_PARAM_INVALID;
@@ -3177,6 +3187,23 @@ mla_status check_tensors(const mla_prolog_desc* d, const mla_prolog_tensors* t, 
   return MLA_OK;
 }
 
+// cacheIndex copied to the host (after the stream's earlier work) and
+// checked: MLA_ERR_PARAM_INVALID if an entry lies outside [0, slots)
+mla_status check_cache_index(const int64_t* idx, int64_t T, int64_t slots, hipStream_t s) {
+  int64_t* host = nullptr;
+  if (hipHostMalloc(reinterpret_cast<void**>(&host), size_t(T) * sizeof(int64_t), hipHostMallocDefault) !=
+      hipSuccess)
+    return MLA_ERR_RUNTIME;
+  mla_status st = MLA_OK;
+  if (hipMemcpyAsync(host, idx, size_t(T) * sizeof(int64_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    st = MLA_ERR_RUNTIME;
+  for (int64_t i = 0; st == MLA_OK && i < T; ++i)
+    if (host[i] < 0 || host[i] >= slots) st = MLA_ERR_PARAM_INVALID;
+  (void)hipHostFree(host);
+  return st;
+}
+
 }  // namespace
 
 constexpr int kProfileRing = 2048;
@@ -3184,14 +3211,14 @@ constexpr int kProfileEvents = 5;
 
 struct mla_prolog {
   mla_prolog_desc desc;
-  int fused_spin;      // poll steps of the fused kernel's waits
+  int spin;            // poll steps of the small-T kernels' bounded waits
   Layout lay;
   uint8_t* ws;
   hipEvent_t* events;  // kProfileRing x kProfileEvents when profiling, else NULL
   uint8_t* fused;      // per recorded run: 0 four kernels, 1 up_proj and uk as one, 2 one kernel
   int64_t recorded;    // runs recorded since the last read
   bool fused_fit[2];   // the fused kernel (16 or 32 tokens) has all 2N blocks resident at once
-  uint32_t fused_run;  // fused runs launched so far
+  uint32_t run_no;     // number of the last run (1, 2, ...; 0 is skipped on a wrap)
 };
 
 namespace {
@@ -3301,8 +3328,6 @@ bool fused_geo(const mla_prolog_desc& dd, FusedGeo* fg) {
   fg->p1 = fg->hi_win * fg->hi_s + (W - fg->hi_win) * (fg->hi_s - 1);
   const int smin = fg->hi_win < W ? fg->hi_s - 1 : fg->hi_s;
   if ((ceil_div(g.nst_he, smin) + 7) / 8 > kFusedP1) return false;
-  fg->run = 0;
-  fg->spin = kFusedSpin;
   return true;
 }
 
@@ -3419,6 +3444,7 @@ mla_status mla_prolog_pack_weights(mla_prolog_t h, const mla_prolog_tensors* t, 
   Dims d;
   d.T = 0; d.He = int(dd.He); d.Hcq = int(dd.Hcq); d.Hckv = int(dd.Hckv); d.N = int(dd.N);
   d.D = int(dd.D); d.Dr = int(dd.Dr); d.slots = 0; d.eps_cq = d.eps_ckv = 0.0;
+  d.run = 0; d.spin = 0;
   Ptrs p;
   std::memset(&p, 0, sizeof p);
   p.w_dq = static_cast<const uint8_t*>(t->weight_dq);
@@ -3438,6 +3464,16 @@ mla_status mla_prolog_create(const mla_prolog_desc* desc, mla_prolog_t* out) {
   *out = nullptr;
   mla_status st = check_desc(desc);
   if (st != MLA_OK) return st;
+  // MLA_PROLOG_FUSED_SPIN overrides the poll steps a bounded wait makes
+  // before it gives up (a test of the failure report sets it to 1); a value
+  // that is not a whole number in [1, kFusedSpin] is refused
+  int spin = kFusedSpin;
+  if (const char* sp = std::getenv("MLA_PROLOG_FUSED_SPIN")) {
+    char* end = nullptr;
+    const long v = std::strtol(sp, &end, 10);
+    if (end == sp || *end != '\0' || v <= 0 || v > kFusedSpin) return MLA_ERR_PARAM_INVALID;
+    spin = int(v);
+  }
   int prev = 0;
   if (hipGetDevice(&prev) != hipSuccess) return MLA_ERR_RUNTIME;
   if (hipSetDevice(desc->device) != hipSuccess) return MLA_ERR_PARAM_INVALID;
@@ -3454,8 +3490,8 @@ mla_status mla_prolog_create(const mla_prolog_desc* desc, mla_prolog_t* out) {
     (void)hipSetDevice(prev);
     return MLA_ERR_RUNTIME;
   }
-  // the exchange flags start at zero and every run leaves them at zero; the
-  // fused kernel's tags and flags start at zero (no run is numbered 0)
+  // the flags and tags of the small-T kernels start at zero, which no run's
+  // number is
   if (hipMemset(h->ws + h->lay.xflag, 0, size_t(4 * desc->N + 1) * 4) != hipSuccess ||
       hipMemset(h->ws + h->lay.fpart, 0, h->lay.total - h->lay.fpart) != hipSuccess ||
       hipDeviceSynchronize() != hipSuccess) {
@@ -3464,17 +3500,11 @@ mla_status mla_prolog_create(const mla_prolog_desc* desc, mla_prolog_t* out) {
     (void)hipSetDevice(prev);
     return MLA_ERR_RUNTIME;
   }
+  h->run_no = 0;
+  h->spin = spin;
   // the fused kernel's blocks wait for one another, so all 2N of them must
   // be resident at once; MLA_PROLOG_FUSED=0 in the environment turns it off
-  h->fused_run = 0;
   h->fused_fit[0] = h->fused_fit[1] = false;
-  // MLA_PROLOG_FUSED_SPIN overrides the poll steps a wait makes before it
-  // gives up (a test of the failure report sets it to 1)
-  h->fused_spin = kFusedSpin;
-  if (const char* sp = std::getenv("MLA_PROLOG_FUSED_SPIN")) {
-    const long v = std::strtol(sp, nullptr, 10);
-    if (v > 0 && v <= kFusedSpin) h->fused_spin = int(v);
-  }
   {
     FusedGeo fg;
     const char* env = std::getenv("MLA_PROLOG_FUSED");
@@ -3506,6 +3536,15 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   if (hipGetDevice(&prev) != hipSuccess) return MLA_ERR_RUNTIME;
   if (prev != dd.device && hipSetDevice(dd.device) != hipSuccess) return MLA_ERR_RUNTIME;
   (void)hipGetLastError();
+  if (dd.check_index && dd.block_num > 0) {
+    // the debugging check of cacheIndex: every entry in [0, slots)
+    st = check_cache_index(t->cache_index, T, dd.block_num * dd.block_size,
+                           static_cast<hipStream_t>(stream));
+    if (st != MLA_OK) {
+      if (prev != dd.device) (void)hipSetDevice(prev);
+      return st;
+    }
+  }
 
   const bool i8d = down_i8(dd), i8u = up_i8(dd), q8 = dd.query_dtype == MLA_INT8;
   const Plan pl = make_plan(dd, T);
@@ -3514,6 +3553,12 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   d.D = int(dd.D); d.Dr = int(dd.Dr);
   d.slots = dd.block_num * dd.block_size;
   d.eps_cq = dd.eps_cq; d.eps_ckv = dd.eps_ckv;
+  // run numbers 1, 2, ...: 0 is what the flags and tags of the workspace
+  // start with, so a wrap of the counter skips it.  A run whose launch fails
+  // still uses up its number: no flag can hold it.
+  if (++h->run_no == 0) h->run_no = 1;
+  d.run = h->run_no;
+  d.spin = h->spin;
   const int row = int(dd.Hckv + dd.Dr);
   d.qs = dd.concat ? row : d.Hckv;
   d.qrs = dd.concat ? row : d.Dr;
@@ -3595,18 +3640,11 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   p.packed = static_cast<const uint8_t*>(t->packed_weights);
   FusedGeo fg;
   if (p.packed && pl.stream && h->fused_fit[pl.mt1 == 1 ? 0 : 1] && fused_geo(dd, &fg)) {
-    // run numbers 1, 2, ...: 0 is what the workspace starts with, so a wrap
-    // of the counter skips it
-    const uint32_t last = h->fused_run;
-    if (++h->fused_run == 0) h->fused_run = 1;
-    fg.run = h->fused_run;
-    fg.spin = h->fused_spin;
     const PackGeo g = geo_of(dd);
     if (pl.mt1 == 1) k_fused<1><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g, fg);
     else k_fused<2><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g, fg);
     mark(-2);
     const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) h->fused_run = last;
     if (prev != dd.device) (void)hipSetDevice(prev);
     return e == hipSuccess ? MLA_OK : MLA_ERR_RUNTIME;
   }
@@ -3716,6 +3754,13 @@ mla_status mla_prolog_destroy(mla_prolog_t h) {
   }
   delete h;
   return st;
+}
+
+mla_status mla_prolog_set_poll_limit(mla_prolog_t h, int32_t steps) {
+  if (!h) return MLA_ERR_NULLPTR;
+  if (steps < 0 || steps > kFusedSpin) return MLA_ERR_PARAM_INVALID;
+  h->spin = steps ? int(steps) : kFusedSpin;
+  return MLA_OK;
 }
 
 mla_status mla_prolog_check(mla_prolog_t h) {

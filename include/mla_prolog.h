@@ -109,6 +109,14 @@ typedef enum { MLA_BF16 = 0, MLA_INT8 = 1, MLA_INT8_PARTIAL = 2, MLA_INT8_STATIC
  *   need packed_weights (the unpacked kernels read (k, n) weights only:
  *   MLA_ERR_UNSUPPORTED otherwise).  0: (k, n) row-major.
  * x_quant_only: see MLA_INT8_STATIC; 0 in the other scenarios.
+ * check_index 1: every run first copies cacheIndex to the host, which waits
+ *   for the stream, and returns MLA_ERR_PARAM_INVALID with nothing enqueued
+ *   if an entry lies outside [0, block_num*block_size) (the prolog page's
+ *   "Parameters" table, cacheIndex: the values must lie in that range).  A
+ *   debugging aid: it costs a device-to-host copy and a wait per run.  With
+ *   0, out-of-range entries are skipped on the device (their rows are
+ *   written nowhere) and nothing is reported.  No check is made when
+ *   block_num is 0 (no cache update).
  * max_tokens bounds T of every run; it sizes the handle's workspace.
  * eps_cq / eps_ckv: the two RmsNorm epsilons (the page recommends 1e-5);
  *   eps_x: that of the RmsNorm of x (MLA_INT8_STATIC; the preprocess page
@@ -126,7 +134,7 @@ typedef struct {
   int32_t concat;      /* 0 or 1 */
   int32_t weights_nk;  /* 0 or 1 */
   int32_t x_quant_only; /* 0 or 1 */
-  int32_t reserved;    /* 0 */
+  int32_t check_index; /* 0 or 1 (a debugging aid, see below) */
   double eps_x;
 } mla_prolog_desc;
 
@@ -223,11 +231,20 @@ typedef struct mla_prolog* mla_prolog_t;
 
 /* Checks a description and, when tensors is not NULL, one run's pointers
  * (presence, 16-byte alignment) and T (0 <= T <= max_tokens).  Pure host
- * code: it touches no device and no device memory. */
+ * code: it touches no device and no device memory.  It stands for the
+ * parameter validation of the page's first-phase call
+ * (aclnnMlaPrologV2WeightNzGetWorkspaceSize, "Function Prototype"), with the
+ * error classes of its "Return Value" table: MLA_ERR_NULLPTR where a required
+ * pointer is missing, MLA_ERR_PARAM_INVALID where a shape, dtype, alignment
+ * or size is outside the domain, MLA_ERR_UNSUPPORTED where the sizes are
+ * legal but no kernel tiling takes them. */
 mla_status mla_prolog_validate(const mla_prolog_desc* desc, const mla_prolog_tensors* tensors,
                                int64_t T);
 
-/* Bytes of device workspace a handle for desc owns (0 if desc is invalid). */
+/* Bytes of device workspace a handle for desc owns (0 if desc is invalid):
+ * the workspaceSize output of the page's first-phase call
+ * (aclnnMlaPrologV2WeightNzGetWorkspaceSize, "Parameters"), fixed here by
+ * the description and max_tokens. */
 size_t mla_prolog_workspace_bytes(const mla_prolog_desc* desc);
 
 /* Bytes of the packed-weight buffer for desc (0 if desc is invalid). */
@@ -239,23 +256,37 @@ size_t mla_prolog_packed_weights_bytes(const mla_prolog_desc* desc);
  * library's packed layout: per matrix, windows of 64 columns, each stored as
  * its k-stages (32 bf16 or 64 int8 rows, 4 KB) in MFMA operand order, so that
  * a run streams every window as one contiguous region.  Like the operator
- * page's weights, which its API takes in a pre-tiled format, this is a
- * one-time conversion per weight set.  Stream-ordered; the other tensor
- * fields are ignored. */
+ * page's weights, which its API takes in a pre-tiled format (the NZ format
+ * of weightDq, weightUqQr and weightDkvKr in its "Parameters" table), this
+ * is a one-time conversion per weight set; the tiling is the library's own.
+ * Stream-ordered; the other tensor fields are ignored.  Returns
+ * MLA_ERR_NULLPTR for a missing weight or buffer, MLA_ERR_PARAM_INVALID for
+ * a misaligned one, MLA_ERR_RUNTIME if the launch fails. */
 mla_status mla_prolog_pack_weights(mla_prolog_t handle, const mla_prolog_tensors* tensors,
                                    void* packed, void* stream);
 
 /* Validates desc, allocates the handle and its device workspace on
- * desc->device (the caller's current device is restored).  On error *out is
- * set to NULL.  Two environment variables, read here, are for diagnosis:
+ * desc->device (the caller's current device is restored).  It stands for the
+ * page's first phase (aclnnMlaPrologV2WeightNzGetWorkspaceSize, "Function
+ * Prototype"), whose workspace the caller allocates: here the handle owns
+ * it, sized for max_tokens, and every run reuses it.  The handle belongs to
+ * the caller until mla_prolog_destroy.  Returns the validation codes of
+ * mla_prolog_validate, or MLA_ERR_RUNTIME if the allocation fails (the
+ * "Return Value" table's runtime class).  On error *out is set to NULL.  Two environment variables, read here, are for diagnosis:
  * MLA_PROLOG_FUSED=0 keeps small-T runs off the one-launch kernel, and
- * MLA_PROLOG_FUSED_SPIN=n (1..2^20) caps the poll steps of that kernel's
- * waits (see mla_prolog_check). */
+ * MLA_PROLOG_FUSED_SPIN=n (a whole number in 1..2^20) caps the poll steps of
+ * the small-T kernels' bounded waits (see mla_prolog_check); any other value
+ * of it makes create return MLA_ERR_PARAM_INVALID. */
 mla_status mla_prolog_create(const mla_prolog_desc* desc, mla_prolog_t* out);
 
 /* Enqueues one prolog over T tokens on stream (a hipStream_t; NULL = the
- * default stream).  Returns after enqueueing; the outputs and caches are
- * ready when the stream reaches this point.  T = 0 enqueues nothing.  A
+ * default stream): the page's second-phase call (aclnnMlaPrologV2WeightNz,
+ * "Function Prototype" and its "Parameters": workspace, executor, stream),
+ * with the tensors given per run and the workspace the handle's.  Every
+ * pointer and T are validated first (as by mla_prolog_validate; nothing is
+ * enqueued on an error); MLA_ERR_RUNTIME if a launch fails.  Returns after
+ * enqueueing; the outputs and caches are ready when the stream reaches this
+ * point.  T = 0 enqueues nothing.  A
  * handle's workspace is shared by its runs: runs of one handle on different
  * streams must be ordered by the caller.  The result is deterministic: the
  * same inputs give bit-identical outputs.
@@ -269,19 +300,32 @@ mla_status mla_prolog_create(const mla_prolog_desc* desc, mla_prolog_t* out);
 mla_status mla_prolog_run(mla_prolog_t handle, const mla_prolog_tensors* tensors, int64_t T,
                           void* stream);
 
-/* Frees the workspace and the handle (after synchronising its device). */
+/* Frees the workspace and the handle (after synchronising its device): the
+ * teardown that follows the page's sample call sequence (releasing the
+ * workspace and the executor).  MLA_ERR_NULLPTR for a NULL handle,
+ * MLA_ERR_RUNTIME if the device reports an error; the handle is freed in
+ * either case. */
 mla_status mla_prolog_destroy(mla_prolog_t handle);
 
 /* Waits for the handle's device and reports whether any earlier run gave up
- * waiting for another block of its own launch (MLA_ERR_RUNTIME; then the
- * outputs of those runs are not to be trusted), else MLA_OK; clears the
- * record.  On the small-T kernels the blocks of one launch hand data to one
+ * waiting for another block of its own launch (MLA_ERR_RUNTIME, the runtime
+ * class of the page's "Return Value" table; then the outputs of those runs
+ * are not to be trusted), else MLA_OK; clears the record.  On the small-T kernels the blocks of one launch hand data to one
  * another and wait, with a bounded spin, for it; that can only fail when
  * the launch does not get the whole device (the library checks at create
  * time that all of its blocks fit on the device at once). */
 mla_status mla_prolog_check(mla_prolog_t handle);
 
-/* Kernel timing with HIP events, for benchmarks.  After
+/* Sets the poll steps after which a bounded wait of the small-T kernels
+ * gives up (see mla_prolog_check), from the next run on: steps in
+ * 1..2^20, or 0 for the default (2^20 steps, about a second).  Other values
+ * return MLA_ERR_PARAM_INVALID.  For diagnosis and tests of the failure
+ * report; a wait that gave up leaves nothing behind that a later run could
+ * mistake for its own data (flags and tags carry the number of their run). */
+mla_status mla_prolog_set_poll_limit(mla_prolog_t handle, int32_t steps);
+
+/* Kernel timing with HIP events, for benchmarks (no passage of the page:
+ * instrumentation of this library).  After
  * mla_prolog_profile_enable(h, 1) every run of h records HIP events on its
  * stream before its first kernel and after each of its four kernels
  * (down_proj, norm_rope_cache, up_proj, uk; where one kernel does both
@@ -297,7 +341,8 @@ mla_status mla_prolog_check(mla_prolog_t handle);
 mla_status mla_prolog_profile_enable(mla_prolog_t handle, int enable);
 mla_status mla_prolog_profile_read(mla_prolog_t handle, double* kernel_ms, int64_t* runs);
 
-/* Text of a status code. */
+/* Text of a status code (the descriptions of the page's "Return Value"
+ * table, in short). */
 const char* mla_prolog_status_string(mla_status status);
 
 #ifdef __cplusplus

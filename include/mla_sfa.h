@@ -82,21 +82,26 @@ typedef struct {
 typedef struct mla_sfa* mla_sfa_t;
 
 /* Checks a description and, when tensors is not NULL, one run's pointers
- * for T tokens; pure host.  MLA_OK, MLA_ERR_NULLPTR, MLA_ERR_PARAM_INVALID
- * or MLA_ERR_UNSUPPORTED. */
+ * for T tokens; pure host: the parameter validation of the attention page's
+ * first-phase call (aclnnSparseFlashAttentionGetWorkspaceSize, function
+ * prototype), with the prolog page's return-code classes.  MLA_OK,
+ * MLA_ERR_NULLPTR, MLA_ERR_PARAM_INVALID or MLA_ERR_UNSUPPORTED. */
 mla_status mla_sfa_validate(const mla_sfa_desc* desc, const mla_sfa_tensors* tensors, int64_t T);
 
-/* Creates a handle on desc->device with its workspace.  MLA_ERR_RUNTIME if
- * the allocation fails.  *out is NULL on failure. */
+/* Creates a handle on desc->device with its workspace (the attention page's
+ * first phase sizes a workspace the caller allocates; here the handle owns
+ * it).  MLA_ERR_RUNTIME if the allocation fails.  *out is NULL on failure. */
 mla_status mla_sfa_create(const mla_sfa_desc* desc, mla_sfa_t* out);
 
 /* Enqueues one attention over T tokens on stream (a hipStream_t, NULL = the
- * default stream).  T = 0 is a no-op.  One handle must not run on two
+ * default stream): the attention page's second-phase call
+ * (aclnnSparseFlashAttention, function prototype).  T = 0 is a no-op.  One handle must not run on two
  * streams at once (its workspace is shared).  MLA_ERR_RUNTIME if a launch
  * fails. */
 mla_status mla_sfa_run(mla_sfa_t handle, const mla_sfa_tensors* tensors, int64_t T, void* stream);
 
-/* Waits for the handle's device, frees the handle and its workspace. */
+/* Waits for the handle's device, frees the handle and its workspace (the
+ * teardown after the page's sample call sequence). */
 mla_status mla_sfa_destroy(mla_sfa_t handle);
 
 #ifdef __cplusplus

@@ -17,7 +17,9 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(HERE, "mla_oracle.cpp")
-LIBRARY = os.path.join(HERE, "libmla_oracle.so")
+#: the built oracle; MLA_ORACLE_LIBRARY names another build of the same
+#: source (the sanitizer test builds one with AddressSanitizer and UBSan)
+LIBRARY = os.environ.get("MLA_ORACLE_LIBRARY") or os.path.join(HERE, "libmla_oracle.so")
 BUILD_CMD = ["g++", "-O2", "-std=c++17", "-ffp-contract=off", "-fno-fast-math", "-shared",
              "-fPIC", "-pthread", SOURCE, "-o", LIBRARY]
 

@@ -273,3 +273,17 @@ def test_sfa_bad_run_arguments():
     t = sfa_tensors(); t["query"] = FAKE + 8
     assert mla.sfa_validate(d, t, 8) == mla.MLA_ERR_PARAM_INVALID
     assert mla.sfa_validate(sfa_desc(concat=1), sfa_tensors(), 8) == mla.MLA_ERR_PARAM_INVALID   # kr given
+
+
+@pytest.mark.parametrize("value", ["0", "-3", "abc", "12x", "", str((1 << 20) + 1)])
+def test_bad_poll_limit_is_refused(value, monkeypatch):
+    # create reads MLA_PROLOG_FUSED_SPIN before it touches a device, and
+    # refuses any value that is not a whole number in [1, 2^20]
+    monkeypatch.setenv("MLA_PROLOG_FUSED_SPIN", value)
+    h = ctypes.c_void_p()
+    assert mla.lib().mla_prolog_create(ctypes.byref(model_desc()), ctypes.byref(h)) == mla.MLA_ERR_PARAM_INVALID
+    assert not h.value
+
+
+def test_poll_limit_setter_needs_a_handle():
+    assert mla.lib().mla_prolog_set_poll_limit(None, 5) == mla.MLA_ERR_NULLPTR
