@@ -3772,11 +3772,16 @@ mla_status mla_prolog_check(mla_prolog_t h) {
   // kernel's follows its 2N block flags
   uint32_t* words[2] = {reinterpret_cast<uint32_t*>(h->ws + h->lay.xflag) + 4 * h->desc.N,
                         reinterpret_cast<uint32_t*>(h->ws + h->lay.fcnt) + 2 * h->desc.N * kFusedFlagStride};
-  mla_status st = hipDeviceSynchronize() == hipSuccess ? MLA_OK : MLA_ERR_RUNTIME;
+  const bool synced = hipDeviceSynchronize() == hipSuccess;
+  mla_status st = synced ? MLA_OK : MLA_ERR_RUNTIME;
+  // every word is read and cleared, also when an earlier one was set
   for (uint32_t* wd : words) {
     uint32_t v = 0;
-    if (st == MLA_OK && hipMemcpy(&v, wd, 4, hipMemcpyDeviceToHost) != hipSuccess) st = MLA_ERR_RUNTIME;
-    if (st == MLA_OK && v != 0) {
+    if (!synced || hipMemcpy(&v, wd, 4, hipMemcpyDeviceToHost) != hipSuccess) {
+      st = MLA_ERR_RUNTIME;
+      continue;
+    }
+    if (v != 0) {
       st = MLA_ERR_RUNTIME;
       const uint32_t zero = 0;
       (void)hipMemcpy(wd, &zero, 4, hipMemcpyHostToDevice);

@@ -371,14 +371,16 @@ def test_fused_gave_up_is_reported(monkeypatch):
 
 @pytest.mark.parametrize("path", ["one_launch", "paired"])
 def test_run_after_a_wait_gave_up_is_correct(path, monkeypatch):
-    # One handle: runs whose bounded waits are capped at one poll step (their
-    # partner blocks are usually not there yet, so waits give up and leave
+    # One handle: runs whose bounded waits are capped at one poll step (the
+    # blocks waited for are often not there yet, so waits give up and leave
     # flags and tags of those runs behind; every access stays in bounds and
     # the kernels end normally), check() reports it; then the default limit,
     # and the next runs on the same workspace must match the oracle.  The
-    # paired path trades q^C (and, with the int8 query, the row maxima)
-    # between a head's two blocks; the one-launch path also hands the
-    # down-projection across blocks.
+    # one-launch path waits on every block of the launch, so its runs give up
+    # every time, and its q^C trade between a head's two blocks uses the
+    # same exchange flags as the paired path.  In the paired path the two
+    # blocks of a head reach their trade together (q^C, and with the int8
+    # query the row maxima), so a one-step poll may or may not give up.
     if path == "paired":
         monkeypatch.setenv("MLA_PROLOG_FUSED", "0")
         inp = synth.make_inputs(PAIR_INT8["pair_q8_t17_n16"])
@@ -401,7 +403,9 @@ def test_run_after_a_wait_gave_up_is_correct(path, monkeypatch):
                 h.check()
             except mla.MlaError:
                 gave_up += 1
-        assert gave_up > 0
+        say(f"  runs that gave up: {gave_up} of 8")
+        if path == "one_launch":
+            assert gave_up > 0
         h.set_poll_limit(0)
         for _ in range(2):
             h.run(t, T)
