@@ -43,7 +43,7 @@ MLA_INT8_STATIC = 3    # in_dtype only: the preprocess page's static int8 scenar
 #: the symbols include/mla_prolog.h declares
 EXPORTS = ("mla_prolog_validate", "mla_prolog_workspace_bytes", "mla_prolog_packed_weights_bytes",
            "mla_prolog_pack_weights", "mla_prolog_create",
-           "mla_prolog_run", "mla_prolog_destroy", "mla_prolog_profile_enable",
+           "mla_prolog_run", "mla_prolog_run_noalloc", "mla_prolog_destroy", "mla_prolog_profile_enable",
            "mla_prolog_profile_read", "mla_prolog_check", "mla_prolog_set_poll_limit",
            "mla_prolog_status_string",
            "mla_sfa_validate", "mla_sfa_create", "mla_sfa_run", "mla_sfa_destroy")
@@ -114,6 +114,9 @@ def lib() -> ctypes.CDLL:
         L.mla_prolog_run.argtypes = [ctypes.c_void_p, ctypes.POINTER(Tensors), ctypes.c_int64,
                                      ctypes.c_void_p]
         L.mla_prolog_run.restype = ctypes.c_int
+        L.mla_prolog_run_noalloc.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Tensors), ctypes.c_int64,
+                                             ctypes.c_void_p]
+        L.mla_prolog_run_noalloc.restype = ctypes.c_int
         L.mla_prolog_destroy.argtypes = [ctypes.c_void_p]
         L.mla_prolog_destroy.restype = ctypes.c_int
         L.mla_prolog_profile_enable.argtypes = [ctypes.c_void_p, ctypes.c_int]
@@ -180,6 +183,16 @@ def workspace_bytes(desc: Desc) -> int:
 
 def packed_weights_bytes(desc: Desc) -> int:
     return int(lib().mla_prolog_packed_weights_bytes(ctypes.byref(desc)))
+
+
+def run_noalloc(desc: Desc, tensors: Dict[str, object], T: int, stream=None) -> None:
+    """One prolog with no handle and no allocation: the library's static
+    per-device workspace (mla_prolog_run_noalloc)."""
+    t = make_tensors(tensors)
+    st = lib().mla_prolog_run_noalloc(ctypes.byref(desc), ctypes.byref(t), int(T),
+                                      ctypes.c_void_p(_stream_handle(stream)))
+    if st != MLA_OK:
+        raise MlaError(st, "mla_prolog_run_noalloc")
 
 
 def _stream_handle(stream) -> int:

@@ -45,6 +45,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <type_traits>
 
@@ -3027,17 +3028,22 @@ struct Layout {
   size_t part, cq, cq_scale, qc, xq, xflag, xmax, x8, fpart, fss, fykr, fcnt, total;
 };
 
-Layout layout(const mla_prolog_desc& d) {
+// split-partial rows (S * T) a run of T tokens writes, on any of its paths
+int64_t part_rows_at(const mla_prolog_desc& d, int64_t T) {
+  const Plan pl = make_plan(d, T);
+  int64_t r = int64_t(pl.S) * T;
+  if (pl.stream) r = std::max<int64_t>(r, int64_t(pl.Sp) * T);
+  else r = std::max<int64_t>(r, int64_t(tiled_plan(d, T).S) * T);
+  return r;
+}
+
+// The workspace regions for runs of up to d.max_tokens tokens whose split
+// partials take part_rows rows.  small_t: also the regions of the small-T
+// kernels that hand data across blocks (exchange buffers, flags, tagged
+// partials); without them those kernels must not run.
+Layout layout(const mla_prolog_desc& d, int64_t part_rows, bool small_t) {
   Layout L;
   const int64_t Ntot = d.Hcq + d.Hckv + d.Dr;
-  int64_t part_rows = 0;
-  // the largest S*T over all T <= max_tokens (plans are cheap host arithmetic)
-  for (int64_t T = 1; T <= d.max_tokens; ++T) {
-    const Plan pl = make_plan(d, T);
-    part_rows = std::max<int64_t>(part_rows, int64_t(pl.S) * T);
-    if (pl.stream) part_rows = std::max<int64_t>(part_rows, int64_t(pl.Sp) * T);
-    else part_rows = std::max<int64_t>(part_rows, int64_t(tiled_plan(d, T).S) * T);
-  }
   // c^Q and q^C are row-major on the row-major-weight path and
   // fragment-packed (16-token tiles of 1 KB k-stages) on the packed path
   const PackGeo g = geo_of(d);
@@ -3049,26 +3055,36 @@ Layout layout(const mla_prolog_desc& d) {
   L.cq_scale = align256(L.cq + cq_bytes);
   L.qc = align256(L.cq_scale + size_t(d.max_tokens) * 4);
   L.xq = align256(L.qc + qc_bytes);
-  L.xflag = align256(L.xq + size_t(d.N) * kPairXq);
-  L.xmax = align256(L.xflag + size_t(4 * d.N + 1) * 4);
+  const size_t st = small_t ? 1 : 0;
+  L.xflag = align256(L.xq + st * size_t(d.N) * kPairXq);
+  L.xmax = align256(L.xflag + st * size_t(4 * d.N + 1) * 4);
   // the fused small-T kernel: 2N blocks' partials, per-window sums of
   // squares, the c^KV / k^R rows, counters
   const size_t nwin = size_t(g.win_dq + g.win_kr);
   // the static scenario's int8 codes of x
-  L.x8 = align256(L.xmax + size_t(d.N) * 64 * 4);
+  L.x8 = align256(L.xmax + st * size_t(d.N) * 64 * 4);
   const size_t x8_bytes = d.in_dtype == MLA_INT8_STATIC ? size_t(d.max_tokens) * d.He : 0;
   L.fpart = align256(L.x8 + x8_bytes);
-  L.fss = align256(L.fpart + size_t(2 * d.N) * 32 * 64 * 8);
-  L.fykr = align256(L.fss + nwin * 32 * 8);
-  L.fcnt = align256(L.fykr + size_t(32) * (d.Hckv + d.Dr) * 4);
-  L.total = align256(L.fcnt + (size_t(2 * d.N) * kFusedFlagStride + 1) * 4);
+  L.fss = align256(L.fpart + st * size_t(2 * d.N) * 32 * 64 * 8);
+  L.fykr = align256(L.fss + st * nwin * 32 * 8);
+  L.fcnt = align256(L.fykr + st * size_t(32) * (d.Hckv + d.Dr) * 4);
+  L.total = align256(L.fcnt + st * (size_t(2 * d.N) * kFusedFlagStride + 1) * 4);
   return L;
+}
+
+// A handle's workspace: every T <= max_tokens, every path
+Layout layout(const mla_prolog_desc& d) {
+  int64_t part_rows = 0;
+  // the largest S*T over all T <= max_tokens (plans are cheap host arithmetic)
+  for (int64_t T = 1; T <= d.max_tokens; ++T) part_rows = std::max(part_rows, part_rows_at(d, T));
+  return layout(d, part_rows, true);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
-mla_status check_desc(const mla_prolog_desc* d) {
+// every rule of a description but the workspace's size
+mla_status check_desc_core(const mla_prolog_desc* d) {
   if (!d) return MLA_ERR_NULLPTR;
   const int64_t dims[6] = {d->He, d->Hcq, d->Hckv, d->N, d->D, d->Dr};
   for (int64_t v : dims)
@@ -3113,6 +3129,12 @@ mla_status check_desc(const mla_prolog_desc* d) {
   if (d->in_dtype == MLA_INT8_PARTIAL && (d->Hcq % 16 || d->D % 16 || d->Dr % 16))
     return MLA_ERR_UNSUPPORTED;
   if (d->N * (d->D + d->Dr) > (1 << 24)) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+mla_status check_desc(const mla_prolog_desc* d) {
+  const mla_status st = check_desc_core(d);
+  if (st != MLA_OK) return st;
   // the norm kernel addresses the split partials with 32-bit offsets
   const Layout L = layout(*d);
   if (L.cq - L.part >= size_t(kOOB)) return MLA_ERR_UNSUPPORTED;
@@ -3209,6 +3231,13 @@ mla_status check_cache_index(const int64_t* idx, int64_t T, int64_t slots, hipSt
 constexpr int kProfileRing = 2048;
 constexpr int kProfileEvents = 5;
 
+// The workspace of mla_prolog_run_noalloc: one array per device, allocated
+// with the library's code object when it is loaded on that device and held
+// until the process ends.  In host code `scratch` is only a stand-in for the
+// symbol; its device address comes from hipGetSymbolAddress.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
 struct mla_prolog {
   mla_prolog_desc desc;
   int spin;            // poll steps of the small-T kernels' bounded waits
@@ -3277,14 +3306,14 @@ bool packed_fits(const mla_prolog_desc& dd) { return (dd.Hckv + 63) / 64 <= 8; }
 // I8U: int8 c^Q and W^UqQr.
 template <bool I8D, bool I8U, int MT, class Mark>
 void packed_launch(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g,
-                   bool q8, Mark& mark) {
+                   bool q8, bool pair_ok, Mark& mark) {
   constexpr bool I8 = I8U;   // the up-projection kernels below
   const int tiles = g.win_dq + g.win_kr;
   k1_packed<I8D, MT, 4, 2><<<dim3(tiles * pl.Sp), 256, 0, s>>>(d, p, g, pl.Sp, pl.sps);
   mark(1);
   launch_norm<I8D, I8U>(s, d, p, pl.Sp, g.nst_cq);
   mark(2);
-  if (g.nope_w == 2 && d.Dr == 64 && g.uk_w <= 8) {
+  if (pair_ok && g.nope_w == 2 && d.Dr == 64 && g.uk_w <= 8) {
     // two balanced blocks per head; the profile books both products to the first
     if (q8) k34_pair<I8, MT, true><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g);
     else k34_pair<I8, MT, false><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g);
@@ -3333,18 +3362,18 @@ bool fused_geo(const mla_prolog_desc& dd, FusedGeo* fg) {
 
 template <int MT, class Mark>
 void packed_launch_mt(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g,
-                      bool i8d, bool i8u, bool q8, Mark& mark) {
-  if (i8d) packed_launch<true, true, MT>(pl, s, d, p, g, q8, mark);
-  else if (i8u) packed_launch<false, true, MT>(pl, s, d, p, g, q8, mark);
-  else packed_launch<false, false, MT>(pl, s, d, p, g, q8, mark);
+                      bool i8d, bool i8u, bool q8, bool pair_ok, Mark& mark) {
+  if (i8d) packed_launch<true, true, MT>(pl, s, d, p, g, q8, pair_ok, mark);
+  else if (i8u) packed_launch<false, true, MT>(pl, s, d, p, g, q8, pair_ok, mark);
+  else packed_launch<false, false, MT>(pl, s, d, p, g, q8, pair_ok, mark);
 }
 
 template <class Mark>
 void launch_packed(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p,
-                   const mla_prolog_desc& dd, bool q8, Mark& mark) {
+                   const mla_prolog_desc& dd, bool q8, bool pair_ok, Mark& mark) {
   const PackGeo g = geo_of(dd);
-  if (pl.mt1 == 1) packed_launch_mt<1>(pl, s, d, p, g, down_i8(dd), up_i8(dd), q8, mark);
-  else packed_launch_mt<2>(pl, s, d, p, g, down_i8(dd), up_i8(dd), q8, mark);
+  if (pl.mt1 == 1) packed_launch_mt<1>(pl, s, d, p, g, down_i8(dd), up_i8(dd), q8, pair_ok, mark);
+  else packed_launch_mt<2>(pl, s, d, p, g, down_i8(dd), up_i8(dd), q8, pair_ok, mark);
 }
 
 // Tiled run on packed weights (token counts above the streaming range).
@@ -3526,26 +3555,31 @@ mla_status mla_prolog_create(const mla_prolog_desc* desc, mla_prolog_t* out) {
   return MLA_OK;
 }
 
-mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T, void* stream) {
-  if (!h) return MLA_ERR_NULLPTR;
-  const mla_prolog_desc& dd = h->desc;
-  mla_status st = check_tensors(&dd, t, T);
-  if (st != MLA_OK) return st;
-  if (T == 0) return MLA_OK;
-  int prev = 0;
-  if (hipGetDevice(&prev) != hipSuccess) return MLA_ERR_RUNTIME;
-  if (prev != dd.device && hipSetDevice(dd.device) != hipSuccess) return MLA_ERR_RUNTIME;
-  (void)hipGetLastError();
-  if (dd.check_index && dd.block_num > 0) {
-    // the debugging check of cacheIndex: every entry in [0, slots)
-    st = check_cache_index(t->cache_index, T, dd.block_num * dd.block_size,
-                           static_cast<hipStream_t>(stream));
-    if (st != MLA_OK) {
-      if (prev != dd.device) (void)hipSetDevice(prev);
-      return st;
-    }
-  }
+}  // extern "C"
 
+namespace {
+
+// One run's launches on stream s, with the workspace at ws (laid out as
+// lay).  fused_ok / pair_ok allow the small-T kernels whose blocks hand data
+// to one another through flags and tagged words that hold the run's number;
+// without them every kernel of the run only reads what earlier kernels of
+// the stream wrote.  ev / mark_kind are this run's profiling events (or
+// NULL).  The caller has validated the run and made its device current.
+struct RunCtx {
+  const mla_prolog_desc* dd;
+  const Layout* lay;
+  uint8_t* ws;
+  bool fused_ok, pair_ok;
+  uint32_t run;
+  int spin;
+  hipEvent_t* ev;
+  uint8_t* mark_kind;
+};
+
+mla_status enqueue(const RunCtx& c, const mla_prolog_tensors* t, int64_t T, hipStream_t s) {
+  const mla_prolog_desc& dd = *c.dd;
+  const Layout& lay = *c.lay;
+  uint8_t* const ws = c.ws;
   const bool i8d = down_i8(dd), i8u = up_i8(dd), q8 = dd.query_dtype == MLA_INT8;
   const Plan pl = make_plan(dd, T);
   Dims d;
@@ -3553,12 +3587,8 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   d.D = int(dd.D); d.Dr = int(dd.Dr);
   d.slots = dd.block_num * dd.block_size;
   d.eps_cq = dd.eps_cq; d.eps_ckv = dd.eps_ckv;
-  // run numbers 1, 2, ...: 0 is what the flags and tags of the workspace
-  // start with, so a wrap of the counter skips it.  A run whose launch fails
-  // still uses up its number: no flag can hold it.
-  if (++h->run_no == 0) h->run_no = 1;
-  d.run = h->run_no;
-  d.spin = h->spin;
+  d.run = c.run;
+  d.spin = c.spin;
   const int row = int(dd.Hckv + dd.Dr);
   d.qs = dd.concat ? row : d.Hckv;
   d.qrs = dd.concat ? row : d.Dr;
@@ -3593,27 +3623,21 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   p.qsc_cq = static_cast<const uint16_t*>(t->quant_scale_cq);
   p.qo_cq = t->quant_offset_cq;
   p.q_scale = t->dequant_scale_q_nope;
-  p.part = h->ws + h->lay.part;
-  p.cq = h->ws + h->lay.cq;
-  p.cq_scale = reinterpret_cast<float*>(h->ws + h->lay.cq_scale);
-  p.qc = reinterpret_cast<uint16_t*>(h->ws + h->lay.qc);
-  p.xq = h->ws + h->lay.xq;
-  p.xflag = reinterpret_cast<uint32_t*>(h->ws + h->lay.xflag);
-  p.xmax = reinterpret_cast<float*>(h->ws + h->lay.xmax);
-  p.fpart = reinterpret_cast<uint32_t*>(h->ws + h->lay.fpart);
-  p.fss = reinterpret_cast<uint32_t*>(h->ws + h->lay.fss);
-  p.fykr = reinterpret_cast<float*>(h->ws + h->lay.fykr);
-  p.fcnt = reinterpret_cast<uint32_t*>(h->ws + h->lay.fcnt);
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  p.part = ws + lay.part;
+  p.cq = ws + lay.cq;
+  p.cq_scale = reinterpret_cast<float*>(ws + lay.cq_scale);
+  p.qc = reinterpret_cast<uint16_t*>(ws + lay.qc);
+  p.xq = ws + lay.xq;
+  p.xflag = reinterpret_cast<uint32_t*>(ws + lay.xflag);
+  p.xmax = reinterpret_cast<float*>(ws + lay.xmax);
+  p.fpart = reinterpret_cast<uint32_t*>(ws + lay.fpart);
+  p.fss = reinterpret_cast<uint32_t*>(ws + lay.fss);
+  p.fykr = reinterpret_cast<float*>(ws + lay.fykr);
+  p.fcnt = reinterpret_cast<uint32_t*>(ws + lay.fcnt);
 
-  hipEvent_t* ev = nullptr;
-  uint8_t* fused = nullptr;
-  if (h->events) {
-    ev = h->events + (h->recorded % kProfileRing) * kProfileEvents;
-    fused = h->fused + (h->recorded % kProfileRing);
-    *fused = 0;
-    ++h->recorded;
-  }
+  hipEvent_t* const ev = c.ev;
+  uint8_t* const fused = c.mark_kind;
+  if (fused) *fused = 0;
   // mark(i): event i (after kernel i); mark(-1): the last event of a run
   // whose up_proj and uk were one kernel; mark(-2): the last event of a run
   // that was one kernel
@@ -3632,27 +3656,25 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
     xq.beta = static_cast<const uint16_t*>(t->beta_x);
     xq.scale = static_cast<const uint16_t*>(t->quant_scale_x);
     xq.offset = t->quant_offset_x;
-    xq.out = h->ws + h->lay.x8;
+    xq.out = ws + lay.x8;
     xq.T = d.T; xq.He = d.He; xq.eps = dd.eps_x;
     k0_xquant<<<dim3(unsigned(T)), kXqThreads, 0, s>>>(xq);
     p.x = xq.out;
   }
   p.packed = static_cast<const uint8_t*>(t->packed_weights);
   FusedGeo fg;
-  if (p.packed && pl.stream && h->fused_fit[pl.mt1 == 1 ? 0 : 1] && fused_geo(dd, &fg)) {
+  if (p.packed && pl.stream && c.fused_ok && fused_geo(dd, &fg)) {
     const PackGeo g = geo_of(dd);
     if (pl.mt1 == 1) k_fused<1><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g, fg);
     else k_fused<2><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g, fg);
     mark(-2);
     const hipError_t e = hipGetLastError();
-    if (prev != dd.device) (void)hipSetDevice(prev);
     return e == hipSuccess ? MLA_OK : MLA_ERR_RUNTIME;
   }
   if (p.packed && (!pl.stream || packed_fits(dd))) {
-    if (pl.stream) launch_packed(pl, s, d, p, dd, q8, mark);
+    if (pl.stream) launch_packed(pl, s, d, p, dd, q8, c.pair_ok, mark);
     else launch_tiled(s, d, p, dd, q8, mark);
     const hipError_t e = hipGetLastError();
-    if (prev != dd.device) (void)hipSetDevice(prev);
     return e == hipSuccess ? MLA_OK : MLA_ERR_RUNTIME;
   }
   const int tiles_q = ceil_div(d.Hcq, 64);
@@ -3679,8 +3701,125 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   mark(4);
 
   const hipError_t e = hipGetLastError();
-  if (prev != dd.device) (void)hipSetDevice(prev);
   return e == hipSuccess ? MLA_OK : MLA_ERR_RUNTIME;
+}
+
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T, void* stream) {
+  if (!h) return MLA_ERR_NULLPTR;
+  const mla_prolog_desc& dd = h->desc;
+  mla_status st = check_tensors(&dd, t, T);
+  if (st != MLA_OK) return st;
+  if (T == 0) return MLA_OK;
+  int prev = 0;
+  if (hipGetDevice(&prev) != hipSuccess) return MLA_ERR_RUNTIME;
+  if (prev != dd.device && hipSetDevice(dd.device) != hipSuccess) return MLA_ERR_RUNTIME;
+  (void)hipGetLastError();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dd.check_index && dd.block_num > 0) {
+    // the debugging check of cacheIndex: every entry in [0, slots)
+    st = check_cache_index(t->cache_index, T, dd.block_num * dd.block_size, s);
+    if (st != MLA_OK) {
+      if (prev != dd.device) (void)hipSetDevice(prev);
+      return st;
+    }
+  }
+  RunCtx c;
+  c.dd = &dd;
+  c.lay = &h->lay;
+  c.ws = h->ws;
+  c.fused_ok = h->fused_fit[T <= 16 ? 0 : 1];
+  c.pair_ok = true;
+  // run numbers 1, 2, ...: 0 is what the flags and tags of the workspace
+  // start with, so a wrap of the counter skips it.  A run whose launch fails
+  // still uses up its number: no flag can hold it.
+  if (++h->run_no == 0) h->run_no = 1;
+  c.run = h->run_no;
+  c.spin = h->spin;
+  c.ev = nullptr;
+  c.mark_kind = nullptr;
+  if (h->events) {
+    c.ev = h->events + (h->recorded % kProfileRing) * kProfileEvents;
+    c.mark_kind = h->fused + (h->recorded % kProfileRing);
+    ++h->recorded;
+  }
+  st = enqueue(c, t, T, s);
+  if (prev != dd.device) (void)hipSetDevice(prev);
+  return st;
+}
+
+}  // extern "C"
+
+namespace {
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mutex;
+uint8_t* g_scratch[kScratchDevices];   // device address of scratch per device, once looked up
+
+// The device address of `scratch` on the current device `dev` (looked up on
+// the first call on that device), or NULL if the lookup fails.
+uint8_t* scratch_on(int dev) {
+  if (dev < 0 || dev >= kScratchDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch[dev] = static_cast<uint8_t*>(ptr);
+  }
+  return g_scratch[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_prolog_run_noalloc(const mla_prolog_desc* desc, const mla_prolog_tensors* t, int64_t T,
+                                  void* stream) {
+  mla_status st = check_desc_core(desc);
+  if (st != MLA_OK) return st;
+  st = check_tensors(desc, t, T);
+  if (st != MLA_OK) return st;
+  // the debugging check of cacheIndex needs a host buffer and a wait
+  if (desc->check_index) return MLA_ERR_PARAM_INVALID;
+  if (T == 0) return MLA_OK;
+  // the workspace of this run alone (no regions of the kernels that hand
+  // data across blocks) must fit the scratch array
+  mla_prolog_desc dT = *desc;
+  dT.max_tokens = T;
+  const Layout L = layout(dT, part_rows_at(dT, T), false);
+  if (L.total > kScratchBytes) return MLA_ERR_PARAM_INVALID;
+  if (L.cq - L.part >= size_t(kOOB)) return MLA_ERR_UNSUPPORTED;
+  int prev = 0;
+  if (hipGetDevice(&prev) != hipSuccess) return MLA_ERR_RUNTIME;
+  if (prev != desc->device && hipSetDevice(desc->device) != hipSuccess) return MLA_ERR_RUNTIME;
+  (void)hipGetLastError();
+  uint8_t* const ws = scratch_on(desc->device);
+  if (!ws) {
+    if (prev != desc->device) (void)hipSetDevice(prev);
+    return MLA_ERR_RUNTIME;
+  }
+  // only kernels that read what earlier kernels of the stream wrote: nothing
+  // in the array has to start at zero, and what an earlier call left there
+  // is overwritten before it is read
+  RunCtx c;
+  c.dd = desc;
+  c.lay = &L;
+  c.ws = ws;
+  c.fused_ok = c.pair_ok = false;
+  c.run = 0;
+  c.spin = 0;
+  c.ev = nullptr;
+  c.mark_kind = nullptr;
+  st = enqueue(c, t, T, static_cast<hipStream_t>(stream));
+  if (prev != desc->device) (void)hipSetDevice(prev);
+  return st;
 }
 
 static void destroy_events(mla_prolog* h) {

@@ -300,6 +300,32 @@ mla_status mla_prolog_create(const mla_prolog_desc* desc, mla_prolog_t* out);
 mla_status mla_prolog_run(mla_prolog_t handle, const mla_prolog_tensors* tensors, int64_t T,
                           void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): one
+ * prolog as mla_prolog_run, with no handle.  Its workspace is a static
+ * array of the library, 64 MiB on each device (held from the library's
+ * first use on that device until the process ends); the call allocates
+ * nothing, also no host memory, and never waits for the device.
+ *   desc, tensors, T, stream: as for mla_prolog_validate and
+ *     mla_prolog_run (T <= desc->max_tokens); packed_weights, when given,
+ *     come from mla_prolog_pack_weights of a handle with the same
+ *     description.  desc->check_index must be 0.
+ *   Returns the validation codes of mla_prolog_validate;
+ *     MLA_ERR_PARAM_INVALID also when the run's workspace would exceed the
+ *     64 MiB (at the model shapes of the prolog page's samples, He 7168,
+ *     Hcq 1536, Hckv 512, N 128, D 128, Dr 64: up to about 400 tokens) or
+ *     check_index is set; MLA_ERR_RUNTIME if the array's device address
+ *     cannot be had or a launch fails.  Nothing is enqueued on an error.
+ * Small token counts take the kernels that hand no data across blocks (the
+ * ones mla_prolog_run takes with MLA_PROLOG_FUSED=0 and no paired blocks),
+ * so runs are not faster than mla_prolog_run's.  Every call on a device
+ * shares its one array: calls that overlap on one device (on different
+ * streams, or from different threads without ordering) race and give wrong
+ * results; calls ordered on one stream are safe.  Nothing in the array has
+ * to start at zero: each call writes what it reads. */
+mla_status mla_prolog_run_noalloc(const mla_prolog_desc* desc, const mla_prolog_tensors* tensors, int64_t T,
+                                  void* stream);
+
 /* Frees the workspace and the handle (after synchronising its device): the
  * teardown that follows the page's sample call sequence (releasing the
  * workspace and the executor).  MLA_ERR_NULLPTR for a NULL handle,

@@ -287,3 +287,17 @@ def test_bad_poll_limit_is_refused(value, monkeypatch):
 
 def test_poll_limit_setter_needs_a_handle():
     assert mla.lib().mla_prolog_set_poll_limit(None, 5) == mla.MLA_ERR_NULLPTR
+
+
+def test_noalloc_refuses_what_it_cannot_take():
+    # host-side refusals come before any device call: a workspace beyond the
+    # 64 MiB array, the debugging check of cacheIndex, the usual validation
+    L = mla.lib()
+    t = mla.make_tensors(fake_tensors())
+    big = model_desc(max_tokens=4096)
+    assert L.mla_prolog_run_noalloc(ctypes.byref(big), ctypes.byref(t), 4096, None) == mla.MLA_ERR_PARAM_INVALID
+    chk = model_desc(check_index=1)
+    assert L.mla_prolog_run_noalloc(ctypes.byref(chk), ctypes.byref(t), 32, None) == mla.MLA_ERR_PARAM_INVALID
+    assert L.mla_prolog_run_noalloc(ctypes.byref(model_desc()), ctypes.byref(t), 257, None) == mla.MLA_ERR_PARAM_INVALID
+    assert L.mla_prolog_run_noalloc(ctypes.byref(model_desc()), None, 32, None) == mla.MLA_ERR_NULLPTR
+    assert L.mla_prolog_run_noalloc(ctypes.byref(model_desc()), ctypes.byref(t), 0, None) == mla.MLA_OK
