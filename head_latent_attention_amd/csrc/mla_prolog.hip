@@ -2768,6 +2768,179 @@ __global__ __launch_bounds__(64 * WM * WN) void k3_tiled(Dims d, Ptrs p, PackGeo
 // taken across the WN waves of a token range.
 // HF: heads vary fastest along the grid, so blocks running together write
 // neighbouring heads of the same tokens (one contiguous q^N row per token).
+// K3r: the medium-T up-projection (up to 16*8*MT tokens) for heads of two
+// nope windows and Dr = 64, one block per (head, half) as in k34_pair: the
+// block's 96 weight columns are nope window `half` and rope column tiles
+// half and half + 2, whose RoPE pairs (i, i + Dr/2) are then all in the
+// block.  Every weight byte is read from HBM once.  Wave w owns the token
+// tiles w, w + 8, ... and all 96 columns.
+//
+// The k-stages stream through a register ring R entries deep; entry i holds
+// an eighth of the weights of stage i + 2 (each wave loads 768 bytes) and
+// the wave's own activation tiles of stage i (fragment-packed c^Q, 1 KB per
+// 16 tokens), so every load of an entry is issued together and used at the
+// same step, and a wave's in-order load completion never holds a later
+// stage behind an earlier one.  The weights pass through three LDS slots:
+// at step i a wave writes its piece of stage i + 2, reads the six weight
+// fragments of stage i + 1 ahead, runs the MFMAs of stage i (weights read at
+// the previous step, activations from the ring), refills the entry with
+// stage i + R, and meets the block at one barrier.  The fragment reads of
+// one stage so overlap the MFMAs of the one before.
+// Epilogue: nope columns -> q^C (bf16, fragment-packed for the W^UK
+// product, its k padding as zeros), rope columns -> RoPE -> queryRopeOut;
+// with int8 operands each value is first dequantised (udq).
+template <bool I8, int MT, int R, int NSTMAX>
+__global__ __launch_bounds__(512) void k3_ring(Dims d, Ptrs p, PackGeo pg) {
+  using St = Stage<I8>;
+  using Acc = typename St::Acc;
+  using Frag = typename St::Frag;
+  constexpr int NW = 8;
+  constexpr int WB = 6 * 1024;                    // weight bytes of a stage
+  __shared__ __attribute__((aligned(16))) uint8_t lds[3 * WB];
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int b = blockIdx.x;
+  // a head's two blocks are 8 apart, so they run on the same XCD
+  const int h = d.N % 8 == 0 ? (b / 16) * 8 + b % 8 : b / 2;
+  const int half = d.N % 8 == 0 ? (b / 8) % 2 : b % 2;
+  const int P = pg.nope_w, DDr = d.D + d.Dr, nst = pg.nst_cq;
+  const int nt = (d.T + 15) / 16;
+  const rsrc_t Wp = make_rsrc(p.packed, pg.total);
+  const int64_t ctile = int64_t(nst) * 1024;
+  const rsrc_t Cq = make_rsrc(p.cq, int64_t(nt) * ctile);
+  const uint32_t nb = uint32_t(pg.off_uq + int64_t(h * (P + 1) + half) * nst * 4096);
+  const uint32_t rb = uint32_t(pg.off_uq + int64_t(h * (P + 1) + P) * nst * 4096);
+  // A stage's 6 KB of weights, in LDS order: the nope window's 4 KB, then
+  // rope tiles half and half + 2.  Wave w loads bytes 768 w .. 768 w + 767
+  // (lanes 0..47), one 16-byte piece per lane, each within one tile.
+  const int wbyte = 768 * w + 16 * lane;
+  const bool wl = lane < 48;
+  const uint32_t wseg = wbyte < 4096   ? nb + uint32_t(wbyte)
+                        : wbyte < 5120 ? rb + uint32_t(half * 1024 + wbyte - 4096)
+                                       : rb + uint32_t((half + 2) * 1024 + wbyte - 5120);
+  auto wload = [&](int st) { return bload16s(Wp, st < nst && wl ? wseg + uint32_t(st) * 4096u : kOOB); };
+  auto aload = [&](int st, int m) {
+    return bload16(Cq, st < nst && w + NW * m < nt
+                           ? uint32_t((w + NW * m) * ctile) + uint32_t(st) * 1024u + uint32_t(lane * 16)
+                           : kOOB);
+  };
+  auto lwrite = [&](int st, const uint4& v) {
+    if (wl) *reinterpret_cast<uint4*>(lds + (st % 3) * WB + wbyte) = v;
+  };
+  auto lread = [&](int st, Frag (&f)[6]) {
+#pragma unroll
+    for (int j = 0; j < 6; ++j) f[j] = *reinterpret_cast<const Frag*>(lds + (st % 3) * WB + j * 1024 + lane * 16);
+  };
+  auto barrier = [] {
+    // orders LDS only: the loads in flight are not waited for
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
+  // stages 0 and 1 of the weights go to LDS first; then entries 0 .. R-1
+  uint4 rw[R], ra[R][MT];
+  {
+    const uint4 w0 = wload(0), w1 = wload(1);
+    lwrite(0, w0);
+    lwrite(1, w1);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < R; ++q) {
+    rw[q] = wload(q + 2);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) ra[q][m] = aload(q, m);
+  }
+  barrier();
+  Frag bf[6], bfn[6];
+  lread(0, bf);
+  Acc acc[MT][6];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < 6; ++j) acc[mt][j] = Acc{0, 0, 0, 0};
+  // all NSTMAX stages, unrolled, with no exit: stages past nst load zeros
+  // (an exact no-op).  At a loop head the wait counts of the ring's
+  // registers would merge and the ring drain once a round; an early exit
+  // lets the compiler sink each load to its use, which drains it at every
+  // stage.
+#pragma unroll
+  for (int st = 0; st < NSTMAX; ++st) {
+    const int q = st % R;
+    lwrite(st + 2, rw[q]);
+    if (st + 1 < NSTMAX) lread(st + 1, bfn);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const Frag af = __builtin_bit_cast(Frag, ra[q][mt]);
+#pragma unroll
+      for (int j = 0; j < 6; ++j) acc[mt][j] = mfma(bf[j], af, acc[mt][j]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    rw[q] = wload(st + 2 + R);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) ra[q][m] = aload(st + R, m);
+    barrier();
+#pragma unroll
+    for (int j = 0; j < 6; ++j) bf[j] = bfn[j];
+  }
+
+  // lane: token 16 (w + 8 mt) + c, columns 16 j + 4 g + r of the block's
+  // tiles (j < 4: nope window `half`; j = 4, 5: rope tiles half, half + 2)
+  const int hf = d.Dr / 2;
+  const int64_t qtile = int64_t(d.N) * pg.nst_d * 1024;
+  uint8_t* const qcb = reinterpret_cast<uint8_t*>(p.qc) + int64_t(h) * pg.nst_d * 1024;
+  const int wq = min(64, 32 * pg.nst_d - 64 * half);   // q^C columns of this window, with the k padding
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int t = 16 * (w + NW * mt) + c;
+    if (t >= d.T) continue;
+    // q^C
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = 16 * j + 4 * g;   // in the window
+      if (col >= wq) continue;
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (I8)
+          v[r] = 64 * half + col + r < d.D ? udq(p, acc[mt][j][r], t, h * DDr + 64 * half + col + r) : 0.0f;
+        else
+          v[r] = acc[mt][j][r];
+      }
+      *reinterpret_cast<uint2*>(qcb + packed_offset(t, 64 * half + col, qtile, false)) =
+          pack_bf16x4(v[0], v[1], v[2], v[3]);
+    }
+    // q^R: pairs (i0 + r, i0 + r + Dr/2)
+    const int i0 = 16 * half + 4 * g;
+    const uint2 c0 = *reinterpret_cast<const uint2*>(p.cos + int64_t(t) * d.Dr + i0);
+    const uint2 c1 = *reinterpret_cast<const uint2*>(p.cos + int64_t(t) * d.Dr + i0 + hf);
+    const uint2 s0v = *reinterpret_cast<const uint2*>(p.sin + int64_t(t) * d.Dr + i0);
+    const uint2 s1v = *reinterpret_cast<const uint2*>(p.sin + int64_t(t) * d.Dr + i0 + hf);
+    const uint16_t* cs0 = reinterpret_cast<const uint16_t*>(&c0);
+    const uint16_t* cs1 = reinterpret_cast<const uint16_t*>(&c1);
+    const uint16_t* sn0 = reinterpret_cast<const uint16_t*>(&s0v);
+    const uint16_t* sn1 = reinterpret_cast<const uint16_t*>(&s1v);
+    float o0[4], o1[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float a, bb;
+      if constexpr (I8) {
+        a = udq(p, acc[mt][4][r], t, h * DDr + d.D + i0 + r);
+        bb = udq(p, acc[mt][5][r], t, h * DDr + d.D + i0 + hf + r);
+      } else {
+        a = acc[mt][4][r];
+        bb = acc[mt][5][r];
+      }
+      o0[r] = a * bf2f(cs0[r]) - bb * bf2f(sn0[r]);
+      o1[r] = bb * bf2f(cs1[r]) + a * bf2f(sn1[r]);
+    }
+    uint16_t* o = p.qr_out + (int64_t(t) * d.N + h) * d.qrs + i0;
+    *reinterpret_cast<uint2*>(o) = pack_bf16x4(o0[0], o0[1], o0[2], o0[3]);
+    *reinterpret_cast<uint2*>(o + hf) = pack_bf16x4(o1[0], o1[1], o1[2], o1[3]);
+  }
+}
+
 template <int MT, int NWW, int WM, int WN, int D, bool Q8, bool LC = false, bool HF = false>
 __global__ __launch_bounds__(64 * WM * WN) void k4_tiled(Dims d, Ptrs p, PackGeo pg, int mtiles,
                                                       int cgroups) {
@@ -2976,10 +3149,15 @@ Plan make_plan(const mla_prolog_desc& d, int64_t T) {
 // 16*mt tokens.  The int8-query K4 always takes 64 tokens x the whole Hckv
 // row per block.
 constexpr int kTiledLargeT = 2048;
+constexpr bool kRingK3 = true;
+// K3r instances unroll 8, 24 or 48 k-stages of Hcq (the smallest that holds
+// the shape's; 48 is Hcq 1536 in bf16, 24 Hcq 1536 in int8)
+constexpr int kRingStages = 48;
 constexpr int kTiledK1Blocks = 512;   // medium: one-wave blocks
 
 struct TiledPlan {
   bool large;
+  bool ring;               // medium up-projection on K3r (heads of two nope windows, Dr = 64, T <= 256)
   int mt;                  // medium: 16-token tiles per K4 wave (and per direct K1 wave)
   int k1v, k3v;            // medium kernel shapes: 0 direct, 1 LDS-staged 256-token, 2 LDS-staged 128-token
   int m1, ngrp1, S, sps;   // K1: token tiles, window groups, splits, stages per split
@@ -2993,6 +3171,7 @@ TiledPlan tiled_plan(const mla_prolog_desc& d, int64_t T) {
   const PackGeo g = geo_of(d);
   const int tiles = g.win_dq + g.win_kr;
   tp.large = T >= kTiledLargeT;
+  tp.ring = !tp.large && T <= 256 && g.nope_w == 2 && d.Dr == 64 && g.nst_cq <= kRingStages && kRingK3;
   tp.mt = T <= 64 ? 4 : 8;
   // medium shapes: LDS-staged blocks above 128 tokens; for an int8 product
   // also from 65 tokens on, in 128-token blocks (the int8 k-stages are twice
@@ -3389,9 +3568,24 @@ void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs&
   mark(1);
   launch_norm<I8D, I8U>(s, d, p, tp.S, g.nst_cq);
   mark(2);
-  if (tp.k3v == 1) k3_tiled<I8U, 2, 1, 8, 2, 2, true, 1, true><<<g3, 1024, 0, s>>>(d, p, g, tp.m3);
-  else if (I8U && tp.k3v == 2) k3_tiled<I8U, 1, 1, 8, 2, 2, true, 1, true><<<g3, 1024, 0, s>>>(d, p, g, tp.m3);
-  else k3_tiled<I8U, 4, 1, 1, 1, 2><<<g3, 64, 0, s>>>(d, p, g, tp.m3);
+  if (tp.ring) {
+    const dim3 gr(2 * d.N);
+    if (d.T <= 128) {
+      if (g.nst_cq <= 8) k3_ring<I8U, 1, 4, 8><<<gr, 512, 0, s>>>(d, p, g);
+      else if (g.nst_cq <= 24) k3_ring<I8U, 1, 4, 24><<<gr, 512, 0, s>>>(d, p, g);
+      else k3_ring<I8U, 1, 4, 48><<<gr, 512, 0, s>>>(d, p, g);
+    } else {
+      if (g.nst_cq <= 8) k3_ring<I8U, 2, 4, 8><<<gr, 512, 0, s>>>(d, p, g);
+      else if (g.nst_cq <= 24) k3_ring<I8U, 2, 4, 24><<<gr, 512, 0, s>>>(d, p, g);
+      else k3_ring<I8U, 2, 4, 48><<<gr, 512, 0, s>>>(d, p, g);
+    }
+  } else if (tp.k3v == 1) {
+    k3_tiled<I8U, 2, 1, 8, 2, 2, true, 1, true><<<g3, 1024, 0, s>>>(d, p, g, tp.m3);
+  } else if (I8U && tp.k3v == 2) {
+    k3_tiled<I8U, 1, 1, 8, 2, 2, true, 1, true><<<g3, 1024, 0, s>>>(d, p, g, tp.m3);
+  } else {
+    k3_tiled<I8U, 4, 1, 1, 1, 2><<<g3, 64, 0, s>>>(d, p, g, tp.m3);
+  }
   mark(3);
   if (q8) k4_tiled<4, 1, 1, 8, 2, true, false, true><<<dim3(tp.m4q * d.N), 512, 0, s>>>(d, p, g, tp.m4q, 1);
   else k4_tiled<MT, 1, 1, 8, 2, false, false, true><<<dim3(tp.m4 * tp.cg4 * d.N), 512, 0, s>>>(d, p, g, tp.m4,

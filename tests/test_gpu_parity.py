@@ -461,6 +461,24 @@ def test_full_size_tiled_packed(name):
     full_check(inp, rows=check_rows(inp), packed=True)
 
 
+# ---- the medium-T up-projection in (head, half) blocks (two nope windows,
+# Dr = 64): D = 96 leaves the second nope window half empty, N = 3 takes the
+# other block-to-head mapping, 33 / 128 / 129 / 256 tokens the ends of its
+# two token-tile counts
+RING_DIMS = {"n3_d96": Dims(He=512, Hcq=192, Hckv=128, N=3, D=96, Dr=64),
+             "n8_d128": Dims(He=256, Hcq=128, Hckv=320, N=8, D=128, Dr=64)}
+
+
+@pytest.mark.parametrize("T", [33, 128, 129, 256])
+@pytest.mark.parametrize("dims", list(RING_DIMS))
+@pytest.mark.parametrize("mode", ["bf16", "int8", "partial"])
+def test_ring_up_projection_packed(mode, dims, T):
+    wl = custom_workload(f"ring_{mode}_{dims}_t{T}", T=T, dims=RING_DIMS[dims], block_num=(T + 15) // 16 + 1,
+                         block_size=16, quant=mode == "int8", partial=mode == "partial",
+                         smooth=mode == "partial", seed=130 + T)
+    full_check(synth.make_inputs(wl), packed=True, repeat=2, prerun_negated=True)
+
+
 # ---- the token counts where the launch shapes change --------------------------
 BOUNDARY_DIMS = Dims(He=512, Hcq=128, Hckv=64, N=2, D=32, Dr=16)
 
