@@ -308,6 +308,7 @@ struct Ptrs {
   uint8_t* xq;       // [N] q^C exchange of the paired small-T kernel, kPairXq bytes a head
   uint32_t* xflag;   // [N][4] its exchange flags (run numbers), then one error word
   float* xmax;       // [N][2][32] its per-token row maxima
+  float* xmax2;      // [N][2][kRingMaxT]: the medium-T fused kernel's per-token row maxima
   uint32_t* fpart;   // fused kernel: [phase-1 blocks][32][64] (fp32 split partial, run tag) words
   uint32_t* fss;     // fused kernel: [windows][32] (fp32 sum of squares, run tag) words
   float* fykr;       // fused kernel: [32][Hckv + Dr] y of the c^KV and k^R columns
@@ -2786,17 +2787,36 @@ __global__ __launch_bounds__(64 * WM * WN) void k3_tiled(Dims d, Ptrs p, PackGeo
 // the previous step, activations from the ring), refills the entry with
 // stage i + R, and meets the block at one barrier.  The fragment reads of
 // one stage so overlap the MFMAs of the one before.
-// Epilogue: nope columns -> q^C (bf16, fragment-packed for the W^UK
-// product, its k padding as zeros), rope columns -> RoPE -> queryRopeOut;
-// with int8 operands each value is first dequantised (udq).
-template <bool I8, int MT, int R, int NSTMAX>
+//
+// Epilogue: rope columns -> RoPE -> queryRopeOut; nope columns -> q^C (bf16;
+// with int8 operands each value is first dequantised, udq).  Without UK, q^C
+// goes to the workspace, fragment-packed for the W^UK kernel.  With UK (the
+// W^UK product in the same launch, as in k34_pair): the block's half of the
+// W^UK columns (the windows of its half of Hckv, at most 64 KB) is loaded
+// into registers during the stream and parked in LDS; each block writes its
+// q^C half to the workspace with agent-scope stores and to LDS, raises its
+// flag (the run's number), waits for the partner's, and multiplies both
+// halves with the parked W^UK fragments: q^N for its tokens and columns, in
+// bf16, or in int8 with the per-(token, head) row maxima traded through the
+// workspace and a second flag.
+constexpr int kRingMaxT = 256;   // K3r: tokens a block holds at most (8 waves x 2 tiles of 16)
+
+template <bool I8, int MT, int R, int NSTMAX, bool UK, bool Q8>
 __global__ __launch_bounds__(512) void k3_ring(Dims d, Ptrs p, PackGeo pg) {
   using St = Stage<I8>;
   using Acc = typename St::Acc;
   using Frag = typename St::Frag;
-  constexpr int NW = 8;
+  constexpr int NW = 8, NTM = NW * MT;
   constexpr int WB = 6 * 1024;                    // weight bytes of a stage
-  __shared__ __attribute__((aligned(16))) uint8_t lds[3 * WB];
+  constexpr int UKB = UK ? 64 * 1024 : 0;         // parked W^UK: 4 windows x 4 stages x 4 KB
+  constexpr int QCB = UK ? NTM * 2048 : 0;        // own q^C half: 2 D-stages per token tile
+  __shared__ __attribute__((aligned(16))) uint8_t lds[3 * WB + UKB + QCB];
+  // int8 operands: the dequantisation scale (and static bias) of each of the
+  // block's 96 columns, loaded once at the start
+  __shared__ float swl[I8 ? 96 : 1];
+  __shared__ int32_t bsl[I8 ? 96 : 1];
+  uint8_t* const ukl = lds + 3 * WB;
+  uint8_t* const qcl = lds + 3 * WB + UKB;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, c = lane & 15;
   const int b = blockIdx.x;
@@ -2837,7 +2857,40 @@ __global__ __launch_bounds__(512) void k3_ring(Dims d, Ptrs p, PackGeo pg) {
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   };
-  // stages 0 and 1 of the weights go to LDS first; then entries 0 .. R-1
+  // this half's W^UK windows jlo .. jhi-1 (at most four), in LDS as chunk
+  // (window - jlo) * 16 + stage * 4 + column tile, 1 KB each; wave w loads
+  // chunks w, w + 8, ..
+  const int ja = (pg.uk_w + 1) / 2, jlo = half ? ja : 0, jhi = half ? pg.uk_w : ja;
+  uint4 ukr[UK ? 8 : 1];
+  auto ukload = [&] {
+#pragma unroll
+    for (int i = 0; i < (UK ? 8 : 0); ++i) {
+      const int ch = w + NW * i, jj = ch >> 4, s = (ch >> 2) & 3, ct = ch & 3;
+      const bool ok = jlo + jj < jhi && s < pg.nst_d;
+      ukr[i] = bload16s(Wp, ok ? uint32_t(pg.off_uk + int64_t(h * pg.uk_w + jlo + jj) * pg.nst_d * 4096) +
+                                     uint32_t(s * 4096 + ct * 1024 + lane * 16)
+                               : kOOB);
+    }
+  };
+  // block column k: k < 64 nope column 64 half + k; 64..79 rope column
+  // 16 half + k - 64; 80..95 rope column Dr/2 + 16 half + k - 80
+  auto wcol = [&](int k) {
+    return h * DDr + (k < 64 ? 64 * half + k : d.D + (k < 80 ? 16 * half + k - 64 : d.Dr / 2 + 16 * half + k - 80));
+  };
+  // (loaded before the stream starts, stored to LDS once the first loads
+  // of the stream are out)
+  float swv = 0.0f;
+  int32_t bsv = 0;
+  if constexpr (I8) {
+    const int k = threadIdx.x < 96 ? threadIdx.x : 0, n = wcol(k);
+    const bool ok = threadIdx.x < 96 && (k >= 64 || 64 * half + k < d.D);
+    const rsrc_t Sw = make_rsrc(p.sw_uq_qr, int64_t(d.N) * DDr * 4);
+    const rsrc_t Bs = make_rsrc(p.bias_uq, p.bias_uq ? int64_t(d.N) * DDr * 4 : 0);
+    swv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(Sw, ok ? uint32_t(n) * 4u : kOOB, 0, 0));
+    bsv = __builtin_bit_cast(int32_t, __builtin_amdgcn_raw_buffer_load_b32(Bs, ok ? uint32_t(n) * 4u : kOOB, 0, 0));
+  }
+  // stages 0 and 1 of the weights go to LDS first; then entries 0 .. R-1,
+  // then the W^UK fragments (used only after the stream)
   uint4 rw[R], ra[R][MT];
   {
     const uint4 w0 = wload(0), w1 = wload(1);
@@ -2850,6 +2903,14 @@ __global__ __launch_bounds__(512) void k3_ring(Dims d, Ptrs p, PackGeo pg) {
     rw[q] = wload(q + 2);
 #pragma unroll
     for (int m = 0; m < MT; ++m) ra[q][m] = aload(q, m);
+  }
+  ukload();
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (I8) {
+    if (threadIdx.x < 96) {
+      swl[threadIdx.x] = swv;
+      bsl[threadIdx.x] = bsv;
+    }
   }
   barrier();
   Frag bf[6], bfn[6];
@@ -2884,60 +2945,201 @@ __global__ __launch_bounds__(512) void k3_ring(Dims d, Ptrs p, PackGeo pg) {
 #pragma unroll
     for (int j = 0; j < 6; ++j) bf[j] = bfn[j];
   }
+  // the epilogue's per-token values, loaded now so that they arrive while
+  // q^C is formed and traded: the lane's cos/sin pieces and c^Q's scale
+  const int hf = d.Dr / 2, i0 = 16 * half + 4 * g;
+  uint2 cs[MT][4];
+  float csc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int t = 16 * (w + NW * mt) + c;
+    const int64_t ro = int64_t(t < d.T ? t : 0) * d.Dr;
+    cs[mt][0] = *reinterpret_cast<const uint2*>(p.cos + ro + i0);
+    cs[mt][1] = *reinterpret_cast<const uint2*>(p.cos + ro + i0 + hf);
+    cs[mt][2] = *reinterpret_cast<const uint2*>(p.sin + ro + i0);
+    cs[mt][3] = *reinterpret_cast<const uint2*>(p.sin + ro + i0 + hf);
+    csc[mt] = I8 ? p.cq_scale[t < d.T ? t : 0] : 1.0f;
+  }
+  if constexpr (UK) {
+    // park the W^UK fragments
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(ukl + (w + NW * i) * 1024 + lane * 16) = ukr[i];
+  }
+  // u of block column k from its accumulator: (acc + bias) s_cq s_w in fp32,
+  // as udq
+  auto dq = [&](auto a, int mt, int k) -> float {
+    if constexpr (I8) return static_cast<float>(a + bsl[k]) * csc[mt] * swl[k];
+    else return a;
+  };
 
   // lane: token 16 (w + 8 mt) + c, columns 16 j + 4 g + r of the block's
   // tiles (j < 4: nope window `half`; j = 4, 5: rope tiles half, half + 2)
-  const int hf = d.Dr / 2;
   const int64_t qtile = int64_t(d.N) * pg.nst_d * 1024;
   uint8_t* const qcb = reinterpret_cast<uint8_t*>(p.qc) + int64_t(h) * pg.nst_d * 1024;
   const int wq = min(64, 32 * pg.nst_d - 64 * half);   // q^C columns of this window, with the k padding
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int t = 16 * (w + NW * mt) + c;
-    if (t >= d.T) continue;
-    // q^C
+    const int tt = w + NW * mt, t = 16 * tt + c;
+    // q^C (for a token past T: zeros into the LDS copy only)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int col = 16 * j + 4 * g;   // in the window
       if (col >= wq) continue;
       float v[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if constexpr (I8)
-          v[r] = 64 * half + col + r < d.D ? udq(p, acc[mt][j][r], t, h * DDr + 64 * half + col + r) : 0.0f;
-        else
-          v[r] = acc[mt][j][r];
+      for (int r = 0; r < 4; ++r) v[r] = t < d.T ? dq(acc[mt][j][r], mt, col + r) : 0.0f;
+      const uint2 pk = pack_bf16x4(v[0], v[1], v[2], v[3]);
+      if constexpr (UK) {
+        // fragment order of the W^UK product's activation operand: stage
+        // 2 half + j / 2, lane group 2 (j % 2) + g / 2, token c
+        const int fo = (16 * (2 * (j % 2) + g / 2) + c) * 16 + 8 * (g % 2);
+        *reinterpret_cast<uint2*>(qcl + (tt * 2 + j / 2) * 1024 + fo) = pk;
+        if (t < d.T) xstore64(qcb + int64_t(tt) * qtile + (2 * half + j / 2) * 1024 + fo, pk);
+      } else {
+        if (t < d.T) *reinterpret_cast<uint2*>(qcb + packed_offset(t, 64 * half + col, qtile, false)) = pk;
       }
-      *reinterpret_cast<uint2*>(qcb + packed_offset(t, 64 * half + col, qtile, false)) =
-          pack_bf16x4(v[0], v[1], v[2], v[3]);
     }
+  }
+  if constexpr (UK) pair_publish(p.xflag + 4 * h + half, d.run);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int t = 16 * (w + NW * mt) + c;
+    if (t >= d.T) continue;
     // q^R: pairs (i0 + r, i0 + r + Dr/2)
-    const int i0 = 16 * half + 4 * g;
-    const uint2 c0 = *reinterpret_cast<const uint2*>(p.cos + int64_t(t) * d.Dr + i0);
-    const uint2 c1 = *reinterpret_cast<const uint2*>(p.cos + int64_t(t) * d.Dr + i0 + hf);
-    const uint2 s0v = *reinterpret_cast<const uint2*>(p.sin + int64_t(t) * d.Dr + i0);
-    const uint2 s1v = *reinterpret_cast<const uint2*>(p.sin + int64_t(t) * d.Dr + i0 + hf);
-    const uint16_t* cs0 = reinterpret_cast<const uint16_t*>(&c0);
-    const uint16_t* cs1 = reinterpret_cast<const uint16_t*>(&c1);
-    const uint16_t* sn0 = reinterpret_cast<const uint16_t*>(&s0v);
-    const uint16_t* sn1 = reinterpret_cast<const uint16_t*>(&s1v);
+    const uint16_t* cs0 = reinterpret_cast<const uint16_t*>(&cs[mt][0]);
+    const uint16_t* cs1 = reinterpret_cast<const uint16_t*>(&cs[mt][1]);
+    const uint16_t* sn0 = reinterpret_cast<const uint16_t*>(&cs[mt][2]);
+    const uint16_t* sn1 = reinterpret_cast<const uint16_t*>(&cs[mt][3]);
     float o0[4], o1[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float a, bb;
-      if constexpr (I8) {
-        a = udq(p, acc[mt][4][r], t, h * DDr + d.D + i0 + r);
-        bb = udq(p, acc[mt][5][r], t, h * DDr + d.D + i0 + hf + r);
-      } else {
-        a = acc[mt][4][r];
-        bb = acc[mt][5][r];
-      }
+      const float a = dq(acc[mt][4][r], mt, 64 + 4 * g + r), bb = dq(acc[mt][5][r], mt, 80 + 4 * g + r);
       o0[r] = a * bf2f(cs0[r]) - bb * bf2f(sn0[r]);
       o1[r] = bb * bf2f(cs1[r]) + a * bf2f(sn1[r]);
     }
     uint16_t* o = p.qr_out + (int64_t(t) * d.N + h) * d.qrs + i0;
     *reinterpret_cast<uint2*>(o) = pack_bf16x4(o0[0], o0[1], o0[2], o0[3]);
     *reinterpret_cast<uint2*>(o + hf) = pack_bf16x4(o1[0], o1[1], o1[2], o1[3]);
+  }
+  if constexpr (UK) {
+    // q^N = q^C W^UK[h] over this half's windows, all of D; the operand's
+    // stages 2 half, 2 half + 1 are this block's (LDS), the others the
+    // partner's (workspace)
+    pair_wait(p.xflag + 4 * h + (1 - half), p.xflag + 4 * d.N, d.run, d.spin);
+    uint4 aq[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int tt = w + NW * mt;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if (s >= pg.nst_d) {
+          aq[mt][s] = make_uint4(0, 0, 0, 0);
+        } else if (s / 2 == half) {
+          aq[mt][s] = *reinterpret_cast<const uint4*>(qcl + (tt * 2 + s % 2) * 1024 + lane * 16);
+        } else {
+          aq[mt][s] = tt < nt ? xload128(qcb + int64_t(tt) * qtile + s * 1024 + lane * 16) : make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+    constexpr int NCT = 16;   // column tiles of the half: 4 windows x 4 tiles
+    f32x4 au[MT][Q8 ? NCT : 1];
+    auto tile_mma = [&](int j, f32x4 (&o)[MT]) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) o[mt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 wf = *reinterpret_cast<const bf16x8*>(ukl + ((j >> 2) * 16 + s * 4 + (j & 3)) * 1024 + lane * 16);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) o[mt] = mfma(wf, __builtin_bit_cast(bf16x8, aq[mt][s]), o[mt]);
+      }
+    };
+    if constexpr (!Q8) {
+      // each 16-token x 64-column piece goes through the wave's tile in the
+      // (idle) ring slots, rows 144 bytes apart, and leaves as 16-byte
+      // non-temporal stores of whole 128-byte row pieces
+      uint16_t* qo = static_cast<uint16_t*>(p.q_out);
+      uint8_t* const tile = lds + w * 16 * 144;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        if (jlo + jj >= jhi) break;
+        f32x4 o[4][MT];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) tile_mma(4 * jj + ct, o[ct]);
+        const int width = min(64, d.Hckv - 64 * (jlo + jj));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct)
+            *reinterpret_cast<uint2*>(tile + c * 144 + (16 * ct + 4 * g) * 2) =
+                pack_bf16x4(o[ct][mt][0], o[ct][mt][1], o[ct][mt][2], o[ct][mt][3]);
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int k = lane + 64 * hh, row = k >> 3, col = 8 * (k & 7);
+            const int t = 16 * (w + NW * mt) + row;
+            if (t < d.T && col < width)
+              __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(tile + row * 144 + col * 2),
+                                          reinterpret_cast<u32x4*>(qo + (int64_t(t) * d.N + h) * d.qs +
+                                                                   64 * (jlo + jj) + col));
+          }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+      }
+    } else {
+      // per-token max |q^N| over this half's columns (a wave holds whole
+      // token rows), traded with the partner
+      float mx[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) mx[mt] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NCT; ++j) {
+        f32x4 o[MT];
+        tile_mma(j, o);
+        const bool on = jlo + j / 4 < jhi && 64 * jlo + 16 * j + 4 * g < d.Hckv;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          au[mt][j] = o[mt];
+          if (on)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mx[mt] = fmaxf(mx[mt], fabsf(o[mt][r]));
+        }
+      }
+      float* const xm = p.xmax2 + int64_t(h) * 2 * kRingMaxT;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        mx[mt] = fmaxf(mx[mt], __shfl_xor(mx[mt], 16, 64));
+        mx[mt] = fmaxf(mx[mt], __shfl_xor(mx[mt], 32, 64));
+        const int t = 16 * (w + NW * mt) + c;
+        if (g == 0 && t < d.T)
+          __hip_atomic_store(xm + half * kRingMaxT + t, mx[mt], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      pair_publish(p.xflag + 4 * h + 2 + half, d.run);
+      pair_wait(p.xflag + 4 * h + 2 + (1 - half), p.xflag + 4 * d.N, d.run, d.spin);
+      int8_t* qo = static_cast<int8_t*>(p.q_out);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int t = 16 * (w + NW * mt) + c;
+        if (t >= d.T) continue;
+        const float amax =
+            fmaxf(mx[mt], __hip_atomic_load(xm + (1 - half) * kRingMaxT + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        const float sc = amax / 127.0f;
+#pragma unroll
+        for (int j = 0; j < NCT; ++j) {
+          const int col = 64 * jlo + 16 * j + 4 * g;
+          if (jlo + j / 4 >= jhi || col >= d.Hckv) continue;
+          uint32_t u = 0;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            u |= uint32_t(uint8_t(sc > 0.0f ? quant_code(au[mt][j][r], sc) : 0)) << (8 * r);
+          *reinterpret_cast<uint32_t*>(qo + (int64_t(t) * d.N + h) * d.qs + col) = u;
+        }
+        if (half == 0 && g == 0) p.q_scale[int64_t(t) * d.N + h] = sc;
+      }
+    }
   }
 }
 
@@ -3204,7 +3406,7 @@ TiledPlan tiled_plan(const mla_prolog_desc& d, int64_t T) {
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t part, cq, cq_scale, qc, xq, xflag, xmax, x8, fpart, fss, fykr, fcnt, total;
+  size_t part, cq, cq_scale, qc, xq, xflag, xmax, xmax2, x8, fpart, fss, fykr, fcnt, total;
 };
 
 // split-partial rows (S * T) a run of T tokens writes, on any of its paths
@@ -3241,7 +3443,8 @@ Layout layout(const mla_prolog_desc& d, int64_t part_rows, bool small_t) {
   // squares, the c^KV / k^R rows, counters
   const size_t nwin = size_t(g.win_dq + g.win_kr);
   // the static scenario's int8 codes of x
-  L.x8 = align256(L.xmax + st * size_t(d.N) * 64 * 4);
+  L.xmax2 = align256(L.xmax + st * size_t(d.N) * 64 * 4);
+  L.x8 = align256(L.xmax2 + st * size_t(d.N) * 2 * kRingMaxT * 4);
   const size_t x8_bytes = d.in_dtype == MLA_INT8_STATIC ? size_t(d.max_tokens) * d.He : 0;
   L.fpart = align256(L.x8 + x8_bytes);
   L.fss = align256(L.fpart + st * size_t(2 * d.N) * 32 * 64 * 8);
@@ -3555,10 +3758,26 @@ void launch_packed(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p,
   else packed_launch_mt<2>(pl, s, d, p, g, down_i8(dd), up_i8(dd), q8, pair_ok, mark);
 }
 
+// K3r: 2N blocks; 16 or 32 tokens per wave; the instance unrolling the
+// fewest stages that hold Hcq's
+template <bool I8U, bool UK, bool Q8>
+void launch_ring(hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g) {
+  const dim3 gr(2 * d.N);
+  if (d.T <= 128) {
+    if (g.nst_cq <= 8) k3_ring<I8U, 1, 4, 8, UK, Q8><<<gr, 512, 0, s>>>(d, p, g);
+    else if (g.nst_cq <= 24) k3_ring<I8U, 1, 4, 24, UK, Q8><<<gr, 512, 0, s>>>(d, p, g);
+    else k3_ring<I8U, 1, 4, 48, UK, Q8><<<gr, 512, 0, s>>>(d, p, g);
+  } else {
+    if (g.nst_cq <= 8) k3_ring<I8U, 2, 4, 8, UK, Q8><<<gr, 512, 0, s>>>(d, p, g);
+    else if (g.nst_cq <= 24) k3_ring<I8U, 2, 4, 24, UK, Q8><<<gr, 512, 0, s>>>(d, p, g);
+    else k3_ring<I8U, 2, 4, 48, UK, Q8><<<gr, 512, 0, s>>>(d, p, g);
+  }
+}
+
 // Tiled run on packed weights (token counts above the streaming range).
 template <bool I8D, bool I8U, int MT, class Mark>
 void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g,
-                  bool q8, Mark& mark) {
+                  bool q8, bool pair_ok, Mark& mark) {
   const dim3 g1(tp.m1 * tp.ngrp1 * tp.S), g3(tp.m3 * tp.ngrp3);
   if (tp.k1v == 1)
     k1_tiled<I8D, 4, 1, 4, 2, 2, true, 1, true><<<g1, 512, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
@@ -3568,16 +3787,15 @@ void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs&
   mark(1);
   launch_norm<I8D, I8U>(s, d, p, tp.S, g.nst_cq);
   mark(2);
+  // with paired blocks allowed (and at most eight W^UK windows of four D
+  // stages), the W^UK product runs in the same launch
+  const bool uk = tp.ring && pair_ok && g.uk_w <= 8 && g.nst_d <= 4;
   if (tp.ring) {
-    const dim3 gr(2 * d.N);
-    if (d.T <= 128) {
-      if (g.nst_cq <= 8) k3_ring<I8U, 1, 4, 8><<<gr, 512, 0, s>>>(d, p, g);
-      else if (g.nst_cq <= 24) k3_ring<I8U, 1, 4, 24><<<gr, 512, 0, s>>>(d, p, g);
-      else k3_ring<I8U, 1, 4, 48><<<gr, 512, 0, s>>>(d, p, g);
+    if (uk) {
+      if (q8) launch_ring<I8U, true, true>(s, d, p, g);
+      else launch_ring<I8U, true, false>(s, d, p, g);
     } else {
-      if (g.nst_cq <= 8) k3_ring<I8U, 2, 4, 8><<<gr, 512, 0, s>>>(d, p, g);
-      else if (g.nst_cq <= 24) k3_ring<I8U, 2, 4, 24><<<gr, 512, 0, s>>>(d, p, g);
-      else k3_ring<I8U, 2, 4, 48><<<gr, 512, 0, s>>>(d, p, g);
+      launch_ring<I8U, false, false>(s, d, p, g);
     }
   } else if (tp.k3v == 1) {
     k3_tiled<I8U, 2, 1, 8, 2, 2, true, 1, true><<<g3, 1024, 0, s>>>(d, p, g, tp.m3);
@@ -3585,6 +3803,12 @@ void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs&
     k3_tiled<I8U, 1, 1, 8, 2, 2, true, 1, true><<<g3, 1024, 0, s>>>(d, p, g, tp.m3);
   } else {
     k3_tiled<I8U, 4, 1, 1, 1, 2><<<g3, 64, 0, s>>>(d, p, g, tp.m3);
+  }
+  if (uk) {
+    // one kernel did both products; the profile books them to the first
+    mark(3);
+    mark(-1);
+    return;
   }
   mark(3);
   if (q8) k4_tiled<4, 1, 1, 8, 2, true, false, true><<<dim3(tp.m4q * d.N), 512, 0, s>>>(d, p, g, tp.m4q, 1);
@@ -3611,20 +3835,20 @@ void tiled_large(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs& 
 
 template <bool I8D, bool I8U, class Mark>
 void tiled_run(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g,
-               bool q8, Mark& mark) {
+               bool q8, bool pair_ok, Mark& mark) {
   if (tp.large) tiled_large<I8D, I8U>(tp, s, d, p, g, q8, mark);
-  else if (tp.mt == 4) tiled_medium<I8D, I8U, 4>(tp, s, d, p, g, q8, mark);
-  else tiled_medium<I8D, I8U, 8>(tp, s, d, p, g, q8, mark);
+  else if (tp.mt == 4) tiled_medium<I8D, I8U, 4>(tp, s, d, p, g, q8, pair_ok, mark);
+  else tiled_medium<I8D, I8U, 8>(tp, s, d, p, g, q8, pair_ok, mark);
 }
 
 template <class Mark>
 void launch_tiled(hipStream_t s, const Dims& d, const Ptrs& p, const mla_prolog_desc& dd, bool q8,
-                  Mark& mark) {
+                  bool pair_ok, Mark& mark) {
   const PackGeo g = geo_of(dd);
   const TiledPlan tp = tiled_plan(dd, d.T);
-  if (down_i8(dd)) tiled_run<true, true>(tp, s, d, p, g, q8, mark);
-  else if (up_i8(dd)) tiled_run<false, true>(tp, s, d, p, g, q8, mark);
-  else tiled_run<false, false>(tp, s, d, p, g, q8, mark);
+  if (down_i8(dd)) tiled_run<true, true>(tp, s, d, p, g, q8, pair_ok, mark);
+  else if (up_i8(dd)) tiled_run<false, true>(tp, s, d, p, g, q8, pair_ok, mark);
+  else tiled_run<false, false>(tp, s, d, p, g, q8, pair_ok, mark);
 }
 
 }  // namespace
@@ -3824,6 +4048,7 @@ mla_status enqueue(const RunCtx& c, const mla_prolog_tensors* t, int64_t T, hipS
   p.xq = ws + lay.xq;
   p.xflag = reinterpret_cast<uint32_t*>(ws + lay.xflag);
   p.xmax = reinterpret_cast<float*>(ws + lay.xmax);
+  p.xmax2 = reinterpret_cast<float*>(ws + lay.xmax2);
   p.fpart = reinterpret_cast<uint32_t*>(ws + lay.fpart);
   p.fss = reinterpret_cast<uint32_t*>(ws + lay.fss);
   p.fykr = reinterpret_cast<float*>(ws + lay.fykr);
@@ -3867,7 +4092,7 @@ mla_status enqueue(const RunCtx& c, const mla_prolog_tensors* t, int64_t T, hipS
   }
   if (p.packed && (!pl.stream || packed_fits(dd))) {
     if (pl.stream) launch_packed(pl, s, d, p, dd, q8, c.pair_ok, mark);
-    else launch_tiled(s, d, p, dd, q8, mark);
+    else launch_tiled(s, d, p, dd, q8, c.pair_ok, mark);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? MLA_OK : MLA_ERR_RUNTIME;
   }
