@@ -2913,6 +2913,28 @@ __global__ __launch_bounds__(512) void k3_ring(Dims d, Ptrs p, PackGeo pg) {
     }
   }
   barrier();
+  // the epilogue's per-token values (the lane's cos/sin pieces and c^Q's
+  // scale), loaded R stages before the stream ends: every later wait of the
+  // ring is for a load issued before them, so they cost the stream nothing,
+  // and they are in before q^C is traded
+  const int hf = d.Dr / 2, i0 = 16 * half + 4 * g;
+  uint2 cs[MT][4];
+  float csc[MT];
+  auto epi_load = [&] {
+    const rsrc_t Cs = make_rsrc(p.cos, int64_t(d.T) * d.Dr * 2), Sn = make_rsrc(p.sin, int64_t(d.T) * d.Dr * 2);
+    const rsrc_t Sc = make_rsrc(p.cq_scale, I8 ? int64_t(d.T) * 4 : 0);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int t = 16 * (w + NW * mt) + c;
+      const uint32_t ro = t < d.T ? uint32_t(t * d.Dr + i0) * 2u : kOOB;
+      cs[mt][0] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(Cs, ro, 0, 0));
+      cs[mt][1] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(Cs, ro == kOOB ? kOOB : ro + hf * 2, 0, 0));
+      cs[mt][2] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(Sn, ro, 0, 0));
+      cs[mt][3] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(Sn, ro == kOOB ? kOOB : ro + hf * 2, 0, 0));
+      csc[mt] = I8 ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(Sc, t < d.T ? uint32_t(t) * 4u : kOOB, 0, 0))
+                   : 1.0f;
+    }
+  };
   Frag bf[6], bfn[6];
   lread(0, bf);
   Acc acc[MT][6];
@@ -2941,24 +2963,10 @@ __global__ __launch_bounds__(512) void k3_ring(Dims d, Ptrs p, PackGeo pg) {
     rw[q] = wload(st + 2 + R);
 #pragma unroll
     for (int m = 0; m < MT; ++m) ra[q][m] = aload(st + R, m);
+    if (st == (NSTMAX > R ? NSTMAX - R : 0)) epi_load();
     barrier();
 #pragma unroll
     for (int j = 0; j < 6; ++j) bf[j] = bfn[j];
-  }
-  // the epilogue's per-token values, loaded now so that they arrive while
-  // q^C is formed and traded: the lane's cos/sin pieces and c^Q's scale
-  const int hf = d.Dr / 2, i0 = 16 * half + 4 * g;
-  uint2 cs[MT][4];
-  float csc[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int t = 16 * (w + NW * mt) + c;
-    const int64_t ro = int64_t(t < d.T ? t : 0) * d.Dr;
-    cs[mt][0] = *reinterpret_cast<const uint2*>(p.cos + ro + i0);
-    cs[mt][1] = *reinterpret_cast<const uint2*>(p.cos + ro + i0 + hf);
-    cs[mt][2] = *reinterpret_cast<const uint2*>(p.sin + ro + i0);
-    cs[mt][3] = *reinterpret_cast<const uint2*>(p.sin + ro + i0 + hf);
-    csc[mt] = I8 ? p.cq_scale[t < d.T ? t : 0] : 1.0f;
   }
   if constexpr (UK) {
     // park the W^UK fragments
