@@ -57,6 +57,7 @@ class Problem(ctypes.Structure):
         ("gamma_x", _P), ("beta_x", _P), ("quant_scale_x", _P), ("quant_offset_x", _P),
         ("bias_dqkv", _P), ("beta_cq", _P), ("quant_scale_cq", _P), ("quant_offset_cq", _P),
         ("bias_uq_qr", _P),
+        ("fp16", ctypes.c_int32), ("pad2_", ctypes.c_int32),
     ]
 
 
@@ -75,6 +76,10 @@ def lib() -> ctypes.CDLL:
         L.mla_oracle_bf16_value.restype = ctypes.c_double
         L.mla_oracle_bf16_bits.argtypes = [ctypes.c_double]
         L.mla_oracle_bf16_bits.restype = ctypes.c_uint16
+        L.mla_oracle_f16_value.argtypes = [ctypes.c_uint16]
+        L.mla_oracle_f16_value.restype = ctypes.c_double
+        L.mla_oracle_f16_bits.argtypes = [ctypes.c_double]
+        L.mla_oracle_f16_bits.restype = ctypes.c_uint16
         L.mla_oracle_rmsnorm.argtypes = [_P, _P, _I64, ctypes.c_double, _P]
         L.mla_oracle_rope.argtypes = [_P, _P, _P, _I64, _P]
         L.mla_oracle_quant_int8.argtypes = [_P, _I64, _P, _P]
@@ -102,6 +107,19 @@ def bf16_bits(values) -> np.ndarray:
     v = np.asarray(values, dtype=np.float64)
     L = lib()
     return np.array([L.mla_oracle_bf16_bits(float(x)) for x in v.ravel()],
+                    dtype=np.uint16).reshape(v.shape)
+
+
+def f16_value(bits) -> np.ndarray:
+    b = np.asarray(bits, dtype=np.uint16)
+    L = lib()
+    return np.array([L.mla_oracle_f16_value(int(v)) for v in b.ravel()]).reshape(b.shape)
+
+
+def f16_bits(values) -> np.ndarray:
+    v = np.asarray(values, dtype=np.float64)
+    L = lib()
+    return np.array([L.mla_oracle_f16_bits(float(x)) for x in v.ravel()],
                     dtype=np.uint16).reshape(v.shape)
 
 
@@ -151,7 +169,8 @@ def run(inp: Dict[str, object], tokens: Optional[Sequence[int]] = None,
     bias, c^Q quantised the same way; ``inp["x_norm"]`` False quantises x
     without its norm); ``inp["concat"]`` its concatenated layout (queryOut
     rows q^N | q^R, kvCache rows c^KV | k^R, no query_rope_out / kr_cache);
-    ``inp["weight_nk"]`` weights given (n, k).  ``tokens`` selects the rows to compute (tokens are independent); row r of
+    ``inp["weight_nk"]`` weights given (n, k); ``inp["fp16"]`` (static scenario
+    only) its FLOAT16 input, every 16-bit float tensor and rounding fp16.  ``tokens`` selects the rows to compute (tokens are independent); row r of
     every output holds token ``tokens[r]``.  With ``caches`` the returned
     ``kv_cache``/``kr_cache`` are copies of the input caches with the computed
     rows written at their cacheIndex slots.
@@ -241,6 +260,7 @@ def run(inp: Dict[str, object], tokens: Optional[Sequence[int]] = None,
             if inp.get(key) is not None:
                 setattr(p, f, _ptr(arr(inp[key], dt)))
     p.concat, p.weight_nk = int(concat), int(bool(inp.get("weight_nk", False)))
+    p.fp16 = int(bool(inp.get("fp16", False)))
     if inp.get("smooth_scales_cq") is not None:
         p.smooth_cq = _ptr(arr(inp["smooth_scales_cq"], np.float32))
     p.kv_int8, p.kr_int8 = int(kv8), int(kr8)

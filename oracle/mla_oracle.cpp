@@ -71,6 +71,11 @@
 // RmsNorm of y_kv with gamma2.  The page's cacheMode 0 concatenates the
 // outputs: each queryOut row holds q^N then q^R (Hckv + Dr values) and each
 // kvCache row c^KV then k^R; its weights come transposed, (n, k) row-major.
+// Its FLOAT16 input (the parameter table gives x, gamma0/beta0/quantScale0,
+// the other gammas and betas, sin/cos and wuk as FLOAT16 or BFLOAT16, and
+// the caches and query outputs in the dtype of the input) makes every 16-bit
+// float of the problem an IEEE binary16 value, and R1, R2, R4, R5 and R6 fp16
+// roundings.
 //
 // The consumer of the caches, mla_oracle_sfa, is the sparse flash attention
 // page (aclnnSparseFlashAttention, "Function" formula, parameter table,
@@ -129,6 +134,42 @@ uint16_t bf16_bits(double v) {
 }
 
 double bf16_round(double v) { return bf16_value(bf16_bits(v)); }
+
+// ---------------------------------------------------------------------------
+// fp16 codec (IEEE-754 binary16): 1 sign bit, 5 exponent bits (bias 15), 10
+// stored fraction bits; exponent field 0 holds the subnormals f * 2^-24, 31
+// the infinities and NaNs.
+// ---------------------------------------------------------------------------
+double f16_value(uint16_t bits) {
+  const int sign = bits >> 15, ex = (bits >> 10) & 0x1F, fr = bits & 0x3FF;
+  double v;
+  if (ex == 0) v = std::ldexp(static_cast<double>(fr), -24);
+  else if (ex == 31) v = fr ? NAN : INFINITY;
+  else v = std::ldexp(static_cast<double>(1024 + fr), ex - 25);
+  return sign ? -v : v;
+}
+
+// Nearest fp16 to v, ties to even, computed from v directly.  The spacing of
+// fp16 values near |v| in [2^e, 2^(e+1)) is 2^(e-10), and 2^-24 below 2^-14;
+// what rounds above the largest finite value, 65504, is infinite.
+uint16_t f16_bits(double v) {
+  if (std::isnan(v)) return 0x7E00;
+  const uint16_t sign = std::signbit(v) ? 0x8000 : 0;
+  const double a = std::fabs(v);
+  if (std::isinf(a)) return sign | 0x7C00;
+  if (a == 0.0) return sign;
+  int e = std::ilogb(a);
+  if (e < -14) e = -14;
+  const double r = std::ldexp(std::nearbyint(std::ldexp(a, 10 - e)), e - 10);  // RNE
+  if (r > 65504.0) return sign | 0x7C00;
+  if (r < std::ldexp(1.0, -14))  // subnormal (or zero): the fraction counts 2^-24
+    return sign | static_cast<uint16_t>(std::ldexp(r, 24));
+  const int er = std::ilogb(r);   // the rounding may have carried into the next binade
+  const int fr = static_cast<int>(std::ldexp(r, 10 - er)) - 1024;
+  return sign | static_cast<uint16_t>(((er + 15) << 10) | fr);
+}
+
+double f16_round(double v) { return f16_value(f16_bits(v)); }
 
 // RmsNorm over n values (aclnnMlaPrologV2WeightNz, "RmsNorm formula").
 void rmsnorm(const double* v, const double* gamma, int64_t n, double eps, double* out,
@@ -266,10 +307,18 @@ typedef struct {
   const uint16_t* quant_scale_cq;  // (1) quantScale1, bf16
   const int8_t* quant_offset_cq;   // (1) quantOffset1
   const int32_t* bias_uq_qr;       // (N*(D+Dr)) bias1, or NULL for zeros
+  // static scenario only: every 16-bit float tensor (x, gamma0/beta0/
+  // quantScale0, gamma1/beta1/quantScale1, gamma2, sin/cos, W^UK, the caches
+  // and the query outputs) is fp16 instead of bf16, and so are the rounding
+  // points R1, R2, R4, R5, R6 (the preprocess page's FLOAT16 input)
+  int32_t fp16;
+  int32_t pad2_;
 } mla_oracle_problem;
 
 double mla_oracle_bf16_value(uint16_t bits) { return bf16_value(bits); }
 uint16_t mla_oracle_bf16_bits(double v) { return bf16_bits(v); }
+double mla_oracle_f16_value(uint16_t bits) { return f16_value(bits); }
+uint16_t mla_oracle_f16_bits(double v) { return f16_bits(v); }
 
 void mla_oracle_rmsnorm(const double* v, const double* gamma, int64_t n, double eps,
                         double* out) {
@@ -306,22 +355,27 @@ static void one_token(const mla_oracle_problem* p, int64_t r, int64_t t) {
   const int64_t Wkr = Hckv + Dr, Wuq = N * (D + Dr);
   const int32_t q8in = p->quant_in;
   const int mut = p->mutation;
+  // the 16-bit float format of the problem's float tensors and roundings
+  const bool h16 = p->fp16 != 0;
+  auto fval = [h16](uint16_t b) { return h16 ? f16_value(b) : bf16_value(b); };
+  auto fbits = [h16](double v) { return h16 ? f16_bits(v) : bf16_bits(v); };
+  auto fround = [h16](double v) { return h16 ? f16_round(v) : bf16_round(v); };
 
   // down-projections: y_q = x W^DQ (Hcq), y_kvr = x [W^DKV | W^KR] (Hckv+Dr)
   std::vector<double> y_q(Hcq, 0.0), y_kvr(Wkr, 0.0);
   if (p->static_quant) {
     // x to int8 codes: RmsNormQuant(x) = code(gamma0 x / RMS(x) + beta0)
     std::vector<double> xv(He), v(He), g0(He);
-    for (int64_t k = 0; k < He; ++k) xv[k] = bf16_value(static_cast<const uint16_t*>(p->x)[t * He + k]);
+    for (int64_t k = 0; k < He; ++k) xv[k] = fval(static_cast<const uint16_t*>(p->x)[t * He + k]);
     if (p->x_norm) {
-      for (int64_t k = 0; k < He; ++k) g0[k] = bf16_value(p->gamma_x[k]);
+      for (int64_t k = 0; k < He; ++k) g0[k] = fval(p->gamma_x[k]);
       rmsnorm(xv.data(), g0.data(), He, p->eps_x, v.data(), mut);
       for (int64_t k = 0; k < He; ++k)
-        if (mut != 10) v[k] += bf16_value(p->beta_x[k]);  // planted 10: beta dropped
+        if (mut != 10) v[k] += fval(p->beta_x[k]);  // planted 10: beta dropped
     } else {
       v = xv;
     }
-    const float qs = static_cast<float>(bf16_value(p->quant_scale_x[0]));
+    const float qs = static_cast<float>(fval(p->quant_scale_x[0]));
     std::vector<int64_t> x8(He);
     for (int64_t k = 0; k < He; ++k) x8[k] = quant_static_asym(v[k], qs, p->quant_offset_x[0], mut);
     const int8_t* wq = static_cast<const int8_t*>(p->w_dq);
@@ -368,16 +422,16 @@ static void one_token(const mla_oracle_problem* p, int64_t r, int64_t t) {
 
   std::vector<double> cosv(Dr), sinv(Dr);
   for (int64_t i = 0; i < Dr; ++i) {
-    cosv[i] = bf16_value(p->rope_cos[t * Dr + i]);
-    sinv[i] = bf16_value(p->rope_sin[t * Dr + i]);
+    cosv[i] = fval(p->rope_cos[t * Dr + i]);
+    sinv[i] = fval(p->rope_sin[t * Dr + i]);
   }
 
   // c^Q and c^KV
   std::vector<double> g(std::max(Hcq, Hckv));
   std::vector<double> c_q(Hcq), c_kv(Hckv), k_r(Dr);
-  for (int64_t i = 0; i < Hcq; ++i) g[i] = bf16_value(p->gamma_cq[i]);
+  for (int64_t i = 0; i < Hcq; ++i) g[i] = fval(p->gamma_cq[i]);
   rmsnorm(y_q.data(), g.data(), Hcq, p->eps_cq, c_q.data(), mut);
-  for (int64_t i = 0; i < Hckv; ++i) g[i] = bf16_value(p->gamma_ckv[i]);
+  for (int64_t i = 0; i < Hckv; ++i) g[i] = fval(p->gamma_ckv[i]);
   rmsnorm(y_kvr.data(), g.data(), Hckv, p->eps_ckv, c_kv.data(), mut);
   rope(y_kvr.data() + Hckv, cosv.data(), sinv.data(), Dr, k_r.data(), mut);
   if (p->cq_out)
@@ -391,7 +445,7 @@ static void one_token(const mla_oracle_problem* p, int64_t r, int64_t t) {
       if (p->kv_int8)   // R1'
         static_cast<int8_t*>(p->kv_rows)[r * Hckv + i] = quant_static(c_kv[i], p->quant_scale_ckv[i], mut);
       else              // R1
-        static_cast<uint16_t*>(p->kv_rows)[r * Hckv + i] = bf16_bits(c_kv[i]);
+        static_cast<uint16_t*>(p->kv_rows)[r * Hckv + i] = fbits(c_kv[i]);
     }
   }
   if (p->kr_rows) {
@@ -399,7 +453,7 @@ static void one_token(const mla_oracle_problem* p, int64_t r, int64_t t) {
       if (p->kr_int8)   // R2'
         static_cast<int8_t*>(p->kr_rows)[r * Dr + i] = quant_static(k_r[i], p->quant_scale_ckr[i], mut);
       else              // R2
-        static_cast<uint16_t*>(p->kr_rows)[r * Dr + i] = bf16_bits(k_r[i]);
+        static_cast<uint16_t*>(p->kr_rows)[r * Dr + i] = fbits(k_r[i]);
     }
   }
 
@@ -409,8 +463,8 @@ static void one_token(const mla_oracle_problem* p, int64_t r, int64_t t) {
     // c^Q to int8 codes: RmsNormQuant(y_q) = code(gamma1 y_q / RMS + beta1)
     std::vector<double> w(c_q);
     for (int64_t i = 0; i < Hcq; ++i)
-      if (mut != 10) w[i] += bf16_value(p->beta_cq[i]);
-    const float qs = static_cast<float>(bf16_value(p->quant_scale_cq[0]));
+      if (mut != 10) w[i] += fval(p->beta_cq[i]);
+    const float qs = static_cast<float>(fval(p->quant_scale_cq[0]));
     std::vector<int64_t> c8(Hcq);
     for (int64_t i = 0; i < Hcq; ++i) c8[i] = quant_static_asym(w[i], qs, p->quant_offset_cq[0], mut);
     const int8_t* wu = static_cast<const int8_t*>(p->w_uq_qr);
@@ -430,7 +484,7 @@ static void one_token(const mla_oracle_problem* p, int64_t r, int64_t t) {
         double m = p->smooth_cq[i];
         if (mut == 6) m = 1.0 / m;   // planted: smoothing divided out
         if (mut == 7) m = 1.0;       // planted: smoothing ignored
-        g[i] = bf16_value(p->gamma_cq[i]) * m;
+        g[i] = fval(p->gamma_cq[i]) * m;
       }
       rmsnorm(y_q.data(), g.data(), Hcq, p->eps_cq, cm.data(), mut);
     }
@@ -447,7 +501,7 @@ static void one_token(const mla_oracle_problem* p, int64_t r, int64_t t) {
       u[n] = static_cast<double>(acc[n]) * static_cast<double>(s_cq) * p->scale_w_uq_qr[n];
   } else {
     for (int64_t k = 0; k < Hcq; ++k) {
-      double cv = p->round_intermediates ? bf16_round(c_q[k]) : c_q[k];  // R3
+      double cv = p->round_intermediates ? fround(c_q[k]) : c_q[k];  // R3
       for (int64_t n = 0; n < Wuq; ++n) u[n] += cv * load(p->w_uq_qr, widx(p, k, n, Hcq, Wuq), 0);
     }
   }
@@ -466,18 +520,18 @@ static void one_token(const mla_oracle_problem* p, int64_t r, int64_t t) {
     rope(u.data() + rope0, cosv.data(), sinv.data(), Dr, qr.data(), mut);
     for (int64_t i = 0; i < Dr; ++i) {  // R4
       if (p->concat)
-        static_cast<uint16_t*>(p->query_out)[(r * N + h) * qrow + Hckv + i] = bf16_bits(qr[i]);
+        static_cast<uint16_t*>(p->query_out)[(r * N + h) * qrow + Hckv + i] = fbits(qr[i]);
       else
-        p->query_rope_out[(r * N + h) * Dr + i] = bf16_bits(qr[i]);
+        p->query_rope_out[(r * N + h) * Dr + i] = fbits(qr[i]);
     }
     for (int64_t d = 0; d < D; ++d)
-      qc[d] = p->round_intermediates ? bf16_round(u[nope0 + d]) : u[nope0 + d];  // R5
+      qc[d] = p->round_intermediates ? fround(u[nope0 + d]) : u[nope0 + d];  // R5
     for (int64_t j = 0; j < Hckv; ++j) qn[j] = 0.0;
     for (int64_t d = 0; d < D; ++d) {
       for (int64_t j = 0; j < Hckv; ++j) {
         // W^UK[h][d][j]; planted mistake 4 reads it as if laid out (N, Hckv, D)
         int64_t idx = (mut == 4) ? (h * Hckv + j) * D + d : (h * D + d) * Hckv + j;
-        qn[j] += qc[d] * bf16_value(p->w_uk[idx]);
+        qn[j] += qc[d] * fval(p->w_uk[idx]);
       }
     }
     if (p->qn_out)
@@ -487,7 +541,7 @@ static void one_token(const mla_oracle_problem* p, int64_t r, int64_t t) {
                  p->dequant_scale_q_nope + r * N + h);
     } else {              // R6
       uint16_t* qo = static_cast<uint16_t*>(p->query_out) + (r * N + h) * qrow;
-      for (int64_t j = 0; j < Hckv; ++j) qo[j] = bf16_bits(qn[j]);
+      for (int64_t j = 0; j < Hckv; ++j) qo[j] = fbits(qn[j]);
     }
   }
 }
@@ -508,6 +562,7 @@ int mla_oracle_run(mla_oracle_problem* p, int nthreads) {
     if (p->x_norm && (!p->gamma_x || !p->beta_x)) return -1;
   }
   if (p->concat && (p->query_int8 || p->kv_int8 || p->kr_int8)) return -1;
+  if (p->fp16 && !p->static_quant) return -1;
   if (p->Dr % 2 != 0 || p->Hcq <= 0 || p->Hckv <= 0 || p->N <= 0 || p->D <= 0 || p->Dr <= 0)
     return -1;
   if (p->quant_in && (!p->scale_x || !p->scale_w_dq || !p->scale_w_uq_qr || !p->scale_w_dkv_kr))

@@ -6,5 +6,5 @@ the MLA prolog operator's inputs; it performs none of the operator's arithmetic.
 """
 from .generate import (  # noqa: F401
     Dims, Workload, WORKLOADS, make_inputs, workload, bf16_bits_to_f32,
-    SENTINEL_BF16, SENTINEL_I8,
+    SENTINEL_BF16, SENTINEL_F16, SENTINEL_I8,
 )

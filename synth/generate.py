@@ -36,6 +36,8 @@ _CHUNK = 1 << 20
 SENTINEL_BF16 = np.uint16(0x7FA5)
 #: the byte an int8 (quantised) cache slot starts with
 SENTINEL_I8 = np.int8(-77)
+#: fp16 bit pattern an fp16 cache slot starts with (a quiet NaN with a payload)
+SENTINEL_F16 = np.uint16(0x7E55)
 
 # one random stream per tensor
 _STREAM = {
@@ -135,6 +137,12 @@ def _to_bf16_bits(v: np.ndarray) -> np.ndarray:
     return out.reshape(np.shape(v))
 
 
+def _to_f16_bits(v: np.ndarray) -> np.ndarray:
+    """Round drawn float64 values to fp16 bit patterns (nearest even, directly
+    from float64)."""
+    return np.asarray(v, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
 @dataclass(frozen=True)
 class Dims:
     """Model sizes in the pages' notation."""
@@ -173,6 +181,7 @@ class Workload:
     x_norm: bool = True
     concat: bool = False     # cacheMode 0: queryOut q^N | q^R, kvCache c^KV | k^R
     weight_nk: bool = False  # weights given transposed, (n, k) row-major
+    fp16: bool = False       # static scenario: FLOAT16 input (every 16-bit float tensor fp16)
 
     def with_tokens(self, T: int) -> "Workload":
         return replace(self, T=T)
@@ -194,6 +203,11 @@ WORKLOADS: Dict[str, Workload] = {
                             preprocess=True, concat=True, weight_nk=True),
     "pre_decode_t32": Workload("pre_decode_t32", 32, MODEL, 1024, 128, False, "uniform:32768", 20269,
                                preprocess=True, concat=True, weight_nk=True),
+    # the static scenario with the preprocess page's FLOAT16 input
+    "tiny_pre_f16_t4": Workload("tiny_pre_f16_t4", 4, TINY_Q, 4, 16, False, "uniform:64", 20270,
+                                preprocess=True, concat=True, weight_nk=True, fp16=True),
+    "pre_f16_decode_t32": Workload("pre_f16_decode_t32", 32, MODEL, 1024, 128, False, "uniform:32768", 20271,
+                                   preprocess=True, concat=True, weight_nk=True, fp16=True),
 }
 
 
@@ -229,14 +243,15 @@ def _positions_and_slots(wl: Workload):
     return pos, slots
 
 
-def rope_tables(pos: np.ndarray, Dr: int, base: float = 10000.0):
-    """Rotate-half sin/cos tables (bf16 bits), one row per token: angle
-    pos * base^(-2i/Dr) for i < Dr/2, repeated for the second half."""
+def rope_tables(pos: np.ndarray, Dr: int, base: float = 10000.0, fp16: bool = False):
+    """Rotate-half sin/cos tables (bf16 bits, or fp16), one row per token:
+    angle pos * base^(-2i/Dr) for i < Dr/2, repeated for the second half."""
     half = Dr // 2
     inv = base ** (-2.0 * np.arange(half, dtype=np.float64) / Dr)
     ang = pos.astype(np.float64)[:, None] * inv[None, :]
     ang = np.concatenate([ang, ang], axis=1)
-    return _to_bf16_bits(np.sin(ang)), _to_bf16_bits(np.cos(ang))
+    to = _to_f16_bits if fp16 else _to_bf16_bits
+    return to(np.sin(ang)), to(np.cos(ang))
 
 
 def make_inputs(wl: Workload, T: Optional[int] = None, with_caches: bool = True,
@@ -260,7 +275,7 @@ def make_inputs(wl: Workload, T: Optional[int] = None, with_caches: bool = True,
                               "block_num": wl.block_num, "block_size": wl.block_size,
                               "quant": wl.quant, "partial": wl.partial, "kv_quant": wl.kv_quant,
                               "preprocess": wl.preprocess, "x_norm": wl.x_norm, "concat": wl.concat,
-                              "weight_nk": wl.weight_nk,
+                              "weight_nk": wl.weight_nk, "fp16": wl.fp16,
                               "eps_cq": wl.eps, "eps_ckv": wl.eps, "eps_x": wl.eps}
     if wl.partial and wl.quant:
         raise ValueError("a workload is either fully or partially quantised")
@@ -272,15 +287,20 @@ def make_inputs(wl: Workload, T: Optional[int] = None, with_caches: bool = True,
         raise ValueError("the static scenario has its own quantisation")
     if wl.concat and (wl.quant or wl.kv_quant):
         raise ValueError("the concatenated layout holds bf16 rows")
+    if wl.fp16 and not wl.preprocess:
+        raise ValueError("the FLOAT16 input belongs to the static scenario")
+    # the 16-bit float format of x, the gammas, betas and quant scales, the
+    # rope tables, W^UK and the caches
+    fbits = _to_f16_bits if wl.fp16 else _to_bf16_bits
 
     pos, slots = _positions_and_slots(wl)
     pos, slots = pos[:T], slots[:T]
     out["positions"] = pos
     out["cache_index"] = np.ascontiguousarray(slots, dtype=np.int64)
-    out["rope_sin"], out["rope_cos"] = rope_tables(pos, Dr)
+    out["rope_sin"], out["rope_cos"] = rope_tables(pos, Dr, fp16=wl.fp16)
 
     def gamma(stream, n):
-        return _to_bf16_bits(0.5 + _uniform(s, stream, n))
+        return fbits(0.5 + _uniform(s, stream, n))
 
     out["rmsnorm_gamma_cq"] = gamma("gamma_cq", Hcq)
     out["rmsnorm_gamma_ckv"] = gamma("gamma_ckv", Hckv)
@@ -293,7 +313,7 @@ def make_inputs(wl: Workload, T: Optional[int] = None, with_caches: bool = True,
     def static_scale(stream):
         # one bf16 quantScale in [12, 24): the normalised values are O(1), so
         # codes reach about +-100 and the largest saturate
-        return _to_bf16_bits(12.0 + 12.0 * _uniform(s, stream, 1))
+        return fbits(12.0 + 12.0 * _uniform(s, stream, 1))
 
     def static_offset(stream):
         return np.floor(-4.0 + 9.0 * _uniform(s, stream, 1)).astype(np.int8)
@@ -310,12 +330,12 @@ def make_inputs(wl: Workload, T: Optional[int] = None, with_caches: bool = True,
         return (comp + extra).astype(np.int32)
 
     if wl.preprocess:
-        out["token_x"] = _to_bf16_bits(_normal(s, "x", full_T * He)[:T * He]).reshape(T, He)
+        out["token_x"] = fbits(_normal(s, "x", full_T * He)[:T * He]).reshape(T, He)
         out["rmsnorm_gamma_x"] = gamma("gamma_x", He)
-        out["rmsnorm_beta_x"] = _to_bf16_bits(-0.1 + 0.2 * _uniform(s, "beta_x", He))
+        out["rmsnorm_beta_x"] = fbits(-0.1 + 0.2 * _uniform(s, "beta_x", He))
         out["quant_scale_x"] = static_scale("qs_x")
         out["quant_offset_x"] = static_offset("qo_x")
-        out["rmsnorm_beta_cq"] = _to_bf16_bits(-0.1 + 0.2 * _uniform(s, "beta_cq", Hcq))
+        out["rmsnorm_beta_cq"] = fbits(-0.1 + 0.2 * _uniform(s, "beta_cq", Hcq))
         out["quant_scale_cq"] = static_scale("qs_cq")
         out["quant_offset_cq"] = static_offset("qo_cq")
         w_dq = _int8_uniform(s, "w_dq", He * Hcq).reshape(He, Hcq)
@@ -364,7 +384,7 @@ def make_inputs(wl: Workload, T: Optional[int] = None, with_caches: bool = True,
     if unpacked:
         out["weight_uq"], out["weight_qr"] = w_uq, w_qr
         out["weight_dkv"], out["weight_kr"] = w_dkv, w_kr
-    out["weight_uk"] = _to_bf16_bits(_normal(s, "w_uk", N * D * Hckv) / np.sqrt(D)).reshape(N, D, Hckv)
+    out["weight_uk"] = fbits(_normal(s, "w_uk", N * D * Hckv) / np.sqrt(D)).reshape(N, D, Hckv)
 
     kr8 = wl.kv_quant and wl.partial
     if wl.kv_quant:
@@ -375,13 +395,14 @@ def make_inputs(wl: Workload, T: Optional[int] = None, with_caches: bool = True,
         out["quant_scale_ckr"] = (16.0 + 32.0 * _uniform(s, "qs_ckr", Dr)).astype(np.float32)
     out["kv_cache_shape"] = (wl.block_num, wl.block_size, 1, Hckv + Dr if wl.concat else Hckv)
     out["kr_cache_shape"] = (wl.block_num, wl.block_size, 1, Dr)
+    sent16 = SENTINEL_F16 if wl.fp16 else SENTINEL_BF16
     if with_caches and wl.concat:
-        out["kv_cache"] = np.full(out["kv_cache_shape"], SENTINEL_BF16, dtype=np.uint16)
+        out["kv_cache"] = np.full(out["kv_cache_shape"], sent16, dtype=np.uint16)
     elif with_caches:
         out["kv_cache"] = (np.full(out["kv_cache_shape"], SENTINEL_I8, dtype=np.int8) if wl.kv_quant
-                           else np.full(out["kv_cache_shape"], SENTINEL_BF16, dtype=np.uint16))
+                           else np.full(out["kv_cache_shape"], sent16, dtype=np.uint16))
         out["kr_cache"] = (np.full(out["kr_cache_shape"], SENTINEL_I8, dtype=np.int8) if kr8
-                           else np.full(out["kr_cache_shape"], SENTINEL_BF16, dtype=np.uint16))
+                           else np.full(out["kr_cache_shape"], sent16, dtype=np.uint16))
     return out
 
 
@@ -389,10 +410,10 @@ def custom_workload(name: str, T: int, dims: Dims, block_num: int, block_size: i
                     quant: bool = False, seed: int = 7, positions: str = "uniform:4096",
                     eps: float = 1e-6, partial: bool = False, smooth: bool = False,
                     kv_quant: bool = False, preprocess: bool = False, x_norm: bool = True,
-                    concat: bool = False, weight_nk: bool = False) -> Workload:
+                    concat: bool = False, weight_nk: bool = False, fp16: bool = False) -> Workload:
     """A workload with arbitrary (small) sizes for tests of ragged shapes."""
     return Workload(name, T, dims, block_num, block_size, quant, positions, seed, eps, partial, smooth,
-                    kv_quant, preprocess, x_norm, concat, weight_nk)
+                    kv_quant, preprocess, x_norm, concat, weight_nk, fp16)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:

@@ -68,6 +68,43 @@ def test_bf16_round_is_nearest():
 
 
 # ---------------------------------------------------------------------------
+# fp16 codec (the preprocess page's FLOAT16 input)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("value,bits", [
+    (1.0, 0x3C00), (-2.0, 0xC000), (0.1, 0x2E66), (0.0, 0x0000), (-0.0, 0x8000),
+    (65504.0, 0x7BFF),                      # largest finite
+    (65519.99, 0x7BFF), (65520.0, 0x7C00),  # below / at the rounding tie to infinity
+    (1.0 + 2.0 ** -11, 0x3C00),             # tie between 1 and 1+2^-10 -> even (1)
+    (1.0 + 3 * 2.0 ** -11, 0x3C02),         # tie between 1+2^-10 and 1+2^-9 -> even
+    (1.0 + 2.0 ** -11 + 2.0 ** -40, 0x3C01),  # just above the tie -> up
+    (2.0 ** -14, 0x0400),                   # smallest normal
+    (2.0 ** -24, 0x0001),                   # smallest subnormal
+    (2.0 ** -25, 0x0000),                   # half of it: tie -> even (zero)
+    (3.0 * 2.0 ** -25, 0x0002),             # 1.5 subnormal steps: tie -> even (2)
+    (1023 * 2.0 ** -24 + 2.0 ** -25, 0x0400),  # the last subnormal tie carries into the normals
+    (1e6, 0x7C00), (-1e6, 0xFC00), (float("inf"), 0x7C00),
+])
+def test_f16_encode_known_values(value, bits):
+    assert int(oracle.f16_bits([value])[0]) == bits
+
+
+def test_f16_encode_matches_library():
+    # numpy's float64 -> float16 conversion rounds to nearest even directly
+    rng = np.random.default_rng(3)
+    v = np.concatenate([rng.standard_normal(20000) * 2.0 ** rng.integers(-30, 17, 20000),
+                        rng.integers(-70000, 70000, 2000).astype(np.float64)])
+    with np.errstate(over="ignore"):
+        ref = v.astype(np.float16).view(np.uint16)
+    assert np.array_equal(oracle.f16_bits(v), ref)
+
+
+def test_f16_decode_matches_library_on_all_finite_patterns():
+    bits = np.arange(0, 1 << 16, 3, dtype=np.uint32).astype(np.uint16)
+    bits = bits[((bits >> 10) & 0x1F) != 0x1F]
+    assert np.array_equal(oracle.f16_value(bits), lib_f16_to_f64(bits))
+
+
+# ---------------------------------------------------------------------------
 # RmsNorm (aclnnMlaPrologV2WeightNz, "RmsNorm formula")
 # ---------------------------------------------------------------------------
 def test_rmsnorm_hand_worked():
@@ -175,9 +212,16 @@ RAGGED_Q8 = custom_workload("ragged_q8", T=6, dims=Dims(He=48, Hcq=16, Hckv=8, N
                             block_num=2, block_size=16, quant=True, seed=12)
 
 
+def lib_f16_to_f64(bits):
+    """fp16 bits -> float64 through numpy's own half type (a library routine)."""
+    return np.ascontiguousarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
 def values(inp, key):
     a = np.asarray(inp[key])
-    return a.astype(np.float64) if a.dtype == np.int8 else lib_bf16_to_f64(a)
+    if a.dtype == np.int8:
+        return a.astype(np.float64)
+    return lib_f16_to_f64(a) if inp.get("fp16") else lib_bf16_to_f64(a)
 
 
 def brute_force(inp, cos_sin=None):
@@ -241,6 +285,14 @@ def near_bf16(bits, ref):
     got = lib_bf16_to_f64(bits)
     ref = np.asarray(ref, dtype=np.float64)
     return np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-30)
+
+
+def near_f16(bits, ref):
+    """Each fp16 value is within half an fp16 step of the float64 reference
+    (2^-11 relative for normal values, 2^-25 absolute below them)."""
+    got = lib_f16_to_f64(bits)
+    ref = np.asarray(ref, dtype=np.float64)
+    return np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -11 + 2.0 ** -25)
 
 
 @pytest.mark.parametrize("wl", [TINY, RAGGED], ids=["tiny_t4", "ragged"])
@@ -626,9 +678,10 @@ def _kn(inp, key):
     return w.T if inp.get("weight_nk") else w
 
 
-def _codes(v, scale_bits, offset):
+def _codes(v, scale_bits, offset, fp16=False):
     """Static codes written with numpy: float32 product, rint (half to even)."""
-    s = np.float32(lib_bf16_to_f64(np.asarray(scale_bits))[0])
+    dec = lib_f16_to_f64 if fp16 else lib_bf16_to_f64
+    s = np.float32(dec(np.asarray(scale_bits))[0])
     r = np.rint(np.asarray(v, np.float64).astype(np.float32) * s).astype(np.float64) + int(offset[0])
     return np.clip(r, -128, 127).astype(np.int64)
 
@@ -639,13 +692,14 @@ def brute_force_static(inp):
     q_r and q_n, the last four before their bf16 rounding."""
     d = inp["dims"]
     T, half = inp["T"], d.Dr // 2
-    x = lib_bf16_to_f64(inp["token_x"])
+    h16 = bool(inp.get("fp16"))
+    x = values(inp, "token_x")
     if inp.get("x_norm", True):
         rms = np.sqrt((x * x).mean(axis=1, keepdims=True) + inp["eps_x"])
         v = values(inp, "rmsnorm_gamma_x") * x / rms + values(inp, "rmsnorm_beta_x")
     else:
         v = x
-    x8 = _codes(v, inp["quant_scale_x"], inp["quant_offset_x"])
+    x8 = _codes(v, inp["quant_scale_x"], inp["quant_offset_x"], h16)
     wcat = np.concatenate([_kn(inp, "weight_dq"), _kn(inp, "weight_dkv_kr")], axis=1)
     ds = np.concatenate([inp["dequant_scale_w_dq"], inp["dequant_scale_w_dkv_kr"]]).astype(np.float64)
     y = (x8 @ wcat + np.asarray(inp["bias_dqkv"], np.int64)).astype(np.float64) * ds
@@ -660,13 +714,15 @@ def brute_force_static(inp):
                                hi * c[..., half:] + lo * s[..., half:]], axis=-1)
 
     cq = norm(yq, values(inp, "rmsnorm_gamma_cq"), inp["eps_cq"])
-    c8 = _codes(cq + values(inp, "rmsnorm_beta_cq"), inp["quant_scale_cq"], inp["quant_offset_cq"])
+    c8 = _codes(cq + values(inp, "rmsnorm_beta_cq"), inp["quant_scale_cq"], inp["quant_offset_cq"], h16)
     u = ((c8 @ _kn(inp, "weight_uq_qr") + np.asarray(inp["bias_uq_qr"], np.int64)).astype(np.float64)
          * inp["dequant_scale_w_uq_qr"].astype(np.float64))
     cos, sin = values(inp, "rope_cos"), values(inp, "rope_sin")
     uh = u.reshape(T, d.N, d.D + d.Dr)
     q_r = rot(uh[:, :, d.D:], cos[:, None, :], sin[:, None, :])
-    qc = lib_bf16_to_f64(oracle.bf16_bits(uh[:, :, :d.D]))
+    # R5: q^C rounded to the 16-bit format (numpy's own half rounding for fp16)
+    qc = (uh[:, :, :d.D].astype(np.float16).astype(np.float64) if h16
+          else lib_bf16_to_f64(oracle.bf16_bits(uh[:, :, :d.D])))
     q_n = np.einsum("thd,hdc->thc", qc, values(inp, "weight_uk"))
     return {"y": y, "c_q": cq, "u": u, "c_kv": norm(ykv, values(inp, "rmsnorm_gamma_ckv"), inp["eps_ckv"]),
             "k_r": rot(ykr, cos, sin), "q_r": q_r, "q_n": q_n}
@@ -678,16 +734,53 @@ def _static_pins_hold(inp, mutation=0):
     bf = brute_force_static(inp)
     q = o["query_out"]
     qn, qr = (q[..., :d.Hckv], q[..., d.Hckv:]) if inp.get("concat") else (q, o["query_rope_out"])
+    near = near_f16 if inp.get("fp16") else near_bf16
     return bool(np.allclose(o["y"], bf["y"], rtol=1e-15, atol=0)
                 and np.allclose(o["c_q"], bf["c_q"], rtol=1e-13, atol=1e-14)
                 and np.allclose(o["u"], bf["u"], rtol=1e-15, atol=0)
-                and near_bf16(o["kv_rows"], bf["c_kv"]) and near_bf16(o["kr_rows"], bf["k_r"])
-                and near_bf16(qr, bf["q_r"]) and near_bf16(qn, bf["q_n"]))
+                and near(o["kv_rows"], bf["c_kv"]) and near(o["kr_rows"], bf["k_r"])
+                and near(qr, bf["q_r"]) and near(qn, bf["q_n"]))
 
 
-@pytest.mark.parametrize("wl", [PRE, RAGGED_PRE], ids=["tiny_pre", "ragged_pre"])
+PRE_F16 = synth.workload("tiny_pre_f16_t4")
+RAGGED_PRE_F16 = custom_workload("ragged_pre_f16", T=5, dims=Dims(He=48, Hcq=32, Hckv=16, N=3, D=16, Dr=16),
+                                 block_num=2, block_size=16, seed=15, preprocess=True, fp16=True)
+
+
+@pytest.mark.parametrize("wl", [PRE, RAGGED_PRE, PRE_F16, RAGGED_PRE_F16],
+                         ids=["tiny_pre", "ragged_pre", "tiny_pre_f16", "ragged_pre_f16"])
 def test_static_scenario_matches_brute_force(wl):
     assert _static_pins_hold(synth.make_inputs(wl))
+
+
+def test_fp16_outputs_are_fp16_roundings():
+    # the FLOAT16 input: every 16-bit output is the fp16 rounding of its
+    # double value (half an fp16 step), which a bf16 rounding misses by far
+    inp = synth.make_inputs(RAGGED_PRE_F16)
+    d = inp["dims"]
+    o = oracle.run(inp, intermediates=True)
+    bf = brute_force_static(inp)
+    assert not inp["concat"]
+    assert near_f16(o["query_out"], bf["q_n"]) and near_f16(o["query_rope_out"], bf["q_r"])
+    assert near_f16(o["kv_rows"], bf["c_kv"]) and near_f16(o["kr_rows"], bf["k_r"])
+    # the same bits read as bf16 are not near the references
+    assert not near_bf16(o["query_out"], bf["q_n"])
+
+
+@pytest.mark.parametrize("mutation", [1, 2, 4, 9, 10, 11],
+                         ids=["rope_sign", "eps_outside", "wuk_transposed", "offset_ignored", "beta_dropped",
+                              "bias_subtracted"])
+def test_planted_mistakes_fail_the_fp16_static_pin(mutation):
+    inp = synth.make_inputs(RAGGED_PRE_F16)
+    try:
+        held = _static_pins_hold(inp, mutation)
+    except Exception:
+        held = False
+    assert not held
+
+
+def test_fp16_static_pin_holds_without_planted_mistake():
+    assert _static_pins_hold(synth.make_inputs(RAGGED_PRE_F16))
 
 
 def test_static_scenario_without_the_input_norm():
