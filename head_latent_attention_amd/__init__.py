@@ -39,6 +39,7 @@ MLA_BF16 = 0
 MLA_INT8 = 1
 MLA_INT8_PARTIAL = 2   # in_dtype only: int8 weightUqQr, every other input bf16
 MLA_INT8_STATIC = 3    # in_dtype only: the preprocess page's static int8 scenario
+MLA_FP16 = 4           # float_dtype only: fp16 tensors in the static scenario
 
 #: the symbols include/mla_prolog.h declares
 EXPORTS = ("mla_prolog_validate", "mla_prolog_workspace_bytes", "mla_prolog_packed_weights_bytes",
@@ -68,7 +69,7 @@ class Desc(ctypes.Structure):
                 ("device", ctypes.c_int32), ("cache_dtype", ctypes.c_int32),
                 ("concat", ctypes.c_int32), ("weights_nk", ctypes.c_int32),
                 ("x_quant_only", ctypes.c_int32), ("check_index", ctypes.c_int32),
-                ("eps_x", ctypes.c_double)]
+                ("eps_x", ctypes.c_double), ("float_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 TENSOR_FIELDS = ("token_x", "weight_dq", "weight_uq_qr", "weight_uk", "weight_dkv_kr",
@@ -149,10 +150,10 @@ def status_string(status: int) -> str:
 def make_desc(He, Hcq, Hckv, N, D, Dr, block_num, block_size, max_tokens, eps_cq=1e-5,
               eps_ckv=1e-5, in_dtype=MLA_BF16, query_dtype=MLA_BF16, device=0,
               cache_dtype=MLA_BF16, concat=0, weights_nk=0, x_quant_only=0, eps_x=1e-5,
-              check_index=0) -> Desc:
+              check_index=0, float_dtype=MLA_BF16) -> Desc:
     return Desc(He, Hcq, Hckv, N, D, Dr, block_num, block_size, max_tokens, eps_cq, eps_ckv,
                 in_dtype, query_dtype, device, cache_dtype, int(concat), int(weights_nk),
-                int(x_quant_only), int(check_index), eps_x)
+                int(x_quant_only), int(check_index), eps_x, int(float_dtype), 0)
 
 
 def _address(v) -> Optional[int]:

@@ -78,6 +78,23 @@ __device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float e)
                     uint32_t(f2bf(c)) | (uint32_t(f2bf(e)) << 16));
 }
 
+// fp16 (IEEE binary16) <-> float; the conversion rounds to nearest even
+__device__ __forceinline__ float h2f(uint16_t b) { return float(__builtin_bit_cast(_Float16, b)); }
+__device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f)); }
+
+// A 16-bit float of the tensors whose format the caller chooses (the MLA
+// preprocess page takes FLOAT16 or BFLOAT16 for them): fp16 when F16, else
+// bf16.
+template <bool F16>
+__device__ __forceinline__ float ld16(uint16_t b) { return F16 ? h2f(b) : bf2f(b); }
+template <bool F16>
+__device__ __forceinline__ uint16_t st16(float f) { return F16 ? f2h(f) : f2bf(f); }
+template <bool F16>
+__device__ __forceinline__ uint2 pack16x4(float a, float b, float c, float e) {
+  return make_uint2(uint32_t(st16<F16>(a)) | (uint32_t(st16<F16>(b)) << 16),
+                    uint32_t(st16<F16>(c)) | (uint32_t(st16<F16>(e)) << 16));
+}
+
 // symmetric int8 code of v for scale s > 0: nearest integer (ties to even)
 // of v / s, kept within [-127, 127]
 __device__ __forceinline__ int8_t quant_code(float v, float s) {
@@ -333,10 +350,10 @@ __device__ __forceinline__ float udq(const Ptrs& p, int32_t acc, int t, int n) {
 // first 8-element chunk of x (and its gamma0 / beta0) in registers, loaded
 // before the reduction; chunks beyond the first 1024 are read again.
 struct XQuant {
-  const uint16_t* x;      // (T, He) bf16
-  const uint16_t* gamma;  // (He) bf16, NULL without the norm
-  const uint16_t* beta;   // (He) bf16
-  const uint16_t* scale;  // one bf16
+  const uint16_t* x;      // (T, He) bf16 (or fp16)
+  const uint16_t* gamma;  // (He) bf16 (or fp16), NULL without the norm
+  const uint16_t* beta;   // (He) bf16 (or fp16)
+  const uint16_t* scale;  // one bf16 (or fp16)
   const int8_t* offset;   // one int8
   uint8_t* out;           // (T, He) int8 codes
   int T, He;
@@ -344,12 +361,15 @@ struct XQuant {
 };
 constexpr int kXqThreads = 1024;
 
-__device__ __forceinline__ void unpack_bf16x8(const uint4& u, double (&v)[8]) {
+template <bool F16>
+__device__ __forceinline__ void unpack16x8(const uint4& u, double (&v)[8]) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = bf2f(uint16_t(w[e / 2] >> (16 * (e & 1))));
+  for (int e = 0; e < 8; ++e) v[e] = ld16<F16>(uint16_t(w[e / 2] >> (16 * (e & 1))));
 }
 
+// F16: x, gamma0, beta0 and quantScale0 are fp16 (else bf16)
+template <bool F16>
 __global__ __launch_bounds__(kXqThreads) void k0_xquant(XQuant a) {
   __shared__ double red[kXqThreads / 64];
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -364,11 +384,11 @@ __global__ __launch_bounds__(kXqThreads) void k0_xquant(XQuant a) {
   if (a.gamma) {
     if (mine) { g0 = g4[tid]; b0 = b4[tid]; }
     double v[8], ss = 0.0;
-    unpack_bf16x8(x0, v);
+    unpack16x8<F16>(x0, v);
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
     for (int j = tid + kXqThreads; j < chunks; j += kXqThreads) {
-      unpack_bf16x8(row[j], v);
+      unpack16x8<F16>(row[j], v);
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
     }
@@ -380,15 +400,15 @@ __global__ __launch_bounds__(kXqThreads) void k0_xquant(XQuant a) {
     for (int k = 0; k < kXqThreads / 64; ++k) tot += red[k];
     rms = sqrt(tot / double(a.He) + a.eps);
   }
-  const float qs = bf2f(*a.scale), off = float(*a.offset);
+  const float qs = ld16<F16>(*a.scale), off = float(*a.offset);
   uint2* out = reinterpret_cast<uint2*>(a.out + int64_t(t) * a.He);
   auto emit = [&](int j, const uint4& xu, const uint4& gu, const uint4& bu) {
     double v[8];
-    unpack_bf16x8(xu, v);
+    unpack16x8<F16>(xu, v);
     if (a.gamma) {
       double g[8], b[8];
-      unpack_bf16x8(gu, g);
-      unpack_bf16x8(bu, b);
+      unpack16x8<F16>(gu, g);
+      unpack16x8<F16>(bu, b);
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = g[e] * v[e] / rms + b[e];
     }
@@ -584,6 +604,21 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
 }
 __device__ __forceinline__ i32x4 mfma(i32x4 a, i32x4 b, i32x4 c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// The 16-bit float products: bf16, or fp16 when F16 (the same 16x16x32
+// shape); int8 fragments pass through to the int8 product
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+template <bool F16>
+__device__ __forceinline__ f32x4 mma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return mfma(a, b, c);
+}
+template <bool F16>
+__device__ __forceinline__ i32x4 mma16(i32x4 a, i32x4 b, i32x4 c) {
+  return mfma(a, b, c);
 }
 
 // Activation operands.  A policy loads the calling lane's 16-byte registers
@@ -894,9 +929,10 @@ __global__ __launch_bounds__(64 * NW) void k1_packed(Dims d, Ptrs p, PackGeo pg,
 // With cq_nst > 0, c^Q is stored fragment-packed (cq_nst k-stages per
 // 16-token tile, the k padding as zeros); with 0, row-major.
 
-template <bool I8D, bool I8U, bool ST, int NWT, int TPB, int CPL>
+template <bool I8D, bool I8U, bool ST, int NWT, int TPB, int CPL, bool F16 = false>
 __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S, int cq_nst) {
   static_assert(!ST || (I8D && I8U), "the static scenario is int8 throughout");
+  static_assert(!F16 || ST, "fp16 tensors belong to the static scenario");
   __shared__ double red[NWT * TPB][3];
   __shared__ double ry[TPB][64];   // the token's y of the k^R columns (Dr <= 64)
   const int w = threadIdx.x >> 6;
@@ -960,7 +996,7 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
 
   // the c^Q weight: gamma, times smoothScalesCq for an int8 c^Q when given
   auto gq = [&](int n) {
-    const double g = double(bf2f(p.gamma_cq[n]));
+    const double g = double(ld16<F16>(p.gamma_cq[n]));
     if constexpr (I8U) return p.smooth_cq ? g * double(p.smooth_cq[n]) : g;
     return g;
   };
@@ -1010,7 +1046,7 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
   // quantOffset1 and its dequantisation scale is 1 (the per-channel deScale1
   // does the rest)
   constexpr bool stq = ST;
-  const float st_s = stq ? bf2f(*p.qsc_cq) : 0.0f, st_o = stq ? float(*p.qo_cq) : 0.0f;
+  const float st_s = stq ? ld16<F16>(*p.qsc_cq) : 0.0f, st_o = stq ? float(*p.qo_cq) : 0.0f;
   float sc = 0.0f;
   if constexpr (I8U) sc = stq ? 1.0f : float(gmax / rms_q) / 127.0f;
   const int64_t slot = p.cache_index[t];
@@ -1031,7 +1067,7 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
       const int64_t o = cq_nst ? packed_offset(t, 8 * j, tile, true) : int64_t(t) * d.Hcq + 8 * j;
       *reinterpret_cast<uint2*>(p.cq + o) = make_uint2(lo, hi);
     } else {
-      const uint2 a = pack_bf16x4(c[0], c[1], c[2], c[3]), b = pack_bf16x4(c[4], c[5], c[6], c[7]);
+      const uint2 a = pack16x4<F16>(c[0], c[1], c[2], c[3]), b = pack16x4<F16>(c[4], c[5], c[6], c[7]);
       const int64_t o = cq_nst ? packed_offset(t, 8 * j, tile, false) : (int64_t(t) * d.Hcq + 8 * j) * 2;
       *reinterpret_cast<uint4*>(p.cq + o) = make_uint4(a.x, a.y, b.x, b.y);
     }
@@ -1042,7 +1078,7 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         double w = gq(8 * j + e) * v[e] / rms_q;
-        if (stq) w += double(bf2f(p.beta_cq[8 * j + e]));
+        if (stq) w += double(ld16<F16>(p.beta_cq[8 * j + e]));
         c[e] = float(w);
       }
       store_cq(j, c, false);
@@ -1052,7 +1088,7 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
     } else if (cache) {
       const int jk = j - cq_c;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) c[e] = float(double(bf2f(p.gamma_ckv[8 * jk + e])) * v[e] / rms_kv);
+      for (int e = 0; e < 8; ++e) c[e] = float(double(ld16<F16>(p.gamma_ckv[8 * jk + e])) * v[e] / rms_kv);
       if (p.qs_ckv) {
         uint32_t lo = 0, hi = 0;
 #pragma unroll
@@ -1063,7 +1099,7 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
         *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(p.kv_cache) + slot * d.kvs + 8 * jk) =
             make_uint2(lo, hi);
       } else {
-        const uint2 a = pack_bf16x4(c[0], c[1], c[2], c[3]), b = pack_bf16x4(c[4], c[5], c[6], c[7]);
+        const uint2 a = pack16x4<F16>(c[0], c[1], c[2], c[3]), b = pack16x4<F16>(c[4], c[5], c[6], c[7]);
         *reinterpret_cast<uint4*>(p.kv_cache + slot * d.kvs + 8 * jk) = make_uint4(a.x, a.y, b.x, b.y);
       }
     }
@@ -1102,14 +1138,14 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
   uint8_t* kr8 = reinterpret_cast<uint8_t*>(p.kr_cache) + slot * d.krs;
   for (int i = lane; i < h; i += L) {
     const double a = yr[i], b = yr[i + h];
-    const float r0 = float(a * bf2f(cs[i]) - b * bf2f(sn[i]));
-    const float r1 = float(b * bf2f(cs[i + h]) + a * bf2f(sn[i + h]));
+    const float r0 = float(a * ld16<F16>(cs[i]) - b * ld16<F16>(sn[i]));
+    const float r1 = float(b * ld16<F16>(cs[i + h]) + a * ld16<F16>(sn[i + h]));
     if (p.qs_ckr) {
       kr8[i] = uint8_t(cache_code(r0, p.qs_ckr[i]));
       kr8[i + h] = uint8_t(cache_code(r1, p.qs_ckr[i + h]));
     } else {
-      kr[i] = f2bf(r0);
-      kr[i + h] = f2bf(r1);
+      kr[i] = st16<F16>(r0);
+      kr[i + h] = st16<F16>(r1);
     }
   }
 }
@@ -2409,7 +2445,7 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
 // four consecutive output columns of one token, stored as one 8- or 16-byte
 // vector.
 // ---------------------------------------------------------------------------
-template <bool I8, int MT, int NWW, int D, class AP>
+template <bool I8, int MT, int NWW, int D, class AP, bool F16 = false>
 __device__ __forceinline__ void tile_mma(const AP& ap, rsrc_t Wp, const uint32_t (&wb)[NWW], int s0,
                                          int ns, typename Stage<I8>::Acc (&acc)[MT][NWW * 4]) {
   using S = Stage<I8>;
@@ -2448,7 +2484,7 @@ __device__ __forceinline__ void tile_mma(const AP& ap, rsrc_t Wp, const uint32_t
         const typename S::Frag af = ap.frag(aq[q], mt);
 #pragma unroll
         for (int j = 0; j < NWW * 4; ++j)
-          acc[mt][j] = mfma(__builtin_bit_cast(typename S::Frag, bq[q][j]), af, acc[mt][j]);
+          acc[mt][j] = mma16<F16>(__builtin_bit_cast(typename S::Frag, bq[q][j]), af, acc[mt][j]);
       }
       issue(bq[q], aq[q], j0 + q + D);
       // keep each slot's MFMAs after its own wait and before the next
@@ -2490,7 +2526,7 @@ __device__ __forceinline__ APacked<I8, MT> tiles_from(const void* base, int64_t 
 // SH: weight loads carry the streaming hint; set where each weight byte is
 // read once per step (few token tiles), left off where token tiles re-read
 // the weights and want them kept in the caches
-template <bool I8, int MT, int NWW, int WM, int WN, class AP, int KPB = 1, bool SH = false>
+template <bool I8, int MT, int NWW, int WM, int WN, class AP, int KPB = 1, bool SH = false, bool F16 = false>
 __device__ __forceinline__ void tile_mma_lds(const AP& ap, rsrc_t Wp, uint32_t wbase, uint32_t wstride,
                                              int nwin, int s0, int ns, uint8_t* lds,
                                              typename Stage<I8>::Acc (&acc)[MT][NWW * 4]) {
@@ -2559,7 +2595,7 @@ __device__ __forceinline__ void tile_mma_lds(const AP& ap, rsrc_t Wp, uint32_t w
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int j = 0; j < NWW * 4; ++j) acc[mt][j] = mfma(bf[j], af[mt], acc[mt][j]);
+        for (int j = 0; j < NWW * 4; ++j) acc[mt][j] = mma16<F16>(bf[j], af[mt], acc[mt][j]);
     }
   };
   const int ngr = (ns + KPB - 1) / KPB;
@@ -2653,7 +2689,8 @@ __global__ __launch_bounds__(64 * WM * WN) void k1_tiled(Dims d, Ptrs p, PackGeo
 // K3t: grid (token tiles fastest, then groups of W^UqQr windows).  Nope
 // windows go to q^C (bf16, workspace); a rope window goes through a per-wave
 // LDS tile of 16 tokens x 64 columns to RoPE and queryRopeOut.
-template <bool I8, int MT, int NWW, int WM, int WN, int D, bool LC = false, int KPB = 1, bool SH = false>
+template <bool I8, int MT, int NWW, int WM, int WN, int D, bool LC = false, int KPB = 1, bool SH = false,
+          bool F16 = false>
 __global__ __launch_bounds__(64 * WM * WN) void k3_tiled(Dims d, Ptrs p, PackGeo pg, int mtiles) {
   using St = Stage<I8>;
   constexpr int BM = 16 * MT * WM, GW = NWW * WN;
@@ -2725,7 +2762,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k3_tiled(Dims d, Ptrs p, PackGeo
             const int col = 16 * ct + 4 * g;
             if (col < wq)
               *reinterpret_cast<uint2*>(qcb + packed_offset(m, 64 * part + col, qtile, false)) =
-                  pack_bf16x4(v[ct][0], v[ct][1], v[ct][2], v[ct][3]);
+                  pack16x4<F16>(v[ct][0], v[ct][1], v[ct][2], v[ct][3]);
           }
         }
       } else {
@@ -2748,11 +2785,11 @@ __global__ __launch_bounds__(64 * WM * WN) void k3_tiled(Dims d, Ptrs p, PackGeo
             for (int r = 0; r < 4; ++r) {
               const int ii = i0 + r;
               const float a = e[c * 65 + ii], b = e[c * 65 + ii + hf];
-              lo[r] = a * bf2f(cs[ii]) - b * bf2f(sn[ii]);
-              hi[r] = b * bf2f(cs[ii + hf]) + a * bf2f(sn[ii + hf]);
+              lo[r] = a * ld16<F16>(cs[ii]) - b * ld16<F16>(sn[ii]);
+              hi[r] = b * ld16<F16>(cs[ii + hf]) + a * ld16<F16>(sn[ii + hf]);
             }
-            *reinterpret_cast<uint2*>(o + i0) = pack_bf16x4(lo[0], lo[1], lo[2], lo[3]);
-            *reinterpret_cast<uint2*>(o + i0 + hf) = pack_bf16x4(hi[0], hi[1], hi[2], hi[3]);
+            *reinterpret_cast<uint2*>(o + i0) = pack16x4<F16>(lo[0], lo[1], lo[2], lo[3]);
+            *reinterpret_cast<uint2*>(o + i0 + hf) = pack16x4<F16>(hi[0], hi[1], hi[2], hi[3]);
           }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -3151,7 +3188,7 @@ __global__ __launch_bounds__(512) void k3_ring(Dims d, Ptrs p, PackGeo pg) {
   }
 }
 
-template <int MT, int NWW, int WM, int WN, int D, bool Q8, bool LC = false, bool HF = false>
+template <int MT, int NWW, int WM, int WN, int D, bool Q8, bool LC = false, bool HF = false, bool F16 = false>
 __global__ __launch_bounds__(64 * WM * WN) void k4_tiled(Dims d, Ptrs p, PackGeo pg, int mtiles,
                                                       int cgroups) {
   constexpr int BM = 16 * MT * WM, GW = NWW * WN;
@@ -3181,7 +3218,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k4_tiled(Dims d, Ptrs p, PackGeo
   if constexpr (LC) {
     __shared__ __attribute__((aligned(16))) uint8_t ring[2 * (MT * WM + NWW * WN * 4) * 1024];
     const int mb = mtile * BM, j0 = cg * GW;
-    tile_mma_lds<false, MT, NWW, WM, WN>(
+    tile_mma_lds<false, MT, NWW, WM, WN, APacked<false, MT * WM>, 1, false, F16>(
         tiles_from<false, MT * WM>(reinterpret_cast<const uint8_t*>(p.qc) + qh, qtile, (d.T + 15) / 16, mb),
         make_rsrc(p.packed, pg.total), uint32_t(pg.off_uk + int64_t(h * pg.uk_w + j0) * pg.nst_d * 4096),
         uint32_t(pg.nst_d * 4096), pg.uk_w - j0, 0, mb < d.T ? pg.nst_d : 0, ring, acc);
@@ -3189,7 +3226,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k4_tiled(Dims d, Ptrs p, PackGeo
     const int ns = m0 < d.T ? pg.nst_d : 0;
     const auto ap = tiles_from<false, MT>(reinterpret_cast<const uint8_t*>(p.qc) + qh, qtile,
                                           (d.T + 15) / 16, m0);
-    tile_mma<false, MT, NWW, D>(ap, make_rsrc(p.packed, pg.total), wb, 0, ns, acc);
+    tile_mma<false, MT, NWW, D, decltype(ap), F16>(ap, make_rsrc(p.packed, pg.total), wb, 0, ns, acc);
   }
   const int g = lane >> 4, c = lane & 15;
   if constexpr (!Q8) {
@@ -3212,7 +3249,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k4_tiled(Dims d, Ptrs p, PackGeo
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
           const auto& a = acc[mt][i * 4 + ct];
-          *reinterpret_cast<uint2*>(tile + c * 144 + (16 * ct + 4 * g) * 2) = pack_bf16x4(a[0], a[1], a[2], a[3]);
+          *reinterpret_cast<uint2*>(tile + c * 144 + (16 * ct + 4 * g) * 2) = pack16x4<F16>(a[0], a[1], a[2], a[3]);
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -3381,7 +3418,8 @@ TiledPlan tiled_plan(const mla_prolog_desc& d, int64_t T) {
   const PackGeo g = geo_of(d);
   const int tiles = g.win_dq + g.win_kr;
   tp.large = T >= kTiledLargeT;
-  tp.ring = !tp.large && T <= 256 && g.nope_w == 2 && d.Dr == 64 && g.nst_cq <= kRingStages && kRingK3;
+  tp.ring = !tp.large && T <= 256 && g.nope_w == 2 && d.Dr == 64 && g.nst_cq <= kRingStages &&
+            d.float_dtype != MLA_FP16 && kRingK3;
   tp.mt = T <= 64 ? 4 : 8;
   // medium shapes: LDS-staged blocks above 128 tokens; for an int8 product
   // also from 65 tokens on, in 128-token blocks (the int8 k-stages are twice
@@ -3498,6 +3536,10 @@ mla_status check_desc_core(const mla_prolog_desc* d) {
     return MLA_ERR_PARAM_INVALID;
   if (d->concat && (d->query_dtype != MLA_BF16 || d->cache_dtype != MLA_BF16)) return MLA_ERR_PARAM_INVALID;
   if (d->x_quant_only && d->in_dtype != MLA_INT8_STATIC) return MLA_ERR_PARAM_INVALID;
+  // fp16 tensors: the preprocess page's FLOAT16 input, its static scenario
+  if ((d->float_dtype != MLA_BF16 && d->float_dtype != MLA_FP16) || d->reserved != 0)
+    return MLA_ERR_PARAM_INVALID;
+  if (d->float_dtype == MLA_FP16 && d->in_dtype != MLA_INT8_STATIC) return MLA_ERR_PARAM_INVALID;
   if (d->in_dtype == MLA_INT8_STATIC && (!(d->eps_x >= 0.0) || !std::isfinite(d->eps_x)))
     return MLA_ERR_PARAM_INVALID;
   if (d->block_num < 0 || d->max_tokens < 0 || d->max_tokens > (1 << 20))
@@ -3569,8 +3611,8 @@ mla_status check_tensors(const mla_prolog_desc* d, const mla_prolog_tensors* t, 
     if (reinterpret_cast<uintptr_t>(q) & 1u) return MLA_ERR_PARAM_INVALID;
   if ((t->bias_dqkv && !aligned4(t->bias_dqkv)) || (t->bias_uq_qr && !aligned4(t->bias_uq_qr)))
     return MLA_ERR_PARAM_INVALID;
-  // the unpacked kernels read (k, n) weights only
-  if (d->weights_nk && !t->packed_weights) return MLA_ERR_UNSUPPORTED;
+  // the unpacked kernels read (k, n) bf16 weights only
+  if ((d->weights_nk || d->float_dtype == MLA_FP16) && !t->packed_weights) return MLA_ERR_UNSUPPORTED;
   // the scales each scenario takes: all four in full quantisation, that of
   // weightUqQr alone in partial quantisation, none without quantisation
   const float* sc[] = {t->scale_x, t->scale_w_dq, t->scale_w_uq_qr, t->scale_w_dkv_kr};
@@ -3674,12 +3716,12 @@ void launch_k4(int ntw, dim3 grid, hipStream_t s, const Dims& d, const Ptrs& p) 
 }
 
 // K2 with eight waves per token when there are few tokens, one otherwise.
-template <bool I8D, bool I8U>
+template <bool I8D, bool I8U, bool F16 = false>
 void launch_norm(hipStream_t s, const Dims& d, const Ptrs& p, int S, int cq_nst) {
   if constexpr (I8D && I8U) {
-    if (p.beta_cq) {   // the static scenario
-      if (d.T <= 512) k2_norm<true, true, true, 8, 1, 1><<<dim3(d.T), 512, 0, s>>>(d, p, S, cq_nst);
-      else k2_norm<true, true, true, 1, 4, 1><<<dim3((d.T + 3) / 4), 256, 0, s>>>(d, p, S, cq_nst);
+    if (p.beta_cq) {   // the static scenario (fp16 tensors when F16)
+      if (d.T <= 512) k2_norm<true, true, true, 8, 1, 1, F16><<<dim3(d.T), 512, 0, s>>>(d, p, S, cq_nst);
+      else k2_norm<true, true, true, 1, 4, 1, F16><<<dim3((d.T + 3) / 4), 256, 0, s>>>(d, p, S, cq_nst);
       return;
     }
   }
@@ -3783,7 +3825,7 @@ void launch_ring(hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g) 
 }
 
 // Tiled run on packed weights (token counts above the streaming range).
-template <bool I8D, bool I8U, int MT, class Mark>
+template <bool I8D, bool I8U, int MT, class Mark, bool F16 = false>
 void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g,
                   bool q8, bool pair_ok, Mark& mark) {
   const dim3 g1(tp.m1 * tp.ngrp1 * tp.S), g3(tp.m3 * tp.ngrp3);
@@ -3793,7 +3835,7 @@ void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs&
     k1_tiled<I8D, 2, 1, 4, 2, 2, true, 1, true><<<g1, 512, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
   else k1_tiled<I8D, MT, 1, 1, 1, 2><<<g1, 64, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
   mark(1);
-  launch_norm<I8D, I8U>(s, d, p, tp.S, g.nst_cq);
+  launch_norm<I8D, I8U, F16>(s, d, p, tp.S, g.nst_cq);
   mark(2);
   // with paired blocks allowed (and at most eight W^UK windows of four D
   // stages), the W^UK product runs in the same launch
@@ -3806,11 +3848,11 @@ void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs&
       launch_ring<I8U, false, false>(s, d, p, g);
     }
   } else if (tp.k3v == 1) {
-    k3_tiled<I8U, 2, 1, 8, 2, 2, true, 1, true><<<g3, 1024, 0, s>>>(d, p, g, tp.m3);
+    k3_tiled<I8U, 2, 1, 8, 2, 2, true, 1, true, F16><<<g3, 1024, 0, s>>>(d, p, g, tp.m3);
   } else if (I8U && tp.k3v == 2) {
-    k3_tiled<I8U, 1, 1, 8, 2, 2, true, 1, true><<<g3, 1024, 0, s>>>(d, p, g, tp.m3);
+    k3_tiled<I8U, 1, 1, 8, 2, 2, true, 1, true, F16><<<g3, 1024, 0, s>>>(d, p, g, tp.m3);
   } else {
-    k3_tiled<I8U, 4, 1, 1, 1, 2><<<g3, 64, 0, s>>>(d, p, g, tp.m3);
+    k3_tiled<I8U, 4, 1, 1, 1, 2, false, 1, false, F16><<<g3, 64, 0, s>>>(d, p, g, tp.m3);
   }
   if (uk) {
     // one kernel did both products; the profile books them to the first
@@ -3820,33 +3862,33 @@ void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs&
   }
   mark(3);
   if (q8) k4_tiled<4, 1, 1, 8, 2, true, false, true><<<dim3(tp.m4q * d.N), 512, 0, s>>>(d, p, g, tp.m4q, 1);
-  else k4_tiled<MT, 1, 1, 8, 2, false, false, true><<<dim3(tp.m4 * tp.cg4 * d.N), 512, 0, s>>>(d, p, g, tp.m4,
+  else k4_tiled<MT, 1, 1, 8, 2, false, false, true, F16><<<dim3(tp.m4 * tp.cg4 * d.N), 512, 0, s>>>(d, p, g, tp.m4,
                                                                                            tp.cg4);
   mark(4);
 }
 
-template <bool I8D, bool I8U, class Mark>
+template <bool I8D, bool I8U, class Mark, bool F16 = false>
 void tiled_large(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g,
                  bool q8, Mark& mark) {
   k1_tiled<I8D, 4, 1, 4, 4, 2, true><<<dim3(tp.m1 * tp.ngrp1 * tp.S), 1024, 0, s>>>(d, p, g, tp.sps,
                                                                                    tp.m1, tp.ngrp1);
   mark(1);
-  launch_norm<I8D, I8U>(s, d, p, tp.S, g.nst_cq);
+  launch_norm<I8D, I8U, F16>(s, d, p, tp.S, g.nst_cq);
   mark(2);
-  k3_tiled<I8U, 4, 1, 4, 4, 2, true><<<dim3(tp.m3 * tp.ngrp3), 1024, 0, s>>>(d, p, g, tp.m3);
+  k3_tiled<I8U, 4, 1, 4, 4, 2, true, 1, false, F16><<<dim3(tp.m3 * tp.ngrp3), 1024, 0, s>>>(d, p, g, tp.m3);
   mark(3);
   if (q8) k4_tiled<4, 1, 1, 8, 2, true, false, true><<<dim3(tp.m4q * d.N), 512, 0, s>>>(d, p, g, tp.m4q, 1);
-  else k4_tiled<4, 1, 4, 4, 2, false, true, true><<<dim3(tp.m4 * tp.cg4 * d.N), 1024, 0, s>>>(d, p, g, tp.m4,
+  else k4_tiled<4, 1, 4, 4, 2, false, true, true, F16><<<dim3(tp.m4 * tp.cg4 * d.N), 1024, 0, s>>>(d, p, g, tp.m4,
                                                                                           tp.cg4);
   mark(4);
 }
 
-template <bool I8D, bool I8U, class Mark>
+template <bool I8D, bool I8U, class Mark, bool F16 = false>
 void tiled_run(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g,
                bool q8, bool pair_ok, Mark& mark) {
-  if (tp.large) tiled_large<I8D, I8U>(tp, s, d, p, g, q8, mark);
-  else if (tp.mt == 4) tiled_medium<I8D, I8U, 4>(tp, s, d, p, g, q8, pair_ok, mark);
-  else tiled_medium<I8D, I8U, 8>(tp, s, d, p, g, q8, pair_ok, mark);
+  if (tp.large) tiled_large<I8D, I8U, Mark, F16>(tp, s, d, p, g, q8, mark);
+  else if (tp.mt == 4) tiled_medium<I8D, I8U, 4, Mark, F16>(tp, s, d, p, g, q8, pair_ok, mark);
+  else tiled_medium<I8D, I8U, 8, Mark, F16>(tp, s, d, p, g, q8, pair_ok, mark);
 }
 
 template <class Mark>
@@ -3854,7 +3896,9 @@ void launch_tiled(hipStream_t s, const Dims& d, const Ptrs& p, const mla_prolog_
                   bool pair_ok, Mark& mark) {
   const PackGeo g = geo_of(dd);
   const TiledPlan tp = tiled_plan(dd, d.T);
-  if (down_i8(dd)) tiled_run<true, true>(tp, s, d, p, g, q8, pair_ok, mark);
+  // fp16 tensors: the static scenario only, on these kernels at every T
+  if (dd.float_dtype == MLA_FP16) tiled_run<true, true, Mark, true>(tp, s, d, p, g, q8, pair_ok, mark);
+  else if (down_i8(dd)) tiled_run<true, true>(tp, s, d, p, g, q8, pair_ok, mark);
   else if (up_i8(dd)) tiled_run<false, true>(tp, s, d, p, g, q8, pair_ok, mark);
   else tiled_run<false, false>(tp, s, d, p, g, q8, pair_ok, mark);
 }
@@ -4085,12 +4129,13 @@ mla_status enqueue(const RunCtx& c, const mla_prolog_tensors* t, int64_t T, hipS
     xq.offset = t->quant_offset_x;
     xq.out = ws + lay.x8;
     xq.T = d.T; xq.He = d.He; xq.eps = dd.eps_x;
-    k0_xquant<<<dim3(unsigned(T)), kXqThreads, 0, s>>>(xq);
+    if (dd.float_dtype == MLA_FP16) k0_xquant<true><<<dim3(unsigned(T)), kXqThreads, 0, s>>>(xq);
+    else k0_xquant<false><<<dim3(unsigned(T)), kXqThreads, 0, s>>>(xq);
     p.x = xq.out;
   }
   p.packed = static_cast<const uint8_t*>(t->packed_weights);
   FusedGeo fg;
-  if (p.packed && pl.stream && c.fused_ok && fused_geo(dd, &fg)) {
+  if (p.packed && pl.stream && c.fused_ok && dd.float_dtype != MLA_FP16 && fused_geo(dd, &fg)) {
     const PackGeo g = geo_of(dd);
     if (pl.mt1 == 1) k_fused<1><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g, fg);
     else k_fused<2><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g, fg);
@@ -4098,8 +4143,8 @@ mla_status enqueue(const RunCtx& c, const mla_prolog_tensors* t, int64_t T, hipS
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? MLA_OK : MLA_ERR_RUNTIME;
   }
-  if (p.packed && (!pl.stream || packed_fits(dd))) {
-    if (pl.stream) launch_packed(pl, s, d, p, dd, q8, c.pair_ok, mark);
+  if (p.packed && (!pl.stream || packed_fits(dd) || dd.float_dtype == MLA_FP16)) {
+    if (pl.stream && dd.float_dtype != MLA_FP16) launch_packed(pl, s, d, p, dd, q8, c.pair_ok, mark);
     else launch_tiled(s, d, p, dd, q8, c.pair_ok, mark);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? MLA_OK : MLA_ERR_RUNTIME;

@@ -42,7 +42,7 @@ typedef enum {
   MLA_ERR_UNSUPPORTED = 561002    /* legal on the page but no kernel tiling for it here */
 } mla_status;
 
-typedef enum { MLA_BF16 = 0, MLA_INT8 = 1, MLA_INT8_PARTIAL = 2, MLA_INT8_STATIC = 3 } mla_dtype;
+typedef enum { MLA_BF16 = 0, MLA_INT8 = 1, MLA_INT8_PARTIAL = 2, MLA_INT8_STATIC = 3, MLA_FP16 = 4 } mla_dtype;
 
 /*
  * Problem description, fixed at create time (the page's "Shape format field
@@ -109,6 +109,17 @@ typedef enum { MLA_BF16 = 0, MLA_INT8 = 1, MLA_INT8_PARTIAL = 2, MLA_INT8_STATIC
  *   need packed_weights (the unpacked kernels read (k, n) weights only:
  *   MLA_ERR_UNSUPPORTED otherwise).  0: (k, n) row-major.
  * x_quant_only: see MLA_INT8_STATIC; 0 in the other scenarios.
+ * float_dtype MLA_FP16 (with in_dtype MLA_INT8_STATIC only; else
+ *   MLA_ERR_PARAM_INVALID): the preprocess page's FLOAT16 input (its
+ *   parameter table, input "FLOAT16, BFLOAT16", and the tensors whose dtype
+ *   it ties to the input's).  tokenX, gamma_x/beta_x/quant_scale_x,
+ *   gamma_cq/beta_cq/quant_scale_cq, gamma_ckv, rope_sin/rope_cos and
+ *   weightUk are fp16, and so are queryOut, queryRopeOut and both caches;
+ *   q^C enters the W^UK product rounded to fp16.  The deScale arguments stay
+ *   fp32 (the page's INT64 deScale of the FLOAT16 input is an encoding of the
+ *   same per-channel scale that this boundary does not take).  Runs need
+ *   packed_weights (MLA_ERR_UNSUPPORTED otherwise).  MLA_BF16: those tensors
+ *   are bf16.
  * check_index 1: every run first copies cacheIndex to the host, which waits
  *   for the stream, and returns MLA_ERR_PARAM_INVALID with nothing enqueued
  *   if an entry lies outside [0, block_num*block_size) (the prolog page's
@@ -136,6 +147,8 @@ typedef struct {
   int32_t x_quant_only; /* 0 or 1 */
   int32_t check_index; /* 0 or 1 (a debugging aid, see below) */
   double eps_x;
+  int32_t float_dtype; /* mla_dtype: MLA_BF16, or MLA_FP16 (MLA_INT8_STATIC only) */
+  int32_t reserved;    /* 0 */
 } mla_prolog_desc;
 
 /*

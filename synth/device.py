@@ -9,10 +9,10 @@ import numpy as np
 import torch
 
 
-def _tensor(a: np.ndarray, device) -> torch.Tensor:
+def _tensor(a: np.ndarray, device, half=torch.bfloat16) -> torch.Tensor:
     a = np.ascontiguousarray(a)
-    if a.dtype == np.uint16:          # bf16 bit patterns
-        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    if a.dtype == np.uint16:          # bf16 (or fp16) bit patterns
+        return torch.from_numpy(a.view(np.int16)).to(device).view(half)
     return torch.from_numpy(a).to(device)
 
 
@@ -46,29 +46,33 @@ def upload(inp: Dict[str, object], device="cuda:0", query_int8=None) -> Dict[str
     for k in ("quant_scale_ckv", "quant_scale_ckr"):
         if inp.get(k) is not None:
             names[k] = k
-    out = {lib_name: _tensor(np.asarray(inp[key]), device) for key, lib_name in names.items()
+    # the 16-bit float tensors are fp16 in the static scenario's FLOAT16
+    # variant, bf16 otherwise
+    half = torch.float16 if inp.get("fp16", False) else torch.bfloat16
+    out = {lib_name: _tensor(np.asarray(inp[key]), device, half) for key, lib_name in names.items()
            if key in inp}
     concat = bool(inp.get("concat", False))
     out["query_out"] = torch.zeros((T, d.N, d.Hckv + d.Dr if concat else d.Hckv),
-                                   dtype=torch.int8 if q8 else torch.bfloat16, device=device)
+                                   dtype=torch.int8 if q8 else half, device=device)
     if not concat:
-        out["query_rope_out"] = torch.zeros((T, d.N, d.Dr), dtype=torch.bfloat16, device=device)
+        out["query_rope_out"] = torch.zeros((T, d.N, d.Dr), dtype=half, device=device)
     if q8:
         out["dequant_scale_q_nope"] = torch.zeros((T, d.N), dtype=torch.float32, device=device)
     return out
 
 
 def bits(t: torch.Tensor) -> np.ndarray:
-    """Host copy of a device tensor; bf16 as uint16 bit patterns."""
+    """Host copy of a device tensor; bf16 and fp16 as uint16 bit patterns."""
     t = t.detach().cpu()
-    if t.dtype == torch.bfloat16:
+    if t.dtype in (torch.bfloat16, torch.float16):
         return t.view(torch.int16).numpy().view(np.uint16)
     return t.numpy()
 
 
 def desc_args(inp: Dict[str, object], max_tokens=None, query_int8=None) -> Dict[str, object]:
     """Keyword arguments of ``make_desc`` for these inputs (in_dtype 0 bf16,
-    1 int8 full quantisation, 2 partial quantisation, 3 the static scenario)."""
+    1 int8 full quantisation, 2 partial quantisation, 3 the static scenario;
+    float_dtype 4 for its fp16 tensors)."""
     d = inp["dims"]
     quant = bool(inp["quant"])
     q8 = quant if query_int8 is None else bool(query_int8)
@@ -81,4 +85,4 @@ def desc_args(inp: Dict[str, object], max_tokens=None, query_int8=None) -> Dict[
                 query_dtype=int(q8), cache_dtype=int(bool(inp.get("kv_quant", False))),
                 concat=int(bool(inp.get("concat", False))), weights_nk=int(bool(inp.get("weight_nk", False))),
                 x_quant_only=int(not inp.get("x_norm", True)) if inp.get("preprocess", False) else 0,
-                eps_x=float(inp.get("eps_x", 1e-5)))
+                eps_x=float(inp.get("eps_x", 1e-5)), float_dtype=4 if inp.get("fp16", False) else 0)

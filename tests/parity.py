@@ -30,15 +30,43 @@ SCALE_RTOL = 1e-2
 TIE_BAND = 1e-3
 
 
+#: fp16 outputs (the static scenario's FLOAT16 variant) take the bf16 bound
+#: above, which holds the int8 decisions on x and c^Q that fp32 and double may
+#: take apart; that the outputs carry fp16's precision and not less is checked
+#: on top: the median relative error stays below 2^-11, one fp16 half-step at
+#: the bottom of a binade, where rounding to bf16 anywhere on the way would
+#: put the median near 2^-10
+FP16_MEDIAN_REL = 2.0 ** -11
+
+
 def bf16_f64(bits) -> np.ndarray:
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
     return b.view(np.float32).astype(np.float64)
 
 
-def assert_bf16_close(got_bits, ref_bits, what, extra=None):
-    """``extra``: an allowance per element on top of the tolerance."""
-    g, r = bf16_f64(got_bits), bf16_f64(ref_bits)
+def fp16_f64(bits) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(bits, dtype=np.uint16)).view(np.float16).astype(np.float64)
+
+
+def half_f64(bits, fp16=False) -> np.ndarray:
+    return fp16_f64(bits) if fp16 else bf16_f64(bits)
+
+
+def assert_fp16_precision(g, r, what):
+    m = np.abs(r) > 1e-3
+    if m.sum() < 64:
+        return
+    rel = float(np.median(np.abs(g[m] - r[m]) / np.abs(r[m])))
+    assert rel < FP16_MEDIAN_REL, f"{what}: median relative error {rel:.3e} is not fp16's"
+
+
+def assert_bf16_close(got_bits, ref_bits, what, extra=None, fp16=False):
+    """``extra``: an allowance per element on top of the tolerance.  With
+    ``fp16`` both sides are fp16 bit patterns (see FP16_MEDIAN_REL)."""
+    g, r = half_f64(got_bits, fp16), half_f64(ref_bits, fp16)
     assert g.shape == r.shape, (what, g.shape, r.shape)
+    if fp16:
+        assert_fp16_precision(g, r, what)
     tol = BF16_ATOL + BF16_RTOL * np.abs(r)
     if extra is not None:
         tol = tol + extra
@@ -106,17 +134,18 @@ def tie_allowance(inp, ref, rows):
     return allow_qr, allow_qn, namb
 
 
-def check_queries(got, ref, rows, int8_query, allow=None):
+def check_queries(got, ref, rows, int8_query, allow=None, fp16=False):
     """got: host arrays of the full run; ref: oracle outputs for ``rows``;
-    allow: None, or the (queryRopeOut, queryOut) allowances of tie_allowance."""
+    allow: None, or the (queryRopeOut, queryOut) allowances of tie_allowance;
+    fp16: the outputs are fp16 bit patterns."""
     allow_qr, allow_qn = (None, None) if allow is None else allow
-    assert_bf16_close(got["query_rope_out"][rows], ref["query_rope_out"], "query_rope_out", allow_qr)
+    assert_bf16_close(got["query_rope_out"][rows], ref["query_rope_out"], "query_rope_out", allow_qr, fp16)
     if int8_query:
         assert_int8_close(got["query_out"][rows], ref["query_out"], "query_out (int8)")
         assert_scales_close(got["dequant_scale_q_nope"][rows], ref["dequant_scale_q_nope"],
                             "dequant_scale_q_nope")
     else:
-        assert_bf16_close(got["query_out"][rows], ref["query_out"], "query_out", allow_qn)
+        assert_bf16_close(got["query_out"][rows], ref["query_out"], "query_out", allow_qn, fp16)
 
 
 def assert_cache_codes(got, ref_codes, v, scale, what):
@@ -150,6 +179,7 @@ def check_caches(inp, kv_after, kr_after, ref, rows):
     assert np.array_equal(kv1[~named], kv0[~named]), "kv cache changed outside the named slots"
     assert np.array_equal(kr1[~named], kr0[~named]), "kr cache changed outside the named slots"
     kv8 = bool(inp.get("kv_quant", False))
+    f16 = bool(inp.get("fp16", False))
     kr8 = kv8 and bool(inp.get("partial", False))
     for r, t in enumerate(rows):
         s = int(idx[t])
@@ -158,11 +188,11 @@ def check_caches(inp, kv_after, kr_after, ref, rows):
                 assert_cache_codes(kv1[s], ref["kv_rows"][r], ref["c_kv"][r], inp["quant_scale_ckv"],
                                    f"kv cache slot {s} (token {t})")
             else:
-                assert_bf16_close(kv1[s], ref["kv_rows"][r], f"kv cache slot {s} (token {t})")
+                assert_bf16_close(kv1[s], ref["kv_rows"][r], f"kv cache slot {s} (token {t})", fp16=f16)
             if kr8:
                 assert_cache_codes(kr1[s], ref["kr_rows"][r], ref["k_r"][r], inp["quant_scale_ckr"],
                                    f"kr cache slot {s} (token {t})")
             else:
-                assert_bf16_close(kr1[s], ref["kr_rows"][r], f"kr cache slot {s} (token {t})")
+                assert_bf16_close(kr1[s], ref["kr_rows"][r], f"kr cache slot {s} (token {t})", fp16=f16)
     if valid.size:
         assert not np.all(kv1[valid] == kv0[valid], axis=1).any(), "a named kv slot was not written"

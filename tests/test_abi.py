@@ -96,6 +96,10 @@ def test_valid_descriptions():
     t = fake_tensors(static=True); t["gamma_x"] = None; t["beta_x"] = None
     assert mla.validate(model_desc(in_dtype=3, x_quant_only=1), t, 32) == mla.MLA_OK
     assert mla.validate(model_desc(concat=1), fake_tensors(concat=True), 32) == mla.MLA_OK
+    # the static scenario's FLOAT16 input, split and concatenated
+    assert mla.validate(model_desc(in_dtype=3, float_dtype=mla.MLA_FP16), fake_tensors(static=True), 32) == mla.MLA_OK
+    assert mla.validate(model_desc(in_dtype=3, concat=1, weights_nk=1, float_dtype=mla.MLA_FP16),
+                        fake_tensors(static=True, concat=True), 32) == mla.MLA_OK
     tiny = mla.make_desc(256, 64, 32, 2, 16, 8, 4, 16, 4)
     assert mla.validate(tiny, fake_tensors(), 4) == mla.MLA_OK
     assert mla.workspace_bytes(model_desc()) > 0
@@ -127,6 +131,12 @@ def test_valid_descriptions():
     (dict(in_dtype=2, query_dtype=1), mla.MLA_ERR_PARAM_INVALID),   # int8 q^N: full quantisation only
     (dict(in_dtype=2, Hcq=1544), mla.MLA_ERR_UNSUPPORTED),
     (dict(in_dtype=2, D=120), mla.MLA_ERR_UNSUPPORTED),
+    (dict(float_dtype=mla.MLA_FP16), mla.MLA_ERR_PARAM_INVALID),        # fp16: the static scenario only
+    (dict(in_dtype=1, float_dtype=mla.MLA_FP16), mla.MLA_ERR_PARAM_INVALID),
+    (dict(in_dtype=2, float_dtype=mla.MLA_FP16), mla.MLA_ERR_PARAM_INVALID),
+    (dict(in_dtype=3, float_dtype=1), mla.MLA_ERR_PARAM_INVALID),
+    (dict(in_dtype=3, float_dtype=5), mla.MLA_ERR_PARAM_INVALID),
+    (dict(in_dtype=3, float_dtype=-1), mla.MLA_ERR_PARAM_INVALID),
     (dict(cache_dtype=1), mla.MLA_ERR_PARAM_INVALID),             # quantised caches: int8 scenarios only
     (dict(in_dtype=1, cache_dtype=2), mla.MLA_ERR_PARAM_INVALID),
 ])
@@ -204,6 +214,14 @@ def test_bad_static_and_concat_arguments():
     t = fake_tensors(); t["packed_weights"] = None
     assert mla.validate(model_desc(weights_nk=1), t, 8) == mla.MLA_ERR_UNSUPPORTED
     assert mla.validate(model_desc(), t, 8) == mla.MLA_OK
+    # and so do fp16 tensors
+    t = fake_tensors(static=True); t["packed_weights"] = None
+    assert mla.validate(model_desc(in_dtype=3, float_dtype=mla.MLA_FP16), t, 8) == mla.MLA_ERR_UNSUPPORTED
+    assert mla.validate(model_desc(in_dtype=3), t, 8) == mla.MLA_OK
+    # the reserved word must be zero
+    d = model_desc(in_dtype=3)
+    d.reserved = 1
+    assert mla.validate(d) == mla.MLA_ERR_PARAM_INVALID
 
 
 def test_empty_run_needs_no_tensors():

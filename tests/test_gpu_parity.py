@@ -81,7 +81,7 @@ def full_check(inp, query_int8=None, rows=None, packed=False, repeat=1, prerun_n
         aqr, aqn, namb = tie_allowance(inp, ref, rows)
         allow = (aqr, aqn)
         say(f"  c^Q codes within the tie band: {namb}")
-    check_queries(got, ref, rows, q8, allow)
+    check_queries(got, ref, rows, q8, allow, fp16=bool(inp.get("fp16", False)))
     check_caches(inp, got["kv_cache"], got["kr_cache"], ref, rows)
     return got
 
@@ -694,6 +694,47 @@ def test_static_row_major(concat):
 def test_full_size_static_decode_packed():
     inp = synth.make_inputs(synth.workload("pre_decode_t32"))
     full_check(inp, rows=np.arange(32), packed=True)
+
+
+# the same scenario with the page's FLOAT16 input: every 16-bit float tensor,
+# and the outputs, fp16; the tiled kernels at every T
+STATIC_F16 = {
+    "pre_f16_t4": synth.workload("tiny_pre_f16_t4"),
+    "pre_f16_t37": _pre("pre_f16_t37", 37, Dims(He=272, Hcq=80, Hckv=48, N=3, D=32, Dr=16), 191, fp16=True),
+    "pre_f16_t17_split": _pre("pre_f16_t17_split", 17, Dims(He=512, Hcq=256, Hckv=256, N=8, D=128, Dr=64), 192,
+                              fp16=True, concat=False),
+    "pre_f16_t70": _pre("pre_f16_t70", 70, MID, 193, fp16=True),
+    "pre_f16_t130_split": _pre("pre_f16_t130_split", 130, Dims(He=1024, Hcq=192, Hckv=512, N=3, D=128, Dr=64),
+                               194, fp16=True, concat=False),
+    "pre_f16_t600": _pre("pre_f16_t600", 600, Dims(He=512, Hcq=128, Hckv=64, N=2, D=32, Dr=16), 195, fp16=True),
+    "pre_f16_t2100": _pre("pre_f16_t2100", 2100, Dims(He=512, Hcq=128, Hckv=64, N=2, D=32, Dr=16), 196,
+                          fp16=True),
+}
+
+
+@pytest.mark.parametrize("name", list(STATIC_F16))
+def test_static_fp16_packed(name):
+    full_check(synth.make_inputs(STATIC_F16[name]), packed=True, repeat=2, prerun_negated=True)
+
+
+def test_static_fp16_without_input_norm_packed():
+    full_check(synth.make_inputs(_pre("pre_f16_xq_t37", 37, Dims(He=272, Hcq=80, Hckv=48, N=3, D=32, Dr=16), 197,
+                                      x_norm=False, fp16=True)), packed=True)
+
+
+def test_full_size_static_fp16_decode_packed():
+    inp = synth.make_inputs(synth.workload("pre_f16_decode_t32"))
+    full_check(inp, rows=np.arange(32), packed=True)
+
+
+def test_static_fp16_needs_packed_weights():
+    inp = synth.make_inputs(STATIC_F16["pre_f16_t37"])
+    say("case static fp16 without packed weights")
+    t = dev.upload(inp)
+    with mla.MlaProlog(mla.make_desc(**dev.desc_args(inp))) as h:
+        with pytest.raises(mla.MlaError) as e:
+            h.run(t, int(inp["T"]))
+    assert e.value.status == mla.MLA_ERR_UNSUPPORTED
 
 
 CONCAT_BF16 = {

@@ -15,7 +15,7 @@ here without the oracle:
 
 The cases take the execution paths that write cache rows: the one-launch
 small-T kernel, the paired kernel, the tiled medium and large paths, the
-row-major kernels, int8 caches and the concatenated layout.  The debugging
+row-major kernels, int8 caches, the concatenated layout and fp16 tensors.  The debugging
 check of cacheIndex (check_index) is covered at the end.
 """
 import sys
@@ -60,6 +60,9 @@ CASES = {
     "static_concat_t37": (custom_workload("sc_pre_t37", T=37, dims=Dims(He=272, Hcq=80, Hckv=48, N=3, D=32, Dr=16),
                                           block_num=4, block_size=16, preprocess=True, concat=True,
                                           weight_nk=True, seed=208), True, {}),
+    "static_fp16_t70": (custom_workload("sc_pre16_t70", T=70, dims=Dims(He=1024, Hcq=256, Hckv=512, N=4, D=128,
+                                                                      Dr=64), block_num=8, block_size=16,
+                                        preprocess=True, weight_nk=True, fp16=True, seed=209), True, {}),
 }
 
 

@@ -47,3 +47,27 @@ def test_allowance_does_not_hide_a_planted_mistake(mutation):
     bad = oracle.run(inp, mutation=mutation)
     with pytest.raises(AssertionError):
         check_queries(bad, ref, rows, False, tie_allowance(inp, ref, rows)[:2])
+
+
+def _bf16_round_as_fp16(bits):
+    # fp16 values rounded to bf16 (nearest even), then written back as fp16
+    v = np.ascontiguousarray(np.asarray(bits, np.uint16)).view(np.float16).astype(np.float32)
+    u = v.view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float16).view(np.uint16)
+
+
+def test_fp16_outputs_must_carry_fp16_precision():
+    # the oracle's own fp16 outputs pass; the same values rounded through
+    # bf16 stay inside the bf16 bound but fail the fp16 precision check
+    inp = synth.make_inputs(synth.workload("tiny_pre_f16_t4"))
+    ref = oracle.run(inp, caches=False)
+    if inp.get("concat", False):
+        d = inp["dims"]
+        q = np.asarray(ref["query_out"])
+        ref = dict(ref, query_out=q[..., :d.Hckv], query_rope_out=q[..., d.Hckv:])
+    rows = np.arange(int(inp["T"]))
+    check_queries(ref, ref, rows, False, fp16=True)
+    bad = dict(ref, query_out=_bf16_round_as_fp16(ref["query_out"]))
+    with pytest.raises(AssertionError, match="not fp16's"):
+        check_queries(bad, ref, rows, False, fp16=True)
