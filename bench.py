@@ -218,7 +218,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_t32",
                     choices=["decode_t32", "decode_t256", "prefill_t8192", "int8_decode_t128",
-                             "partial_decode_t32", "int8_kvq_decode_t128", "pre_decode_t32", "tiny_t4",
+                             "partial_decode_t32", "int8_kvq_decode_t128", "pre_decode_t32", "pre_f16_decode_t32", "tiny_t4",
                              "sfa_decode_t32"])
     ap.add_argument("--replicas", type=int, default=0, help="weight replicas (0 = enough to "
                     "exceed twice the Infinity Cache)")
@@ -357,7 +357,7 @@ def main():
         "metric": METRIC, "value": T * args.steps / (ms_total * 1e-3), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": ("int8" if inp["quant"] or inp.get("preprocess", False)
+        "dtype": ("int8+fp16" if inp.get("fp16", False) else "int8" if inp["quant"] or inp.get("preprocess", False)
                   else "bf16+int8" if inp.get("partial", False) else "bf16"),
         "data": "synthetic",
         "config": {"workload": wl.name, "T": T, "He": d.He, "Hcq": d.Hcq, "Hckv": d.Hckv,
@@ -366,7 +366,8 @@ def main():
                    "query_out": "int8" if inp["quant"] else "bf16",
                    "kv_cache": "int8" if inp.get("kv_quant", False) else "bf16",
                    "weights": "row-major" if args.row_major else "packed",
-                   "scenario": ("static int8 (preprocess)" if inp.get("preprocess", False) else
+                   "scenario": ("static int8 (preprocess), fp16 tensors" if inp.get("fp16", False) else
+                                "static int8 (preprocess)" if inp.get("preprocess", False) else
                                 "int8" if inp["quant"] else "partial int8" if inp.get("partial", False)
                                 else "bf16"),
                    "layout": "concatenated" if inp.get("concat", False) else "separate",

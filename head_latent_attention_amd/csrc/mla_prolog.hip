@@ -943,10 +943,58 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
   const int Ntot = d.Hcq + d.Hckv + d.Dr;
   const int cq_c = d.Hcq / 8, kv_c = d.Hckv / 8, chunks = cq_c + kv_c + d.Dr / 8;
   const rsrc_t P = make_rsrc(p.part, int64_t(S) * d.T * Ntot * 4);
-  const double sx = (I8D && !ST && active) ? double(p.sx[t]) : 1.0;
+  const int tt = active ? t : 0;
+  // the token's scalars, loaded first
+  const double sx = (I8D && !ST) ? double(p.sx[tt]) : 1.0;
+  const int64_t slot = p.cache_index[tt];
+  const bool cache = active && slot >= 0 && slot < d.slots;
+  const float st_s = ST ? ld16<F16>(*p.qsc_cq) : 0.0f, st_o = ST ? float(*p.qo_cq) : 0.0f;
+  // a chunk's column parameters (dequantisation scales, bias, gamma,
+  // smoothing, beta, cache scales); for the lane's first CPL chunks they are
+  // loaded before the partials, so that every load of the kernel is in
+  // flight at once.  Lanes without a chunk read chunk 0's.
+  struct Side { uint4 sw0, sw1, b0, b1, g, sm0, sm1, be, qk0, qk1; };
+  auto side = [&](int j) {
+    Side r;
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    const int jj = j < chunks ? j : 0;
+    const bool isq = jj < cq_c, iskv = !isq && jj < cq_c + kv_c;
+    const int n = 8 * jj, nq = isq ? n : 0, nk = iskv ? n - d.Hcq : 0;
+    r.sw0 = r.sw1 = r.b0 = r.b1 = r.sm0 = r.sm1 = r.be = r.qk0 = r.qk1 = z;
+    if constexpr (I8D) {
+      const float* sw = isq ? p.sw_dq + n : p.sw_dkv_kr + (n - d.Hcq);
+      r.sw0 = *reinterpret_cast<const uint4*>(sw);
+      r.sw1 = *reinterpret_cast<const uint4*>(sw + 4);
+    }
+    if (ST && p.bias_dq) {
+      r.b0 = *reinterpret_cast<const uint4*>(p.bias_dq + n);
+      r.b1 = *reinterpret_cast<const uint4*>(p.bias_dq + n + 4);
+    }
+    r.g = *reinterpret_cast<const uint4*>(isq ? p.gamma_cq + nq : p.gamma_ckv + nk);
+    if (I8U && p.smooth_cq) {
+      r.sm0 = *reinterpret_cast<const uint4*>(p.smooth_cq + nq);
+      r.sm1 = *reinterpret_cast<const uint4*>(p.smooth_cq + nq + 4);
+    }
+    if (ST) r.be = *reinterpret_cast<const uint4*>(p.beta_cq + nq);
+    if (p.qs_ckv) {
+      r.qk0 = *reinterpret_cast<const uint4*>(p.qs_ckv + nk);
+      r.qk1 = *reinterpret_cast<const uint4*>(p.qs_ckv + nk + 4);
+    }
+    return r;
+  };
+  auto w32 = [](const uint4& a, const uint4& b, int e) {
+    const uint4& v = e < 4 ? a : b;
+    const int k = e & 3;
+    return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+  };
+  auto w16 = [](const uint4& a, int e) {
+    const int k = e >> 1;
+    const uint32_t v = k == 0 ? a.x : k == 1 ? a.y : k == 2 ? a.z : a.w;
+    return uint16_t(v >> (16 * (e & 1)));
+  };
   // y of the eight columns 8j .. 8j+7; the loads of eight splits at a time
   // are issued together (a missing split reads as zeros, an exact no-op)
-  auto y8 = [&](int j, double (&v)[8]) {
+  auto y8 = [&](int j, const Side& sd, double (&v)[8]) {
     double f[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     int32_t iv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (S <= 2) {
@@ -984,9 +1032,8 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       if constexpr (I8D) {
-        const int n = 8 * j + e;
-        const double sw = n < d.Hcq ? p.sw_dq[n] : p.sw_dkv_kr[n - d.Hcq];
-        const int32_t b = (ST && p.bias_dq) ? p.bias_dq[n] : 0;
+        const double sw = double(__uint_as_float(w32(sd.sw0, sd.sw1, e)));
+        const int32_t b = ST ? int32_t(w32(sd.b0, sd.b1, e)) : 0;
         v[e] = double(iv[e] + b) * sx * sw;
       } else {
         v[e] = f[e];
@@ -995,36 +1042,48 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
   };
 
   // the c^Q weight: gamma, times smoothScalesCq for an int8 c^Q when given
-  auto gq = [&](int n) {
-    const double g = double(ld16<F16>(p.gamma_cq[n]));
-    if constexpr (I8U) return p.smooth_cq ? g * double(p.smooth_cq[n]) : g;
+  auto gq = [&](const Side& sd, int e) {
+    const double g = double(ld16<F16>(w16(sd.g, e)));
+    if constexpr (I8U) return p.smooth_cq ? g * double(__uint_as_float(w32(sd.sm0, sd.sm1, e))) : g;
     return g;
   };
   double sq = 0.0, skv = 0.0, gmax = 0.0;
-  auto sums = [&](int j, const double (&v)[8]) {
+  auto sums = [&](int j, const Side& sd, const double (&v)[8]) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       if (j < cq_c) {
         sq += v[e] * v[e];
-        if constexpr (I8U) gmax = fmax(gmax, fabs(gq(8 * j + e) * v[e]));
+        if constexpr (I8U) gmax = fmax(gmax, fabs(gq(sd, e) * v[e]));
       } else if (j < cq_c + kv_c) {
         skv += v[e] * v[e];
       }
     }
   };
+  // the RoPE lanes' sin/cos (and kr cache scales), loaded up front too
+  const int h = d.Dr / 2;
+  const int ir = lane < h ? lane : 0;
+  const uint16_t* cs = p.cos + int64_t(tt) * d.Dr;
+  const uint16_t* sn = p.sin + int64_t(tt) * d.Dr;
+  const float cs0 = ld16<F16>(cs[ir]), cs1 = ld16<F16>(cs[ir + h]);
+  const float sn0 = ld16<F16>(sn[ir]), sn1 = ld16<F16>(sn[ir + h]);
+  const float qr0 = p.qs_ckr ? p.qs_ckr[ir] : 0.0f, qr1 = p.qs_ckr ? p.qs_ckr[ir + h] : 0.0f;
+  Side sdv[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) sdv[c] = side(lane + c * L);
   double yv[CPL][8];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     const int j = lane + c * L;
     if (active && j < chunks) {
-      y8(j, yv[c]);
-      sums(j, yv[c]);
+      y8(j, sdv[c], yv[c]);
+      sums(j, sdv[c], yv[c]);
     }
   }
   for (int j = lane + CPL * L; active && j < chunks; j += L) {
     double v[8];
-    y8(j, v);
-    sums(j, v);
+    const Side sd = side(j);
+    y8(j, sd, v);
+    sums(j, sd, v);
   }
   sq = wave_sum_f64(sq);
   skv = wave_sum_f64(skv);
@@ -1046,11 +1105,8 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
   // quantOffset1 and its dequantisation scale is 1 (the per-channel deScale1
   // does the rest)
   constexpr bool stq = ST;
-  const float st_s = stq ? ld16<F16>(*p.qsc_cq) : 0.0f, st_o = stq ? float(*p.qo_cq) : 0.0f;
   float sc = 0.0f;
   if constexpr (I8U) sc = stq ? 1.0f : float(gmax / rms_q) / 127.0f;
-  const int64_t slot = p.cache_index[t];
-  const bool cache = slot >= 0 && slot < d.slots;
   const int64_t tile = int64_t(cq_nst) * 1024;
 
   auto store_cq = [&](int j, const float (&c)[8], bool pad) {
@@ -1072,13 +1128,13 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
       *reinterpret_cast<uint4*>(p.cq + o) = make_uint4(a.x, a.y, b.x, b.y);
     }
   };
-  auto emit = [&](int j, const double (&v)[8]) {
+  auto emit = [&](int j, const Side& sd, const double (&v)[8]) {
     float c[8];
     if (j < cq_c) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        double w = gq(8 * j + e) * v[e] / rms_q;
-        if (stq) w += double(ld16<F16>(p.beta_cq[8 * j + e]));
+        double w = gq(sd, e) * v[e] / rms_q;
+        if (stq) w += double(ld16<F16>(w16(sd.be, e)));
         c[e] = float(w);
       }
       store_cq(j, c, false);
@@ -1088,13 +1144,13 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
     } else if (cache) {
       const int jk = j - cq_c;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) c[e] = float(double(ld16<F16>(p.gamma_ckv[8 * jk + e])) * v[e] / rms_kv);
+      for (int e = 0; e < 8; ++e) c[e] = float(double(ld16<F16>(w16(sd.g, e))) * v[e] / rms_kv);
       if (p.qs_ckv) {
         uint32_t lo = 0, hi = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          lo |= cache_code(c[e], p.qs_ckv[8 * jk + e]) << (8 * e);
-          hi |= cache_code(c[e + 4], p.qs_ckv[8 * jk + e + 4]) << (8 * e);
+          lo |= cache_code(c[e], __uint_as_float(w32(sd.qk0, sd.qk1, e))) << (8 * e);
+          hi |= cache_code(c[e + 4], __uint_as_float(w32(sd.qk0, sd.qk1, e + 4))) << (8 * e);
         }
         *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(p.kv_cache) + slot * d.kvs + 8 * jk) =
             make_uint2(lo, hi);
@@ -1107,13 +1163,14 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     const int j = lane + c * L;
-    if (j < chunks) emit(j, yv[c]);
+    if (j < chunks) emit(j, sdv[c], yv[c]);
   }
   for (int j = lane + CPL * L; j < chunks; j += L) {
     if (j >= cq_c && !cache) break;
     double v[8];
-    y8(j, v);
-    emit(j, v);
+    const Side sd = side(j);
+    y8(j, sd, v);
+    emit(j, sd, v);
   }
   // the zero k padding of packed c^Q
   const int cq_chunks = cq_nst ? cq_nst * (I8U ? 8 : 4) : cq_c;
@@ -1130,19 +1187,18 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
-  const int h = d.Dr / 2;
   const double* yr = ry[w / NWT];
-  const uint16_t* cs = p.cos + int64_t(t) * d.Dr;
-  const uint16_t* sn = p.sin + int64_t(t) * d.Dr;
   uint16_t* kr = p.kr_cache + slot * d.krs;
   uint8_t* kr8 = reinterpret_cast<uint8_t*>(p.kr_cache) + slot * d.krs;
-  for (int i = lane; i < h; i += L) {
+  // Dr <= 64, so each RoPE pair has a lane of its own (L >= 64)
+  if (lane < h) {
+    const int i = lane;
     const double a = yr[i], b = yr[i + h];
-    const float r0 = float(a * ld16<F16>(cs[i]) - b * ld16<F16>(sn[i]));
-    const float r1 = float(b * ld16<F16>(cs[i + h]) + a * ld16<F16>(sn[i + h]));
+    const float r0 = float(a * cs0 - b * sn0);
+    const float r1 = float(b * cs1 + a * sn1);
     if (p.qs_ckr) {
-      kr8[i] = uint8_t(cache_code(r0, p.qs_ckr[i]));
-      kr8[i + h] = uint8_t(cache_code(r1, p.qs_ckr[i + h]));
+      kr8[i] = uint8_t(cache_code(r0, qr0));
+      kr8[i + h] = uint8_t(cache_code(r1, qr1));
     } else {
       kr[i] = st16<F16>(r0);
       kr[i + h] = st16<F16>(r1);
@@ -3509,7 +3565,6 @@ Layout layout(const mla_prolog_desc& d) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 // every rule of a description but the workspace's size
 mla_status check_desc_core(const mla_prolog_desc* d) {
@@ -3603,14 +3658,15 @@ mla_status check_tensors(const mla_prolog_desc* d, const mla_prolog_tensors* t, 
   if (xn && (!t->gamma_x || !t->beta_x)) return MLA_ERR_NULLPTR;
   if (!xn && (t->gamma_x || t->beta_x)) return MLA_ERR_PARAM_INVALID;
   if (!st && (t->bias_dqkv || t->bias_uq_qr)) return MLA_ERR_PARAM_INVALID;
-  // gamma0 / beta0 are read in 16-byte chunks; the one-value scales as bf16
-  if ((t->gamma_x && !aligned16(t->gamma_x)) || (t->beta_x && !aligned16(t->beta_x)))
-    return MLA_ERR_PARAM_INVALID;
-  const void* st_bf16[] = {t->quant_scale_x, t->beta_cq, t->quant_scale_cq};
-  for (const void* q : st_bf16)
-    if (reinterpret_cast<uintptr_t>(q) & 1u) return MLA_ERR_PARAM_INVALID;
-  if ((t->bias_dqkv && !aligned4(t->bias_dqkv)) || (t->bias_uq_qr && !aligned4(t->bias_uq_qr)))
-    return MLA_ERR_PARAM_INVALID;
+  // every tensor is 16-byte aligned (the per-channel vectors are read in
+  // 16-byte chunks)
+  const void* opt[] = {t->gamma_x, t->beta_x, t->quant_scale_x, t->quant_offset_x, t->beta_cq,
+                       t->quant_scale_cq, t->quant_offset_cq, t->bias_dqkv, t->bias_uq_qr,
+                       t->scale_x, t->scale_w_dq, t->scale_w_uq_qr, t->scale_w_dkv_kr,
+                       t->smooth_scales_cq, t->quant_scale_ckv, t->quant_scale_ckr,
+                       t->dequant_scale_q_nope};
+  for (const void* q : opt)
+    if (q && !aligned16(q)) return MLA_ERR_PARAM_INVALID;
   // the unpacked kernels read (k, n) bf16 weights only
   if ((d->weights_nk || d->float_dtype == MLA_FP16) && !t->packed_weights) return MLA_ERR_UNSUPPORTED;
   // the scales each scenario takes: all four in full quantisation, that of
@@ -3620,10 +3676,9 @@ mla_status check_tensors(const mla_prolog_desc* d, const mla_prolog_tensors* t, 
   for (int i = 0; i < 4; ++i) {
     if (need[i] && !sc[i]) return MLA_ERR_NULLPTR;
     if (!need[i] && sc[i]) return MLA_ERR_PARAM_INVALID;
-    if (sc[i] && !aligned4(sc[i])) return MLA_ERR_PARAM_INVALID;
   }
   // smoothScalesCq: optional with an int8 weightUqQr, absent otherwise
-  if (t->smooth_scales_cq && (!up_i8(*d) || st || !aligned4(t->smooth_scales_cq)))
+  if (t->smooth_scales_cq && (!up_i8(*d) || st))
     return MLA_ERR_PARAM_INVALID;
   // quantScaleCkv with an int8 kv cache; quantScaleCkr with an int8 kr
   // cache, which partial quantisation has and full quantisation does not
@@ -3631,13 +3686,10 @@ mla_status check_tensors(const mla_prolog_desc* d, const mla_prolog_tensors* t, 
   if (kv8 && !t->quant_scale_ckv) return MLA_ERR_NULLPTR;
   if (kr8 && !t->quant_scale_ckr) return MLA_ERR_NULLPTR;
   if ((!kv8 && t->quant_scale_ckv) || (!kr8 && t->quant_scale_ckr)) return MLA_ERR_PARAM_INVALID;
-  if ((t->quant_scale_ckv && !aligned4(t->quant_scale_ckv)) || (t->quant_scale_ckr && !aligned4(t->quant_scale_ckr)))
-    return MLA_ERR_PARAM_INVALID;
   if (t->packed_weights && (reinterpret_cast<uintptr_t>(t->packed_weights) & 255u))
     return MLA_ERR_PARAM_INVALID;
   if (d->query_dtype == MLA_INT8 && !t->dequant_scale_q_nope) return MLA_ERR_NULLPTR;
   if (d->query_dtype == MLA_BF16 && t->dequant_scale_q_nope) return MLA_ERR_PARAM_INVALID;
-  if (t->dequant_scale_q_nope && !aligned4(t->dequant_scale_q_nope)) return MLA_ERR_PARAM_INVALID;
   return MLA_OK;
 }
 

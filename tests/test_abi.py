@@ -180,6 +180,13 @@ def test_bad_run_arguments():
     assert mla.validate(dpk, t, 8) == mla.MLA_ERR_NULLPTR
     t = fake_tensors(partial=True); t["quant_scale_ckv"] = FAKE                       # bf16 caches
     assert mla.validate(dp, t, 8) == mla.MLA_ERR_PARAM_INVALID
+    # every tensor 16-byte aligned: the per-channel vectors are read in
+    # 16-byte chunks, so a 4-byte aligned scale is refused too
+    for f in ("scale_x", "scale_w_dq", "scale_w_uq_qr", "scale_w_dkv_kr", "smooth_scales_cq"):
+        t = fake_tensors(q8=True, in8=True, smooth=True); t[f] = FAKE + 4
+        assert mla.validate(d8, t, 8) == mla.MLA_ERR_PARAM_INVALID, f
+    t = fake_tensors(True, True, kvq=True); t["quant_scale_ckv"] = FAKE + 4
+    assert mla.validate(model_desc(in_dtype=1, query_dtype=1, cache_dtype=1), t, 8) == mla.MLA_ERR_PARAM_INVALID
 
 
 def test_bad_static_and_concat_arguments():
@@ -194,8 +201,9 @@ def test_bad_static_and_concat_arguments():
     assert mla.validate(st, t, 8) == mla.MLA_ERR_PARAM_INVALID
     t = fake_tensors(static=True)                                                 # gamma0 without the norm
     assert mla.validate(model_desc(in_dtype=3, x_quant_only=1), t, 8) == mla.MLA_ERR_PARAM_INVALID
-    t = fake_tensors(static=True); t["bias_dqkv"] = FAKE + 2
-    assert mla.validate(st, t, 8) == mla.MLA_ERR_PARAM_INVALID
+    for f in ("bias_dqkv", "bias_uq_qr", "beta_cq", "quant_scale_x", "quant_offset_cq"):
+        t = fake_tensors(static=True); t[f] = FAKE + 4
+        assert mla.validate(st, t, 8) == mla.MLA_ERR_PARAM_INVALID, f
     t = fake_tensors(static=True); t["gamma_x"] = FAKE + 8                        # read in 16-byte chunks
     assert mla.validate(st, t, 8) == mla.MLA_ERR_PARAM_INVALID
     for f in STATIC_ONLY:                                                         # other scenarios
