@@ -3634,13 +3634,19 @@ mla_status check_tensors(const mla_prolog_desc* d, const mla_prolog_tensors* t, 
   if (T == 0) return MLA_OK;
   // the concatenated layout has no separate q^R output or k^R cache
   const void* qr_or_q = d->concat ? t->query_out : t->query_rope_out;
-  const void* req[] = {t->token_x, t->weight_dq, t->weight_uq_qr, t->weight_uk, t->weight_dkv_kr,
-                       t->gamma_cq, t->gamma_ckv, t->rope_sin, t->rope_cos, t->cache_index,
+  const void* req[] = {t->token_x, t->gamma_cq, t->gamma_ckv, t->rope_sin, t->rope_cos, t->cache_index,
                        t->query_out, qr_or_q};
   for (const void* q : req)
     if (!q) return MLA_ERR_NULLPTR;
   for (const void* q : req)
     if (!aligned16(q)) return MLA_ERR_PARAM_INVALID;
+  // the unpacked weights: read only by the kernels of runs without the
+  // packed copy
+  const void* wts[] = {t->weight_dq, t->weight_uq_qr, t->weight_uk, t->weight_dkv_kr};
+  for (const void* q : wts) {
+    if (!q && !t->packed_weights) return MLA_ERR_NULLPTR;
+    if (q && !aligned16(q)) return MLA_ERR_PARAM_INVALID;
+  }
   if (d->concat && (t->query_rope_out || t->kr_cache)) return MLA_ERR_PARAM_INVALID;
   if (d->block_num > 0) {
     const void* kr = d->concat ? t->kv_cache : t->kr_cache;
@@ -3782,8 +3788,6 @@ void launch_norm(hipStream_t s, const Dims& d, const Ptrs& p, int S, int cq_nst)
 }
 
 // The int8-query W^UK kernel gives one wave to each 64-column window of Hckv.
-bool packed_fits(const mla_prolog_desc& dd) { return (dd.Hckv + 63) / 64 <= 8; }
-
 // Small-T run on packed weights: K1p (down-projection, split partials), K2
 // (norms, c^Q, caches), K3p (up-projection, q-RoPE, q^C), K4p (W^UK).
 // Profiling marks follow the kernels.  I8D: int8 down-projection operands;
@@ -4195,7 +4199,9 @@ mla_status enqueue(const RunCtx& c, const mla_prolog_tensors* t, int64_t T, hipS
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? MLA_OK : MLA_ERR_RUNTIME;
   }
-  if (p.packed && (!pl.stream || packed_fits(dd) || dd.float_dtype == MLA_FP16)) {
+  // with the packed copy, every run stays on kernels that read it (the
+  // unpacked weights may be absent)
+  if (p.packed) {
     if (pl.stream && dd.float_dtype != MLA_FP16) launch_packed(pl, s, d, p, dd, q8, c.pair_ok, mark);
     else launch_tiled(s, d, p, dd, q8, c.pair_ok, mark);
     const hipError_t e = hipGetLastError();

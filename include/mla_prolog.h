@@ -183,9 +183,11 @@ typedef struct {
  *                                       mla_prolog_pack_weights for these
  *                                       four weights, 256-byte aligned.  When
  *                                       given, every run streams the weights
- *                                       from it; the unpacked weights stay
- *                                       required (they are the fallback of
- *                                       shapes without a packed tiling).
+ *                                       from it, and weight_dq, weight_uq_qr,
+ *                                       weight_uk and weight_dkv_kr may be
+ *                                       NULL (no kernel of the run reads
+ *                                       them); when NULL, all four are
+ *                                       required.
  *   smooth_scales_cq (Hcq)              fp32 smoothScalesCq, optional (NULL =
  *                                       none) with an int8 weightUqQr, NULL
  *                                       otherwise

@@ -149,7 +149,7 @@ def test_bad_run_arguments():
     d = model_desc()
     assert mla.validate(d, fake_tensors(), 257) == mla.MLA_ERR_PARAM_INVALID   # T > max_tokens
     assert mla.validate(d, fake_tensors(), -1) == mla.MLA_ERR_PARAM_INVALID
-    t = fake_tensors(); t["weight_uk"] = None
+    t = fake_tensors(); t["weight_uk"] = None; t["packed_weights"] = None
     assert mla.validate(d, t, 8) == mla.MLA_ERR_NULLPTR
     t = fake_tensors(); t["kv_cache"] = None
     assert mla.validate(d, t, 8) == mla.MLA_ERR_NULLPTR
@@ -222,6 +222,14 @@ def test_bad_static_and_concat_arguments():
     t = fake_tensors(); t["packed_weights"] = None
     assert mla.validate(model_desc(weights_nk=1), t, 8) == mla.MLA_ERR_UNSUPPORTED
     assert mla.validate(model_desc(), t, 8) == mla.MLA_OK
+    # with the packed copy, the unpacked weights are optional
+    for f in ("weight_dq", "weight_uq_qr", "weight_uk", "weight_dkv_kr"):
+        t = fake_tensors(); t[f] = None
+        assert mla.validate(model_desc(), t, 8) == mla.MLA_OK, f
+        t["packed_weights"] = None
+        assert mla.validate(model_desc(), t, 8) == mla.MLA_ERR_NULLPTR, f
+        t = fake_tensors(); t[f] = FAKE + 4
+        assert mla.validate(model_desc(), t, 8) == mla.MLA_ERR_PARAM_INVALID, f
     # and so do fp16 tensors
     t = fake_tensors(static=True); t["packed_weights"] = None
     assert mla.validate(model_desc(in_dtype=3, float_dtype=mla.MLA_FP16), t, 8) == mla.MLA_ERR_UNSUPPORTED

@@ -27,12 +27,17 @@ def say(msg):
     sys.stdout.flush()
 
 
-def run_gpu(inp, query_int8=None, max_tokens=None, T=None, repeat=1, packed=False, prerun_negated=False):
+WEIGHTS = ("weight_dq", "weight_uq_qr", "weight_uk", "weight_dkv_kr")
+
+
+def run_gpu(inp, query_int8=None, max_tokens=None, T=None, repeat=1, packed=False, prerun_negated=False,
+            drop_unpacked=False):
     """Upload, run through the C ABI, download.  Returns host arrays.  With
     ``packed`` the weights are first converted by mla_prolog_pack_weights
-    and the run reads the packed copy.  With ``prerun_negated`` the handle
-    first runs once on -x (every intermediate differs), so that a result
-    left in the workspace by an earlier run cannot pass for this one's."""
+    and the run reads the packed copy (with ``drop_unpacked`` the runs get
+    no unpacked weights at all).  With ``prerun_negated`` the handle first
+    runs once on -x (every intermediate differs), so that a result left in
+    the workspace by an earlier run cannot pass for this one's."""
     T = int(inp["T"]) if T is None else T
     t = dev.upload(inp, query_int8=query_int8)
     desc = mla.make_desc(**dev.desc_args(inp, max_tokens=max_tokens, query_int8=query_int8))
@@ -41,6 +46,10 @@ def run_gpu(inp, query_int8=None, max_tokens=None, T=None, repeat=1, packed=Fals
             buf = torch.empty(mla.packed_weights_bytes(desc), dtype=torch.uint8, device="cuda")
             h.pack_weights(t, buf)
             t["packed_weights"] = buf
+            if drop_unpacked:
+                for k in WEIGHTS:
+                    del t[k]
+                torch.cuda.synchronize()
         if prerun_negated:
             h.run(dict(t, token_x=-t["token_x"]), T)
         for _ in range(repeat):
@@ -64,12 +73,13 @@ def split_concat(inp, arrays):
     return out
 
 
-def full_check(inp, query_int8=None, rows=None, packed=False, repeat=1, prerun_negated=False):
+def full_check(inp, query_int8=None, rows=None, packed=False, repeat=1, prerun_negated=False, drop_unpacked=False):
     q8 = bool(inp["quant"]) if query_int8 is None else bool(query_int8)
     rows = np.arange(int(inp["T"])) if rows is None else np.asarray(rows)
     say(f"case {inp['workload']} T={inp['T']} dims={inp['dims']} q8={q8} rows={len(rows)} packed={packed} "
         f"static={inp.get('preprocess', False)} concat={inp.get('concat', False)} nk={inp.get('weight_nk', False)}")
-    got = run_gpu(inp, query_int8=query_int8, packed=packed, repeat=repeat, prerun_negated=prerun_negated)
+    got = run_gpu(inp, query_int8=query_int8, packed=packed, repeat=repeat, prerun_negated=prerun_negated,
+                  drop_unpacked=drop_unpacked)
     partial = bool(inp.get("partial", False))
     ref = oracle.run(inp, tokens=rows, query_int8=query_int8, caches=False,
                      intermediates=partial or bool(inp.get("kv_quant", False)))
@@ -735,6 +745,24 @@ def test_static_fp16_needs_packed_weights():
         with pytest.raises(mla.MlaError) as e:
             h.run(t, int(inp["T"]))
     assert e.value.status == mla.MLA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("name", ["bf16_t16_one_launch", "bf16_t37", "int8_t130_ring", "static_t600",
+                                  "static_fp16_t70", "bf16_t2100_large"])
+def test_packed_runs_without_unpacked_weights(name):
+    # with the packed copy given, a run reads no unpacked weight: the four
+    # tensors are freed before it
+    wl = {"bf16_t16_one_launch": custom_workload("nw_t16", T=16, dims=Dims(He=384, Hcq=128, Hckv=512, N=16, D=128,
+                                                                          Dr=64), block_num=4, block_size=16,
+                                                 seed=301),
+          "bf16_t37": SMALL["ragged_t37"],
+          "int8_t130_ring": INT8_SMALL["q8_t130"],
+          "static_t600": STATIC["pre_t600"],
+          "static_fp16_t70": STATIC_F16["pre_f16_t70"],
+          "bf16_t2100_large": custom_workload("nw_t2100", T=2100, dims=Dims(He=264, Hcq=72, Hckv=40, N=3, D=24,
+                                                                            Dr=16), block_num=160, block_size=16,
+                                              seed=302)}[name]
+    full_check(synth.make_inputs(wl), packed=True, drop_unpacked=True)
 
 
 CONCAT_BF16 = {
