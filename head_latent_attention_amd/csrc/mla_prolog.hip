@@ -2856,6 +2856,130 @@ __global__ __launch_bounds__(64 * WM * WN) void k3_tiled(Dims d, Ptrs p, PackGeo
   }
 }
 
+// K4w: the W^UK product of long runs, q^N = q^C[., h, .] W^UK[h] in bf16 (or
+// fp16).  ph blocks per head, heads fastest, so that the blocks running
+// together write neighbouring heads of the same token rows; block (h, j)
+// takes the 512-token tiles j, j + ph, ...  The head's whole W^UK (at most
+// 8 windows x 4 D stages x 4 KB = 128 KB) is loaded into LDS once.  Wave w
+// holds the q^C fragments of its 64 tokens of a tile (every D stage,
+// D <= 128) in registers, the next tile's loading while the current one is
+// multiplied, and walks the windows with no block barrier; each 16-token x
+// 64-column result goes out through the wave's LDS tile as 16-byte
+// non-temporal stores of whole 128-byte row pieces.  q^C is read once, and
+// the stores of one tile overlap the loads of the next.
+constexpr int kRowsTile = 512;   // K4w: tokens of a tile (8 waves x 64)
+
+template <bool F16>
+__global__ __launch_bounds__(512) void k4_rows(Dims d, Ptrs p, PackGeo pg, int ph) {
+  constexpr int MT = 4, NW = 8, NSD = 4, UKMAX = 8 * NSD * 4 * 1024;
+  __shared__ __attribute__((aligned(16))) uint8_t wl[UKMAX];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[NW * 16 * 144];
+  const int h = blockIdx.x % d.N, j0 = blockIdx.x / d.N;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int nst = pg.nst_d, nt = (d.T + 15) / 16, mtiles = (d.T + kRowsTile - 1) / kRowsTile;
+  const int64_t qtile = int64_t(d.N) * nst * 1024;
+  const rsrc_t Q = make_rsrc(p.qc, int64_t(nt) * qtile);
+  const rsrc_t Wp = make_rsrc(p.packed, pg.total);
+  const uint32_t wbytes = uint32_t(nst) * 4096u, ubytes = uint32_t(pg.uk_w) * wbytes;
+  const uint32_t ukh = uint32_t(pg.off_uk + int64_t(h) * ubytes);
+  // the wave's q^C fragments of tile j (zeros past the run)
+  using AF = uint4[MT][NSD];
+  auto aload = [&](AF& a, int j) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int st = 0; st < NSD; ++st) {
+        const int tt = (j * NW + w) * MT + mt;
+        a[mt][st] = bload16(Q, j < mtiles && tt < nt && st < nst
+                                   ? uint32_t(tt * qtile + int64_t(h) * nst * 1024) + uint32_t(st) * 1024u +
+                                         uint32_t(lane * 16)
+                                   : kOOB);
+      }
+  };
+  // the head's W^UK: 16 bytes at thread offsets 0, 8192, ... of its ubytes
+  {
+    uint4 r[UKMAX / 8192];
+#pragma unroll
+    for (int i = 0; i < UKMAX / 8192; ++i) {
+      const uint32_t o = uint32_t(threadIdx.x) * 16u + 8192u * i;
+      r[i] = bload16(Wp, o < ubytes ? ukh + o : kOOB);
+    }
+#pragma unroll
+    for (int i = 0; i < UKMAX / 8192; ++i) {
+      const uint32_t o = uint32_t(threadIdx.x) * 16u + 8192u * i;
+      if (o < ubytes) *reinterpret_cast<uint4*>(wl + o) = r[i];
+    }
+  }
+  AF a0, a1;
+  aload(a0, j0);
+  // orders LDS only (the q^C loads may still be in flight)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  using Frag = bf16x8;
+  const int64_t qbytes = int64_t(d.T) * d.N * d.qs * 2;
+  const int64_t rows_n = int64_t(d.N) * d.qs * 2;   // bytes from one token row to the next
+  uint8_t* tile = stage + w * 16 * 144;
+  auto work = [&](const AF& a, int j) {
+    const int tt0 = (j * NW + w) * MT;
+    for (int jw = 0; jw < pg.uk_w; ++jw) {
+      const uint8_t* L = wl + jw * wbytes;
+      f32x4 acc[MT][4];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) acc[mt][ct] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int st = 0; st < NSD; ++st) {
+        if (st >= nst) break;
+        Frag bf[4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) bf[ct] = *reinterpret_cast<const Frag*>(L + (st * 4 + ct) * 1024 + lane * 16);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct)
+            acc[mt][ct] = mma16<F16>(bf[ct], __builtin_bit_cast(Frag, a[mt][st]), acc[mt][ct]);
+      }
+      // each 16-token x 64-column piece through the wave's LDS tile, out as
+      // 16-byte non-temporal buffer stores (rows past T and columns past
+      // Hckv at an out-of-range offset, which the hardware drops)
+      const int width = min(64, d.Hckv - 64 * jw);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+          *reinterpret_cast<uint2*>(tile + c * 144 + (16 * ct + 4 * g) * 2) =
+              pack16x4<F16>(acc[mt][ct][0], acc[mt][ct][1], acc[mt][ct][2], acc[mt][ct][3]);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int m0 = 16 * (tt0 + mt);
+        const int64_t base = m0 < d.T ? (int64_t(m0) * d.N + h) * d.qs * 2 : qbytes;
+        const rsrc_t O = make_rsrc(reinterpret_cast<uint8_t*>(p.q_out) + base, qbytes - base);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int k = lane + 64 * hh, row = k >> 3, col = 8 * (k & 7);
+          const uint32_t off = m0 + row < d.T && col < width ? uint32_t(row * rows_n + (64 * jw + col) * 2) : kOOB;
+          __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const i32x4*>(tile + row * 144 + col * 2), O,
+                                                 off, 0, 2);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+    }
+  };
+  // two tiles a round, each loading while the other is multiplied
+  for (int j = j0; j < mtiles; j += 2 * ph) {
+    aload(a1, j + ph);
+    work(a0, j);
+    aload(a0, j + 2 * ph);
+    if (j + ph < mtiles) work(a1, j + ph);
+  }
+}
+
 // K4t: grid (token tiles fastest, then column groups, then heads).  q^N =
 // q^C[., h, .] W^UK[h]; bf16 stores, or (one column group holding the whole
 // Hckv row) the per-(token, head) int8 quantisation with the row maximum
@@ -3934,6 +4058,12 @@ void tiled_large(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs& 
   k3_tiled<I8U, 4, 1, 4, 4, 2, true, 1, false, F16><<<dim3(tp.m3 * tp.ngrp3), 1024, 0, s>>>(d, p, g, tp.m3);
   mark(3);
   if (q8) k4_tiled<4, 1, 1, 8, 2, true, false, true><<<dim3(tp.m4q * d.N), 512, 0, s>>>(d, p, g, tp.m4q, 1);
+  else if (g.nst_d <= 4) {
+    // about one block per CU, all of a head's blocks sharing its W^UK
+    const int mtiles = ceil_div(d.T, kRowsTile);
+    const int ph = std::max(1, std::min(mtiles, 256 / d.N));
+    k4_rows<F16><<<dim3(ph * d.N), 512, 0, s>>>(d, p, g, ph);
+  }
   else k4_tiled<4, 1, 4, 4, 2, false, true, true, F16><<<dim3(tp.m4 * tp.cg4 * d.N), 1024, 0, s>>>(d, p, g, tp.m4,
                                                                                           tp.cg4);
   mark(4);
