@@ -72,19 +72,20 @@ def algorithmic(inp, T):
                 step_bytes=step_bytes, step_flop=k1_flop + k3_flop + k4_flop)
 
 
-def measured_traffic(workload, kernel):
-    """HBM bytes per launch of the dominant kernel from the committed counter
-    summary profiles/traffic_<workload>.json (FETCH_SIZE and WRITE_SIZE per
-    dispatch, each scaled by what the counter reads for a plain copy of known
-    size), or None when there is none or the kernel source has changed since
-    the counters were taken."""
+def measured_traffic(workload, kernel, source="mla_prolog.hip"):
+    """HBM bytes per launch of the dominant kernel (per step of the listed
+    kernels) from the committed counter summary
+    profiles/traffic_<workload>.json (FETCH_SIZE and WRITE_SIZE per dispatch,
+    each scaled by what the counter reads for a plain copy of known size), or
+    None when there is none or the kernel source has changed since the
+    counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    src = os.path.join(ROOT, "head_latent_attention_amd", "csrc", "mla_prolog.hip")
+    src = os.path.join(ROOT, "head_latent_attention_amd", "csrc", source)
     with open(src, "rb") as f:
         digest = hashlib.sha256(f.read()).hexdigest()
     if t.get("source_sha256") != digest or t.get("bench_kernel") != kernel:
@@ -189,8 +190,9 @@ def bench_sfa(args):
                    "kv_len": [wl.len_lo, wl.len_hi], "cache_bytes": int(kv.numel() * 2 + kr.numel() * 2),
                    "index_sets": sets},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "k_sfa + k_sfa_combine",
-                     "per_launch": f"{nbytes} B"},
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(wl.name, "k_sfa + k_sfa_combine", "mla_sfa.hip"),
+                     "kernel": "k_sfa + k_sfa_combine", "per_launch": f"{nbytes} B"},
         "wall_s": wall,
     }
     if not args.no_cpu_baseline:
