@@ -323,13 +323,14 @@ struct Ptrs {
   float* cq_scale;   // [T]
   uint16_t* qc;      // [T][N][D] bf16
   uint8_t* xq;       // [N] q^C exchange of the paired small-T kernel, kPairXq bytes a head
-  uint32_t* xflag;   // [N][4] its exchange flags (run numbers), then one error word
+  uint32_t* xflag;   // [N][4] its exchange flags (run numbers), then one spare word
   float* xmax;       // [N][2][32] its per-token row maxima
   float* xmax2;      // [N][2][kRingMaxT]: the medium-T fused kernel's per-token row maxima
   uint32_t* fpart;   // fused kernel: [phase-1 blocks][32][64] (fp32 split partial, run tag) words
   uint32_t* fss;     // fused kernel: [windows][32] (fp32 sum of squares, run tag) words
   float* fykr;       // fused kernel: [32][Hckv + Dr] y of the c^KV and k^R columns
-  uint32_t* fcnt;    // fused kernel: [2N] flags, 64 bytes apart, then an error word
+  uint32_t* fcnt;    // fused kernel: [2N] flags, 64 bytes apart
+  uint32_t* herr;    // the handle's error word, in host-visible memory: set when a bounded wait gives up
   const uint8_t* packed;  // weights in the packed layout, or NULL
 };
 
@@ -1658,7 +1659,7 @@ __device__ __forceinline__ void pair_wait(const uint32_t* flag, uint32_t* err, u
     int n = 0;
     while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != run) {
       if (++n > spin) {
-        __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         break;
       }
       __builtin_amdgcn_s_sleep(2);
@@ -1835,7 +1836,7 @@ __global__ __launch_bounds__(512) void k34_pair(Dims d, Ptrs p, PackGeo pg) {
   }
 
   // q^N = q^C W^UK[h] over this half's columns, all of D
-  pair_wait(p.xflag + 4 * h + (1 - half), p.xflag + 4 * d.N, d.run, d.spin);
+  pair_wait(p.xflag + 4 * h + (1 - half), p.herr, d.run, d.spin);
   uint4 aq[4][MT];
 #pragma unroll
   for (int s = 0; s < 4; ++s)
@@ -1892,7 +1893,7 @@ __global__ __launch_bounds__(512) void k34_pair(Dims d, Ptrs p, PackGeo pg) {
       __hip_atomic_store(xm + 32 * half + lane, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     pair_publish(p.xflag + 4 * h + 2 + half, d.run);
-    pair_wait(p.xflag + 4 * h + 2 + (1 - half), p.xflag + 4 * d.N, d.run, d.spin);
+    pair_wait(p.xflag + 4 * h + 2 + (1 - half), p.herr, d.run, d.spin);
     if (!ukact) return;
     int8_t* qo = static_cast<int8_t*>(p.q_out);
 #pragma unroll
@@ -1996,7 +1997,7 @@ __device__ __forceinline__ uint2 bload8u(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ bool fused_poll_done(bool ok, int& n, int spin, uint32_t* err) {
   if (__builtin_amdgcn_ballot_w64(!ok) == 0) return true;
   if (++n > spin) {
-    if ((threadIdx.x & 63) == 0) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((threadIdx.x & 63) == 0) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     return true;
   }
   __builtin_amdgcn_s_sleep(2);
@@ -2012,9 +2013,9 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
   const int g = lane >> 4, c = lane & 15;
   const int b = blockIdx.x, G = gridDim.x;
   const rsrc_t Wp = make_rsrc(p.packed, pg.total);
-  // flags of the split blocks, one per 64-byte line, then the error word
+  // flags of the split blocks, one per 64-byte line
   uint32_t* const flag = p.fcnt;
-  uint32_t* const err = p.fcnt + G * kFusedFlagStride;
+  uint32_t* const err = p.herr;
 
   // ---- the block's head and half in phase 3 (as in k34_pair)
   const int h = d.N % 8 == 0 ? (b / 16) * 8 + b % 8 : b / 2;
@@ -2456,7 +2457,7 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
   }
 
   // q^N = q^C W^UK[h] over this half's columns, all of D
-  pair_wait(p.xflag + 4 * h + (1 - half), p.xflag + 4 * d.N, d.run, d.spin);
+  pair_wait(p.xflag + 4 * h + (1 - half), p.herr, d.run, d.spin);
   uint4 aqc[4][MT];
 #pragma unroll
   for (int st = 0; st < 4; ++st)
@@ -3250,7 +3251,7 @@ __global__ __launch_bounds__(512) void k3_ring(Dims d, Ptrs p, PackGeo pg) {
     // q^N = q^C W^UK[h] over this half's windows, all of D; the operand's
     // stages 2 half, 2 half + 1 are this block's (LDS), the others the
     // partner's (workspace)
-    pair_wait(p.xflag + 4 * h + (1 - half), p.xflag + 4 * d.N, d.run, d.spin);
+    pair_wait(p.xflag + 4 * h + (1 - half), p.herr, d.run, d.spin);
     uint4 aq[MT][4];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -3343,7 +3344,7 @@ __global__ __launch_bounds__(512) void k3_ring(Dims d, Ptrs p, PackGeo pg) {
           __hip_atomic_store(xm + half * kRingMaxT + t, mx[mt], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       pair_publish(p.xflag + 4 * h + 2 + half, d.run);
-      pair_wait(p.xflag + 4 * h + 2 + (1 - half), p.xflag + 4 * d.N, d.run, d.spin);
+      pair_wait(p.xflag + 4 * h + 2 + (1 - half), p.herr, d.run, d.spin);
       int8_t* qo = static_cast<int8_t*>(p.q_out);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -3862,6 +3863,8 @@ struct mla_prolog {
   int64_t recorded;    // runs recorded since the last read
   bool fused_fit[2];   // the fused kernel (16 or 32 tokens) has all 2N blocks resident at once
   uint32_t run_no;     // number of the last run (1, 2, ...; 0 is skipped on a wrap)
+  uint32_t* herr;      // error word in mapped, coherent host memory (host address)
+  uint32_t* herr_dev;  // the same word's device address
 };
 
 namespace {
@@ -4170,16 +4173,30 @@ mla_status mla_prolog_create(const mla_prolog_desc* desc, mla_prolog_t* out) {
   h->events = nullptr;
   h->fused = nullptr;
   h->recorded = 0;
+  h->herr = h->herr_dev = nullptr;
   if (hipMalloc(&h->ws, h->lay.total) != hipSuccess) {
     delete h;
     (void)hipSetDevice(prev);
     return MLA_ERR_RUNTIME;
   }
+  // the error word of the bounded waits, where the host can read it at any
+  // time without a synchronisation
+  if (hipHostMalloc(reinterpret_cast<void**>(&h->herr), 64, hipHostMallocMapped | hipHostMallocCoherent) !=
+          hipSuccess ||
+      hipHostGetDevicePointer(reinterpret_cast<void**>(&h->herr_dev), h->herr, 0) != hipSuccess) {
+    if (h->herr) (void)hipHostFree(h->herr);
+    (void)hipFree(h->ws);
+    delete h;
+    (void)hipSetDevice(prev);
+    return MLA_ERR_RUNTIME;
+  }
+  __atomic_store_n(h->herr, 0u, __ATOMIC_RELEASE);
   // the flags and tags of the small-T kernels start at zero, which no run's
   // number is
   if (hipMemset(h->ws + h->lay.xflag, 0, size_t(4 * desc->N + 1) * 4) != hipSuccess ||
       hipMemset(h->ws + h->lay.fpart, 0, h->lay.total - h->lay.fpart) != hipSuccess ||
       hipDeviceSynchronize() != hipSuccess) {
+    (void)hipHostFree(h->herr);
     (void)hipFree(h->ws);
     delete h;
     (void)hipSetDevice(prev);
@@ -4230,6 +4247,7 @@ struct RunCtx {
   int spin;
   hipEvent_t* ev;
   uint8_t* mark_kind;
+  uint32_t* herr;   // device address of the error word of the bounded waits
 };
 
 mla_status enqueue(const RunCtx& c, const mla_prolog_tensors* t, int64_t T, hipStream_t s) {
@@ -4291,6 +4309,7 @@ mla_status enqueue(const RunCtx& c, const mla_prolog_tensors* t, int64_t T, hipS
   p.fss = reinterpret_cast<uint32_t*>(ws + lay.fss);
   p.fykr = reinterpret_cast<float*>(ws + lay.fykr);
   p.fcnt = reinterpret_cast<uint32_t*>(ws + lay.fcnt);
+  p.herr = c.herr;
 
   hipEvent_t* const ev = c.ev;
   uint8_t* const fused = c.mark_kind;
@@ -4375,6 +4394,9 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   mla_status st = check_tensors(&dd, t, T);
   if (st != MLA_OK) return st;
   if (T == 0) return MLA_OK;
+  // an earlier run that gave up a bounded wait, once its mark is visible
+  // here: nothing more runs until mla_prolog_check has reported it
+  if (__atomic_load_n(h->herr, __ATOMIC_ACQUIRE) != 0) return MLA_ERR_RUNTIME;
   int prev = 0;
   if (hipGetDevice(&prev) != hipSuccess) return MLA_ERR_RUNTIME;
   if (prev != dd.device && hipSetDevice(dd.device) != hipSuccess) return MLA_ERR_RUNTIME;
@@ -4402,6 +4424,7 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   c.spin = h->spin;
   c.ev = nullptr;
   c.mark_kind = nullptr;
+  c.herr = h->herr_dev;
   if (h->events) {
     c.ev = h->events + (h->recorded % kProfileRing) * kProfileEvents;
     c.mark_kind = h->fused + (h->recorded % kProfileRing);
@@ -4477,6 +4500,8 @@ mla_status mla_prolog_run_noalloc(const mla_prolog_desc* desc, const mla_prolog_
   c.spin = 0;
   c.ev = nullptr;
   c.mark_kind = nullptr;
+  // (no kernel of these runs waits on another block: the word is never written)
+  c.herr = reinterpret_cast<uint32_t*>(ws + L.xflag) + 4 * desc->N;
   st = enqueue(c, t, T, static_cast<hipStream_t>(stream));
   if (prev != desc->device) (void)hipSetDevice(prev);
   return st;
@@ -4549,6 +4574,7 @@ mla_status mla_prolog_destroy(mla_prolog_t h) {
     if (hipDeviceSynchronize() != hipSuccess) st = MLA_ERR_RUNTIME;
     destroy_events(h);
     if (hipFree(h->ws) != hipSuccess) st = MLA_ERR_RUNTIME;
+    if (hipHostFree(h->herr) != hipSuccess) st = MLA_ERR_RUNTIME;
     (void)hipSetDevice(prev);
   }
   delete h;
@@ -4567,27 +4593,11 @@ mla_status mla_prolog_check(mla_prolog_t h) {
   int prev = 0;
   if (hipGetDevice(&prev) != hipSuccess || hipSetDevice(h->desc.device) != hipSuccess)
     return MLA_ERR_RUNTIME;
-  // the paired kernel's error word follows its 4N exchange flags; the fused
-  // kernel's follows its 2N block flags
-  uint32_t* words[2] = {reinterpret_cast<uint32_t*>(h->ws + h->lay.xflag) + 4 * h->desc.N,
-                        reinterpret_cast<uint32_t*>(h->ws + h->lay.fcnt) + 2 * h->desc.N * kFusedFlagStride};
   const bool synced = hipDeviceSynchronize() == hipSuccess;
-  mla_status st = synced ? MLA_OK : MLA_ERR_RUNTIME;
-  // every word is read and cleared, also when an earlier one was set
-  for (uint32_t* wd : words) {
-    uint32_t v = 0;
-    if (!synced || hipMemcpy(&v, wd, 4, hipMemcpyDeviceToHost) != hipSuccess) {
-      st = MLA_ERR_RUNTIME;
-      continue;
-    }
-    if (v != 0) {
-      st = MLA_ERR_RUNTIME;
-      const uint32_t zero = 0;
-      (void)hipMemcpy(wd, &zero, 4, hipMemcpyHostToDevice);
-    }
-  }
   (void)hipSetDevice(prev);
-  return st;
+  // the word is read and cleared, also when the synchronisation failed
+  const uint32_t v = __atomic_exchange_n(h->herr, 0u, __ATOMIC_ACQ_REL);
+  return synced && v == 0 ? MLA_OK : MLA_ERR_RUNTIME;
 }
 
 const char* mla_prolog_status_string(mla_status s) {

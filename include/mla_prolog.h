@@ -311,7 +311,11 @@ mla_status mla_prolog_create(const mla_prolog_desc* desc, mla_prolog_t* out);
  * processes must not occupy the device while it runs.  Otherwise a bounded
  * wait gives up and mla_prolog_check reports the run; MLA_PROLOG_FUSED=0
  * (see mla_prolog_create) keeps small-T runs on kernels that wait only
- * between the two blocks of a head. */
+ * between the two blocks of a head.  A wait that gives up marks a word in
+ * host-visible memory: once an earlier run's mark is visible to the host,
+ * mla_prolog_run returns MLA_ERR_RUNTIME with nothing enqueued, until
+ * mla_prolog_check has reported it (a run enqueued before the mark became
+ * visible still runs; mla_prolog_check is the one certain report). */
 mla_status mla_prolog_run(mla_prolog_t handle, const mla_prolog_tensors* tensors, int64_t T,
                           void* stream);
 
@@ -351,7 +355,8 @@ mla_status mla_prolog_destroy(mla_prolog_t handle);
 /* Waits for the handle's device and reports whether any earlier run gave up
  * waiting for another block of its own launch (MLA_ERR_RUNTIME, the runtime
  * class of the page's "Return Value" table; then the outputs of those runs
- * are not to be trusted), else MLA_OK; clears the record.  On the small-T kernels the blocks of one launch hand data to one
+ * are not to be trusted), else MLA_OK; clears the record, after which
+ * mla_prolog_run accepts runs again.  On the small-T kernels the blocks of one launch hand data to one
  * another and wait, with a bounded spin, for it; that can only fail when
  * the launch does not get the whole device (the library checks at create
  * time that all of its blocks fit on the device at once). */

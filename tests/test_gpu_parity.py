@@ -369,11 +369,19 @@ def test_fused_gave_up_is_reported(monkeypatch):
     buf = torch.empty(mla.packed_weights_bytes(desc), dtype=torch.uint8, device="cuda")
     h.pack_weights(t, buf)
     t["packed_weights"] = buf
-    for _ in range(3):
+    h.run(t, int(inp["T"]))
+    torch.cuda.synchronize()
+    # the give-up is visible to the host: the next run is refused, nothing
+    # enqueued, until check() has reported it
+    with pytest.raises(mla.MlaError) as e:
         h.run(t, int(inp["T"]))
+    assert e.value.status == mla.MLA_ERR_RUNTIME
     with pytest.raises(mla.MlaError):
         h.check()
     h.check()   # the record was cleared
+    h.set_poll_limit(0)
+    h.run(t, int(inp["T"]))   # accepted again
+    h.check()
     h.close()
     monkeypatch.delenv("MLA_PROLOG_FUSED_SPIN")
     full_check(inp, packed=True)
@@ -408,7 +416,7 @@ def test_run_after_a_wait_gave_up_is_correct(path, monkeypatch):
         h.set_poll_limit(1)
         gave_up = 0
         for _ in range(8):
-            h.run(dict(t, token_x=-t["token_x"]), T)
+            h.run(dict(t, token_x=-t["token_x"]), T)   # refused only after a give-up that check() clears
             try:
                 h.check()
             except mla.MlaError:
