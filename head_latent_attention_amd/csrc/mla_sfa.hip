@@ -111,10 +111,15 @@ struct SfaArgs {
 
 __global__ __launch_bounds__(64 * kWaves) void k_sfa(SfaArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t kt[kRows * kPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t pw[kWaves][16 * kPPitch];
+  // P of a head group (16 heads x the tile's 32 rows), its two halves
+  // written by the group's two waves; their row maxima of the tile
+  __shared__ __attribute__((aligned(16))) uint16_t pw[kWaves / 2][16 * kPPitch];
+  __shared__ float xmax[kWaves][16];
   __shared__ int32_t slots[kMaxRows];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c = lane & 15;
-  const int hg = w % 4, dh = w / 4;   // head group of 16 and column half of this wave
+  // head group of 16 and column half of this wave; the wave also takes the
+  // tile's rows 16 dh .. 16 dh + 15 in S = Q K^T
+  const int hg = w % 4, dh = w / 4;
   // block -> (token, split) and head group: the head groups of one (token,
   // split) are 8 blocks apart, so they run on the same XCD and share its L2
   const int HB = (a.N + kHeads - 1) / kHeads;
@@ -200,41 +205,42 @@ __global__ __launch_bounds__(64 * kWaves) void k_sfa(SfaArgs a) {
   float m[4], l[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) { m[i] = -INFINITY; l[i] = 0.0f; }
-  uint16_t* pwr = pw[w];
+  uint16_t* pwr = pw[hg];
 
   auto step = [&](int tile) {
-    // S = Q K^T for the tile's two 16-row halves
-    f32x4 sacc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+    // S = Q K^T for this wave's 16-row half of the tile
+    f32x4 sacc = f32x4{0, 0, 0, 0};
 #pragma unroll
     for (int ks = 0; ks < kMaxKS; ++ks) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&kt[(16 * j + c) * kPitch + 32 * ks + 8 * g]);
-        sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb, sacc[j], 0, 0, 0);
-      }
+      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&kt[(16 * dh + c) * kPitch + 32 * ks + 8 * g]);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb, sacc, 0, 0, 0);
     }
-    // sacc[j][i]: head 4g+i of the wave, row 16j + c of the tile
-    bool ok[2];
+    // sacc[i]: head 4g+i of the wave, row 16 dh + c of the tile
+    const int r = tile * kRows + 16 * dh + c;
+    const bool ok = r < nrows && slots[r] >= 0;
+    float sv[4], mh[4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = tile * kRows + 16 * j + c;
-      ok[j] = r < nrows && slots[r] >= 0;
+    for (int i = 0; i < 4; ++i) {
+      sv[i] = ok ? sacc[i] * a.scale : -INFINITY;
+      mh[i] = row16_max(sv[i]);
+      if (c == 0) xmax[w][4 * g + i] = mh[i];
     }
+    // the tile's row maximum of each head takes both halves: the partner's
+    // (the other column half of the head group) through LDS
+    lds_barrier();
     float alpha[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float s0 = ok[0] ? sacc[0][i] * a.scale : -INFINITY;
-      const float s1 = ok[1] ? sacc[1][i] * a.scale : -INFINITY;
-      const float mx = row16_max(fmaxf(s0, s1));
+      const float mx = fmaxf(mh[i], xmax[w ^ 4][4 * g + i]);
       const float mn = fmaxf(m[i], mx);
       const bool none = mn == -INFINITY;
       alpha[i] = none ? 1.0f : __expf(m[i] - mn);
-      const float p0 = none ? 0.0f : __expf(s0 - mn), p1 = none ? 0.0f : __expf(s1 - mn);
-      const float ps = row16_sum(p0 + p1);
-      l[i] = l[i] * alpha[i] + ps;
+      const float pv = none ? 0.0f : __expf(sv[i] - mn);
+      // this half's sum; both waves of the group scale theirs by the same
+      // alpha, so the two sums add up at the end
+      l[i] = l[i] * alpha[i] + row16_sum(pv);
       m[i] = mn;
-      pwr[(4 * g + i) * kPPitch + c] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(p0));
-      pwr[(4 * g + i) * kPPitch + 16 + c] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(p1));
+      pwr[(4 * g + i) * kPPitch + 16 * dh + c] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(pv));
     }
     // rescale O only when a running max of the wave moved (once the maxima
     // settle, most tiles leave them alone)
@@ -244,10 +250,8 @@ __global__ __launch_bounds__(64 * kWaves) void k_sfa(SfaArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[dt][i] *= alpha[i];
     }
-    // P is read back by other lanes of the wave
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // P (both halves) is read back by the lanes of both waves
+    lds_barrier();
     const bf16x8 pa = *reinterpret_cast<const bf16x8*>(&pwr[c * kPPitch + 8 * g]);   // head c, rows 8g..
     // O += P V over this wave's column half: the B fragment (rows 8g..8g+7,
     // column 256dh + 16dt + c) from two transposing reads of 4 rows x 4
@@ -276,6 +280,14 @@ __global__ __launch_bounds__(64 * kWaves) void k_sfa(SfaArgs a) {
     step(tile);
     lds_barrier();
   }
+
+  // each wave holds the sum over its half of the rows: add the partner's
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (c == 0) xmax[w][4 * g + i] = l[i];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) l[i] += xmax[w ^ 4][4 * g + i];
 
   // this split's result, per head row 4g+i of the wave, its column half
 #pragma unroll
