@@ -208,13 +208,16 @@ __global__ __launch_bounds__(64 * kWaves) void k_sfa(SfaArgs a) {
   uint16_t* pwr = pw[hg];
 
   auto step = [&](int tile) {
-    // S = Q K^T for this wave's 16-row half of the tile
-    f32x4 sacc = f32x4{0, 0, 0, 0};
+    // S = Q K^T for this wave's 16-row half of the tile, in two accumulator
+    // chains (even and odd k-steps) so that consecutive MFMAs do not wait
+    // for each other, added at the end
+    f32x4 s2[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
 #pragma unroll
     for (int ks = 0; ks < kMaxKS; ++ks) {
       const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&kt[(16 * dh + c) * kPitch + 32 * ks + 8 * g]);
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb, sacc, 0, 0, 0);
+      s2[ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb, s2[ks & 1], 0, 0, 0);
     }
+    const f32x4 sacc = s2[0] + s2[1];
     // sacc[i]: head 4g+i of the wave, row 16 dh + c of the tile
     const int r = tile * kRows + 16 * dh + c;
     const bool ok = r < nrows && slots[r] >= 0;
