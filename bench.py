@@ -125,7 +125,7 @@ def sfa_bytes(inp, T):
             + T * K * 4 + T * int(inp["max_blocks"]) * 4 + T * 4)
 
 
-def bench_sfa(args):
+def bench_sfa(args, workload):
     """One step = one mla_sfa_run over the workload's tokens.  The caches
     (filled on the device) are several times the Infinity Cache and each
     step takes the next of several index sets, so the selected rows come
@@ -134,7 +134,7 @@ def bench_sfa(args):
     import head_latent_attention_amd as mla
     from dataclasses import replace
     from synth.sfa import make_sfa_inputs, sfa_workload
-    wl = sfa_workload(args.workload)
+    wl = sfa_workload(workload)
     # longer sequences than the parity workload: a 2 GB cache
     wl = replace(wl, len_lo=49152, len_hi=65536)
     sets = 8
@@ -197,7 +197,7 @@ def bench_sfa(args):
     }
     if not args.no_cpu_baseline:
         import oracle
-        small = make_sfa_inputs(replace(sfa_workload(args.workload), T=2, len_lo=4096, len_hi=8192))
+        small = make_sfa_inputs(replace(sfa_workload(workload), T=2, len_lo=4096, len_hi=8192))
         cores = len(os.sched_getaffinity(0))
         oracle.sfa(small, tokens=[0], nthreads=cores)
         done, t0 = 0, time.perf_counter()
@@ -210,7 +210,30 @@ def bench_sfa(args):
         res["cpu_baseline"] = {"value": done / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
                                "sample": f"{done} tokens (passes over a 2-token instance of the workload's "
                                          f"shapes, same sparse_size) in {el:.1f} s"}
-    print(json.dumps(res), flush=True)
+    del dev_sets, kv, kr
+    torch.cuda.empty_cache()
+    return res
+
+
+WORKLOADS = ["decode_t32", "decode_t256", "prefill_t8192", "int8_decode_t128", "partial_decode_t32",
+             "int8_kvq_decode_t128", "pre_decode_t32", "pre_f16_decode_t32", "tiny_t4", "sfa_decode_t32"]
+#: measured after the headline workload in a default run (one line per run
+#: of bench.py, so the other configurations ride along in it)
+OTHERS = ["decode_t256", "int8_decode_t128", "prefill_t8192", "int8_kvq_decode_t128", "partial_decode_t32",
+          "pre_decode_t32", "pre_f16_decode_t32", "sfa_decode_t32"]
+
+
+def summary(res):
+    """The compact record of a secondary workload in the default run's line."""
+    out = {k: res[k] for k in ("value", "unit", "ms_per_step", "steps", "warmup", "dtype") if k in res}
+    out["roofline"] = {k: res["roofline"][k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic",
+                                                       "kernel") if k in res["roofline"]}
+    if "path_roofline" in res:
+        out["path_roofline_frac"] = res["path_roofline"]["frac"]
+    if "kernel_us" in res:
+        out["kernel_us"] = res["kernel_us"]
+    out["config"] = res["config"]
+    return out
 
 
 def main():
@@ -218,10 +241,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode_t32",
-                    choices=["decode_t32", "decode_t256", "prefill_t8192", "int8_decode_t128",
-                             "partial_decode_t32", "int8_kvq_decode_t128", "pre_decode_t32", "pre_f16_decode_t32", "tiny_t4",
-                             "sfa_decode_t32"])
+    ap.add_argument("--workload", default=None, choices=WORKLOADS,
+                    help="one workload; without it, decode_t32 (the line's metric) and then the other "
+                         "configurations at --other-steps steps each, recorded in the same line")
+    ap.add_argument("--other-steps", type=int, default=50)
+    ap.add_argument("--other-warmup", type=int, default=10)
     ap.add_argument("--replicas", type=int, default=0, help="weight replicas (0 = enough to "
                     "exceed twice the Infinity Cache)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -250,15 +274,33 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    if args.workload.startswith("sfa_"):
-        bench_sfa(args)
+    if args.workload is not None:
+        res = (bench_sfa if args.workload.startswith("sfa_") else bench_prolog)(args, args.workload)
+        print(json.dumps(res), flush=True)
         return
+    res = bench_prolog(args, "decode_t32")
+    others = {}
+    sub = argparse.Namespace(**vars(args))
+    sub.steps, sub.warmup, sub.no_cpu_baseline = args.other_steps, args.other_warmup, True
+    for name in OTHERS:
+        try:
+            r = (bench_sfa if name.startswith("sfa_") else bench_prolog)(sub, name)
+            others[name] = summary(r)
+        except Exception as e:   # a failure of one configuration is recorded, not fatal
+            others[name] = {"error": f"{type(e).__name__}: {e}"}
+        print(f"bench: {name} done", file=sys.stderr, flush=True)
+    res["other_workloads"] = others
+    print(json.dumps(res), flush=True)
+
+
+def bench_prolog(args, workload):
+    """One prolog workload: returns its bench record."""
     import torch
     import head_latent_attention_amd as mla
     import synth
     from synth import device as dev
 
-    wl = synth.workload(args.workload)
+    wl = synth.workload(workload)
     inp = synth.make_inputs(wl)
     T = int(inp["T"])
     d = inp["dims"]
@@ -382,7 +424,9 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
-    print(json.dumps(out), flush=True)
+    del sets, base
+    torch.cuda.empty_cache()
+    return out
 
 
 if __name__ == "__main__":
