@@ -773,6 +773,35 @@ def test_packed_runs_without_unpacked_weights(name):
     full_check(synth.make_inputs(wl), packed=True, drop_unpacked=True)
 
 
+@pytest.mark.parametrize("name", ["bf16_t16_one_launch", "int8_t17_paired", "int8_q8_t130_ring", "bf16_t2100_large",
+                                  "static_t37"])
+def test_zero_tokens(name, monkeypatch):
+    # tokens whose x is all zeros: y = 0, c^Q = 0 (eps keeps the norm
+    # finite), the dynamic int8 scales of c^Q and q^N are 0 with codes 0
+    wl = {"bf16_t16_one_launch": custom_workload("z_t16", T=16, dims=Dims(He=384, Hcq=128, Hckv=512, N=16, D=128,
+                                                                         Dr=64), block_num=4, block_size=16, seed=311),
+          "int8_t17_paired": PAIR_INT8["pair_q8_t17_n16"],
+          "int8_q8_t130_ring": INT8_SMALL["q8_t130"],
+          "bf16_t2100_large": custom_workload("z_t2100", T=2100, dims=Dims(He=264, Hcq=72, Hckv=40, N=3, D=24,
+                                                                           Dr=16), block_num=160, block_size=16,
+                                              seed=312),
+          "static_t37": STATIC["pre_t37"]}[name]
+    inp = synth.make_inputs(wl)
+    T = int(inp["T"])
+    x = np.array(inp["token_x"])
+    for t in (0, T // 2, T - 1):
+        x[t] = 0
+    inp["token_x"] = x
+    if name == "int8_t17_paired":
+        monkeypatch.setenv("MLA_PROLOG_FUSED", "0")
+    got = full_check(inp, packed=True)
+    if inp["quant"]:
+        # the zero tokens' int8 q^N is all zeros with scale 0
+        for t in (0, T // 2, T - 1):
+            assert not np.asarray(got["query_out"][t]).any()
+            assert not np.asarray(got["dequant_scale_q_nope"][t]).any()
+
+
 CONCAT_BF16 = {
     "cat_t5": _pre("cat_t5", 5, Dims(He=264, Hcq=72, Hckv=40, N=3, D=24, Dr=16), 101, preprocess=False),
     "cat_t32_pair": _pre("cat_t32_pair", 32, Dims(He=256, Hcq=192, Hckv=320, N=8, D=96, Dr=64), 102,
