@@ -3638,11 +3638,11 @@ struct Layout {
 
 // split-partial rows (S * T) a run of T tokens writes, on any of its paths
 int64_t part_rows_at(const mla_prolog_desc& d, int64_t T) {
+  // every down-projection a run of T tokens may take (row-major, packed
+  // small-T, tiled: fp16 runs take the tiled one at any T)
   const Plan pl = make_plan(d, T);
-  int64_t r = int64_t(pl.S) * T;
-  if (pl.stream) r = std::max<int64_t>(r, int64_t(pl.Sp) * T);
-  else r = std::max<int64_t>(r, int64_t(tiled_plan(d, T).S) * T);
-  return r;
+  const int S = std::max(pl.S, std::max(pl.Sp, tiled_plan(d, T).S));
+  return int64_t(S) * T;
 }
 
 // The workspace regions for runs of up to d.max_tokens tokens whose split

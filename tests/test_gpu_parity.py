@@ -727,6 +727,11 @@ STATIC_F16 = {
     "pre_f16_t600": _pre("pre_f16_t600", 600, Dims(He=512, Hcq=128, Hckv=64, N=2, D=32, Dr=16), 195, fp16=True),
     "pre_f16_t2100": _pre("pre_f16_t2100", 2100, Dims(He=512, Hcq=128, Hckv=64, N=2, D=32, Dr=16), 196,
                           fp16=True),
+    # a small-T run on the tiled down-projection with more He splits than
+    # the small-T plans take (the workspace holds the partials of every
+    # down-projection a run may take)
+    "pre_f16_t17_he2048": _pre("pre_f16_t17_he2048", 17, Dims(He=2048, Hcq=1536, Hckv=512, N=2, D=128, Dr=64),
+                               198, fp16=True),
 }
 
 
