@@ -28,7 +28,7 @@
 //     4 KB k-stages in MFMA operand order), T <= 32, bf16: one launch
 //     (k_fused) whose blocks hand partial results to one another through
 //     agent-scope tagged words and flags;
-//   - packed weights, T <= 32 otherwise: k1_packed, k2_norm, then the
+//   - packed weights, T <= 32 otherwise: k1_tiled, k2_norm, then the
 //     up-projection and W^UK product (k34_pair, k34_stream, or k3_packed
 //     and k4_packed);
 //   - packed weights, T > 32: k1_tiled, k2_norm, k3_tiled, k4_tiled
@@ -869,49 +869,6 @@ __device__ __forceinline__ void stream_packed(const AP& ap, rsrc_t Wp, uint32_t 
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-}
-
-// K1p: grid (windows of W^DQ and W^DkvKr x splits); writes split partials.
-template <bool I8, int MT, int NW, int D>
-__global__ __launch_bounds__(64 * NW) void k1_packed(Dims d, Ptrs p, PackGeo pg, int S, int sps) {
-  using St = Stage<I8>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[(NW / 2) * MT * 16 * 64 * 4];
-  const int tiles = pg.win_dq + pg.win_kr;
-  const int jt = blockIdx.x % tiles, split = blockIdx.x / tiles;
-  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int Nkr = d.Hckv + d.Dr, Ntot = d.Hcq + Nkr;
-  int64_t wbase;
-  int width, outc;
-  if (jt < pg.win_dq) {
-    wbase = pg.off_dq + int64_t(jt) * pg.nst_he * 4096; width = min(64, d.Hcq - 64 * jt); outc = 64 * jt;
-  } else {
-    const int j = jt - pg.win_dq;
-    wbase = pg.off_kr + int64_t(j) * pg.nst_he * 4096; width = min(64, Nkr - 64 * j); outc = d.Hcq + 64 * j;
-  }
-  const int s0 = split * sps, s1 = min(pg.nst_he, s0 + sps);
-  const int ns = s0 + w < s1 ? (s1 - s0 - w + NW - 1) / NW : 0;
-  typename St::Acc acc[MT][4];
-  const APlain<I8, MT> ap{make_rsrc(p.x, int64_t(d.T) * d.He * St::EB), uint32_t(d.He * St::EB), d.T,
-                          d.He};
-  stream_packed<I8, MT, D>(ap, make_rsrc(p.packed, pg.total), uint32_t(wbase), s0 + w, NW, ns, acc);
-  reduce_waves<NW, MT>(acc, reinterpret_cast<uint32_t*>(lds));
-  if (w != 0) return;
-  const int g = lane >> 4, c = lane & 15;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const int col = 16 * ct + c;
-      if (col >= width) continue;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 16 * mt + 4 * g + i;
-        if (m >= d.T) continue;
-        const int64_t o = (int64_t(split) * d.T + m) * Ntot + outc + col;
-        if constexpr (I8) static_cast<int32_t*>(p.part)[o] = acc[mt][ct][i];
-        else static_cast<float*>(p.part)[o] = acc[mt][ct][i];
-      }
-    }
 }
 
 // K2: NWT waves per token, TPB tokens per block.  y is the split-order sum
@@ -3508,7 +3465,6 @@ __global__ __launch_bounds__(64 * WM * WN) void k4_tiled(Dims d, Ptrs p, PackGeo
 constexpr int kStreamMaxT = 32;
 
 struct Plan {
-  int Sp, sps;       // packed K1: split count, stages per split
   bool stream;       // T small enough for the packed kernels
   int mt1, S, kps;   // K1 rows per tile (16*mt1), split count, k per split
   int mt3;           // K3
@@ -3536,13 +3492,6 @@ Plan make_plan(const mla_prolog_desc& d, int64_t T) {
   Plan pl;
   const bool i8 = down_i8(d);
   pl.stream = T <= kStreamMaxT;
-  {
-    const PackGeo g = geo_of(d);
-    const int ptiles = g.win_dq + g.win_kr;
-    int Sp = std::max(1, std::min(g.nst_he, ((i8 ? 256 : 512) + ptiles / 2) / ptiles));
-    pl.sps = ceil_div(g.nst_he, Sp);
-    pl.Sp = ceil_div(g.nst_he, pl.sps);
-  }
   const int bk = i8 ? 128 : 64;
   pl.mt1 = mt_for(T, 16);
   const int col_tiles = ceil_div(d.Hcq, 64) + ceil_div(d.Hckv + d.Dr, 64);
@@ -3641,7 +3590,7 @@ int64_t part_rows_at(const mla_prolog_desc& d, int64_t T) {
   // every down-projection a run of T tokens may take (row-major, packed
   // small-T, tiled: fp16 runs take the tiled one at any T)
   const Plan pl = make_plan(d, T);
-  const int S = std::max(pl.S, std::max(pl.Sp, tiled_plan(d, T).S));
+  const int S = std::max(pl.S, tiled_plan(d, T).S);
   return int64_t(S) * T;
 }
 
@@ -3923,10 +3872,17 @@ template <bool I8D, bool I8U, int MT, class Mark>
 void packed_launch(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g,
                    bool q8, bool pair_ok, Mark& mark) {
   constexpr bool I8 = I8U;   // the up-projection kernels below
-  const int tiles = g.win_dq + g.win_kr;
-  k1_packed<I8D, MT, 4, 2><<<dim3(tiles * pl.Sp), 256, 0, s>>>(d, p, g, pl.Sp, pl.sps);
+  // the down-projection as on the tiled path at these token counts: one
+  // 64-token wave per 64-column window, He split to about kTiledK1Blocks
+  // blocks (9.5 -> 6.7 us int8 and 12.4 -> 9.7 us bf16 at 32 tokens, the
+  // model shapes, against a four-wave split-window kernel)
+  const int tiles = g.win_dq + g.win_kr, m1 = ceil_div(d.T, 64);
+  int S1 = std::max(1, std::min(g.nst_he, kTiledK1Blocks / std::max(1, m1 * tiles)));
+  const int sps1 = ceil_div(g.nst_he, S1);
+  S1 = ceil_div(g.nst_he, sps1);
+  k1_tiled<I8D, 4, 1, 1, 1, 2><<<dim3(m1 * tiles * S1), 64, 0, s>>>(d, p, g, sps1, m1, tiles);
   mark(1);
-  launch_norm<I8D, I8U>(s, d, p, pl.Sp, g.nst_cq);
+  launch_norm<I8D, I8U>(s, d, p, S1, g.nst_cq);
   mark(2);
   if (pair_ok && g.nope_w == 2 && d.Dr == 64 && g.uk_w <= 8) {
     // two balanced blocks per head; the profile books both products to the first
