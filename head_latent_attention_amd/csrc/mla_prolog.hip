@@ -1627,8 +1627,9 @@ __device__ __forceinline__ void pair_wait(const uint32_t* flag, uint32_t* err, u
 
 constexpr int kPairXq = 8192;   // exchange bytes per head: 2 token tiles x 4 D stages x 1 KB
 
-template <bool I8, int MT, bool Q8, int D = 2>
+template <bool I8, int MT, bool Q8, int D = 2, bool F16 = false>
 __global__ __launch_bounds__(512) void k34_pair(Dims d, Ptrs p, PackGeo pg) {
+  static_assert(!F16 || (I8 && !Q8), "fp16 tensors: the static scenario, 16-bit q^N");
   using St = Stage<I8>;
   using Acc = typename St::Acc;
   using Frag = typename St::Frag;
@@ -1754,7 +1755,7 @@ __global__ __launch_bounds__(512) void k34_pair(Dims d, Ptrs p, PackGeo pg) {
     const int st = 2 * half + ct / 2;
     if (st < pg.nst_d)
       xstore64(xq + (mt * 4 + st) * 1024 + (16 * (2 * (ct % 2) + g / 2) + c) * 16 + 8 * (g % 2),
-               pack_bf16x4(v[0], v[1], v[2], v[3]));
+               pack16x4<F16>(v[0], v[1], v[2], v[3]));
   }
   pair_publish(p.xflag + 4 * h + half, d.run);
 
@@ -1783,12 +1784,12 @@ __global__ __launch_bounds__(512) void k34_pair(Dims d, Ptrs p, PackGeo pg) {
           a = a0[r];
           bb = a1[r];
         }
-        o0[r] = a * bf2f(cs0[r]) - bb * bf2f(sn0[r]);
-        o1[r] = bb * bf2f(cs1[r]) + a * bf2f(sn1[r]);
+        o0[r] = a * ld16<F16>(cs0[r]) - bb * ld16<F16>(sn0[r]);
+        o1[r] = bb * ld16<F16>(cs1[r]) + a * ld16<F16>(sn1[r]);
       }
       uint16_t* o = p.qr_out + (int64_t(t) * d.N + h) * d.qrs + i0;
-      *reinterpret_cast<uint2*>(o) = pack_bf16x4(o0[0], o0[1], o0[2], o0[3]);
-      *reinterpret_cast<uint2*>(o + hf) = pack_bf16x4(o1[0], o1[1], o1[2], o1[3]);
+      *reinterpret_cast<uint2*>(o) = pack16x4<F16>(o0[0], o0[1], o0[2], o0[3]);
+      *reinterpret_cast<uint2*>(o + hf) = pack16x4<F16>(o1[0], o1[1], o1[2], o1[3]);
     }
   }
 
@@ -1808,7 +1809,7 @@ __global__ __launch_bounds__(512) void k34_pair(Dims d, Ptrs p, PackGeo pg) {
       au[mt][k] = f32x4{0, 0, 0, 0};
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        au[mt][k] = mfma(__builtin_bit_cast(bf16x8, bu[s][k]), __builtin_bit_cast(bf16x8, aq[s][mt]), au[mt][k]);
+        au[mt][k] = mma16<F16>(__builtin_bit_cast(bf16x8, bu[s][k]), __builtin_bit_cast(bf16x8, aq[s][mt]), au[mt][k]);
     }
   const int col0 = 64 * j + 16 * ctu + 4 * g;   // q^N column of element 0 of tile k = 0
   if constexpr (!Q8) {
@@ -1823,7 +1824,7 @@ __global__ __launch_bounds__(512) void k34_pair(Dims d, Ptrs p, PackGeo pg) {
         const int col = col0 + 16 * k;
         if (col < d.Hckv)
           *reinterpret_cast<uint2*>(qo + (int64_t(t) * d.N + h) * d.qs + col) =
-              pack_bf16x4(au[mt][k][0], au[mt][k][1], au[mt][k][2], au[mt][k][3]);
+              pack16x4<F16>(au[mt][k][0], au[mt][k][1], au[mt][k][2], au[mt][k][3]);
       }
     }
   } else {
@@ -3868,22 +3869,37 @@ void launch_norm(hipStream_t s, const Dims& d, const Ptrs& p, int S, int cq_nst)
 // (norms, c^Q, caches), K3p (up-projection, q-RoPE, q^C), K4p (W^UK).
 // Profiling marks follow the kernels.  I8D: int8 down-projection operands;
 // I8U: int8 c^Q and W^UqQr.
-template <bool I8D, bool I8U, int MT, class Mark>
-void packed_launch(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g,
-                   bool q8, bool pair_ok, Mark& mark) {
-  constexpr bool I8 = I8U;   // the up-projection kernels below
-  // the down-projection as on the tiled path at these token counts: one
-  // 64-token wave per 64-column window, He split to about kTiledK1Blocks
-  // blocks (9.5 -> 6.7 us int8 and 12.4 -> 9.7 us bf16 at 32 tokens, the
-  // model shapes, against a four-wave split-window kernel)
+// The down-projection of a small-T packed run, as on the tiled path at these
+// token counts: one 64-token wave per 64-column window, He split to about
+// kTiledK1Blocks blocks (9.5 -> 6.7 us int8 and 12.4 -> 9.7 us bf16 at 32
+// tokens, the model shapes, against a four-wave split-window kernel), then
+// the norm kernel.
+template <bool I8D, bool I8U, class Mark, bool F16 = false>
+void small_down_norm(hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g, Mark& mark) {
   const int tiles = g.win_dq + g.win_kr, m1 = ceil_div(d.T, 64);
   int S1 = std::max(1, std::min(g.nst_he, kTiledK1Blocks / std::max(1, m1 * tiles)));
   const int sps1 = ceil_div(g.nst_he, S1);
   S1 = ceil_div(g.nst_he, sps1);
   k1_tiled<I8D, 4, 1, 1, 1, 2><<<dim3(m1 * tiles * S1), 64, 0, s>>>(d, p, g, sps1, m1, tiles);
   mark(1);
-  launch_norm<I8D, I8U>(s, d, p, S1, g.nst_cq);
+  launch_norm<I8D, I8U, F16>(s, d, p, S1, g.nst_cq);
   mark(2);
+}
+
+// fp16 tensors (the static scenario), small T, the paired kernel's shapes
+template <int MT, class Mark>
+void packed_launch_f16(hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g, Mark& mark) {
+  small_down_norm<true, true, Mark, true>(s, d, p, g, mark);
+  k34_pair<true, MT, false, 2, true><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g);
+  mark(3);
+  mark(-1);
+}
+
+template <bool I8D, bool I8U, int MT, class Mark>
+void packed_launch(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g,
+                   bool q8, bool pair_ok, Mark& mark) {
+  constexpr bool I8 = I8U;   // the up-projection kernels below
+  small_down_norm<I8D, I8U>(s, d, p, g, mark);
   if (pair_ok && g.nope_w == 2 && d.Dr == 64 && g.uk_w <= 8) {
     // two balanced blocks per head; the profile books both products to the first
     if (q8) k34_pair<I8, MT, true><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g);
@@ -4307,7 +4323,12 @@ mla_status enqueue(const RunCtx& c, const mla_prolog_tensors* t, int64_t T, hipS
   // with the packed copy, every run stays on kernels that read it (the
   // unpacked weights may be absent)
   if (p.packed) {
-    if (pl.stream && dd.float_dtype != MLA_FP16) launch_packed(pl, s, d, p, dd, q8, c.pair_ok, mark);
+    const PackGeo g16 = geo_of(dd);
+    const bool f16_pair = dd.float_dtype == MLA_FP16 && pl.stream && c.pair_ok && g16.nope_w == 2 && d.Dr == 64 &&
+                          g16.uk_w <= 8;
+    if (f16_pair && pl.mt1 == 1) packed_launch_f16<1>(s, d, p, g16, mark);
+    else if (f16_pair) packed_launch_f16<2>(s, d, p, g16, mark);
+    else if (pl.stream && dd.float_dtype != MLA_FP16) launch_packed(pl, s, d, p, dd, q8, c.pair_ok, mark);
     else launch_tiled(s, d, p, dd, q8, c.pair_ok, mark);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? MLA_OK : MLA_ERR_RUNTIME;
