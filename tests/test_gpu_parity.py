@@ -81,8 +81,7 @@ def full_check(inp, query_int8=None, rows=None, packed=False, repeat=1, prerun_n
     got = run_gpu(inp, query_int8=query_int8, packed=packed, repeat=repeat, prerun_negated=prerun_negated,
                   drop_unpacked=drop_unpacked)
     partial = bool(inp.get("partial", False))
-    ref = oracle.run(inp, tokens=rows, query_int8=query_int8, caches=False,
-                     intermediates=partial or bool(inp.get("kv_quant", False)))
+    ref = oracle.run(inp, tokens=rows, query_int8=query_int8, caches=False, intermediates=True)
     if inp.get("concat", False):
         got, ref, inp = split_concat(inp, got), split_concat(inp, ref), split_concat(inp, inp)
     allow = None
@@ -91,7 +90,7 @@ def full_check(inp, query_int8=None, rows=None, packed=False, repeat=1, prerun_n
         aqr, aqn, namb = tie_allowance(inp, ref, rows)
         allow = (aqr, aqn)
         say(f"  c^Q codes within the tie band: {namb}")
-    check_queries(got, ref, rows, q8, allow, fp16=bool(inp.get("fp16", False)))
+    check_queries(got, ref, rows, q8, allow, fp16=bool(inp.get("fp16", False)), inp=inp)
     check_caches(inp, got["kv_cache"], got["kr_cache"], ref, rows)
     return got
 
@@ -160,9 +159,9 @@ def test_no_cache_blocks_still_computes_queries():
     with mla.MlaProlog(mla.make_desc(**args)) as h:
         h.run(t, 6)
         torch.cuda.synchronize()
-    ref = oracle.run(inp, caches=False)
+    ref = oracle.run(inp, caches=False, intermediates=True)
     got = {k: dev.bits(v) for k, v in t.items()}
-    check_queries(got, ref, np.arange(6), False)
+    check_queries(got, ref, np.arange(6), False, inp=inp)
 
 
 def test_out_of_range_slots_are_skipped():
@@ -179,8 +178,8 @@ def test_smaller_run_than_max_tokens():
     say("case T=19 of max 70")
     small = synth.make_inputs(SMALL["mid_t70"], T=19)
     got = run_gpu(small, max_tokens=70)
-    ref = oracle.run(small, caches=False)
-    check_queries(got, ref, np.arange(19), False)
+    ref = oracle.run(small, caches=False, intermediates=True)
+    check_queries(got, ref, np.arange(19), False, inp=small)
     check_caches(small, got["kv_cache"], got["kr_cache"], ref, np.arange(19))
 
 
@@ -351,8 +350,8 @@ def test_fused_mixed_token_counts():
             torch.cuda.synchronize()
             h.check()
             got = {k: dev.bits(v) for k, v in t.items() if k != "packed_weights"}
-            ref = oracle.run(inp, caches=False)
-            check_queries(got, ref, np.arange(T), False)
+            ref = oracle.run(inp, caches=False, intermediates=True)
+            check_queries(got, ref, np.arange(T), False, inp=inp)
             check_caches(inp, got["kv_cache"], got["kr_cache"], ref, np.arange(T))
 
 
@@ -430,8 +429,8 @@ def test_run_after_a_wait_gave_up_is_correct(path, monkeypatch):
             torch.cuda.synchronize()
             h.check()
             got = {k: dev.bits(v) for k, v in t.items() if k != "packed_weights"}
-            ref = oracle.run(inp, caches=False)
-            check_queries(got, ref, np.arange(T), q8)
+            ref = oracle.run(inp, caches=False, intermediates=True)
+            check_queries(got, ref, np.arange(T), q8, inp=inp)
             check_caches(inp, got["kv_cache"], got["kr_cache"], ref, np.arange(T))
 
 
@@ -638,7 +637,8 @@ def test_quantised_cache_skipped_slots_and_no_blocks():
         torch.cuda.synchronize()
     ref = oracle.run(inp0, caches=False, intermediates=True)
     rows = np.arange(5)
-    check_queries({k: dev.bits(v) for k, v in t.items()}, ref, rows, False, tie_allowance(inp0, ref, rows)[:2])
+    check_queries({k: dev.bits(v) for k, v in t.items()}, ref, rows, False, tie_allowance(inp0, ref, rows)[:2],
+                  inp=inp0)
 
 
 def test_full_size_int8_quantised_cache_packed():
@@ -866,9 +866,9 @@ def test_static_no_cache_blocks_still_computes_queries():
         t["packed_weights"] = buf
         h.run(t, int(inp["T"]))
         torch.cuda.synchronize()
-    ref = split_concat(inp, oracle.run(inp, caches=False))
+    ref = split_concat(inp, oracle.run(inp, caches=False, intermediates=True))
     got = split_concat(inp, {"query_out": dev.bits(t["query_out"])})
-    check_queries(got, ref, np.arange(int(inp["T"])), False)
+    check_queries(got, ref, np.arange(int(inp["T"])), False, inp=inp)
 
 
 def test_static_smaller_run_than_max_tokens():
@@ -884,6 +884,6 @@ def test_static_smaller_run_than_max_tokens():
         h.run(t, 23)
         torch.cuda.synchronize()
     got = split_concat(small, {k: dev.bits(v) for k, v in t.items() if k in ("query_out", "kv_cache")})
-    ref = split_concat(small, oracle.run(small, caches=False))
-    check_queries(got, ref, np.arange(23), False)
+    ref = split_concat(small, oracle.run(small, caches=False, intermediates=True))
+    check_queries(got, ref, np.arange(23), False, inp=small)
     check_caches(split_concat(small, small), got["kv_cache"], got["kr_cache"], ref, np.arange(23))

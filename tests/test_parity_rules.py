@@ -1,13 +1,13 @@
 """The comparison rules of tests/parity.py on the CPU, with the oracle on both
-sides: the allowance for int8 c^Q codes at a rounding tie covers a code
-rounded the other way and nothing more."""
+sides: the allowances for int8 c^Q codes at a rounding tie and for q^C at a
+rounding midpoint cover a value rounded the other way and nothing more."""
 import numpy as np
 import pytest
 
 import oracle
 import synth
 from synth.generate import Dims, custom_workload
-from parity import check_queries, tie_allowance
+from parity import check_queries, qc_tie_allowance, tie_allowance
 
 # token 35 of this workload has a c^Q * m code exactly at a tie in fp32
 WL = custom_workload("partial_t37", T=37, dims=Dims(He=264, Hcq=80, Hckv=40, N=3, D=32, Dr=16),
@@ -71,3 +71,47 @@ def test_fp16_outputs_must_carry_fp16_precision():
     bad = dict(ref, query_out=_bf16_round_as_fp16(ref["query_out"]))
     with pytest.raises(AssertionError, match="not fp16's"):
         check_queries(bad, ref, rows, False, fp16=True)
+
+
+# token 209 of this workload has u (head 2, nope column 70) within 1e-5 of a
+# bf16 step of a rounding midpoint: q^C = bf16(u) may round either way
+QC_WL = custom_workload("ring_partial_n3_d96_t256", T=256, dims=Dims(He=512, Hcq=192, Hckv=128, N=3, D=96, Dr=64),
+                        block_num=17, block_size=16, partial=True, smooth=True, seed=386)
+QC_TOKEN, QC_HEAD, QC_COL = 209, 2, 70
+
+
+def _qc_case():
+    inp = synth.make_inputs(QC_WL)
+    rows = [QC_TOKEN]
+    ref = oracle.run(inp, tokens=rows, caches=False, intermediates=True)
+    d = inp["dims"]
+    # nudge that column's dequantisation scale so that the oracle's u crosses
+    # the midpoint; no other element of u moves
+    col = QC_HEAD * (d.D + d.Dr) + QC_COL
+    sw = inp["dequant_scale_w_uq_qr"].copy()
+    sw[col] = np.float32(sw[col] * np.float32(1 + 2 ** -20))
+    flipped = oracle.run(dict(inp, dequant_scale_w_uq_qr=sw), tokens=rows, caches=False, intermediates=True)
+    return inp, ref, flipped
+
+
+def test_qc_allowance_covers_a_midpoint_rounded_the_other_way():
+    inp, ref, flipped = _qc_case()
+    d = inp["dims"]
+    u0 = ref["u"].reshape(d.N, d.D + d.Dr)
+    u1 = flipped["u"].reshape(d.N, d.D + d.Dr)
+    moved = np.argwhere(u0 != u1)
+    assert moved.tolist() == [[QC_HEAD, QC_COL]]
+    assert abs(u1[QC_HEAD, QC_COL] / u0[QC_HEAD, QC_COL] - 1) < 2e-6
+    allow = qc_tie_allowance(inp, ref)
+    assert allow[0, QC_HEAD].max() > 0 and allow[0, :QC_HEAD].max() == 0
+    rows = np.array([0])
+    with pytest.raises(AssertionError):
+        check_queries(flipped, ref, rows, False)             # the plain tolerance is too tight
+    check_queries(flipped, ref, rows, False, inp=inp)         # the allowance covers the other rounding
+
+
+def test_qc_allowance_does_not_hide_a_planted_mistake():
+    inp, ref, _ = _qc_case()
+    bad = oracle.run(inp, tokens=[QC_TOKEN], caches=False, mutation=4)   # W^UK read transposed
+    with pytest.raises(AssertionError):
+        check_queries(bad, ref, np.array([0]), False, inp=inp)
