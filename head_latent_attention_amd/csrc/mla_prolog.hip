@@ -1917,9 +1917,9 @@ __global__ __launch_bounds__(512) void k34_pair(Dims d, Ptrs p, PackGeo pg) {
 // The memory counter of a wave completes in order, so a wave that waits on
 // another block must not have loads of its own in flight: wave 0 does all the
 // waiting and takes no phase-3 k-stages, while waves 1..7 share the Hcq
-// stages and issue their phase-3 weight loads (W^UK and the first kFusedPE
-// k-stages) once wave 0 has summed its window rows, holding them in
-// registers through the rest of the wait.  Wave 0 issues no load that spans
+// stages, issue their W^UK loads right behind phase 1's and the first
+// kFusedPE k-stages of phase 3 once wave 0 has summed its window rows, and
+// hold them in registers through the rest of the wait.  Wave 0 issues no load that spans
 // that point (the compiler merges outstanding-load counts where the waves'
 // paths join, so a load older than the prefetch would make wave 0 wait for
 // loads it never issued).
@@ -2042,6 +2042,11 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
     ax.load(a1[q], st, ok);
   }
   __builtin_amdgcn_sched_barrier(0);
+  // waves 1..7 fetch their W^UK fragments behind phase 1's loads: phase 1
+  // leaves HBM short of its rate, and phase 1's waits are for the loads
+  // issued before these (wave 0's are out of range and return at once)
+  issue_uk(w != 0);
+  __builtin_amdgcn_sched_barrier(0);
   Acc acc1[MT][4];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -2143,14 +2148,13 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
       }
     }
   }
-  // the phase-3 prefetch goes out once phase 1's loads are in (so that it
-  // does not delay them) and wave 0 has summed its window rows (the partials
-  // land far faster while HBM is quiet); the barrier orders LDS only
+  // the phase-3 ring prefetch goes out once phase 1's loads are in (so that
+  // it does not delay them) and wave 0 has summed its window rows (the
+  // partials land far faster while HBM is quiet); the barrier orders LDS only
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   if (w != 0) {
-    issue_uk(true);
 #pragma unroll
     for (int q = 0; q < kFusedPE; ++q) issue_w3(pre[q], q);
   }
