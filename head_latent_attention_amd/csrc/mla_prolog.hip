@@ -25,7 +25,8 @@
 //
 // Execution paths, by token count and weight layout:
 //   - packed weights (mla_prolog_pack_weights: 64-column windows stored as
-//     4 KB k-stages in MFMA operand order), T <= 32, bf16: one launch
+//     4 KB k-stages in MFMA operand order), T <= 32, bf16 or partial
+//     quantisation (int8 c^Q and W^UqQr): one launch
 //     (k_fused) whose blocks hand partial results to one another through
 //     agent-scope tagged words and flags;
 //   - packed weights, T <= 32 otherwise: k1_tiled, k2_norm, then the
@@ -327,7 +328,8 @@ struct Ptrs {
   float* xmax;       // [N][2][32] its per-token row maxima
   float* xmax2;      // [N][2][kRingMaxT]: the medium-T fused kernel's per-token row maxima
   uint32_t* fpart;   // fused kernel: [phase-1 blocks][32][64] (fp32 split partial, run tag) words
-  uint32_t* fss;     // fused kernel: [windows][32] (fp32 sum of squares, run tag) words
+  uint32_t* fss;     // fused kernel: [windows][32] (fp32 sum of squares, run tag) words, then (int8
+                     // c^Q) [c^Q windows][32] (fp32 max |gamma m y|, run tag) words
   float* fykr;       // fused kernel: [32][Hckv + Dr] y of the c^KV and k^R columns
   uint32_t* fcnt;    // fused kernel: [2N] flags, 64 bytes apart
   uint32_t* herr;    // the handle's error word, in host-visible memory: set when a bounded wait gives up
@@ -1877,9 +1879,10 @@ __global__ __launch_bounds__(512) void k34_pair(Dims d, Ptrs p, PackGeo pg) {
 }
 
 // ---------------------------------------------------------------------------
-// Fused small-T kernel: the whole prolog (bf16) in one launch of 2N blocks,
-// two per head, 512 threads, all resident on the device at once (the host
-// checks the occupancy before it picks this kernel).
+// Fused small-T kernel: the whole prolog (bf16, or with I8U the partial
+// quantisation scenario: bf16 down-projection, int8 c^Q and W^UqQr) in one
+// launch of 2N blocks, two per head, 512 threads, all resident on the device
+// at once (the host checks the occupancy before it picks this kernel).
 //
 // Phase 1.  Blocks 0 .. P1-1 each take a split of the He k-stages of one
 // 64-column window of [W^DQ | W^DkvKr] (at most eight splits a window, the
@@ -1897,8 +1900,12 @@ __global__ __launch_bounds__(512) void k34_pair(Dims d, Ptrs p, PackGeo pg) {
 // tagged window sums of its rows, adds them in a fixed order (the same bits
 // in every block) and writes c^Q = bf16(gamma_cq y / rms), fragment-packed
 // like c^Q on the packed path: the rounding point of the row-by-row
-// RmsNorm.  Every split block raises its own flag once its stores are
-// complete, and every block waits for all flags of the run.
+// RmsNorm.  With I8U each c^Q window's split blocks also publish the row's
+// max |gamma m y| over the window (m: smoothScalesCq), tagged next to the
+// sum of squares, so the c^Q blocks take the row's int8 scale
+// s = max |c^Q m| / 127 from the same poll and write int8 codes (and window
+// 0's blocks the scale) instead.  Every split block raises its own flag once
+// its stores are complete, and every block waits for all flags of the run.
 //
 // Phase 3 is the paired up-projection and W^UK product of k34_pair.  One
 // wave per block also writes one 64-column chunk of a c^KV row (and, for
@@ -1962,11 +1969,19 @@ __device__ __forceinline__ bool fused_poll_done(bool ok, int& n, int spin, uint3
   return false;
 }
 
-template <int MT>
+template <int MT, bool I8U = false>
 __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, FusedGeo fg) {
   using Acc = f32x4;
+  // the up-projection's operands: bf16, or int8 c^Q codes and W^UqQr (the
+  // partial-quantisation scenario)
+  using S3 = Stage<I8U>;
+  using Acc3 = typename S3::Acc;
+  using Frag3 = typename S3::Frag;
   constexpr int NW = 8, NT = 6 * MT, R = 16 * MT;
   __shared__ __attribute__((aligned(16))) uint4 red[NW * NT * 64];
+  // int8: the dequantisation scales of the block's 96 up-projection columns
+  // (nope window `half`, then rope column tiles half and half + 2)
+  __shared__ float swl[I8U ? 96 : 1];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, c = lane & 15;
   const int b = blockIdx.x, G = gridDim.x;
@@ -1974,6 +1989,8 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
   // flags of the split blocks, one per 64-byte line
   uint32_t* const flag = p.fcnt;
   uint32_t* const err = p.herr;
+  // int8 c^Q: the row maxima's tagged words follow the sums of squares
+  uint32_t* const fgm = p.fss + (pg.win_dq + pg.win_kr) * 64;
 
   // ---- the block's head and half in phase 3 (as in k34_pair)
   const int h = d.N % 8 == 0 ? (b / 16) * 8 + b % 8 : b / 2;
@@ -2046,6 +2063,14 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
   // leaves HBM short of its rate, and phase 1's waits are for the loads
   // issued before these (wave 0's are out of range and return at once)
   issue_uk(w != 0);
+  // int8: the 96 column scales, behind phase 1's loads; they go to LDS once
+  // phase 1's waves have been summed
+  float swv = 0.0f;
+  if constexpr (I8U) {
+    const int k = threadIdx.x;
+    const int col = k < 64 ? 64 * half + k : d.D + 16 * (half + 2 * ((k - 64) >> 4)) + (k & 15);
+    if (k < 96 && (k >= 64 || col < d.D)) swv = p.sw_uq_qr[h * DDr + col];
+  }
   __builtin_amdgcn_sched_barrier(0);
   Acc acc1[MT][4];
 #pragma unroll
@@ -2061,6 +2086,9 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
       for (int ct = 0; ct < 4; ++ct) acc1[mt][ct] = mfma(af, __builtin_bit_cast(bf16x8, b1[q][ct]), acc1[mt][ct]);
     }
   reduce_waves<NW, MT>(acc1, reinterpret_cast<uint32_t*>(red));
+  if constexpr (I8U) {
+    if (threadIdx.x < 96) swl[threadIdx.x] = swv;
+  }
 
   // wave 0 of a split block publishes the block's partial before any
   // prefetch is issued (its memory pipeline is then free of other loads).
@@ -2070,6 +2098,16 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
   const bool qwin = j < pg.win_dq;
   const int col0 = (qwin ? 64 * j : 64 * (j - pg.win_dq)) + 2 * q2;   // column in W^DQ or W^DkvKr
   const uint32_t run = d.run;
+  // int8 c^Q: gamma times the smoothing factor of the lane's two columns
+  double gq2[2] = {0.0, 0.0};
+  if constexpr (I8U) {
+    if (w == 0 && S && qwin) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        if (col0 + e < d.Hcq)
+          gq2[e] = double(bf2f(p.gamma_cq[col0 + e])) * (p.smooth_cq ? double(p.smooth_cq[col0 + e]) : 1.0);
+    }
+  }
   if (w == 0 && S) {
     // the block's partial, rows 16 mt + 4 g + i, columns 16 ct + c, each
     // value next to this run's tag
@@ -2136,6 +2174,15 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
 #pragma unroll
           for (int o = 1; o < 32; o <<= 1) ss += __shfl_xor(ss, o, 64);
           if (act[u] && q2 == 0) xstore64(p.fss + (j * 32 + r) * 2, make_uint2(__float_as_uint(float(ss)), run));
+          if constexpr (I8U) {
+            // and the row's max |gamma m y| over the window, for c^Q's int8 scale
+            if (qwin) {
+              double gm = fmax(fabs(gq2[0] * double(y[0])), fabs(gq2[1] * double(y[1])));
+#pragma unroll
+              for (int o = 1; o < 32; o <<= 1) gm = fmax(gm, __shfl_xor(gm, o, 64));
+              if (act[u] && q2 == 0) xstore64(fgm + (j * 32 + r) * 2, make_uint2(__float_as_uint(float(gm)), run));
+            }
+          }
           if (!act[u]) continue;
           if (qwin) {
             ylds[r * 64 + 2 * q2] = y[0];
@@ -2170,21 +2217,24 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         const rsrc_t Sp = make_rsrc(p.fss, int64_t(pg.win_dq) * 32 * 8);
+        const rsrc_t Gp = make_rsrc(fgm, I8U ? int64_t(pg.win_dq) * 32 * 8 : 0);
         for (int rb = r0; rb < r1; rb += 2 * kFusedRowSets) {
           int rr[kFusedRowSets];
           bool act[kFusedRowSets];
           double ss[kFusedRowSets];
+          float gmx[kFusedRowSets];   // int8: the row's max |gamma m y| so far
 #pragma unroll
           for (int u = 0; u < kFusedRowSets; ++u) {
             rr[u] = rb + 2 * u + (lane >> 5);
             act[u] = rr[u] < r1;
             ss[u] = 0.0;
+            gmx[u] = 0.0f;
           }
           // lane q2 adds windows q2, q2 + 32, ..., then the row's 32 lanes
           // are added: a fixed order, the same in every block; the row sets
           // are polled together
           for (int j0 = q2; j0 < pg.win_dq; j0 += 128) {
-            uint2 v[kFusedRowSets][4];
+            uint2 v[kFusedRowSets][4], vg[kFusedRowSets][I8U ? 4 : 1];
             int n = 0;
             for (;;) {
 #pragma unroll
@@ -2193,24 +2243,56 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
                 for (int k = 0; k < 4; ++k) {
                   const int jj = j0 + 32 * k;
                   v[u][k] = bload8u(Sp, act[u] && jj < pg.win_dq ? uint32_t(jj * 32 + rr[u]) * 8u : kOOB);
+                  if constexpr (I8U)
+                    vg[u][k] = bload8u(Gp, act[u] && jj < pg.win_dq ? uint32_t(jj * 32 + rr[u]) * 8u : kOOB);
                 }
               bool ok = true;
 #pragma unroll
               for (int u = 0; u < kFusedRowSets; ++u)
 #pragma unroll
-                for (int k = 0; k < 4; ++k) ok &= !(act[u] && j0 + 32 * k < pg.win_dq) || v[u][k].y == run;
+                for (int k = 0; k < 4; ++k) {
+                  ok &= !(act[u] && j0 + 32 * k < pg.win_dq) || v[u][k].y == run;
+                  if constexpr (I8U) ok &= !(act[u] && j0 + 32 * k < pg.win_dq) || vg[u][k].y == run;
+                }
               if (fused_poll_done(ok, n, d.spin, err)) break;
             }
 #pragma unroll
             for (int u = 0; u < kFusedRowSets; ++u)
 #pragma unroll
-              for (int k = 0; k < 4; ++k) ss[u] += double(__uint_as_float(v[u][k].x));   // zeros past win_dq
+              for (int k = 0; k < 4; ++k) {
+                ss[u] += double(__uint_as_float(v[u][k].x));   // zeros past win_dq
+                if constexpr (I8U) gmx[u] = fmaxf(gmx[u], __uint_as_float(vg[u][k].x));
+              }
           }
 #pragma unroll
           for (int u = 0; u < kFusedRowSets; ++u) {
             const int r = rr[u];
 #pragma unroll
             for (int o = 1; o < 32; o <<= 1) ss[u] += __shfl_xor(ss[u], o, 64);
+            if constexpr (I8U) {
+              // int8 c^Q: the row's scale s = max |c^Q m| / 127 and the
+              // codes of the lane's two columns; the even lane of each pair
+              // stores the pair's four codes, and window 0's blocks the scale
+#pragma unroll
+              for (int o = 1; o < 32; o <<= 1) gmx[u] = fmaxf(gmx[u], __shfl_xor(gmx[u], o, 64));
+              const double rms = sqrt(ss[u] / double(d.Hcq) + d.eps_cq);
+              const float sc = float(double(gmx[u]) / rms) / 127.0f;
+              uint32_t mine = 0;
+#pragma unroll
+              for (int e = 0; e < 2; ++e) {
+                const float cv = float(gq2[e] * double(ylds[r * 64 + 2 * q2 + e]) / rms);
+                mine |= uint32_t(uint8_t(sc > 0.0f ? quant_code(cv, sc) : int8_t(0))) << (8 * e);
+              }
+              const uint32_t other = __shfl_xor(mine, 1, 64);
+              if (act[u] && (q2 & 1) == 0) {
+                uint32_t* dst = reinterpret_cast<uint32_t*>(
+                    p.cq + packed_offset(r, col0, int64_t(pg.nst_cq) * 1024, true));
+                __hip_atomic_store(dst, mine | (other << 16), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              }
+              if (act[u] && j == 0 && q2 == 0 && r < d.T)
+                __hip_atomic_store(p.cq_scale + r, sc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              continue;
+            }
             const int stg = col0 / 32;
             if (act[u] && stg < pg.nst_cq) {
               const double rms = sqrt(ss[u] / double(d.Hcq) + d.eps_cq);
@@ -2255,6 +2337,16 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
 
   // ---- phase 3 (wave 0's W^UK fragments are only read at the very end)
   if (w == 0) issue_uk(true);
+  // int8: c^Q's scale for the lane's tokens c and 16 + c (written this run
+  // by window 0's blocks, before their flags)
+  float scq[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    scq[mt] = 0.0f;
+    if constexpr (I8U)
+      if (16 * mt + c < d.T)
+        scq[mt] = __hip_atomic_load(p.cq_scale + 16 * mt + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   // cache jobs: job jb = (token jb / cj, 64-column chunk jb % cj of c^KV;
   // chunk 0 also writes k^R).  Wave 7 takes jobs b, b + G, ...; the loads of
   // the first are issued now and used after the stream.
@@ -2323,22 +2415,22 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
 #pragma unroll
   for (int q = 0; q < kFusedPF; ++q) issue_a(aq[q], q);
   __builtin_amdgcn_sched_barrier(0);
-  Acc an[MT][4], ar[MT][2];
+  Acc3 an[MT][4], ar[MT][2];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) an[mt][ct] = Acc{0, 0, 0, 0};
+    for (int ct = 0; ct < 4; ++ct) an[mt][ct] = Acc3{0, 0, 0, 0};
 #pragma unroll
-    for (int k = 0; k < 2; ++k) ar[mt][k] = Acc{0, 0, 0, 0};
+    for (int k = 0; k < 2; ++k) ar[mt][k] = Acc3{0, 0, 0, 0};
   }
   auto consume = [&](const uint4 (&wq)[6], const uint4 (&a)[MT]) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const bf16x8 af = __builtin_bit_cast(bf16x8, a[mt]);
+      const Frag3 af = __builtin_bit_cast(Frag3, a[mt]);
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) an[mt][ct] = mfma(__builtin_bit_cast(bf16x8, wq[ct]), af, an[mt][ct]);
+      for (int ct = 0; ct < 4; ++ct) an[mt][ct] = mma16<false>(__builtin_bit_cast(Frag3, wq[ct]), af, an[mt][ct]);
 #pragma unroll
-      for (int k = 0; k < 2; ++k) ar[mt][k] = mfma(__builtin_bit_cast(bf16x8, wq[4 + k]), af, ar[mt][k]);
+      for (int k = 0; k < 2; ++k) ar[mt][k] = mma16<false>(__builtin_bit_cast(Frag3, wq[4 + k]), af, ar[mt][k]);
     }
   };
   // a register ring of kFusedPF stages: stage q + kFusedPF refills the slot
@@ -2365,10 +2457,21 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
   }
   __syncthreads();
   auto sum_tile = [&](int q) {
-    Acc sm = __builtin_bit_cast(Acc, red[q * 64 + lane]);
+    Acc3 sm = __builtin_bit_cast(Acc3, red[q * 64 + lane]);
 #pragma unroll
-    for (int w2 = 1; w2 < NW; ++w2) sm += __builtin_bit_cast(Acc, red[(w2 * NT + q) * 64 + lane]);
+    for (int w2 = 1; w2 < NW; ++w2) sm += __builtin_bit_cast(Acc3, red[(w2 * NT + q) * 64 + lane]);
     return sm;
+  };
+  // a summed tile as floats: int8 products dequantised (s_cq of the lane's
+  // token, the column's scale), in fp32 as the other int8 paths do
+  auto to_f = [&](const Acc3& v, int mt, int k0) {
+    f32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (I8U) o[i] = static_cast<float>(v[i]) * scq[mt] * swl[k0 + i];
+      else o[i] = v[i];
+    }
+    return o;
   };
   uint8_t* xq = p.xq + int64_t(h) * kPairXq;
 
@@ -2376,7 +2479,7 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
   // fragment order of the W^UK product's activation operand
   if (w < 4 * MT) {
     const int mt = w / 4, ct = w % 4;
-    const Acc sm = sum_tile(w);
+    const Acc sm = to_f(sum_tile(w), mt, 16 * ct + 4 * g);
     const int st = 2 * half + ct / 2;
     if (st < pg.nst_d)
       xstore64(xq + (mt * 4 + st) * 1024 + (16 * (2 * (ct % 2) + g / 2) + c) * 16 + 8 * (g % 2),
@@ -2394,7 +2497,8 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
   // q^R: the owner of token tile mt holds both tiles of every RoPE pair
   if (w >= NW - MT) {
     const int mt = NW - 1 - w, t = 16 * mt + c;
-    const Acc a0 = sum_tile(4 * MT + 2 * mt), a1v = sum_tile(4 * MT + 2 * mt + 1);
+    const Acc a0 = to_f(sum_tile(4 * MT + 2 * mt), mt, 64 + 4 * g),
+              a1v = to_f(sum_tile(4 * MT + 2 * mt + 1), mt, 80 + 4 * g);
     if (t < d.T) {
       const int i0 = 16 * half + 4 * g, hf = d.Dr / 2;
       const uint2 c0 = *reinterpret_cast<const uint2*>(p.cos + int64_t(t) * d.Dr + i0);
@@ -3629,7 +3733,7 @@ Layout layout(const mla_prolog_desc& d, int64_t part_rows, bool small_t) {
   const size_t x8_bytes = d.in_dtype == MLA_INT8_STATIC ? size_t(d.max_tokens) * d.He : 0;
   L.fpart = align256(L.x8 + x8_bytes);
   L.fss = align256(L.fpart + st * size_t(2 * d.N) * 32 * 64 * 8);
-  L.fykr = align256(L.fss + st * nwin * 32 * 8);
+  L.fykr = align256(L.fss + st * (nwin + g.win_dq) * 32 * 8);
   L.fcnt = align256(L.fykr + st * size_t(32) * (d.Hckv + d.Dr) * 4);
   L.total = align256(L.fcnt + st * (size_t(2 * d.N) * kFusedFlagStride + 1) * 4);
   return L;
@@ -3931,7 +4035,9 @@ void packed_launch(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p, 
 // the phase-1 windows over the 2N blocks, or false when the shapes are
 // outside what the kernel holds in registers.
 bool fused_geo(const mla_prolog_desc& dd, FusedGeo* fg) {
-  if (dd.in_dtype != MLA_BF16 || dd.query_dtype != MLA_BF16 || dd.cache_dtype != MLA_BF16) return false;
+  if ((dd.in_dtype != MLA_BF16 && dd.in_dtype != MLA_INT8_PARTIAL) || dd.query_dtype != MLA_BF16 ||
+      dd.cache_dtype != MLA_BF16)
+    return false;
   const PackGeo g = geo_of(dd);
   if (g.nope_w != 2 || dd.Dr != 64 || g.uk_w > 8 || g.nst_d > 4) return false;
   const int G = int(2 * dd.N), W = g.win_dq + g.win_kr;
@@ -4189,10 +4295,16 @@ mla_status mla_prolog_create(const mla_prolog_desc* desc, mla_prolog_t* out) {
     int cus = 0, nb1 = 0, nb2 = 0;
     if (!(env && env[0] == '0') && fused_geo(*desc, &fg) &&
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, desc->device) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb1, reinterpret_cast<const void*>(k_fused<1>), 512, 0) ==
-            hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb2, reinterpret_cast<const void*>(k_fused<2>), 512, 0) ==
-            hipSuccess) {
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &nb1,
+            desc->in_dtype == MLA_INT8_PARTIAL ? reinterpret_cast<const void*>(k_fused<1, true>)
+                                               : reinterpret_cast<const void*>(k_fused<1>),
+            512, 0) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &nb2,
+            desc->in_dtype == MLA_INT8_PARTIAL ? reinterpret_cast<const void*>(k_fused<2, true>)
+                                               : reinterpret_cast<const void*>(k_fused<2>),
+            512, 0) == hipSuccess) {
       h->fused_fit[0] = int64_t(nb1) * cus >= 2 * desc->N;
       h->fused_fit[1] = int64_t(nb2) * cus >= 2 * desc->N;
     }
@@ -4318,8 +4430,14 @@ mla_status enqueue(const RunCtx& c, const mla_prolog_tensors* t, int64_t T, hipS
   FusedGeo fg;
   if (p.packed && pl.stream && c.fused_ok && dd.float_dtype != MLA_FP16 && fused_geo(dd, &fg)) {
     const PackGeo g = geo_of(dd);
-    if (pl.mt1 == 1) k_fused<1><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g, fg);
-    else k_fused<2><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g, fg);
+    if (dd.in_dtype == MLA_INT8_PARTIAL) {
+      if (pl.mt1 == 1) k_fused<1, true><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g, fg);
+      else k_fused<2, true><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g, fg);
+    } else if (pl.mt1 == 1) {
+      k_fused<1><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g, fg);
+    } else {
+      k_fused<2><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g, fg);
+    }
     mark(-2);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? MLA_OK : MLA_ERR_RUNTIME;

@@ -550,6 +550,15 @@ def test_partial_packed(name):
     full_check(inp, packed=True, repeat=2, prerun_negated=True)
 
 
+@pytest.mark.parametrize("name", ["pair_partial_t5_n4", "pair_partial_t32_n8"])
+def test_partial_packed_unfused(name, monkeypatch):
+    # up to 32 tokens these run in one launch; this keeps the down-projection,
+    # norm and paired int8 kernels that serve when not all of that launch's
+    # blocks fit on the device
+    monkeypatch.setenv("MLA_PROLOG_FUSED", "0")
+    full_check(synth.make_inputs(PARTIAL[name]), packed=True, repeat=2, prerun_negated=True)
+
+
 @pytest.mark.parametrize("T", [32, 33, 64, 65, 100, 128, 129])
 def test_shape_boundaries_partial_packed(T):
     wl = custom_workload(f"boundary_partial_t{T}", T=T, dims=Dims(He=520, Hcq=128, Hckv=88, N=2, D=32, Dr=32),
