@@ -25,8 +25,9 @@
 //
 // Execution paths, by token count and weight layout:
 //   - packed weights (mla_prolog_pack_weights: 64-column windows stored as
-//     4 KB k-stages in MFMA operand order), T <= 32, bf16 or partial
-//     quantisation (int8 c^Q and W^UqQr): one launch
+//     4 KB k-stages in MFMA operand order), T <= 32, bf16 tensors (bf16,
+//     partial quantisation, or the static scenario after k0_xquant): one
+//     launch
 //     (k_fused) whose blocks hand partial results to one another through
 //     agent-scope tagged words and flags;
 //   - packed weights, T <= 32 otherwise: k1_tiled, k2_norm, then the
@@ -1879,10 +1880,12 @@ __global__ __launch_bounds__(512) void k34_pair(Dims d, Ptrs p, PackGeo pg) {
 }
 
 // ---------------------------------------------------------------------------
-// Fused small-T kernel: the whole prolog (bf16, or with I8U the partial
-// quantisation scenario: bf16 down-projection, int8 c^Q and W^UqQr) in one
-// launch of 2N blocks, two per head, 512 threads, all resident on the device
-// at once (the host checks the occupancy before it picks this kernel).
+// Fused small-T kernel: the whole prolog (bf16; with I8U the partial
+// quantisation scenario: bf16 down-projection, int8 c^Q and W^UqQr; with ST
+// as well the static scenario: int8 x codes and weights, bias0/deScale0,
+// static c^Q codes, bias1/deScale1) in one launch of 2N blocks, two per
+// head, 512 threads, all resident on the device at once (the host checks
+// the occupancy before it picks this kernel).
 //
 // Phase 1.  Blocks 0 .. P1-1 each take a split of the He k-stages of one
 // 64-column window of [W^DQ | W^DkvKr] (at most eight splits a window, the
@@ -1904,7 +1907,9 @@ __global__ __launch_bounds__(512) void k34_pair(Dims d, Ptrs p, PackGeo pg) {
 // max |gamma m y| over the window (m: smoothScalesCq), tagged next to the
 // sum of squares, so the c^Q blocks take the row's int8 scale
 // s = max |c^Q m| / 127 from the same poll and write int8 codes (and window
-// 0's blocks the scale) instead.  Every split block raises its own flag once
+// 0's blocks the scale) instead; with ST the window sums are exact int32
+// sums made y = (acc + bias0) deScale0 in double, and c^Q takes the static
+// codes of gamma y / rms + beta1.  Every split block raises its own flag once
 // its stores are complete, and every block waits for all flags of the run.
 //
 // Phase 3 is the paired up-projection and W^UK product of k34_pair.  One
@@ -1969,11 +1974,17 @@ __device__ __forceinline__ bool fused_poll_done(bool ok, int& n, int spin, uint3
   return false;
 }
 
-template <int MT, bool I8U = false>
+template <int MT, bool I8U = false, bool ST = false>
 __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, FusedGeo fg) {
+  static_assert(!ST || I8U, "the static scenario is int8 throughout");
   using Acc = f32x4;
+  // the down-projection's operands: bf16, or (ST, the static scenario) the
+  // int8 codes of x and int8 [W^DQ | W^DkvKr], exact int32 partials
+  using S1 = Stage<ST>;
+  using Acc1 = typename S1::Acc;
+  using Frag1 = typename S1::Frag;
   // the up-projection's operands: bf16, or int8 c^Q codes and W^UqQr (the
-  // partial-quantisation scenario)
+  // partial-quantisation and static scenarios)
   using S3 = Stage<I8U>;
   using Acc3 = typename S3::Acc;
   using Frag3 = typename S3::Frag;
@@ -1982,6 +1993,7 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
   // int8: the dequantisation scales of the block's 96 up-projection columns
   // (nope window `half`, then rope column tiles half and half + 2)
   __shared__ float swl[I8U ? 96 : 1];
+  __shared__ int32_t bsl[ST ? 96 : 1];   // ST: their bias1
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, c = lane & 15;
   const int b = blockIdx.x, G = gridDim.x;
@@ -2047,7 +2059,7 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
   const int ns1 = st0 + w < st1 ? (st1 - st0 - w + NW - 1) / NW : 0;
   const uint32_t w1b = uint32_t(j < pg.win_dq ? pg.off_dq + int64_t(j) * pg.nst_he * 4096
                                               : pg.off_kr + int64_t(j - pg.win_dq) * pg.nst_he * 4096);
-  const APlain<false, MT> ax{make_rsrc(p.x, int64_t(d.T) * d.He * 2), uint32_t(d.He * 2), d.T, d.He};
+  const APlain<ST, MT> ax{make_rsrc(p.x, int64_t(d.T) * d.He * S1::EB), uint32_t(d.He * S1::EB), d.T, d.He};
   uint4 b1[kFusedP1][4], a1[kFusedP1][MT];
 #pragma unroll
   for (int q = 0; q < kFusedP1; ++q) {
@@ -2066,28 +2078,36 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
   // int8: the 96 column scales, behind phase 1's loads; they go to LDS once
   // phase 1's waves have been summed
   float swv = 0.0f;
+  int32_t bsv = 0;
   if constexpr (I8U) {
     const int k = threadIdx.x;
     const int col = k < 64 ? 64 * half + k : d.D + 16 * (half + 2 * ((k - 64) >> 4)) + (k & 15);
-    if (k < 96 && (k >= 64 || col < d.D)) swv = p.sw_uq_qr[h * DDr + col];
+    if (k < 96 && (k >= 64 || col < d.D)) {
+      swv = p.sw_uq_qr[h * DDr + col];
+      if (ST && p.bias_uq) bsv = p.bias_uq[h * DDr + col];
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
-  Acc acc1[MT][4];
+  Acc1 acc1[MT][4];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) acc1[mt][ct] = Acc{0, 0, 0, 0};
+    for (int ct = 0; ct < 4; ++ct) acc1[mt][ct] = Acc1{0, 0, 0, 0};
 #pragma unroll
   for (int q = 0; q < kFusedP1; ++q)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const bf16x8 af = __builtin_bit_cast(bf16x8, a1[q][mt]);
+      const Frag1 af = __builtin_bit_cast(Frag1, a1[q][mt]);
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) acc1[mt][ct] = mfma(af, __builtin_bit_cast(bf16x8, b1[q][ct]), acc1[mt][ct]);
+      for (int ct = 0; ct < 4; ++ct)
+        acc1[mt][ct] = mma16<false>(af, __builtin_bit_cast(Frag1, b1[q][ct]), acc1[mt][ct]);
     }
   reduce_waves<NW, MT>(acc1, reinterpret_cast<uint32_t*>(red));
   if constexpr (I8U) {
-    if (threadIdx.x < 96) swl[threadIdx.x] = swv;
+    if (threadIdx.x < 96) {
+      swl[threadIdx.x] = swv;
+      if constexpr (ST) bsl[threadIdx.x] = bsv;
+    }
   }
 
   // wave 0 of a split block publishes the block's partial before any
@@ -2100,12 +2120,30 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
   const uint32_t run = d.run;
   // int8 c^Q: gamma times the smoothing factor of the lane's two columns
   double gq2[2] = {0.0, 0.0};
+  // ST: the lane's columns' bias0 and deScale0 (y = (acc + bias) deScale,
+  // in double), and beta1 of its c^Q columns
+  int32_t bq2[2] = {0, 0};
+  double sw2[2] = {0.0, 0.0}, be2[2] = {0.0, 0.0};
   if constexpr (I8U) {
     if (w == 0 && S && qwin) {
 #pragma unroll
       for (int e = 0; e < 2; ++e)
-        if (col0 + e < d.Hcq)
+        if (col0 + e < d.Hcq) {
           gq2[e] = double(bf2f(p.gamma_cq[col0 + e])) * (p.smooth_cq ? double(p.smooth_cq[col0 + e]) : 1.0);
+          if constexpr (ST) be2[e] = double(bf2f(p.beta_cq[col0 + e]));
+        }
+    }
+  }
+  if constexpr (ST) {
+    if (w == 0 && S) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int cc = col0 + e;
+        if (cc < (qwin ? d.Hcq : d.Hckv + d.Dr)) {
+          if (p.bias_dq) bq2[e] = p.bias_dq[(qwin ? 0 : d.Hcq) + cc];
+          sw2[e] = double(qwin ? p.sw_dq[cc] : p.sw_dkv_kr[cc]);
+        }
+      }
     }
   }
   if (w == 0 && S) {
@@ -2118,11 +2156,13 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float v = acc1[mt][ct][i];
-          xstore64(mine + ((16 * mt + 4 * g + i) * 64 + 16 * ct + c) * 2, make_uint2(__float_as_uint(v), run));
+          const auto v = acc1[mt][ct][i];
+          xstore64(mine + ((16 * mt + 4 * g + i) * 64 + 16 * ct + c) * 2,
+                   make_uint2(__builtin_bit_cast(uint32_t, v), run));
         }
   }
   float* const ylds = reinterpret_cast<float*>(red);   // [R][64] y of the c^Q window rows
+  double* const ylds_d = reinterpret_cast<double*>(red);   // ST: in double
   if (w == 0 && S) {
     {
       const rsrc_t Fp = make_rsrc(p.fpart, int64_t(fg.p1) * R * 64 * 8);
@@ -2161,20 +2201,37 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
         for (int u = 0; u < kFusedRowSets; ++u) {
           const int r = rr[u];
           float y[2] = {0, 0};
+          double yd[2];   // ST: y in double
+          if constexpr (ST) {
+            // exact int32 sums, then (acc + bias0) deScale0
+            int32_t iy[2] = {0, 0};
 #pragma unroll
-          for (int k = 0; k < kFusedMaxSplits; ++k)
+            for (int k = 0; k < kFusedMaxSplits; ++k)
 #pragma unroll
-            for (int e = 0; e < 2; ++e) y[e] += __uint_as_float(v[u][k][e].x);   // words past S read zeros
+              for (int e = 0; e < 2; ++e) iy[e] += int32_t(v[u][k][e].x);   // words past S read zeros
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              yd[e] = double(iy[e] + bq2[e]) * sw2[e];
+              y[e] = float(yd[e]);
+            }
+          } else {
+#pragma unroll
+            for (int k = 0; k < kFusedMaxSplits; ++k)
+#pragma unroll
+              for (int e = 0; e < 2; ++e) y[e] += __uint_as_float(v[u][k][e].x);   // words past S read zeros
+#pragma unroll
+            for (int e = 0; e < 2; ++e) yd[e] = double(y[e]);
+          }
           // the row's sum of squares over the window (c^KV columns only in
           // the c^KV / k^R windows), tagged
           double ss = 0.0;
 #pragma unroll
           for (int e = 0; e < 2; ++e)
-            if (qwin || col0 + e < d.Hckv) ss += double(y[e]) * double(y[e]);
+            if (qwin || col0 + e < d.Hckv) ss += yd[e] * yd[e];
 #pragma unroll
           for (int o = 1; o < 32; o <<= 1) ss += __shfl_xor(ss, o, 64);
           if (act[u] && q2 == 0) xstore64(p.fss + (j * 32 + r) * 2, make_uint2(__float_as_uint(float(ss)), run));
-          if constexpr (I8U) {
+          if constexpr (I8U && !ST) {
             // and the row's max |gamma m y| over the window, for c^Q's int8 scale
             if (qwin) {
               double gm = fmax(fabs(gq2[0] * double(y[0])), fabs(gq2[1] * double(y[1])));
@@ -2184,7 +2241,10 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
             }
           }
           if (!act[u]) continue;
-          if (qwin) {
+          if (qwin && ST) {
+            ylds_d[r * 64 + 2 * q2] = yd[0];
+            ylds_d[r * 64 + 2 * q2 + 1] = yd[1];
+          } else if (qwin) {
             ylds[r * 64 + 2 * q2] = y[0];
             ylds[r * 64 + 2 * q2 + 1] = y[1];
           } else if (col0 < d.Hckv + d.Dr) {
@@ -2243,7 +2303,7 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
                 for (int k = 0; k < 4; ++k) {
                   const int jj = j0 + 32 * k;
                   v[u][k] = bload8u(Sp, act[u] && jj < pg.win_dq ? uint32_t(jj * 32 + rr[u]) * 8u : kOOB);
-                  if constexpr (I8U)
+                  if constexpr (I8U && !ST)
                     vg[u][k] = bload8u(Gp, act[u] && jj < pg.win_dq ? uint32_t(jj * 32 + rr[u]) * 8u : kOOB);
                 }
               bool ok = true;
@@ -2252,7 +2312,7 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                   ok &= !(act[u] && j0 + 32 * k < pg.win_dq) || v[u][k].y == run;
-                  if constexpr (I8U) ok &= !(act[u] && j0 + 32 * k < pg.win_dq) || vg[u][k].y == run;
+                  if constexpr (I8U && !ST) ok &= !(act[u] && j0 + 32 * k < pg.win_dq) || vg[u][k].y == run;
                 }
               if (fused_poll_done(ok, n, d.spin, err)) break;
             }
@@ -2261,7 +2321,7 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
 #pragma unroll
               for (int k = 0; k < 4; ++k) {
                 ss[u] += double(__uint_as_float(v[u][k].x));   // zeros past win_dq
-                if constexpr (I8U) gmx[u] = fmaxf(gmx[u], __uint_as_float(vg[u][k].x));
+                if constexpr (I8U && !ST) gmx[u] = fmaxf(gmx[u], __uint_as_float(vg[u][k].x));
               }
           }
 #pragma unroll
@@ -2269,7 +2329,25 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
             const int r = rr[u];
 #pragma unroll
             for (int o = 1; o < 32; o <<= 1) ss[u] += __shfl_xor(ss[u], o, 64);
-            if constexpr (I8U) {
+            if constexpr (ST) {
+              // static codes of c^Q + beta1 (quantScale1, quantOffset1); the
+              // even lane of each pair stores the pair's four codes
+              const double rms = sqrt(ss[u] / double(d.Hcq) + d.eps_cq);
+              const float st_s = bf2f(*p.qsc_cq), st_o = float(*p.qo_cq);
+              uint32_t mine = 0;
+#pragma unroll
+              for (int e = 0; e < 2; ++e) {
+                const float cv = float(gq2[e] * ylds_d[r * 64 + 2 * q2 + e] / rms + be2[e]);
+                mine |= static_code(cv, st_s, st_o) << (8 * e);
+              }
+              const uint32_t other = __shfl_xor(mine, 1, 64);
+              if (act[u] && (q2 & 1) == 0) {
+                uint32_t* dst = reinterpret_cast<uint32_t*>(
+                    p.cq + packed_offset(r, col0, int64_t(pg.nst_cq) * 1024, true));
+                __hip_atomic_store(dst, mine | (other << 16), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              }
+              continue;
+            } else if constexpr (I8U) {
               // int8 c^Q: the row's scale s = max |c^Q m| / 127 and the
               // codes of the lane's two columns; the even lane of each pair
               // stores the pair's four codes, and window 0's blocks the scale
@@ -2342,8 +2420,8 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
   float scq[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    scq[mt] = 0.0f;
-    if constexpr (I8U)
+    scq[mt] = ST ? 1.0f : 0.0f;   // static codes: the per-channel deScale1 does all the scaling
+    if constexpr (I8U && !ST)
       if (16 * mt + c < d.T)
         scq[mt] = __hip_atomic_load(p.cq_scale + 16 * mt + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -2468,7 +2546,8 @@ __global__ __launch_bounds__(512) void k_fused(Dims d, Ptrs p, PackGeo pg, Fused
     f32x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if constexpr (I8U) o[i] = static_cast<float>(v[i]) * scq[mt] * swl[k0 + i];
+      if constexpr (ST) o[i] = static_cast<float>(v[i] + bsl[k0 + i]) * scq[mt] * swl[k0 + i];
+      else if constexpr (I8U) o[i] = static_cast<float>(v[i]) * scq[mt] * swl[k0 + i];
       else o[i] = v[i];
     }
     return o;
@@ -4035,8 +4114,8 @@ void packed_launch(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p, 
 // the phase-1 windows over the 2N blocks, or false when the shapes are
 // outside what the kernel holds in registers.
 bool fused_geo(const mla_prolog_desc& dd, FusedGeo* fg) {
-  if ((dd.in_dtype != MLA_BF16 && dd.in_dtype != MLA_INT8_PARTIAL) || dd.query_dtype != MLA_BF16 ||
-      dd.cache_dtype != MLA_BF16)
+  if ((dd.in_dtype != MLA_BF16 && dd.in_dtype != MLA_INT8_PARTIAL && dd.in_dtype != MLA_INT8_STATIC) ||
+      dd.query_dtype != MLA_BF16 || dd.cache_dtype != MLA_BF16 || dd.float_dtype != MLA_BF16)
     return false;
   const PackGeo g = geo_of(dd);
   if (g.nope_w != 2 || dd.Dr != 64 || g.uk_w > 8 || g.nst_d > 4) return false;
@@ -4055,6 +4134,16 @@ bool fused_geo(const mla_prolog_desc& dd, FusedGeo* fg) {
   const int smin = fg->hi_win < W ? fg->hi_s - 1 : fg->hi_s;
   if ((ceil_div(g.nst_he, smin) + 7) / 8 > kFusedP1) return false;
   return true;
+}
+
+// the fused kernel's instance for a description's scenario, MT 1 or 2
+const void* fused_kernel(const mla_prolog_desc& dd, int mt) {
+  if (dd.in_dtype == MLA_INT8_STATIC)
+    return mt == 1 ? reinterpret_cast<const void*>(k_fused<1, true, true>)
+                   : reinterpret_cast<const void*>(k_fused<2, true, true>);
+  if (dd.in_dtype == MLA_INT8_PARTIAL)
+    return mt == 1 ? reinterpret_cast<const void*>(k_fused<1, true>) : reinterpret_cast<const void*>(k_fused<2, true>);
+  return mt == 1 ? reinterpret_cast<const void*>(k_fused<1>) : reinterpret_cast<const void*>(k_fused<2>);
 }
 
 template <int MT, class Mark>
@@ -4295,16 +4384,8 @@ mla_status mla_prolog_create(const mla_prolog_desc* desc, mla_prolog_t* out) {
     int cus = 0, nb1 = 0, nb2 = 0;
     if (!(env && env[0] == '0') && fused_geo(*desc, &fg) &&
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, desc->device) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &nb1,
-            desc->in_dtype == MLA_INT8_PARTIAL ? reinterpret_cast<const void*>(k_fused<1, true>)
-                                               : reinterpret_cast<const void*>(k_fused<1>),
-            512, 0) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &nb2,
-            desc->in_dtype == MLA_INT8_PARTIAL ? reinterpret_cast<const void*>(k_fused<2, true>)
-                                               : reinterpret_cast<const void*>(k_fused<2>),
-            512, 0) == hipSuccess) {
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb1, fused_kernel(*desc, 1), 512, 0) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb2, fused_kernel(*desc, 2), 512, 0) == hipSuccess) {
       h->fused_fit[0] = int64_t(nb1) * cus >= 2 * desc->N;
       h->fused_fit[1] = int64_t(nb2) * cus >= 2 * desc->N;
     }
@@ -4430,7 +4511,10 @@ mla_status enqueue(const RunCtx& c, const mla_prolog_tensors* t, int64_t T, hipS
   FusedGeo fg;
   if (p.packed && pl.stream && c.fused_ok && dd.float_dtype != MLA_FP16 && fused_geo(dd, &fg)) {
     const PackGeo g = geo_of(dd);
-    if (dd.in_dtype == MLA_INT8_PARTIAL) {
+    if (dd.in_dtype == MLA_INT8_STATIC) {
+      if (pl.mt1 == 1) k_fused<1, true, true><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g, fg);
+      else k_fused<2, true, true><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g, fg);
+    } else if (dd.in_dtype == MLA_INT8_PARTIAL) {
       if (pl.mt1 == 1) k_fused<1, true><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g, fg);
       else k_fused<2, true><<<dim3(2 * d.N), 512, 0, s>>>(d, p, g, fg);
     } else if (pl.mt1 == 1) {

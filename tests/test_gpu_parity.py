@@ -694,6 +694,7 @@ STATIC = {
     "pre_t4": synth.workload("tiny_pre_t4"),
     "pre_t37": _pre("pre_t37", 37, Dims(He=272, Hcq=80, Hckv=48, N=3, D=32, Dr=16), 91),
     "pre_t17_pair": _pre("pre_t17_pair", 17, Dims(He=512, Hcq=256, Hckv=256, N=8, D=128, Dr=64), 92),
+    "pre_t9_pair": _pre("pre_t9_pair", 9, Dims(He=528, Hcq=320, Hckv=192, N=8, D=128, Dr=64), 99),
     "pre_t70": _pre("pre_t70", 70, MID, 93),
     "pre_t130": _pre("pre_t130", 130, Dims(He=1024, Hcq=192, Hckv=512, N=3, D=128, Dr=64), 94),
     "pre_t600": _pre("pre_t600", 600, Dims(He=512, Hcq=128, Hckv=64, N=2, D=32, Dr=16), 95),
@@ -703,6 +704,15 @@ STATIC = {
 
 @pytest.mark.parametrize("name", list(STATIC))
 def test_static_packed(name):
+    full_check(synth.make_inputs(STATIC[name]), packed=True, repeat=2, prerun_negated=True)
+
+
+@pytest.mark.parametrize("name", ["pre_t9_pair", "pre_t17_pair"])
+def test_static_packed_unfused(name, monkeypatch):
+    # up to 32 tokens these run in one launch after the x quantiser; this
+    # keeps the down-projection, norm and paired int8 kernels that serve when
+    # not all of that launch's blocks fit on the device
+    monkeypatch.setenv("MLA_PROLOG_FUSED", "0")
     full_check(synth.make_inputs(STATIC[name]), packed=True, repeat=2, prerun_negated=True)
 
 
