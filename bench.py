@@ -367,9 +367,10 @@ def bench_prolog(args, workload):
     one = kernel_us["down_proj"] == 0.0 and kernel_us["norm_rope_cache"] == 0.0
     fused = kernel_us["uk"] == 0.0
     if one:
-        # one launch per step: the timed region's per-step time (HIP events
-        # around back-to-back launches on the run's stream) is the kernel's
-        # average duration, free of the per-kernel events' dispatch delay
+        # one launch per step (two in the static scenario, whose x quantiser
+        # comes first): the timed region's per-step time (HIP events around
+        # back-to-back launches on the run's stream) is the kernel's average
+        # duration, free of the per-kernel events' dispatch delay
         alg["k3_bytes"] = alg["step_bytes"]
         alg["k3_flop"] = alg["step_flop"]
         k3_us = ms_step * 1000.0
@@ -392,7 +393,9 @@ def bench_prolog(args, workload):
         path = {"bound": "mfma", "achieved": path_ach, "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": path_ach / BF16_PEAK_TFLOPS,
                 "flop_per_step": alg["step_flop"]}
-    roof["kernel"] = "prolog (one kernel)" if one else "up_proj+uk (fused)" if fused else "up_proj"
+    # (the static scenario's one-kernel runs have the x quantiser in front)
+    roof["kernel"] = (("x quantiser + prolog (one kernel)" if inp.get("preprocess", False) else "prolog (one kernel)")
+                      if one else "up_proj+uk (fused)" if fused else "up_proj")
     if not args.row_major:
         roof["traffic"] = measured_traffic(wl.name, roof["kernel"])
     roof["per_launch"] = (f"{alg['k3_bytes']} B" if decode else f"{alg['k3_flop']} FLOP")
