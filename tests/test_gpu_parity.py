@@ -452,6 +452,12 @@ TILED = {
     "t2100_large": custom_workload("t2100_large", T=2100,
                                    dims=Dims(He=264, Hcq=72, Hckv=40, N=3, D=24, Dr=16),
                                    block_num=160, block_size=16, seed=36),
+    # the long-run kernels at Dr = 64: a ragged last token tile, a ragged
+    # last window group (15 windows), a half-empty second nope window (D = 96)
+    # and an odd k-stage count (Hcq = 200)
+    "t2100_wide": custom_workload("t2100_wide", T=2100,
+                                  dims=Dims(He=520, Hcq=200, Hckv=136, N=5, D=96, Dr=64),
+                                  block_num=160, block_size=16, seed=38),
 }
 
 
