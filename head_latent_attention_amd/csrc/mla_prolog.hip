@@ -896,6 +896,11 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
   static_assert(!F16 || ST, "fp16 tensors belong to the static scenario");
   __shared__ double red[NWT * TPB][3];
   __shared__ double ry[TPB][64];   // the token's y of the k^R columns (Dr <= 64)
+  // one wave per token: the lane's chunks CPL .. CPL+YX-1 of y wait for the
+  // second pass in the wave's own LDS rows (element e of chunk k of lane l
+  // at [k][e][l]), so only chunks past those are read twice
+  constexpr int YX = NWT == 1 ? 4 : 0;
+  __shared__ double ysl[YX ? TPB : 1][YX ? YX : 1][8][64];
   const int w = threadIdx.x >> 6;
   const int lane = (w % NWT) * 64 + (threadIdx.x & 63);   // lane among the token's waves
   constexpr int L = 64 * NWT;
@@ -955,21 +960,46 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
   };
   // y of the eight columns 8j .. 8j+7; the loads of eight splits at a time
   // are issued together (a missing split reads as zeros, an exact no-op)
+  // with at most two splits, the loads (ld2, zeros unless ok) and the sum
+  // (sum2) of a chunk are separate steps, so several chunks' loads can go
+  // out together
+  auto ld2 = [&](int j, bool ok, uint4 (&r)[4]) {
+    const uint32_t o = uint32_t((int64_t(t) * Ntot + 8 * j) * 4);
+    const uint32_t o2 = uint32_t(((int64_t(d.T) + t) * Ntot + 8 * j) * 4);
+    r[0] = bload16(P, ok ? o : kOOB);
+    r[1] = bload16(P, ok ? o + 16 : kOOB);
+    r[2] = bload16(P, ok && S == 2 ? o2 : kOOB);
+    r[3] = bload16(P, ok && S == 2 ? o2 + 16 : kOOB);
+  };
+  auto sum2 = [&](const uint4 (&r)[4], double (&f)[8], int32_t (&iv)[8]) {
+    const uint32_t w8[8] = {r[0].x, r[0].y, r[0].z, r[0].w, r[1].x, r[1].y, r[1].z, r[1].w};
+    const uint32_t v8[8] = {r[2].x, r[2].y, r[2].z, r[2].w, r[3].x, r[3].y, r[3].z, r[3].w};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      if constexpr (I8D) iv[c] = int32_t(w8[c]) + int32_t(v8[c]);
+      else f[c] = double(__uint_as_float(w8[c])) + double(__uint_as_float(v8[c]));
+    }
+  };
+  // the column scaling of a chunk's sums into y
+  auto scale8 = [&](const Side& sd, const double (&f)[8], const int32_t (&iv)[8], double (&v)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (I8D) {
+        const double sw = double(__uint_as_float(w32(sd.sw0, sd.sw1, e)));
+        const int32_t b = ST ? int32_t(w32(sd.b0, sd.b1, e)) : 0;
+        v[e] = double(iv[e] + b) * sx * sw;
+      } else {
+        v[e] = f[e];
+      }
+    }
+  };
   auto y8 = [&](int j, const Side& sd, double (&v)[8]) {
     double f[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     int32_t iv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (S <= 2) {
-      const uint32_t o = uint32_t((int64_t(t) * Ntot + 8 * j) * 4);
-      const uint32_t o2 = uint32_t(((int64_t(d.T) + t) * Ntot + 8 * j) * 4);
-      const uint4 a = bload16(P, o), b = bload16(P, o + 16);
-      const uint4 a2 = bload16(P, S == 2 ? o2 : kOOB), b2 = bload16(P, S == 2 ? o2 + 16 : kOOB);
-      const uint32_t w8[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-      const uint32_t v8[8] = {a2.x, a2.y, a2.z, a2.w, b2.x, b2.y, b2.z, b2.w};
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        if constexpr (I8D) iv[c] = int32_t(w8[c]) + int32_t(v8[c]);
-        else f[c] = double(__uint_as_float(w8[c])) + double(__uint_as_float(v8[c]));
-      }
+      uint4 r[4];
+      ld2(j, true, r);
+      sum2(r, f, iv);
     }
     for (int s0 = 0; S > 2 && s0 < S; s0 += 8) {
       uint4 r[16];
@@ -990,16 +1020,7 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
         }
       }
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if constexpr (I8D) {
-        const double sw = double(__uint_as_float(w32(sd.sw0, sd.sw1, e)));
-        const int32_t b = ST ? int32_t(w32(sd.b0, sd.b1, e)) : 0;
-        v[e] = double(iv[e] + b) * sx * sw;
-      } else {
-        v[e] = f[e];
-      }
-    }
+    scale8(sd, f, iv, v);
   };
 
   // the c^Q weight: gamma, times smoothScalesCq for an int8 c^Q when given
@@ -1032,15 +1053,69 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
 #pragma unroll
   for (int c = 0; c < CPL; ++c) sdv[c] = side(lane + c * L);
   double yv[CPL][8];
+  // pass 1 over the register-held chunks, then the LDS-held ones (YX); with
+  // those and at most two splits every load of both goes out at once
+  if (YX > 0 && S <= 2) {
+    uint4 rc[CPL][4], raw[YX ? YX : 1][4];
+    Side sdx[YX ? YX : 1];
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    const int j = lane + c * L;
-    if (active && j < chunks) {
-      y8(j, sdv[c], yv[c]);
-      sums(j, sdv[c], yv[c]);
+    for (int c = 0; c < CPL; ++c) {
+      const int j = lane + c * L;
+      ld2(j, active && j < chunks, rc[c]);
+    }
+#pragma unroll
+    for (int k = 0; k < YX; ++k) {
+      const int j = lane + (CPL + k) * L;
+      ld2(j, active && j < chunks, raw[k]);
+      sdx[k] = side(j);
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int j = lane + c * L;
+      if (active && j < chunks) {
+        double f[8];
+        int32_t iv[8];
+        sum2(rc[c], f, iv);
+        scale8(sdv[c], f, iv, yv[c]);
+        sums(j, sdv[c], yv[c]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < YX; ++k) {
+      const int j = lane + (CPL + k) * L;
+      if (active && j < chunks) {
+        double f[8], v[8];
+        int32_t iv[8];
+        sum2(raw[k], f, iv);
+        scale8(sdx[k], f, iv, v);
+        sums(j, sdx[k], v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ysl[w / NWT][k][e][lane] = v[e];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int j = lane + c * L;
+      if (active && j < chunks) {
+        y8(j, sdv[c], yv[c]);
+        sums(j, sdv[c], yv[c]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < YX; ++k) {
+      const int j = lane + (CPL + k) * L;
+      if (active && j < chunks) {
+        double v[8];
+        const Side sd = side(j);
+        y8(j, sd, v);
+        sums(j, sd, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ysl[w / NWT][k][e][lane] = v[e];
+      }
     }
   }
-  for (int j = lane + CPL * L; active && j < chunks; j += L) {
+  for (int j = lane + (CPL + YX) * L; active && j < chunks; j += L) {
     double v[8];
     const Side sd = side(j);
     y8(j, sd, v);
@@ -1126,7 +1201,17 @@ __global__ __launch_bounds__(64 * NWT * TPB) void k2_norm(Dims d, Ptrs p, int S,
     const int j = lane + c * L;
     if (j < chunks) emit(j, sdv[c], yv[c]);
   }
-  for (int j = lane + CPL * L; j < chunks; j += L) {
+#pragma unroll
+  for (int k = 0; k < YX; ++k) {
+    const int j = lane + (CPL + k) * L;
+    if (j < chunks && (j < cq_c || cache)) {
+      double v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = ysl[w / NWT][k][e][lane];
+      emit(j, side(j), v);
+    }
+  }
+  for (int j = lane + (CPL + YX) * L; j < chunks; j += L) {
     if (j >= cq_c && !cache) break;
     double v[8];
     const Side sd = side(j);
