@@ -881,10 +881,11 @@ __device__ __forceinline__ void stream_packed(const AP& ap, rsrc_t Wp, uint32_t 
 // column's deScale0, and c^Q + beta1 takes static codes with scale 1).  A first pass sums the squares of the c^Q and c^KV parts
 // (and, for an int8 c^Q, I8U, finds the largest |gamma m y| of the c^Q part,
 // m the optional smoothScalesCq), keeping each lane's first CPL 8-column
-// chunks of y in registers; a second pass writes c^Q (bf16, or the
-// per-token int8 of c^Q * m + scale), the c^KV row at the token's cacheIndex
-// slot and, through a small LDS row, the RoPE'd k^R row, reloading only the
-// chunks beyond CPL.  The norms are computed in double, so the per-token
+// chunks of y in registers (and, with one wave per token, the next four in
+// the wave's LDS rows); a second pass writes c^Q (bf16, or the per-token
+// int8 of c^Q * m + scale), the c^KV row at the token's cacheIndex slot and,
+// through a small LDS row, the RoPE'd k^R row, reloading only the chunks
+// held in neither.  The norms are computed in double, so the per-token
 // int8 decision of c^Q sees c rounded once to fp32; c^Q * m is formed as
 // (gamma m) y / rms, gamma m being exact in double.
 // With cq_nst > 0, c^Q is stored fragment-packed (cq_nst k-stages per
