@@ -120,14 +120,6 @@ __device__ __forceinline__ uint32_t static_code(float v, float s, float off) {
   return uint32_t(uint8_t(int8_t(r)));
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
 __device__ __forceinline__ double wave_sum_f64(double v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
@@ -135,20 +127,6 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 __device__ __forceinline__ double wave_max_f64(double v) {
   for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
   return v;
-}
-
-// Sum (or max) of one value per thread over the 256-thread block, in a fixed
-// order; red must hold 4 floats.  Every thread gets the result.
-template <bool MAX>
-__device__ float block_reduce(float v, float* red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  v = MAX ? wave_max(v) : wave_sum(v);
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  float r = red[0];
-  for (int w = 1; w < 4; ++w) r = MAX ? fmaxf(r, red[w]) : r + red[w];
-  return r;
 }
 
 // ---------------------------------------------------------------------------
@@ -4169,8 +4147,8 @@ void packed_launch_f16(hipStream_t s, const Dims& d, const Ptrs& p, const PackGe
 }
 
 template <bool I8D, bool I8U, int MT, class Mark>
-void packed_launch(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g,
-                   bool q8, bool pair_ok, Mark& mark) {
+void packed_launch(hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g, bool q8, bool pair_ok,
+                   Mark& mark) {
   constexpr bool I8 = I8U;   // the up-projection kernels below
   small_down_norm<I8D, I8U>(s, d, p, g, mark);
   if (pair_ok && g.nope_w == 2 && d.Dr == 64 && g.uk_w <= 8) {
@@ -4233,19 +4211,19 @@ const void* fused_kernel(const mla_prolog_desc& dd, int mt) {
 }
 
 template <int MT, class Mark>
-void packed_launch_mt(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g,
-                      bool i8d, bool i8u, bool q8, bool pair_ok, Mark& mark) {
-  if (i8d) packed_launch<true, true, MT>(pl, s, d, p, g, q8, pair_ok, mark);
-  else if (i8u) packed_launch<false, true, MT>(pl, s, d, p, g, q8, pair_ok, mark);
-  else packed_launch<false, false, MT>(pl, s, d, p, g, q8, pair_ok, mark);
+void packed_launch_mt(hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g, bool i8d, bool i8u,
+                      bool q8, bool pair_ok, Mark& mark) {
+  if (i8d) packed_launch<true, true, MT>(s, d, p, g, q8, pair_ok, mark);
+  else if (i8u) packed_launch<false, true, MT>(s, d, p, g, q8, pair_ok, mark);
+  else packed_launch<false, false, MT>(s, d, p, g, q8, pair_ok, mark);
 }
 
 template <class Mark>
 void launch_packed(const Plan& pl, hipStream_t s, const Dims& d, const Ptrs& p,
                    const mla_prolog_desc& dd, bool q8, bool pair_ok, Mark& mark) {
   const PackGeo g = geo_of(dd);
-  if (pl.mt1 == 1) packed_launch_mt<1>(pl, s, d, p, g, down_i8(dd), up_i8(dd), q8, pair_ok, mark);
-  else packed_launch_mt<2>(pl, s, d, p, g, down_i8(dd), up_i8(dd), q8, pair_ok, mark);
+  if (pl.mt1 == 1) packed_launch_mt<1>(s, d, p, g, down_i8(dd), up_i8(dd), q8, pair_ok, mark);
+  else packed_launch_mt<2>(s, d, p, g, down_i8(dd), up_i8(dd), q8, pair_ok, mark);
 }
 
 // K3r: 2N blocks; 16 or 32 tokens per wave; the instance unrolling the

@@ -50,7 +50,6 @@ constexpr int kPer = 5;               // 16-byte loads per thread per tile: 32 r
 constexpr int kMaxRows = 2048;        // selected rows of one block
 constexpr int kPPitch = kRows + 8;    // per-wave P tile pitch (bf16)
 
-__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 __device__ __forceinline__ uint16_t f2bf(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
