@@ -4649,6 +4649,21 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   if (prev != dd.device && hipSetDevice(dd.device) != hipSuccess) return MLA_ERR_RUNTIME;
   (void)hipGetLastError();
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // under HIP graph capture a launch keeps the run number it was captured
+  // with, so a replay could take the previous replay's tags and flags for
+  // its own: a captured run takes only the kernels that hand no data across
+  // blocks (as mla_prolog_run_noalloc), records no profiling events, and
+  // cannot do the debugging check of cacheIndex, which waits for the device
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cap) != hipSuccess) {
+    (void)hipGetLastError();
+    cap = hipStreamCaptureStatusNone;
+  }
+  const bool captured = cap != hipStreamCaptureStatusNone;
+  if (captured && dd.check_index) {
+    if (prev != dd.device) (void)hipSetDevice(prev);
+    return MLA_ERR_PARAM_INVALID;
+  }
   if (dd.check_index && dd.block_num > 0) {
     // the debugging check of cacheIndex: every entry in [0, slots)
     st = check_cache_index(t->cache_index, T, dd.block_num * dd.block_size, s);
@@ -4661,8 +4676,8 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   c.dd = &dd;
   c.lay = &h->lay;
   c.ws = h->ws;
-  c.fused_ok = h->fused_fit[T <= 16 ? 0 : 1];
-  c.pair_ok = true;
+  c.fused_ok = !captured && h->fused_fit[T <= 16 ? 0 : 1];
+  c.pair_ok = !captured;
   // run numbers 1, 2, ...: 0 is what the flags and tags of the workspace
   // start with, so a wrap of the counter skips it.  A run whose launch fails
   // still uses up its number: no flag can hold it.
@@ -4672,7 +4687,7 @@ mla_status mla_prolog_run(mla_prolog_t h, const mla_prolog_tensors* t, int64_t T
   c.ev = nullptr;
   c.mark_kind = nullptr;
   c.herr = h->herr_dev;
-  if (h->events) {
+  if (h->events && !captured) {
     c.ev = h->events + (h->recorded % kProfileRing) * kProfileEvents;
     c.mark_kind = h->fused + (h->recorded % kProfileRing);
     ++h->recorded;

@@ -315,7 +315,16 @@ mla_status mla_prolog_create(const mla_prolog_desc* desc, mla_prolog_t* out);
  * host-visible memory: once an earlier run's mark is visible to the host,
  * mla_prolog_run returns MLA_ERR_RUNTIME with nothing enqueued, until
  * mla_prolog_check has reported it (a run enqueued before the mark became
- * visible still runs; mla_prolog_check is the one certain report). */
+ * visible still runs; mla_prolog_check is the one certain report).
+ * A run enqueued while stream is being captured into a HIP graph takes
+ * only the kernels that hand no data across blocks (the selection of
+ * mla_prolog_run_noalloc), since a captured launch would replay the run
+ * number it was captured with: every replay of the graph then computes the
+ * prolog of the tensors' contents at that time.  Replays use the handle's
+ * workspace like runs do, so they must be ordered with the handle's other
+ * runs and replays.  No profiling events are recorded for such a run, and
+ * with check_index set it returns MLA_ERR_PARAM_INVALID (the check waits
+ * for the device). */
 mla_status mla_prolog_run(mla_prolog_t handle, const mla_prolog_tensors* tensors, int64_t T,
                           void* stream);
 
