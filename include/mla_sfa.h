@@ -97,7 +97,10 @@ mla_status mla_sfa_create(const mla_sfa_desc* desc, mla_sfa_t* out);
  * default stream): the attention page's second-phase call
  * (aclnnSparseFlashAttention, function prototype).  T = 0 is a no-op.  One handle must not run on two
  * streams at once (its workspace is shared).  MLA_ERR_RUNTIME if a launch
- * fails. */
+ * fails.  The run only launches kernels, none of which waits on another
+ * block, so it can be captured into a HIP graph: each replay computes the
+ * attention of the tensors' contents at that time (replays share the
+ * handle's workspace with its runs and must be ordered with them). */
 mla_status mla_sfa_run(mla_sfa_t handle, const mla_sfa_tensors* tensors, int64_t T, void* stream);
 
 /* Waits for the handle's device, frees the handle and its workspace (the

@@ -6,7 +6,9 @@ selection as mla_prolog_run_noalloc, so every replay is compared bit for bit
 with a no-allocation call on the same inputs.  Between replays the test
 changes the contents of token_x in place, runs the no-allocation reference
 and synchronises, as a serving loop would; a handle run after the replays
-checks that eager runs of the same handle still agree.
+checks that eager runs of the same handle still agree.  The attention
+consumer's run (mla_sfa_run) is captured and replayed the same way, each
+replay compared bit for bit with an eager run.
 """
 import sys
 
@@ -111,3 +113,52 @@ def test_captured_run_refuses_the_index_check():
                 h.run(tg, T)
         assert e.value.status == mla.MLA_ERR_PARAM_INVALID
         torch.cuda.synchronize()
+
+
+# ---- the attention consumer (mla_sfa_run): no data crosses blocks there, so
+# a captured run replays as the eager one; split rows go through the combine
+# kernel (long_t1) or not (heads80_t4)
+SFA_CASES = ["heads80_t4", "long_t1"]
+
+
+@pytest.mark.parametrize("name", SFA_CASES)
+def test_captured_attention_replays(name):
+    from synth.sfa import make_sfa_inputs
+    from test_gpu_sfa import SMALL
+    inp = make_sfa_inputs(SMALL[name])
+    T, N, D = int(inp["T"]), int(inp["N"]), int(inp["D"])
+    t = {"query": inp["query"], "query_rope": inp["query_rope"], "kv_cache": inp["kv_cache"],
+         "kr_cache": inp["kr_cache"], "sparse_indices": inp["indices"], "block_table": inp["block_table"],
+         "seq_lens_kv": inp["seq_lens"]}
+
+    def tensors():
+        g = {k: dev._tensor(np.asarray(v), "cuda:0") for k, v in t.items()}
+        g["attention_out"] = torch.zeros((T, N, D), dtype=torch.bfloat16, device="cuda:0")
+        g["softmax_max"] = torch.zeros((T, N), dtype=torch.float32, device="cuda:0")
+        g["softmax_sum"] = torch.zeros((T, N), dtype=torch.float32, device="cuda:0")
+        return g
+
+    desc = mla.make_sfa_desc(N=N, D=D, Dr=int(inp["Dr"]), block_num=int(inp["block_num"]),
+                             block_size=int(inp["block_size"]), max_blocks=int(inp["max_blocks"]),
+                             sparse_size=int(inp["K"]), sparse_block_size=int(inp["sparse_block_size"]),
+                             max_tokens=T, scale=float(inp["scale"]), concat=0)
+    with mla.MlaSfa(desc) as h:
+        gt = tensors()
+        torch.cuda.synchronize()
+        qs = [gt["query"].clone(), other_x(gt["query"], 11), gt["query"].clone()]
+        say(f"case attention graph capture {name} T={T}")
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            h.run(gt, T)
+        torch.cuda.synchronize()
+        for i, q in enumerate(qs):
+            say(f"case attention graph replay {name} #{i}")
+            gt["query"].copy_(q)
+            ref = tensors()
+            ref["query"].copy_(q)
+            h.run(ref, T)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for k in ("attention_out", "softmax_max", "softmax_sum"):
+                assert np.array_equal(dev.bits(gt[k]), dev.bits(ref[k])), f"replay {i}: {k} differs from the eager run"
