@@ -3784,8 +3784,17 @@ constexpr bool kRingK3 = true;
 constexpr int kRingStages = 48;
 constexpr int kTiledK1Blocks = 512;   // medium: one-wave blocks
 
+// Medium token counts also take some of the large shapes' kernels, each
+// from where it measured faster at the model shapes (bf16): the 256 x 256
+// up-projection above 256 tokens (past the ring kernel), the long-run W^UK
+// kernel from kMixK4RowsT and the 256 x 256 down-projection from
+// kMixK1LargeT tokens.
+constexpr int kMixK4RowsT = 768;
+constexpr int kMixK1LargeT = 1792;
+
 struct TiledPlan {
   bool large;
+  bool k1L, k3L, k4R;      // the large shapes' down-projection, up-projection, W^UK kernel (k4_rows)
   bool ring;               // medium up-projection on K3r (heads of two nope windows, Dr = 64, T <= 256)
   int mt;                  // medium: 16-token tiles per K4 wave (and per direct K1 wave)
   int k1v, k3v;            // medium kernel shapes: 0 direct, 1 LDS-staged 256-token, 2 LDS-staged 128-token
@@ -3808,6 +3817,10 @@ TiledPlan tiled_plan(const mla_prolog_desc& d, int64_t T) {
   // as deep)
   tp.k1v = T > 128 ? 1 : (down_i8(d) && T > 64) ? 2 : 0;
   tp.k3v = T > 128 ? 1 : (up_i8(d) && T > 64) ? 2 : 0;
+  const bool bf16 = !down_i8(d) && !up_i8(d) && d.float_dtype != MLA_FP16;
+  tp.k1L = tp.large || (bf16 && T >= kMixK1LargeT);
+  tp.k3L = tp.large || (bf16 && !tp.ring && T > 256);
+  tp.k4R = d.query_dtype != MLA_INT8 && g.nst_d <= 4 && (tp.large || (bf16 && T >= kMixK4RowsT));
   if (tp.large) {
     tp.m1 = ceil_div(T, 256); tp.ngrp1 = ceil_div(tiles, 4);      // LDS-staged 256 x 256
     tp.m3 = ceil_div(T, 256); tp.ngrp3 = ceil_div(g.win_uq, 4);
@@ -3815,15 +3828,17 @@ TiledPlan tiled_plan(const mla_prolog_desc& d, int64_t T) {
   } else {
     // LDS-staged block rows
     const int bm1 = tp.k1v == 1 ? 256 : 128, bm3 = tp.k3v == 1 ? 256 : 128;
-    if (tp.k1v) { tp.m1 = ceil_div(T, bm1); tp.ngrp1 = ceil_div(tiles, 2); }
+    if (tp.k1L) { tp.m1 = ceil_div(T, 256); tp.ngrp1 = ceil_div(tiles, 4); }
+    else if (tp.k1v) { tp.m1 = ceil_div(T, bm1); tp.ngrp1 = ceil_div(tiles, 2); }
     else { tp.m1 = ceil_div(T, 16 * tp.mt); tp.ngrp1 = tiles; }
-    if (tp.k3v) { tp.m3 = ceil_div(T, bm3); tp.ngrp3 = ceil_div(g.win_uq, 2); }
+    if (tp.k3L) { tp.m3 = ceil_div(T, 256); tp.ngrp3 = ceil_div(g.win_uq, 4); }
+    else if (tp.k3v) { tp.m3 = ceil_div(T, bm3); tp.ngrp3 = ceil_div(g.win_uq, 2); }
     else { tp.m3 = ceil_div(T, 64); tp.ngrp3 = g.win_uq; }                            // 64-token waves
     tp.m4 = ceil_div(T, 16 * tp.mt); tp.cg4 = ceil_div(g.uk_w, 8);
   }
   // large: two k splits, so that the 1-block-per-CU grid fills whole rounds;
   // medium LDS-staged: about one block per CU
-  const int target = tp.large ? 2 * tp.m1 * tp.ngrp1 : tp.k1v ? 256 : kTiledK1Blocks;
+  const int target = tp.k1L ? 2 * tp.m1 * tp.ngrp1 : tp.k1v ? 256 : kTiledK1Blocks;
   int S = std::max(1, std::min(g.nst_he, target / std::max(1, tp.m1 * tp.ngrp1)));
   tp.sps = ceil_div(g.nst_he, S);
   tp.S = ceil_div(g.nst_he, tp.sps);
@@ -4242,12 +4257,23 @@ void launch_ring(hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g) 
   }
 }
 
+// The long-run W^UK kernel: about one block per CU, all of a head's blocks
+// sharing its W^UK
+template <bool F16>
+void launch_k4_rows(hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g) {
+  const int mtiles = ceil_div(d.T, kRowsTile);
+  const int ph = std::max(1, std::min(mtiles, 256 / d.N));
+  k4_rows<F16><<<dim3(ph * d.N), 512, 0, s>>>(d, p, g, ph);
+}
+
 // Tiled run on packed weights (token counts above the streaming range).
 template <bool I8D, bool I8U, int MT, class Mark, bool F16 = false>
 void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g,
                   bool q8, bool pair_ok, Mark& mark) {
   const dim3 g1(tp.m1 * tp.ngrp1 * tp.S), g3(tp.m3 * tp.ngrp3);
-  if (tp.k1v == 1)
+  if (tp.k1L)
+    k1_tiled<I8D, 4, 1, 4, 4, 2, true><<<g1, 1024, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
+  else if (tp.k1v == 1)
     k1_tiled<I8D, 4, 1, 4, 2, 2, true, 1, true><<<g1, 512, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
   else if (I8D && tp.k1v == 2)
     k1_tiled<I8D, 2, 1, 4, 2, 2, true, 1, true><<<g1, 512, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
@@ -4265,6 +4291,8 @@ void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs&
     } else {
       launch_ring<I8U, false, false>(s, d, p, g);
     }
+  } else if (tp.k3L) {
+    k3_tiled<I8U, 4, 1, 4, 4, 2, true, 1, false, F16><<<g3, 1024, 0, s>>>(d, p, g, tp.m3);
   } else if (tp.k3v == 1) {
     k3_tiled<I8U, 2, 1, 8, 2, 2, true, 1, true, F16><<<g3, 1024, 0, s>>>(d, p, g, tp.m3);
   } else if (I8U && tp.k3v == 2) {
@@ -4280,6 +4308,7 @@ void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs&
   }
   mark(3);
   if (q8) k4_tiled<4, 1, 1, 8, 2, true, false, true><<<dim3(tp.m4q * d.N), 512, 0, s>>>(d, p, g, tp.m4q, 1);
+  else if (tp.k4R) launch_k4_rows<F16>(s, d, p, g);
   else k4_tiled<MT, 1, 1, 8, 2, false, false, true, F16><<<dim3(tp.m4 * tp.cg4 * d.N), 512, 0, s>>>(d, p, g, tp.m4,
                                                                                            tp.cg4);
   mark(4);
@@ -4296,12 +4325,7 @@ void tiled_large(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs& 
   k3_tiled<I8U, 4, 1, 4, 4, 2, true, 1, false, F16><<<dim3(tp.m3 * tp.ngrp3), 1024, 0, s>>>(d, p, g, tp.m3);
   mark(3);
   if (q8) k4_tiled<4, 1, 1, 8, 2, true, false, true><<<dim3(tp.m4q * d.N), 512, 0, s>>>(d, p, g, tp.m4q, 1);
-  else if (g.nst_d <= 4) {
-    // about one block per CU, all of a head's blocks sharing its W^UK
-    const int mtiles = ceil_div(d.T, kRowsTile);
-    const int ph = std::max(1, std::min(mtiles, 256 / d.N));
-    k4_rows<F16><<<dim3(ph * d.N), 512, 0, s>>>(d, p, g, ph);
-  }
+  else if (tp.k4R) launch_k4_rows<F16>(s, d, p, g);
   else k4_tiled<4, 1, 4, 4, 2, false, true, true, F16><<<dim3(tp.m4 * tp.cg4 * d.N), 1024, 0, s>>>(d, p, g, tp.m4,
                                                                                           tp.cg4);
   mark(4);

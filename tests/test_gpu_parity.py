@@ -484,6 +484,21 @@ def test_full_size_tiled_packed(name):
     full_check(inp, rows=check_rows(inp), packed=True)
 
 
+# model shapes at medium token counts past the ring kernel, where the launch
+# mixes medium and large kernel shapes: 300 (the 256 x 256 up-projection),
+# 1000 (also the long-run W^UK kernel), 1900 (also the 256 x 256
+# down-projection)
+MODEL_DIMS = Dims(He=7168, Hcq=1536, Hckv=512, N=128, D=128, Dr=64)
+
+
+@pytest.mark.parametrize("T", [300, 1000, 1900])
+def test_full_size_medium_mixed_packed(T):
+    wl = custom_workload(f"model_t{T}", T=T, dims=MODEL_DIMS, block_num=(T + 127) // 128 + 2, block_size=128,
+                         seed=500 + T)
+    inp = synth.make_inputs(wl)
+    full_check(inp, rows=check_rows(inp), packed=True)
+
+
 # ---- the medium-T up-projection in (head, half) blocks (two nope windows,
 # Dr = 64): D = 96 leaves the second nope window half empty, N = 3 takes the
 # other block-to-head mapping, 33 / 128 / 129 / 256 tokens the ends of its
