@@ -3785,10 +3785,10 @@ constexpr int kRingStages = 48;
 constexpr int kTiledK1Blocks = 512;   // medium: one-wave blocks
 
 // Medium token counts also take some of the large shapes' kernels, each
-// from where it measured faster at the model shapes (bf16): the 256 x 256
-// up-projection above 256 tokens (past the ring kernel), the long-run W^UK
-// kernel from kMixK4RowsT and the 256 x 256 down-projection from
-// kMixK1LargeT tokens.
+// from where it measured faster at the model shapes (bf16 and int8): the
+// 256 x 256 up-projection above 256 tokens (past the ring kernel), the
+// long-run W^UK kernel (bf16 query) from kMixK4RowsT and the 256 x 256
+// down-projection from kMixK1LargeT tokens.
 constexpr int kMixK4RowsT = 768;
 constexpr int kMixK1LargeT = 1792;
 
@@ -3817,10 +3817,9 @@ TiledPlan tiled_plan(const mla_prolog_desc& d, int64_t T) {
   // as deep)
   tp.k1v = T > 128 ? 1 : (down_i8(d) && T > 64) ? 2 : 0;
   tp.k3v = T > 128 ? 1 : (up_i8(d) && T > 64) ? 2 : 0;
-  const bool bf16 = !down_i8(d) && !up_i8(d) && d.float_dtype != MLA_FP16;
-  tp.k1L = tp.large || (bf16 && T >= kMixK1LargeT);
-  tp.k3L = tp.large || (bf16 && !tp.ring && T > 256);
-  tp.k4R = d.query_dtype != MLA_INT8 && g.nst_d <= 4 && (tp.large || (bf16 && T >= kMixK4RowsT));
+  tp.k1L = tp.large || T >= kMixK1LargeT;
+  tp.k3L = tp.large || (!tp.ring && T > 256);
+  tp.k4R = d.query_dtype != MLA_INT8 && g.nst_d <= 4 && (tp.large || T >= kMixK4RowsT);
   if (tp.large) {
     tp.m1 = ceil_div(T, 256); tp.ngrp1 = ceil_div(tiles, 4);      // LDS-staged 256 x 256
     tp.m3 = ceil_div(T, 256); tp.ngrp3 = ceil_div(g.win_uq, 4);
