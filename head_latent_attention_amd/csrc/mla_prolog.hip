@@ -3190,6 +3190,129 @@ __global__ __launch_bounds__(512) void k4_rows(Dims d, Ptrs p, PackGeo pg, int p
   }
 }
 
+// K4w with the int8 query: q^N = q^C[., h, .] W^UK[h] quantised per
+// (token, head) with scale RowMax(|q^N|)/127 (the same fp32 accumulation
+// order per element as K4t's int8 epilogue).  ph blocks per head, heads
+// fastest; block (h, j) takes the 128-token tiles j, j + ph, ...  The head's
+// whole W^UK is loaded into LDS once.  Wave w takes 16 tokens of a tile and
+// every window, so the whole 512-column row of its tokens is in its
+// registers (32 accumulators) and the row maximum needs no other wave; the
+// next tile's q^C fragments load while the current tile is multiplied.
+constexpr int kRowsQ8Tile = 128;   // tokens of a tile (8 waves x 16)
+
+__global__ __launch_bounds__(512) void k4_rows_q8(Dims d, Ptrs p, PackGeo pg, int ph) {
+  constexpr int NW = 8, NSD = 4, NWIN = 8, UKMAX = NWIN * NSD * 4 * 1024;
+  constexpr int TP = 80;   // the code tile's row pitch (bytes): 16 tokens x 64 codes
+  __shared__ __attribute__((aligned(16))) uint8_t wl[UKMAX];
+  __shared__ __attribute__((aligned(16))) uint8_t ctile[NW * 16 * TP];
+  const int h = blockIdx.x % d.N, j0 = blockIdx.x / d.N;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int nst = pg.nst_d, nt = (d.T + 15) / 16, mtiles = (d.T + kRowsQ8Tile - 1) / kRowsQ8Tile;
+  const int64_t qtile = int64_t(d.N) * nst * 1024;
+  const rsrc_t Q = make_rsrc(p.qc, int64_t(nt) * qtile);
+  const rsrc_t Wp = make_rsrc(p.packed, pg.total);
+  const uint32_t wbytes = uint32_t(nst) * 4096u, ubytes = uint32_t(pg.uk_w) * wbytes;
+  const uint32_t ukh = uint32_t(pg.off_uk + int64_t(h) * ubytes);
+  // the wave's q^C fragments of tile j (zeros past the run)
+  using AF = uint4[NSD];
+  auto aload = [&](AF& a, int j) {
+    const int tt = j * NW + w;
+#pragma unroll
+    for (int st = 0; st < NSD; ++st)
+      a[st] = bload16(Q, j < mtiles && tt < nt && st < nst
+                             ? uint32_t(tt * qtile + int64_t(h) * nst * 1024) + uint32_t(st) * 1024u +
+                                   uint32_t(lane * 16)
+                             : kOOB);
+  };
+  {
+    uint4 r[UKMAX / 8192];
+#pragma unroll
+    for (int i = 0; i < UKMAX / 8192; ++i) {
+      const uint32_t o = uint32_t(threadIdx.x) * 16u + 8192u * i;
+      r[i] = bload16(Wp, o < ubytes ? ukh + o : kOOB);
+    }
+#pragma unroll
+    for (int i = 0; i < UKMAX / 8192; ++i) {
+      const uint32_t o = uint32_t(threadIdx.x) * 16u + 8192u * i;
+      if (o < ubytes) *reinterpret_cast<uint4*>(wl + o) = r[i];
+    }
+  }
+  AF a0, a1;
+  aload(a0, j0);
+  // orders LDS only (the q^C loads may still be in flight)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  int8_t* const qo = static_cast<int8_t*>(p.q_out);
+  auto work = [&](const AF& a, int j) {
+    f32x4 acc[NWIN * 4];
+#pragma unroll
+    for (int i = 0; i < NWIN * 4; ++i) acc[i] = f32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int jw = 0; jw < NWIN; ++jw) {
+      if (jw >= pg.uk_w) break;
+      const uint8_t* L = wl + jw * wbytes;
+#pragma unroll
+      for (int st = 0; st < NSD; ++st) {
+        if (st >= nst) break;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const bf16x8 bf = *reinterpret_cast<const bf16x8*>(L + (st * 4 + ct) * 1024 + lane * 16);
+          acc[jw * 4 + ct] = mfma(bf, __builtin_bit_cast(bf16x8, a[st]), acc[jw * 4 + ct]);
+        }
+      }
+    }
+    // the row maximum of |q^N| over the valid columns: lane (c, g) holds
+    // token c, columns 16 ct + 4 g + r of each window
+    float mx = 0.0f;
+#pragma unroll
+    for (int jw = 0; jw < NWIN; ++jw)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        if (jw < pg.uk_w && 64 * jw + 16 * ct + 4 * g < d.Hckv)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(acc[jw * 4 + ct][r]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const int m = 16 * (j * NW + w) + c;
+    const float sc = mx / 127.0f;
+    // each window's 16 x 64 codes through the wave's LDS tile, out as
+    // 16-byte stores of whole 64-byte row pieces (lane: token l/4, piece l%4)
+    uint8_t* const tl = ctile + w * 16 * TP;
+    const int mr = 16 * (j * NW + w) + (lane >> 2), pc = 16 * (lane & 3);
+#pragma unroll
+    for (int jw = 0; jw < NWIN; ++jw) {
+      if (jw >= pg.uk_w) break;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        uint32_t q = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          q |= uint32_t(uint8_t(sc > 0.0f ? quant_code(acc[jw * 4 + ct][r], sc) : int8_t(0))) << (8 * r);
+        *reinterpret_cast<uint32_t*>(tl + c * TP + 16 * ct + 4 * g) = q;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const uint4 v = *reinterpret_cast<const uint4*>(tl + (lane >> 2) * TP + pc);
+      if (j < mtiles && mr < d.T && 64 * jw + pc < d.Hckv)
+        *reinterpret_cast<uint4*>(qo + (int64_t(mr) * d.N + h) * d.qs + 64 * jw + pc) = v;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    if (g == 0 && j < mtiles && m < d.T) p.q_scale[int64_t(m) * d.N + h] = sc;
+  };
+  // two tiles a round, each loading while the other is multiplied
+  for (int j = j0; j < mtiles; j += 2 * ph) {
+    aload(a1, j + ph);
+    work(a0, j);
+    aload(a0, j + 2 * ph);
+    if (j + ph < mtiles) work(a1, j + ph);
+  }
+}
+
 // K4t: grid (token tiles fastest, then column groups, then heads).  q^N =
 // q^C[., h, .] W^UK[h]; bf16 stores, or (one column group holding the whole
 // Hckv row) the per-(token, head) int8 quantisation with the row maximum
@@ -3787,9 +3910,10 @@ constexpr int kTiledK1Blocks = 512;   // medium: one-wave blocks
 // Medium token counts also take some of the large shapes' kernels, each
 // from where it measured faster at the model shapes (bf16 and int8): the
 // 256 x 256 up-projection above 256 tokens (past the ring kernel), the
-// long-run W^UK kernel (bf16 query) from kMixK4RowsT and the 256 x 256
-// down-projection from kMixK1LargeT tokens.
+// long-run W^UK kernels from kMixK4RowsT (bf16 query) or kMixK4RowsQ8T
+// (int8 query) and the 256 x 256 down-projection from kMixK1LargeT tokens.
 constexpr int kMixK4RowsT = 768;
+constexpr int kMixK4RowsQ8T = 768;
 constexpr int kMixK1LargeT = 1792;
 
 struct TiledPlan {
@@ -3819,7 +3943,7 @@ TiledPlan tiled_plan(const mla_prolog_desc& d, int64_t T) {
   tp.k3v = T > 128 ? 1 : (up_i8(d) && T > 64) ? 2 : 0;
   tp.k1L = tp.large || T >= kMixK1LargeT;
   tp.k3L = tp.large || (!tp.ring && T > 256);
-  tp.k4R = d.query_dtype != MLA_INT8 && g.nst_d <= 4 && (tp.large || T >= kMixK4RowsT);
+  tp.k4R = g.nst_d <= 4 && g.uk_w <= 8 && (tp.large || T >= (d.query_dtype == MLA_INT8 ? kMixK4RowsQ8T : kMixK4RowsT));
   if (tp.large) {
     tp.m1 = ceil_div(T, 256); tp.ngrp1 = ceil_div(tiles, 4);      // LDS-staged 256 x 256
     tp.m3 = ceil_div(T, 256); tp.ngrp3 = ceil_div(g.win_uq, 4);
@@ -4265,6 +4389,13 @@ void launch_k4_rows(hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& 
   k4_rows<F16><<<dim3(ph * d.N), 512, 0, s>>>(d, p, g, ph);
 }
 
+// The long-run W^UK kernel with the int8 query: about one block per CU
+void launch_k4_rows_q8(hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g) {
+  const int mtiles = ceil_div(d.T, kRowsQ8Tile);
+  const int ph = std::max(1, std::min(mtiles, 256 / d.N));
+  k4_rows_q8<<<dim3(ph * d.N), 512, 0, s>>>(d, p, g, ph);
+}
+
 // Tiled run on packed weights (token counts above the streaming range).
 template <bool I8D, bool I8U, int MT, class Mark, bool F16 = false>
 void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs& p, const PackGeo& g,
@@ -4306,7 +4437,8 @@ void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs&
     return;
   }
   mark(3);
-  if (q8) k4_tiled<4, 1, 1, 8, 2, true, false, true><<<dim3(tp.m4q * d.N), 512, 0, s>>>(d, p, g, tp.m4q, 1);
+  if (q8 && tp.k4R) launch_k4_rows_q8(s, d, p, g);
+  else if (q8) k4_tiled<4, 1, 1, 8, 2, true, false, true><<<dim3(tp.m4q * d.N), 512, 0, s>>>(d, p, g, tp.m4q, 1);
   else if (tp.k4R) launch_k4_rows<F16>(s, d, p, g);
   else k4_tiled<MT, 1, 1, 8, 2, false, false, true, F16><<<dim3(tp.m4 * tp.cg4 * d.N), 512, 0, s>>>(d, p, g, tp.m4,
                                                                                            tp.cg4);
@@ -4323,7 +4455,8 @@ void tiled_large(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs& 
   mark(2);
   k3_tiled<I8U, 4, 1, 4, 4, 2, true, 1, false, F16><<<dim3(tp.m3 * tp.ngrp3), 1024, 0, s>>>(d, p, g, tp.m3);
   mark(3);
-  if (q8) k4_tiled<4, 1, 1, 8, 2, true, false, true><<<dim3(tp.m4q * d.N), 512, 0, s>>>(d, p, g, tp.m4q, 1);
+  if (q8 && tp.k4R) launch_k4_rows_q8(s, d, p, g);
+  else if (q8) k4_tiled<4, 1, 1, 8, 2, true, false, true><<<dim3(tp.m4q * d.N), 512, 0, s>>>(d, p, g, tp.m4q, 1);
   else if (tp.k4R) launch_k4_rows<F16>(s, d, p, g);
   else k4_tiled<4, 1, 4, 4, 2, false, true, true, F16><<<dim3(tp.m4 * tp.cg4 * d.N), 1024, 0, s>>>(d, p, g, tp.m4,
                                                                                           tp.cg4);

@@ -491,6 +491,21 @@ def test_full_size_tiled_packed(name):
 MODEL_DIMS = Dims(He=7168, Hcq=1536, Hckv=512, N=128, D=128, Dr=64)
 
 
+# the long-run int8-query W^UK kernel (whole 512-column rows per wave) from
+# 768 tokens on: model shapes, and small dims with a half-width last window
+# (Hckv 96) and a ragged token tail
+def test_full_size_int8_query_long_run_packed():
+    wl = custom_workload("model_q8_t900", T=900, dims=MODEL_DIMS, block_num=10, block_size=128, quant=True, seed=611)
+    inp = synth.make_inputs(wl)
+    full_check(inp, rows=check_rows(inp), packed=True)
+
+
+def test_int8_query_long_run_ragged_packed():
+    wl = custom_workload("q8_t780", T=780, dims=Dims(He=512, Hcq=128, Hckv=96, N=3, D=32, Dr=32),
+                         block_num=50, block_size=16, seed=612, quant=True)
+    full_check(synth.make_inputs(wl), packed=True)
+
+
 @pytest.mark.parametrize("T", [300, 1000, 1900])
 def test_full_size_medium_mixed_packed(T):
     wl = custom_workload(f"model_t{T}", T=T, dims=MODEL_DIMS, block_num=(T + 127) // 128 + 2, block_size=128,
