@@ -3225,18 +3225,20 @@ __global__ __launch_bounds__(512) void k4_rows_q8(Dims d, Ptrs p, PackGeo pg, in
                                    uint32_t(lane * 16)
                              : kOOB);
   };
+  // the head's W^UK in LDS at 16 KB per window (4 D stages of 4 KB), the
+  // stages past nst and the windows past uk_w as zeros, so that the product
+  // below runs over 8 windows x 4 D stages with no branch
   {
     uint4 r[UKMAX / 8192];
 #pragma unroll
     for (int i = 0; i < UKMAX / 8192; ++i) {
-      const uint32_t o = uint32_t(threadIdx.x) * 16u + 8192u * i;
-      r[i] = bload16(Wp, o < ubytes ? ukh + o : kOOB);
+      const uint32_t o = uint32_t(threadIdx.x) * 16u + 8192u * i;   // LDS byte
+      const uint32_t jw = o / (NSD * 4096u), rem = o % (NSD * 4096u);
+      r[i] = bload16(Wp, int(jw) < pg.uk_w && rem < wbytes ? ukh + jw * wbytes + rem : kOOB);
     }
 #pragma unroll
-    for (int i = 0; i < UKMAX / 8192; ++i) {
-      const uint32_t o = uint32_t(threadIdx.x) * 16u + 8192u * i;
-      if (o < ubytes) *reinterpret_cast<uint4*>(wl + o) = r[i];
-    }
+    for (int i = 0; i < UKMAX / 8192; ++i)
+      *reinterpret_cast<uint4*>(wl + uint32_t(threadIdx.x) * 16u + 8192u * i) = r[i];
   }
   AF a0, a1;
   aload(a0, j0);
@@ -3249,19 +3251,21 @@ __global__ __launch_bounds__(512) void k4_rows_q8(Dims d, Ptrs p, PackGeo pg, in
     f32x4 acc[NWIN * 4];
 #pragma unroll
     for (int i = 0; i < NWIN * 4; ++i) acc[i] = f32x4{0, 0, 0, 0};
+    // step k = (window, D stage, column tile); its W^UK fragment is read RA
+    // steps ahead into a ring
+    constexpr int NSTEP = NWIN * NSD * 4, RA = 8;
+    auto frag = [&](int k) {
+      const int jw = k / 16, st = (k / 4) % 4, ct = k % 4;
+      return *reinterpret_cast<const bf16x8*>(wl + jw * NSD * 4096 + (st * 4 + ct) * 1024 + lane * 16);
+    };
+    bf16x8 ring[RA];
 #pragma unroll
-    for (int jw = 0; jw < NWIN; ++jw) {
-      if (jw >= pg.uk_w) break;
-      const uint8_t* L = wl + jw * wbytes;
+    for (int k = 0; k < RA; ++k) ring[k] = frag(k);
 #pragma unroll
-      for (int st = 0; st < NSD; ++st) {
-        if (st >= nst) break;
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          const bf16x8 bf = *reinterpret_cast<const bf16x8*>(L + (st * 4 + ct) * 1024 + lane * 16);
-          acc[jw * 4 + ct] = mfma(bf, __builtin_bit_cast(bf16x8, a[st]), acc[jw * 4 + ct]);
-        }
-      }
+    for (int k = 0; k < NSTEP; ++k) {
+      const int jw = k / 16, st = (k / 4) % 4, ct = k % 4;
+      acc[jw * 4 + ct] = mfma(ring[k % RA], __builtin_bit_cast(bf16x8, a[st]), acc[jw * 4 + ct]);
+      if (k + RA < NSTEP) ring[k % RA] = frag(k + RA);
     }
     // the row maximum of |q^N| over the valid columns: lane (c, g) holds
     // token c, columns 16 ct + 4 g + r of each window
@@ -3913,7 +3917,7 @@ constexpr int kTiledK1Blocks = 512;   // medium: one-wave blocks
 // long-run W^UK kernels from kMixK4RowsT (bf16 query) or kMixK4RowsQ8T
 // (int8 query) and the 256 x 256 down-projection from kMixK1LargeT tokens.
 constexpr int kMixK4RowsT = 768;
-constexpr int kMixK4RowsQ8T = 768;
+constexpr int kMixK4RowsQ8T = 448;
 constexpr int kMixK1LargeT = 1792;
 
 struct TiledPlan {

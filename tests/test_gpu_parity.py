@@ -492,7 +492,7 @@ MODEL_DIMS = Dims(He=7168, Hcq=1536, Hckv=512, N=128, D=128, Dr=64)
 
 
 # the long-run int8-query W^UK kernel (whole 512-column rows per wave) from
-# 768 tokens on: model shapes, and small dims with a half-width last window
+# 448 tokens on: model shapes, and small dims with a half-width last window
 # (Hckv 96) and a ragged token tail
 def test_full_size_int8_query_long_run_packed():
     wl = custom_workload("model_q8_t900", T=900, dims=MODEL_DIMS, block_num=10, block_size=128, quant=True, seed=611)
