@@ -3943,7 +3943,10 @@ TiledPlan tiled_plan(const mla_prolog_desc& d, int64_t T) {
   // medium shapes: LDS-staged blocks above 128 tokens; for an int8 product
   // also from 65 tokens on, in 128-token blocks (the int8 k-stages are twice
   // as deep)
-  tp.k1v = T > 128 ? 1 : (down_i8(d) && T > 64) ? 2 : 0;
+  // (224-256 tokens: two full 128-token tiles halve the splits, and so
+  // the partials the norm kernel reads, for one more read of the weights
+  // from the caches)
+  tp.k1v = (T >= 224 && T <= 256) ? 2 : T > 128 ? 1 : (down_i8(d) && T > 64) ? 2 : 0;
   tp.k3v = T > 128 ? 1 : (up_i8(d) && T > 64) ? 2 : 0;
   tp.k1L = tp.large || T >= kMixK1LargeT;
   tp.k3L = tp.large || (!tp.ring && T > 256);
@@ -4409,7 +4412,7 @@ void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs&
     k1_tiled<I8D, 4, 1, 4, 4, 2, true><<<g1, 1024, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
   else if (tp.k1v == 1)
     k1_tiled<I8D, 4, 1, 4, 2, 2, true, 1, true><<<g1, 512, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
-  else if (I8D && tp.k1v == 2)
+  else if (tp.k1v == 2)
     k1_tiled<I8D, 2, 1, 4, 2, 2, true, 1, true><<<g1, 512, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
   else k1_tiled<I8D, MT, 1, 1, 1, 2><<<g1, 64, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
   mark(1);
