@@ -3925,7 +3925,7 @@ struct TiledPlan {
   bool k1L, k3L, k4R;      // the large shapes' down-projection, up-projection, W^UK kernel (k4_rows)
   bool ring;               // medium up-projection on K3r (heads of two nope windows, Dr = 64, T <= 256)
   int mt;                  // medium: 16-token tiles per K4 wave (and per direct K1 wave)
-  int k1v, k3v;            // medium kernel shapes: 0 direct, 1 LDS-staged 256-token, 2 LDS-staged 128-token
+  int k1v, k3v;            // medium kernel shapes: 0 direct, 1 LDS-staged 256-token, 2 128-token, 3 64-token
   int m1, ngrp1, S, sps;   // K1: token tiles, window groups, splits, stages per split
   int m3, ngrp3;           // K3
   int m4, cg4;             // K4 bf16
@@ -3945,8 +3945,8 @@ TiledPlan tiled_plan(const mla_prolog_desc& d, int64_t T) {
   // as deep)
   // (224-256 tokens: two full 128-token tiles halve the splits, and so
   // the partials the norm kernel reads, for one more read of the weights
-  // from the caches)
-  tp.k1v = (T >= 224 && T <= 256) ? 2 : T > 128 ? 1 : (down_i8(d) && T > 64) ? 2 : 0;
+  // from the caches; int8 x at 65-128 tokens likewise in 64-token tiles)
+  tp.k1v = (T >= 224 && T <= 256) ? 2 : T > 128 ? 1 : (down_i8(d) && T > 64) ? 3 : 0;
   tp.k3v = T > 128 ? 1 : (up_i8(d) && T > 64) ? 2 : 0;
   tp.k1L = tp.large || T >= kMixK1LargeT;
   tp.k3L = tp.large || (!tp.ring && T > 256);
@@ -3957,7 +3957,7 @@ TiledPlan tiled_plan(const mla_prolog_desc& d, int64_t T) {
     tp.m4 = ceil_div(T, 256); tp.cg4 = ceil_div(g.uk_w, 4);      // LDS-staged 256 x 256
   } else {
     // LDS-staged block rows
-    const int bm1 = tp.k1v == 1 ? 256 : 128, bm3 = tp.k3v == 1 ? 256 : 128;
+    const int bm1 = tp.k1v == 1 ? 256 : tp.k1v == 3 ? 64 : 128, bm3 = tp.k3v == 1 ? 256 : 128;
     if (tp.k1L) { tp.m1 = ceil_div(T, 256); tp.ngrp1 = ceil_div(tiles, 4); }
     else if (tp.k1v) { tp.m1 = ceil_div(T, bm1); tp.ngrp1 = ceil_div(tiles, 2); }
     else { tp.m1 = ceil_div(T, 16 * tp.mt); tp.ngrp1 = tiles; }
@@ -4412,6 +4412,8 @@ void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs&
     k1_tiled<I8D, 4, 1, 4, 4, 2, true><<<g1, 1024, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
   else if (tp.k1v == 1)
     k1_tiled<I8D, 4, 1, 4, 2, 2, true, 1, true><<<g1, 512, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
+  else if (tp.k1v == 3)
+    k1_tiled<I8D, 1, 1, 4, 2, 2, true, 1, true><<<g1, 512, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
   else if (tp.k1v == 2)
     k1_tiled<I8D, 2, 1, 4, 2, 2, true, 1, true><<<g1, 512, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
   else k1_tiled<I8D, MT, 1, 1, 1, 2><<<g1, 64, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
