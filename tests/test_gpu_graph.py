@@ -40,6 +40,13 @@ CASES = {
     # W^UK kernel
     "int8_q8_t130": custom_workload("graph_q8", T=130, dims=Dims(He=1024, Hcq=192, Hckv=512, N=3, D=128, Dr=64),
                                     block_num=16, block_size=16, quant=True, seed=402),
+    # the mixed medium kernels (the 256 x 256 up-projection, the long-run
+    # W^UK kernels) and the long-run path, bf16 and the int8 query
+    "bf16_t900": custom_workload("graph_t900", T=900, dims=Dims(He=520, Hcq=200, Hckv=136, N=5, D=96, Dr=64),
+                                 block_num=64, block_size=16, seed=403),
+    "int8_q8_t2100": custom_workload("graph_q8_t2100", T=2100, dims=Dims(He=512, Hcq=128, Hckv=96, N=3, D=32,
+                                                                          Dr=32),
+                                     block_num=140, block_size=16, quant=True, seed=404),
 }
 
 
