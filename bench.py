@@ -278,7 +278,11 @@ def main():
         res = (bench_sfa if args.workload.startswith("sfa_") else bench_prolog)(args, args.workload)
         print(json.dumps(res), flush=True)
         return
-    res = bench_prolog(args, "decode_t32")
+    # the CPU oracle's leg runs after every GPU leg: ten seconds of host work
+    # with the GPU idle would leave the next workload's warmup on a cold clock
+    first = argparse.Namespace(**vars(args))
+    first.no_cpu_baseline = True
+    res = bench_prolog(first, "decode_t32")
     others = {}
     sub = argparse.Namespace(**vars(args))
     sub.steps, sub.warmup, sub.no_cpu_baseline = args.other_steps, args.other_warmup, True
@@ -289,6 +293,9 @@ def main():
         except Exception as e:   # a failure of one configuration is recorded, not fatal
             others[name] = {"error": f"{type(e).__name__}: {e}"}
         print(f"bench: {name} done", file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        import synth
+        res["cpu_baseline"] = cpu_baseline(synth.make_inputs(synth.workload("decode_t32")), args.cpu_seconds)
     res["other_workloads"] = others
     print(json.dumps(res), flush=True)
 
