@@ -49,6 +49,7 @@ constexpr int kMaxDT = 512 / 16 / 2;  // 16-column tiles of O per wave (half of 
 constexpr int kPer = 5;               // 16-byte loads per thread per tile: 32 rows in passes of >= 7 rows
 constexpr int kMaxRows = 2048;        // selected rows of one block
 constexpr int kPPitch = kRows + 8;    // per-wave P tile pitch (bf16)
+constexpr float kLazy = 8.0f;         // how far a tile's maximum may pass the softmax reference
 
 __device__ __forceinline__ uint16_t f2bf(float f) {
   uint32_t u = __float_as_uint(f);
@@ -201,9 +202,11 @@ __global__ __launch_bounds__(64 * kWaves) void k_sfa(SfaArgs a) {
   f32x4 acc[kMaxDT];
 #pragma unroll
   for (int dt = 0; dt < kMaxDT; ++dt) acc[dt] = f32x4{0, 0, 0, 0};
-  float m[4], l[4];
+  // m: the reference the exponentials and l are taken against; mt: the
+  // running maximum itself
+  float m[4], mt[4], l[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) { m[i] = -INFINITY; l[i] = 0.0f; }
+  for (int i = 0; i < 4; ++i) { m[i] = -INFINITY; mt[i] = -INFINITY; l[i] = 0.0f; }
   uint16_t* pwr = pw[hg];
 
   auto step = [&](int tile) {
@@ -234,7 +237,12 @@ __global__ __launch_bounds__(64 * kWaves) void k_sfa(SfaArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float mx = fmaxf(mh[i], xmax[w ^ 4][4 * g + i]);
-      const float mn = fmaxf(m[i], mx);
+      mt[i] = fmaxf(mt[i], mx);
+      // the reference moves only when the tile's maximum passes it by more
+      // than kLazy, so P stays below e^kLazy and O is rescaled about once per
+      // row (softmax does not depend on the reference; the sum is referred
+      // to the true maximum at the end)
+      const float mn = mx > m[i] + kLazy ? mx : m[i];
       const bool none = mn == -INFINITY;
       alpha[i] = none ? 1.0f : __expf(m[i] - mn);
       const float pv = none ? 0.0f : __expf(sv[i] - mn);
@@ -297,14 +305,15 @@ __global__ __launch_bounds__(64 * kWaves) void k_sfa(SfaArgs a) {
     const int h = hb * kHeads + 16 * hg + 4 * g + i;
     if (h >= a.N) continue;
     const float inv = l[i] > 0.0f ? 1.0f / l[i] : 0.0f;
+    const float sum = mt[i] == -INFINITY ? 0.0f : l[i] * __expf(m[i] - mt[i]);
     if (a.S == 1) {
       uint16_t* o = a.out + (int64_t(t) * a.N + h) * a.D + 256 * dh;
 #pragma unroll
       for (int dt = 0; dt < kMaxDT; ++dt)
         if (256 * dh + 16 * dt < a.D) o[16 * dt + c] = f2bf(acc[dt][i] * inv);
       if (c == 0 && dh == 0) {
-        if (a.smax) a.smax[int64_t(t) * a.N + h] = m[i];
-        if (a.ssum) a.ssum[int64_t(t) * a.N + h] = l[i];
+        if (a.smax) a.smax[int64_t(t) * a.N + h] = mt[i];
+        if (a.ssum) a.ssum[int64_t(t) * a.N + h] = sum;
       }
     } else {
       const int64_t row = (int64_t(t) * a.S + s) * a.N + h;
@@ -312,7 +321,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_sfa(SfaArgs a) {
 #pragma unroll
       for (int dt = 0; dt < kMaxDT; ++dt)
         if (256 * dh + 16 * dt < a.D) o[16 * dt + c] = acc[dt][i] * inv;
-      if (c == 0 && dh == 0) { a.part_ml[2 * row] = m[i]; a.part_ml[2 * row + 1] = l[i]; }
+      if (c == 0 && dh == 0) { a.part_ml[2 * row] = mt[i]; a.part_ml[2 * row + 1] = sum; }
     }
   }
 }
