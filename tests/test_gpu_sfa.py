@@ -131,6 +131,42 @@ def test_small(name):
     check(make_sfa_inputs(SMALL[name]))
 
 
+def wide_spread_inputs():
+    """8 tokens x 8 heads over 4096 selected rows (32 splits of four 32-row
+    tiles each), scale 3 over 96 dimensions: scores spread by ~30."""
+    inp = make_sfa_inputs(custom_sfa_workload("wide_t8", T=8, N=8, D=64, Dr=32, block_size=64, K=4096,
+                                              len_lo=4200, len_hi=5000, seed=56))
+    inp["scale"] = 3.0
+    return inp
+
+
+def tile_jumps(inp, rows=128):
+    """How often, over the first `rows` selected rows of each (token, head),
+    a 32-row tile's maximum score passes the running maximum of the tiles
+    before it by more than 8 (float64)."""
+    D, Dr, bs = int(inp["D"]), int(inp["Dr"]), int(inp["block_size"])
+    kvall, krall = bf16(inp["kv_cache"]).reshape(-1, D), bf16(inp["kr_cache"]).reshape(-1, Dr)
+    jumps = 0
+    for t in range(int(inp["T"])):
+        slots = [int(inp["block_table"][t][p // bs]) * bs + int(p) % bs for p in inp["indices"][t][:rows]]
+        sc = inp["scale"] * (bf16(inp["query"][t]) @ kvall[slots].T + bf16(inp["query_rope"][t]) @ krall[slots].T)
+        tmax = sc.reshape(sc.shape[0], rows // 32, 32).max(axis=2)
+        run = np.maximum.accumulate(tmax, axis=1)
+        jumps += int((tmax[:, 1:] > run[:, :-1] + 8.0).sum())
+    return jumps
+
+
+def test_wide_score_spread():
+    """The attention kernel takes its exponentials against a reference that
+    lags the running maximum by up to 8 and rescales O only when a tile
+    passes it by more.  With scores spread this widely later tiles do, so the
+    rescale runs after the first tile too; softmax_max and softmax_sum (the
+    sum referred back to the true maximum) are compared as well."""
+    inp = wide_spread_inputs()
+    assert tile_jumps(inp) > 0
+    check(inp)
+
+
 @pytest.mark.parametrize("name", ["ragged_t5", "heads80_t4"])
 def test_concatenated_cache(name):
     check(make_sfa_inputs(replace(SMALL[name], concat=True)))
