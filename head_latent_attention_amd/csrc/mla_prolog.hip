@@ -4418,15 +4418,15 @@ void tiled_medium(const TiledPlan& tp, hipStream_t s, const Dims& d, const Ptrs&
                   bool q8, bool pair_ok, Mark& mark) {
   const dim3 g1(tp.m1 * tp.ngrp1 * tp.S), g3(tp.m3 * tp.ngrp3);
   const int n1 = tp.m1 * tp.ngrp1 * tp.S;
-  // the 128-token tiles run in XCD order (the two token tiles of a window
-  // group share an XCD's L2: 24.1 -> 22.9 us for 256 bf16 tokens at the
-  // model's shapes); the 64- and 256-token shapes keep the plain order (the
-  // int8 64-token tiles at 128 tokens measured 13.6 -> 14.0 us with it)
+  // the 128- and 256-token tiles run in XCD order (the token tiles of a
+  // window group share an XCD's L2: at the model's shapes 24.1 -> 22.9 us
+  // for 256 bf16 tokens, 94.8 -> 86 us for 1536); the int8 64-token tiles
+  // keep the plain order (13.6 -> 14.0 us at 128 tokens with it)
   const dim3 g1x((n1 + 7) / 8 * 8);
   if (tp.k1L)
     k1_tiled<I8D, 4, 1, 4, 4, 2, true><<<g1, 1024, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
   else if (tp.k1v == 1)
-    k1_tiled<I8D, 4, 1, 4, 2, 2, true, 1, true><<<g1, 512, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
+    k1_tiled<I8D, 4, 1, 4, 2, 2, true, 1, true><<<g1x, 512, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1, n1);
   else if (tp.k1v == 3)
     k1_tiled<I8D, 1, 1, 4, 2, 2, true, 1, true><<<g1, 512, 0, s>>>(d, p, g, tp.sps, tp.m1, tp.ngrp1);
   else if (tp.k1v == 2)
